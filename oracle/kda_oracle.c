@@ -1,0 +1,133 @@
+/*
+ * kda_oracle.c -- plain, slow, sequential fp64 CPU oracle for Kimi Delta
+ * Attention (KDA).  TEST INFRASTRUCTURE ONLY: the GPU library never links,
+ * includes or calls this file; only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark use it.
+ *
+ * What it computes (source: "Kimi K3 Open Weights: What Is Actually New In Its
+ * 2.8 Trillion Parameter Architecture", shivasnotes.com, section 1 "Kimi Delta
+ * Attention is a real new kernel family"):
+ *
+ *   recurrence (the single-head state equation of that section):
+ *       S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *       o_t = S_t^T q_t                  (the read uses the UPDATED state)
+ *   decay gate (the bounded-sigmoid equation of the same section):
+ *       g_t = g_min * sigma(e^A * z_t),  alpha_t = e^{g_t},  g_min = -5
+ *
+ * S has dk key rows and dv value columns; alpha_t is a vector over the dk key
+ * channels and scales S's rows ("fade (channel-wise alpha) -> erase (delta
+ * rule) -> write", kimi-k3-course capstone, one-page map, SEQUENCE block).
+ *
+ * Readings where the page leaves a step open:
+ *   - "sigma(e^A z_t)" is read as the logistic function of the product
+ *     e^{A_h} * z_t, with one scalar A per head.
+ *   - no 1/sqrt(dk) query scale, no output norm or gate: o_t is the raw read.
+ *   - beta is used as given (not clamped).
+ *
+ * Every step below is the literal matrix product in the order written above:
+ * fade the rows, erase along k with the faded state, write beta k v^T, read
+ * with q.  Nothing is blocked, fused or reordered.  Sums over the key index run
+ * in ascending order, so the result does not depend on the thread count.
+ *
+ * Layouts (row-major, contiguous):
+ *   q, k, z : [B, T, H, dk]      v, o : [B, T, H, dv]      beta : [B, T, H]
+ *   A       : [H]                S0, S_T : [B, H, dk, dv]  (S0 may be NULL = 0)
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define KDA_ORACLE_GMIN (-5.0)
+
+/* Bounded decay gate g = g_min * sigma(c * z) with sigma(x) = 1/(1+e^{-x}).
+ * For c*z -> -inf, exp(+inf) = inf and 1/inf = 0, so g = -0 and alpha = 1
+ * exactly; for c*z -> +inf, g -> g_min. */
+static double oracle_gate(double c, double z) {
+    return KDA_ORACLE_GMIN / (1.0 + exp(-(c * z)));
+}
+
+/* g for n values of z with one head scale A (c = e^A). */
+void kda_oracle_gate_f64(int64_t n, const double *z, double A, double *g_out) {
+    const double c = exp(A);
+    for (int64_t i = 0; i < n; ++i) g_out[i] = oracle_gate(c, z[i]);
+}
+
+int kda_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Runs the recurrence for every (b, h).  Returns 0 on success, 1 on a bad
+ * argument, 2 when scratch memory cannot be allocated. */
+int kda_oracle_f64(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                   const double *q, const double *k, const double *v,
+                   const double *z, const double *beta, const double *A,
+                   const double *S0, double *o, double *S_T, int nthreads) {
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return 1;
+    if (!A || !S_T) return 1;
+    if (T > 0 && (!q || !k || !v || !z || !beta || !o)) return 1;
+    const int64_t units = B * H;
+    if (units == 0) return 0;
+    int failed = 0;
+    if (nthreads < 1) nthreads = 1;
+
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(| : failed)
+    for (int64_t u = 0; u < units; ++u) {
+        const int64_t b = u / H, h = u % H;
+        double *S = (double *)malloc(sizeof(double) * (size_t)(dk * dv));
+        double *alpha = (double *)malloc(sizeof(double) * (size_t)dk);
+        double *w = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !alpha || !w) {
+            free(S); free(alpha); free(w);
+            failed |= 1;
+            continue;
+        }
+        const double *s0 = S0 ? S0 + u * dk * dv : NULL;
+        for (int64_t e = 0; e < dk * dv; ++e) S[e] = s0 ? s0[e] : 0.0;
+        const double c = exp(A[h]);
+
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t row = (b * T + t) * H + h;
+            const double *qt = q + row * dk;
+            const double *kt = k + row * dk;
+            const double *zt = z + row * dk;
+            const double *vt = v + row * dv;
+            const double bt = beta[row];
+            double *ot = o + row * dv;
+
+            /* gate: alpha_i = exp(g_min * sigma(c * z_i)) */
+            for (int64_t i = 0; i < dk; ++i) alpha[i] = exp(oracle_gate(c, zt[i]));
+
+            /* fade: S <- Diag(alpha) S   (alpha scales key rows) */
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) S[i * dv + j] *= alpha[i];
+
+            /* erase: S <- (I - beta k k^T) S, via w = S^T k */
+            for (int64_t j = 0; j < dv; ++j) w[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) w[j] += kt[i] * S[i * dv + j];
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) S[i * dv + j] -= bt * kt[i] * w[j];
+
+            /* write: S <- S + beta k v^T */
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) S[i * dv + j] += bt * kt[i] * vt[j];
+
+            /* read: o = S^T q with the updated state */
+            for (int64_t j = 0; j < dv; ++j) ot[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) ot[j] += S[i * dv + j] * qt[i];
+        }
+        memcpy(S_T + u * dk * dv, S, sizeof(double) * (size_t)(dk * dv));
+        free(S); free(alpha); free(w);
+    }
+    return failed ? 2 : 0;
+}
