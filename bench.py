@@ -1,0 +1,172 @@
+"""KDA benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk 16|64] [--no-cpu]
+
+A step is one chunkwise prefill over the K3 head-shape workload (B=1, H=96,
+T=4096, dk=dv=128, bf16 inputs, fp32 state, S0 ~ N(0, 0.02^2)) with inputs
+resident in HBM; ``value`` is tokens/s over the K timed steps.  The same run
+also times the fused decode step on the batched decode workload (B=64, H=96,
+d=128, 256 steps on a persistent fp32 state) and reports head-state updates/s
+under ``decode``.  Times come from HIP events recorded on the stream the
+kernels are launched on (torch's current stream).
+
+Roofline: both kernels are HBM-bound at these shapes.  ``achieved`` is the
+algorithmic bytes one launch must move divided by its average duration:
+  prefill: B*T*H*(4*d*2 + d*2 + 2) + 2*B*H*d*d*4 + H*4 bytes
+           (q, k, z, v read, o written, beta read; S0 read and S_T written; A)
+  decode : B*H*(2*d*d*4 + 4*d*2 + 2 + d*2) + H*4 bytes per step
+The fp64 oracle is timed on the host cores over the full prefill workload
+(``cpu_baseline``), reported in the same unit.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KDA prefill tokens/s (H=96,d=128,bf16) + decode state-updates/s; % roofline"
+
+
+def prefill_bytes(B, T, H, d, esz=2):
+    return B * T * H * (4 * d * esz + d * esz + esz) + 2 * B * H * d * d * 4 + H * 4
+
+
+def decode_bytes(B, H, d, esz=2):
+    return B * H * (2 * d * d * 4 + 4 * d * esz + esz + d * esz) + H * 4
+
+
+def _events(torch):
+    return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+
+def time_prefill(torch, kda, inp, chunk, steps, warmup):
+    out = torch.empty_like(inp["v"])
+    S_T = torch.empty_like(inp["S0"])
+
+    def run():
+        kda.prefill(inp["q"], inp["k"], inp["v"], inp["z"], inp["beta"], inp["A"], inp["S0"],
+                    chunk=chunk, out=out, S_T=S_T)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps   # ms per launch
+
+
+def time_decode(torch, kda, dinp, reps):
+    S = dinp["S"]
+    steps = dinp["q"].shape[0]
+    out = torch.empty_like(dinp["v"][0])
+
+    def one_pass():
+        for t in range(steps):
+            kda.decode_step(dinp["q"][t], dinp["k"][t], dinp["v"][t], dinp["z"][t],
+                            dinp["beta"][t], dinp["A"], S, out=out)
+
+    one_pass()   # warm-up pass
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(reps):
+        one_pass()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * steps)   # ms per decode step
+
+
+def cpu_baseline(w, inp_cpu):
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = max(1, min(threads, os.cpu_count() or 1, w.B * w.H))
+    f = lambda t: None if t is None else t.float().numpy()
+    args = [f(inp_cpu[n]) for n in ("q", "k", "v", "z", "beta", "A", "S0")]
+    t0 = time.perf_counter()
+    oracle.prefill(*args, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"full {w.name} prefill (B{w.B} H{w.H} T{w.T} d{w.dk}), fp64 sequential "
+                      f"recurrence, {dt:.2f} s wall"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--chunk", type=int, default=16, choices=(16, 64))
+    ap.add_argument("--decode-reps", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (got --gpus {args.gpus}); "
+              "multi-GPU runs are not part of it", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import linear_recurrent_attention_chunkwise_amd as kda
+    from linear_recurrent_attention_chunkwise_amd.inputs import (WORKLOADS, make_decode_inputs,
+                                                                 make_prefill_inputs)
+
+    dev = torch.device("cuda:0")
+    w = WORKLOADS["k3_prefill_bf16"].with_(chunk=args.chunk)
+    inp_cpu = make_prefill_inputs(w)
+    inp = {k: (v.to(dev) if v is not None else None) for k, v in inp_cpu.items()}
+    ms = time_prefill(torch, kda, inp, args.chunk, args.steps, args.warmup)
+    pbytes = prefill_bytes(w.B, w.T, w.H, w.dk)
+    achieved = pbytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": w.B * w.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: KDA chunkwise prefill B={w.B} H={w.H} T={w.T} "
+                               f"dk=dv={w.dk} chunk={args.chunk} bf16 in, fp32 state",
+                   "B": w.B, "H": w.H, "T": w.T, "d": w.dk, "chunk": args.chunk},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kda_prefill_kernel", "bytes_per_launch": pbytes},
+    }
+    if not args.no_decode:
+        wd = WORKLOADS["k3_decode_bf16"]
+        dinp = make_decode_inputs(wd, device=dev)
+        dms = time_decode(torch, kda, dinp, args.decode_reps)
+        dbytes = decode_bytes(wd.B, wd.H, wd.dk)
+        dach = dbytes / (dms * 1e-3) / 1e9
+        result["decode"] = {
+            "value": wd.B * wd.H / (dms * 1e-3), "unit": "head-state-updates/s",
+            "us_per_step": dms * 1e3,
+            "workload": f"{wd.name}: B={wd.B} H={wd.H} d={wd.dk}, {wd.steps} steps, fp32 state",
+            "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dach / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "kda_decode_kernel", "bytes_per_launch": dbytes}}
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, inp_cpu)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,140 @@
+/*
+ * kda.h -- C ABI of libkda.so: Kimi Delta Attention (KDA) on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * KDA is the gated delta-rule recurrence of "Kimi K3 Open Weights: What Is
+ * Actually New In Its 2.8 Trillion Parameter Architecture" (shivasnotes.com),
+ * section 1 "Kimi Delta Attention is a real new kernel family":
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *     alpha_t = exp(g_t),  g_t = g_min * sigma(e^{A_h} z_t),  g_min = -5
+ *
+ * per batch entry b and head h.  S_t has dk key rows and dv value columns;
+ * alpha_t is a per-key-channel vector scaling S's rows; sigma is the logistic
+ * function.  The same section splits the work into a chunked-parallel prefill
+ * ("tokens are processed in parallel within chunks") and a fused recurrent
+ * one-token decode step that keeps the state persistent.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer on the current HIP device; the
+ *    caller owns all memory.  The library allocates no device memory and keeps
+ *    no mutable global state; calls are thread-safe and re-entrant.
+ *  - Layouts are dense row-major:
+ *        q, k, z : [B, T, H, dk]        v, o : [B, T, H, dv]
+ *        beta    : [B, T, H]            A    : [H]  (fp32)
+ *        S0, S_T : [B, H, dk, dv]  (fp32; key rows, value columns)
+ *    Decode drops the T axis.  q, k, v, z, beta and o use `dtype`; A and every
+ *    state tensor are fp32.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    returns without waiting.  All argument checks run before anything is
+ *    enqueued: on any error status nothing is launched and no output is
+ *    written.  A failed launch returns KDA_ERR_HIP.
+ *  - Pointers must be 16-byte aligned.  Sizes are int64.
+ *  - Supported: dtype in {KDA_F32, KDA_BF16}; dk == dv in {16, 128}; prefill
+ *    chunk in {16, 64}.  Anything else returns KDA_ERR_UNSUPPORTED.
+ *  - Numerics: fp32 accumulation and an fp32 state.  bf16 outputs are rounded
+ *    to nearest even.  NaN/Inf inputs are not checked and propagate.  Results
+ *    are bitwise reproducible run to run (no atomics in the arithmetic).
+ *  - Preconditions (not checked): q and k are L2-normalised over dk (the
+ *    caller's Q/K normalisation; the chunkwise rescaling relies on |k_d| <= 1
+ *    for its bf16 range), beta is used as given.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    KDA_ERR_SHAPE = 2,       /* a size is negative, or B*H overflows           */
+    KDA_ERR_UNSUPPORTED = 3, /* dtype / head size / chunk outside the set      */
+    KDA_ERR_MISALIGNED = 4,  /* a pointer is not 16-byte aligned               */
+    KDA_ERR_ALIAS = 5,       /* outputs overlap inputs (other than S_T == S0)  */
+    KDA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required     */
+    KDA_ERR_HIP = 7          /* the HIP runtime reported an error              */
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype;
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *kda_status_str(int status);
+
+/* Bytes of device workspace kda_prefill needs for these sizes (0 means none:
+ * NULL may then be passed).  Returns 0 for unsupported arguments too. */
+size_t kda_prefill_workspace_size(int dtype, int64_t B, int64_t T, int64_t H,
+                                  int64_t dk, int64_t dv, int32_t chunk);
+
+/*
+ * Chunkwise prefill over T tokens (the "KDA prefill" half of the runtime
+ * split in the section quoted above).  Tokens are grouped into chunks of
+ * `chunk`; within a chunk all interactions run as dense tiles, between chunks
+ * the state is carried.  A last partial chunk is allowed (any T >= 0).
+ *
+ *   in : q, k, z [B,T,H,dk], v [B,T,H,dv], beta [B,T,H] (dtype); A [H] fp32;
+ *        S0 [B,H,dk,dv] fp32, or NULL for a zero initial state.
+ *   out: o [B,T,H,dv] (dtype) -- o_t = S_t^T q_t, the raw read, no scale;
+ *        S_T [B,H,dk,dv] fp32 -- the state after token T-1 (S0 when T = 0).
+ *        S_T may be the same pointer as S0 (in-place state carry); any other
+ *        overlap between an output and an input is KDA_ERR_ALIAS.
+ *   workspace: device memory of at least kda_prefill_workspace_size(...)
+ *        bytes (may be NULL when that size is 0).
+ * The result depends on `chunk` only through floating-point rounding.
+ */
+kda_status kda_prefill(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                       int64_t dv, int32_t chunk,
+                       const void *q, const void *k, const void *v, const void *z,
+                       const void *beta, const float *A, const float *S0,
+                       void *o, float *S_T,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Same as kda_prefill, with the number of value columns each workgroup owns
+ * fixed by the caller (`dv_per_block` in {16, 32, 64, 128}, dividing dv; 0
+ * picks automatically).  Value columns of the state evolve independently, so
+ * every choice gives the same result up to rounding order; it only changes
+ * how the work is spread over the GPU.
+ */
+kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                          int64_t dv, int32_t chunk,
+                          const void *q, const void *k, const void *v, const void *z,
+                          const void *beta, const float *A, const float *S0,
+                          void *o, float *S_T,
+                          void *workspace, size_t workspace_bytes, void *stream,
+                          int32_t dv_per_block);
+
+/*
+ * One fused recurrent decode step for B sequences (the "KDA decode" half of
+ * the runtime split: one recurrent-state update per layer and token, with the
+ * state kept persistent).
+ *
+ *   in : q, k, z [B,H,dk], v [B,H,dv], beta [B,H] (dtype); A [H] fp32.
+ *   in/out: S [B,H,dk,dv] fp32 -- read once and overwritten with S_t.
+ *   out: o [B,H,dv] (dtype), o = S_t^T q.  o must not overlap any input or S.
+ * Each state entry is read once and written once per call.
+ */
+kda_status kda_decode_step(int dtype, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                           const void *q, const void *k, const void *v, const void *z,
+                           const void *beta, const float *A,
+                           float *S, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

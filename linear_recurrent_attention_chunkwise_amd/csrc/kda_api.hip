@@ -1,0 +1,163 @@
+// kda_api.hip -- the extern "C" entry points of libkda.so (see include/kda.h).
+//
+// Every check runs before anything is enqueued; on an error status no kernel
+// is launched and no output is touched.  No device memory is allocated here
+// and no global state is kept.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kda_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 62;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// a * b without int64 overflow; returns false when the product exceeds lim.
+bool mul_ok(int64_t a, int64_t b, int64_t lim, int64_t *out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > lim / a) return false;
+    *out = a * b;
+    return true;
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void *p, int64_t bytes) {
+    const uintptr_t lo = (uintptr_t)p;
+    return Range{lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlaps(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_status_str(int status) {
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: a size is negative or too large";
+        case KDA_ERR_UNSUPPORTED:
+            return "KDA_ERR_UNSUPPORTED: dtype / head size / chunk / split not supported";
+        case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: a pointer is not 16-byte aligned";
+        case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
+        default: return "unknown kda_status";
+    }
+}
+
+size_t kda_prefill_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                                  int64_t dv, int32_t chunk) {
+    (void)dtype; (void)B; (void)T; (void)H; (void)dk; (void)dv; (void)chunk;
+    return 0;
+}
+
+kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                          int32_t chunk, const void *q, const void *k, const void *v,
+                          const void *z, const void *beta, const float *A, const float *S0,
+                          void *o, float *S_T, void *workspace, size_t workspace_bytes,
+                          void *stream, int32_t dv_per_block) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (dk != dv || (dk != 16 && dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if (chunk != 16 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+    const int64_t D = dk;
+    const int64_t esz = dtype == KDA_BF16 ? 2 : 4;
+    int64_t bt, bth, nin, nstate, bh;
+    if (!mul_ok(B, T, kMaxElems, &bt) || !mul_ok(bt, H, kMaxElems, &bth) ||
+        !mul_ok(bth, D, kMaxElems / 4, &nin) || !mul_ok(B, H, kMaxElems, &bh) ||
+        !mul_ok(bh, D * D, kMaxElems / 4, &nstate))
+        return KDA_ERR_SHAPE;
+    if (bh > 0x7fffffff / 8) return KDA_ERR_SHAPE;  // grid size
+    int dvb = dv_per_block;
+    if (dvb == 0) dvb = kda::prefill_default_dv_per_block(dtype, B, H, D, chunk);
+    if (dvb <= 0 || D % dvb != 0 || !kda::prefill_supported(dtype, D, chunk, dvb))
+        return KDA_ERR_UNSUPPORTED;
+    if (!A || !S_T) return KDA_ERR_NULL;
+    if (bth > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, z, beta, A, S0, o, S_T};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const Range rq = range_of(q, nin * esz), rk = range_of(k, nin * esz),
+                rv = range_of(v, nin * esz), rz = range_of(z, nin * esz),
+                rb = range_of(beta, bth * esz), rA = range_of(A, H * 4),
+                rS0 = range_of(S0, nstate * 4), ro = range_of(o, nin * esz),
+                rST = range_of(S_T, nstate * 4);
+    const Range ins[] = {rq, rk, rv, rz, rb, rA};
+    for (const Range &r : ins)
+        if (overlaps(ro, r) || overlaps(rST, r)) return KDA_ERR_ALIAS;
+    if (overlaps(ro, rS0) || overlaps(ro, rST)) return KDA_ERR_ALIAS;
+    if (overlaps(rST, rS0) && (const void *)S_T != (const void *)S0) return KDA_ERR_ALIAS;
+    if (bh == 0) return KDA_OK;
+
+    kda::PrefillArgs a;
+    a.dtype = dtype; a.B = B; a.T = T; a.H = H; a.D = D; a.chunk = chunk;
+    a.dv_per_block = dvb;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.A = A; a.S0 = S0;
+    a.o = o; a.S_T = S_T;
+    a.stream = (hipStream_t)stream;
+    return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_prefill(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                       int32_t chunk, const void *q, const void *k, const void *v,
+                       const void *z, const void *beta, const float *A, const float *S0,
+                       void *o, float *S_T, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    return kda_prefill_ex(dtype, B, T, H, dk, dv, chunk, q, k, v, z, beta, A, S0, o, S_T,
+                          workspace, workspace_bytes, stream, 0);
+}
+
+kda_status kda_decode_step(int dtype, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                           const void *q, const void *k, const void *v, const void *z,
+                           const void *beta, const float *A, float *S, void *o,
+                           void *stream) {
+    if (B < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (dk != dv || !kda::decode_supported(dtype, dk)) return KDA_ERR_UNSUPPORTED;
+    const int64_t D = dk;
+    const int64_t esz = dtype == KDA_BF16 ? 2 : 4;
+    int64_t bh, nin, nstate;
+    if (!mul_ok(B, H, kMaxElems, &bh) || !mul_ok(bh, D, kMaxElems / 4, &nin) ||
+        !mul_ok(bh, D * D, kMaxElems / 4, &nstate))
+        return KDA_ERR_SHAPE;
+    if (bh > 0x7fffffff) return KDA_ERR_SHAPE;
+    if (!A) return KDA_ERR_NULL;
+    if (bh > 0 && (!q || !k || !v || !z || !beta || !S || !o)) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, z, beta, A, S, o};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const Range rq = range_of(q, nin * esz), rk = range_of(k, nin * esz),
+                rv = range_of(v, nin * esz), rz = range_of(z, nin * esz),
+                rb = range_of(beta, bh * esz), rA = range_of(A, H * 4),
+                rS = range_of(S, nstate * 4), ro = range_of(o, nin * esz);
+    const Range others[] = {rq, rk, rv, rz, rb, rA, rS};
+    for (const Range &r : others)
+        if (overlaps(ro, r)) return KDA_ERR_ALIAS;
+    const Range ins[] = {rq, rk, rv, rz, rb, rA};
+    for (const Range &r : ins)
+        if (overlaps(rS, r)) return KDA_ERR_ALIAS;
+    if (bh == 0) return KDA_OK;
+
+    kda::DecodeArgs a;
+    a.dtype = dtype; a.B = B; a.H = H; a.D = D;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.A = A; a.S = S; a.o = o;
+    a.stream = (hipStream_t)stream;
+    return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// kda_decode.hip -- fused one-token KDA decode step (gfx950).
+//
+// The step is the KDA recurrence of "Kimi K3 Open Weights: What Is Actually
+// New", section 1, for a single token, with the state kept in HBM between
+// calls ("one recurrent-state update per layer and token ... recurrent state
+// kept persistent").  Writing a = alpha*k, b = alpha*q:
+//
+//     w = S^T a,  y = S^T b           (one pass over S, reductions over dk)
+//     u = beta (v - w)
+//     o = y + (q . k) u               (= S_t^T q)
+//     S <- Diag(alpha) S + k u^T      (= (I - beta k k^T) Diag(alpha) S + beta k v^T)
+//
+// Memory-bound: every state entry is read once and written once.  One
+// workgroup owns one (b, h); the dk x dv fp32 state is held in registers
+// between the read and the write-back, as float4 column quads, so each wave
+// load/store instruction touches whole contiguous state rows.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <typename TI, int D, int NT>
+__global__ __launch_bounds__(NT) void kda_decode_kernel(
+    const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v,
+    const TI *__restrict__ z, const TI *__restrict__ beta, const float *__restrict__ A,
+    float *__restrict__ S, TI *__restrict__ o, int64_t H) {
+    constexpr int NCG = D / 4;          // float4 column quads per state row
+    constexpr int RG = NT / NCG;        // row groups
+    constexpr int RPT = D / RG;         // state rows per thread
+    constexpr int NWAVE = NT / 64;
+    static_assert(RG * RPT == D && NCG <= 64 && NT % 64 == 0, "bad decode tiling");
+
+    __shared__ float s_alpha[D], s_k[D], s_ak[D], s_aq[D];
+    __shared__ float s_red[NWAVE][2][D];
+    __shared__ float s_qk[NWAVE];
+
+    const int64_t bh = blockIdx.x;
+    const int h = (int)(bh % H);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cg = tid % NCG, rg = tid / NCG;
+    float *Sp = S + bh * (int64_t)(D * D);
+
+    // Issue the whole state read first; it streams while the gate is computed.
+    f32x4 s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        s[m] = *reinterpret_cast<const f32x4 *>(Sp + (rg + RG * m) * D + 4 * cg);
+
+    float qk = 0.0f;
+    if (tid < D) {
+        const int64_t off = bh * D + tid;
+        const float zi = to_f32(z[off]), ki = to_f32(k[off]), qi = to_f32(q[off]);
+        const float c2 = -__builtin_amdgcn_exp2f(A[h] * kLog2e) * kLog2e;
+        const float al = kda_alpha(c2, zi);
+        s_alpha[tid] = al;
+        s_k[tid] = ki;
+        s_ak[tid] = al * ki;
+        s_aq[tid] = al * qi;
+        qk = qi * ki;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) qk += __shfl_xor(qk, off);
+    if (lane == 0) s_qk[wave] = qk;
+    __syncthreads();
+
+    f32x4 w = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RG * m;
+        w += s[m] * s_ak[i];
+        y += s[m] * s_aq[i];
+    }
+    // Lanes holding the same column quad differ by multiples of NCG.
+#pragma unroll
+    for (int off = NCG; off < 64; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            w[e] += __shfl_xor(w[e], off);
+            y[e] += __shfl_xor(y[e], off);
+        }
+    }
+    if (lane < NCG) {
+        *reinterpret_cast<f32x4 *>(&s_red[wave][0][4 * cg]) = w;
+        *reinterpret_cast<f32x4 *>(&s_red[wave][1][4 * cg]) = y;
+    }
+    __syncthreads();
+
+    f32x4 wt = {0.f, 0.f, 0.f, 0.f}, yt = {0.f, 0.f, 0.f, 0.f};
+    float qkt = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < NWAVE; ++wv) {
+        wt += *reinterpret_cast<const f32x4 *>(&s_red[wv][0][4 * cg]);
+        yt += *reinterpret_cast<const f32x4 *>(&s_red[wv][1][4 * cg]);
+        qkt += s_qk[wv];
+    }
+    const float bt = to_f32(beta[bh]);
+    f32x4 vv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vv[e] = to_f32(v[bh * D + 4 * cg + e]);
+    const f32x4 u = bt * (vv - wt);
+    if (rg == 0) {
+        const f32x4 ov = yt + qkt * u;
+        TI *op = o + bh * D + 4 * cg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) op[e] = from_f32<TI>(ov[e]);
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RG * m;
+        const f32x4 ns = s_alpha[i] * s[m] + s_k[i] * u;
+        *reinterpret_cast<f32x4 *>(Sp + i * D + 4 * cg) = ns;
+    }
+}
+
+bool decode_supported(int dtype, int64_t D) {
+    return (dtype == 0 || dtype == 1) && (D == 16 || D == 128);
+}
+
+template <typename TI, int D, int NT>
+static hipError_t launch_decode_t(const DecodeArgs &a) {
+    const int64_t nblk = a.B * a.H;
+    hipLaunchKernelGGL((kda_decode_kernel<TI, D, NT>), dim3((unsigned)nblk), dim3(NT), 0,
+                       a.stream, (const TI *)a.q, (const TI *)a.k, (const TI *)a.v,
+                       (const TI *)a.z, (const TI *)a.beta, a.A, a.S, (TI *)a.o, a.H);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a) {
+    if (a.dtype == 1) {
+        if (a.D == 128) return launch_decode_t<bf16, 128, 256>(a);
+        return launch_decode_t<bf16, 16, 64>(a);
+    }
+    if (a.D == 128) return launch_decode_t<float, 128, 256>(a);
+    return launch_decode_t<float, 16, 64>(a);
+}
+
+}  // namespace kda

@@ -1,0 +1,45 @@
+// kda_launch.h -- host-side launchers behind the C ABI (internal).
+//
+// The C entry points (kda_api.hip) validate every argument and then call one
+// of these; they only pick a kernel instantiation, size the grid and enqueue
+// it.  They return the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace kda {
+
+struct PrefillArgs {
+    int dtype;          // KDA_F32 / KDA_BF16
+    int64_t B, T, H, D; // dk == dv == D
+    int chunk;
+    int dv_per_block;   // value columns per workgroup (16 * waves)
+    const void *q, *k, *v, *z, *beta;
+    const float *A, *S0;
+    void *o;
+    float *S_T;
+    hipStream_t stream;
+};
+
+struct DecodeArgs {
+    int dtype;
+    int64_t B, H, D;
+    const void *q, *k, *v, *z, *beta;
+    const float *A;
+    float *S;
+    void *o;
+    hipStream_t stream;
+};
+
+// Whether an instantiation exists for (dtype, D, chunk, dv_per_block).
+bool prefill_supported(int dtype, int64_t D, int chunk, int dv_per_block);
+// Default value columns per workgroup for these sizes.
+int prefill_default_dv_per_block(int dtype, int64_t B, int64_t H, int64_t D, int chunk);
+hipError_t launch_prefill(const PrefillArgs &a);
+
+bool decode_supported(int dtype, int64_t D);
+hipError_t launch_decode(const DecodeArgs &a);
+
+}  // namespace kda

@@ -1,0 +1,633 @@
+// kda_prefill.hip -- chunkwise KDA prefill (gfx950).
+//
+// Method: the KDA recurrence and bounded decay gate of "Kimi K3 Open Weights:
+// What Is Actually New", section 1, processed "recurrent between, parallel
+// within" chunks (kimi-k3-course capstone, one-page map, SEQUENCE block).
+// The in-chunk algebra is the WY / UT form of the delta rule, derived from the
+// recurrence.  For a chunk of C tokens with entering state S, per key channel
+// cumulative log-decay G_r = sum_{s<=r} g_s (r = 0..C-1, chunk-relative):
+//
+//   L[r,s] = beta_r sum_d k_r[d] k_s[d] e^{G_r[d]-G_s[d]}      (s <  r)
+//   P[r,s] =        sum_d q_r[d] k_s[d] e^{G_r[d]-G_s[d]}      (s <= r)
+//   W  = (I+L)^-1 diag(beta) (K * e^G),   U~ = (I+L)^-1 diag(beta) V
+//   U  = U~ - W S
+//   O  = (Q * e^G) S + P U
+//   S <- e^{G_C} * S + (K * e^{G_C - G})^T U
+//
+// Range (the reason for the K3 gate bound): g >= -5, so the decay over any
+// 16 tokens is >= e^-80 and its reciprocal <= e^80 < bf16 max.  The chunk is
+// therefore cut into 16-token sub-tiles p; every pairwise decay factor is
+// split at the END of a sub-tile into a factor >= 1 on the row side (at most
+// e^75) and a factor <= 1 on the column side, so all MFMA operands stay
+// finite and normal-range, and both diagonal and off-diagonal sub-tile blocks
+// are plain dense products:
+//   row side    Qd_r = q_r e^{G_r - E_p}      (E_p = G at the end of r's sub-tile p)
+//   column side Kt_s = k_s e^{E_p' - G_s}     (s in sub-tile p')
+//   block (p,p') = Qd_p (Kt_p' * F_{p,p'})^T,  F_{p,p'} = e^{E_p - E_p'} <= 1.
+// (I+L)^-1 is never formed beyond its 16 x 16 diagonal blocks: W and U~ are
+// obtained by block forward substitution, W_p = T_pp (B_p - sum_{j<p} L_pj W_j).
+//
+// Work split (one workgroup per (b, h, slice of value columns)):
+//   * value columns of the state evolve independently, so a workgroup owns
+//     DVB = 16 * NW of them; each wave owns 16 columns and the full dk x 16
+//     fp32 state slice in registers, and runs the S-dependent chain (U, O,
+//     state update) with no cross-wave traffic;
+//   * the S-independent per-chunk work (gate, decay factors, P, L, the
+//     triangular solve, W) is done cooperatively by the waves into LDS;
+//   * the next chunk's q, k, z, beta, v are prefetched into registers while
+//     the current chunk is processed.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+struct PrefillParams {
+    const void *q, *k, *v, *z, *beta;
+    const float *A, *S0;
+    void *o;
+    float *S_T;
+    int64_t T, H;
+    int nsplit;
+};
+
+template <typename T, int D, int C, int NW>
+struct PrefillCfg {
+    static constexpr int NT = 64 * NW;
+    static constexpr int DVB = 16 * NW;
+    static constexpr int NP = C / 16;
+    static constexpr int NDT = D / 16;
+    static constexpr int PADE = sizeof(T) == 2 ? 8 : 4;
+    static constexpr int DP = D + PADE;      // row stride of [token][d] tiles
+    static constexpr int CP = C + PADE;      // row stride of [d][token] / [token][token] tiles
+    static constexpr int LP = C + 4;         // row stride of the fp32 L tile
+    static constexpr int OP = DVB + PADE;    // row stride of the output staging tile
+    static constexpr int NPAIR = D / 2;
+    static constexpr int NSEG_RAW = NT / (NPAIR * NP);
+    static constexpr int NSEG = NSEG_RAW < 1 ? 1 : (NSEG_RAW > 16 ? 16 : NSEG_RAW);
+    static constexpr int SEGLEN = 16 / NSEG;
+    static constexpr int NITEM = NPAIR * NP * NSEG;
+    static constexpr int IPT = NITEM / NT;   // gate items per thread
+    static constexpr int NOFF = NP * (NP - 1) / 2;
+    static constexpr int NB = NP * (NP + 1) / 2;  // lower sub-tile blocks
+    static constexpr int BPW = (NB + NW - 1) / NW;
+    static constexpr int VQ = C * DVB / (4 * NT);  // v quads per thread
+    static_assert(NITEM % NT == 0 && IPT >= 1, "gate items must tile the workgroup");
+    static_assert(16 % NSEG == 0, "segments must tile a sub-tile");
+    static_assert(VQ >= 1 && (C * DVB) % (4 * NT) == 0, "v quads must tile the workgroup");
+
+    // LDS map (bytes).  Small fp32 tables first, then region X, which holds
+    // Qd, Kd, Kt while P and L are formed, then P, T, L plus one slot shared
+    // by W^T (block forward substitution only) and the output staging tile
+    // (after the chain only); then the chain operands.
+    static constexpr int SZ_TOKD = C * DP * (int)sizeof(T);
+    static constexpr int SZ_DTOK = D * CP * (int)sizeof(T);
+    static constexpr int SZ_P = C * CP * (int)sizeof(T);
+    static constexpr int SZ_L = C * LP * 4;
+    static constexpr int SZ_O = C * OP * (int)sizeof(T);
+    static constexpr int SZ_WT = NP > 1 ? SZ_DTOK : 0;
+    static constexpr int SZ_SLOT = SZ_WT > SZ_O ? SZ_WT : SZ_O;
+    static constexpr int OFF_GC = 0;
+    static constexpr int OFF_F = OFF_GC + D * 4;
+    static constexpr int OFF_E = OFF_F + (NOFF > 0 ? NOFF : 1) * D * 4;
+    static constexpr int OFF_BETA = OFF_E + NP * NSEG * D * 4;
+    static constexpr int OFF_X = (OFF_BETA + C * 4 + 15) / 16 * 16;
+    static constexpr int SZ_X1 = 3 * SZ_TOKD;
+    static constexpr int SZ_X2 = 2 * SZ_P + SZ_L + SZ_SLOT;
+    static constexpr int SZ_X = SZ_X1 > SZ_X2 ? SZ_X1 : SZ_X2;
+    static constexpr int OFF_QD = OFF_X;
+    static constexpr int OFF_KD = OFF_QD + SZ_TOKD;
+    static constexpr int OFF_KT = OFF_KD + SZ_TOKD;
+    static constexpr int OFF_P = OFF_X;
+    static constexpr int OFF_T = OFF_P + SZ_P;
+    static constexpr int OFF_L = OFF_T + SZ_P;
+    static constexpr int OFF_WT = OFF_L + SZ_L;
+    static constexpr int OFF_O = OFF_WT;
+    static constexpr int OFF_QG = OFF_X + SZ_X;
+    static constexpr int OFF_KGBT = OFF_QG + SZ_TOKD;
+    static constexpr int OFF_KHT = OFF_KGBT + SZ_DTOK;
+    static constexpr int OFF_VBT = OFF_KHT + SZ_DTOK;
+    static constexpr int OFF_WN = OFF_VBT + DVB * CP * (int)sizeof(T);
+    static constexpr int LDS_BYTES = OFF_WN + SZ_TOKD;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget exceeded");
+    static_assert(OFF_WT + SZ_SLOT <= OFF_X + SZ_X, "region X overflow");
+};
+
+// Index of the off-diagonal sub-tile block (p, p'), p' < p, in the F table.
+__host__ __device__ constexpr int off_index(int p, int pq) { return p * (p - 1) / 2 + pq; }
+
+template <typename T> struct PairOf;
+template <> struct PairOf<bf16> { typedef uint32_t type; };
+template <> struct PairOf<float> { typedef uint2 type; };
+
+__device__ __forceinline__ void unpack2(uint32_t u, float &a, float &b) {
+    a = __uint_as_float(u << 16);
+    b = __uint_as_float(u & 0xffff0000u);
+}
+__device__ __forceinline__ void unpack2(uint2 u, float &a, float &b) {
+    a = __uint_as_float(u.x);
+    b = __uint_as_float(u.y);
+}
+__device__ __forceinline__ void store_pair(bf16 *p, float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<bf16x2 *>(p) = bf16x2{(bf16)a, (bf16)b};
+}
+__device__ __forceinline__ void store_pair(float *p, float a, float b) {
+    *reinterpret_cast<float2 *>(p) = make_float2(a, b);
+}
+
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from_f32(const f32x4 &x) {
+    return acc_frag<T>(x);
+}
+
+// acc += A[16 x K] * B[K x 16], A rows from a K-contiguous LDS tile, B given
+// as K16 fragments.
+template <typename T, int K>
+__device__ __forceinline__ void contract_lds_frag(f32x4 &acc, const T *A, int lda,
+                                                  const Frag<T> *Bf, int lane) {
+    if constexpr (K >= 32) {
+#pragma unroll
+        for (int kk = 0; kk + 32 <= K; kk += 32)
+            mma32(acc, lds_frag(A, lda, kk, lane), lds_frag(A, lda, kk + 16, lane),
+                  Bf[kk / 16], Bf[kk / 16 + 1]);
+        if constexpr (K % 32 != 0)
+            mma16(acc, lds_frag(A, lda, K - 16, lane), Bf[K / 16 - 1]);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < K; kk += 16) mma16(acc, lds_frag(A, lda, kk, lane), Bf[kk / 16]);
+    }
+}
+
+template <typename T, int D, int C, int NW>
+__global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm) {
+    using Cfg = PrefillCfg<T, D, C, NW>;
+    using Pair = typename PairOf<T>::type;
+    constexpr int NT = Cfg::NT, DVB = Cfg::DVB, NP = Cfg::NP, NDT = Cfg::NDT;
+    constexpr int DP = Cfg::DP, CP = Cfg::CP, LP = Cfg::LP, OP = Cfg::OP;
+    constexpr int NSEG = Cfg::NSEG, SEGLEN = Cfg::SEGLEN, IPT = Cfg::IPT, NPAIR = Cfg::NPAIR;
+    constexpr int VQ = Cfg::VQ;
+
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+    T *sQd = reinterpret_cast<T *>(smem + Cfg::OFF_QD);
+    T *sKd = reinterpret_cast<T *>(smem + Cfg::OFF_KD);
+    T *sKt = reinterpret_cast<T *>(smem + Cfg::OFF_KT);
+    T *sP = reinterpret_cast<T *>(smem + Cfg::OFF_P);
+    T *sT = reinterpret_cast<T *>(smem + Cfg::OFF_T);
+    float *sL = reinterpret_cast<float *>(smem + Cfg::OFF_L);
+    T *sO = reinterpret_cast<T *>(smem + Cfg::OFF_O);
+    T *sQG = reinterpret_cast<T *>(smem + Cfg::OFF_QG);
+    T *sKGbT = reinterpret_cast<T *>(smem + Cfg::OFF_KGBT);
+    T *sKhT = reinterpret_cast<T *>(smem + Cfg::OFF_KHT);
+    T *sWT = reinterpret_cast<T *>(smem + Cfg::OFF_WT);
+    T *sVbT = reinterpret_cast<T *>(smem + Cfg::OFF_VBT);
+    T *sWn = reinterpret_cast<T *>(smem + Cfg::OFF_WN);
+    float *sGC = reinterpret_cast<float *>(smem + Cfg::OFF_GC);
+    float *sF = reinterpret_cast<float *>(smem + Cfg::OFF_F);
+    float *sE = reinterpret_cast<float *>(smem + Cfg::OFF_E);
+    float *sBeta = reinterpret_cast<float *>(smem + Cfg::OFF_BETA);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, n = lane & 15;
+
+    // Workgroup -> (b, h, value-column slice).  Workgroups are dealt to the
+    // 8 XCDs round-robin; renumber so the slices of one head share an XCD
+    // (and its L2), which dedupes their reads of q, k, z.
+    int64_t x = blockIdx.x;
+    const int64_t nblk = gridDim.x;
+    if (nblk % 8 == 0) x = (x % 8) * (nblk / 8) + x / 8;
+    const int64_t bh = x / prm.nsplit;
+    const int split = (int)(x % prm.nsplit);
+    const int64_t H = prm.H, Tn = prm.T;
+    const int64_t b = bh / H;
+    const int h = (int)(bh % H);
+    const int j0 = split * DVB;         // first value column of the workgroup
+    const int jw = j0 + 16 * wave;      // first value column of this wave
+
+    const T *gq = static_cast<const T *>(prm.q);
+    const T *gk = static_cast<const T *>(prm.k);
+    const T *gz = static_cast<const T *>(prm.z);
+    const T *gv = static_cast<const T *>(prm.v);
+    const T *gbeta = static_cast<const T *>(prm.beta);
+    T *go = static_cast<T *>(prm.o);
+    const int64_t tok_stride = H * D;               // elements between tokens
+    const int64_t base = (b * Tn * H + h) * D;       // token 0 of (b, h)
+    const int64_t bbase = b * Tn * H + h;            // beta of token 0
+    const float c2 = -__builtin_amdgcn_exp2f(prm.A[h] * kLog2e) * kLog2e;
+
+    // ---- state slice: S[16 i + 4 g + e][jw + n] -------------------------
+    f32x4 S[NDT];
+    if (prm.S0) {
+        const float *s0 = prm.S0 + bh * (int64_t)(D * D);
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[i][e] = s0[(16 * i + 4 * g + e) * D + jw + n];
+    } else {
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // ---- prefetch registers --------------------------------------------
+    // gate item it = tid + NT*ii: channel pair cp, segment sg of sub-tile sp
+    Pair rq[IPT][SEGLEN], rk[IPT][SEGLEN], rz[IPT][SEGLEN];
+    T rb[IPT][SEGLEN];   // raw beta bits; converted where used
+    typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type Quad;
+    Quad rv[VQ];
+
+    // Loads are branch-free: tokens past the end read the last token (Tn >= 1
+    // whenever a chunk is loaded) and are masked where they are used, so the
+    // compiler keeps every prefetch in flight instead of waiting on each one.
+    auto load_chunk = [&](int64_t t0) {
+#pragma unroll
+        for (int ii = 0; ii < IPT; ++ii) {
+            const int it = tid + NT * ii;
+            const int cp = it % NPAIR, rest = it / NPAIR;
+            const int sg = rest % NSEG, sp = rest / NSEG;
+#pragma unroll
+            for (int s = 0; s < SEGLEN; ++s) {
+                const int r = 16 * sp + sg * SEGLEN + s;
+                const int64_t t = t0 + r < Tn ? t0 + r : Tn - 1;
+                const int64_t off = base + t * tok_stride + 2 * cp;
+                rq[ii][s] = *reinterpret_cast<const Pair *>(gq + off);
+                rk[ii][s] = *reinterpret_cast<const Pair *>(gk + off);
+                rz[ii][s] = *reinterpret_cast<const Pair *>(gz + off);
+                rb[ii][s] = gbeta[bbase + t * H];
+            }
+        }
+#pragma unroll
+        for (int vi = 0; vi < VQ; ++vi) {
+            const int Q = tid + NT * vi;
+            const int r = Q / (DVB / 4), cq = Q % (DVB / 4);
+            const int64_t t = t0 + r < Tn ? t0 + r : Tn - 1;
+            rv[vi] = *reinterpret_cast<const Quad *>(gv + base + t * tok_stride + j0 + 4 * cq);
+        }
+    };
+
+    const int64_t nchunks = (Tn + C - 1) / C;
+    if (nchunks > 0) load_chunk(0);
+
+    f32x4 Ut[NP];   // U~ rows of each sub-tile for this wave's columns
+
+    for (int64_t ch = 0; ch < nchunks; ++ch) {
+        const int64_t t0 = ch * C;
+
+        // ================= phase A: gate, decay factors, operands ==========
+        float fl0[IPT][SEGLEN], fl1[IPT][SEGLEN], al0[IPT][SEGLEN], al1[IPT][SEGLEN];
+#pragma unroll
+        for (int ii = 0; ii < IPT; ++ii) {
+            const int it = tid + NT * ii;
+            const int cp = it % NPAIR, rest = it / NPAIR;
+            const int sg = rest % NSEG, sp = rest / NSEG;
+            float run0 = 1.0f, run1 = 1.0f;
+#pragma unroll
+            for (int s = 0; s < SEGLEN; ++s) {
+                const int r = 16 * sp + sg * SEGLEN + s;
+                float z0, z1;
+                unpack2(rz[ii][s], z0, z1);
+                const bool valid = t0 + r < Tn;
+                const float a0 = valid ? kda_alpha(c2, z0) : 1.0f;
+                const float a1 = valid ? kda_alpha(c2, z1) : 1.0f;
+                run0 *= a0;
+                run1 *= a1;
+                fl0[ii][s] = run0;
+                fl1[ii][s] = run1;
+                al0[ii][s] = a0;
+                al1[ii][s] = a1;
+            }
+            sE[(sp * NSEG + sg) * D + 2 * cp] = run0;
+            sE[(sp * NSEG + sg) * D + 2 * cp + 1] = run1;
+            if (cp == 0) {
+#pragma unroll
+                for (int s = 0; s < SEGLEN; ++s) {
+                    const int r = 16 * sp + sg * SEGLEN + s;
+                    sBeta[r] = t0 + r < Tn ? to_f32(rb[ii][s]) : 0.0f;
+                }
+            }
+        }
+        lds_barrier();
+
+#pragma unroll
+        for (int ii = 0; ii < IPT; ++ii) {
+            const int it = tid + NT * ii;
+            const int cp = it % NPAIR, rest = it / NPAIR;
+            const int sg = rest % NSEG, sp = rest / NSEG;
+            const int d0 = 2 * cp;
+            // products of the segment decays: within this sub-tile before /
+            // after this segment, and whole sub-tiles before / after it
+            float bef0 = 1.f, bef1 = 1.f, aft0 = 1.f, aft1 = 1.f;
+            float pre0 = 1.f, pre1 = 1.f, post0 = 1.f, post1 = 1.f;
+            float tot[NP][2];
+#pragma unroll
+            for (int p2 = 0; p2 < NP; ++p2) {
+                float t0v = 1.f, t1v = 1.f;
+#pragma unroll
+                for (int s2 = 0; s2 < NSEG; ++s2) {
+                    const float e0 = sE[(p2 * NSEG + s2) * D + d0];
+                    const float e1 = sE[(p2 * NSEG + s2) * D + d0 + 1];
+                    t0v *= e0;
+                    t1v *= e1;
+                    if (p2 == sp && s2 < sg) { bef0 *= e0; bef1 *= e1; }
+                    if (p2 == sp && s2 > sg) { aft0 *= e0; aft1 *= e1; }
+                }
+                tot[p2][0] = t0v;
+                tot[p2][1] = t1v;
+                if (p2 < sp) { pre0 *= t0v; pre1 *= t1v; }
+                if (p2 > sp) { post0 *= t0v; post1 *= t1v; }
+            }
+            const float itot0 = __builtin_amdgcn_rcpf(tot[sp][0]);
+            const float itot1 = __builtin_amdgcn_rcpf(tot[sp][1]);
+            float rl0 = aft0, rl1 = aft1;   // decay over (r, end of sub-tile]
+#pragma unroll
+            for (int s = SEGLEN - 1; s >= 0; --s) {
+                const int r = 16 * sp + sg * SEGLEN + s;
+                float q0, q1, k0, k1;
+                unpack2(rq[ii][s], q0, q1);
+                unpack2(rk[ii][s], k0, k1);
+                const bool valid = t0 + r < Tn;   // padded tokens: q = k = beta = 0
+                q0 = valid ? q0 : 0.0f;
+                q1 = valid ? q1 : 0.0f;
+                k0 = valid ? k0 : 0.0f;
+                k1 = valid ? k1 : 0.0f;
+                const float F0 = bef0 * fl0[ii][s], F1 = bef1 * fl1[ii][s];  // e^{G_r - start}
+                const float bt = valid ? to_f32(rb[ii][s]) : 0.0f;
+                store_pair(sQd + r * DP + d0, q0 * F0 * itot0, q1 * F1 * itot1);
+                store_pair(sKd + r * DP + d0, k0 * F0 * itot0, k1 * F1 * itot1);
+                store_pair(sKt + r * DP + d0, k0 * rl0, k1 * rl1);
+                store_pair(sQG + r * DP + d0, q0 * F0 * pre0, q1 * F1 * pre1);
+                sKGbT[d0 * CP + r] = from_f32<T>(bt * k0 * F0 * pre0);
+                sKGbT[(d0 + 1) * CP + r] = from_f32<T>(bt * k1 * F1 * pre1);
+                sKhT[d0 * CP + r] = from_f32<T>(k0 * rl0 * post0);
+                sKhT[(d0 + 1) * CP + r] = from_f32<T>(k1 * rl1 * post1);
+                rl0 *= al0[ii][s];
+                rl1 *= al1[ii][s];
+            }
+            if (sp == 0 && sg == 0) {
+                float gc0 = 1.f, gc1 = 1.f;
+#pragma unroll
+                for (int p2 = 0; p2 < NP; ++p2) { gc0 *= tot[p2][0]; gc1 *= tot[p2][1]; }
+                sGC[d0] = gc0;
+                sGC[d0 + 1] = gc1;
+#pragma unroll
+                for (int p2 = 1; p2 < NP; ++p2) {
+#pragma unroll
+                    for (int pq = 0; pq < p2; ++pq) {
+                        float f0 = 1.f, f1 = 1.f;
+#pragma unroll
+                        for (int x2 = pq + 1; x2 <= p2; ++x2) { f0 *= tot[x2][0]; f1 *= tot[x2][1]; }
+                        sF[off_index(p2, pq) * D + d0] = f0;
+                        sF[off_index(p2, pq) * D + d0 + 1] = f1;
+                    }
+                }
+            }
+        }
+        // beta * v, transposed to [column][token]
+#pragma unroll
+        for (int vi = 0; vi < VQ; ++vi) {
+            const int Q = tid + NT * vi;
+            const int r = Q / (DVB / 4), cq = Q % (DVB / 4);
+            const float bt = sBeta[r];
+            float vv[4];
+            if constexpr (sizeof(T) == 2) {
+                unpack2(rv[vi].x, vv[0], vv[1]);
+                unpack2(rv[vi].y, vv[2], vv[3]);
+            } else {
+                vv[0] = __uint_as_float(rv[vi].x);
+                vv[1] = __uint_as_float(rv[vi].y);
+                vv[2] = __uint_as_float(rv[vi].z);
+                vv[3] = __uint_as_float(rv[vi].w);
+            }
+            const bool valid = t0 + r < Tn;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sVbT[(4 * cq + e) * CP + r] = from_f32<T>(valid ? bt * vv[e] : 0.0f);
+        }
+        lds_barrier();
+
+        // prefetch the next chunk while this one is processed
+        if (ch + 1 < nchunks) load_chunk(t0 + C);
+
+        // ================= phase B: P and L sub-tile blocks ================
+        f32x4 accP[Cfg::BPW], accL[Cfg::BPW];
+#pragma unroll
+        for (int bi = 0; bi < Cfg::BPW; ++bi) {
+            const int blk = wave + NW * bi;
+            accP[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accL[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (blk < Cfg::NB) {
+                // blk -> (p, pq), pq <= p, row-major over the lower triangle
+                int p = 0;
+                while ((p + 1) * (p + 2) / 2 <= blk) ++p;
+                const int pq = blk - p * (p + 1) / 2;
+                const T *Aq = sQd + 16 * p * DP;
+                const T *Ak = sKd + 16 * p * DP;
+                const T *Bk = sKt + 16 * pq * DP;
+                const float *Fs = pq < p ? sF + off_index(p, pq) * D : nullptr;
+#pragma unroll
+                for (int kk = 0; kk < D; kk += 16) {
+                    Frag<T> bf = lds_frag(Bk, DP, kk, lane);
+                    if (Fs) bf = frag_scaled(bf, *reinterpret_cast<const f32x4 *>(Fs + kk + 4 * g));
+                    mma16(accP[bi], lds_frag(Aq, DP, kk, lane), bf);
+                    mma16(accL[bi], lds_frag(Ak, DP, kk, lane), bf);
+                }
+            }
+        }
+        lds_barrier();   // region X switches from Qd/Kd/Kt to P/T/L
+#pragma unroll
+        for (int bi = 0; bi < Cfg::BPW; ++bi) {
+            const int blk = wave + NW * bi;
+            if (blk < Cfg::NB) {
+                int p = 0;
+                while ((p + 1) * (p + 2) / 2 <= blk) ++p;
+                const int pq = blk - p * (p + 1) / 2;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * p + 4 * g + e, s = 16 * pq + n;
+                    const bool lower = pq < p || s <= r;
+                    const bool strict = pq < p || s < r;
+                    sP[r * CP + s] = from_f32<T>(lower ? accP[bi][e] : 0.0f);
+                    sL[r * LP + s] = strict ? sBeta[r] * accL[bi][e] : 0.0f;
+                }
+            }
+        }
+        lds_barrier();
+
+        // ================= phase C: 16 x 16 diagonal inverses ==============
+        // T_pp = (I + L_pp)^-1 by column-wise forward substitution in fp32:
+        // sub-tile p goes to wave p % NW, lane group p / NW, and lane c of
+        // that group owns column c; right-looking updates keep the dependent
+        // chain one FMA per row.
+        static_assert(NP <= 4 * NW, "diagonal blocks must fit the lane groups");
+        if (wave + NW * g < NP) {
+            const int p = wave + NW * g, c = n;
+            const float *Lb = sL + 16 * p * LP + 16 * p;
+            float t[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) t[r] = r == c ? 1.0f : 0.0f;
+#pragma unroll
+            for (int s = 0; s < 15; ++s) {
+#pragma unroll
+                for (int r = s + 1; r < 16; ++r) t[r] -= Lb[r * LP + s] * t[s];
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sT[(16 * p + r) * CP + 16 * p + c] = from_f32<T>(t[r]);
+        }
+        lds_barrier();
+
+        // ================= phase D: W and U~ by block forward substitution =
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const Frag<T> Tpp = lds_frag(sT + 16 * p * CP, CP, 16 * p, lane);
+            // W_p for the d-tiles of this wave
+            for (int dt = wave; dt < NDT; dt += NW) {
+                f32x4 R;
+                {
+                    const Frag<T> kb = lds_frag(sKGbT + 16 * dt * CP, CP, 16 * p, lane);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) R[e] = to_f32(kb.v[e]);
+                }
+                for (int j = 0; j < p; ++j) {
+                    const f32x4 lf = *reinterpret_cast<const f32x4 *>(
+                        sL + (16 * p + n) * LP + 16 * j + 4 * g);
+                    mma16(R, frag_from_f32<T>(-lf), lds_frag(sWT + 16 * dt * CP, CP, 16 * j, lane));
+                }
+                f32x4 Wt = {0.f, 0.f, 0.f, 0.f};
+                mma16(Wt, Tpp, acc_frag<T>(R));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * p + 4 * g + e, d = 16 * dt + n;
+                    sWn[r * DP + d] = from_f32<T>(-Wt[e]);
+                    if constexpr (NP > 1) sWT[d * CP + r] = from_f32<T>(Wt[e]);
+                }
+            }
+            // U~_p for this wave's 16 value columns
+            {
+                f32x4 R;
+                const Frag<T> vb = lds_frag(sVbT + 16 * wave * CP, CP, 16 * p, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) R[e] = to_f32(vb.v[e]);
+                for (int j = 0; j < p; ++j) {
+                    const f32x4 lf = *reinterpret_cast<const f32x4 *>(
+                        sL + (16 * p + n) * LP + 16 * j + 4 * g);
+                    mma16(R, frag_from_f32<T>(-lf), acc_frag<T>(Ut[j]));
+                }
+                Ut[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                mma16(Ut[p], Tpp, acc_frag<T>(R));
+            }
+            if constexpr (NP > 1) lds_barrier();
+        }
+        if constexpr (NP == 1) lds_barrier();
+
+        // ================= phase E: the state chain (per wave) =============
+        {
+            Frag<T> Sf[NDT];
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) Sf[i] = acc_frag<T>(S[i]);
+            f32x4 U[NP], O[NP];
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                U[p] = Ut[p];   // U = U~ - W S  (sWn holds -W)
+                contract_lds_frag<T, D>(U[p], sWn + 16 * p * DP, DP, Sf, lane);
+            }
+            Frag<T> Uf[NP];
+#pragma unroll
+            for (int p = 0; p < NP; ++p) Uf[p] = acc_frag<T>(U[p]);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                O[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                contract_lds_frag<T, D>(O[p], sQG + 16 * p * DP, DP, Sf, lane);
+#pragma unroll
+                for (int j = 0; j <= p; ++j)
+                    mma16(O[p], lds_frag(sP + 16 * p * CP, CP, 16 * j, lane), Uf[j]);
+            }
+            // S <- e^{G_C} * S + Kh^T U
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) {
+                const f32x4 gc = *reinterpret_cast<const f32x4 *>(sGC + 16 * i + 4 * g);
+                S[i] *= gc;
+#pragma unroll
+                for (int j = 0; j < NP; ++j)
+                    mma16(S[i], lds_frag(sKhT + 16 * i * CP, CP, 16 * j, lane), Uf[j]);
+            }
+            // stage O for coalesced stores
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sO[(16 * p + 4 * g + e) * OP + 16 * wave + n] = from_f32<T>(O[p][e]);
+        }
+        lds_barrier();
+        {
+            constexpr int E16 = 16 / (int)sizeof(T);
+            constexpr int CPR = DVB / E16;          // 16-byte pieces per row
+            const int64_t nvalid = Tn - t0 < C ? Tn - t0 : C;
+            for (int idx = tid; idx < C * CPR; idx += NT) {
+                const int r = idx / CPR, c = idx % CPR;
+                if (r < nvalid) {
+                    const uint4 val = *reinterpret_cast<const uint4 *>(sO + r * OP + c * E16);
+                    *reinterpret_cast<uint4 *>(go + base + (t0 + r) * tok_stride + j0 + c * E16) = val;
+                }
+            }
+        }
+        lds_barrier();
+    }
+
+    // ---- final state ------------------------------------------------------
+    float *sT_out = prm.S_T + bh * (int64_t)(D * D);
+#pragma unroll
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sT_out[(16 * i + 4 * g + e) * D + jw + n] = S[i][e];
+}
+
+// ---------------------------------------------------------------- host ----
+
+template <typename T, int D, int C, int NW>
+static hipError_t launch_prefill_t(const PrefillArgs &a) {
+    PrefillParams prm;
+    prm.q = a.q; prm.k = a.k; prm.v = a.v; prm.z = a.z; prm.beta = a.beta;
+    prm.A = a.A; prm.S0 = a.S0; prm.o = a.o; prm.S_T = a.S_T;
+    prm.T = a.T; prm.H = a.H;
+    prm.nsplit = (int)(D / (16 * NW));
+    const int64_t nblk = a.B * a.H * prm.nsplit;
+    hipLaunchKernelGGL((kda_prefill_kernel<T, D, C, NW>), dim3((unsigned)nblk), dim3(64 * NW), 0,
+                       a.stream, prm);
+    return hipGetLastError();
+}
+
+#define KDA_PREFILL_CASES(X)                                                             \
+    X(bf16, 128, 16, 1) X(bf16, 128, 16, 2) X(bf16, 128, 16, 4) X(bf16, 128, 16, 8)        \
+    X(bf16, 128, 64, 1) X(bf16, 128, 64, 2) X(bf16, 128, 64, 4)                            \
+    X(bf16, 16, 16, 1) X(bf16, 16, 64, 1)                                                  \
+    X(float, 128, 16, 1) X(float, 128, 16, 2) X(float, 128, 16, 4)                         \
+    X(float, 16, 16, 1) X(float, 16, 64, 1)
+
+template <typename T> constexpr int dtype_code();
+template <> constexpr int dtype_code<bf16>() { return 1; }
+template <> constexpr int dtype_code<float>() { return 0; }
+
+bool prefill_supported(int dtype, int64_t D, int chunk, int dv_per_block) {
+#define X(T_, D_, C_, NW_)                                                               \
+    if (dtype == dtype_code<T_>() && D == D_ && chunk == C_ && dv_per_block == 16 * NW_)  \
+        return true;
+    KDA_PREFILL_CASES(X)
+#undef X
+    return false;
+}
+
+int prefill_default_dv_per_block(int dtype, int64_t B, int64_t H, int64_t D, int chunk) {
+    (void)B; (void)H; (void)chunk; (void)dtype;
+    if (D == 16) return 16;
+    return 64;
+}
+
+hipError_t launch_prefill(const PrefillArgs &a) {
+#define X(T_, D_, C_, NW_)                                                               \
+    if (a.dtype == dtype_code<T_>() && a.D == D_ && a.chunk == C_ &&                       \
+        a.dv_per_block == 16 * NW_)                                                        \
+        return launch_prefill_t<T_, D_, C_, NW_>(a);
+    KDA_PREFILL_CASES(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -1,0 +1,175 @@
+"""ctypes binding over libkda.so (include/kda.h).
+
+Argument marshalling only: shapes, dtypes, devices and contiguity are checked
+here, output tensors are allocated with torch on the inputs' device, and the
+call goes to the library on torch's current stream.  Every arithmetic step
+runs in the library's HIP kernels.  If the library is missing, or no GPU is
+visible, these functions raise; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libkda.so"
+
+KDA_F32, KDA_BF16 = 0, 1
+_DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+
+class KDAError(RuntimeError):
+    """A libkda call returned a non-OK status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    lib.kda_abi_version.restype = ctypes.c_int
+    lib.kda_abi_version.argtypes = []
+    lib.kda_status_str.restype = ctypes.c_char_p
+    lib.kda_status_str.argtypes = [ctypes.c_int]
+    lib.kda_prefill_workspace_size.restype = sz
+    lib.kda_prefill_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i32]
+    pre = [ctypes.c_int, i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp,
+           vp, vp, vp, sz, vp]
+    lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill.argtypes = pre
+    lib.kda_prefill_ex.restype = ctypes.c_int
+    lib.kda_prefill_ex.argtypes = pre + [i32]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, vp, vp,
+                                    vp, vp, vp, vp]
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(_load().kda_abi_version())
+
+
+def status_str(status: int) -> str:
+    return _load().kda_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise KDAError(status, f"{what}: {status_str(status)}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def prefill_workspace_size(dtype: torch.dtype, B: int, T: int, H: int, dk: int, dv: int,
+                           chunk: int) -> int:
+    return int(_load().kda_prefill_workspace_size(_DTYPES[dtype], B, T, H, dk, dv, chunk))
+
+
+def prefill(q, k, v, z, beta, A, S0=None, chunk: int = 16, out=None, S_T=None,
+            dv_per_block: int = 0):
+    """Chunkwise KDA prefill on the GPU.
+
+    q, k, z [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H] (fp32 or bf16, all one
+    dtype); A [H] fp32; S0 [B,H,dk,dv] fp32 or None.  Returns (o, S_T) with
+    o [B,T,H,dv] in the input dtype and S_T [B,H,dk,dv] fp32.  ``out`` and
+    ``S_T`` may be given preallocated (``S_T`` may be ``S0`` itself)."""
+    lib = _load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("KDA prefill runs on the GPU; inputs must be cuda tensors")
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    _require(q, "q", (B, T, H, dk), dt, dev)
+    _require(k, "k", (B, T, H, dk), dt, dev)
+    _require(z, "z", (B, T, H, dk), dt, dev)
+    _require(v, "v", (B, T, H, dv), dt, dev)
+    _require(beta, "beta", (B, T, H), dt, dev)
+    _require(A, "A", (H,), torch.float32, dev)
+    if S0 is not None:
+        _require(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _require(out, "out", (B, T, H, dv), dt, dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _require(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
+    ws_bytes = int(lib.kda_prefill_workspace_size(_DTYPES[dt], B, T, H, dk, dv, int(chunk)))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = lib.kda_prefill_ex(_DTYPES[dt], B, T, H, dk, dv, int(chunk), _ptr(q), _ptr(k),
+                            _ptr(v), _ptr(z), _ptr(beta), _ptr(A), _ptr(S0), _ptr(out),
+                            _ptr(S_T), _ptr(ws), ws_bytes, _stream_handle(dev),
+                            int(dv_per_block))
+    _check(st, "kda_prefill")
+    return out, S_T
+
+
+def decode_step(q, k, v, z, beta, A, S, out=None):
+    """One fused KDA decode step on the GPU; S [B,H,dk,dv] fp32 is updated in
+    place.  q, k, z [B,H,dk]; v [B,H,dv]; beta [B,H]; A [H] fp32.  Returns o
+    [B,H,dv] in the input dtype."""
+    lib = _load()
+    if q.dim() != 3:
+        raise ValueError("q must be [B,H,dk]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("KDA decode runs on the GPU; inputs must be cuda tensors")
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    _require(q, "q", (B, H, dk), dt, dev)
+    _require(k, "k", (B, H, dk), dt, dev)
+    _require(z, "z", (B, H, dk), dt, dev)
+    _require(v, "v", (B, H, dv), dt, dev)
+    _require(beta, "beta", (B, H), dt, dev)
+    _require(A, "A", (H,), torch.float32, dev)
+    _require(S, "S", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _require(out, "out", (B, H, dv), dt, dev)
+    st = lib.kda_decode_step(_DTYPES[dt], B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(z),
+                             _ptr(beta), _ptr(A), _ptr(S), _ptr(out), _stream_handle(dev))
+    _check(st, "kda_decode_step")
+    return out

@@ -1,0 +1,281 @@
+"""GPU parity: libkda (through its C ABI) against the fp64 oracle.
+
+Tolerances (normwise per (b, h) slice, o and S_T separately): 1e-4 for fp32
+inputs, 2e-2 for bf16 inputs with fp32 accumulation.  Inputs come from the
+seeded workload recipes; the oracle sees the exact same (bf16-rounded) values.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrent_attention_chunkwise_amd.inputs import (WORKLOADS, make_decode_inputs,
+                                                             make_prefill_inputs)
+from tests.gpu_helpers import (TOL, gpu_prefill, host, oracle_prefill, slice_relerr,
+                               to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import linear_recurrent_attention_chunkwise_amd as m
+    assert m.abi_version() == 1
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _check_prefill(kda, dev, w, chunk=None, T=None, dvb=0, heads=None, oracle_T=None):
+    chunk = chunk or w.chunk
+    inp = make_prefill_inputs(w, T=T)
+    _say(f"[prefill] {w.name} dtype={w.dtype} B={w.B} H={w.H} T={inp['q'].shape[1]} "
+         f"chunk={chunk} dvb={dvb}")
+    g = to_dev(inp, dev)
+    o, S_T = gpu_prefill(kda, g, chunk, dv_per_block=dvb)
+    o_ref, S_ref = oracle_prefill(inp)
+    dt = inp["q"].dtype
+    eo = slice_relerr(host(o), o_ref, 2)
+    es = slice_relerr(host(S_T), S_ref, 1)
+    _say(f"   o err {eo:.3e}  S_T err {es:.3e}  tol {TOL[dt]}")
+    assert eo <= TOL[dt] and es <= TOL[dt]
+    return o, S_T
+
+
+# ------------------------------------------------------------- prefill ----
+
+def test_tiny_fp32_workload(kda, gpu_device):
+    _check_prefill(kda, gpu_device, WORKLOADS["tiny_prefill_f32"])
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_tiny_fp32_ragged(kda, gpu_device, chunk):
+    w = WORKLOADS["tiny_prefill_f32"].with_(H=3, B=2, s0_std=0.5)
+    for T in (1, 15, 17, 63, 65, 130):
+        _check_prefill(kda, gpu_device, w, chunk=chunk, T=T)
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+@pytest.mark.parametrize("dvb", [0, 16, 32, 64, 128])
+def test_bf16_d128_small(kda, gpu_device, chunk, dvb):
+    """Every workgroup width (value columns per workgroup) gives the oracle's
+    result; chunk 64 with 128 columns per workgroup exceeds LDS and is refused."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(H=3, B=2)
+    if chunk == 64 and dvb == 128:
+        g = to_dev(make_prefill_inputs(w, T=64), gpu_device)
+        with pytest.raises(kda.KDAError):
+            gpu_prefill(kda, g, chunk, dv_per_block=dvb)
+        return
+    _check_prefill(kda, gpu_device, w, chunk=chunk, T=333, dvb=dvb)
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_bf16_d128_ragged_tails(kda, gpu_device, chunk):
+    w = WORKLOADS["k3_prefill_bf16"].with_(H=2)
+    for T in (1, 15, 17, 63, 65, 129):
+        _check_prefill(kda, gpu_device, w, chunk=chunk, T=T)
+
+
+def test_fp32_d128(kda, gpu_device):
+    w = WORKLOADS["k3_prefill_bf16"].with_(dtype="f32", H=2)
+    for dvb in (0, 16, 32):
+        _check_prefill(kda, gpu_device, w, chunk=16, T=200, dvb=dvb)
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_bf16_d16(kda, gpu_device, chunk):
+    w = WORKLOADS["tiny_prefill_f32"].with_(dtype="bf16", H=4, B=2, s0_std=0.3)
+    _check_prefill(kda, gpu_device, w, chunk=chunk, T=150)
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_long_memory_variant(kda, gpu_device, chunk):
+    """z ~ N(-6, 1): alpha ~ 0.6..1, so the state carries across many chunks."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(H=4, z_mean=-6.0)
+    _check_prefill(kda, gpu_device, w, chunk=chunk, T=2048)
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_k3_prefill_full_size(kda, gpu_device, chunk):
+    """B1 H96 T4096 d128 bf16, S0 ~ N(0, 0.02^2): every head against the oracle."""
+    _check_prefill(kda, gpu_device, WORKLOADS["k3_prefill_bf16"], chunk=chunk)
+
+
+def test_long_prefill_sampled_heads(kda, gpu_device):
+    """B1 H96 T65536 C64, z ~ N(2,1) (decay near g_min): two heads, all tokens."""
+    w = WORKLOADS["long_prefill_bf16"]
+    _say(f"[prefill] {w.name} full size on GPU, oracle on heads 0 and 95")
+    inp = make_prefill_inputs(w, device=gpu_device)
+    o, S_T = gpu_prefill(kda, inp, w.chunk)
+    heads = [0, 95]
+    o_ref, S_ref = oracle_prefill(inp, heads=heads)
+    eo = slice_relerr(host(o[:, :, heads]), o_ref, 2)
+    es = slice_relerr(host(S_T[:, heads]), S_ref, 1)
+    _say(f"   o err {eo:.3e}  S_T err {es:.3e}")
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_million_token_prefill(kda, gpu_device):
+    """B1 H16 T2^20 C64 bf16.  Outputs are causal, so the first 8192 tokens of
+    two heads are checked against the oracle over that prefix; the final state
+    is checked by the split property (two halves chained through S)."""
+    w = WORKLOADS["million_prefill_bf16"]
+    _say(f"[prefill] {w.name} full size")
+    inp = make_prefill_inputs(w, device=gpu_device)
+    o, S_T = gpu_prefill(kda, inp, w.chunk)
+    heads, Tp = [3, 12], 8192
+    o_ref, _ = oracle_prefill(inp, heads=heads, T=Tp)
+    eo = slice_relerr(host(o[:, :Tp][:, :, heads]), o_ref, 2)
+    _say(f"   prefix o err {eo:.3e}")
+    assert eo <= 2e-2
+    half = w.T // 2
+    first = {k: (v[:, :half].clone() if v is not None and v.dim() >= 3 else v)
+             for k, v in inp.items()}
+    o1, S1 = gpu_prefill(kda, first, w.chunk)
+    second = {k: (v[:, half:].clone() if v is not None and v.dim() >= 3 else v)
+              for k, v in inp.items()}
+    second["S0"] = S1
+    o2, S2 = gpu_prefill(kda, second, w.chunk)
+    torch.testing.assert_close(S2, S_T, rtol=0, atol=0)
+    assert torch.equal(o1, o[:, :half]) and torch.equal(o2, o[:, half:])
+    assert torch.isfinite(S_T).all()
+
+
+# -------------------------------------------------------- properties ----
+
+def test_empty_sequence_copies_state(kda, gpu_device):
+    w = WORKLOADS["k3_prefill_bf16"].with_(H=3)
+    inp = to_dev(make_prefill_inputs(w, T=0), gpu_device)
+    o, S_T = gpu_prefill(kda, inp, 16)
+    assert o.shape[1] == 0 and torch.equal(S_T, inp["S0"])
+    inp["S0"] = None
+    _, S_T0 = gpu_prefill(kda, inp, 64)
+    assert torch.count_nonzero(S_T0) == 0
+
+
+def test_in_place_state_and_split(kda, gpu_device):
+    """S_T may alias S0; running [0,t) then [t,T) equals one run (up to the
+    chunk boundaries the split introduces)."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(H=4)
+    inp = to_dev(make_prefill_inputs(w, T=320), gpu_device)
+    o, S_T = gpu_prefill(kda, inp, 16)
+    for t in (160, 37):
+        S = inp["S0"].clone()
+        # clone: a token-offset view of beta is not 16-byte aligned
+        a = {k: (v[:, :t].clone() if v is not None and v.dim() >= 3 else v) for k, v in inp.items()}
+        bpart = {k: (v[:, t:].clone() if v is not None and v.dim() >= 3 else v) for k, v in inp.items()}
+        a["S0"] = S
+        kda.prefill(a["q"], a["k"], a["v"], a["z"], a["beta"], a["A"], S, chunk=16, S_T=S)
+        bpart["S0"] = S
+        o2, _ = kda.prefill(bpart["q"], bpart["k"], bpart["v"], bpart["z"], bpart["beta"],
+                            bpart["A"], S, chunk=16, S_T=S)
+        torch.cuda.synchronize()
+        if t % 16 == 0:
+            assert torch.equal(S, S_T) and torch.equal(o2, o[:, t:])
+        else:
+            assert slice_relerr(host(S), host(S_T), 1) < 2e-2
+
+
+def test_deterministic_and_chunk_invariant(kda, gpu_device):
+    w = WORKLOADS["k3_prefill_bf16"].with_(H=4)
+    inp = to_dev(make_prefill_inputs(w, T=500), gpu_device)
+    o1, S1 = gpu_prefill(kda, inp, 64)
+    o2, S2 = gpu_prefill(kda, inp, 64)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    o16, S16 = gpu_prefill(kda, inp, 16)
+    assert slice_relerr(host(o16), host(o1), 2) < 2e-2
+    assert slice_relerr(host(S16), host(S1), 1) < 2e-2
+
+
+def test_overwrite_on_gpu(kda, gpu_device):
+    """alpha = 1 (z = -1e4), beta = 1, the same unit key twice: o = v2."""
+    dev = gpu_device
+    B, T, H, D = 1, 2, 1, 128
+    key = torch.zeros(D); key[5] = 1.0
+    v = torch.randn(1, T, 1, D, generator=torch.Generator().manual_seed(3))
+    for dt in (torch.float32, torch.bfloat16):
+        q = key.expand(B, T, H, D).contiguous().to(dt)
+        z = torch.full((B, T, H, D), -1e4).to(dt)
+        beta = torch.ones(B, T, H).to(dt)
+        A = torch.zeros(H)
+        vv = v.to(dt)
+        g = dict(q=q.to(dev), k=q.to(dev), v=vv.to(dev), z=z.to(dev), beta=beta.to(dev),
+                 A=A.to(dev), S0=None)
+        for chunk in (16, 64):
+            o, S_T = gpu_prefill(kda, g, chunk)
+            tol = 1e-6 if dt == torch.float32 else 1e-2
+            assert torch.allclose(o[0, 1, 0].float().cpu(), vv[0, 1, 0].float(), atol=tol, rtol=tol)
+
+
+# --------------------------------------------------------------- decode ----
+
+def test_decode_steps_match_oracle(kda, gpu_device):
+    w = WORKLOADS["k3_decode_bf16"].with_(B=4, steps=24)
+    inp = make_decode_inputs(w)
+    S = inp["S"].to(gpu_device)
+    S_ref = inp["S"].double().numpy()
+    A = inp["A"].to(gpu_device)
+    worst_o = worst_s = 0.0
+    for t in range(w.steps):
+        args = [inp[n][t] for n in ("q", "k", "v", "z", "beta")]
+        o = kda.decode_step(*[a.to(gpu_device) for a in args], A, S)
+        o_ref, S_ref = oracle.decode_step(*[host(a) for a in args], host(inp["A"]), S_ref)
+        torch.cuda.synchronize()
+        worst_o = max(worst_o, slice_relerr(host(o)[:, None], o_ref[:, None], 2))
+        worst_s = max(worst_s, slice_relerr(host(S), S_ref, 1))
+    _say(f"[decode] 24 steps: o err {worst_o:.3e} S err {worst_s:.3e}")
+    assert worst_o <= 2e-2 and worst_s <= 2e-2
+
+
+def test_decode_full_batch_one_step(kda, gpu_device):
+    """B64 H96 d128 from a nonzero state: every head, one step."""
+    w = WORKLOADS["k3_decode_bf16"]
+    inp = make_decode_inputs(w, steps=1)
+    S0 = torch.randn(w.B, w.H, w.dk, w.dv, generator=torch.Generator().manual_seed(7)) * 0.05
+    S = S0.to(gpu_device)
+    args = [inp[n][0] for n in ("q", "k", "v", "z", "beta")]
+    o = kda.decode_step(*[a.to(gpu_device) for a in args], inp["A"].to(gpu_device), S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.decode_step(*[host(a) for a in args], host(inp["A"]), S0.numpy())
+    eo = slice_relerr(host(o)[:, None], o_ref[:, None], 2)
+    es = slice_relerr(host(S), S_ref, 1)
+    _say(f"[decode] full batch: o err {eo:.3e} S err {es:.3e}")
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_decode_fp32_d16(kda, gpu_device):
+    g = torch.Generator().manual_seed(11)
+    B, H, D = 3, 5, 16
+    q = torch.nn.functional.normalize(torch.randn(B, H, D, generator=g), dim=-1)
+    k = torch.nn.functional.normalize(torch.randn(B, H, D, generator=g), dim=-1)
+    v, z = torch.randn(B, H, D, generator=g), torch.randn(B, H, D, generator=g)
+    beta = torch.rand(B, H, generator=g)
+    A = torch.rand(H, generator=g) * 2 - 1
+    S0 = torch.randn(B, H, D, D, generator=g)
+    S = S0.to(gpu_device)
+    o = kda.decode_step(q.to(gpu_device), k.to(gpu_device), v.to(gpu_device), z.to(gpu_device),
+                        beta.to(gpu_device), A.to(gpu_device), S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.decode_step(q.numpy(), k.numpy(), v.numpy(), z.numpy(), beta.numpy(),
+                                      A.numpy(), S0.numpy())
+    assert slice_relerr(host(o)[:, None], o_ref[:, None], 2) <= 1e-4
+    assert slice_relerr(host(S), S_ref, 1) <= 1e-4
+
+
+def test_decode_equals_prefill(kda, gpu_device):
+    """T decode steps on the GPU equal one GPU prefill over the same T tokens."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(H=3, B=2)
+    inp = to_dev(make_prefill_inputs(w, T=40), gpu_device)
+    o_p, S_p = gpu_prefill(kda, inp, 16)
+    S = inp["S0"].clone()
+    outs = []
+    for t in range(40):
+        outs.append(kda.decode_step(inp["q"][:, t].contiguous(), inp["k"][:, t].contiguous(),
+                                    inp["v"][:, t].contiguous(), inp["z"][:, t].contiguous(),
+                                    inp["beta"][:, t].contiguous(), inp["A"], S))
+    torch.cuda.synchronize()
+    o_d = torch.stack(outs, 1)
+    assert slice_relerr(host(o_d), host(o_p), 2) < 2e-2
+    assert slice_relerr(host(S), host(S_p), 1) < 2e-2
