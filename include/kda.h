@@ -33,7 +33,9 @@
  *    written.  A failed launch returns KDA_ERR_HIP.
  *  - Pointers must be 16-byte aligned.  Sizes are int64.
  *  - Supported: dtype in {KDA_F32, KDA_BF16}; dk == dv in {16, 128}; prefill
- *    chunk in {16, 64}.  Anything else returns KDA_ERR_UNSUPPORTED.
+ *    chunk in {16, 64}, except fp32 with dk = 128, which runs chunk 16 only
+ *    (its chunk-64 tiles do not fit in LDS).  Anything else returns
+ *    KDA_ERR_UNSUPPORTED.
  *  - Numerics: fp32 accumulation and an fp32 state.  bf16 outputs are rounded
  *    to nearest even.  NaN/Inf inputs are not checked and propagate.  Results
  *    are bitwise reproducible run to run (no atomics in the arithmetic).

@@ -203,7 +203,7 @@ def test_overwrite_on_gpu(kda, gpu_device):
         vv = v.to(dt)
         g = dict(q=q.to(dev), k=q.to(dev), v=vv.to(dev), z=z.to(dev), beta=beta.to(dev),
                  A=A.to(dev), S0=None)
-        for chunk in (16, 64):
+        for chunk in ((16,) if dt == torch.float32 else (16, 64)):   # fp32 d128: chunk 16
             o, S_T = gpu_prefill(kda, g, chunk)
             tol = 1e-6 if dt == torch.float32 else 1e-2
             assert torch.allclose(o[0, 1, 0].float().cpu(), vv[0, 1, 0].float(), atol=tol, rtol=tol)
