@@ -85,7 +85,8 @@ kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk
     if (bh > 0x7fffffff / 8) return KDA_ERR_SHAPE;  // grid size
     int dvb = dv_per_block;
     if (dvb == 0) dvb = kda::prefill_default_dv_per_block(dtype, B, H, D, chunk);
-    if (dvb <= 0 || D % dvb != 0 || !kda::prefill_supported(dtype, D, chunk, dvb))
+    const bool role_split = kda::prefill16_supported(dtype, D, chunk, dvb);
+    if (dvb <= 0 || D % dvb != 0 || (!role_split && !kda::prefill_supported(dtype, D, chunk, dvb)))
         return KDA_ERR_UNSUPPORTED;
     if (!A || !S_T) return KDA_ERR_NULL;
     if (bth > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL;
@@ -110,7 +111,8 @@ kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk
     a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.A = A; a.S0 = S0;
     a.o = o; a.S_T = S_T;
     a.stream = (hipStream_t)stream;
-    return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    const hipError_t err = role_split ? kda::launch_prefill16(a) : kda::launch_prefill(a);
+    return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status kda_prefill(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,

@@ -38,6 +38,9 @@ bool prefill_supported(int dtype, int64_t D, int chunk, int dv_per_block);
 // Default value columns per workgroup for these sizes.
 int prefill_default_dv_per_block(int dtype, int64_t B, int64_t H, int64_t D, int chunk);
 hipError_t launch_prefill(const PrefillArgs &a);
+// Role-split variant for bf16, D = 128, chunk 16 (kda_prefill16.hip).
+bool prefill16_supported(int dtype, int64_t D, int chunk, int dv_per_block);
+hipError_t launch_prefill16(const PrefillArgs &a);
 
 bool decode_supported(int dtype, int64_t D);
 hipError_t launch_decode(const DecodeArgs &a);

@@ -1,0 +1,452 @@
+// kda_prefill16.hip -- chunkwise KDA prefill, 16-token chunks, bf16, d = 128,
+// with role-split waves (gfx950).
+//
+// Same method and chunk algebra as kda_prefill.hip (the KDA recurrence and
+// bounded gate of "Kimi K3 Open Weights: What Is Actually New", section 1,
+// run "recurrent between, parallel within" 16-token chunks), organised for
+// overlap instead of lock-step phases:
+//
+//  * PREP waves (NPW per workgroup).  Prep wave w owns chunks w, w+NPW, ...
+//    and does the S-independent work of a chunk by itself, with no workgroup
+//    barrier: gate, decay factors, the P and L tiles, the 16 x 16 inverse and
+//    W.  It writes the chain operands into an LDS slot (chunk m uses slot
+//    m mod NSLOT).
+//  * CHAIN waves (NCW per workgroup, 16 value columns each, fp32 state slice
+//    in registers).  They consume the slots in chunk order and run the
+//    S-dependent chain: U = T diag(beta) V - W S, O = Q^ S + P U,
+//    S <- e^{G_C} S + Kh^T U.  Each chain wave loads its own 16 columns of V
+//    straight into MFMA fragments.
+//  Slot hand-off uses two LDS counters per slot: `ready` (set by the prep
+//  wave to u+1 once the slot holds its u-th chunk) and `done` (bumped once
+//  per chain wave, from one lane, after it has read the slot into
+//  registers).  A prep wave waits for done >= NCW*u before writing the u-th
+//  use of a slot; chain waves wait for ready >= u+1.  Production of chunk m
+//  only depends on consumption of chunk m - NSLOT, so the hand-off cannot
+//  deadlock; every wait is additionally bounded.  A SIMD hosts one prep wave
+//  (VALU-bound) and one chain wave (MFMA/LDS-latency-bound), which overlap.
+//
+// With one chunk per 16-token sub-tile, every decay factor can be referred to
+// the chunk start, G_r = sum_{s<=r} g_s:
+//    Q^ = Q * e^G   (row operand of P, and of the inter-chunk read Q^ S)
+//    K^ = K * e^G   (row operand of L, and W = T diag(beta) K^)
+//    Kc = K * e^-G  (column operand of P and L; |Kc| <= e^80 since g >= -5)
+//    Kh = K * e^{G_C - G}   (state update)
+// so P = tril(Q^ Kc^T), L = diag(beta) strict_tril(K^ Kc^T).  The bound
+// e^-80 <= e^G <= 1 over 16 tokens is the range argument of the pages.
+//
+// The 16 x 16 inverse T = (I + L)^-1 uses L's nilpotency (L^16 = 0):
+//    T = (I - L)(I + L^2)(I + L^4)(I + L^8),
+// nine bf16 MFMAs kept in registers.  An MFMA result tile sits in B-operand
+// layout (lane (g,n) holds rows 4g..4g+3 of column n), and the A-operand
+// layout of M is the B-operand layout of M^T, so every product is formed
+// together with the transposes the next one needs.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+struct Prefill16Params {
+    const bf16 *q, *k, *v, *z, *beta;
+    const float *A, *S0;
+    bf16 *o;
+    float *S_T;
+    int64_t T, H;
+    int nsplit;
+};
+
+template <int NCW, int NPW, int NSLOT>
+struct P16Cfg {
+    static constexpr int D = 128, C = 16;
+    static constexpr int DVB = 16 * NCW;           // value columns per workgroup
+    static constexpr int DP = D + 8;               // [token][d] row stride
+    static constexpr int CP = C + 8;               // [d][token] / [token][token] row stride
+    // slot: the chain operands of one chunk
+    static constexpr int S_QG = 0;                         // Q^         [C][DP]
+    static constexpr int S_WN = S_QG + C * DP * 2;         // K^, then -W [C][DP]
+    static constexpr int S_KHT = S_WN + C * DP * 2;        // Kh^T       [D][CP]
+    static constexpr int S_P = S_KHT + D * CP * 2;         // P          [C][CP]
+    static constexpr int S_TB = S_P + C * CP * 2;          // T diag(b)  [C][CP]
+    static constexpr int S_GC = S_TB + C * CP * 2;         // e^{G_C}    [D] fp32
+    static constexpr int SLOT = S_GC + D * 4;
+    // prep-wave scratch
+    static constexpr int W_KC = 0;                          // Kc    [C][DP]
+    static constexpr int W_KGT = W_KC + C * DP * 2;         // K^^T  [D][CP]
+    static constexpr int W_BETA = W_KGT + D * CP * 2;       // beta  [C] fp32
+    static constexpr int SCR = (W_BETA + C * 4 + 15) / 16 * 16;
+    static constexpr int OFF_FLAGS = 0;                     // ready[NSLOT], done[NSLOT]
+    static constexpr int OFF_SLOTS = 64;
+    static constexpr int OFF_SCR = OFF_SLOTS + NSLOT * SLOT;
+    static constexpr int LDS_BYTES = OFF_SCR + NPW * SCR;
+    static_assert(2 * NSLOT * 4 <= 64, "flag area");
+    static_assert(SLOT % 16 == 0 && SCR % 16 == 0, "alignment");
+    static_assert(LDS_BYTES <= 150 * 1024, "LDS budget");
+};
+
+// Bounded LDS wait: returns once *flag >= target (workgroup-scope acquire).
+__device__ __forceinline__ void wait_at_least(int *flag, int target) {
+    for (int it = 0; it < (1 << 22); ++it) {
+        if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+            return;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = bf16x2{(bf16)a, (bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Raw buffer resource over [p, p + bytes): loads past the end return 0 and
+// stores past the end are dropped, which masks a partial last chunk.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16 values -> one [.][token] row of 16 bf16 (two 16-byte stores).
+__device__ __forceinline__ void store_row16(bf16 *row, const float *x) {
+    uint4 *r = reinterpret_cast<uint4 *>(row);
+    r[0] = uint4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
+                 pack_bf16(x[6], x[7])};
+    r[1] = uint4{pack_bf16(x[8], x[9]), pack_bf16(x[10], x[11]), pack_bf16(x[12], x[13]),
+                 pack_bf16(x[14], x[15])};
+}
+
+template <int NCW, int NPW, int NSLOT>
+__global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill16Params prm) {
+    using Cfg = P16Cfg<NCW, NPW, NSLOT>;
+    constexpr int D = Cfg::D, C = Cfg::C, DVB = Cfg::DVB, DP = Cfg::DP, CP = Cfg::CP,
+                  NDT = D / 16;
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+    int *ready = reinterpret_cast<int *>(smem + Cfg::OFF_FLAGS);
+    int *done = ready + NSLOT;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave-uniform by construction; readfirstlane lets the compiler keep it
+    // (and every address derived from it) in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, n = lane & 15;
+
+    int64_t x = blockIdx.x;
+    const int64_t nblk = gridDim.x;
+    if (nblk % 8 == 0) x = (x % 8) * (nblk / 8) + x / 8;   // slices of a head share an XCD
+    const int64_t bh = x / prm.nsplit;
+    const int split = (int)(x % prm.nsplit);
+    const int64_t H = prm.H, Tn = prm.T;
+    const int64_t b = bh / H;
+    const int h = (int)(bh % H);
+    const int j0 = split * DVB;
+    const int64_t tok_stride = H * D;
+    const int64_t base = (b * Tn * H + h) * D;
+    const int64_t bbase = b * Tn * H + h;
+    const int64_t nchunks = (Tn + C - 1) / C;
+
+    if (tid < 2 * NSLOT) ready[tid] = 0;
+    __syncthreads();
+
+    if (wave < NCW) {
+        // ============================ chain wave ============================
+        const int jw = j0 + 16 * wave;
+        f32x4 S[NDT];
+        if (prm.S0) {
+            const float *s0 = prm.S0 + bh * (int64_t)(D * D);
+#pragma unroll
+            for (int i = 0; i < NDT; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[i][e] = s0[(16 * i + 4 * g + e) * D + jw + n];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        // V fragment of a chunk: V[t0 + 4g + e][jw + n], e = 0..3 (zero past T)
+        const int64_t row_bytes = tok_stride * 2;
+        auto chunk_rows = [&](int64_t t0) { return (Tn - t0 < C ? Tn - t0 : (int64_t)C); };
+        short vr[4];
+        auto load_v = [&](int64_t t0) {
+            const auto rs = make_rsrc(prm.v + base + t0 * tok_stride + jw, chunk_rows(t0) * row_bytes);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                vr[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, (4 * g + e) * (int)row_bytes + 2 * n, 0, 0);
+        };
+        if (nchunks > 0) load_v(0);
+        for (int64_t m = 0; m < nchunks; ++m) {
+            const int s = (int)(m % NSLOT);
+            const int use = (int)(m / NSLOT);
+            const int64_t t0 = m * C;
+            Frag<bf16> Vf;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Vf.v[e] = __builtin_bit_cast(bf16, vr[e]);
+            if (m + 1 < nchunks) load_v(t0 + C);
+            wait_at_least(&ready[s], use + 1);
+            const char *slot = smem + Cfg::OFF_SLOTS + s * Cfg::SLOT;
+            const bf16 *sQG = reinterpret_cast<const bf16 *>(slot + Cfg::S_QG);
+            const bf16 *sWn = reinterpret_cast<const bf16 *>(slot + Cfg::S_WN);
+            const bf16 *sKhT = reinterpret_cast<const bf16 *>(slot + Cfg::S_KHT);
+            const bf16 *sP = reinterpret_cast<const bf16 *>(slot + Cfg::S_P);
+            const bf16 *sTb = reinterpret_cast<const bf16 *>(slot + Cfg::S_TB);
+            const float *sGC = reinterpret_cast<const float *>(slot + Cfg::S_GC);
+            Frag<bf16> Wf[NDT], Qf[NDT], Kf[NDT];
+            f32x4 gc[NDT];
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) {
+                Wf[i] = lds_frag(sWn, DP, 16 * i, lane);
+                Qf[i] = lds_frag(sQG, DP, 16 * i, lane);
+                Kf[i] = lds_frag(sKhT + 16 * i * CP, CP, 0, lane);
+                gc[i] = *reinterpret_cast<const f32x4 *>(sGC + 16 * i + 4 * g);
+            }
+            const Frag<bf16> Pf = lds_frag(sP, CP, 0, lane);
+            const Frag<bf16> Tf = lds_frag(sTb, CP, 0, lane);
+            // everything this wave needs from the slot is in registers now
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // one increment per wave (an add from every lane would count 64)
+            if (lane == 0)
+                __hip_atomic_fetch_add(&done[s], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+
+            Frag<bf16> Sf[NDT];
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) Sf[i] = acc_frag<bf16>(S[i]);
+            // U = T diag(beta) V - W S  (two accumulators halve the dependent chain)
+            f32x4 Ua = {0.f, 0.f, 0.f, 0.f}, Ub = {0.f, 0.f, 0.f, 0.f};
+            mma16(Ua, Tf, Vf);
+            mma32(Ub, Wf[0], Wf[1], Sf[0], Sf[1]);
+            mma32(Ua, Wf[2], Wf[3], Sf[2], Sf[3]);
+            mma32(Ub, Wf[4], Wf[5], Sf[4], Sf[5]);
+            mma32(Ua, Wf[6], Wf[7], Sf[6], Sf[7]);
+            const f32x4 U = Ua + Ub;
+            const Frag<bf16> Uf = acc_frag<bf16>(U);
+            // S <- e^{G_C} S + Kh^T U
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) {
+                S[i] *= gc[i];
+                mma16(S[i], Kf[i], Uf);
+            }
+            // O = Q^ S_old + P U
+            f32x4 Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
+            mma32(Oa, Qf[0], Qf[1], Sf[0], Sf[1]);
+            mma32(Ob, Qf[2], Qf[3], Sf[2], Sf[3]);
+            mma32(Oa, Qf[4], Qf[5], Sf[4], Sf[5]);
+            mma32(Ob, Qf[6], Qf[7], Sf[6], Sf[7]);
+            mma16(Oa, Pf, Uf);
+            const f32x4 O = Oa + Ob;
+            const auto ors = make_rsrc(prm.o + base + t0 * tok_stride + jw, chunk_rows(t0) * row_bytes);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (bf16)O[e]), ors,
+                                                      (4 * g + e) * (int)row_bytes + 2 * n, 0, 0);
+        }
+        float *st = prm.S_T + bh * (int64_t)(D * D);
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[(16 * i + 4 * g + e) * D + jw + n] = S[i][e];
+        return;
+    }
+
+    // ============================== prep wave ===============================
+    const int pw = wave - NCW;
+    char *scr = smem + Cfg::OFF_SCR + pw * Cfg::SCR;
+    bf16 *sKc = reinterpret_cast<bf16 *>(scr + Cfg::W_KC);
+    bf16 *sKGT = reinterpret_cast<bf16 *>(scr + Cfg::W_KGT);
+    float *sBeta = reinterpret_cast<float *>(scr + Cfg::W_BETA);
+
+    const float c2 = -__builtin_amdgcn_exp2f(prm.A[h] * kLog2e) * kLog2e;
+    const int d0 = 2 * lane;                           // this lane's channel pair
+
+    uint32_t rq[C], rk[C], rz[C];
+    short rb;   // lane s < 16: beta of token s
+    const int64_t row_bytes = tok_stride * 2;
+    auto load_chunk = [&](int64_t t0) {
+        // one uniform buffer resource per tensor and chunk; rows past T read 0
+        const int64_t rows = Tn - t0 < C ? Tn - t0 : (int64_t)C;
+        const auto rq_ = make_rsrc(prm.q + base + t0 * tok_stride, rows * row_bytes);
+        const auto rk_ = make_rsrc(prm.k + base + t0 * tok_stride, rows * row_bytes);
+        const auto rz_ = make_rsrc(prm.z + base + t0 * tok_stride, rows * row_bytes);
+        const auto rb_ = make_rsrc(prm.beta + bbase + t0 * H, rows * H * 2);
+        rb = __builtin_amdgcn_raw_buffer_load_b16(rb_, (lane & 15) * (int)H * 2, 0, 0);
+#pragma unroll
+        for (int s = 0; s < C; ++s) {
+            const int so = s * (int)row_bytes;
+            rq[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rq_, 4 * lane, so, 0);
+            rk[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk_, 4 * lane, so, 0);
+            rz[s] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rz_, 4 * lane, so, 0);
+        }
+    };
+    if (pw < nchunks) load_chunk((int64_t)pw * C);
+
+    for (int kk = 0;; ++kk) {
+        const int64_t m = pw + (int64_t)NPW * kk;
+        if (m >= nchunks) break;
+        const int64_t t0 = m * C;
+        const int s_ = (int)(m % NSLOT);
+        const int use = (int)(m / NSLOT);
+        char *slot = smem + Cfg::OFF_SLOTS + s_ * Cfg::SLOT;
+        bf16 *sQG = reinterpret_cast<bf16 *>(slot + Cfg::S_QG);
+        bf16 *sWn = reinterpret_cast<bf16 *>(slot + Cfg::S_WN);   // K^ until W overwrites it
+        bf16 *sKhT = reinterpret_cast<bf16 *>(slot + Cfg::S_KHT);
+        bf16 *sP = reinterpret_cast<bf16 *>(slot + Cfg::S_P);
+        bf16 *sTb = reinterpret_cast<bf16 *>(slot + Cfg::S_TB);
+        float *sGC = reinterpret_cast<float *>(slot + Cfg::S_GC);
+        const bool full = t0 + C <= Tn;
+
+        // unpacked inputs; tokens past the end load as 0 and get alpha = 1
+        float q0[C], q1[C], k0[C], k1[C], a0[C], a1[C];
+#pragma unroll
+        for (int s = 0; s < C; ++s) {
+            const bool valid = full || t0 + s < Tn;
+            q0[s] = bf_lo(rq[s]);
+            q1[s] = bf_hi(rq[s]);
+            k0[s] = bf_lo(rk[s]);
+            k1[s] = bf_hi(rk[s]);
+            a0[s] = valid ? kda_alpha(c2, bf_lo(rz[s])) : 1.0f;
+            a1[s] = valid ? kda_alpha(c2, bf_hi(rz[s])) : 1.0f;
+        }
+        const float beta_l = __uint_as_float((uint32_t)(unsigned short)rb << 16);  // lane < 16
+        // this wave's next chunk streams in while the rest of this one runs
+        if (m + NPW < nchunks) load_chunk(t0 + (int64_t)NPW * C);
+
+        wait_at_least(&done[s_], NCW * use);   // every chain wave has read the previous use
+
+        // ---- decay factors and operands (lane = channel pair d0, d0+1) ------
+        float kg0[C], kg1[C];
+        float F0 = 1.f, F1 = 1.f;
+#pragma unroll
+        for (int s = 0; s < C; ++s) {
+            F0 *= a0[s];
+            F1 *= a1[s];
+            kg0[s] = k0[s] * F0;
+            kg1[s] = k1[s] * F1;
+            *reinterpret_cast<uint32_t *>(sQG + s * DP + d0) = pack_bf16(q0[s] * F0, q1[s] * F1);
+            *reinterpret_cast<uint32_t *>(sWn + s * DP + d0) = pack_bf16(kg0[s], kg1[s]);
+        }
+        store_row16(sKGT + d0 * CP, kg0);
+        store_row16(sKGT + (d0 + 1) * CP, kg1);
+        sGC[d0] = F0;
+        sGC[d0 + 1] = F1;
+        {
+            const float it0 = __builtin_amdgcn_rcpf(F0), it1 = __builtin_amdgcn_rcpf(F1);
+            float R0 = 1.f, R1 = 1.f;     // decay over (s, end of chunk]
+            float h0[C], h1[C];
+#pragma unroll
+            for (int s = C - 1; s >= 0; --s) {
+                h0[s] = k0[s] * R0;
+                h1[s] = k1[s] * R1;
+                *reinterpret_cast<uint32_t *>(sKc + s * DP + d0) = pack_bf16(h0[s] * it0, h1[s] * it1);
+                R0 *= a0[s];
+                R1 *= a1[s];
+            }
+            store_row16(sKhT + d0 * CP, h0);
+            store_row16(sKhT + (d0 + 1) * CP, h1);
+        }
+        if (lane < C) sBeta[lane] = beta_l;
+        compiler_fence();
+
+        // ---- P^T, L, L^T from Q^, K^, Kc (B-layout results) --------------------
+        // accP[e]  = sum_d Kc[4g+e][d] Q^[n][d]   = P'[n][4g+e]   (P = tril P')
+        // accL[e]  = sum_d K^[4g+e][d] Kc[n][d]   = L'[4g+e][n]
+        // accLT[e] = sum_d Kc[4g+e][d] K^[n][d]   = L'[n][4g+e]   (L = beta strict_tril L')
+        f32x4 accP = {0.f, 0.f, 0.f, 0.f}, accL = {0.f, 0.f, 0.f, 0.f},
+              accLT = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k32 = 0; k32 < D; k32 += 32) {
+            const Frag<bf16> c0 = lds_frag(sKc, DP, k32, lane), c1 = lds_frag(sKc, DP, k32 + 16, lane);
+            const Frag<bf16> q0f = lds_frag(sQG, DP, k32, lane), q1f = lds_frag(sQG, DP, k32 + 16, lane);
+            const Frag<bf16> h0f = lds_frag(sWn, DP, k32, lane), h1f = lds_frag(sWn, DP, k32 + 16, lane);
+            mma32(accP, c0, c1, q0f, q1f);
+            mma32(accL, h0f, h1f, c0, c1);
+            mma32(accLT, c0, c1, h0f, h1f);
+        }
+        const f32x4 brow = *reinterpret_cast<const f32x4 *>(sBeta + 4 * g);   // beta_{4g+e}
+        const float bcol = sBeta[n];                                            // beta_n
+        f32x4 Lb, LTb, ImLT;   // L, L^T (B layout); I - L^T
+        {
+            typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+            bf16x4v pw4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                pw4[e] = (bf16)(r <= n ? accP[e] : 0.0f);          // P[n][4g+e]
+                Lb[e] = n < r ? brow[e] * accL[e] : 0.0f;           // L[4g+e][n]
+                LTb[e] = r < n ? bcol * accLT[e] : 0.0f;            // L[n][4g+e]
+                ImLT[e] = (r == n ? 1.0f : 0.0f) - LTb[e];
+            }
+            *reinterpret_cast<bf16x4v *>(sP + n * CP + 4 * g) = pw4;
+        }
+        // ---- T^T = Y^T X^T with X = (I-L)(I+L^2), Y = (I+L^4)(I+L^8) ----------
+        // B-layout inputs: M (B) and M^T (= A-layout of M).
+        auto bf = [](const f32x4 &x) { return acc_frag<bf16>(x); };
+        auto mm = [](const Frag<bf16> &a, const Frag<bf16> &b) {
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            mma16(d, a, b);
+            return d;
+        };
+        auto plus_i = [&](f32x4 x) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] += (4 * g + e == n) ? 1.0f : 0.0f;
+            return x;
+        };
+        const Frag<bf16> fL = bf(Lb), fLT = bf(LTb);
+        const f32x4 L2 = mm(fLT, fL), L2T = mm(fL, fLT);                 // L^2, (L^2)^T
+        const Frag<bf16> fL2 = bf(L2), fL2T = bf(L2T);
+        const f32x4 L4 = mm(fL2T, fL2), L4T = mm(fL2, fL2T);             // L^4, (L^4)^T
+        const Frag<bf16> fL4 = bf(L4), fL4T = bf(L4T);
+        const f32x4 L8 = mm(fL4T, fL4);                                  // L^8
+        const f32x4 Y = mm(bf(plus_i(L4T)), bf(plus_i(L8)));            // (I+L^4)(I+L^8)
+        const f32x4 XT = mm(bf(plus_i(L2)), bf(ImLT));                   // (I+L^2)^T (I-L)^T
+        const f32x4 TT = mm(bf(Y), bf(XT));                              // T^T = Y^T X^T
+        // T^T in B layout = T in A layout: lane (g,n) holds T[n][4g+e]
+        Frag<bf16> Tf;   // A-layout of Tb = T diag(beta): T[n][4g+e] beta_{4g+e}
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Tf.v[e] = (bf16)(TT[e] * brow[e]);
+        *reinterpret_cast<bf16x4 *>(sTb + n * CP + 4 * g) = Tf.v;
+
+        // ---- W^T = K^^T Tb^T, written as -W rows ----------------------------
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            f32x4 w = {0.f, 0.f, 0.f, 0.f};
+            mma16(w, lds_frag(sKGT + 16 * dt * CP, CP, 0, lane), Tf);
+            // w[e] = W[n][16 dt + 4 g + e]
+            *reinterpret_cast<bf16x4 *>(sWn + n * DP + 16 * dt + 4 * g) =
+                bf16x4{(bf16)(-w[0]), (bf16)(-w[1]), (bf16)(-w[2]), (bf16)(-w[3])};
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __hip_atomic_store(&ready[s_], use + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
+template <int NCW, int NPW, int NSLOT>
+static hipError_t launch_p16(const PrefillArgs &a) {
+    Prefill16Params prm;
+    prm.q = static_cast<const bf16 *>(a.q);
+    prm.k = static_cast<const bf16 *>(a.k);
+    prm.v = static_cast<const bf16 *>(a.v);
+    prm.z = static_cast<const bf16 *>(a.z);
+    prm.beta = static_cast<const bf16 *>(a.beta);
+    prm.A = a.A;
+    prm.S0 = a.S0;
+    prm.o = static_cast<bf16 *>(a.o);
+    prm.S_T = a.S_T;
+    prm.T = a.T;
+    prm.H = a.H;
+    prm.nsplit = 128 / (16 * NCW);
+    const int64_t nblk = a.B * a.H * prm.nsplit;
+    hipLaunchKernelGGL((kda_prefill16_kernel<NCW, NPW, NSLOT>), dim3((unsigned)nblk),
+                       dim3(64 * (NCW + NPW)), 0, a.stream, prm);
+    return hipGetLastError();
+}
+
+bool prefill16_supported(int dtype, int64_t D, int chunk, int dv_per_block) {
+    return dtype == 1 && D == 128 && chunk == 16 && (dv_per_block == 32 || dv_per_block == 64);
+}
+
+hipError_t launch_prefill16(const PrefillArgs &a) {
+    if (a.dv_per_block == 64) return launch_p16<4, 4, 6>(a);
+    if (a.dv_per_block == 32) return launch_p16<2, 4, 6>(a);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda
