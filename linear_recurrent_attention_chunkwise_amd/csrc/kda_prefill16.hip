@@ -70,14 +70,14 @@ struct P16Cfg {
     static constexpr int SLOT = S_GC + D * 4;
     // prep-wave scratch
     static constexpr int W_KC = 0;                          // Kc    [C][DP]
-    static constexpr int W_KGT = W_KC + C * DP * 2;         // K^^T  [D][CP]
-    static constexpr int W_BETA = W_KGT + D * CP * 2;       // beta  [C] fp32
+    static constexpr int W_BETA = W_KC + C * DP * 2;        // beta  [C] fp32
     static constexpr int SCR = (W_BETA + C * 4 + 15) / 16 * 16;
     static constexpr int OFF_FLAGS = 0;                     // ready[NSLOT], done[NSLOT]
     static constexpr int OFF_SLOTS = 64;
     static constexpr int OFF_SCR = OFF_SLOTS + NSLOT * SLOT;
     static constexpr int LDS_BYTES = OFF_SCR + NPW * SCR;
     static_assert(2 * NSLOT * 4 <= 64, "flag area");
+    static_assert(NCW + NPW <= 16, "workgroup size");
     static_assert(SLOT % 16 == 0 && SCR % 16 == 0, "alignment");
     static_assert(LDS_BYTES <= 150 * 1024, "LDS budget");
 };
@@ -174,38 +174,38 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
                 vr[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, (4 * g + e) * (int)row_bytes + 2 * n, 0, 0);
         };
         if (nchunks > 0) load_v(0);
+        auto slot_of = [&](int64_t m) { return smem + Cfg::OFF_SLOTS + (int)(m % NSLOT) * Cfg::SLOT; };
+        // W, T diag(beta) and Kh^T fragments of chunk m (read one chunk ahead)
+        Frag<bf16> Wf[NDT], Kf[NDT], Tf;
+        auto read_wtk = [&](int64_t m) {
+            wait_at_least(&ready[m % NSLOT], (int)(m / NSLOT) + 1);
+            const char *slot = slot_of(m);
+            const bf16 *sWn = reinterpret_cast<const bf16 *>(slot + Cfg::S_WN);
+            const bf16 *sKhT = reinterpret_cast<const bf16 *>(slot + Cfg::S_KHT);
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) Wf[i] = lds_frag(sWn, DP, 16 * i, lane);
+            Tf = lds_frag(reinterpret_cast<const bf16 *>(slot + Cfg::S_TB), CP, 0, lane);
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) Kf[i] = lds_frag(sKhT + 16 * i * CP, CP, 0, lane);
+        };
+        if (nchunks > 0) read_wtk(0);
         for (int64_t m = 0; m < nchunks; ++m) {
-            const int s = (int)(m % NSLOT);
-            const int use = (int)(m / NSLOT);
             const int64_t t0 = m * C;
+            const char *slot = slot_of(m);
+            // the rest of chunk m's operands; their latency overlaps U below
+            const bf16 *sQG = reinterpret_cast<const bf16 *>(slot + Cfg::S_QG);
+            const float *sGC = reinterpret_cast<const float *>(slot + Cfg::S_GC);
+            Frag<bf16> Qf[NDT];
+            f32x4 gc[NDT];
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) gc[i] = *reinterpret_cast<const f32x4 *>(sGC + 16 * i + 4 * g);
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) Qf[i] = lds_frag(sQG, DP, 16 * i, lane);
+            const Frag<bf16> Pf = lds_frag(reinterpret_cast<const bf16 *>(slot + Cfg::S_P), CP, 0, lane);
             Frag<bf16> Vf;
 #pragma unroll
             for (int e = 0; e < 4; ++e) Vf.v[e] = __builtin_bit_cast(bf16, vr[e]);
             if (m + 1 < nchunks) load_v(t0 + C);
-            wait_at_least(&ready[s], use + 1);
-            const char *slot = smem + Cfg::OFF_SLOTS + s * Cfg::SLOT;
-            const bf16 *sQG = reinterpret_cast<const bf16 *>(slot + Cfg::S_QG);
-            const bf16 *sWn = reinterpret_cast<const bf16 *>(slot + Cfg::S_WN);
-            const bf16 *sKhT = reinterpret_cast<const bf16 *>(slot + Cfg::S_KHT);
-            const bf16 *sP = reinterpret_cast<const bf16 *>(slot + Cfg::S_P);
-            const bf16 *sTb = reinterpret_cast<const bf16 *>(slot + Cfg::S_TB);
-            const float *sGC = reinterpret_cast<const float *>(slot + Cfg::S_GC);
-            Frag<bf16> Wf[NDT], Qf[NDT], Kf[NDT];
-            f32x4 gc[NDT];
-#pragma unroll
-            for (int i = 0; i < NDT; ++i) {
-                Wf[i] = lds_frag(sWn, DP, 16 * i, lane);
-                Qf[i] = lds_frag(sQG, DP, 16 * i, lane);
-                Kf[i] = lds_frag(sKhT + 16 * i * CP, CP, 0, lane);
-                gc[i] = *reinterpret_cast<const f32x4 *>(sGC + 16 * i + 4 * g);
-            }
-            const Frag<bf16> Pf = lds_frag(sP, CP, 0, lane);
-            const Frag<bf16> Tf = lds_frag(sTb, CP, 0, lane);
-            // everything this wave needs from the slot is in registers now
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            // one increment per wave (an add from every lane would count 64)
-            if (lane == 0)
-                __hip_atomic_fetch_add(&done[s], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 
             Frag<bf16> Sf[NDT];
 #pragma unroll
@@ -232,6 +232,13 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             mma32(Oa, Qf[4], Qf[5], Sf[4], Sf[5]);
             mma32(Ob, Qf[6], Qf[7], Sf[6], Sf[7]);
             mma16(Oa, Pf, Uf);
+            // every read of slot m has been consumed by the MFMAs above; release
+            // it (one increment per wave: an add from every lane would count 64)
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0)
+                __hip_atomic_fetch_add(&done[m % NSLOT], 1, __ATOMIC_RELEASE,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (m + 1 < nchunks) read_wtk(m + 1);
             const f32x4 O = Oa + Ob;
             const auto ors = make_rsrc(prm.o + base + t0 * tok_stride + jw, chunk_rows(t0) * row_bytes);
 #pragma unroll
@@ -251,7 +258,6 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
     const int pw = wave - NCW;
     char *scr = smem + Cfg::OFF_SCR + pw * Cfg::SCR;
     bf16 *sKc = reinterpret_cast<bf16 *>(scr + Cfg::W_KC);
-    bf16 *sKGT = reinterpret_cast<bf16 *>(scr + Cfg::W_KGT);
     float *sBeta = reinterpret_cast<float *>(scr + Cfg::W_BETA);
 
     const float c2 = -__builtin_amdgcn_exp2f(prm.A[h] * kLog2e) * kLog2e;
@@ -293,38 +299,29 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         float *sGC = reinterpret_cast<float *>(slot + Cfg::S_GC);
         const bool full = t0 + C <= Tn;
 
-        // unpacked inputs; tokens past the end load as 0 and get alpha = 1
-        float q0[C], q1[C], k0[C], k1[C], a0[C], a1[C];
+        // decays; tokens past the end load as 0 and get alpha = 1
+        float a0[C], a1[C];
 #pragma unroll
         for (int s = 0; s < C; ++s) {
             const bool valid = full || t0 + s < Tn;
-            q0[s] = bf_lo(rq[s]);
-            q1[s] = bf_hi(rq[s]);
-            k0[s] = bf_lo(rk[s]);
-            k1[s] = bf_hi(rk[s]);
             a0[s] = valid ? kda_alpha(c2, bf_lo(rz[s])) : 1.0f;
             a1[s] = valid ? kda_alpha(c2, bf_hi(rz[s])) : 1.0f;
         }
         const float beta_l = __uint_as_float((uint32_t)(unsigned short)rb << 16);  // lane < 16
-        // this wave's next chunk streams in while the rest of this one runs
-        if (m + NPW < nchunks) load_chunk(t0 + (int64_t)NPW * C);
 
         wait_at_least(&done[s_], NCW * use);   // every chain wave has read the previous use
 
         // ---- decay factors and operands (lane = channel pair d0, d0+1) ------
-        float kg0[C], kg1[C];
         float F0 = 1.f, F1 = 1.f;
 #pragma unroll
         for (int s = 0; s < C; ++s) {
             F0 *= a0[s];
             F1 *= a1[s];
-            kg0[s] = k0[s] * F0;
-            kg1[s] = k1[s] * F1;
-            *reinterpret_cast<uint32_t *>(sQG + s * DP + d0) = pack_bf16(q0[s] * F0, q1[s] * F1);
-            *reinterpret_cast<uint32_t *>(sWn + s * DP + d0) = pack_bf16(kg0[s], kg1[s]);
+            *reinterpret_cast<uint32_t *>(sQG + s * DP + d0) =
+                pack_bf16(bf_lo(rq[s]) * F0, bf_hi(rq[s]) * F1);
+            *reinterpret_cast<uint32_t *>(sWn + s * DP + d0) =
+                pack_bf16(bf_lo(rk[s]) * F0, bf_hi(rk[s]) * F1);
         }
-        store_row16(sKGT + d0 * CP, kg0);
-        store_row16(sKGT + (d0 + 1) * CP, kg1);
         sGC[d0] = F0;
         sGC[d0 + 1] = F1;
         {
@@ -333,8 +330,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             float h0[C], h1[C];
 #pragma unroll
             for (int s = C - 1; s >= 0; --s) {
-                h0[s] = k0[s] * R0;
-                h1[s] = k1[s] * R1;
+                h0[s] = bf_lo(rk[s]) * R0;
+                h1[s] = bf_hi(rk[s]) * R1;
                 *reinterpret_cast<uint32_t *>(sKc + s * DP + d0) = pack_bf16(h0[s] * it0, h1[s] * it1);
                 R0 *= a0[s];
                 R1 *= a1[s];
@@ -342,6 +339,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             store_row16(sKhT + d0 * CP, h0);
             store_row16(sKhT + (d0 + 1) * CP, h1);
         }
+        // this wave's next chunk streams in while the rest of this one runs
+        if (m + NPW < nchunks) load_chunk(t0 + (int64_t)NPW * C);
         if (lane < C) sBeta[lane] = beta_l;
         compiler_fence();
 
@@ -404,11 +403,17 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         for (int e = 0; e < 4; ++e) Tf.v[e] = (bf16)(TT[e] * brow[e]);
         *reinterpret_cast<bf16x4 *>(sTb + n * CP + 4 * g) = Tf.v;
 
-        // ---- W^T = K^^T Tb^T, written as -W rows ----------------------------
+        // ---- W^T = K^^T Tb^T, written as -W rows over K^ ---------------------
+        // A-layout of K^^T for d-tile dt: lane (g,n) holds K^[4g+e][16 dt + n]
+        // (strided 2-byte reads, conflict-free); a tile is read completely
+        // before its W rows overwrite the same columns.
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
+            Frag<bf16> ka;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ka.v[e] = sWn[(4 * g + e) * DP + 16 * dt + n];
             f32x4 w = {0.f, 0.f, 0.f, 0.f};
-            mma16(w, lds_frag(sKGT + 16 * dt * CP, CP, 0, lane), Tf);
+            mma16(w, ka, Tf);
             // w[e] = W[n][16 dt + 4 g + e]
             *reinterpret_cast<bf16x4 *>(sWn + n * DP + 16 * dt + 4 * g) =
                 bf16x4{(bf16)(-w[0]), (bf16)(-w[1]), (bf16)(-w[2]), (bf16)(-w[3])};
@@ -444,8 +449,8 @@ bool prefill16_supported(int dtype, int64_t D, int chunk, int dv_per_block) {
 }
 
 hipError_t launch_prefill16(const PrefillArgs &a) {
-    if (a.dv_per_block == 64) return launch_p16<4, 4, 6>(a);
-    if (a.dv_per_block == 32) return launch_p16<2, 4, 6>(a);
+    if (a.dv_per_block == 64) return launch_p16<4, 8, 6>(a);
+    if (a.dv_per_block == 32) return launch_p16<2, 6, 6>(a);
     return hipErrorInvalidValue;
 }
 
