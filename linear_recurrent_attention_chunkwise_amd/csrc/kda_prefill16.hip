@@ -108,15 +108,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64
                                              0x00020000);
 }
 
-// 16 values -> one [.][token] row of 16 bf16 (two 16-byte stores).
-__device__ __forceinline__ void store_row16(bf16 *row, const float *x) {
-    uint4 *r = reinterpret_cast<uint4 *>(row);
-    r[0] = uint4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
-                 pack_bf16(x[6], x[7])};
-    r[1] = uint4{pack_bf16(x[8], x[9]), pack_bf16(x[10], x[11]), pack_bf16(x[12], x[13]),
-                 pack_bf16(x[14], x[15])};
-}
-
 template <int NCW, int NPW, int NSLOT>
 __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill16Params prm) {
     using Cfg = P16Cfg<NCW, NPW, NSLOT>;
@@ -192,21 +183,10 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         for (int64_t m = 0; m < nchunks; ++m) {
             const int64_t t0 = m * C;
             const char *slot = slot_of(m);
-            // the rest of chunk m's operands; their latency overlaps U below
-            const bf16 *sQG = reinterpret_cast<const bf16 *>(slot + Cfg::S_QG);
-            const float *sGC = reinterpret_cast<const float *>(slot + Cfg::S_GC);
-            Frag<bf16> Qf[NDT];
-            f32x4 gc[NDT];
-#pragma unroll
-            for (int i = 0; i < NDT; ++i) gc[i] = *reinterpret_cast<const f32x4 *>(sGC + 16 * i + 4 * g);
-#pragma unroll
-            for (int i = 0; i < NDT; ++i) Qf[i] = lds_frag(sQG, DP, 16 * i, lane);
-            const Frag<bf16> Pf = lds_frag(reinterpret_cast<const bf16 *>(slot + Cfg::S_P), CP, 0, lane);
             Frag<bf16> Vf;
 #pragma unroll
             for (int e = 0; e < 4; ++e) Vf.v[e] = __builtin_bit_cast(bf16, vr[e]);
             if (m + 1 < nchunks) load_v(t0 + C);
-
             Frag<bf16> Sf[NDT];
 #pragma unroll
             for (int i = 0; i < NDT; ++i) Sf[i] = acc_frag<bf16>(S[i]);
@@ -217,6 +197,19 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             mma32(Ua, Wf[2], Wf[3], Sf[2], Sf[3]);
             mma32(Ub, Wf[4], Wf[5], Sf[4], Sf[5]);
             mma32(Ua, Wf[6], Wf[7], Sf[6], Sf[7]);
+            // The remaining operands of chunk m are read only now (the fence
+            // keeps the compiler from hoisting them), so that they are not
+            // live together with W; U's MFMA latency covers the LDS reads.
+            compiler_fence();
+            const bf16 *sQG = reinterpret_cast<const bf16 *>(slot + Cfg::S_QG);
+            const float *sGC = reinterpret_cast<const float *>(slot + Cfg::S_GC);
+            Frag<bf16> Qf[NDT];
+            f32x4 gc[NDT];
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) gc[i] = *reinterpret_cast<const f32x4 *>(sGC + 16 * i + 4 * g);
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) Qf[i] = lds_frag(sQG, DP, 16 * i, lane);
+            const Frag<bf16> Pf = lds_frag(reinterpret_cast<const bf16 *>(slot + Cfg::S_P), CP, 0, lane);
             const f32x4 U = Ua + Ub;
             const Frag<bf16> Uf = acc_frag<bf16>(U);
             // S <- e^{G_C} S + Kh^T U
@@ -299,13 +292,22 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         float *sGC = reinterpret_cast<float *>(slot + Cfg::S_GC);
         const bool full = t0 + C <= Tn;
 
-        // decays; tokens past the end load as 0 and get alpha = 1
+        // decays, all 32 evaluations independent (no per-token branch, so
+        // their transcendental latencies overlap); tokens past the end load
+        // as 0 and are then given alpha = 1
         float a0[C], a1[C];
 #pragma unroll
         for (int s = 0; s < C; ++s) {
-            const bool valid = full || t0 + s < Tn;
-            a0[s] = valid ? kda_alpha(c2, bf_lo(rz[s])) : 1.0f;
-            a1[s] = valid ? kda_alpha(c2, bf_hi(rz[s])) : 1.0f;
+            a0[s] = kda_alpha(c2, bf_lo(rz[s]));
+            a1[s] = kda_alpha(c2, bf_hi(rz[s]));
+        }
+        if (!full) {
+            const int nvalid = (int)(Tn - t0);
+#pragma unroll
+            for (int s = 0; s < C; ++s) {
+                a0[s] = s < nvalid ? a0[s] : 1.0f;
+                a1[s] = s < nvalid ? a1[s] : 1.0f;
+            }
         }
         const float beta_l = __uint_as_float((uint32_t)(unsigned short)rb << 16);  // lane < 16
 
@@ -327,17 +329,29 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         {
             const float it0 = __builtin_amdgcn_rcpf(F0), it1 = __builtin_amdgcn_rcpf(F1);
             float R0 = 1.f, R1 = 1.f;     // decay over (s, end of chunk]
-            float h0[C], h1[C];
+            // Kh^T rows d0 and d0+1, kept as packed bf16 token pairs
+            uint32_t p0[C / 2], p1[C / 2];
+            float hn0 = 0.f, hn1 = 0.f;   // Kh of token s+1
 #pragma unroll
             for (int s = C - 1; s >= 0; --s) {
-                h0[s] = bf_lo(rk[s]) * R0;
-                h1[s] = bf_hi(rk[s]) * R1;
-                *reinterpret_cast<uint32_t *>(sKc + s * DP + d0) = pack_bf16(h0[s] * it0, h1[s] * it1);
+                const float h0 = bf_lo(rk[s]) * R0, h1 = bf_hi(rk[s]) * R1;
+                *reinterpret_cast<uint32_t *>(sKc + s * DP + d0) = pack_bf16(h0 * it0, h1 * it1);
+                if (s % 2 == 0) {
+                    p0[s / 2] = pack_bf16(h0, hn0);
+                    p1[s / 2] = pack_bf16(h1, hn1);
+                }
+                hn0 = h0;
+                hn1 = h1;
                 R0 *= a0[s];
                 R1 *= a1[s];
             }
-            store_row16(sKhT + d0 * CP, h0);
-            store_row16(sKhT + (d0 + 1) * CP, h1);
+            static_assert(C == 16, "two 16-byte stores per Kh^T row");
+            uint4 *r0 = reinterpret_cast<uint4 *>(sKhT + d0 * CP);
+            uint4 *r1 = reinterpret_cast<uint4 *>(sKhT + (d0 + 1) * CP);
+            r0[0] = uint4{p0[0], p0[1], p0[2], p0[3]};
+            r0[1] = uint4{p0[4], p0[5], p0[6], p0[7]};
+            r1[0] = uint4{p1[0], p1[1], p1[2], p1[3]};
+            r1[1] = uint4{p1[4], p1[5], p1[6], p1[7]};
         }
         // this wave's next chunk streams in while the rest of this one runs
         if (m + NPW < nchunks) load_chunk(t0 + (int64_t)NPW * C);
