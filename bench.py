@@ -1,6 +1,7 @@
 """KDA benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk 16|64] [--no-cpu]
+                    [--no-decode] [--decode-reps R] [--calib-mib M]
 
 A step is one chunkwise prefill over the K3 head-shape workload (B=1, H=96,
 T=4096, dk=dv=128, bf16 inputs, fp32 state, S0 ~ N(0, 0.02^2)) with inputs
@@ -17,12 +18,24 @@ algorithmic bytes one launch must move divided by its average duration:
   decode : B*H*(2*d*d*4 + 4*d*2 + 2 + d*2) + H*4 bytes per step
 The fp64 oracle is timed on the host cores over the full prefill workload
 (``cpu_baseline``), reported in the same unit.  Prints ONE JSON line.
+
+``--calib-mib M`` adds, after the timed region, one elementwise copy of M MiB
+(read M, write M): the reference a hardware byte counter (FETCH_SIZE,
+WRITE_SIZE) is scaled by when the kernels' HBM traffic is measured.
+``roofline.traffic`` is the measured HBM bytes per launch recorded in the
+kernel's summary under profiles/, reported only while the kernel source still
+hashes to the one the counters were taken on (null otherwise).
+
+The default warm-up (several seconds of back-to-back launches) lets the GPU's
+clocks settle before the timed region.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,6 +44,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "linear_recurrent_attention_chunkwise_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "KDA prefill tokens/s (H=96,d=128,bf16) + decode state-updates/s; % roofline"
 
 
@@ -40,6 +55,51 @@ def prefill_bytes(B, T, H, d, esz=2):
 
 def decode_bytes(B, H, d, esz=2):
     return B * H * (2 * d * d * 4 + 4 * d * esz + esz + d * esz) + H * 4
+
+
+def prefill_kernel_name(chunk):
+    """Name of the kernel a default-configured prefill of the K3 workload runs."""
+    return "kda_prefill16_kernel" if chunk == 16 else "kda_prefill_kernel"
+
+
+def source_hash(files):
+    """sha256 over the given kernel sources (in order), as hex."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+KERNEL_SOURCES = {
+    "kda_prefill16_kernel": ["kda_prefill16.hip", "kda_device.h"],
+    "kda_prefill_kernel": ["kda_prefill.hip", "kda_device.h"],
+    "kda_decode_kernel": ["kda_decode.hip", "kda_device.h"],
+}
+
+
+def recorded_traffic(kernel, summary):
+    """HBM bytes per launch from a committed counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    path = os.path.join(PROFILES, summary)
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    mb = re.search(r"^traffic_bytes_per_launch:\s*([0-9]+)", text, re.M)
+    mh = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    if not mb or not mh or mh.group(1) != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return int(mb.group(1))
+
+
+def calibration_copy(torch, mib):
+    """One elementwise copy of `mib` MiB on the current stream (not timed)."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def _events(torch):
@@ -104,12 +164,14 @@ def cpu_baseline(w, inp_cpu):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=8000)
     ap.add_argument("--chunk", type=int, default=16, choices=(16, 64))
     ap.add_argument("--decode-reps", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calib-mib", type=int, default=0,
+                    help="also run one elementwise copy of this many MiB (byte-counter reference)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU (got --gpus {args.gpus}); "
@@ -129,6 +191,8 @@ def main(argv=None):
     ms = time_prefill(torch, kda, inp, args.chunk, args.steps, args.warmup)
     pbytes = prefill_bytes(w.B, w.T, w.H, w.dk)
     achieved = pbytes / (ms * 1e-3) / 1e9
+    pkernel = prefill_kernel_name(args.chunk)
+    ptraffic = recorded_traffic(pkernel, f"{pkernel}_{w.name}_c{args.chunk}.md")
     result = {
         "metric": METRIC,
         "value": w.B * w.T / (ms * 1e-3),
@@ -146,8 +210,8 @@ def main(argv=None):
                                f"dk=dv={w.dk} chunk={args.chunk} bf16 in, fp32 state",
                    "B": w.B, "H": w.H, "T": w.T, "d": w.dk, "chunk": args.chunk},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "kda_prefill_kernel", "bytes_per_launch": pbytes},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": ptraffic,
+                     "kernel": pkernel, "bytes_per_launch": pbytes},
     }
     if not args.no_decode:
         wd = WORKLOADS["k3_decode_bf16"]
@@ -160,8 +224,12 @@ def main(argv=None):
             "us_per_step": dms * 1e3,
             "workload": f"{wd.name}: B={wd.B} H={wd.H} d={wd.dk}, {wd.steps} steps, fp32 state",
             "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dach / HBM_PEAK_GBS, "traffic": None,
+                         "frac": dach / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic("kda_decode_kernel",
+                                                     f"kda_decode_kernel_{wd.name}.md"),
                          "kernel": "kda_decode_kernel", "bytes_per_launch": dbytes}}
+    if args.calib_mib > 0:
+        calibration_copy(torch, args.calib_mib)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, inp_cpu)
     print(json.dumps(result), flush=True)
