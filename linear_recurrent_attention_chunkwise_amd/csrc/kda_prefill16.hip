@@ -16,14 +16,16 @@
 //    S-dependent chain: U = T diag(beta) V - W S, O = Q^ S + P U,
 //    S <- e^{G_C} S + Kh^T U.  Each chain wave loads its own 16 columns of V
 //    straight into MFMA fragments.
-//  Slot hand-off uses two LDS counters per slot: `ready` (set by the prep
-//  wave to u+1 once the slot holds its u-th chunk) and `done` (bumped once
-//  per chain wave, from one lane, after it has read the slot into
-//  registers).  A prep wave waits for done >= NCW*u before writing the u-th
-//  use of a slot; chain waves wait for ready >= u+1.  Production of chunk m
-//  only depends on consumption of chunk m - NSLOT, so the hand-off cannot
-//  deadlock; every wait is additionally bounded.  A SIMD hosts one prep wave
-//  (VALU-bound) and one chain wave (MFMA/LDS-latency-bound), which overlap.
+//  Slot hand-off uses LDS counters: `ready[slot]` (stored by the prep wave
+//  as u+1 once the slot holds its u-th chunk) and `done[slot][chain wave]`
+//  (stored by each chain wave as u+1 once it has issued every read of the
+//  slot's u-th use; a wave's LDS operations execute in order, so a later
+//  write by a prep wave cannot overtake them).  A prep wave waits until every
+//  chain wave's count for the slot is >= u before writing its u-th use; chain
+//  waves wait for ready >= u+1.  Production of chunk m only depends on
+//  consumption of chunk m - NSLOT, so the hand-off cannot deadlock; every
+//  wait is additionally bounded.  Each SIMD hosts one chain wave and two prep
+//  waves, whose work overlaps.
 //
 // With one chunk per 16-token sub-tile, every decay factor can be referred to
 // the chunk start, G_r = sum_{s<=r} g_s:
@@ -72,11 +74,12 @@ struct P16Cfg {
     static constexpr int W_KC = 0;                          // Kc    [C][DP]
     static constexpr int W_BETA = W_KC + C * DP * 2;        // beta  [C] fp32
     static constexpr int SCR = (W_BETA + C * 4 + 15) / 16 * 16;
-    static constexpr int OFF_FLAGS = 0;                     // ready[NSLOT], done[NSLOT]
-    static constexpr int OFF_SLOTS = 64;
+    static constexpr int OFF_FLAGS = 0;                     // ready[8], done[NSLOT][NCW]
+    static constexpr int OFF_DONE = 32;
+    static constexpr int OFF_SLOTS = 128;
     static constexpr int OFF_SCR = OFF_SLOTS + NSLOT * SLOT;
     static constexpr int LDS_BYTES = OFF_SCR + NPW * SCR;
-    static_assert(2 * NSLOT * 4 <= 64, "flag area");
+    static_assert(NSLOT <= 8 && OFF_DONE + NSLOT * NCW * 4 <= OFF_SLOTS, "flag area");
     static_assert(NCW + NPW <= 16, "workgroup size");
     static_assert(SLOT % 16 == 0 && SCR % 16 == 0, "alignment");
     static_assert(LDS_BYTES <= 150 * 1024, "LDS budget");
@@ -108,6 +111,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64
                                              0x00020000);
 }
 
+// 16 values -> one [.][token] row of 16 bf16 (two 16-byte stores).
+__device__ __forceinline__ void store_row16(bf16 *row, const float *x) {
+    uint4 *r = reinterpret_cast<uint4 *>(row);
+    r[0] = uint4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
+                 pack_bf16(x[6], x[7])};
+    r[1] = uint4{pack_bf16(x[8], x[9]), pack_bf16(x[10], x[11]), pack_bf16(x[12], x[13]),
+                 pack_bf16(x[14], x[15])};
+}
+
 template <int NCW, int NPW, int NSLOT>
 __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill16Params prm) {
     using Cfg = P16Cfg<NCW, NPW, NSLOT>;
@@ -115,7 +127,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
                   NDT = D / 16;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
     int *ready = reinterpret_cast<int *>(smem + Cfg::OFF_FLAGS);
-    int *done = ready + NSLOT;
+    int *done = reinterpret_cast<int *>(smem + Cfg::OFF_DONE);   // [slot][chain wave]
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wave-uniform by construction; readfirstlane lets the compiler keep it
@@ -137,7 +149,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
     const int64_t bbase = b * Tn * H + h;
     const int64_t nchunks = (Tn + C - 1) / C;
 
-    if (tid < 2 * NSLOT) ready[tid] = 0;
+    if (tid < Cfg::OFF_SLOTS / 4) ready[tid] = 0;   // every flag
     __syncthreads();
 
     if (wave < NCW) {
@@ -165,79 +177,101 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
                 vr[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, (4 * g + e) * (int)row_bytes + 2 * n, 0, 0);
         };
         if (nchunks > 0) load_v(0);
-        auto slot_of = [&](int64_t m) { return smem + Cfg::OFF_SLOTS + (int)(m % NSLOT) * Cfg::SLOT; };
-        // W, T diag(beta) and Kh^T fragments of chunk m (read one chunk ahead)
-        Frag<bf16> Wf[NDT], Kf[NDT], Tf;
-        auto read_wtk = [&](int64_t m) {
-            wait_at_least(&ready[m % NSLOT], (int)(m / NSLOT) + 1);
-            const char *slot = slot_of(m);
-            const bf16 *sWn = reinterpret_cast<const bf16 *>(slot + Cfg::S_WN);
-            const bf16 *sKhT = reinterpret_cast<const bf16 *>(slot + Cfg::S_KHT);
-#pragma unroll
-            for (int i = 0; i < NDT; ++i) Wf[i] = lds_frag(sWn, DP, 16 * i, lane);
-            Tf = lds_frag(reinterpret_cast<const bf16 *>(slot + Cfg::S_TB), CP, 0, lane);
-#pragma unroll
-            for (int i = 0; i < NDT; ++i) Kf[i] = lds_frag(sKhT + 16 * i * CP, CP, 0, lane);
+        // per-lane byte offsets of the fragment reads, fixed over chunks; a
+        // chunk adds its slot's (uniform) byte offset once per tile layout
+        const int offDP = ((lane & 15) * DP + 4 * (lane >> 4)) * 2;   // [.][DP] tiles
+        const int offCP = ((lane & 15) * CP + 4 * (lane >> 4)) * 2;   // [.][CP] tiles
+        const int offG = 16 * g;                                       // e^{G_C}[4g..4g+3]
+        auto frag_at = [](const char *p) {
+            Frag<bf16> f;
+            f.v = *reinterpret_cast<const bf16x4 *>(p);
+            return f;
         };
-        if (nchunks > 0) read_wtk(0);
+        // W, T diag(beta) and Kh^T fragments of a chunk (read one chunk ahead)
+        Frag<bf16> Wf[NDT], Kf[NDT], Tf;
+        auto read_wtk = [&](int sl, int use) {
+            wait_at_least(&ready[sl], use + 1);
+            const int off = Cfg::OFF_SLOTS + sl * Cfg::SLOT;
+            const char *pd = smem + off + offDP;
+            const char *pc = smem + off + offCP;
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) Wf[i] = frag_at(pd + Cfg::S_WN + 32 * i);
+            Tf = frag_at(pc + Cfg::S_TB);
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) Kf[i] = frag_at(pc + Cfg::S_KHT + 32 * CP * i);
+        };
+        if (nchunks > 0) read_wtk(0, 0);
+        int sl = 0, use = 0;   // slot and use of chunk m
         for (int64_t m = 0; m < nchunks; ++m) {
             const int64_t t0 = m * C;
-            const char *slot = slot_of(m);
+            const int off = Cfg::OFF_SLOTS + sl * Cfg::SLOT;
+            int sl1 = sl + 1, use1 = use;
+            if (sl1 == NSLOT) { sl1 = 0; ++use1; }
+            // (1) chunk m's remaining operands: the decay e^{G_C} (needed by
+            // the state update) and Q^, P (needed by the output only)
+            const char *pd = smem + off + offDP;
+            const char *pc = smem + off + offCP;
+            const char *pg = smem + off + Cfg::S_GC + offG;
+            f32x4 gc[NDT];
+            Frag<bf16> Qf[NDT];
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) gc[i] = *reinterpret_cast<const f32x4 *>(pg + 64 * i);
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) Qf[i] = frag_at(pd + Cfg::S_QG + 32 * i);
+            const Frag<bf16> Pf = frag_at(pc + Cfg::S_P);
+            // Every read of slot m has now been issued.  A wave's LDS operations
+            // execute in order, so a prep wave that sees this count and then
+            // writes the slot writes after these reads have executed: no wait
+            // for the data to arrive is needed before releasing the slot.
+            compiler_fence();
+            __hip_atomic_store(&done[sl * NCW + wave], use + 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+            compiler_fence();
             Frag<bf16> Vf;
 #pragma unroll
             for (int e = 0; e < 4; ++e) Vf.v[e] = __builtin_bit_cast(bf16, vr[e]);
             if (m + 1 < nchunks) load_v(t0 + C);
+            __builtin_amdgcn_sched_barrier(0);
+            // (2) U = T diag(beta) V - W S  (two accumulators halve the dependent chain)
             Frag<bf16> Sf[NDT];
 #pragma unroll
             for (int i = 0; i < NDT; ++i) Sf[i] = acc_frag<bf16>(S[i]);
-            // U = T diag(beta) V - W S  (two accumulators halve the dependent chain)
             f32x4 Ua = {0.f, 0.f, 0.f, 0.f}, Ub = {0.f, 0.f, 0.f, 0.f};
             mma16(Ua, Tf, Vf);
             mma32(Ub, Wf[0], Wf[1], Sf[0], Sf[1]);
             mma32(Ua, Wf[2], Wf[3], Sf[2], Sf[3]);
             mma32(Ub, Wf[4], Wf[5], Sf[4], Sf[5]);
             mma32(Ua, Wf[6], Wf[7], Sf[6], Sf[7]);
-            // The remaining operands of chunk m are read only now (the fence
-            // keeps the compiler from hoisting them), so that they are not
-            // live together with W; U's MFMA latency covers the LDS reads.
-            compiler_fence();
-            const bf16 *sQG = reinterpret_cast<const bf16 *>(slot + Cfg::S_QG);
-            const float *sGC = reinterpret_cast<const float *>(slot + Cfg::S_GC);
-            Frag<bf16> Qf[NDT];
-            f32x4 gc[NDT];
-#pragma unroll
-            for (int i = 0; i < NDT; ++i) gc[i] = *reinterpret_cast<const f32x4 *>(sGC + 16 * i + 4 * g);
-#pragma unroll
-            for (int i = 0; i < NDT; ++i) Qf[i] = lds_frag(sQG, DP, 16 * i, lane);
-            const Frag<bf16> Pf = lds_frag(reinterpret_cast<const bf16 *>(slot + Cfg::S_P), CP, 0, lane);
-            const f32x4 U = Ua + Ub;
-            const Frag<bf16> Uf = acc_frag<bf16>(U);
-            // S <- e^{G_C} S + Kh^T U
+            Frag<bf16> Uf;
+            {
+                const uint32_t lo = pack_bf16(Ua[0] + Ub[0], Ua[1] + Ub[1]);
+                const uint32_t hi = pack_bf16(Ua[2] + Ub[2], Ua[3] + Ub[3]);
+                Uf.v = __builtin_bit_cast(bf16x4, (uint64_t)lo | ((uint64_t)hi << 32));
+            }
+            // (3) S <- e^{G_C} S + Kh^T U
 #pragma unroll
             for (int i = 0; i < NDT; ++i) {
                 S[i] *= gc[i];
                 mma16(S[i], Kf[i], Uf);
             }
-            // O = Q^ S_old + P U
+            __builtin_amdgcn_sched_barrier(0);
+            // (4) chunk m+1's W, T diag(beta), Kh^T, read while O is formed
+            if (m + 1 < nchunks) read_wtk(sl1, use1);
+            // (5) O = Q^ S_old + P U
             f32x4 Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
             mma32(Oa, Qf[0], Qf[1], Sf[0], Sf[1]);
             mma32(Ob, Qf[2], Qf[3], Sf[2], Sf[3]);
             mma32(Oa, Qf[4], Qf[5], Sf[4], Sf[5]);
             mma32(Ob, Qf[6], Qf[7], Sf[6], Sf[7]);
             mma16(Oa, Pf, Uf);
-            // every read of slot m has been consumed by the MFMAs above; release
-            // it (one increment per wave: an add from every lane would count 64)
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (lane == 0)
-                __hip_atomic_fetch_add(&done[m % NSLOT], 1, __ATOMIC_RELEASE,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (m + 1 < nchunks) read_wtk(m + 1);
             const f32x4 O = Oa + Ob;
             const auto ors = make_rsrc(prm.o + base + t0 * tok_stride + jw, chunk_rows(t0) * row_bytes);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (bf16)O[e]), ors,
                                                       (4 * g + e) * (int)row_bytes + 2 * n, 0, 0);
+            sl = sl1;
+            use = use1;
         }
         float *st = prm.S_T + bh * (int64_t)(D * D);
 #pragma unroll
@@ -311,7 +345,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         }
         const float beta_l = __uint_as_float((uint32_t)(unsigned short)rb << 16);  // lane < 16
 
-        wait_at_least(&done[s_], NCW * use);   // every chain wave has read the previous use
+        // every chain wave has read the previous use of the slot
+#pragma unroll
+        for (int w = 0; w < NCW; ++w) wait_at_least(&done[s_ * NCW + w], use);
 
         // ---- decay factors and operands (lane = channel pair d0, d0+1) ------
         float F0 = 1.f, F1 = 1.f;
