@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -110,7 +110,9 @@ kda_status kda_prefill(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
  * fixed by the caller (`dv_per_block` in {16, 32, 64, 128}, dividing dv; 0
  * picks automatically).  Value columns of the state evolve independently, so
  * every choice gives the same result up to rounding order; it only changes
- * how the work is spread over the GPU.
+ * how the work is spread over the GPU.  With dk = 128, chunk 64 runs 32 or
+ * 64 columns per workgroup (bf16 only); other values return
+ * KDA_ERR_UNSUPPORTED.
  */
 kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
                           int64_t dv, int32_t chunk,
@@ -119,6 +121,46 @@ kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk
                           void *o, float *S_T,
                           void *workspace, size_t workspace_bytes, void *stream,
                           int32_t dv_per_block);
+
+/*
+ * Prefill over N variable-length sequences packed along one token axis, with
+ * optional state checkpoints.  The state is "kept persistent per request and
+ * layer", and a reused prefix is only valid together with the KDA state
+ * checkpoint taken at the same token boundary ("Kimi K3 Open Weights: What Is
+ * Actually New ...", section "Why '104B active' still understates the systems
+ * problem"); this entry point produces those checkpoints as it goes.
+ *
+ *   cu_seqlens : DEVICE int64 [N+1], 8-byte aligned.  Sequence i is tokens
+ *                [cu_seqlens[i], cu_seqlens[i+1]) of the packing.  Expected:
+ *                cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = T_total
+ *                (not checked on the host; the kernels clamp every range into
+ *                [0, T_total], so malformed offsets cannot cause an access
+ *                outside the tensors).
+ *   in : q, k, z [T_total,H,dk], v [T_total,H,dv], beta [T_total,H] (dtype);
+ *        A [H] fp32; S0 [N,H,dk,dv] fp32 per sequence, or NULL (zeros).
+ *   out: o [T_total,H,dv] (dtype); S_T [N,H,dk,dv] fp32, the state after each
+ *        sequence's last token (S_T may be S0 itself).
+ *   ckpt_every : 0 for no checkpoints, else a positive multiple of `chunk`.
+ *        For sequence i of length L_i, checkpoint j = 1 .. floor(L_i /
+ *        ckpt_every) is the state after token j*ckpt_every - 1 of the
+ *        sequence, written to row  R_i + j - 1  of ckpt [n_ckpt,H,dk,dv]
+ *        (fp32), where R_i = sum over earlier sequences of floor(L / ckpt_every).
+ *        Rows at or beyond n_ckpt are not written.  ckpt must not overlap any
+ *        other argument.
+ * All other conventions (dtype, sizes, alignment, aliasing, errors, the
+ * dv_per_block split) are those of kda_prefill_ex; each sequence's result is
+ * that of kda_prefill on the sequence alone.  Exception: with checkpoints,
+ * bf16 with dk = 128 and chunk 64 runs 32 value columns per workgroup (0
+ * picks it; 64 returns KDA_ERR_UNSUPPORTED).
+ */
+kda_status kda_prefill_varlen(int dtype, int64_t N, int64_t T_total, int64_t H,
+                              int64_t dk, int64_t dv, int32_t chunk,
+                              const int64_t *cu_seqlens,
+                              const void *q, const void *k, const void *v, const void *z,
+                              const void *beta, const float *A, const float *S0,
+                              void *o, float *S_T,
+                              int32_t ckpt_every, float *ckpt, int64_t n_ckpt,
+                              void *stream, int32_t dv_per_block);
 
 /*
  * One fused recurrent decode step for B sequences (the "KDA decode" half of

@@ -6,8 +6,8 @@ binding over it: torch supplies device memory and streams, every arithmetic
 step runs in the library.  There is no CPU fallback; calling into the binding
 without a built library or without a GPU raises.
 """
-from .kda import (KDAError, abi_version, decode_step, library_path, prefill,
-                  prefill_workspace_size)
+from .kda import (KDAError, abi_version, checkpoint_rows, decode_step, library_path, prefill,
+                  prefill_varlen, prefill_workspace_size)
 
-__all__ = ["KDAError", "abi_version", "decode_step", "library_path", "prefill",
-           "prefill_workspace_size"]
+__all__ = ["KDAError", "abi_version", "checkpoint_rows", "decode_step", "library_path",
+           "prefill", "prefill_varlen", "prefill_workspace_size"]

@@ -64,44 +64,69 @@ size_t kda_prefill_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, in
     return 0;
 }
 
-kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                          int32_t chunk, const void *q, const void *k, const void *v,
-                          const void *z, const void *beta, const float *A, const float *S0,
-                          void *o, float *S_T, void *workspace, size_t workspace_bytes,
-                          void *stream, int32_t dv_per_block) {
-    (void)workspace;
-    (void)workspace_bytes;
-    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+}  // extern "C"
+
+namespace {
+
+// Shared validation and dispatch of the prefill entry points.  `cu` == NULL:
+// dense [B, T, H, d]; otherwise B packed sequences over T tokens.
+kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                        int32_t chunk, const int64_t *cu, const void *q, const void *k,
+                        const void *v, const void *z, const void *beta, const float *A,
+                        const float *S0, void *o, float *S_T, int32_t ckpt_every,
+                        float *ckpt, int64_t n_ckpt, void *stream, int32_t dv_per_block) {
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || n_ckpt < 0 || ckpt_every < 0)
+        return KDA_ERR_SHAPE;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (dk != dv || (dk != 16 && dk != 128)) return KDA_ERR_UNSUPPORTED;
     if (chunk != 16 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+    if (ckpt_every > 0 && ckpt_every % chunk != 0) return KDA_ERR_UNSUPPORTED;
     const int64_t D = dk;
     const int64_t esz = dtype == KDA_BF16 ? 2 : 4;
-    int64_t bt, bth, nin, nstate, bh;
-    if (!mul_ok(B, T, kMaxElems, &bt) || !mul_ok(bt, H, kMaxElems, &bth) ||
+    const int64_t ntok_seqs = cu ? 1 : B;   // the token axis is shared when packed
+    int64_t bt, bth, nin, nstate, bh, nck = 0;
+    if (!mul_ok(ntok_seqs, T, kMaxElems, &bt) || !mul_ok(bt, H, kMaxElems, &bth) ||
         !mul_ok(bth, D, kMaxElems / 4, &nin) || !mul_ok(B, H, kMaxElems, &bh) ||
         !mul_ok(bh, D * D, kMaxElems / 4, &nstate))
         return KDA_ERR_SHAPE;
+    int64_t nckh = 0;
+    if (ckpt_every > 0 && (!mul_ok(n_ckpt, H, kMaxElems, &nckh) ||
+                           !mul_ok(nckh, D * D, kMaxElems / 4, &nck)))
+        return KDA_ERR_SHAPE;
     if (bh > 0x7fffffff / 8) return KDA_ERR_SHAPE;  // grid size
+    const bool want_ckpt = ckpt_every > 0 && n_ckpt > 0;
     int dvb = dv_per_block;
-    if (dvb == 0) dvb = kda::prefill_default_dv_per_block(dtype, B, H, D, chunk);
+    if (dvb == 0) {
+        dvb = kda::prefill_default_dv_per_block(dtype, B, H, D, chunk);
+        if (want_ckpt && !kda::prefill16_supported(dtype, D, chunk, dvb) &&
+            !kda::prefill_ckpt_supported(dtype, D, chunk, dvb))
+            dvb /= 2;
+    }
     const bool role_split = kda::prefill16_supported(dtype, D, chunk, dvb);
     if (dvb <= 0 || D % dvb != 0 || (!role_split && !kda::prefill_supported(dtype, D, chunk, dvb)))
         return KDA_ERR_UNSUPPORTED;
+    if (want_ckpt && !role_split && !kda::prefill_ckpt_supported(dtype, D, chunk, dvb))
+        return KDA_ERR_UNSUPPORTED;
     if (!A || !S_T) return KDA_ERR_NULL;
     if (bth > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL;
-    const void *ptrs[] = {q, k, v, z, beta, A, S0, o, S_T};
+    if (ckpt_every > 0 && n_ckpt > 0 && !ckpt) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, z, beta, A, S0, o, S_T, ckpt};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    if (cu && ((uintptr_t)cu & 7u) != 0) return KDA_ERR_MISALIGNED;
     const Range rq = range_of(q, nin * esz), rk = range_of(k, nin * esz),
                 rv = range_of(v, nin * esz), rz = range_of(z, nin * esz),
                 rb = range_of(beta, bth * esz), rA = range_of(A, H * 4),
                 rS0 = range_of(S0, nstate * 4), ro = range_of(o, nin * esz),
-                rST = range_of(S_T, nstate * 4);
-    const Range ins[] = {rq, rk, rv, rz, rb, rA};
+                rST = range_of(S_T, nstate * 4),
+                rcu = range_of(cu, cu ? (B + 1) * 8 : 0),
+                rck = range_of(ckpt_every > 0 ? ckpt : nullptr, nck * 4);
+    const Range ins[] = {rq, rk, rv, rz, rb, rA, rcu};
     for (const Range &r : ins)
-        if (overlaps(ro, r) || overlaps(rST, r)) return KDA_ERR_ALIAS;
-    if (overlaps(ro, rS0) || overlaps(ro, rST)) return KDA_ERR_ALIAS;
+        if (overlaps(ro, r) || overlaps(rST, r) || overlaps(rck, r)) return KDA_ERR_ALIAS;
+    if (overlaps(ro, rS0) || overlaps(ro, rST) || overlaps(rck, rS0) || overlaps(rck, ro) ||
+        overlaps(rck, rST))
+        return KDA_ERR_ALIAS;
     if (overlaps(rST, rS0) && (const void *)S_T != (const void *)S0) return KDA_ERR_ALIAS;
     if (bh == 0) return KDA_OK;
 
@@ -110,9 +135,39 @@ kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk
     a.dv_per_block = dvb;
     a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.A = A; a.S0 = S0;
     a.o = o; a.S_T = S_T;
+    a.cu_seqlens = cu;
+    a.ckpt_every = ckpt_every > 0 && n_ckpt > 0 ? ckpt_every : 0;
+    a.ckpt = a.ckpt_every > 0 ? ckpt : nullptr;
+    a.n_ckpt = n_ckpt;
     a.stream = (hipStream_t)stream;
     const hipError_t err = role_split ? kda::launch_prefill16(a) : kda::launch_prefill(a);
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                          int32_t chunk, const void *q, const void *k, const void *v,
+                          const void *z, const void *beta, const float *A, const float *S0,
+                          void *o, float *S_T, void *workspace, size_t workspace_bytes,
+                          void *stream, int32_t dv_per_block) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return prefill_impl(dtype, B, T, H, dk, dv, chunk, nullptr, q, k, v, z, beta, A, S0, o, S_T,
+                        0, nullptr, 0, stream, dv_per_block);
+}
+
+kda_status kda_prefill_varlen(int dtype, int64_t N, int64_t T_total, int64_t H, int64_t dk,
+                              int64_t dv, int32_t chunk, const int64_t *cu_seqlens,
+                              const void *q, const void *k, const void *v, const void *z,
+                              const void *beta, const float *A, const float *S0, void *o,
+                              float *S_T, int32_t ckpt_every, float *ckpt, int64_t n_ckpt,
+                              void *stream, int32_t dv_per_block) {
+    if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
+    return prefill_impl(dtype, N, T_total, H, dk, dv, chunk, cu_seqlens, q, k, v, z, beta, A,
+                        S0, o, S_T, ckpt_every, ckpt, n_ckpt, stream, dv_per_block);
 }
 
 kda_status kda_prefill(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,

@@ -124,6 +124,37 @@ __device__ __forceinline__ Frag<TO> frag_scaled(const Frag<TO> &f, const f32x4 &
     return r;
 }
 
+// Raw buffer resource over [p, p + bytes): loads past the end return 0 and
+// stores past the end are dropped, which masks a partial last chunk.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// ------------------------------------------------------- sequences ----
+
+// Token range of sequence b: dense layout (cu == NULL: b*T .. b*T+T) or the
+// packed layout [cu[b], cu[b+1]), clamped into [0, T] so that malformed
+// offsets can never move an access outside the tensors.
+struct SeqRange {
+    int64_t start, len;
+};
+__device__ __forceinline__ SeqRange seq_range(const int64_t *cu, int64_t b, int64_t T) {
+    if (!cu) return SeqRange{b * T, T};
+    int64_t lo = cu[b], hi = cu[b + 1];
+    lo = lo < 0 ? 0 : (lo > T ? T : lo);
+    hi = hi < lo ? lo : (hi > T ? T : hi);
+    return SeqRange{lo, hi - lo};
+}
+
+// First checkpoint row of sequence b: the rows of earlier sequences come
+// first, floor(len / every) per sequence.
+__device__ __forceinline__ int64_t ckpt_row0(const int64_t *cu, int64_t b, int64_t T, int every) {
+    int64_t r = 0;
+    for (int64_t j = 0; j < b; ++j) r += seq_range(cu, j, T).len / every;
+    return r;
+}
+
 // Workgroup barrier that waits for LDS traffic only: outstanding global loads
 // (prefetches of the next chunk) stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {

@@ -13,13 +13,22 @@ namespace kda {
 
 struct PrefillArgs {
     int dtype;          // KDA_F32 / KDA_BF16
-    int64_t B, T, H, D; // dk == dv == D
+    int64_t B, T, H, D; // dk == dv == D; B sequences (dense: of T tokens each)
     int chunk;
     int dv_per_block;   // value columns per workgroup (16 * waves)
     const void *q, *k, *v, *z, *beta;
     const float *A, *S0;
     void *o;
     float *S_T;
+    // Packed variable-length mode: sequence b holds tokens
+    // [cu_seqlens[b], cu_seqlens[b+1]) of a [T, H, d] packing (T = total
+    // tokens).  NULL: dense [B, T, H, d].
+    const int64_t *cu_seqlens;
+    // State checkpoints: every ckpt_every tokens of a sequence (0 = none),
+    // rows of ckpt [n_ckpt, H, D, D] in sequence order.
+    int ckpt_every;
+    float *ckpt;
+    int64_t n_ckpt;
     hipStream_t stream;
 };
 
@@ -38,6 +47,8 @@ bool prefill_supported(int dtype, int64_t D, int chunk, int dv_per_block);
 // Default value columns per workgroup for these sizes.
 int prefill_default_dv_per_block(int dtype, int64_t B, int64_t H, int64_t D, int chunk);
 hipError_t launch_prefill(const PrefillArgs &a);
+// Whether the general kernel takes state checkpoints for this configuration.
+bool prefill_ckpt_supported(int dtype, int64_t D, int chunk, int dv_per_block);
 // Role-split variant for bf16, D = 128, chunk 16 (kda_prefill16.hip).
 bool prefill16_supported(int dtype, int64_t D, int chunk, int dv_per_block);
 hipError_t launch_prefill16(const PrefillArgs &a);

@@ -46,8 +46,12 @@ struct PrefillParams {
     const float *A, *S0;
     void *o;
     float *S_T;
-    int64_t T, H;
+    int64_t T, H;   // T: tokens per sequence (dense) or in the packing (cu != NULL)
     int nsplit;
+    const int64_t *cu;   // packed sequence offsets, or NULL
+    float *ckpt;         // state checkpoints [n_ckpt, H, D, D], or NULL
+    int64_t n_ckpt;
+    int ckpt_every;      // tokens between checkpoints (0: none)
 };
 
 template <typename T, int D, int C, int NW>
@@ -158,7 +162,7 @@ __device__ __forceinline__ void contract_lds_frag(f32x4 &acc, const T *A, int ld
     }
 }
 
-template <typename T, int D, int C, int NW>
+template <typename T, int D, int C, int NW, bool CKPT>
 __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm) {
     using Cfg = PrefillCfg<T, D, C, NW>;
     using Pair = typename PairOf<T>::type;
@@ -197,8 +201,10 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
     if (nblk % 8 == 0) x = (x % 8) * (nblk / 8) + x / 8;
     const int64_t bh = x / prm.nsplit;
     const int split = (int)(x % prm.nsplit);
-    const int64_t H = prm.H, Tn = prm.T;
+    const int64_t H = prm.H;
     const int64_t b = bh / H;
+    const SeqRange sr = seq_range(prm.cu, b, prm.T);
+    const int64_t Tn = sr.len;
     const int h = (int)(bh % H);
     const int j0 = split * DVB;         // first value column of the workgroup
     const int jw = j0 + 16 * wave;      // first value column of this wave
@@ -210,8 +216,8 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
     const T *gbeta = static_cast<const T *>(prm.beta);
     T *go = static_cast<T *>(prm.o);
     const int64_t tok_stride = H * D;               // elements between tokens
-    const int64_t base = (b * Tn * H + h) * D;       // token 0 of (b, h)
-    const int64_t bbase = b * Tn * H + h;            // beta of token 0
+    const int64_t base = (sr.start * H + h) * D;     // token 0 of (b, h)
+    const int64_t bbase = sr.start * H + h;          // beta of token 0
     const float c2 = -__builtin_amdgcn_exp2f(prm.A[h] * kLog2e) * kLog2e;
 
     // ---- state slice: S[16 i + 4 g + e][jw + n] -------------------------
@@ -264,12 +270,22 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
     };
 
     const int64_t nchunks = (Tn + C - 1) / C;
-    if (nchunks > 0) load_chunk(0);
+    // Wide workgroups prefetch the next chunk into registers during the
+    // current one.  With one or two waves each thread owns so many gate items
+    // that the prefetch would not fit the register file; those variants load
+    // each chunk at the top of its step instead.
+    constexpr bool kPrefetch = NW >= 4;
+    if (kPrefetch && nchunks > 0) load_chunk(0);
 
     f32x4 Ut[NP];   // U~ rows of each sub-tile for this wave's columns
 
+    // state checkpoints: the state after every ckpt_every tokens
+    const int every = CKPT ? prm.ckpt_every : 0;   // CKPT: prm.ckpt set, every > 0
+    int64_t ck_row = every > 0 ? ckpt_row0(prm.cu, b, prm.T, every) : 0;
+    int64_t ck_next = every;   // token count of the next checkpoint
     for (int64_t ch = 0; ch < nchunks; ++ch) {
         const int64_t t0 = ch * C;
+        if (!kPrefetch) load_chunk(t0);
 
         // ================= phase A: gate, decay factors, operands ==========
         float fl0[IPT][SEGLEN], fl1[IPT][SEGLEN], al0[IPT][SEGLEN], al1[IPT][SEGLEN];
@@ -404,7 +420,7 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
         lds_barrier();
 
         // prefetch the next chunk while this one is processed
-        if (ch + 1 < nchunks) load_chunk(t0 + C);
+        if (kPrefetch && ch + 1 < nchunks) load_chunk(t0 + C);
 
         // ================= phase B: P and L sub-tile blocks ================
         f32x4 accP[Cfg::BPW], accL[Cfg::BPW];
@@ -569,6 +585,23 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
             }
         }
         lds_barrier();
+        // state checkpoint after this chunk (S is final for the chunk here)
+        if (CKPT && t0 + C == ck_next) {
+            if (t0 + C <= Tn && ck_row < prm.n_ckpt) {
+                // one lane offset, row offsets as scalars: no per-store addresses
+                const auto crs = make_rsrc(prm.ckpt + (ck_row * H + h) * (int64_t)(D * D),
+                                           (int64_t)(D * D) * 4);
+                const int voff = (4 * g * D + jw + n) * 4;
+#pragma unroll
+                for (int i = 0; i < NDT; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[i][e]), crs, voff,
+                                                              (16 * i + e) * D * 4, 0);
+            }
+            ++ck_row;
+            ck_next += every;
+        }
     }
 
     // ---- final state ------------------------------------------------------
@@ -582,21 +615,43 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
 // ---------------------------------------------------------------- host ----
 
 template <typename T, int D, int C, int NW>
+constexpr bool ckpt_variant_supported() {
+    return !(sizeof(T) == 2 && D == 128 && C == 64 && NW == 4);
+}
+
+bool prefill_ckpt_supported(int dtype, int64_t D, int chunk, int dv_per_block) {
+    return !(dtype == 1 && D == 128 && chunk == 64 && dv_per_block == 64);
+}
+
+template <typename T, int D, int C, int NW>
 static hipError_t launch_prefill_t(const PrefillArgs &a) {
     PrefillParams prm;
     prm.q = a.q; prm.k = a.k; prm.v = a.v; prm.z = a.z; prm.beta = a.beta;
     prm.A = a.A; prm.S0 = a.S0; prm.o = a.o; prm.S_T = a.S_T;
     prm.T = a.T; prm.H = a.H;
+    prm.cu = a.cu_seqlens; prm.ckpt = a.ckpt; prm.n_ckpt = a.n_ckpt;
+    prm.ckpt_every = a.ckpt_every;
     prm.nsplit = (int)(D / (16 * NW));
     const int64_t nblk = a.B * a.H * prm.nsplit;
-    hipLaunchKernelGGL((kda_prefill_kernel<T, D, C, NW>), dim3((unsigned)nblk), dim3(64 * NW), 0,
-                       a.stream, prm);
+    if (a.ckpt != nullptr && a.ckpt_every > 0) {
+        // The checkpointing build of the 64-token, 64-column bf16 variant
+        // (4 waves, at the register-file limit) produced wrong outputs on
+        // MI355X while its checkpoints and final state were right; it is not
+        // built, and the entry points refuse that combination.
+        if constexpr (ckpt_variant_supported<T, D, C, NW>())
+            hipLaunchKernelGGL((kda_prefill_kernel<T, D, C, NW, true>), dim3((unsigned)nblk),
+                               dim3(64 * NW), 0, a.stream, prm);
+        else
+            return hipErrorInvalidValue;
+    } else
+        hipLaunchKernelGGL((kda_prefill_kernel<T, D, C, NW, false>), dim3((unsigned)nblk),
+                           dim3(64 * NW), 0, a.stream, prm);
     return hipGetLastError();
 }
 
 #define KDA_PREFILL_CASES(X)                                                             \
     X(bf16, 128, 16, 1) X(bf16, 128, 16, 2) X(bf16, 128, 16, 4) X(bf16, 128, 16, 8)        \
-    X(bf16, 128, 64, 1) X(bf16, 128, 64, 2) X(bf16, 128, 64, 4)                            \
+    X(bf16, 128, 64, 2) X(bf16, 128, 64, 4)                                                \
     X(bf16, 16, 16, 1) X(bf16, 16, 64, 1)                                                  \
     X(float, 128, 16, 1) X(float, 128, 16, 2) X(float, 128, 16, 4)                         \
     X(float, 16, 16, 1) X(float, 16, 64, 1)

@@ -13,9 +13,9 @@
 //    m mod NSLOT).
 //  * CHAIN waves (NCW per workgroup, 16 value columns each, fp32 state slice
 //    in registers).  They consume the slots in chunk order and run the
-//    S-dependent chain: U = T diag(beta) V - W S, O = Q^ S + P U,
-//    S <- e^{G_C} S + Kh^T U.  Each chain wave loads its own 16 columns of V
-//    straight into MFMA fragments.
+//    S-dependent chain: S' = e^{G_C} S, U = T diag(beta) V - W~ S',
+//    O = Q~ S' + P U, S <- S' + Kh^T U.  Each chain wave loads its own 16
+//    columns of V straight into MFMA fragments.
 //  Slot hand-off uses LDS counters: `ready[slot]` (stored by the prep wave
 //  as u+1 once the slot holds its u-th chunk) and `done[slot][chain wave]`
 //  (stored by each chain wave as u+1 once it has issued every read of the
@@ -28,13 +28,16 @@
 //  waves, whose work overlaps.
 //
 // With one chunk per 16-token sub-tile, every decay factor can be referred to
-// the chunk start, G_r = sum_{s<=r} g_s:
-//    Q^ = Q * e^G   (row operand of P, and of the inter-chunk read Q^ S)
-//    K^ = K * e^G   (row operand of L, and W = T diag(beta) K^)
-//    Kc = K * e^-G  (column operand of P and L; |Kc| <= e^80 since g >= -5)
-//    Kh = K * e^{G_C - G}   (state update)
-// so P = tril(Q^ Kc^T), L = diag(beta) strict_tril(K^ Kc^T).  The bound
-// e^-80 <= e^G <= 1 over 16 tokens is the range argument of the pages.
+// the chunk end: with G_r = sum_{s<=r} g_s and G_C the chunk total,
+//    Q~ = Q * e^{G - G_C}   (row operand of P; the read O = Q~ (e^{G_C} S))
+//    K~ = K * e^{G - G_C}   (row operand of L; W~ = T diag(beta) K~ = W e^{-G_C})
+//    Kh = K * e^{G_C - G}   (column operand of P and L; the state update)
+// so P = tril(Q~ Kh^T), L = diag(beta) strict_tril(K~ Kh^T).  Over at most 15
+// later tokens of a chunk, 1 <= e^{G - G_C} <= e^75 and e^{-75} <= e^{G_C - G}
+// <= 1, inside bf16 range: the range argument of the pages.  Referring to
+// the end (not the start) makes the factors of a chunk's last token exactly
+// 1, so the diagonal entry q.k of P, which can cancel, is formed from the
+// unrounded inputs for that token (a one-token sequence is exact there).
 //
 // The 16 x 16 inverse T = (I + L)^-1 uses L's nilpotency (L^16 = 0):
 //    T = (I - L)(I + L^2)(I + L^4)(I + L^8),
@@ -52,8 +55,12 @@ struct Prefill16Params {
     const float *A, *S0;
     bf16 *o;
     float *S_T;
-    int64_t T, H;
+    int64_t T, H;   // T: tokens per sequence (dense) or in the packing (cu != NULL)
     int nsplit;
+    const int64_t *cu;   // packed sequence offsets, or NULL
+    float *ckpt;         // state checkpoints [n_ckpt, H, D, D], or NULL
+    int64_t n_ckpt;
+    int ckpt_every;      // tokens between checkpoints (0: none)
 };
 
 template <int NCW, int NPW, int NSLOT>
@@ -63,16 +70,16 @@ struct P16Cfg {
     static constexpr int DP = D + 8;               // [token][d] row stride
     static constexpr int CP = C + 8;               // [d][token] / [token][token] row stride
     // slot: the chain operands of one chunk
-    static constexpr int S_QG = 0;                         // Q^         [C][DP]
-    static constexpr int S_WN = S_QG + C * DP * 2;         // K^, then -W [C][DP]
+    static constexpr int S_QG = 0;                         // Q~         [C][DP]
+    static constexpr int S_WN = S_QG + C * DP * 2;         // K~, then -W~ [C][DP]
     static constexpr int S_KHT = S_WN + C * DP * 2;        // Kh^T       [D][CP]
     static constexpr int S_P = S_KHT + D * CP * 2;         // P          [C][CP]
     static constexpr int S_TB = S_P + C * CP * 2;          // T diag(b)  [C][CP]
     static constexpr int S_GC = S_TB + C * CP * 2;         // e^{G_C}    [D] fp32
     static constexpr int SLOT = S_GC + D * 4;
     // prep-wave scratch
-    static constexpr int W_KC = 0;                          // Kc    [C][DP]
-    static constexpr int W_BETA = W_KC + C * DP * 2;        // beta  [C] fp32
+    static constexpr int W_KH = 0;                          // Kh    [C][DP]
+    static constexpr int W_BETA = W_KH + C * DP * 2;        // beta  [C] fp32
     static constexpr int SCR = (W_BETA + C * 4 + 15) / 16 * 16;
     static constexpr int OFF_FLAGS = 0;                     // ready[8], done[NSLOT][NCW]
     static constexpr int OFF_DONE = 32;
@@ -104,13 +111,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Raw buffer resource over [p, p + bytes): loads past the end return 0 and
-// stores past the end are dropped, which masks a partial last chunk.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
 // 16 values -> one [.][token] row of 16 bf16 (two 16-byte stores).
 __device__ __forceinline__ void store_row16(bf16 *row, const float *x) {
     uint4 *r = reinterpret_cast<uint4 *>(row);
@@ -120,7 +120,7 @@ __device__ __forceinline__ void store_row16(bf16 *row, const float *x) {
                  pack_bf16(x[14], x[15])};
 }
 
-template <int NCW, int NPW, int NSLOT>
+template <int NCW, int NPW, int NSLOT, bool CKPT>
 __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill16Params prm) {
     using Cfg = P16Cfg<NCW, NPW, NSLOT>;
     constexpr int D = Cfg::D, C = Cfg::C, DVB = Cfg::DVB, DP = Cfg::DP, CP = Cfg::CP,
@@ -140,13 +140,15 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
     if (nblk % 8 == 0) x = (x % 8) * (nblk / 8) + x / 8;   // slices of a head share an XCD
     const int64_t bh = x / prm.nsplit;
     const int split = (int)(x % prm.nsplit);
-    const int64_t H = prm.H, Tn = prm.T;
+    const int64_t H = prm.H;
     const int64_t b = bh / H;
     const int h = (int)(bh % H);
+    const SeqRange sr = seq_range(prm.cu, b, prm.T);
+    const int64_t Tn = sr.len;
     const int j0 = split * DVB;
     const int64_t tok_stride = H * D;
-    const int64_t base = (b * Tn * H + h) * D;
-    const int64_t bbase = b * Tn * H + h;
+    const int64_t base = (sr.start * H + h) * D;   // token 0 of (b, h)
+    const int64_t bbase = sr.start * H + h;
     const int64_t nchunks = (Tn + C - 1) / C;
 
     if (tid < Cfg::OFF_SLOTS / 4) ready[tid] = 0;   // every flag
@@ -202,20 +204,46 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         };
         if (nchunks > 0) read_wtk(0, 0);
         int sl = 0, use = 0;   // slot and use of chunk m
+        // state checkpoints: the state after every ckpt_every tokens
+        const int every = CKPT ? prm.ckpt_every : 0;   // CKPT: prm.ckpt set, every > 0
+        int64_t ck_row = every > 0 ? ckpt_row0(prm.cu, b, prm.T, every) : 0;
+        int64_t ck_next = every;   // token count of the next checkpoint
         for (int64_t m = 0; m < nchunks; ++m) {
             const int64_t t0 = m * C;
             const int off = Cfg::OFF_SLOTS + sl * Cfg::SLOT;
             int sl1 = sl + 1, use1 = use;
             if (sl1 == NSLOT) { sl1 = 0; ++use1; }
-            // (1) chunk m's remaining operands: the decay e^{G_C} (needed by
-            // the state update) and Q^, P (needed by the output only)
+            // (1) chunk m's remaining operands: the decay e^{G_C} (applied to S
+            // first) and Q~, P (needed by the output only)
             const char *pd = smem + off + offDP;
             const char *pc = smem + off + offCP;
             const char *pg = smem + off + Cfg::S_GC + offG;
             f32x4 gc[NDT];
-            Frag<bf16> Qf[NDT];
 #pragma unroll
             for (int i = 0; i < NDT; ++i) gc[i] = *reinterpret_cast<const f32x4 *>(pg + 64 * i);
+            Frag<bf16> Vf;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Vf.v[e] = __builtin_bit_cast(bf16, vr[e]);
+            if (m + 1 < nchunks) load_v(t0 + C);
+            __builtin_amdgcn_sched_barrier(0);
+            // (2) S <- e^{G_C} S; U = T diag(beta) V - W~ S, where W~ = W e^{-G_C}
+            // (two accumulators halve the dependent chain)
+            f32x4 Ua = {0.f, 0.f, 0.f, 0.f}, Ub = {0.f, 0.f, 0.f, 0.f};
+            mma16(Ua, Tf, Vf);
+            Frag<bf16> Sf[NDT];
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) {
+                S[i] *= gc[i];
+                Sf[i] = acc_frag<bf16>(S[i]);
+            }
+            mma32(Ub, Wf[0], Wf[1], Sf[0], Sf[1]);
+            mma32(Ua, Wf[2], Wf[3], Sf[2], Sf[3]);
+            mma32(Ub, Wf[4], Wf[5], Sf[4], Sf[5]);
+            mma32(Ua, Wf[6], Wf[7], Sf[6], Sf[7]);
+            // Q~ and P are only needed for the output; reading them now keeps
+            // their registers free while W~ and e^{G_C} are live
+            compiler_fence();
+            Frag<bf16> Qf[NDT];
 #pragma unroll
             for (int i = 0; i < NDT; ++i) Qf[i] = frag_at(pd + Cfg::S_QG + 32 * i);
             const Frag<bf16> Pf = frag_at(pc + Cfg::S_P);
@@ -227,37 +255,35 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             __hip_atomic_store(&done[sl * NCW + wave], use + 1, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
             compiler_fence();
-            Frag<bf16> Vf;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Vf.v[e] = __builtin_bit_cast(bf16, vr[e]);
-            if (m + 1 < nchunks) load_v(t0 + C);
-            __builtin_amdgcn_sched_barrier(0);
-            // (2) U = T diag(beta) V - W S  (two accumulators halve the dependent chain)
-            Frag<bf16> Sf[NDT];
-#pragma unroll
-            for (int i = 0; i < NDT; ++i) Sf[i] = acc_frag<bf16>(S[i]);
-            f32x4 Ua = {0.f, 0.f, 0.f, 0.f}, Ub = {0.f, 0.f, 0.f, 0.f};
-            mma16(Ua, Tf, Vf);
-            mma32(Ub, Wf[0], Wf[1], Sf[0], Sf[1]);
-            mma32(Ua, Wf[2], Wf[3], Sf[2], Sf[3]);
-            mma32(Ub, Wf[4], Wf[5], Sf[4], Sf[5]);
-            mma32(Ua, Wf[6], Wf[7], Sf[6], Sf[7]);
             Frag<bf16> Uf;
             {
                 const uint32_t lo = pack_bf16(Ua[0] + Ub[0], Ua[1] + Ub[1]);
                 const uint32_t hi = pack_bf16(Ua[2] + Ub[2], Ua[3] + Ub[3]);
                 Uf.v = __builtin_bit_cast(bf16x4, (uint64_t)lo | ((uint64_t)hi << 32));
             }
-            // (3) S <- e^{G_C} S + Kh^T U
+            // (3) S <- S + Kh^T U
 #pragma unroll
-            for (int i = 0; i < NDT; ++i) {
-                S[i] *= gc[i];
-                mma16(S[i], Kf[i], Uf);
+            for (int i = 0; i < NDT; ++i) mma16(S[i], Kf[i], Uf);
+            if (CKPT && t0 + C == ck_next) {
+                if (t0 + C <= Tn && ck_row < prm.n_ckpt) {
+                    // one lane offset, row offsets as scalars: no per-store addresses
+                    const auto crs = make_rsrc(prm.ckpt + (ck_row * H + h) * (int64_t)(D * D),
+                                               (int64_t)(D * D) * 4);
+                    const int voff = (4 * g * D + jw + n) * 4;
+#pragma unroll
+                    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[i][e]), crs, voff,
+                                                                  (16 * i + e) * D * 4, 0);
+                }
+                ++ck_row;
+                ck_next += every;
             }
             __builtin_amdgcn_sched_barrier(0);
             // (4) chunk m+1's W, T diag(beta), Kh^T, read while O is formed
             if (m + 1 < nchunks) read_wtk(sl1, use1);
-            // (5) O = Q^ S_old + P U
+            // (5) O = Q~ (e^{G_C} S_old) + P U
             f32x4 Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
             mma32(Oa, Qf[0], Qf[1], Sf[0], Sf[1]);
             mma32(Ob, Qf[2], Qf[3], Sf[2], Sf[3]);
@@ -284,7 +310,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
     // ============================== prep wave ===============================
     const int pw = wave - NCW;
     char *scr = smem + Cfg::OFF_SCR + pw * Cfg::SCR;
-    bf16 *sKc = reinterpret_cast<bf16 *>(scr + Cfg::W_KC);
+    bf16 *sKh = reinterpret_cast<bf16 *>(scr + Cfg::W_KH);
     float *sBeta = reinterpret_cast<float *>(scr + Cfg::W_BETA);
 
     const float c2 = -__builtin_amdgcn_exp2f(prm.A[h] * kLog2e) * kLog2e;
@@ -319,7 +345,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         const int use = (int)(m / NSLOT);
         char *slot = smem + Cfg::OFF_SLOTS + s_ * Cfg::SLOT;
         bf16 *sQG = reinterpret_cast<bf16 *>(slot + Cfg::S_QG);
-        bf16 *sWn = reinterpret_cast<bf16 *>(slot + Cfg::S_WN);   // K^ until W overwrites it
+        bf16 *sWn = reinterpret_cast<bf16 *>(slot + Cfg::S_WN);   // K~ until -W~ overwrites it
         bf16 *sKhT = reinterpret_cast<bf16 *>(slot + Cfg::S_KHT);
         bf16 *sP = reinterpret_cast<bf16 *>(slot + Cfg::S_P);
         bf16 *sTb = reinterpret_cast<bf16 *>(slot + Cfg::S_TB);
@@ -350,59 +376,67 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         for (int w = 0; w < NCW; ++w) wait_at_least(&done[s_ * NCW + w], use);
 
         // ---- decay factors and operands (lane = channel pair d0, d0+1) ------
-        float F0 = 1.f, F1 = 1.f;
-#pragma unroll
-        for (int s = 0; s < C; ++s) {
-            F0 *= a0[s];
-            F1 *= a1[s];
-            *reinterpret_cast<uint32_t *>(sQG + s * DP + d0) =
-                pack_bf16(bf_lo(rq[s]) * F0, bf_hi(rq[s]) * F1);
-            *reinterpret_cast<uint32_t *>(sWn + s * DP + d0) =
-                pack_bf16(bf_lo(rk[s]) * F0, bf_hi(rk[s]) * F1);
-        }
-        sGC[d0] = F0;
-        sGC[d0 + 1] = F1;
+        // Backward over the chunk: R = decay over (s, end of chunk], so that
+        // Kh = K e^{G_C - G} (<= 1), written token-major (scratch, for P and
+        // L) and as Kh^T rows (slot, for the state update).  At the end R is
+        // the decay over the whole chunk, e^{G_C}.
+        float R0 = 1.f, R1 = 1.f;
         {
-            const float it0 = __builtin_amdgcn_rcpf(F0), it1 = __builtin_amdgcn_rcpf(F1);
-            float R0 = 1.f, R1 = 1.f;     // decay over (s, end of chunk]
-            // Kh^T rows d0 and d0+1, kept as packed bf16 token pairs
-            uint32_t p0[C / 2], p1[C / 2];
-            float hn0 = 0.f, hn1 = 0.f;   // Kh of token s+1
+            static_assert(C == 16, "two 16-byte stores per Kh^T row");
+            uint4 *r0 = reinterpret_cast<uint4 *>(sKhT + d0 * CP);
+            uint4 *r1 = reinterpret_cast<uint4 *>(sKhT + (d0 + 1) * CP);
+            uint32_t p0[4], p1[4];       // 8 tokens of Kh^T rows d0, d0+1 as bf16 pairs
+            float hn0 = 0.f, hn1 = 0.f;  // Kh of token s+1
 #pragma unroll
             for (int s = C - 1; s >= 0; --s) {
                 const float h0 = bf_lo(rk[s]) * R0, h1 = bf_hi(rk[s]) * R1;
-                *reinterpret_cast<uint32_t *>(sKc + s * DP + d0) = pack_bf16(h0 * it0, h1 * it1);
+                *reinterpret_cast<uint32_t *>(sKh + s * DP + d0) = pack_bf16(h0, h1);
                 if (s % 2 == 0) {
-                    p0[s / 2] = pack_bf16(h0, hn0);
-                    p1[s / 2] = pack_bf16(h1, hn1);
+                    p0[(s / 2) % 4] = pack_bf16(h0, hn0);
+                    p1[(s / 2) % 4] = pack_bf16(h1, hn1);
+                }
+                if (s % 8 == 0) {   // tokens s .. s+7 complete: one 16-byte store per row
+                    r0[s / 8] = uint4{p0[0], p0[1], p0[2], p0[3]};
+                    r1[s / 8] = uint4{p1[0], p1[1], p1[2], p1[3]};
                 }
                 hn0 = h0;
                 hn1 = h1;
                 R0 *= a0[s];
                 R1 *= a1[s];
             }
-            static_assert(C == 16, "two 16-byte stores per Kh^T row");
-            uint4 *r0 = reinterpret_cast<uint4 *>(sKhT + d0 * CP);
-            uint4 *r1 = reinterpret_cast<uint4 *>(sKhT + (d0 + 1) * CP);
-            r0[0] = uint4{p0[0], p0[1], p0[2], p0[3]};
-            r0[1] = uint4{p0[4], p0[5], p0[6], p0[7]};
-            r1[0] = uint4{p1[0], p1[1], p1[2], p1[3]};
-            r1[1] = uint4{p1[4], p1[5], p1[6], p1[7]};
+        }
+        sGC[d0] = R0;
+        sGC[d0 + 1] = R1;
+        // Forward: e^{G - G_C} = e^{G} / e^{G_C} (in [1, e^75]): Q~ = Q e^{G-G_C},
+        // K~ = K e^{G-G_C}.  For the chunk's last token both factors are exactly 1.
+        {
+            const float ic0 = __builtin_amdgcn_rcpf(R0), ic1 = __builtin_amdgcn_rcpf(R1);
+            float F0 = 1.f, F1 = 1.f;
+#pragma unroll
+            for (int s = 0; s < C; ++s) {
+                F0 *= a0[s];
+                F1 *= a1[s];
+                const float f0 = F0 * ic0, f1 = F1 * ic1;
+                *reinterpret_cast<uint32_t *>(sQG + s * DP + d0) =
+                    pack_bf16(bf_lo(rq[s]) * f0, bf_hi(rq[s]) * f1);
+                *reinterpret_cast<uint32_t *>(sWn + s * DP + d0) =
+                    pack_bf16(bf_lo(rk[s]) * f0, bf_hi(rk[s]) * f1);
+            }
         }
         // this wave's next chunk streams in while the rest of this one runs
         if (m + NPW < nchunks) load_chunk(t0 + (int64_t)NPW * C);
         if (lane < C) sBeta[lane] = beta_l;
         compiler_fence();
 
-        // ---- P^T, L, L^T from Q^, K^, Kc (B-layout results) --------------------
-        // accP[e]  = sum_d Kc[4g+e][d] Q^[n][d]   = P'[n][4g+e]   (P = tril P')
-        // accL[e]  = sum_d K^[4g+e][d] Kc[n][d]   = L'[4g+e][n]
-        // accLT[e] = sum_d Kc[4g+e][d] K^[n][d]   = L'[n][4g+e]   (L = beta strict_tril L')
+        // ---- P^T, L, L^T from Q~, K~, Kh (B-layout results) --------------------
+        // accP[e]  = sum_d Kh[4g+e][d] Q~[n][d]   = P'[n][4g+e]   (P = tril P')
+        // accL[e]  = sum_d K~[4g+e][d] Kh[n][d]   = L'[4g+e][n]
+        // accLT[e] = sum_d Kh[4g+e][d] K~[n][d]   = L'[n][4g+e]   (L = beta strict_tril L')
         f32x4 accP = {0.f, 0.f, 0.f, 0.f}, accL = {0.f, 0.f, 0.f, 0.f},
               accLT = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k32 = 0; k32 < D; k32 += 32) {
-            const Frag<bf16> c0 = lds_frag(sKc, DP, k32, lane), c1 = lds_frag(sKc, DP, k32 + 16, lane);
+            const Frag<bf16> c0 = lds_frag(sKh, DP, k32, lane), c1 = lds_frag(sKh, DP, k32 + 16, lane);
             const Frag<bf16> q0f = lds_frag(sQG, DP, k32, lane), q1f = lds_frag(sQG, DP, k32 + 16, lane);
             const Frag<bf16> h0f = lds_frag(sWn, DP, k32, lane), h1f = lds_frag(sWn, DP, k32 + 16, lane);
             mma32(accP, c0, c1, q0f, q1f);
@@ -453,8 +487,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         for (int e = 0; e < 4; ++e) Tf.v[e] = (bf16)(TT[e] * brow[e]);
         *reinterpret_cast<bf16x4 *>(sTb + n * CP + 4 * g) = Tf.v;
 
-        // ---- W^T = K^^T Tb^T, written as -W rows over K^ ---------------------
-        // A-layout of K^^T for d-tile dt: lane (g,n) holds K^[4g+e][16 dt + n]
+        // ---- W~^T = K~^T Tb^T, written as -W~ rows over K~ -------------------
+        // A-layout of K~^T for d-tile dt: lane (g,n) holds K~[4g+e][16 dt + n]
         // (strided 2-byte reads, conflict-free); a tile is read completely
         // before its W rows overwrite the same columns.
 #pragma unroll
@@ -473,7 +507,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
     }
 }
 
-template <int NCW, int NPW, int NSLOT>
+template <int NCW, int NPW, int NSLOT, bool CKPT>
 static hipError_t launch_p16(const PrefillArgs &a) {
     Prefill16Params prm;
     prm.q = static_cast<const bf16 *>(a.q);
@@ -488,8 +522,12 @@ static hipError_t launch_p16(const PrefillArgs &a) {
     prm.T = a.T;
     prm.H = a.H;
     prm.nsplit = 128 / (16 * NCW);
+    prm.cu = a.cu_seqlens;
+    prm.ckpt = a.ckpt;
+    prm.n_ckpt = a.n_ckpt;
+    prm.ckpt_every = a.ckpt_every;
     const int64_t nblk = a.B * a.H * prm.nsplit;
-    hipLaunchKernelGGL((kda_prefill16_kernel<NCW, NPW, NSLOT>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((kda_prefill16_kernel<NCW, NPW, NSLOT, CKPT>), dim3((unsigned)nblk),
                        dim3(64 * (NCW + NPW)), 0, a.stream, prm);
     return hipGetLastError();
 }
@@ -499,8 +537,11 @@ bool prefill16_supported(int dtype, int64_t D, int chunk, int dv_per_block) {
 }
 
 hipError_t launch_prefill16(const PrefillArgs &a) {
-    if (a.dv_per_block == 64) return launch_p16<4, 8, 6>(a);
-    if (a.dv_per_block == 32) return launch_p16<2, 6, 6>(a);
+    const bool ck = a.ckpt != nullptr && a.ckpt_every > 0;
+    if (a.dv_per_block == 64)
+        return ck ? launch_p16<4, 8, 6, true>(a) : launch_p16<4, 8, 6, false>(a);
+    if (a.dv_per_block == 32)
+        return ck ? launch_p16<2, 6, 6, true>(a) : launch_p16<2, 6, 6, false>(a);
     return hipErrorInvalidValue;
 }
 

@@ -27,7 +27,7 @@ from dataclasses import dataclass, replace
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_prefill_inputs", "make_decode_inputs",
+__all__ = ["Workload", "WORKLOADS", "make_prefill_inputs", "make_decode_inputs", "make_varlen_inputs",
            "torch_dtype"]
 
 
@@ -123,3 +123,35 @@ def make_decode_inputs(w: Workload, device="cpu", steps: int | None = None):
     S = torch.zeros(w.B, w.H, w.dk, w.dv, dtype=torch.float32, device=device)
     return dict(q=_unit(q).to(dt), k=_unit(k).to(dt), v=v.to(dt), z=z.to(dt),
                 beta=torch.sigmoid(beta_logit).to(dt), A=A, S=S)
+
+
+def make_varlen_inputs(w: Workload, lengths, device="cpu"):
+    """Packed inputs for sequences of the given lengths, drawn as one workload.
+
+    Token tensors come from the prefill recipe with B=1 and T=sum(lengths),
+    laid out [T, H, d] (``beta`` [T, H]); then one initial state per sequence
+    ([N, H, dk, dv], N(0, s0_std^2) when s0_std is set, else zeros) from the
+    same generator stream.  ``cu_seqlens`` is the int64 [N+1] prefix sum."""
+    lengths = [int(L) for L in lengths]
+    T = sum(lengths)
+    g = _gen(w.seed, device)
+    dt = torch_dtype(w.dtype)
+    f32 = dict(dtype=torch.float32, device=device, generator=g)
+    q = torch.randn(T, w.H, w.dk, **f32)
+    k = torch.randn(T, w.H, w.dk, **f32)
+    v = torch.randn(T, w.H, w.dv, **f32)
+    beta_logit = torch.randn(T, w.H, **f32)
+    z = torch.randn(T, w.H, w.dk, **f32)
+    if w.z_mean:
+        z.add_(w.z_mean)
+    A = torch.rand(w.H, **f32).mul_(2.0).sub_(1.0)
+    N = len(lengths)
+    if w.s0_std is not None:
+        S0 = torch.randn(N, w.H, w.dk, w.dv, **f32).mul_(w.s0_std)
+    else:
+        S0 = torch.zeros(N, w.H, w.dk, w.dv, dtype=torch.float32, device=device)
+    cu = torch.zeros(N + 1, dtype=torch.int64)
+    if N:
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0)
+    return dict(q=_unit(q).to(dt), k=_unit(k).to(dt), v=v.to(dt), z=z.to(dt),
+                beta=torch.sigmoid(beta_logit).to(dt), A=A, S0=S0, cu_seqlens=cu.to(device))

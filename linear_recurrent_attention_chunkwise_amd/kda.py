@@ -57,6 +57,10 @@ def _load():
     lib.kda_prefill.argtypes = pre
     lib.kda_prefill_ex.restype = ctypes.c_int
     lib.kda_prefill_ex.argtypes = pre + [i32]
+    lib.kda_prefill_varlen.restype = ctypes.c_int
+    lib.kda_prefill_varlen.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i32, vp,
+                                       vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       i32, vp, i64, vp, i32]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, vp, vp,
                                     vp, vp, vp, vp]
@@ -143,6 +147,81 @@ def prefill(q, k, v, z, beta, A, S0=None, chunk: int = 16, out=None, S_T=None,
                             int(dv_per_block))
     _check(st, "kda_prefill")
     return out, S_T
+
+
+def checkpoint_rows(seq_lens, ckpt_every: int):
+    """First checkpoint row of each sequence and the total row count, for the
+    layout of ``prefill_varlen``: floor(L_i / ckpt_every) rows per sequence,
+    in sequence order."""
+    rows, r0 = [], 0
+    for L in seq_lens:
+        rows.append(r0)
+        r0 += int(L) // ckpt_every if ckpt_every > 0 else 0
+    return rows, r0
+
+
+def prefill_varlen(q, k, v, z, beta, A, cu_seqlens, S0=None, chunk: int = 16,
+                   ckpt_every: int = 0, out=None, S_T=None, ckpt=None,
+                   dv_per_block: int = 0):
+    """KDA prefill over N sequences packed along one token axis.
+
+    q, k, z [T,H,dk]; v [T,H,dv]; beta [T,H] (one dtype, fp32 or bf16);
+    A [H] fp32; cu_seqlens int64 [N+1] (sequence i is tokens
+    cu_seqlens[i]:cu_seqlens[i+1]); S0 [N,H,dk,dv] fp32 or None.
+    ckpt_every > 0 (a multiple of ``chunk``) also returns the state after every
+    ckpt_every tokens of each sequence: ckpt [R,H,dk,dv] fp32, rows in sequence
+    order (see ``checkpoint_rows``).  Returns (o, S_T, ckpt-or-None).
+
+    ``cu_seqlens`` may be a CPU or GPU tensor; the library reads a GPU copy,
+    and the host copy sizes the checkpoint buffer."""
+    lib = _load()
+    if q.dim() != 3:
+        raise ValueError("q must be [T,H,dk] (packed sequences)")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("KDA prefill runs on the GPU; inputs must be cuda tensors")
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    if not isinstance(cu_seqlens, torch.Tensor):
+        cu_seqlens = torch.tensor(list(cu_seqlens), dtype=torch.int64)
+    if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int64 tensor [N+1]")
+    cu_host = cu_seqlens.cpu()
+    lens = (cu_host[1:] - cu_host[:-1]).tolist()
+    N = len(lens)
+    if int(cu_host[0]) != 0 or any(L < 0 for L in lens) or int(cu_host[-1]) != T:
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    cu_dev = cu_seqlens.to(dev).contiguous()
+    _require(q, "q", (T, H, dk), dt, dev)
+    _require(k, "k", (T, H, dk), dt, dev)
+    _require(z, "z", (T, H, dk), dt, dev)
+    _require(v, "v", (T, H, dv), dt, dev)
+    _require(beta, "beta", (T, H), dt, dev)
+    _require(A, "A", (H,), torch.float32, dev)
+    if S0 is not None:
+        _require(S0, "S0", (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=dt, device=dev)
+    _require(out, "out", (T, H, dv), dt, dev)
+    if S_T is None:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _require(S_T, "S_T", (N, H, dk, dv), torch.float32, dev)
+    n_ckpt = 0
+    if ckpt_every > 0:
+        _, n_ckpt = checkpoint_rows(lens, int(ckpt_every))
+        if ckpt is None:
+            ckpt = torch.empty((n_ckpt, H, dk, dv), dtype=torch.float32, device=dev)
+        _require(ckpt, "ckpt", (n_ckpt, H, dk, dv), torch.float32, dev)
+    else:
+        ckpt = None
+    st = lib.kda_prefill_varlen(_DTYPES[dt], N, T, H, dk, dv, int(chunk), _ptr(cu_dev),
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
+                                _ptr(S0), _ptr(out), _ptr(S_T), int(ckpt_every), _ptr(ckpt),
+                                n_ckpt, _stream_handle(dev), int(dv_per_block))
+    _check(st, "kda_prefill_varlen")
+    return out, S_T, ckpt
 
 
 def decode_step(q, k, v, z, beta, A, S, out=None):

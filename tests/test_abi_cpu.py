@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_expected_api():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_str", "kda_prefill_workspace_size",
-        "kda_prefill", "kda_prefill_ex", "kda_decode_step"])
+        "kda_prefill", "kda_prefill_ex", "kda_prefill_varlen", "kda_decode_step"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     for s in range(8):
         assert lib.kda_status_str(s).decode().startswith("KDA_")
     assert lib.kda_status_str(99) == b"unknown kda_status"
@@ -84,6 +84,7 @@ def test_prefill_shape_and_support_errors(lib):
     assert prefill(lib, chunk=32) == UNSUP
     assert prefill(lib, dvb=48) == UNSUP
     assert prefill(lib, dtype=F32, chunk=64) == UNSUP      # fp32 with dk=128 runs chunk 16
+    assert prefill(lib, chunk=64, dvb=16) == UNSUP         # one-wave 64-token variant not built
     assert prefill(lib, B=1 << 40, T=1 << 40) == SHAPE     # element count overflows
 
 
@@ -123,3 +124,40 @@ def test_decode_errors(lib):
     assert decode(lib, ptrs={"o": P(6, 32)}) == ALIAS       # o inside S
     assert decode(lib, ptrs={"S": P(0, 0)}) == ALIAS        # S over q
     assert decode(lib, B=0) == OK
+
+
+def varlen(lib, dtype=BF16, N=2, T=64, H=2, dk=128, dv=128, chunk=16, every=0, n_ckpt=0,
+           ptrs=None, dvb=0):
+    names = ["q", "k", "v", "z", "beta", "A", "S0", "o", "S_T", "cu", "ckpt"]
+    p = {n: P(i) for i, n in enumerate(names)}
+    if ptrs:
+        p.update(ptrs)
+    return lib.kda_prefill_varlen(dtype, N, T, H, dk, dv, chunk, p["cu"], p["q"], p["k"],
+                                  p["v"], p["z"], p["beta"], p["A"], p["S0"], p["o"],
+                                  p["S_T"], every, p["ckpt"], n_ckpt, None, dvb)
+
+
+def test_varlen_argument_errors(lib):
+    assert varlen(lib, N=-1) == SHAPE
+    assert varlen(lib, every=-16) == SHAPE
+    assert varlen(lib, every=16, n_ckpt=-1) == SHAPE
+    assert varlen(lib, ptrs={"cu": None}) == NULL            # N > 0 needs offsets
+    assert varlen(lib, every=16, n_ckpt=4, ptrs={"ckpt": None}) == NULL
+    assert varlen(lib, every=24) == UNSUP                    # not a multiple of the chunk
+    assert varlen(lib, chunk=64, every=32) == UNSUP
+    assert varlen(lib, ptrs={"cu": P(20, 4)}) == MISALIGNED  # int64 offsets need 8 bytes
+    assert varlen(lib, every=16, n_ckpt=4, ptrs={"ckpt": P(20, 8)}) == MISALIGNED
+    # checkpoints overlapping the outputs, the initial state or an input
+    assert varlen(lib, every=16, n_ckpt=4, ptrs={"ckpt": P(7, 64)}) == ALIAS
+    assert varlen(lib, every=16, n_ckpt=4, ptrs={"ckpt": P(6, 64)}) == ALIAS
+    assert varlen(lib, every=16, n_ckpt=4, ptrs={"ckpt": P(0, 64)}) == ALIAS
+    assert varlen(lib, ptrs={"o": P(9, 0)}) == ALIAS         # o over the offsets
+    # checkpoints at 64-token chunks: not with 64 value columns per workgroup
+    assert varlen(lib, chunk=64, every=64, n_ckpt=4, dvb=64) == UNSUP
+
+
+def test_varlen_empty_work_launches_nothing(lib):
+    assert varlen(lib, N=0, ptrs={"cu": None}) == OK
+    assert varlen(lib, H=0) == OK
+    # without checkpoints the checkpoint buffer is not looked at
+    assert varlen(lib, N=0, every=0, n_ckpt=5, ptrs={"ckpt": P(7, 64)}) == OK
