@@ -126,6 +126,38 @@ def time_prefill(torch, kda, inp, chunk, steps, warmup):
     return e0.elapsed_time(e1) / steps   # ms per launch
 
 
+VARLEN_LENGTHS = [4096, 1000, 37, 2500, 16, 513, 64, 3000]   # mixed, ragged, 11226 tokens
+VARLEN_CKPT_EVERY = 1024
+
+
+def time_varlen(torch, kda, vin, ckpt_every, steps, warmup):
+    """ms per launch of the packed prefill (optionally with checkpoints)."""
+    o = torch.empty_like(vin["v"])
+    S_T = torch.empty_like(vin["S0"])
+    cu = vin["cu_seqlens"]
+    ck = None
+    if ckpt_every > 0:
+        _, n = kda.checkpoint_rows(VARLEN_LENGTHS, ckpt_every)
+        ck = torch.empty((n,) + tuple(vin["S0"].shape[1:]), dtype=torch.float32,
+                         device=vin["S0"].device)
+
+    def run():
+        kda.prefill_varlen(vin["q"], vin["k"], vin["v"], vin["z"], vin["beta"], vin["A"], cu,
+                           S0=vin["S0"], chunk=16, ckpt_every=ckpt_every, out=o, S_T=S_T,
+                           ckpt=ck, seq_lens=VARLEN_LENGTHS)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def time_decode(torch, kda, dinp, reps):
     S = dinp["S"]
     steps = dinp["q"].shape[0]
@@ -170,6 +202,7 @@ def main(argv=None):
     ap.add_argument("--decode-reps", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="also run one elementwise copy of this many MiB (byte-counter reference)")
     args = ap.parse_args(argv)
@@ -228,6 +261,31 @@ def main(argv=None):
                          "traffic": recorded_traffic("kda_decode_kernel",
                                                      f"kda_decode_kernel_{wd.name}.md"),
                          "kernel": "kda_decode_kernel", "bytes_per_launch": dbytes}}
+    if not args.no_varlen:
+        from linear_recurrent_attention_chunkwise_amd.inputs import make_varlen_inputs
+        wv = WORKLOADS["k3_prefill_bf16"].with_(seed=5)
+        vin = {k: (v.to(dev) if v is not None else None)
+               for k, v in make_varlen_inputs(wv, VARLEN_LENGTHS).items()}
+        ntok = sum(VARLEN_LENGTHS)
+        nseq = len(VARLEN_LENGTHS)
+        vbytes = (ntok * wv.H * (5 * wv.dk * 2 + 2) + 2 * nseq * wv.H * wv.dk * wv.dk * 4
+                  + wv.H * 4)
+        vms = time_varlen(torch, kda, vin, 0, max(1, args.steps // 4), max(1, args.warmup // 40))
+        cms = time_varlen(torch, kda, vin, VARLEN_CKPT_EVERY, max(1, args.steps // 4),
+                          max(1, args.warmup // 40))
+        nck = sum(L // VARLEN_CKPT_EVERY for L in VARLEN_LENGTHS)
+        cbytes = vbytes + nck * wv.H * wv.dk * wv.dk * 4
+        result["varlen"] = {
+            "value": ntok / (vms * 1e-3), "unit": "tokens/s", "ms_per_launch": vms,
+            "workload": f"packed prefill, {nseq} sequences of lengths {VARLEN_LENGTHS} "
+                        f"({ntok} tokens), H={wv.H}, d={wv.dk}, bf16, chunk 16",
+            "roofline": {"bound": "hbm", "achieved": vbytes / (vms * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": vbytes / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "bytes_per_launch": vbytes},
+            "with_checkpoints": {"ckpt_every": VARLEN_CKPT_EVERY, "checkpoints": nck,
+                                 "ms_per_launch": cms, "value": ntok / (cms * 1e-3),
+                                 "bytes_per_launch": cbytes}}
     if args.calib_mib > 0:
         calibration_copy(torch, args.calib_mib)
     if not args.no_cpu:

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -147,6 +147,11 @@ kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk
  *        (fp32), where R_i = sum over earlier sequences of floor(L / ckpt_every).
  *        Rows at or beyond n_ckpt are not written.  ckpt must not overlap any
  *        other argument.
+ *   workspace: device memory of at least kda_prefill_varlen_workspace_size(N)
+ *        bytes, 16-byte aligned (NULL allowed when that size is 0).  The call
+ *        ranks the sequences longest first there, and the kernels dispatch
+ *        the long sequences first, which balances the load of a mixed batch.
+ *        Its contents are scratch; calls sharing a workspace must not overlap.
  * All other conventions (dtype, sizes, alignment, aliasing, errors, the
  * dv_per_block split) are those of kda_prefill_ex; each sequence's result is
  * that of kda_prefill on the sequence alone.  Exception: with checkpoints,
@@ -160,7 +165,12 @@ kda_status kda_prefill_varlen(int dtype, int64_t N, int64_t T_total, int64_t H,
                               const void *beta, const float *A, const float *S0,
                               void *o, float *S_T,
                               int32_t ckpt_every, float *ckpt, int64_t n_ckpt,
+                              void *workspace, size_t workspace_bytes,
                               void *stream, int32_t dv_per_block);
+
+/* Bytes of device workspace kda_prefill_varlen needs for N sequences (0 for
+ * N <= 1, and above 8192 sequences, which run in sequence order). */
+size_t kda_prefill_varlen_workspace_size(int64_t N);
 
 /*
  * One fused recurrent decode step for B sequences (the "KDA decode" half of

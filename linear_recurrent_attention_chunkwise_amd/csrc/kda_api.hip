@@ -70,11 +70,16 @@ namespace {
 
 // Shared validation and dispatch of the prefill entry points.  `cu` == NULL:
 // dense [B, T, H, d]; otherwise B packed sequences over T tokens.
+size_t order_bytes(int64_t N) {
+    return N > 1 && N <= kda::kMaxOrderSeqs ? (size_t)((N * 4 + 255) / 256 * 256) : 0;
+}
+
 kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                         int32_t chunk, const int64_t *cu, const void *q, const void *k,
                         const void *v, const void *z, const void *beta, const float *A,
                         const float *S0, void *o, float *S_T, int32_t ckpt_every,
-                        float *ckpt, int64_t n_ckpt, void *stream, int32_t dv_per_block) {
+                        float *ckpt, int64_t n_ckpt, void *workspace, size_t workspace_bytes,
+                        void *stream, int32_t dv_per_block) {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || n_ckpt < 0 || ckpt_every < 0)
         return KDA_ERR_SHAPE;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -114,12 +119,16 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
     if (cu && ((uintptr_t)cu & 7u) != 0) return KDA_ERR_MISALIGNED;
+    const size_t need_ws = cu && H > 0 ? order_bytes(B) : 0;   // longest-first order
+    if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_WORKSPACE;
+    if (need_ws > 0 && !aligned16(workspace)) return KDA_ERR_MISALIGNED;
     const Range rq = range_of(q, nin * esz), rk = range_of(k, nin * esz),
                 rv = range_of(v, nin * esz), rz = range_of(z, nin * esz),
                 rb = range_of(beta, bth * esz), rA = range_of(A, H * 4),
                 rS0 = range_of(S0, nstate * 4), ro = range_of(o, nin * esz),
                 rST = range_of(S_T, nstate * 4),
                 rcu = range_of(cu, cu ? (B + 1) * 8 : 0),
+                rws = range_of(need_ws > 0 ? workspace : nullptr, (int64_t)need_ws),
                 rck = range_of(ckpt_every > 0 ? ckpt : nullptr, nck * 4);
     const Range ins[] = {rq, rk, rv, rz, rb, rA, rcu};
     for (const Range &r : ins)
@@ -128,6 +137,11 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
         overlaps(rck, rST))
         return KDA_ERR_ALIAS;
     if (overlaps(rST, rS0) && (const void *)S_T != (const void *)S0) return KDA_ERR_ALIAS;
+    {
+        const Range all[] = {rq, rk, rv, rz, rb, rA, rS0, ro, rST, rcu, rck};
+        for (const Range &r : all)
+            if (overlaps(rws, r)) return KDA_ERR_ALIAS;
+    }
     if (bh == 0) return KDA_OK;
 
     kda::PrefillArgs a;
@@ -136,6 +150,13 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
     a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.A = A; a.S0 = S0;
     a.o = o; a.S_T = S_T;
     a.cu_seqlens = cu;
+    a.order = nullptr;
+    if (need_ws > 0) {
+        int32_t *order = static_cast<int32_t *>(workspace);
+        if (kda::launch_seq_order(cu, B, T, order, (hipStream_t)stream) != hipSuccess)
+            return KDA_ERR_HIP;
+        a.order = order;
+    }
     a.ckpt_every = ckpt_every > 0 && n_ckpt > 0 ? ckpt_every : 0;
     a.ckpt = a.ckpt_every > 0 ? ckpt : nullptr;
     a.n_ckpt = n_ckpt;
@@ -156,18 +177,22 @@ kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk
     (void)workspace;
     (void)workspace_bytes;
     return prefill_impl(dtype, B, T, H, dk, dv, chunk, nullptr, q, k, v, z, beta, A, S0, o, S_T,
-                        0, nullptr, 0, stream, dv_per_block);
+                        0, nullptr, 0, nullptr, 0, stream, dv_per_block);
 }
+
+size_t kda_prefill_varlen_workspace_size(int64_t N) { return order_bytes(N); }
 
 kda_status kda_prefill_varlen(int dtype, int64_t N, int64_t T_total, int64_t H, int64_t dk,
                               int64_t dv, int32_t chunk, const int64_t *cu_seqlens,
                               const void *q, const void *k, const void *v, const void *z,
                               const void *beta, const float *A, const float *S0, void *o,
                               float *S_T, int32_t ckpt_every, float *ckpt, int64_t n_ckpt,
-                              void *stream, int32_t dv_per_block) {
+                              void *workspace, size_t workspace_bytes, void *stream,
+                              int32_t dv_per_block) {
     if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
     return prefill_impl(dtype, N, T_total, H, dk, dv, chunk, cu_seqlens, q, k, v, z, beta, A,
-                        S0, o, S_T, ckpt_every, ckpt, n_ckpt, stream, dv_per_block);
+                        S0, o, S_T, ckpt_every, ckpt, n_ckpt, workspace, workspace_bytes, stream,
+                        dv_per_block);
 }
 
 kda_status kda_prefill(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,

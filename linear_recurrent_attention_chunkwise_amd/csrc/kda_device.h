@@ -147,6 +147,35 @@ __device__ __forceinline__ SeqRange seq_range(const int64_t *cu, int64_t b, int6
     return SeqRange{lo, hi - lo};
 }
 
+// Workgroup -> (head unit, value-column slice).  A head unit is r*H + h for
+// the sequence of rank r (rank order: `order[r]` when given, else r itself).
+// Workgroups are dealt to the 8 XCDs round-robin in dispatch order; within each
+// run of 8*nsplit consecutive workgroups, workgroup 8*nsplit*a + 8*s + i takes
+// slice s of unit 8a + i.  So the slices of one head land on one XCD (and
+// share its L2 for the head's q, k, z), and units are dispatched in order,
+// which lets a longest-first ranking of packed sequences balance the load.
+struct BlockMap {
+    int64_t b;      // sequence (batch entry)
+    int h;          // head
+    int split;      // value-column slice
+};
+__device__ __forceinline__ BlockMap block_map(int64_t x, int64_t nblk, int nsplit, int64_t H,
+                                              const int32_t *order) {
+    const int64_t grp = 8 * (int64_t)nsplit;
+    int64_t unit;
+    int split;
+    if (nblk % grp == 0) {
+        const int64_t a = x / grp, rem = x % grp;
+        split = (int)(rem / 8);
+        unit = 8 * a + rem % 8;
+    } else {
+        unit = x / nsplit;
+        split = (int)(x % nsplit);
+    }
+    const int64_t r = unit / H;
+    return BlockMap{order ? (int64_t)order[r] : r, (int)(unit % H), split};
+}
+
 // First checkpoint row of sequence b: the rows of earlier sequences come
 // first, floor(len / every) per sequence.
 __device__ __forceinline__ int64_t ckpt_row0(const int64_t *cu, int64_t b, int64_t T, int every) {

@@ -24,6 +24,9 @@ struct PrefillArgs {
     // [cu_seqlens[b], cu_seqlens[b+1]) of a [T, H, d] packing (T = total
     // tokens).  NULL: dense [B, T, H, d].
     const int64_t *cu_seqlens;
+    // Optional longest-first order of the sequences (device int32 [B]): rank r
+    // runs sequence order[r].  NULL: sequence order.
+    const int32_t *order;
     // State checkpoints: every ckpt_every tokens of a sequence (0 = none),
     // rows of ckpt [n_ckpt, H, D, D] in sequence order.
     int ckpt_every;
@@ -52,6 +55,12 @@ bool prefill_ckpt_supported(int dtype, int64_t D, int chunk, int dv_per_block);
 // Role-split variant for bf16, D = 128, chunk 16 (kda_prefill16.hip).
 bool prefill16_supported(int dtype, int64_t D, int chunk, int dv_per_block);
 hipError_t launch_prefill16(const PrefillArgs &a);
+
+// Longest-first ranking of packed sequences (device): order[rank] = sequence.
+// Only used for 1 < N <= kMaxOrderSeqs.
+constexpr int64_t kMaxOrderSeqs = 8192;
+hipError_t launch_seq_order(const int64_t *cu, int64_t N, int64_t T, int32_t *order,
+                            hipStream_t stream);
 
 bool decode_supported(int dtype, int64_t D);
 hipError_t launch_decode(const DecodeArgs &a);

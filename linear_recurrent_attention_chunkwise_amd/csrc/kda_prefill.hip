@@ -49,6 +49,7 @@ struct PrefillParams {
     int64_t T, H;   // T: tokens per sequence (dense) or in the packing (cu != NULL)
     int nsplit;
     const int64_t *cu;   // packed sequence offsets, or NULL
+    const int32_t *order;   // longest-first sequence order, or NULL
     float *ckpt;         // state checkpoints [n_ckpt, H, D, D], or NULL
     int64_t n_ckpt;
     int ckpt_every;      // tokens between checkpoints (0: none)
@@ -193,16 +194,13 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, n = lane & 15;
 
-    // Workgroup -> (b, h, value-column slice).  Workgroups are dealt to the
-    // 8 XCDs round-robin; renumber so the slices of one head share an XCD
-    // (and its L2), which dedupes their reads of q, k, z.
-    int64_t x = blockIdx.x;
-    const int64_t nblk = gridDim.x;
-    if (nblk % 8 == 0) x = (x % 8) * (nblk / 8) + x / 8;
-    const int64_t bh = x / prm.nsplit;
-    const int split = (int)(x % prm.nsplit);
+    // Workgroup -> (b, h, value-column slice); the slices of one head share
+    // an XCD (and its L2), which dedupes their reads of q, k, z.
     const int64_t H = prm.H;
-    const int64_t b = bh / H;
+    const BlockMap bm = block_map(blockIdx.x, gridDim.x, prm.nsplit, H, prm.order);
+    const int64_t b = bm.b;
+    const int split = bm.split;
+    const int64_t bh = b * H + bm.h;
     const SeqRange sr = seq_range(prm.cu, b, prm.T);
     const int64_t Tn = sr.len;
     const int h = (int)(bh % H);
@@ -612,6 +610,22 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
         for (int e = 0; e < 4; ++e) sT_out[(16 * i + 4 * g + e) * D + jw + n] = S[i][e];
 }
 
+// Longest-first ranking of packed sequences: sequence j gets the rank
+// #{i : L_i > L_j, or L_i == L_j and i < j}, and order[rank] = j.  One thread
+// per sequence, O(N) each; lengths are the clamped ranges the prefill uses.
+__global__ __launch_bounds__(256) void kda_seq_order_kernel(const int64_t *cu, int64_t N,
+                                                            int64_t T, int32_t *order) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= N) return;
+    const int64_t Lj = seq_range(cu, j, T).len;
+    int64_t rank = 0;
+    for (int64_t i = 0; i < N; ++i) {
+        const int64_t Li = seq_range(cu, i, T).len;
+        rank += (Li > Lj || (Li == Lj && i < j)) ? 1 : 0;
+    }
+    order[rank] = (int32_t)j;
+}
+
 // ---------------------------------------------------------------- host ----
 
 template <typename T, int D, int C, int NW>
@@ -629,7 +643,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
     prm.q = a.q; prm.k = a.k; prm.v = a.v; prm.z = a.z; prm.beta = a.beta;
     prm.A = a.A; prm.S0 = a.S0; prm.o = a.o; prm.S_T = a.S_T;
     prm.T = a.T; prm.H = a.H;
-    prm.cu = a.cu_seqlens; prm.ckpt = a.ckpt; prm.n_ckpt = a.n_ckpt;
+    prm.cu = a.cu_seqlens; prm.order = a.order; prm.ckpt = a.ckpt; prm.n_ckpt = a.n_ckpt;
     prm.ckpt_every = a.ckpt_every;
     prm.nsplit = (int)(D / (16 * NW));
     const int64_t nblk = a.B * a.H * prm.nsplit;
@@ -673,6 +687,13 @@ int prefill_default_dv_per_block(int dtype, int64_t B, int64_t H, int64_t D, int
     (void)B; (void)H; (void)chunk; (void)dtype;
     if (D == 16) return 16;
     return 64;
+}
+
+hipError_t launch_seq_order(const int64_t *cu, int64_t N, int64_t T, int32_t *order,
+                            hipStream_t stream) {
+    const unsigned nb = (unsigned)((N + 255) / 256);
+    hipLaunchKernelGGL(kda_seq_order_kernel, dim3(nb), dim3(256), 0, stream, cu, N, T, order);
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillArgs &a) {

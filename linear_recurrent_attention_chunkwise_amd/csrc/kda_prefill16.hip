@@ -58,6 +58,7 @@ struct Prefill16Params {
     int64_t T, H;   // T: tokens per sequence (dense) or in the packing (cu != NULL)
     int nsplit;
     const int64_t *cu;   // packed sequence offsets, or NULL
+    const int32_t *order;   // longest-first sequence order, or NULL
     float *ckpt;         // state checkpoints [n_ckpt, H, D, D], or NULL
     int64_t n_ckpt;
     int ckpt_every;      // tokens between checkpoints (0: none)
@@ -135,14 +136,12 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
 
-    int64_t x = blockIdx.x;
-    const int64_t nblk = gridDim.x;
-    if (nblk % 8 == 0) x = (x % 8) * (nblk / 8) + x / 8;   // slices of a head share an XCD
-    const int64_t bh = x / prm.nsplit;
-    const int split = (int)(x % prm.nsplit);
     const int64_t H = prm.H;
-    const int64_t b = bh / H;
-    const int h = (int)(bh % H);
+    const BlockMap bm = block_map(blockIdx.x, gridDim.x, prm.nsplit, H, prm.order);
+    const int64_t b = bm.b;
+    const int h = bm.h;
+    const int split = bm.split;
+    const int64_t bh = b * H + h;
     const SeqRange sr = seq_range(prm.cu, b, prm.T);
     const int64_t Tn = sr.len;
     const int j0 = split * DVB;
@@ -523,6 +522,7 @@ static hipError_t launch_p16(const PrefillArgs &a) {
     prm.H = a.H;
     prm.nsplit = 128 / (16 * NCW);
     prm.cu = a.cu_seqlens;
+    prm.order = a.order;
     prm.ckpt = a.ckpt;
     prm.n_ckpt = a.n_ckpt;
     prm.ckpt_every = a.ckpt_every;

@@ -60,7 +60,9 @@ def _load():
     lib.kda_prefill_varlen.restype = ctypes.c_int
     lib.kda_prefill_varlen.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i32, vp,
                                        vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                       i32, vp, i64, vp, i32]
+                                       i32, vp, i64, vp, sz, vp, i32]
+    lib.kda_prefill_varlen_workspace_size.restype = sz
+    lib.kda_prefill_varlen_workspace_size.argtypes = [i64]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, vp, vp,
                                     vp, vp, vp, vp]
@@ -162,7 +164,7 @@ def checkpoint_rows(seq_lens, ckpt_every: int):
 
 def prefill_varlen(q, k, v, z, beta, A, cu_seqlens, S0=None, chunk: int = 16,
                    ckpt_every: int = 0, out=None, S_T=None, ckpt=None,
-                   dv_per_block: int = 0):
+                   dv_per_block: int = 0, seq_lens=None):
     """KDA prefill over N sequences packed along one token axis.
 
     q, k, z [T,H,dk]; v [T,H,dv]; beta [T,H] (one dtype, fp32 or bf16);
@@ -173,7 +175,9 @@ def prefill_varlen(q, k, v, z, beta, A, cu_seqlens, S0=None, chunk: int = 16,
     order (see ``checkpoint_rows``).  Returns (o, S_T, ckpt-or-None).
 
     ``cu_seqlens`` may be a CPU or GPU tensor; the library reads a GPU copy,
-    and the host copy sizes the checkpoint buffer."""
+    and host values size the checkpoint buffer.  Passing ``seq_lens`` (the
+    host list of lengths) together with a GPU ``cu_seqlens`` avoids every
+    host-device copy in this call."""
     lib = _load()
     if q.dim() != 3:
         raise ValueError("q must be [T,H,dk] (packed sequences)")
@@ -188,12 +192,18 @@ def prefill_varlen(q, k, v, z, beta, A, cu_seqlens, S0=None, chunk: int = 16,
         cu_seqlens = torch.tensor(list(cu_seqlens), dtype=torch.int64)
     if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
         raise ValueError("cu_seqlens must be a 1-D int64 tensor [N+1]")
-    cu_host = cu_seqlens.cpu()
-    lens = (cu_host[1:] - cu_host[:-1]).tolist()
+    if seq_lens is not None and cu_seqlens.device == dev:
+        lens = [int(L) for L in seq_lens]
+        if len(lens) != cu_seqlens.numel() - 1 or any(L < 0 for L in lens) or sum(lens) != T:
+            raise ValueError("seq_lens must hold N non-negative lengths summing to T")
+        cu_dev = cu_seqlens.contiguous()
+    else:
+        cu_host = cu_seqlens.cpu()
+        lens = (cu_host[1:] - cu_host[:-1]).tolist()
+        if int(cu_host[0]) != 0 or any(L < 0 for L in lens) or int(cu_host[-1]) != T:
+            raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+        cu_dev = cu_seqlens.to(dev).contiguous()
     N = len(lens)
-    if int(cu_host[0]) != 0 or any(L < 0 for L in lens) or int(cu_host[-1]) != T:
-        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
-    cu_dev = cu_seqlens.to(dev).contiguous()
     _require(q, "q", (T, H, dk), dt, dev)
     _require(k, "k", (T, H, dk), dt, dev)
     _require(z, "z", (T, H, dk), dt, dev)
@@ -216,10 +226,13 @@ def prefill_varlen(q, k, v, z, beta, A, cu_seqlens, S0=None, chunk: int = 16,
         _require(ckpt, "ckpt", (n_ckpt, H, dk, dv), torch.float32, dev)
     else:
         ckpt = None
+    ws_bytes = int(lib.kda_prefill_varlen_workspace_size(N))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     st = lib.kda_prefill_varlen(_DTYPES[dt], N, T, H, dk, dv, int(chunk), _ptr(cu_dev),
                                 _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
                                 _ptr(S0), _ptr(out), _ptr(S_T), int(ckpt_every), _ptr(ckpt),
-                                n_ckpt, _stream_handle(dev), int(dv_per_block))
+                                n_ckpt, _ptr(ws), ws_bytes, _stream_handle(dev),
+                                int(dv_per_block))
     _check(st, "kda_prefill_varlen")
     return out, S_T, ckpt
 

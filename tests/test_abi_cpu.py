@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 LIB = os.path.join(ROOT, "linear_recurrent_attention_chunkwise_amd", "libkda.so")
 
-OK, NULL, SHAPE, UNSUP, MISALIGNED, ALIAS = 0, 1, 2, 3, 4, 5
+OK, NULL, SHAPE, UNSUP, MISALIGNED, ALIAS, WORKSPACE = 0, 1, 2, 3, 4, 5, 6
 F32, BF16 = 0, 1
 
 
@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_expected_api():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_str", "kda_prefill_workspace_size",
-        "kda_prefill", "kda_prefill_ex", "kda_prefill_varlen", "kda_decode_step"])
+        "kda_prefill", "kda_prefill_ex", "kda_prefill_varlen",
+        "kda_prefill_varlen_workspace_size", "kda_decode_step"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     for s in range(8):
         assert lib.kda_status_str(s).decode().startswith("KDA_")
     assert lib.kda_status_str(99) == b"unknown kda_status"
@@ -128,13 +129,15 @@ def test_decode_errors(lib):
 
 def varlen(lib, dtype=BF16, N=2, T=64, H=2, dk=128, dv=128, chunk=16, every=0, n_ckpt=0,
            ptrs=None, dvb=0):
-    names = ["q", "k", "v", "z", "beta", "A", "S0", "o", "S_T", "cu", "ckpt"]
+    names = ["q", "k", "v", "z", "beta", "A", "S0", "o", "S_T", "cu", "ckpt", "ws"]
     p = {n: P(i) for i, n in enumerate(names)}
     if ptrs:
         p.update(ptrs)
+    ws_bytes = lib.kda_prefill_varlen_workspace_size(N)
     return lib.kda_prefill_varlen(dtype, N, T, H, dk, dv, chunk, p["cu"], p["q"], p["k"],
                                   p["v"], p["z"], p["beta"], p["A"], p["S0"], p["o"],
-                                  p["S_T"], every, p["ckpt"], n_ckpt, None, dvb)
+                                  p["S_T"], every, p["ckpt"], n_ckpt, p["ws"], ws_bytes, None,
+                                  dvb)
 
 
 def test_varlen_argument_errors(lib):
@@ -152,6 +155,12 @@ def test_varlen_argument_errors(lib):
     assert varlen(lib, every=16, n_ckpt=4, ptrs={"ckpt": P(6, 64)}) == ALIAS
     assert varlen(lib, every=16, n_ckpt=4, ptrs={"ckpt": P(0, 64)}) == ALIAS
     assert varlen(lib, ptrs={"o": P(9, 0)}) == ALIAS         # o over the offsets
+    # the longest-first ranking needs its workspace
+    assert lib.kda_prefill_varlen_workspace_size(1) == 0
+    assert lib.kda_prefill_varlen_workspace_size(2) >= 8
+    assert varlen(lib, ptrs={"ws": None}) == WORKSPACE
+    assert varlen(lib, ptrs={"ws": P(11, 8)}) == MISALIGNED
+    assert varlen(lib, ptrs={"ws": P(7, 16)}) == ALIAS       # workspace over the outputs
     # checkpoints at 64-token chunks: not with 64 value columns per workgroup
     assert varlen(lib, chunk=64, every=64, n_ckpt=4, dvb=64) == UNSUP
 

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(scope="module")
 def kda():
     import linear_recurrent_attention_chunkwise_amd as m
-    assert m.abi_version() == 2
+    assert m.abi_version() == 3
     return m
 
 
@@ -193,9 +193,11 @@ def test_malformed_offsets_are_clamped(kda, gpu_device):
         o = torch.zeros((T, H, d), dtype=g["q"].dtype, device=gpu_device)
         S = torch.zeros((2, H, d, d), dtype=torch.float32, device=gpu_device)
         p = lambda t: ctypes.c_void_p(t.data_ptr())
+        ws_bytes = lib.kda_prefill_varlen_workspace_size(2)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=gpu_device)
         st = lib.kda_prefill_varlen(1, 2, T, H, d, d, 16, p(cu), p(g["q"]), p(g["k"]), p(g["v"]),
                                     p(g["z"]), p(g["beta"]), p(g["A"]), p(g["S0"]), p(o), p(S),
-                                    0, None, 0, None, 0)
+                                    0, None, 0, p(ws), ws_bytes, None, 0)
         torch.cuda.synchronize()
         assert st == 0
         return o, S
@@ -206,3 +208,25 @@ def test_malformed_offsets_are_clamped(kda, gpu_device):
     o_neg, S_neg = raw([0, -7, 20])     # sequence 0 empty, sequence 1 = all 20 tokens
     S0 = g["S0"]
     assert torch.equal(S_neg[0], S0[0])
+
+
+def test_longest_first_order_does_not_change_results(kda, gpu_device):
+    """Sequences are dispatched longest first; a sequence's result does not
+    depend on where it sits in the packing (bitwise)."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(H=2, seed=18)
+    lengths = [5, 300, 40, 300, 0, 129]
+    inp = make_varlen_inputs(w, lengths)
+    cu = inp["cu_seqlens"].tolist()
+    o, S_T, _ = _run(kda, inp, gpu_device, 16)
+    perm = [5, 2, 0, 4, 3, 1]
+    pieces = {n: [inp[n][cu[i]:cu[i + 1]] for i in perm] for n in ("q", "k", "v", "z", "beta")}
+    inp2 = {n: torch.cat(pieces[n]) for n in pieces}
+    inp2["A"] = inp["A"]
+    inp2["S0"] = inp["S0"][perm].contiguous()
+    lens2 = [lengths[i] for i in perm]
+    inp2["cu_seqlens"] = torch.tensor([0] + list(np.cumsum(lens2)), dtype=torch.int64)
+    o2, S2, _ = _run(kda, inp2, gpu_device, 16)
+    cu2 = inp2["cu_seqlens"].tolist()
+    for pos, i in enumerate(perm):
+        assert torch.equal(S2[pos], S_T[i])
+        assert torch.equal(o2[cu2[pos]:cu2[pos + 1]], o[cu[i]:cu[i + 1]])
