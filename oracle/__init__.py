@@ -15,6 +15,9 @@ Parity status of each function (what pins it, see ``tests/test_oracle_pins.py``)
                T=1, dk=1), overwrite, capacity, an independent fp64 chunked
                model, split / linearity / independence invariants.
   decode_step -- pinned: T single steps equal one prefill over T, T=1 closed form.
+  prefill_conv, decode_step_conv -- the prologue of ``oracle/prologue.py``
+               (short convolutions, q/k normalization) followed by the pinned
+               recurrence; see that module for the readings and pins.
 """
 from __future__ import annotations
 
@@ -29,7 +32,8 @@ _SRC = os.path.join(_HERE, "kda_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
 _lib = None
 
-__all__ = ["build", "gate", "prefill", "decode_step", "max_threads"]
+__all__ = ["build", "gate", "prefill", "decode_step", "prefill_conv", "decode_step_conv",
+           "max_threads"]
 
 
 def build(force: bool = True) -> str:
@@ -136,3 +140,26 @@ def decode_step(q, k, v, z, beta, A, S, threads: int | None = None):
     q, k, v, z, beta = (_f64(x)[:, None] for x in (q, k, v, z, beta))
     o, S_new = prefill(q, k, v, z, beta, A, S, threads=threads)
     return o[:, 0], S_new
+
+
+def prefill_conv(q, k, v, z, beta, A, wq, wk, wv, conv_state=None, act="none", eps=1e-6,
+                 S0=None, threads: int | None = None):
+    """Prologue + recurrence over a segment of T tokens.
+
+    q, k, v raw (pre-convolution) [B,T,H,d]; wq, wk [H,dk,W], wv [H,dv,W];
+    conv_state None or (state_q, state_k, state_v), each [B,W-1,H,d].
+    Returns (o, S_T, (state_q, state_k, state_v)) in fp64."""
+    from .prologue import conv_norm
+    sq, sk, sv = conv_state if conv_state is not None else (None, None, None)
+    qh, kh, vc, states = conv_norm(q, k, v, wq, wk, wv, sq, sk, sv, act, eps)
+    o, S_T = prefill(qh, kh, vc, z, beta, A, S0, threads=threads)
+    return o, S_T, states
+
+
+def decode_step_conv(q, k, v, z, beta, A, wq, wk, wv, conv_state, S, act="none", eps=1e-6):
+    """One token through prologue and recurrence.  q, k, z [B,H,dk]; v [B,H,dv];
+    beta [B,H]; conv_state (state_q, state_k, state_v) each [B,W-1,H,d]; S [B,H,dk,dv].
+    Returns (o [B,H,dv], S_new, new conv states)."""
+    o, S_new, states = prefill_conv(*(_f64(x)[:, None] for x in (q, k, v, z, beta)), A,
+                                    wq, wk, wv, conv_state, act, eps, S)
+    return o[:, 0], S_new, states
