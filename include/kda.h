@@ -41,7 +41,9 @@
  *    are bitwise reproducible run to run (no atomics in the arithmetic).
  *  - Preconditions (not checked): q and k are L2-normalised over dk (the
  *    caller's Q/K normalisation; the chunkwise rescaling relies on |k_d| <= 1
- *    for its bf16 range), beta is used as given.
+ *    for its bf16 range), beta is used as given.  The *_conv entry points
+ *    take raw q, k, v instead and run the layer's prologue (short
+ *    convolutions and the q/k normalisation) themselves.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -53,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -186,6 +188,106 @@ kda_status kda_decode_step(int dtype, int64_t B, int64_t H, int64_t dk, int64_t 
                            const void *q, const void *k, const void *v, const void *z,
                            const void *beta, const float *A,
                            float *S, void *o, void *stream);
+
+/* ------------------------------------------------------------------------
+ * The layer prologue: short convolutions and Q/K normalisation.
+ *
+ * "Kimi K3 Open Weights: What Is Actually New ...", section 1, lists short
+ * convolutions and Q/K normalisation among the steps of a KDA prefill and
+ * says one-token decode keeps a convolution state persistent beside the
+ * recurrent state; section "Why '104B active' still understates the systems
+ * problem" counts that short-convolution state per request and layer.  The
+ * page gives no width, activation or normalisation guard; this library reads
+ * the steps as follows (each choice a parameter where one exists):
+ *
+ *   1. q, k and v each pass through their own causal depthwise convolution
+ *      over the tokens of a sequence, channel c of token t being
+ *          y_t[c] = sum_{j=0}^{W-1} w[c][j] * x_{t-(W-1)+j}[c]
+ *      (tap W-1 weighs the current token).  Tokens before the segment come
+ *      from the convolution state: the last W-1 RAW inputs of the sequence,
+ *      oldest first; a fresh sequence uses zeros.
+ *   2. Optionally y <- y * logistic(y) (KDA_ACT_SILU).
+ *   3. q and k are L2-normalised per token and head over their dk channels:
+ *      x <- x / sqrt(sum_c x[c]^2 + eps).  v is not normalised.
+ *   4. z and beta bypass the prologue.
+ * The recurrence then runs on the results exactly as in kda_prefill /
+ * kda_decode_step.
+ *
+ * Convolution-state layout: one tensor per input, [B, W-1, H, d] in `dtype`
+ * (the raw inputs themselves, so the state is exact).  States are passed as a
+ * HOST array of three device pointers {q state, k state, v state}.  With
+ * W = 1 the states are empty and the arrays are not read.
+ * ------------------------------------------------------------------------ */
+
+typedef enum kda_activation {
+    KDA_ACT_NONE = 0,
+    KDA_ACT_SILU = 1
+} kda_activation;
+
+/* Prologue parameters (a host struct; the taps are device memory). */
+typedef struct kda_short_conv {
+    int32_t width;       /* W, taps per channel, 1..4                         */
+    int32_t activation;  /* KDA_ACT_NONE or KDA_ACT_SILU                      */
+    float eps;           /* normalisation guard, finite and >= 0              */
+    int32_t reserved;    /* must be 0                                         */
+    const float *wq;     /* [H, dk, W] fp32, taps of q's channels             */
+    const float *wk;     /* [H, dk, W] fp32                                   */
+    const float *wv;     /* [H, dv, W] fp32                                   */
+} kda_short_conv;
+
+/*
+ * The prologue alone over a segment of T tokens:
+ *   in : q, k [B,T,H,dk], v [B,T,H,dv] raw (dtype); conv (host, non-NULL);
+ *        state_in: NULL (zero states) or 3 device pointers [B,W-1,H,d].
+ *   out: q_out, k_out [B,T,H,dk] (normalised), v_out [B,T,H,dv] (dtype,
+ *        rounded once from fp32); state_out: NULL (not written) or 3 device
+ *        pointers receiving the states after the segment (T = 0 copies
+ *        state_in).
+ * No output may overlap an input or another output (KDA_ERR_ALIAS).  Other
+ * conventions as kda_prefill; supported for the same dtypes and dk == dv in
+ * {16, 128}.  Invalid width / activation / eps / reserved: KDA_ERR_UNSUPPORTED.
+ */
+kda_status kda_conv_norm(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                         int64_t dv, const kda_short_conv *conv,
+                         const void *q, const void *k, const void *v,
+                         const void *const *state_in, void *const *state_out,
+                         void *q_out, void *k_out, void *v_out, void *stream);
+
+/* Bytes of device workspace kda_prefill_conv needs (the prologue's outputs:
+ * three [B,T,H,d] tensors in dtype, each rounded up to 256 bytes). */
+size_t kda_prefill_conv_workspace_size(int dtype, int64_t B, int64_t T, int64_t H,
+                                       int64_t dk, int64_t dv, int32_t chunk);
+
+/*
+ * Prologue + chunkwise prefill: kda_conv_norm of the raw q, k, v into the
+ * workspace, then kda_prefill_ex on the results.  Arguments as in those two
+ * calls; workspace (16-byte aligned, at least
+ * kda_prefill_conv_workspace_size bytes) must not overlap any other argument,
+ * and state_out must not overlap state_in.  Every check of both steps runs
+ * before the first launch.
+ */
+kda_status kda_prefill_conv(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                            int64_t dv, int32_t chunk, const kda_short_conv *conv,
+                            const void *q, const void *k, const void *v, const void *z,
+                            const void *beta, const float *A,
+                            const void *const *state_in, void *const *state_out,
+                            const float *S0, void *o, float *S_T,
+                            void *workspace, size_t workspace_bytes, void *stream,
+                            int32_t dv_per_block);
+
+/*
+ * One decode step with the prologue fused in: q, k, v [B,H,d] are the raw
+ * inputs of the new token; `state` (3 device pointers, required when W > 1)
+ * holds each sequence's convolution states and is updated in place (shifted
+ * by one token), as S is.  The result is that of kda_conv_norm over the one
+ * token followed by kda_decode_step.  State tensors must not overlap each
+ * other, an input, S or o.
+ */
+kda_status kda_decode_step_conv(int dtype, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                                const kda_short_conv *conv,
+                                const void *q, const void *k, const void *v, const void *z,
+                                const void *beta, const float *A,
+                                void *const *state, float *S, void *o, void *stream);
 
 #ifdef __cplusplus
 }

@@ -6,8 +6,10 @@ binding over it: torch supplies device memory and streams, every arithmetic
 step runs in the library.  There is no CPU fallback; calling into the binding
 without a built library or without a GPU raises.
 """
-from .kda import (KDAError, abi_version, checkpoint_rows, decode_step, library_path, prefill,
-                  prefill_varlen, prefill_workspace_size)
+from .kda import (KDAError, ShortConv, abi_version, checkpoint_rows, conv_norm, decode_step,
+                  decode_step_conv, library_path, prefill, prefill_conv,
+                  prefill_conv_workspace_size, prefill_varlen, prefill_workspace_size)
 
-__all__ = ["KDAError", "abi_version", "checkpoint_rows", "decode_step", "library_path",
-           "prefill", "prefill_varlen", "prefill_workspace_size"]
+__all__ = ["KDAError", "ShortConv", "abi_version", "checkpoint_rows", "conv_norm",
+           "decode_step", "decode_step_conv", "library_path", "prefill", "prefill_conv",
+           "prefill_conv_workspace_size", "prefill_varlen", "prefill_workspace_size"]

@@ -79,7 +79,7 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
                         const void *v, const void *z, const void *beta, const float *A,
                         const float *S0, void *o, float *S_T, int32_t ckpt_every,
                         float *ckpt, int64_t n_ckpt, void *workspace, size_t workspace_bytes,
-                        void *stream, int32_t dv_per_block) {
+                        void *stream, int32_t dv_per_block, bool check_only = false) {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || n_ckpt < 0 || ckpt_every < 0)
         return KDA_ERR_SHAPE;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -142,7 +142,7 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
         for (const Range &r : all)
             if (overlaps(rws, r)) return KDA_ERR_ALIAS;
     }
-    if (bh == 0) return KDA_OK;
+    if (bh == 0 || check_only) return KDA_OK;
 
     kda::PrefillArgs a;
     a.dtype = dtype; a.B = B; a.T = T; a.H = H; a.D = D; a.chunk = chunk;
@@ -235,9 +235,276 @@ kda_status kda_decode_step(int dtype, int64_t B, int64_t H, int64_t dk, int64_t 
         if (overlaps(rS, r)) return KDA_ERR_ALIAS;
     if (bh == 0) return KDA_OK;
 
-    kda::DecodeArgs a;
+    kda::DecodeArgs a{};
     a.dtype = dtype; a.B = B; a.H = H; a.D = D;
     a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.A = A; a.S = S; a.o = o;
+    a.conv = 0;
+    a.stream = (hipStream_t)stream;
+    return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ prologue ----
+
+namespace {
+
+size_t round256(int64_t bytes) { return (size_t)((bytes + 255) / 256 * 256); }
+
+// Checked prologue parameters of one call.
+struct ConvSpec {
+    int W, act;
+    float eps;
+    const float *w[3];
+    const void *sin[3];
+    void *sout[3];
+    Range rw[3], rsin[3], rsout[3];
+};
+
+// Validates the prologue parameters and state arrays of a call over B
+// sequences of H heads (d = D channels per head).  `need_state_in`: the state
+// array is required (decode).  Fills `cs` on success.
+kda_status conv_check(int dtype, int64_t B, int64_t H, int64_t D, const kda_short_conv *conv,
+                      const void *const *state_in, void *const *state_out, bool need_state_in,
+                      ConvSpec *cs) {
+    if (!conv) return KDA_ERR_NULL;
+    if (conv->width < 1 || conv->width > 4 || conv->reserved != 0) return KDA_ERR_UNSUPPORTED;
+    if (conv->activation != KDA_ACT_NONE && conv->activation != KDA_ACT_SILU)
+        return KDA_ERR_UNSUPPORTED;
+    if (!(conv->eps >= 0.0f) || !(conv->eps <= 3.4e38f)) return KDA_ERR_UNSUPPORTED;
+    if (!kda::conv_supported(dtype, D)) return KDA_ERR_UNSUPPORTED;
+    const int W = conv->width;
+    const int64_t esz = dtype == KDA_BF16 ? 2 : 4;
+    int64_t bw, bwh, nst;
+    if (!mul_ok(B, W - 1, kMaxElems, &bw) || !mul_ok(bw, H, kMaxElems, &bwh) ||
+        !mul_ok(bwh, D, kMaxElems / 4, &nst))
+        return KDA_ERR_SHAPE;
+    cs->W = W;
+    cs->act = conv->activation;
+    cs->eps = conv->eps;
+    cs->w[0] = conv->wq; cs->w[1] = conv->wk; cs->w[2] = conv->wv;
+    const bool states = W > 1;
+    for (int i = 0; i < 3; ++i) {
+        cs->sin[i] = states && state_in ? state_in[i] : nullptr;
+        cs->sout[i] = states && state_out ? state_out[i] : nullptr;
+    }
+    if (H > 0)
+        for (int i = 0; i < 3; ++i)
+            if (!cs->w[i]) return KDA_ERR_NULL;
+    if (states && B > 0 && H > 0) {
+        if (need_state_in && !state_in) return KDA_ERR_NULL;
+        for (int i = 0; i < 3; ++i) {
+            if (state_in && !cs->sin[i]) return KDA_ERR_NULL;
+            if (state_out && !cs->sout[i]) return KDA_ERR_NULL;
+        }
+    }
+    for (int i = 0; i < 3; ++i) {
+        const void *ptrs[] = {cs->w[i], cs->sin[i], cs->sout[i]};
+        for (const void *p : ptrs)
+            if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+        cs->rw[i] = range_of(cs->w[i], H * D * W * 4);
+        cs->rsin[i] = range_of(cs->sin[i], nst * esz);
+        cs->rsout[i] = range_of(cs->sout[i], nst * esz);
+    }
+    // state outputs must not overlap each other, the taps or the state inputs
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) {
+            if (i != j && overlaps(cs->rsout[i], cs->rsout[j])) return KDA_ERR_ALIAS;
+            if (overlaps(cs->rsout[i], cs->rw[j])) return KDA_ERR_ALIAS;
+            if (!need_state_in && overlaps(cs->rsout[i], cs->rsin[j])) return KDA_ERR_ALIAS;
+        }
+    return KDA_OK;
+}
+
+// Sizes the prologue kernel can address: (tile + 3) token rows in 32-bit
+// buffer offsets, and the grid.
+bool conv_sizes_ok(int dtype, int64_t B, int64_t T, int64_t H, int64_t D) {
+    const int64_t esz = dtype == KDA_BF16 ? 2 : 4;
+    const int64_t tt = kda::conv_tile_tokens(dtype);
+    if (H * D * esz * (tt + 3) >= ((int64_t)1 << 31)) return false;
+    const int64_t ntile = T > 0 ? (T + tt - 1) / tt : 1;
+    const int64_t nslab = (H * (D / 8) + 63) / 64;
+    int64_t n1, n2;
+    return mul_ok(B, nslab, kMaxElems, &n1) && mul_ok(n1, (ntile + 3) / 4, kMaxElems, &n2) &&
+           n2 < ((int64_t)1 << 32) - 1;
+}
+
+kda::ConvNormArgs conv_args(int dtype, int64_t B, int64_t T, int64_t H, int64_t D,
+                            const ConvSpec &cs, const void *const x[3], void *const y[3],
+                            void *stream) {
+    kda::ConvNormArgs a{};
+    a.dtype = dtype; a.B = B; a.T = T; a.H = H; a.D = D;
+    for (int i = 0; i < 3; ++i) {
+        a.t[i].x = x[i];
+        a.t[i].w = cs.w[i];
+        a.t[i].sin = cs.sin[i];
+        a.t[i].y = y[i];
+        a.t[i].sout = cs.sout[i];
+        a.t[i].norm = i < 2;
+    }
+    a.W = cs.W; a.act = cs.act; a.eps = cs.eps;
+    a.stream = (hipStream_t)stream;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_conv_norm(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                         const kda_short_conv *conv, const void *q, const void *k,
+                         const void *v, const void *const *state_in, void *const *state_out,
+                         void *q_out, void *k_out, void *v_out, void *stream) {
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (dk != dv) return KDA_ERR_UNSUPPORTED;
+    const int64_t D = dk, esz = dtype == KDA_BF16 ? 2 : 4;
+    ConvSpec cs;
+    const kda_status st = conv_check(dtype, B, H, D, conv, state_in, state_out, false, &cs);
+    if (st != KDA_OK) return st;
+    int64_t bt, bth, nin;
+    if (!mul_ok(B, T, kMaxElems, &bt) || !mul_ok(bt, H, kMaxElems, &bth) ||
+        !mul_ok(bth, D, kMaxElems / 4, &nin))
+        return KDA_ERR_SHAPE;
+    if (!conv_sizes_ok(dtype, B, T, H, D)) return KDA_ERR_SHAPE;
+    if (nin > 0 && (!q || !k || !v || !q_out || !k_out || !v_out)) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, q_out, k_out, v_out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const Range rin[] = {range_of(q, nin * esz), range_of(k, nin * esz), range_of(v, nin * esz),
+                         cs.rw[0], cs.rw[1], cs.rw[2], cs.rsin[0], cs.rsin[1], cs.rsin[2]};
+    const Range rout[] = {range_of(q_out, nin * esz), range_of(k_out, nin * esz),
+                          range_of(v_out, nin * esz), cs.rsout[0], cs.rsout[1], cs.rsout[2]};
+    for (int i = 0; i < 6; ++i) {
+        for (const Range &r : rin)
+            if (overlaps(rout[i], r)) return KDA_ERR_ALIAS;
+        for (int j = 0; j < 6; ++j)
+            if (i != j && overlaps(rout[i], rout[j])) return KDA_ERR_ALIAS;
+    }
+    if (B == 0 || H == 0) return KDA_OK;
+    const void *x[3] = {q, k, v};
+    void *y[3] = {q_out, k_out, v_out};
+    const kda::ConvNormArgs a = conv_args(dtype, B, T, H, D, cs, x, y, stream);
+    return kda::launch_conv_norm(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_prefill_conv_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                                       int64_t dv, int32_t chunk) {
+    (void)chunk;
+    if ((dtype != KDA_F32 && dtype != KDA_BF16) || B < 0 || T < 0 || H < 0 || dk <= 0 ||
+        dv <= 0)
+        return 0;
+    const int64_t esz = dtype == KDA_BF16 ? 2 : 4;
+    int64_t bt, bth, nk, nv;
+    if (!mul_ok(B, T, kMaxElems, &bt) || !mul_ok(bt, H, kMaxElems, &bth) ||
+        !mul_ok(bth, dk, kMaxElems / 4, &nk) || !mul_ok(bth, dv, kMaxElems / 4, &nv))
+        return 0;
+    return 2 * round256(nk * esz) + round256(nv * esz);
+}
+
+kda_status kda_prefill_conv(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                            int32_t chunk, const kda_short_conv *conv, const void *q,
+                            const void *k, const void *v, const void *z, const void *beta,
+                            const float *A, const void *const *state_in,
+                            void *const *state_out, const float *S0, void *o, float *S_T,
+                            void *workspace, size_t workspace_bytes, void *stream,
+                            int32_t dv_per_block) {
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (dk != dv) return KDA_ERR_UNSUPPORTED;
+    const int64_t D = dk, esz = dtype == KDA_BF16 ? 2 : 4;
+    ConvSpec cs;
+    kda_status st = conv_check(dtype, B, H, D, conv, state_in, state_out, false, &cs);
+    if (st != KDA_OK) return st;
+    int64_t bt, bth, nin;
+    if (!mul_ok(B, T, kMaxElems, &bt) || !mul_ok(bt, H, kMaxElems, &bth) ||
+        !mul_ok(bth, D, kMaxElems / 4, &nin))
+        return KDA_ERR_SHAPE;
+    if (!conv_sizes_ok(dtype, B, T, H, D)) return KDA_ERR_SHAPE;
+    const size_t need = kda_prefill_conv_workspace_size(dtype, B, T, H, dk, dv, chunk);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return KDA_ERR_MISALIGNED;
+    char *ws = static_cast<char *>(workspace);
+    void *qh = need > 0 ? ws : nullptr;
+    void *kh = need > 0 ? ws + round256(nin * esz) : nullptr;
+    void *vh = need > 0 ? ws + 2 * round256(nin * esz) : nullptr;
+    // the recurrence's own checks, on the prologue's outputs, before any launch
+    st = prefill_impl(dtype, B, T, H, dk, dv, chunk, nullptr, qh, kh, vh, z, beta, A, S0, o, S_T,
+                      0, nullptr, 0, nullptr, 0, stream, dv_per_block, true);
+    if (st != KDA_OK) return st;
+    if (nin > 0 && (!q || !k || !v)) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const int64_t bh = B * H;
+    const Range rws = range_of(need > 0 ? workspace : nullptr, (int64_t)need);
+    const Range rin[] = {range_of(q, nin * esz), range_of(k, nin * esz), range_of(v, nin * esz),
+                         range_of(z, nin * esz), range_of(beta, bth * esz), range_of(A, H * 4),
+                         range_of(S0, bh * D * D * 4), cs.rw[0], cs.rw[1], cs.rw[2],
+                         cs.rsin[0], cs.rsin[1], cs.rsin[2]};
+    const Range rout[] = {range_of(o, nin * esz), range_of(S_T, bh * D * D * 4), rws,
+                          cs.rsout[0], cs.rsout[1], cs.rsout[2]};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 13; ++j) {
+            // S_T == S0 is the allowed in-place carry of the recurrent state
+            if (i == 1 && j == 6 && (const void *)S_T == (const void *)S0) continue;
+            if (overlaps(rout[i], rin[j])) return KDA_ERR_ALIAS;
+        }
+        for (int j = 0; j < 6; ++j)
+            if (i != j && overlaps(rout[i], rout[j])) return KDA_ERR_ALIAS;
+    }
+    if (bh == 0) return KDA_OK;
+    const void *x[3] = {q, k, v};
+    void *y[3] = {qh, kh, vh};
+    const kda::ConvNormArgs a = conv_args(dtype, B, T, H, D, cs, x, y, stream);
+    if (kda::launch_conv_norm(a) != hipSuccess) return KDA_ERR_HIP;
+    return prefill_impl(dtype, B, T, H, dk, dv, chunk, nullptr, qh, kh, vh, z, beta, A, S0, o,
+                        S_T, 0, nullptr, 0, nullptr, 0, stream, dv_per_block);
+}
+
+kda_status kda_decode_step_conv(int dtype, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                                const kda_short_conv *conv, const void *q, const void *k,
+                                const void *v, const void *z, const void *beta, const float *A,
+                                void *const *state, float *S, void *o, void *stream) {
+    if (B < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (dk != dv || !kda::decode_supported(dtype, dk)) return KDA_ERR_UNSUPPORTED;
+    const int64_t D = dk, esz = dtype == KDA_BF16 ? 2 : 4;
+    ConvSpec cs;
+    // the states are read and written in place: pass them as input and output
+    kda_status st = conv_check(dtype, B, H, D, conv, state, state, true, &cs);
+    if (st != KDA_OK) return st;
+    int64_t bh, nin, nstate;
+    if (!mul_ok(B, H, kMaxElems, &bh) || !mul_ok(bh, D, kMaxElems / 4, &nin) ||
+        !mul_ok(bh, D * D, kMaxElems / 4, &nstate))
+        return KDA_ERR_SHAPE;
+    if (bh > 0x7fffffff) return KDA_ERR_SHAPE;
+    if (!A) return KDA_ERR_NULL;
+    if (bh > 0 && (!q || !k || !v || !z || !beta || !S || !o)) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, z, beta, A, S, o};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const Range rin[] = {range_of(q, nin * esz), range_of(k, nin * esz), range_of(v, nin * esz),
+                         range_of(z, nin * esz), range_of(beta, bh * esz), range_of(A, H * 4),
+                         cs.rw[0], cs.rw[1], cs.rw[2]};
+    const Range rout[] = {range_of(o, nin * esz), range_of(S, nstate * 4), cs.rsin[0],
+                          cs.rsin[1], cs.rsin[2]};
+    for (int i = 0; i < 5; ++i) {
+        for (const Range &r : rin)
+            if (overlaps(rout[i], r)) return KDA_ERR_ALIAS;
+        for (int j = 0; j < 5; ++j)
+            if (i != j && overlaps(rout[i], rout[j])) return KDA_ERR_ALIAS;
+    }
+    if (bh == 0) return KDA_OK;
+    kda::DecodeArgs a{};
+    a.dtype = dtype; a.B = B; a.H = H; a.D = D;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.A = A; a.S = S; a.o = o;
+    a.conv = 1;
+    a.wq = cs.w[0]; a.wk = cs.w[1]; a.wv = cs.w[2];
+    a.cq = const_cast<void *>(cs.sin[0]);
+    a.ck = const_cast<void *>(cs.sin[1]);
+    a.cv = const_cast<void *>(cs.sin[2]);
+    a.W = cs.W; a.act = cs.act; a.eps = cs.eps;
     a.stream = (hipStream_t)stream;
     return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -1,0 +1,262 @@
+// kda_conv.hip -- the prologue of a KDA layer (gfx950): short causal depthwise
+// convolutions of q, k and v over tokens, an optional SiLU, and L2
+// normalization of q and k per token and head.
+//
+// "Kimi K3 Open Weights: What Is Actually New", section 1, puts short
+// convolutions and Q/K normalization ahead of the decay products and chunk
+// interactions of a KDA prefill.  The page fixes neither the width nor an
+// activation nor the normalization's guard; this library reads them as: per
+// channel c,  y_t[c] = sum_{j<W} w[c][j] x_{t-(W-1)+j}[c]  (tap W-1 on the
+// current token, earlier tokens of the sequence from a convolution state of
+// the last W-1 raw inputs, zeros for a fresh sequence), then optionally
+// y * logistic(y), then q, k <- y / sqrt(sum_c y^2 + eps).
+//
+// The pass is bound by HBM: each input element is read once and each output
+// written once, ~2 * sizeof(dtype) bytes per element and tensor.  Layout of
+// the work:
+//  * A lane owns one octet of 8 consecutive channels of a token row (16 bytes
+//    in bf16: one buffer_load_dwordx4), so 64 lanes cover 512 channels of a
+//    row, four heads of 128.  A head's 128 channels are 16 lanes, one DPP row,
+//    and the per-token sum of squares reduces inside it with four DPP adds.
+//  * A wave owns TT consecutive tokens of its 512 channels and keeps the TT
+//    rows plus the three rows before them in registers; the convolution is a
+//    sliding window over those rows (W <= 4 taps, zero-padded to 4).  All
+//    TT + 3 loads are issued before any arithmetic.
+//  * The four waves of a workgroup take four consecutive tiles of the same
+//    channels, so a tile's three leading rows are its neighbour's last rows
+//    (a cache hit, not a second HBM read).
+//  * The wave holding a sequence's last tile writes the new convolution state
+//    (the last W-1 raw rows, exact copies) from its registers.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+__device__ __forceinline__ float lo16(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, bf16x2{(bf16)a, (bf16)b});
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Eight consecutive channels of one token row, as loaded.
+template <typename TI> struct Oct;
+template <> struct Oct<bf16> {
+    uint32_t u[4];
+    __device__ __forceinline__ float at(int e) const { return e & 1 ? hi16(u[e >> 1]) : lo16(u[e >> 1]); }
+    __device__ __forceinline__ void zero() { u[0] = u[1] = u[2] = u[3] = 0u; }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+        const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+        u[0] = r[0]; u[1] = r[1]; u[2] = r[2]; u[3] = r[3];
+    }
+    __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t rs, int voff, int soff) const {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{u[0], u[1], u[2], u[3]}, rs, voff, soff, 0);
+    }
+    __device__ __forceinline__ static void store_f32(const float *y, __amdgpu_buffer_rsrc_t rs,
+                                                     int voff, int soff) {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7])}, rs,
+            voff, soff, 0);
+    }
+};
+template <> struct Oct<float> {
+    uint32_t u[8];
+    __device__ __forceinline__ float at(int e) const { return __uint_as_float(u[e]); }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = 0u;
+    }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, soff, 0);
+        u[0] = a[0]; u[1] = a[1]; u[2] = a[2]; u[3] = a[3];
+        u[4] = b[0]; u[5] = b[1]; u[6] = b[2]; u[7] = b[3];
+    }
+    __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t rs, int voff, int soff) const {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{u[0], u[1], u[2], u[3]}, rs, voff, soff, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{u[4], u[5], u[6], u[7]}, rs, voff + 16, soff, 0);
+    }
+    __device__ __forceinline__ static void store_f32(const float *y, __amdgpu_buffer_rsrc_t rs,
+                                                     int voff, int soff) {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                  __float_as_uint(y[3])}, rs, voff, soff, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]),
+                  __float_as_uint(y[7])}, rs, voff + 16, soff, 0);
+    }
+};
+
+// DPP lane exchange inside a row of 16 lanes.
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7-i within each half row
+constexpr int kRowMirror = 0x140;     // lane i <- lane 15-i within the row
+
+// Sum over the LPR consecutive lanes that hold one head's channels (LPR in
+// {2, 16}; groups are aligned to LPR).
+template <int LPR> __device__ __forceinline__ float head_sum(float x) {
+    static_assert(LPR == 2 || LPR == 16, "one head = 2 or 16 lanes");
+    x += dpp<kQuadXor1>(x);
+    if constexpr (LPR == 16) {
+        x += dpp<kQuadXor2>(x);
+        x += dpp<kRowHalfMirror>(x);
+        x += dpp<kRowMirror>(x);
+    }
+    return x;
+}
+
+__device__ __forceinline__ float silu(float y) {
+    // y * logistic(y); e = 2^(-y log2 e) -> inf for y -> -inf gives y * 0
+    const float e = __builtin_amdgcn_exp2f(-y * kLog2e);
+    return y * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+}  // namespace
+
+// One workgroup = 4 waves = 4 consecutive token tiles of one 512-channel slab
+// of one tensor (blockIdx.y) of one sequence.
+template <typename TI, int D, int TT>
+__global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormArgs p) {
+    constexpr int ESZ = sizeof(TI);
+    constexpr int LPR = D / 8;   // lanes per head row
+    const ConvTensor ct = blockIdx.y == 0 ? p.t[0] : (blockIdx.y == 1 ? p.t[1] : p.t[2]);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t H = p.H, T = p.T;
+    const int64_t rowoct = H * (D / 8);          // channel octets per token row
+    const int64_t nslab = (rowoct + 63) / 64;
+    int64_t x = blockIdx.x;
+    const int64_t grp = x % p.ngroup;
+    x /= p.ngroup;
+    const int64_t slab = x % nslab;
+    const int64_t b = x / nslab;
+    const int64_t tile = grp * 4 + wave;
+    if (tile >= p.ntile) return;   // wave-uniform
+
+    const int64_t c8 = slab * 64 + lane;
+    const bool active = c8 < rowoct;
+    const int64_t c8c = active ? c8 : 0;         // clamped for the weight reads
+    const int rowbytes = (int)(H * D * ESZ);      // host-checked: (TT + 3) rows fit in int
+    const int voff = (int)(c8 * 8 * ESZ);
+    const int64_t t0 = tile * TT;
+    const int W = p.W;
+
+    // taps zero-padded to 4: tap 3 weighs the current token
+    float wt[8][4];
+    {
+        const float *wp = ct.w + c8c * 8 * W;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wt[e][j] = j >= 4 - W ? wp[e * W + j - (4 - W)] : 0.0f;
+    }
+
+    // rows r = 0 .. TT+2 hold tokens t0 - 3 + r
+    Oct<TI> xr[TT + 3];
+    const int64_t nrows = T - t0 < TT ? (T - t0 > 0 ? T - t0 : 0) : TT;
+    const int64_t rowel = H * D;
+    const char *xb = static_cast<const char *>(ct.x) + ((b * T + t0) * rowel) * ESZ;
+    {
+        const auto rs = make_rsrc(xb, nrows * rowbytes);
+#pragma unroll
+        for (int s = 0; s < TT; ++s) xr[3 + s].load(rs, voff, s * rowbytes);
+    }
+    if (tile > 0) {
+        const auto rs = make_rsrc(xb - 3 * (int64_t)rowbytes, 3 * (int64_t)rowbytes);
+#pragma unroll
+        for (int r = 0; r < 3; ++r) xr[r].load(rs, voff, r * rowbytes);
+    } else if (ct.sin && W > 1) {
+        // state row (W-1) + (token) for tokens -3..-1; rows before the state are 0
+        const char *sb = static_cast<const char *>(ct.sin) + (b * (W - 1) * rowel) * ESZ;
+        const auto rs = make_rsrc(sb, (int64_t)(W - 1) * rowbytes);
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const int sr = r - (4 - W);
+            if (sr >= 0) xr[r].load(rs, voff, sr * rowbytes);
+            else xr[r].zero();
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) xr[r].zero();
+    }
+
+    char *yb = static_cast<char *>(ct.y) + ((b * T + t0) * rowel) * ESZ;
+    const auto ys = make_rsrc(yb, nrows * rowbytes);
+    const float eps = p.eps;
+#pragma unroll
+    for (int s = 0; s < TT; ++s) {
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            y[e] = wt[e][0] * xr[s].at(e);
+            y[e] = fmaf(wt[e][1], xr[s + 1].at(e), y[e]);
+            y[e] = fmaf(wt[e][2], xr[s + 2].at(e), y[e]);
+            y[e] = fmaf(wt[e][3], xr[s + 3].at(e), y[e]);
+        }
+        if (p.act) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = silu(y[e]);
+        }
+        if (ct.norm) {
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
+            ss = head_sum<LPR>(ss);
+            const float r = __builtin_amdgcn_rsqf(ss + eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= r;
+        }
+        if (active) Oct<TI>::store_f32(y, ys, voff, s * rowbytes);
+    }
+
+    // the last tile of the sequence writes the new state: raw tokens T-(W-1) .. T-1
+    if (tile == p.ntile - 1 && ct.sout && W > 1 && active) {
+        char *sb = static_cast<char *>(ct.sout) + (b * (W - 1) * rowel) * ESZ;
+        const auto rs = make_rsrc(sb, (int64_t)(W - 1) * rowbytes);
+        const int64_t first = T - (W - 1);   // token of state row 0 (may be < 0)
+#pragma unroll
+        for (int r = 0; r < TT + 3; ++r) {
+            const int64_t i = t0 - 3 + r - first;
+            if (i >= 0 && i < W - 1) xr[r].store(rs, voff, (int)i * rowbytes);
+        }
+    }
+}
+
+bool conv_supported(int dtype, int64_t D) {
+    return (dtype == 0 || dtype == 1) && (D == 16 || D == 128);
+}
+
+int conv_tile_tokens(int dtype) { return dtype == 1 ? 16 : 8; }
+
+template <typename TI, int D, int TT>
+static hipError_t launch_conv_t(const ConvNormArgs &a0) {
+    ConvNormArgs a = a0;
+    const int64_t ntile = a.T > 0 ? (a.T + TT - 1) / TT : 1;   // T = 0 still carries the state
+    const int64_t rowoct = a.H * (D / 8);
+    const int64_t nslab = (rowoct + 63) / 64;
+    a.ntile = ntile;
+    a.ngroup = (ntile + 3) / 4;
+    const int64_t nblk = a.B * nslab * a.ngroup;
+    hipLaunchKernelGGL((kda_conv_norm_kernel<TI, D, TT>), dim3((unsigned)nblk, 3), dim3(256), 0,
+                       a.stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_norm(const ConvNormArgs &a) {
+    if (a.dtype == 1) {
+        if (a.D == 128) return launch_conv_t<bf16, 128, 16>(a);
+        return launch_conv_t<bf16, 16, 16>(a);
+    }
+    if (a.D == 128) return launch_conv_t<float, 128, 8>(a);
+    return launch_conv_t<float, 16, 8>(a);
+}
+
+}  // namespace kda

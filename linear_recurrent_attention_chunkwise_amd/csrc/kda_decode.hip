@@ -17,31 +17,72 @@
 // is written with nontemporal stores: it is not read again within the step,
 // and streaming it past the caches keeps the read stream of the other heads'
 // states at full rate (measured on MI355X: 6.9 TB/s instead of 5.3 TB/s).
+//
+// The CONV instantiation fuses the layer's prologue into the step (same page
+// section: decode keeps "convolution state and recurrent state" persistent):
+// each of q, k, v is convolved with its W-1 previous raw inputs, held in a
+// per-sequence convolution state that the step shifts in place, and q, k are
+// L2-normalized.  The normalization is a scalar per vector, so it is applied
+// after the pass over S:  S^T(alpha k^) = S^T(alpha k) / |k|,  and likewise
+// for q and for q^.k^.  The prologue adds about 4% to the step's HBM bytes.
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 
-template <typename TI, int D, int NT>
-__global__ __launch_bounds__(NT) void kda_decode_kernel(
-    const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v,
-    const TI *__restrict__ z, const TI *__restrict__ beta, const float *__restrict__ A,
-    float *__restrict__ S, TI *__restrict__ o, int64_t H) {
+// One channel of the fused prologue: the short causal convolution of the
+// current raw input x with the W-1 raw inputs before it (convolution state
+// rows, oldest first; tap W-1 weighs x), optionally followed by SiLU.  The
+// state rows shift down by one and x becomes the newest row, in place; the
+// stored values are the raw inputs, so the state stays exact.
+template <typename TI>
+__device__ __forceinline__ float conv_step(TI x, const float *w, TI *st, int64_t stride, int W,
+                                           int act) {
+    TI raw[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+        if (j < W - 1) raw[j] = st[j * stride];
+    float y = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+        if (j < W - 1) y = fmaf(w[j], to_f32(raw[j]), y);
+    y = fmaf(w[W - 1], to_f32(x), y);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        if (j < W - 2) st[j * stride] = raw[j + 1];
+    if (W > 1) st[(W - 2) * stride] = x;
+    if (act) {
+        const float e = __builtin_amdgcn_exp2f(-y * kLog2e);
+        y *= __builtin_amdgcn_rcpf(1.0f + e);
+    }
+    return y;
+}
+
+template <typename TI, int D, int NT, bool CONV>
+__global__ __launch_bounds__(NT) void kda_decode_kernel(DecodeArgs p) {
     constexpr int NCG = D / 4;          // float4 column quads per state row
     constexpr int RG = NT / NCG;        // row groups
     constexpr int RPT = D / RG;         // state rows per thread
     constexpr int NWAVE = NT / 64;
+    constexpr int NRED = CONV ? 3 : 1;  // q.k, and with the prologue |q|^2, |k|^2
     static_assert(RG * RPT == D && NCG <= 64 && NT % 64 == 0, "bad decode tiling");
 
     __shared__ float s_alpha[D], s_k[D], s_ak[D], s_aq[D];
-    __shared__ float s_red[NWAVE][2][D];
-    __shared__ float s_qk[NWAVE];
+    __shared__ __attribute__((aligned(16))) float s_v[CONV ? D : 1];
+    __shared__ __attribute__((aligned(16))) float s_red[NWAVE][2][D];
+    __shared__ float s_qk[NWAVE][NRED];
 
+    const TI *__restrict__ q = static_cast<const TI *>(p.q);
+    const TI *__restrict__ k = static_cast<const TI *>(p.k);
+    const TI *__restrict__ v = static_cast<const TI *>(p.v);
+    const TI *__restrict__ z = static_cast<const TI *>(p.z);
+    const TI *__restrict__ beta = static_cast<const TI *>(p.beta);
+    const int64_t H = p.H;
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % H);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = tid % NCG, rg = tid / NCG;
-    float *Sp = S + bh * (int64_t)(D * D);
+    float *Sp = p.S + bh * (int64_t)(D * D);
 
     // Issue the whole state read first; it streams while the gate is computed.
     f32x4 s[RPT];
@@ -49,21 +90,45 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
     for (int m = 0; m < RPT; ++m)
         s[m] = *reinterpret_cast<const f32x4 *>(Sp + (rg + RG * m) * D + 4 * cg);
 
-    float qk = 0.0f;
+    float red[NRED];
+#pragma unroll
+    for (int r = 0; r < NRED; ++r) red[r] = 0.0f;
     if (tid < D) {
         const int64_t off = bh * D + tid;
-        const float zi = to_f32(z[off]), ki = to_f32(k[off]), qi = to_f32(q[off]);
-        const float c2 = -__builtin_amdgcn_exp2f(A[h] * kLog2e) * kLog2e;
+        const float zi = to_f32(z[off]);
+        float ki, qi;
+        if constexpr (CONV) {
+            // prologue: convolve q, k, v (states updated in place); q and k are
+            // normalized below through their squared norms
+            const int64_t b = bh / H;
+            const int64_t hd = H * D;
+            const int64_t sb = b * (p.W - 1) * hd + (int64_t)h * D + tid;
+            const int64_t wb = ((int64_t)h * D + tid) * p.W;
+            ki = conv_step(k[off], p.wk + wb, static_cast<TI *>(p.ck) + sb, hd, p.W, p.act);
+            qi = conv_step(q[off], p.wq + wb, static_cast<TI *>(p.cq) + sb, hd, p.W, p.act);
+            s_v[tid] = conv_step(v[off], p.wv + wb, static_cast<TI *>(p.cv) + sb, hd, p.W, p.act);
+            red[1] = qi * qi;
+            red[2] = ki * ki;
+        } else {
+            ki = to_f32(k[off]);
+            qi = to_f32(q[off]);
+        }
+        const float c2 = -__builtin_amdgcn_exp2f(p.A[h] * kLog2e) * kLog2e;
         const float al = kda_alpha(c2, zi);
         s_alpha[tid] = al;
         s_k[tid] = ki;
         s_ak[tid] = al * ki;
         s_aq[tid] = al * qi;
-        qk = qi * ki;
+        red[0] = qi * ki;
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) qk += __shfl_xor(qk, off);
-    if (lane == 0) s_qk[wave] = qk;
+    for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+        for (int r = 0; r < NRED; ++r) red[r] += __shfl_xor(red[r], off);
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < NRED; ++r) s_qk[wave][r] = red[r];
+    }
     __syncthreads();
 
     f32x4 w = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
@@ -89,28 +154,43 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
     __syncthreads();
 
     f32x4 wt = {0.f, 0.f, 0.f, 0.f}, yt = {0.f, 0.f, 0.f, 0.f};
-    float qkt = 0.0f;
+    float tot[NRED];
+#pragma unroll
+    for (int r = 0; r < NRED; ++r) tot[r] = 0.0f;
 #pragma unroll
     for (int wv = 0; wv < NWAVE; ++wv) {
         wt += *reinterpret_cast<const f32x4 *>(&s_red[wv][0][4 * cg]);
         yt += *reinterpret_cast<const f32x4 *>(&s_red[wv][1][4 * cg]);
-        qkt += s_qk[wv];
+#pragma unroll
+        for (int r = 0; r < NRED; ++r) tot[r] += s_qk[wv][r];
+    }
+    float qkt = tot[0], kscale = 1.0f;
+    f32x4 vv;
+    if constexpr (CONV) {
+        // q^ = q / sqrt(|q|^2 + eps), k^ likewise: S^T(alpha k^) = rk S^T(alpha k), ...
+        const float rq = __builtin_amdgcn_rsqf(tot[1] + p.eps);
+        const float rk = __builtin_amdgcn_rsqf(tot[2] + p.eps);
+        wt *= rk;
+        yt *= rq;
+        qkt *= rq * rk;
+        kscale = rk;
+        vv = *reinterpret_cast<const f32x4 *>(&s_v[4 * cg]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv[e] = to_f32(v[bh * D + 4 * cg + e]);
     }
     const float bt = to_f32(beta[bh]);
-    f32x4 vv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vv[e] = to_f32(v[bh * D + 4 * cg + e]);
     const f32x4 u = bt * (vv - wt);
     if (rg == 0) {
         const f32x4 ov = yt + qkt * u;
-        TI *op = o + bh * D + 4 * cg;
+        TI *op = static_cast<TI *>(p.o) + bh * D + 4 * cg;
 #pragma unroll
         for (int e = 0; e < 4; ++e) op[e] = from_f32<TI>(ov[e]);
     }
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int i = rg + RG * m;
-        const f32x4 ns = s_alpha[i] * s[m] + s_k[i] * u;
+        const f32x4 ns = s_alpha[i] * s[m] + (kscale * s_k[i]) * u;
         __builtin_nontemporal_store(ns, reinterpret_cast<f32x4 *>(Sp + i * D + 4 * cg));
     }
 }
@@ -122,9 +202,12 @@ bool decode_supported(int dtype, int64_t D) {
 template <typename TI, int D, int NT>
 static hipError_t launch_decode_t(const DecodeArgs &a) {
     const int64_t nblk = a.B * a.H;
-    hipLaunchKernelGGL((kda_decode_kernel<TI, D, NT>), dim3((unsigned)nblk), dim3(NT), 0,
-                       a.stream, (const TI *)a.q, (const TI *)a.k, (const TI *)a.v,
-                       (const TI *)a.z, (const TI *)a.beta, a.A, a.S, (TI *)a.o, a.H);
+    if (a.conv)
+        hipLaunchKernelGGL((kda_decode_kernel<TI, D, NT, true>), dim3((unsigned)nblk), dim3(NT), 0,
+                           a.stream, a);
+    else
+        hipLaunchKernelGGL((kda_decode_kernel<TI, D, NT, false>), dim3((unsigned)nblk), dim3(NT),
+                           0, a.stream, a);
     return hipGetLastError();
 }
 

@@ -35,6 +35,32 @@ struct PrefillArgs {
     hipStream_t stream;
 };
 
+// Short causal convolution of one of q, k, v (prologue of a layer).
+struct ConvTensor {
+    const void *x;        // raw input [B, T, H, D]
+    const float *w;       // taps [H, D, W]
+    const void *sin;      // convolution state in [B, W-1, H, D], or NULL (zeros)
+    void *y;              // output [B, T, H, D]
+    void *sout;           // convolution state out, or NULL
+    int norm;             // L2-normalize each token's head row
+};
+
+struct ConvNormArgs {
+    int dtype;
+    int64_t B, T, H, D;
+    ConvTensor t[3];      // q, k, v
+    int W;                // taps, 1..4
+    int act;              // 0: none, 1: SiLU
+    float eps;
+    int64_t ntile, ngroup;   // set by the launcher
+    hipStream_t stream;
+};
+
+bool conv_supported(int dtype, int64_t D);
+// Tokens per wave tile of the prologue kernel.
+int conv_tile_tokens(int dtype);
+hipError_t launch_conv_norm(const ConvNormArgs &a);
+
 struct DecodeArgs {
     int dtype;
     int64_t B, H, D;
@@ -42,6 +68,13 @@ struct DecodeArgs {
     const float *A;
     float *S;
     void *o;
+    // Fused prologue (conv != 0): taps wq, wk, wv [H, D, W] and the persistent
+    // convolution states cq, ck, cv [B, W-1, H, D] (updated in place).
+    int conv;
+    const float *wq, *wk, *wv;
+    void *cq, *ck, *cv;
+    int W, act;
+    float eps;
     hipStream_t stream;
 };
 

@@ -16,6 +16,13 @@ q, k, v, z, beta are then rounded to the run dtype (round-to-nearest-even for
 bf16); A and S0 stay fp32.  Decode workloads draw every step up front with a
 leading [steps] axis and start from a zero state.
 
+Layer inputs for the prologue (short convolutions + q/k normalization) follow
+the same recipe without the L2 normalization of q and k (the prologue
+normalizes), then draw, from the same generator: taps wq, wk, wv ~ N(0, 1/W)
+[H, d, W] (fp32), then convolution states ~ N(0, 1) [B, W-1, H, d] rounded to
+the run dtype (a sequence that continues earlier tokens).  The pages give no
+tap distribution; N(0, 1/W) keeps the convolution's output at unit scale.
+
 The workload shapes follow the Kimi K3 KDA context quoted on the pages
 (96 heads, 128-dim heads, a 1,048,576-token context limit); the head count and
 head size of the KDA layers are not stated there and are assumed equal to the
@@ -28,7 +35,7 @@ from dataclasses import dataclass, replace
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_prefill_inputs", "make_decode_inputs", "make_varlen_inputs",
-           "torch_dtype"]
+           "make_layer_inputs", "make_layer_decode_inputs", "torch_dtype"]
 
 
 @dataclass(frozen=True)
@@ -155,3 +162,58 @@ def make_varlen_inputs(w: Workload, lengths, device="cpu"):
         cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0)
     return dict(q=_unit(q).to(dt), k=_unit(k).to(dt), v=v.to(dt), z=z.to(dt),
                 beta=torch.sigmoid(beta_logit).to(dt), A=A, S0=S0, cu_seqlens=cu.to(device))
+
+
+def _taps_and_states(w: Workload, width: int, g, B: int, device, dt):
+    f32 = dict(dtype=torch.float32, device=device, generator=g)
+    scale = 1.0 / float(width) ** 0.5
+    taps = tuple(torch.randn(w.H, d, width, **f32).mul_(scale) for d in (w.dk, w.dk, w.dv))
+    states = tuple(torch.randn(B, width - 1, w.H, d, **f32).to(dt) for d in (w.dk, w.dk, w.dv))
+    return taps, states
+
+
+def make_layer_inputs(w: Workload, width: int, device="cpu", T: int | None = None):
+    """Raw layer inputs of a prefill workload for the prologue path: q, k, v
+    (not normalized), z, beta, A, S0, taps (wq, wk, wv) and conv states
+    (sq, sk, sv)."""
+    T = w.T if T is None else int(T)
+    g = _gen(w.seed, device)
+    dt = torch_dtype(w.dtype)
+    f32 = dict(dtype=torch.float32, device=device, generator=g)
+    q = torch.randn(w.B, T, w.H, w.dk, **f32)
+    k = torch.randn(w.B, T, w.H, w.dk, **f32)
+    v = torch.randn(w.B, T, w.H, w.dv, **f32)
+    beta_logit = torch.randn(w.B, T, w.H, **f32)
+    z = torch.randn(w.B, T, w.H, w.dk, **f32)
+    if w.z_mean:
+        z.add_(w.z_mean)
+    A = torch.rand(w.H, **f32).mul_(2.0).sub_(1.0)
+    S0 = None
+    if w.s0_std is not None:
+        S0 = torch.randn(w.B, w.H, w.dk, w.dv, **f32).mul_(w.s0_std)
+    (wq, wk, wv), (sq, sk, sv) = _taps_and_states(w, width, g, w.B, device, dt)
+    return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), z=z.to(dt),
+                beta=torch.sigmoid(beta_logit).to(dt), A=A, S0=S0,
+                wq=wq, wk=wk, wv=wv, sq=sq, sk=sk, sv=sv)
+
+
+def make_layer_decode_inputs(w: Workload, width: int, device="cpu", steps: int | None = None):
+    """Per-step raw decode inputs (leading [steps] axis, q, k not normalized),
+    A, a zero S, taps and conv states."""
+    steps = w.steps if steps is None else int(steps)
+    g = _gen(w.seed, device)
+    dt = torch_dtype(w.dtype)
+    f32 = dict(dtype=torch.float32, device=device, generator=g)
+    q = torch.randn(steps, w.B, w.H, w.dk, **f32)
+    k = torch.randn(steps, w.B, w.H, w.dk, **f32)
+    v = torch.randn(steps, w.B, w.H, w.dv, **f32)
+    beta_logit = torch.randn(steps, w.B, w.H, **f32)
+    z = torch.randn(steps, w.B, w.H, w.dk, **f32)
+    if w.z_mean:
+        z.add_(w.z_mean)
+    A = torch.rand(w.H, **f32).mul_(2.0).sub_(1.0)
+    S = torch.zeros(w.B, w.H, w.dk, w.dv, dtype=torch.float32, device=device)
+    (wq, wk, wv), (sq, sk, sv) = _taps_and_states(w, width, g, w.B, device, dt)
+    return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), z=z.to(dt),
+                beta=torch.sigmoid(beta_logit).to(dt), A=A, S=S,
+                wq=wq, wk=wk, wv=wv, sq=sq, sk=sk, sv=sv)

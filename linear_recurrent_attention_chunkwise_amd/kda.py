@@ -28,6 +28,15 @@ class KDAError(RuntimeError):
         self.status = status
 
 
+class ShortConv(ctypes.Structure):
+    """kda_short_conv of include/kda.h (host struct; the taps are device memory)."""
+    _fields_ = [("width", ctypes.c_int32), ("activation", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("wq", ctypes.c_void_p), ("wk", ctypes.c_void_p), ("wv", ctypes.c_void_p)]
+
+
+ACTIVATIONS = {"none": 0, "silu": 1}
+
 _lib = None
 
 
@@ -66,6 +75,18 @@ def _load():
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, vp, vp,
                                     vp, vp, vp, vp]
+    cp = ctypes.POINTER(ShortConv)
+    lib.kda_conv_norm.restype = ctypes.c_int
+    lib.kda_conv_norm.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, cp, vp, vp, vp,
+                                  vp, vp, vp, vp, vp, vp]
+    lib.kda_prefill_conv_workspace_size.restype = sz
+    lib.kda_prefill_conv_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i32]
+    lib.kda_prefill_conv.restype = ctypes.c_int
+    lib.kda_prefill_conv.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i32, cp,
+                                     vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i32]
+    lib.kda_decode_step_conv.restype = ctypes.c_int
+    lib.kda_decode_step_conv.argtypes = [ctypes.c_int, i64, i64, i64, i64, cp, vp, vp, vp, vp,
+                                         vp, vp, vp, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -264,4 +285,161 @@ def decode_step(q, k, v, z, beta, A, S, out=None):
     st = lib.kda_decode_step(_DTYPES[dt], B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(z),
                              _ptr(beta), _ptr(A), _ptr(S), _ptr(out), _stream_handle(dev))
     _check(st, "kda_decode_step")
+    return out
+
+
+# ------------------------------------------------------------- prologue ----
+
+def _short_conv(wq, wk, wv, act, eps, H, dk, dv, dev):
+    if not isinstance(wq, torch.Tensor) or wq.dim() != 3:
+        raise ValueError("wq must be [H,dk,W]")
+    W = wq.shape[-1]
+    _require(wq, "wq", (H, dk, W), torch.float32, dev)
+    _require(wk, "wk", (H, dk, W), torch.float32, dev)
+    _require(wv, "wv", (H, dv, W), torch.float32, dev)
+    if act not in ACTIVATIONS:
+        raise ValueError(f"act must be one of {sorted(ACTIVATIONS)}")
+    cs = ShortConv(int(W), ACTIVATIONS[act], float(eps), 0, wq.data_ptr(), wk.data_ptr(),
+                   wv.data_ptr())
+    return cs, int(W)
+
+
+def _states(states, name, B, W, H, dk, dv, dt, dev):
+    """(sq, sk, sv) tensors [B,W-1,H,d] -> host array of 3 device pointers."""
+    if states is None:
+        return None
+    sq, sk, sv = states
+    _require(sq, f"{name}[0]", (B, W - 1, H, dk), dt, dev)
+    _require(sk, f"{name}[1]", (B, W - 1, H, dk), dt, dev)
+    _require(sv, f"{name}[2]", (B, W - 1, H, dv), dt, dev)
+    return (ctypes.c_void_p * 3)(sq.data_ptr(), sk.data_ptr(), sv.data_ptr())
+
+
+def _new_states(B, W, H, dk, dv, dt, dev):
+    return tuple(torch.empty((B, W - 1, H, d), dtype=dt, device=dev) for d in (dk, dk, dv))
+
+
+def _seg_shapes(q, v, what):
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,dk]")
+    B, T, H, dk = q.shape
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError(f"{what} runs on the GPU; inputs must be cuda tensors")
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    return B, T, H, dk, v.shape[-1], dev, dt
+
+
+def conv_norm(q, k, v, wq, wk, wv, state=None, act: str = "none", eps: float = 1e-6,
+              out=None, state_out=True):
+    """The layer prologue on the GPU: causal depthwise convolutions of raw q, k, v
+    (taps wq, wk [H,dk,W], wv [H,dv,W] fp32), optional SiLU, then q, k
+    L2-normalized.  ``state`` is None (fresh sequences) or (sq, sk, sv), each
+    [B,W-1,H,d] in the input dtype.  Returns (q_hat, k_hat, v_conv, new_state);
+    new_state is a fresh tuple when ``state_out`` is True, the given tuple when
+    one is passed, None when False."""
+    lib = _load()
+    B, T, H, dk, dv, dev, dt = _seg_shapes(q, v, "the KDA prologue")
+    _require(q, "q", (B, T, H, dk), dt, dev)
+    _require(k, "k", (B, T, H, dk), dt, dev)
+    _require(v, "v", (B, T, H, dv), dt, dev)
+    cs, W = _short_conv(wq, wk, wv, act, eps, H, dk, dv, dev)
+    sin = _states(state, "state", B, W, H, dk, dv, dt, dev)
+    if state_out is True:
+        state_out = _new_states(B, W, H, dk, dv, dt, dev)
+    elif state_out is False:
+        state_out = None
+    sout = _states(state_out, "state_out", B, W, H, dk, dv, dt, dev)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    for t, ref, name in zip(out, (q, k, v), ("q_out", "k_out", "v_out")):
+        _require(t, name, tuple(ref.shape), dt, dev)
+    st = lib.kda_conv_norm(_DTYPES[dt], B, T, H, dk, dv, ctypes.byref(cs), _ptr(q), _ptr(k),
+                           _ptr(v), sin, sout, _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+                           _stream_handle(dev))
+    _check(st, "kda_conv_norm")
+    return out[0], out[1], out[2], state_out
+
+
+def prefill_conv_workspace_size(dtype: torch.dtype, B: int, T: int, H: int, dk: int, dv: int,
+                                chunk: int) -> int:
+    return int(_load().kda_prefill_conv_workspace_size(_DTYPES[dtype], B, T, H, dk, dv, chunk))
+
+
+def prefill_conv(q, k, v, z, beta, A, wq, wk, wv, state=None, act: str = "none",
+                 eps: float = 1e-6, S0=None, chunk: int = 16, out=None, S_T=None,
+                 state_out=True, workspace=None, dv_per_block: int = 0):
+    """Prologue + chunkwise prefill of raw q, k, v (see ``conv_norm`` and
+    ``prefill``).  Returns (o, S_T, new_state).  ``workspace`` may be a
+    preallocated uint8 cuda tensor of at least ``prefill_conv_workspace_size``
+    bytes."""
+    lib = _load()
+    B, T, H, dk, dv, dev, dt = _seg_shapes(q, v, "KDA prefill")
+    _require(q, "q", (B, T, H, dk), dt, dev)
+    _require(k, "k", (B, T, H, dk), dt, dev)
+    _require(z, "z", (B, T, H, dk), dt, dev)
+    _require(v, "v", (B, T, H, dv), dt, dev)
+    _require(beta, "beta", (B, T, H), dt, dev)
+    _require(A, "A", (H,), torch.float32, dev)
+    if S0 is not None:
+        _require(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    cs, W = _short_conv(wq, wk, wv, act, eps, H, dk, dv, dev)
+    sin = _states(state, "state", B, W, H, dk, dv, dt, dev)
+    if state_out is True:
+        state_out = _new_states(B, W, H, dk, dv, dt, dev)
+    elif state_out is False:
+        state_out = None
+    sout = _states(state_out, "state_out", B, W, H, dk, dv, dt, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _require(out, "out", (B, T, H, dv), dt, dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _require(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
+    ws_bytes = prefill_conv_workspace_size(dt, B, T, H, dk, dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    elif workspace.numel() < ws_bytes or workspace.device != dev:
+        raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
+    st = lib.kda_prefill_conv(_DTYPES[dt], B, T, H, dk, dv, int(chunk), ctypes.byref(cs),
+                              _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A), sin, sout,
+                              _ptr(S0), _ptr(out), _ptr(S_T), _ptr(workspace),
+                              workspace.numel() if workspace is not None else 0,
+                              _stream_handle(dev), int(dv_per_block))
+    _check(st, "kda_prefill_conv")
+    return out, S_T, state_out
+
+
+def decode_step_conv(q, k, v, z, beta, A, wq, wk, wv, state, S, act: str = "none",
+                     eps: float = 1e-6, out=None):
+    """One decode step with the prologue fused in.  q, k, z [B,H,dk], v [B,H,dv]
+    raw; ``state`` = (sq, sk, sv) [B,W-1,H,d] and S [B,H,dk,dv] fp32 are
+    updated in place.  Returns o [B,H,dv]."""
+    lib = _load()
+    if q.dim() != 3:
+        raise ValueError("q must be [B,H,dk]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("KDA decode runs on the GPU; inputs must be cuda tensors")
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    _require(q, "q", (B, H, dk), dt, dev)
+    _require(k, "k", (B, H, dk), dt, dev)
+    _require(z, "z", (B, H, dk), dt, dev)
+    _require(v, "v", (B, H, dv), dt, dev)
+    _require(beta, "beta", (B, H), dt, dev)
+    _require(A, "A", (H,), torch.float32, dev)
+    _require(S, "S", (B, H, dk, dv), torch.float32, dev)
+    cs, W = _short_conv(wq, wk, wv, act, eps, H, dk, dv, dev)
+    sarr = _states(state, "state", B, W, H, dk, dv, dt, dev) if W > 1 else None
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _require(out, "out", (B, H, dv), dt, dev)
+    st = lib.kda_decode_step_conv(_DTYPES[dt], B, H, dk, dv, ctypes.byref(cs), _ptr(q),
+                                  _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A), sarr,
+                                  _ptr(S), _ptr(out), _stream_handle(dev))
+    _check(st, "kda_decode_step_conv")
     return out

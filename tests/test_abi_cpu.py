@@ -34,7 +34,8 @@ def test_header_declares_expected_api():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_str", "kda_prefill_workspace_size",
         "kda_prefill", "kda_prefill_ex", "kda_prefill_varlen",
-        "kda_prefill_varlen_workspace_size", "kda_decode_step"])
+        "kda_prefill_varlen_workspace_size", "kda_decode_step", "kda_conv_norm",
+        "kda_prefill_conv_workspace_size", "kda_prefill_conv", "kda_decode_step_conv"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     for s in range(8):
         assert lib.kda_status_str(s).decode().startswith("KDA_")
     assert lib.kda_status_str(99) == b"unknown kda_status"
@@ -170,3 +171,127 @@ def test_varlen_empty_work_launches_nothing(lib):
     assert varlen(lib, H=0) == OK
     # without checkpoints the checkpoint buffer is not looked at
     assert varlen(lib, N=0, every=0, n_ckpt=5, ptrs={"ckpt": P(7, 64)}) == OK
+
+
+# ------------------------------------------------------------- prologue ----
+
+def _addr(i):
+    """Fake device address: an int is a slot index for P(), a c_void_p is used as is."""
+    if i is None:
+        return None
+    return i.value if isinstance(i, ctypes.c_void_p) else P(i).value
+
+
+def short_conv(W=4, act=0, eps=1e-6, reserved=0, w=(40, 41, 42)):
+    from linear_recurrent_attention_chunkwise_amd.kda import ShortConv
+    return ShortConv(W, act, eps, reserved, *[_addr(i) for i in w])
+
+
+def states(*idx):
+    return (ctypes.c_void_p * 3)(*[_addr(i) for i in idx])
+
+
+def conv_norm(lib, dtype=BF16, B=2, T=64, H=2, dk=128, dv=128, conv=None, sin=None,
+              sout=None, ptrs=None):
+    p = {n: P(i) for i, n in enumerate(["q", "k", "v", "qo", "ko", "vo"])}
+    if ptrs:
+        p.update(ptrs)
+    cs = conv if conv is not None else short_conv()
+    return lib.kda_conv_norm(dtype, B, T, H, dk, dv, ctypes.byref(cs), p["q"], p["k"], p["v"],
+                             sin, sout, p["qo"], p["ko"], p["vo"], None)
+
+
+def test_conv_norm_argument_errors(lib):
+    assert conv_norm(lib, B=-1) == SHAPE
+    assert conv_norm(lib, dk=64, dv=64) == UNSUP
+    assert conv_norm(lib, dk=128, dv=16) == UNSUP
+    for bad in (short_conv(W=0), short_conv(W=5), short_conv(act=2), short_conv(eps=-1.0),
+                short_conv(eps=float("nan")), short_conv(eps=float("inf")),
+                short_conv(reserved=1)):
+        assert conv_norm(lib, conv=bad) == UNSUP
+    assert lib.kda_conv_norm(BF16, 1, 4, 2, 128, 128, None, P(0), P(1), P(2), None, None,
+                             P(3), P(4), P(5), None) == NULL
+    assert conv_norm(lib, conv=short_conv(w=(40, None, 42))) == NULL
+    assert conv_norm(lib, ptrs={"vo": None}) == NULL
+    assert conv_norm(lib, sin=states(50, None, 52)) == NULL       # all three or none
+    assert conv_norm(lib, sout=states(50, 51, None)) == NULL
+    assert conv_norm(lib, ptrs={"ko": P(20, 8)}) == MISALIGNED
+    assert conv_norm(lib, conv=short_conv(w=(40, P(21, 4), 42))) == MISALIGNED
+    assert conv_norm(lib, sin=states(50, P(51, 8), 52)) == MISALIGNED
+    # outputs overlapping an input, each other, the taps or the state inputs
+    assert conv_norm(lib, ptrs={"qo": P(1, 64)}) == ALIAS
+    assert conv_norm(lib, ptrs={"ko": P(3, 16)}) == ALIAS
+    assert conv_norm(lib, sin=states(50, 51, 52), sout=states(53, 51, 55)) == ALIAS
+    assert conv_norm(lib, sout=states(53, 54, 40)) == ALIAS
+    assert conv_norm(lib, sout=states(53, 54, 3)) == ALIAS
+    # nothing to do
+    assert conv_norm(lib, B=0) == OK
+    assert conv_norm(lib, H=0, conv=short_conv(w=(None, None, None))) == OK
+    # width 1 has no state: the arrays are not read
+    assert conv_norm(lib, B=0, conv=short_conv(W=1), sin=states(None, None, None)) == OK
+    assert conv_norm(lib, B=0, conv=short_conv(W=1), sout=states(0, 1, 2)) == OK
+
+
+def test_conv_workspace_size(lib):
+    n = 2 * 64 * 2 * 128 * 2
+    assert lib.kda_prefill_conv_workspace_size(BF16, 2, 64, 2, 128, 128, 16) == 3 * n
+    assert lib.kda_prefill_conv_workspace_size(F32, 1, 3, 1, 16, 16, 16) == 3 * 256
+    assert lib.kda_prefill_conv_workspace_size(7, 1, 3, 1, 16, 16, 16) == 0
+    assert lib.kda_prefill_conv_workspace_size(BF16, -1, 3, 1, 16, 16, 16) == 0
+
+
+def prefill_conv(lib, dtype=BF16, B=2, T=64, H=2, dk=128, dv=128, chunk=16, conv=None,
+                 sin=None, sout=None, ptrs=None, ws_bytes=None, dvb=0):
+    names = ["q", "k", "v", "z", "beta", "A", "S0", "o", "S_T", "ws"]
+    p = {n: P(i) for i, n in enumerate(names)}
+    if ptrs:
+        p.update(ptrs)
+    cs = conv if conv is not None else short_conv()
+    if ws_bytes is None:
+        ws_bytes = lib.kda_prefill_conv_workspace_size(dtype, B, T, H, dk, dv, chunk)
+    return lib.kda_prefill_conv(dtype, B, T, H, dk, dv, chunk, ctypes.byref(cs), p["q"], p["k"],
+                                p["v"], p["z"], p["beta"], p["A"], sin, sout, p["S0"], p["o"],
+                                p["S_T"], p["ws"], ws_bytes, None, dvb)
+
+
+def test_prefill_conv_argument_errors(lib):
+    assert prefill_conv(lib, T=-1) == SHAPE
+    assert prefill_conv(lib, chunk=32) == UNSUP
+    assert prefill_conv(lib, conv=short_conv(W=7)) == UNSUP
+    assert prefill_conv(lib, ptrs={"ws": None}) == WORKSPACE
+    assert prefill_conv(lib, ws_bytes=1024) == WORKSPACE
+    assert prefill_conv(lib, ptrs={"ws": P(9, 8)}) == MISALIGNED
+    assert prefill_conv(lib, ptrs={"z": None}) == NULL
+    assert prefill_conv(lib, ptrs={"q": None}) == NULL
+    # workspace over an input or an output; state out over a state in
+    assert prefill_conv(lib, ptrs={"ws": P(0, 256)}) == ALIAS
+    assert prefill_conv(lib, ptrs={"ws": P(7, 0)}) == ALIAS
+    assert prefill_conv(lib, sin=states(50, 51, 52), sout=states(52, 53, 54)) == ALIAS
+    assert prefill_conv(lib, sout=states(53, 54, 4)) == ALIAS
+    # the in-place recurrent state carry stays allowed
+    assert prefill_conv(lib, B=0, ptrs={"S_T": P(6)}) == OK
+
+
+def decode_conv(lib, dtype=BF16, B=2, H=2, dk=128, dv=128, conv=None, st="default",
+                ptrs=None):
+    p = {n: P(i) for i, n in enumerate(["q", "k", "v", "z", "beta", "A", "S", "o"])}
+    if ptrs:
+        p.update(ptrs)
+    cs = conv if conv is not None else short_conv()
+    sarr = states(50, 51, 52) if st == "default" else st
+    return lib.kda_decode_step_conv(dtype, B, H, dk, dv, ctypes.byref(cs), p["q"], p["k"],
+                                    p["v"], p["z"], p["beta"], p["A"], sarr, p["S"], p["o"], None)
+
+
+def test_decode_conv_argument_errors(lib):
+    assert decode_conv(lib, B=-1) == SHAPE
+    assert decode_conv(lib, dk=64, dv=64) == UNSUP
+    assert decode_conv(lib, conv=short_conv(act=5)) == UNSUP
+    assert decode_conv(lib, st=None) == NULL                 # W > 1 needs the states
+    assert decode_conv(lib, st=states(50, None, 52)) == NULL
+    assert decode_conv(lib, B=0, conv=short_conv(W=1), st=None) == OK   # no state at W = 1
+    assert decode_conv(lib, st=states(50, 51, P(53, 4))) == MISALIGNED
+    assert decode_conv(lib, st=states(50, 51, 6)) == ALIAS           # a state over S
+    assert decode_conv(lib, st=states(50, 50, 52)) == ALIAS          # two states at once
+    assert decode_conv(lib, st=states(50, 51, 40)) == ALIAS          # a state over taps
+    assert decode_conv(lib, B=0) == OK
