@@ -1,7 +1,8 @@
 """KDA benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk 16|64] [--no-cpu]
-                    [--no-decode] [--decode-reps R] [--calib-mib M]
+                    [--no-decode] [--no-varlen] [--no-prologue] [--decode-reps R]
+                    [--calib-mib M]
 
 A step is one chunkwise prefill over the K3 head-shape workload (B=1, H=96,
 T=4096, dk=dv=128, bf16 inputs, fp32 state, S0 ~ N(0, 0.02^2)) with inputs
@@ -18,6 +19,12 @@ algorithmic bytes one launch must move divided by its average duration:
   decode : B*H*(2*d*d*4 + 4*d*2 + 2 + d*2) + H*4 bytes per step
 The fp64 oracle is timed on the host cores over the full prefill workload
 (``cpu_baseline``), reported in the same unit.  Prints ONE JSON line.
+
+``prologue`` times the layer's prologue on raw inputs of the same shapes
+(short convolutions of width 4, SiLU, q/k L2 norm, continued sequences): the
+prologue kernel alone (HBM-bound: q, k, v read and written once, states and
+taps), prologue + prefill end to end, and the decode step with the prologue
+fused in.
 
 ``--calib-mib M`` adds, after the timed region, one elementwise copy of M MiB
 (read M, write M): the reference a hardware byte counter (FETCH_SIZE,
@@ -75,6 +82,7 @@ KERNEL_SOURCES = {
     "kda_prefill16_kernel": ["kda_prefill16.hip", "kda_device.h"],
     "kda_prefill_kernel": ["kda_prefill.hip", "kda_device.h"],
     "kda_decode_kernel": ["kda_decode.hip", "kda_device.h"],
+    "kda_conv_norm_kernel": ["kda_conv.hip", "kda_device.h"],
 }
 
 
@@ -179,6 +187,76 @@ def time_decode(torch, kda, dinp, reps):
     return e0.elapsed_time(e1) / (reps * steps)   # ms per decode step
 
 
+PROLOGUE_WIDTH, PROLOGUE_ACT = 4, "silu"
+
+
+def conv_norm_bytes(B, T, H, d, W, esz=2):
+    """q, k, v read and written once, convolution states read and written, taps."""
+    return 6 * B * T * H * d * esz + 2 * 3 * B * (W - 1) * H * d * esz + 3 * H * d * W * 4
+
+
+def time_layer(torch, kda, lin, steps, warmup):
+    """ms per launch of kda_conv_norm alone and of kda_prefill_conv (prologue +
+    prefill) on the raw layer inputs."""
+    dev = lin["q"].device
+    st_in = (lin["sq"], lin["sk"], lin["sv"])
+    st_out = tuple(torch.empty_like(t) for t in st_in)
+    outs = tuple(torch.empty_like(lin[n]) for n in ("q", "k", "v"))
+    o = torch.empty_like(lin["v"])
+    S_T = torch.empty_like(lin["S0"])
+    B, T, H, d = lin["q"].shape
+    ws = torch.empty(kda.prefill_conv_workspace_size(lin["q"].dtype, B, T, H, d, d, 16),
+                     dtype=torch.uint8, device=dev)
+    taps = (lin["wq"], lin["wk"], lin["wv"])
+
+    def conv():
+        kda.conv_norm(lin["q"], lin["k"], lin["v"], *taps, state=st_in, act=PROLOGUE_ACT,
+                      out=outs, state_out=st_out)
+
+    def layer():
+        kda.prefill_conv(lin["q"], lin["k"], lin["v"], lin["z"], lin["beta"], lin["A"], *taps,
+                         state=st_in, act=PROLOGUE_ACT, S0=lin["S0"], chunk=16, out=o, S_T=S_T,
+                         state_out=st_out, workspace=ws)
+
+    res = []
+    for fn in (conv, layer):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / steps)
+    return res
+
+
+def time_decode_conv(torch, kda, dl, reps):
+    """ms per fused decode step with the prologue (kda_decode_step_conv)."""
+    S = dl["S"]
+    steps = dl["q"].shape[0]
+    out = torch.empty_like(dl["v"][0])
+    st = (dl["sq"], dl["sk"], dl["sv"])
+    taps = (dl["wq"], dl["wk"], dl["wv"])
+
+    def one_pass():
+        for t in range(steps):
+            kda.decode_step_conv(dl["q"][t], dl["k"][t], dl["v"][t], dl["z"][t], dl["beta"][t],
+                                 dl["A"], *taps, st, S, act=PROLOGUE_ACT, out=out)
+
+    one_pass()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(reps):
+        one_pass()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * steps)
+
+
 def cpu_baseline(w, inp_cpu):
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
@@ -203,6 +281,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="also run one elementwise copy of this many MiB (byte-counter reference)")
     args = ap.parse_args(argv)
@@ -286,6 +365,47 @@ def main(argv=None):
             "with_checkpoints": {"ckpt_every": VARLEN_CKPT_EVERY, "checkpoints": nck,
                                  "ms_per_launch": cms, "value": ntok / (cms * 1e-3),
                                  "bytes_per_launch": cbytes}}
+    if not args.no_prologue:
+        from linear_recurrent_attention_chunkwise_amd.inputs import (make_layer_decode_inputs,
+                                                                     make_layer_inputs)
+        Wc = PROLOGUE_WIDTH
+        lin = {k: (v.to(dev) if v is not None else None)
+               for k, v in make_layer_inputs(w, Wc).items()}
+        cms_, lms = time_layer(torch, kda, lin, max(1, args.steps // 4), max(1, args.warmup // 40))
+        del lin
+        cb = conv_norm_bytes(w.B, w.T, w.H, w.dk, Wc)
+        wd = WORKLOADS["k3_decode_bf16"]
+        dl = make_layer_decode_inputs(wd, Wc, device=dev)
+        dcms = time_decode_conv(torch, kda, dl, args.decode_reps)
+        del dl
+        dcb = (decode_bytes(wd.B, wd.H, wd.dk) + 2 * 3 * wd.B * (Wc - 1) * wd.H * wd.dk * 2
+               + 3 * wd.H * wd.dk * Wc * 4)
+        result["prologue"] = {
+            "width": Wc, "activation": PROLOGUE_ACT,
+            "workload": f"{w.name} raw layer inputs (B={w.B} H={w.H} T={w.T} d={w.dk} bf16), "
+                        f"short convolutions of width {Wc} + {PROLOGUE_ACT} + q/k L2 norm, "
+                        f"continued sequence",
+            "conv_norm": {"us_per_launch": cms_ * 1e3, "kernel": "kda_conv_norm_kernel",
+                          "roofline": {"bound": "hbm", "achieved": cb / (cms_ * 1e-3) / 1e9,
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": cb / (cms_ * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                       "traffic": recorded_traffic(
+                                           "kda_conv_norm_kernel",
+                                           f"kda_conv_norm_kernel_{w.name}.md"),
+                                       "bytes_per_launch": cb}},
+            "prefill_conv": {"value": w.B * w.T / (lms * 1e-3), "unit": "tokens/s",
+                             "ms_per_launch": lms},
+            "decode_step_conv": {
+                "value": wd.B * wd.H / (dcms * 1e-3), "unit": "head-state-updates/s",
+                "us_per_step": dcms * 1e3,
+                "workload": f"{wd.name} with the fused prologue (B={wd.B} H={wd.H})",
+                "roofline": {"bound": "hbm", "achieved": dcb / (dcms * 1e-3) / 1e9,
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": dcb / (dcms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "traffic": recorded_traffic(
+                                 "kda_decode_kernel", f"kda_decode_kernel_conv_{wd.name}.md"),
+                             "kernel": "kda_decode_kernel (prologue fused)",
+                             "bytes_per_launch": dcb}}}
     if args.calib_mib > 0:
         calibration_copy(torch, args.calib_mib)
     if not args.no_cpu:

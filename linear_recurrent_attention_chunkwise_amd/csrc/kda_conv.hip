@@ -24,7 +24,15 @@
 //    TT + 3 loads are issued before any arithmetic.
 //  * The four waves of a workgroup take four consecutive tiles of the same
 //    channels, so a tile's three leading rows are its neighbour's last rows
-//    (a cache hit, not a second HBM read).
+//    (a cache hit, not a second HBM read).  The workgroup stages its 512
+//    channels' taps through LDS once (coalesced), transposed so that each
+//    lane's reads are conflict-free.
+//  * Consecutive workgroups take the 512-channel slabs of the same tokens, so
+//    the workgroups in flight stream whole token rows.
+//  * Outputs are written with nontemporal stores: the next kernel reads them
+//    from HBM anyway, and streaming them past the caches keeps the read
+//    stream at full rate (measured on MI355X: 105 us instead of 117 us for
+//    the K3 prefill shape).
 //  * The wave holding a sequence's last tile writes the new convolution state
 //    (the last W-1 raw rows, exact copies) from its registers.
 #include "kda_device.h"
@@ -43,6 +51,9 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Cache-policy operand of a buffer store: the nt (nontemporal) bit.
+constexpr int kNontemporal = 2;
+
 // Eight consecutive channels of one token row, as loaded.
 template <typename TI> struct Oct;
 template <> struct Oct<bf16> {
@@ -60,7 +71,7 @@ template <> struct Oct<bf16> {
                                                      int voff, int soff) {
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7])}, rs,
-            voff, soff, 0);
+            voff, soff, kNontemporal);
     }
 };
 template <> struct Oct<float> {
@@ -84,10 +95,10 @@ template <> struct Oct<float> {
                                                      int voff, int soff) {
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
-                  __float_as_uint(y[3])}, rs, voff, soff, 0);
+                  __float_as_uint(y[3])}, rs, voff, soff, kNontemporal);
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]),
-                  __float_as_uint(y[7])}, rs, voff + 16, soff, 0);
+                  __float_as_uint(y[7])}, rs, voff + 16, soff, kNontemporal);
     }
 };
 
@@ -121,45 +132,26 @@ __device__ __forceinline__ float silu(float y) {
 
 }  // namespace
 
-// One workgroup = 4 waves = 4 consecutive token tiles of one 512-channel slab
-// of one tensor (blockIdx.y) of one sequence.
-template <typename TI, int D, int TT>
-__global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormArgs p) {
-    constexpr int ESZ = sizeof(TI);
-    constexpr int LPR = D / 8;   // lanes per head row
-    const ConvTensor ct = blockIdx.y == 0 ? p.t[0] : (blockIdx.y == 1 ? p.t[1] : p.t[2]);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int64_t H = p.H, T = p.T;
-    const int64_t rowoct = H * (D / 8);          // channel octets per token row
-    const int64_t nslab = (rowoct + 63) / 64;
-    int64_t x = blockIdx.x;
-    const int64_t grp = x % p.ngroup;
-    x /= p.ngroup;
-    const int64_t slab = x % nslab;
-    const int64_t b = x / nslab;
-    const int64_t tile = grp * 4 + wave;
-    if (tile >= p.ntile) return;   // wave-uniform
 
+// The tile of one wave: TT tokens x 512 channels (lane = channel octet).
+template <typename TI, int D, int TT, int W, bool ACT, bool NORM>
+__device__ __forceinline__ void conv_body(const ConvTensor &ct, const ConvNormArgs &p, int64_t b,
+                                          int64_t slab, int64_t tile, int lane,
+                                          const float *sw) {
+    constexpr int ESZ = sizeof(TI);
+    constexpr int LPR = D / 8;
+    const int64_t H = p.H, T = p.T;
+    const int64_t rowoct = H * (D / 8);
     const int64_t c8 = slab * 64 + lane;
     const bool active = c8 < rowoct;
-    const int64_t c8c = active ? c8 : 0;         // clamped for the weight reads
-    const int rowbytes = (int)(H * D * ESZ);      // host-checked: (TT + 3) rows fit in int
+    const int rowbytes = (int)(H * D * ESZ);
     const int voff = (int)(c8 * 8 * ESZ);
     const int64_t t0 = tile * TT;
-    const int W = p.W;
-
-    // taps zero-padded to 4: tap 3 weighs the current token
     float wt[8][4];
-    {
-        const float *wp = ct.w + c8c * 8 * W;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 8; ++e)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) wt[e][j] = j >= 4 - W ? wp[e * W + j - (4 - W)] : 0.0f;
-    }
-
-    // rows r = 0 .. TT+2 hold tokens t0 - 3 + r
+        for (int j = 0; j < 4; ++j) wt[e][j] = j >= 4 - W ? sw[(e * W + j - (4 - W)) * 64 + lane] : 0.0f;
     Oct<TI> xr[TT + 3];
     const int64_t nrows = T - t0 < TT ? (T - t0 > 0 ? T - t0 : 0) : TT;
     const int64_t rowel = H * D;
@@ -174,7 +166,6 @@ __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormArgs p) {
 #pragma unroll
         for (int r = 0; r < 3; ++r) xr[r].load(rs, voff, r * rowbytes);
     } else if (ct.sin && W > 1) {
-        // state row (W-1) + (token) for tokens -3..-1; rows before the state are 0
         const char *sb = static_cast<const char *>(ct.sin) + (b * (W - 1) * rowel) * ESZ;
         const auto rs = make_rsrc(sb, (int64_t)(W - 1) * rowbytes);
 #pragma unroll
@@ -187,7 +178,6 @@ __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormArgs p) {
 #pragma unroll
         for (int r = 0; r < 3; ++r) xr[r].zero();
     }
-
     char *yb = static_cast<char *>(ct.y) + ((b * T + t0) * rowel) * ESZ;
     const auto ys = make_rsrc(yb, nrows * rowbytes);
     const float eps = p.eps;
@@ -201,11 +191,11 @@ __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormArgs p) {
             y[e] = fmaf(wt[e][2], xr[s + 2].at(e), y[e]);
             y[e] = fmaf(wt[e][3], xr[s + 3].at(e), y[e]);
         }
-        if (p.act) {
+        if constexpr (ACT) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] = silu(y[e]);
         }
-        if (ct.norm) {
+        if constexpr (NORM) {
             float ss = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
@@ -216,12 +206,10 @@ __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormArgs p) {
         }
         if (active) Oct<TI>::store_f32(y, ys, voff, s * rowbytes);
     }
-
-    // the last tile of the sequence writes the new state: raw tokens T-(W-1) .. T-1
     if (tile == p.ntile - 1 && ct.sout && W > 1 && active) {
         char *sb = static_cast<char *>(ct.sout) + (b * (W - 1) * rowel) * ESZ;
         const auto rs = make_rsrc(sb, (int64_t)(W - 1) * rowbytes);
-        const int64_t first = T - (W - 1);   // token of state row 0 (may be < 0)
+        const int64_t first = T - (W - 1);
 #pragma unroll
         for (int r = 0; r < TT + 3; ++r) {
             const int64_t i = t0 - 3 + r - first;
@@ -230,33 +218,79 @@ __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormArgs p) {
     }
 }
 
+// One workgroup = 4 waves = 4 consecutive token tiles of one 512-channel slab
+// of one tensor (blockIdx.y: q, k, v) of one sequence.
+template <typename TI, int D, int TT, int W, bool ACT>
+__global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormArgs p) {
+    __shared__ float sw[8 * 4 * 64];   // taps of the slab's 512 channels, [e*W + j][lane]
+    const ConvTensor ct = blockIdx.y == 0 ? p.t[0] : (blockIdx.y == 1 ? p.t[1] : p.t[2]);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t H = p.H;
+    const int64_t rowoct = H * (D / 8);
+    const int64_t nslab = (rowoct + 63) / 64;
+    int64_t x = blockIdx.x;
+    const int64_t slab = x % nslab;
+    x /= nslab;
+    const int64_t grp = x % p.ngroup;
+    const int64_t b = x / p.ngroup;
+    {
+        // the slab's taps are contiguous: channels slab*512 .. +512, W each
+        const int64_t base = slab * 64 * 8 * W;
+        const int64_t lim = H * D * W;
+        for (int i = threadIdx.x; i < 64 * 8 * W; i += 256) {
+            const int l = i / (8 * W), r = i % (8 * W);
+            sw[r * 64 + l] = base + i < lim ? ct.w[base + i] : 0.0f;
+        }
+    }
+    __syncthreads();
+    const int64_t tile = grp * 4 + wave;
+    if (tile >= p.ntile) return;
+    if (ct.norm) conv_body<TI, D, TT, W, ACT, true>(ct, p, b, slab, tile, lane, sw);
+    else conv_body<TI, D, TT, W, ACT, false>(ct, p, b, slab, tile, lane, sw);
+}
+
 bool conv_supported(int dtype, int64_t D) {
     return (dtype == 0 || dtype == 1) && (D == 16 || D == 128);
 }
 
 int conv_tile_tokens(int dtype) { return dtype == 1 ? 16 : 8; }
 
-template <typename TI, int D, int TT>
+template <typename TI, int D, int TT, int W, bool ACT>
 static hipError_t launch_conv_t(const ConvNormArgs &a0) {
     ConvNormArgs a = a0;
-    const int64_t ntile = a.T > 0 ? (a.T + TT - 1) / TT : 1;   // T = 0 still carries the state
+    const int64_t ntile = a.T > 0 ? (a.T + TT - 1) / TT : 1;
     const int64_t rowoct = a.H * (D / 8);
     const int64_t nslab = (rowoct + 63) / 64;
     a.ntile = ntile;
     a.ngroup = (ntile + 3) / 4;
     const int64_t nblk = a.B * nslab * a.ngroup;
-    hipLaunchKernelGGL((kda_conv_norm_kernel<TI, D, TT>), dim3((unsigned)nblk, 3), dim3(256), 0,
+    hipLaunchKernelGGL((kda_conv_norm_kernel<TI, D, TT, W, ACT>), dim3((unsigned)nblk, 3), dim3(256), 0,
                        a.stream, a);
     return hipGetLastError();
 }
 
+template <typename TI, int D, int TT>
+static hipError_t launch_conv_w(const ConvNormArgs &a) {
+    switch (a.W * 2 + (a.act ? 1 : 0)) {
+        case 2: return launch_conv_t<TI, D, TT, 1, false>(a);
+        case 3: return launch_conv_t<TI, D, TT, 1, true>(a);
+        case 4: return launch_conv_t<TI, D, TT, 2, false>(a);
+        case 5: return launch_conv_t<TI, D, TT, 2, true>(a);
+        case 6: return launch_conv_t<TI, D, TT, 3, false>(a);
+        case 7: return launch_conv_t<TI, D, TT, 3, true>(a);
+        case 8: return launch_conv_t<TI, D, TT, 4, false>(a);
+        default: return launch_conv_t<TI, D, TT, 4, true>(a);
+    }
+}
+
 hipError_t launch_conv_norm(const ConvNormArgs &a) {
     if (a.dtype == 1) {
-        if (a.D == 128) return launch_conv_t<bf16, 128, 16>(a);
-        return launch_conv_t<bf16, 16, 16>(a);
+        if (a.D == 128) return launch_conv_w<bf16, 128, 16>(a);
+        return launch_conv_w<bf16, 16, 16>(a);
     }
-    if (a.D == 128) return launch_conv_t<float, 128, 8>(a);
-    return launch_conv_t<float, 16, 8>(a);
+    if (a.D == 128) return launch_conv_w<float, 128, 8>(a);
+    return launch_conv_w<float, 16, 8>(a);
 }
 
 }  // namespace kda

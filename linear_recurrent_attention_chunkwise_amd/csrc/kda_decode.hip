@@ -30,33 +30,49 @@
 
 namespace kda {
 
-// One channel of the fused prologue: the short causal convolution of the
-// current raw input x with the W-1 raw inputs before it (convolution state
-// rows, oldest first; tap W-1 weighs x), optionally followed by SiLU.  The
-// state rows shift down by one and x becomes the newest row, in place; the
-// stored values are the raw inputs, so the state stays exact.
-template <typename TI>
-__device__ __forceinline__ float conv_step(TI x, const float *w, TI *st, int64_t stride, int W,
-                                           int act) {
-    TI raw[3];
+// One channel of the fused prologue.  load(): the current raw input x, the
+// W-1 raw inputs before it (convolution state rows, oldest first) and the W
+// taps.  conv(): the short causal convolution (tap W-1 weighs x), optionally
+// followed by SiLU.  shift(): the state rows move down by one and x becomes
+// the newest row, in place; the stored values are the raw inputs, so the
+// state stays exact.  Every load of the three tensors is issued before any
+// state store, so the loads do not wait on stores they might alias.
+template <typename TI> struct ConvChannel {
+    TI x, raw[3];
+    float w[4];
+    __device__ __forceinline__ void load(const TI *xp, const float *wp, const TI *st,
+                                         int64_t stride, int W) {
+        x = *xp;
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-        if (j < W - 1) raw[j] = st[j * stride];
-    float y = 0.0f;
+        for (int j = 0; j < 3; ++j)
+            if (j < W - 1) raw[j] = st[j * stride];
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-        if (j < W - 1) y = fmaf(w[j], to_f32(raw[j]), y);
-    y = fmaf(w[W - 1], to_f32(x), y);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-        if (j < W - 2) st[j * stride] = raw[j + 1];
-    if (W > 1) st[(W - 2) * stride] = x;
-    if (act) {
-        const float e = __builtin_amdgcn_exp2f(-y * kLog2e);
-        y *= __builtin_amdgcn_rcpf(1.0f + e);
+        for (int j = 0; j < 4; ++j)
+            if (j < W) w[j] = wp[j];
     }
-    return y;
-}
+    __device__ __forceinline__ float conv(int W, int act) const {
+        float y = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (j < W - 1) y = fmaf(w[j], to_f32(raw[j]), y);
+#pragma unroll
+        for (int j = 1; j <= 4; ++j)
+            if (j == W) y = fmaf(w[j - 1], to_f32(x), y);
+        if (act) {
+            const float e = __builtin_amdgcn_exp2f(-y * kLog2e);
+            y *= __builtin_amdgcn_rcpf(1.0f + e);
+        }
+        return y;
+    }
+    __device__ __forceinline__ void shift(TI *st, int64_t stride, int W) const {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (j < W - 2) st[j * stride] = raw[j + 1];
+#pragma unroll
+        for (int j = 1; j <= 3; ++j)
+            if (j == W - 1) st[(j - 1) * stride] = x;
+    }
+};
 
 template <typename TI, int D, int NT, bool CONV>
 __global__ __launch_bounds__(NT) void kda_decode_kernel(DecodeArgs p) {
@@ -84,7 +100,33 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(DecodeArgs p) {
     const int cg = tid % NCG, rg = tid / NCG;
     float *Sp = p.S + bh * (int64_t)(D * D);
 
-    // Issue the whole state read first; it streams while the gate is computed.
+    // The token's own inputs are loaded first and the whole state read right
+    // after: loads return in order, so the gate and prologue arithmetic runs
+    // while the state streams in.
+    const int64_t off = bh * D + tid;
+    TI zr{}, kr{}, qr{};
+    ConvChannel<TI> cnq, cnk, cnv;
+    TI *cq = nullptr, *ck = nullptr, *cv = nullptr;
+    int64_t hd = 0;
+    if (tid < D) {
+        zr = z[off];
+        if constexpr (CONV) {
+            const int W = p.W;
+            const int64_t b = bh / H;
+            hd = H * D;
+            const int64_t sb = b * (W - 1) * hd + (int64_t)h * D + tid;
+            const int64_t wb = ((int64_t)h * D + tid) * W;
+            cq = static_cast<TI *>(p.cq) + sb;
+            ck = static_cast<TI *>(p.ck) + sb;
+            cv = static_cast<TI *>(p.cv) + sb;
+            cnk.load(k + off, p.wk + wb, ck, hd, W);
+            cnq.load(q + off, p.wq + wb, cq, hd, W);
+            cnv.load(v + off, p.wv + wb, cv, hd, W);
+        } else {
+            kr = k[off];
+            qr = q[off];
+        }
+    }
     f32x4 s[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
@@ -94,24 +136,23 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(DecodeArgs p) {
 #pragma unroll
     for (int r = 0; r < NRED; ++r) red[r] = 0.0f;
     if (tid < D) {
-        const int64_t off = bh * D + tid;
-        const float zi = to_f32(z[off]);
+        const float zi = to_f32(zr);
         float ki, qi;
         if constexpr (CONV) {
             // prologue: convolve q, k, v (states updated in place); q and k are
             // normalized below through their squared norms
-            const int64_t b = bh / H;
-            const int64_t hd = H * D;
-            const int64_t sb = b * (p.W - 1) * hd + (int64_t)h * D + tid;
-            const int64_t wb = ((int64_t)h * D + tid) * p.W;
-            ki = conv_step(k[off], p.wk + wb, static_cast<TI *>(p.ck) + sb, hd, p.W, p.act);
-            qi = conv_step(q[off], p.wq + wb, static_cast<TI *>(p.cq) + sb, hd, p.W, p.act);
-            s_v[tid] = conv_step(v[off], p.wv + wb, static_cast<TI *>(p.cv) + sb, hd, p.W, p.act);
+            const int W = p.W;
+            ki = cnk.conv(W, p.act);
+            qi = cnq.conv(W, p.act);
+            s_v[tid] = cnv.conv(W, p.act);
+            cnk.shift(ck, hd, W);
+            cnq.shift(cq, hd, W);
+            cnv.shift(cv, hd, W);
             red[1] = qi * qi;
             red[2] = ki * ki;
         } else {
-            ki = to_f32(k[off]);
-            qi = to_f32(q[off]);
+            ki = to_f32(kr);
+            qi = to_f32(qr);
         }
         const float c2 = -__builtin_amdgcn_exp2f(p.A[h] * kLog2e) * kLog2e;
         const float al = kda_alpha(c2, zi);
