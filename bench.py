@@ -20,6 +20,12 @@ algorithmic bytes one launch must move divided by its average duration:
 The fp64 oracle is timed on the host cores over the full prefill workload
 (``cpu_baseline``), reported in the same unit.  Prints ONE JSON line.
 
+``long`` times the long-context (B1 H96 T65536, z ~ N(2,1)) and million-token
+(B1 H16 T2^20) prefill workloads at 64- and 16-token chunks over 3 launches
+each, inputs drawn on the device; the million-token head share also split
+into 4 and 8 segments (kda_prefill_split).  ``timing`` gives the median and minimum
+per-launch time of 10 equal segments of the timed steps.
+
 ``prologue`` times the layer's prologue on raw inputs of the same shapes
 (short convolutions of width 4, SiLU, q/k L2 norm, continued sequences): the
 prologue kernel alone (HBM-bound: q, k, v read and written once, states and
@@ -114,24 +120,40 @@ def _events(torch):
     return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
 
 
-def time_prefill(torch, kda, inp, chunk, steps, warmup):
+SEGMENTS = 10
+
+
+def time_prefill(torch, kda, inp, chunk, steps, warmup, segments=1):
+    """ms per launch over the timed steps, plus the median and minimum of the
+    per-launch times of SEGMENTS equal segments (events between segments)."""
     out = torch.empty_like(inp["v"])
-    S_T = torch.empty_like(inp["S0"])
+    S_T = torch.empty_like(inp["S0"]) if inp["S0"] is not None else None
+
+    ws = None
+    if segments > 1:
+        B, T, H, d = inp["q"].shape
+        ws = torch.empty(kda.prefill_split_workspace_size(inp["q"].dtype, B, T, H, d, d, chunk,
+                                                          segments),
+                         dtype=torch.uint8, device=inp["q"].device)
 
     def run():
         kda.prefill(inp["q"], inp["k"], inp["v"], inp["z"], inp["beta"], inp["A"], inp["S0"],
-                    chunk=chunk, out=out, S_T=S_T)
+                    chunk=chunk, out=out, S_T=S_T, segments=segments, workspace=ws)
 
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    e0, e1 = _events(torch)
-    e0.record()
-    for _ in range(steps):
-        run()
-    e1.record()
+    nseg = min(SEGMENTS, steps)
+    bounds = [steps * i // nseg for i in range(nseg + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nseg + 1)]
+    ev[0].record()
+    for i in range(nseg):
+        for _ in range(bounds[i + 1] - bounds[i]):
+            run()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps   # ms per launch
+    seg = sorted(ev[i].elapsed_time(ev[i + 1]) / (bounds[i + 1] - bounds[i]) for i in range(nseg))
+    return ev[0].elapsed_time(ev[nseg]) / steps, seg[len(seg) // 2], seg[0]
 
 
 VARLEN_LENGTHS = [4096, 1000, 37, 2500, 16, 513, 64, 3000]   # mixed, ragged, 11226 tokens
@@ -257,7 +279,22 @@ def time_decode_conv(torch, kda, dl, reps):
     return e0.elapsed_time(e1) / (reps * steps)
 
 
+def _host_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(w, inp_cpu):
+    """The fp64 oracle on the host cores: the full prefill workload on all
+    threads, and two heads on one thread (per-core rate)."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     threads = max(1, min(threads, os.cpu_count() or 1, w.B * w.H))
@@ -266,9 +303,52 @@ def cpu_baseline(w, inp_cpu):
     t0 = time.perf_counter()
     oracle.prefill(*args, threads=threads)
     dt = time.perf_counter() - t0
+    heads = [0, 1]
+    sub = [a[:, :, heads] if a.ndim == 4 else a[:, :, heads] for a in args[:5]]
+    sub += [args[5][heads], args[6][:, heads] if args[6] is not None else None]
+    t1 = time.perf_counter()
+    oracle.prefill(*sub, threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"full {w.name} prefill (B{w.B} H{w.H} T{w.T} d{w.dk}), fp64 sequential "
-                      f"recurrence, {dt:.2f} s wall"}
+                      f"recurrence, {dt:.2f} s wall",
+            "single_thread": {"value": w.B * w.T * len(heads) / dt1, "unit": "token-heads/s/core",
+                              "sample": f"heads {heads} of the same workload on 1 thread, "
+                                        f"{dt1:.2f} s wall"},
+            "host": _host_info()}
+
+
+LONG_CASES = [("long_prefill_bf16", 64, 1), ("long_prefill_bf16", 16, 1),
+              ("million_prefill_bf16", 64, 1), ("million_prefill_bf16", 16, 1),
+              ("million_prefill_bf16", 16, 4), ("million_prefill_bf16", 16, 8)]
+
+
+def time_long(torch, kda, steps):
+    """The long-context (B1 H96 T65536) and million-token (B1 H16 T2^20) prefill
+    workloads, inputs drawn on the device (same recipe and seed, device
+    generator), timed over a few launches at each chunk size."""
+    from linear_recurrent_attention_chunkwise_amd.inputs import WORKLOADS, make_prefill_inputs
+    dev = torch.device("cuda:0")
+    res = {}
+    cache = {}
+    for name, chunk, segments in LONG_CASES:
+        w = WORKLOADS[name]
+        if name not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            cache[name] = make_prefill_inputs(w, device=dev)
+        inp = cache[name]
+        ms, med, mn = time_prefill(torch, kda, inp, chunk, steps, 1, segments)
+        b = prefill_bytes(w.B, w.T, w.H, w.dk)
+        key = f"{name}_c{chunk}" + (f"_split{segments}" if segments > 1 else "")
+        res[key] = {
+            "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s", "ms_per_launch": ms,
+            "median_ms": med, "min_ms": mn, "chunk": chunk, "segments": segments,
+            "workload": f"{name}: B={w.B} H={w.H} T={w.T} d={w.dk} bf16, z mean {w.z_mean}",
+            "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    cache.clear()
+    torch.cuda.empty_cache()
+    return res
 
 
 def main(argv=None):
@@ -282,6 +362,8 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context and million-token prefill timings")
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="also run one elementwise copy of this many MiB (byte-counter reference)")
     args = ap.parse_args(argv)
@@ -300,7 +382,7 @@ def main(argv=None):
     w = WORKLOADS["k3_prefill_bf16"].with_(chunk=args.chunk)
     inp_cpu = make_prefill_inputs(w)
     inp = {k: (v.to(dev) if v is not None else None) for k, v in inp_cpu.items()}
-    ms = time_prefill(torch, kda, inp, args.chunk, args.steps, args.warmup)
+    ms, ms_med, ms_min = time_prefill(torch, kda, inp, args.chunk, args.steps, args.warmup)
     pbytes = prefill_bytes(w.B, w.T, w.H, w.dk)
     achieved = pbytes / (ms * 1e-3) / 1e9
     pkernel = prefill_kernel_name(args.chunk)
@@ -313,6 +395,8 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "timing": {"segments": min(SEGMENTS, args.steps), "median_ms_per_step": ms_med,
+                   "min_ms_per_step": ms_min, "clock": "HIP events on the launch stream"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -406,6 +490,8 @@ def main(argv=None):
                                  "kda_decode_kernel", f"kda_decode_kernel_conv_{wd.name}.md"),
                              "kernel": "kda_decode_kernel (prologue fused)",
                              "bytes_per_launch": dcb}}}
+    if not args.no_long:
+        result["long"] = time_long(torch, kda, 3)
     if args.calib_mib > 0:
         calibration_copy(torch, args.calib_mib)
     if not args.no_cpu:

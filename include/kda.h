@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -173,6 +173,41 @@ kda_status kda_prefill_varlen(int dtype, int64_t N, int64_t T_total, int64_t H,
 /* Bytes of device workspace kda_prefill_varlen needs for N sequences (0 for
  * N <= 1, and above 8192 sequences, which run in sequence order). */
 size_t kda_prefill_varlen_workspace_size(int64_t N);
+
+/*
+ * Prefill of long sequences split into `segments` parallel pieces.
+ *
+ * The recurrence is affine in the state, so over a segment S_end = M S_start
+ * + N (M: the product of the segment's transitions (I - beta k k^T)Diag(alpha),
+ * N: its final state from a zero start).  Splitting a sequence and combining
+ * the pieces through these maps is the sequence-parallel form of the same
+ * section's recurrence; here it runs inside one GPU to occupy it when B*H
+ * alone cannot (a head share of a long context: e.g. H = 16, T = 2^20).  Each
+ * sequence is cut into `segments` pieces of L = ceil(T / segments) tokens
+ * rounded up to a whole chunk (trailing pieces may be empty); the call runs
+ * (1) every piece's M and N, (2) the pieces' start states by the scan
+ * S_{j+1} = M_j S_j + N_j in fp32, (3) every piece from its start state.  It
+ * costs about three prefills of work spread over B*H*segments units.
+ *
+ * Arguments and results as kda_prefill (o, S_T identical in meaning; S_T may
+ * be S0).  Supported: bf16, dk = dv = 128, chunk 16, 1 <= segments <= 1024
+ * (1: the plain prefill).  workspace: kda_prefill_split_workspace_size bytes,
+ * 16-byte aligned, not overlapping any other argument; scratch (calls sharing
+ * it must not overlap).  The result equals the unsplit call's up to rounding
+ * (the start states pass through bf16-rounded products once more).
+ */
+kda_status kda_prefill_split(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                             int64_t dv, int32_t chunk, int32_t segments,
+                             const void *q, const void *k, const void *v, const void *z,
+                             const void *beta, const float *A, const float *S0,
+                             void *o, float *S_T,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace kda_prefill_split needs (0 for segments == 1 and for
+ * unsupported arguments). */
+size_t kda_prefill_split_workspace_size(int dtype, int64_t B, int64_t T, int64_t H,
+                                        int64_t dk, int64_t dv, int32_t chunk,
+                                        int32_t segments);
 
 /*
  * One fused recurrent decode step for B sequences (the "KDA decode" half of

@@ -8,8 +8,10 @@ without a built library or without a GPU raises.
 """
 from .kda import (KDAError, ShortConv, abi_version, checkpoint_rows, conv_norm, decode_step,
                   decode_step_conv, library_path, prefill, prefill_conv,
-                  prefill_conv_workspace_size, prefill_varlen, prefill_workspace_size)
+                  prefill_conv_workspace_size, prefill_split_workspace_size, prefill_varlen,
+                  prefill_workspace_size)
 
 __all__ = ["KDAError", "ShortConv", "abi_version", "checkpoint_rows", "conv_norm",
            "decode_step", "decode_step_conv", "library_path", "prefill", "prefill_conv",
-           "prefill_conv_workspace_size", "prefill_varlen", "prefill_workspace_size"]
+           "prefill_conv_workspace_size", "prefill_split_workspace_size", "prefill_varlen",
+           "prefill_workspace_size"]

@@ -79,7 +79,8 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
                         const void *v, const void *z, const void *beta, const float *A,
                         const float *S0, void *o, float *S_T, int32_t ckpt_every,
                         float *ckpt, int64_t n_ckpt, void *workspace, size_t workspace_bytes,
-                        void *stream, int32_t dv_per_block, bool check_only = false) {
+                        void *stream, int32_t dv_per_block, int mode = 0,
+                        bool check_only = false) {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || n_ckpt < 0 || ckpt_every < 0)
         return KDA_ERR_SHAPE;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -112,6 +113,7 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
         return KDA_ERR_UNSUPPORTED;
     if (want_ckpt && !role_split && !kda::prefill_ckpt_supported(dtype, D, chunk, dvb))
         return KDA_ERR_UNSUPPORTED;
+    if (mode != 0 && (!role_split || dvb != 64 || want_ckpt)) return KDA_ERR_UNSUPPORTED;
     if (!A || !S_T) return KDA_ERR_NULL;
     if (bth > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL;
     if (ckpt_every > 0 && n_ckpt > 0 && !ckpt) return KDA_ERR_NULL;
@@ -160,6 +162,7 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
     a.ckpt_every = ckpt_every > 0 && n_ckpt > 0 ? ckpt_every : 0;
     a.ckpt = a.ckpt_every > 0 ? ckpt : nullptr;
     a.n_ckpt = n_ckpt;
+    a.mode = mode;
     a.stream = (hipStream_t)stream;
     const hipError_t err = role_split ? kda::launch_prefill16(a) : kda::launch_prefill(a);
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -430,7 +433,7 @@ kda_status kda_prefill_conv(int dtype, int64_t B, int64_t T, int64_t H, int64_t 
     void *vh = need > 0 ? ws + 2 * round256(nin * esz) : nullptr;
     // the recurrence's own checks, on the prologue's outputs, before any launch
     st = prefill_impl(dtype, B, T, H, dk, dv, chunk, nullptr, qh, kh, vh, z, beta, A, S0, o, S_T,
-                      0, nullptr, 0, nullptr, 0, stream, dv_per_block, true);
+                      0, nullptr, 0, nullptr, 0, stream, dv_per_block, 0, true);
     if (st != KDA_OK) return st;
     if (nin > 0 && (!q || !k || !v)) return KDA_ERR_NULL;
     const void *ptrs[] = {q, k, v};
@@ -507,6 +510,118 @@ kda_status kda_decode_step_conv(int dtype, int64_t B, int64_t H, int64_t dk, int
     a.W = cs.W; a.act = cs.act; a.eps = cs.eps;
     a.stream = (hipStream_t)stream;
     return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------- sequence split ----
+
+namespace {
+
+constexpr int kMaxSegments = 1024;
+
+// Segment length: ceil(T / P) rounded up to a whole chunk, so that every
+// segment boundary is a chunk boundary of the unsplit run.
+int64_t split_len(int64_t T, int P, int chunk) {
+    const int64_t L = (T + P - 1) / P;
+    return (L + chunk - 1) / chunk * chunk;
+}
+
+struct SplitLayout {
+    size_t cu, order, M, N, S, total;   // byte offsets into the workspace, and its size
+};
+
+bool split_layout(int64_t B, int64_t H, int64_t D, int P, SplitLayout *lay) {
+    int64_t n, nh, ne;
+    if (!mul_ok(B, P, kMaxElems, &n) || !mul_ok(n, H, kMaxElems, &nh) ||
+        !mul_ok(nh, D * D, kMaxElems / 16, &ne))
+        return false;
+    lay->cu = 0;
+    lay->order = round256((n + 1) * 8);
+    lay->M = lay->order + round256((int64_t)order_bytes(n));
+    lay->N = lay->M + round256(ne * 4);
+    lay->S = lay->N + round256(ne * 4);
+    lay->total = lay->S + round256(ne * 4);
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_prefill_split_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                                        int64_t dv, int32_t chunk, int32_t segments) {
+    (void)T;
+    if (dtype != KDA_BF16 || dk != 128 || dv != 128 || chunk != 16 || B < 0 || H < 0 ||
+        segments < 1 || segments > kMaxSegments)
+        return 0;
+    if (segments == 1) return 0;
+    SplitLayout lay;
+    return split_layout(B, H, dk, segments, &lay) ? lay.total : 0;
+}
+
+kda_status kda_prefill_split(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             int32_t chunk, int32_t segments, const void *q, const void *k,
+                             const void *v, const void *z, const void *beta, const float *A,
+                             const float *S0, void *o, float *S_T, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (segments < 1 || segments > kMaxSegments) return KDA_ERR_UNSUPPORTED;
+    if (dtype != KDA_BF16 || dk != 128 || dv != 128 || chunk != 16) return KDA_ERR_UNSUPPORTED;
+    // every check of the plain call on the caller's arguments
+    kda_status st = prefill_impl(dtype, B, T, H, dk, dv, chunk, nullptr, q, k, v, z, beta, A, S0,
+                                 o, S_T, 0, nullptr, 0, nullptr, 0, stream, 64, 0, true);
+    if (st != KDA_OK) return st;
+    const int P = segments;
+    if (P == 1)
+        return prefill_impl(dtype, B, T, H, dk, dv, chunk, nullptr, q, k, v, z, beta, A, S0, o,
+                            S_T, 0, nullptr, 0, nullptr, 0, stream, 64);
+    SplitLayout lay;
+    if (!split_layout(B, H, dk, P, &lay)) return KDA_ERR_SHAPE;
+    int64_t nseg;
+    if (!mul_ok(B, P, 0x7fffffff / 8 / (H > 0 ? H : 1), &nseg)) return KDA_ERR_SHAPE;
+    if (!workspace || workspace_bytes < lay.total) return KDA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;
+    {
+        const int64_t esz = 2, D = dk;
+        const Range rws = range_of(workspace, (int64_t)lay.total);
+        const Range all[] = {range_of(q, B * T * H * D * esz), range_of(k, B * T * H * D * esz),
+                             range_of(v, B * T * H * D * esz), range_of(z, B * T * H * D * esz),
+                             range_of(beta, B * T * H * esz), range_of(A, H * 4),
+                             range_of(S0, B * H * D * D * 4), range_of(o, B * T * H * D * esz),
+                             range_of(S_T, B * H * D * D * 4)};
+        for (const Range &r : all)
+            if (overlaps(rws, r)) return KDA_ERR_ALIAS;
+    }
+    if (B * H == 0) return KDA_OK;
+    char *ws = static_cast<char *>(workspace);
+    int64_t *cu = reinterpret_cast<int64_t *>(ws + lay.cu);
+    void *order = ws + lay.order;
+    const size_t order_sz = order_bytes(nseg);
+    float *Mb = reinterpret_cast<float *>(ws + lay.M);
+    float *Nb = reinterpret_cast<float *>(ws + lay.N);
+    float *Sb = reinterpret_cast<float *>(ws + lay.S);
+    const hipStream_t s = (hipStream_t)stream;
+    const int64_t L = split_len(T, P, chunk);
+    const int64_t Ttot = B * T;   // [B, T, H, d] read as the packing [B*T, H, d]
+    if (kda::launch_split_setup(cu, Mb, B, T, L, P, H, (int)dk, s) != hipSuccess)
+        return KDA_ERR_HIP;
+    // (1) transitions M (from S0 = I, v as zero) and offsets N (from S0 = 0)
+    st = prefill_impl(dtype, nseg, Ttot, H, dk, dv, chunk, cu, q, k, v, z, beta, A, Mb, o, Mb, 0,
+                      nullptr, 0, order, order_sz, stream, 64, 2);
+    if (st != KDA_OK) return st;
+    st = prefill_impl(dtype, nseg, Ttot, H, dk, dv, chunk, cu, q, k, v, z, beta, A, nullptr, o,
+                      Nb, 0, nullptr, 0, order, order_sz, stream, 64, 1);
+    if (st != KDA_OK) return st;
+    // (2) start state of every segment
+    if (kda::launch_split_scan(S0, Mb, Nb, Sb, B, H, P, (int)dk, s) != hipSuccess)
+        return KDA_ERR_HIP;
+    // (3) every segment from its start state; its final states go to Mb
+    st = prefill_impl(dtype, nseg, Ttot, H, dk, dv, chunk, cu, q, k, v, z, beta, A, Sb, o, Mb, 0,
+                      nullptr, 0, order, order_sz, stream, 64, 0);
+    if (st != KDA_OK) return st;
+    return kda::launch_split_gather(Mb, S_T, B, H, P, (int)dk, s) == hipSuccess ? KDA_OK
+                                                                                : KDA_ERR_HIP;
 }
 
 }  // extern "C"

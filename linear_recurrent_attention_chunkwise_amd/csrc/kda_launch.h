@@ -32,6 +32,10 @@ struct PrefillArgs {
     int ckpt_every;
     float *ckpt;
     int64_t n_ckpt;
+    // 0: the prefill.  1: final states only (o not written).  2: the state
+    // transition of each sequence (v read as zero, o not written).  Modes 1
+    // and 2 exist for the role-split kernel at 64 columns without checkpoints.
+    int mode = 0;
     hipStream_t stream;
 };
 
@@ -94,6 +98,15 @@ hipError_t launch_prefill16(const PrefillArgs &a);
 constexpr int64_t kMaxOrderSeqs = 8192;
 hipError_t launch_seq_order(const int64_t *cu, int64_t N, int64_t T, int32_t *order,
                             hipStream_t stream);
+
+// Sequence split (kda_split.hip): segment offsets + identity start states,
+// the scan of segment start states, the gather of the final states.
+hipError_t launch_split_setup(int64_t *cu, float *eye, int64_t B, int64_t T, int64_t L, int P,
+                              int64_t H, int D, hipStream_t stream);
+hipError_t launch_split_scan(const float *S0, const float *M, const float *N, float *Sstart,
+                             int64_t B, int64_t H, int P, int D, hipStream_t stream);
+hipError_t launch_split_gather(const float *Sseg, float *S_T, int64_t B, int64_t H, int P, int D,
+                               hipStream_t stream);
 
 bool decode_supported(int dtype, int64_t D);
 hipError_t launch_decode(const DecodeArgs &a);

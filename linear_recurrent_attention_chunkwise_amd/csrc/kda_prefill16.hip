@@ -121,7 +121,12 @@ __device__ __forceinline__ void store_row16(bf16 *row, const float *x) {
                  pack_bf16(x[14], x[15])};
 }
 
-template <int NCW, int NPW, int NSLOT, bool CKPT>
+// MODE 0: the prefill.  MODE 1: the final states only (no o).  MODE 2: the
+// segment's state transition -- V taken as zero and no o, so that run from
+// S0 = I (dv = dk columns) the final "state" is the matrix M with
+// S_end = M S_start + (the MODE 1 result from S_start = 0); used to split one
+// long sequence into segments that run in parallel.
+template <int NCW, int NPW, int NSLOT, bool CKPT, int MODE>
 __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill16Params prm) {
     using Cfg = P16Cfg<NCW, NPW, NSLOT>;
     constexpr int D = Cfg::D, C = Cfg::C, DVB = Cfg::DVB, DP = Cfg::DP, CP = Cfg::CP,
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             for (int e = 0; e < 4; ++e)
                 vr[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, (4 * g + e) * (int)row_bytes + 2 * n, 0, 0);
         };
-        if (nchunks > 0) load_v(0);
+        if (MODE != 2 && nchunks > 0) load_v(0);
         // per-lane byte offsets of the fragment reads, fixed over chunks; a
         // chunk adds its slot's (uniform) byte offset once per tile layout
         const int offDP = ((lane & 15) * DP + 4 * (lane >> 4)) * 2;   // [.][DP] tiles
@@ -221,14 +226,16 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
 #pragma unroll
             for (int i = 0; i < NDT; ++i) gc[i] = *reinterpret_cast<const f32x4 *>(pg + 64 * i);
             Frag<bf16> Vf;
+            if constexpr (MODE != 2) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Vf.v[e] = __builtin_bit_cast(bf16, vr[e]);
-            if (m + 1 < nchunks) load_v(t0 + C);
+                for (int e = 0; e < 4; ++e) Vf.v[e] = __builtin_bit_cast(bf16, vr[e]);
+                if (m + 1 < nchunks) load_v(t0 + C);
+            }
             __builtin_amdgcn_sched_barrier(0);
             // (2) S <- e^{G_C} S; U = T diag(beta) V - W~ S, where W~ = W e^{-G_C}
             // (two accumulators halve the dependent chain)
             f32x4 Ua = {0.f, 0.f, 0.f, 0.f}, Ub = {0.f, 0.f, 0.f, 0.f};
-            mma16(Ua, Tf, Vf);
+            if constexpr (MODE != 2) mma16(Ua, Tf, Vf);
             Frag<bf16> Sf[NDT];
 #pragma unroll
             for (int i = 0; i < NDT; ++i) {
@@ -242,10 +249,12 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             // Q~ and P are only needed for the output; reading them now keeps
             // their registers free while W~ and e^{G_C} are live
             compiler_fence();
-            Frag<bf16> Qf[NDT];
+            Frag<bf16> Qf[NDT], Pf;
+            if constexpr (MODE == 0) {
 #pragma unroll
-            for (int i = 0; i < NDT; ++i) Qf[i] = frag_at(pd + Cfg::S_QG + 32 * i);
-            const Frag<bf16> Pf = frag_at(pc + Cfg::S_P);
+                for (int i = 0; i < NDT; ++i) Qf[i] = frag_at(pd + Cfg::S_QG + 32 * i);
+                Pf = frag_at(pc + Cfg::S_P);
+            }
             // Every read of slot m has now been issued.  A wave's LDS operations
             // execute in order, so a prep wave that sees this count and then
             // writes the slot writes after these reads have executed: no wait
@@ -283,18 +292,22 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             // (4) chunk m+1's W, T diag(beta), Kh^T, read while O is formed
             if (m + 1 < nchunks) read_wtk(sl1, use1);
             // (5) O = Q~ (e^{G_C} S_old) + P U
-            f32x4 Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
-            mma32(Oa, Qf[0], Qf[1], Sf[0], Sf[1]);
-            mma32(Ob, Qf[2], Qf[3], Sf[2], Sf[3]);
-            mma32(Oa, Qf[4], Qf[5], Sf[4], Sf[5]);
-            mma32(Ob, Qf[6], Qf[7], Sf[6], Sf[7]);
-            mma16(Oa, Pf, Uf);
-            const f32x4 O = Oa + Ob;
-            const auto ors = make_rsrc(prm.o + base + t0 * tok_stride + jw, chunk_rows(t0) * row_bytes);
+            if constexpr (MODE == 0) {
+                f32x4 Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
+                mma32(Oa, Qf[0], Qf[1], Sf[0], Sf[1]);
+                mma32(Ob, Qf[2], Qf[3], Sf[2], Sf[3]);
+                mma32(Oa, Qf[4], Qf[5], Sf[4], Sf[5]);
+                mma32(Ob, Qf[6], Qf[7], Sf[6], Sf[7]);
+                mma16(Oa, Pf, Uf);
+                const f32x4 O = Oa + Ob;
+                const auto ors =
+                    make_rsrc(prm.o + base + t0 * tok_stride + jw, chunk_rows(t0) * row_bytes);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (bf16)O[e]), ors,
-                                                      (4 * g + e) * (int)row_bytes + 2 * n, 0, 0);
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (bf16)O[e]),
+                                                          ors, (4 * g + e) * (int)row_bytes + 2 * n,
+                                                          0, 0);
+            }
             sl = sl1;
             use = use1;
         }
@@ -506,7 +519,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
     }
 }
 
-template <int NCW, int NPW, int NSLOT, bool CKPT>
+template <int NCW, int NPW, int NSLOT, bool CKPT, int MODE = 0>
 static hipError_t launch_p16(const PrefillArgs &a) {
     Prefill16Params prm;
     prm.q = static_cast<const bf16 *>(a.q);
@@ -527,7 +540,7 @@ static hipError_t launch_p16(const PrefillArgs &a) {
     prm.n_ckpt = a.n_ckpt;
     prm.ckpt_every = a.ckpt_every;
     const int64_t nblk = a.B * a.H * prm.nsplit;
-    hipLaunchKernelGGL((kda_prefill16_kernel<NCW, NPW, NSLOT, CKPT>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((kda_prefill16_kernel<NCW, NPW, NSLOT, CKPT, MODE>), dim3((unsigned)nblk),
                        dim3(64 * (NCW + NPW)), 0, a.stream, prm);
     return hipGetLastError();
 }
@@ -538,6 +551,10 @@ bool prefill16_supported(int dtype, int64_t D, int chunk, int dv_per_block) {
 
 hipError_t launch_prefill16(const PrefillArgs &a) {
     const bool ck = a.ckpt != nullptr && a.ckpt_every > 0;
+    if (a.mode != 0) {   // segment passes: 64 columns, no checkpoints
+        if (a.dv_per_block != 64 || ck) return hipErrorInvalidValue;
+        return a.mode == 1 ? launch_p16<4, 8, 6, false, 1>(a) : launch_p16<4, 8, 6, false, 2>(a);
+    }
     if (a.dv_per_block == 64)
         return ck ? launch_p16<4, 8, 6, true>(a) : launch_p16<4, 8, 6, false>(a);
     if (a.dv_per_block == 32)

@@ -75,6 +75,12 @@ def _load():
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, vp, vp,
                                     vp, vp, vp, vp]
+    lib.kda_prefill_split.restype = ctypes.c_int
+    lib.kda_prefill_split.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp,
+                                      vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kda_prefill_split_workspace_size.restype = sz
+    lib.kda_prefill_split_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i32,
+                                                     i32]
     cp = ctypes.POINTER(ShortConv)
     lib.kda_conv_norm.restype = ctypes.c_int
     lib.kda_conv_norm.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, cp, vp, vp, vp,
@@ -131,13 +137,17 @@ def prefill_workspace_size(dtype: torch.dtype, B: int, T: int, H: int, dk: int, 
 
 
 def prefill(q, k, v, z, beta, A, S0=None, chunk: int = 16, out=None, S_T=None,
-            dv_per_block: int = 0):
+            dv_per_block: int = 0, segments: int = 1, workspace=None):
     """Chunkwise KDA prefill on the GPU.
 
     q, k, z [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H] (fp32 or bf16, all one
     dtype); A [H] fp32; S0 [B,H,dk,dv] fp32 or None.  Returns (o, S_T) with
     o [B,T,H,dv] in the input dtype and S_T [B,H,dk,dv] fp32.  ``out`` and
-    ``S_T`` may be given preallocated (``S_T`` may be ``S0`` itself)."""
+    ``S_T`` may be given preallocated (``S_T`` may be ``S0`` itself).
+    ``segments`` > 1 splits every sequence into that many pieces run in
+    parallel and combined through their state maps (kda_prefill_split; bf16,
+    d = 128, chunk 16); ``workspace`` may then be a preallocated uint8 cuda
+    tensor of ``prefill_split_workspace_size`` bytes."""
     lib = _load()
     if q.dim() != 4:
         raise ValueError("q must be [B,T,H,dk]")
@@ -162,6 +172,19 @@ def prefill(q, k, v, z, beta, A, S0=None, chunk: int = 16, out=None, S_T=None,
     if S_T is None:
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _require(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
+    if segments > 1:
+        ws_bytes = prefill_split_workspace_size(dt, B, T, H, dk, dv, chunk, segments)
+        if workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+        elif workspace.numel() < ws_bytes or workspace.device != dev:
+            raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
+        st = lib.kda_prefill_split(_DTYPES[dt], B, T, H, dk, dv, int(chunk), int(segments),
+                                   _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A),
+                                   _ptr(S0), _ptr(out), _ptr(S_T), _ptr(workspace),
+                                   workspace.numel() if workspace is not None else 0,
+                                   _stream_handle(dev))
+        _check(st, "kda_prefill_split")
+        return out, S_T
     ws_bytes = int(lib.kda_prefill_workspace_size(_DTYPES[dt], B, T, H, dk, dv, int(chunk)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     st = lib.kda_prefill_ex(_DTYPES[dt], B, T, H, dk, dv, int(chunk), _ptr(q), _ptr(k),
@@ -170,6 +193,12 @@ def prefill(q, k, v, z, beta, A, S0=None, chunk: int = 16, out=None, S_T=None,
                             int(dv_per_block))
     _check(st, "kda_prefill")
     return out, S_T
+
+
+def prefill_split_workspace_size(dtype: torch.dtype, B: int, T: int, H: int, dk: int, dv: int,
+                                 chunk: int, segments: int) -> int:
+    return int(_load().kda_prefill_split_workspace_size(_DTYPES[dtype], B, T, H, dk, dv,
+                                                        int(chunk), int(segments)))
 
 
 def checkpoint_rows(seq_lens, ckpt_every: int):

@@ -35,7 +35,8 @@ def test_header_declares_expected_api():
         "kda_abi_version", "kda_status_str", "kda_prefill_workspace_size",
         "kda_prefill", "kda_prefill_ex", "kda_prefill_varlen",
         "kda_prefill_varlen_workspace_size", "kda_decode_step", "kda_conv_norm",
-        "kda_prefill_conv_workspace_size", "kda_prefill_conv", "kda_decode_step_conv"])
+        "kda_prefill_conv_workspace_size", "kda_prefill_conv", "kda_decode_step_conv",
+        "kda_prefill_split", "kda_prefill_split_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 4
+    assert lib.kda_abi_version() == 5
     for s in range(8):
         assert lib.kda_status_str(s).decode().startswith("KDA_")
     assert lib.kda_status_str(99) == b"unknown kda_status"
@@ -295,3 +296,42 @@ def test_decode_conv_argument_errors(lib):
     assert decode_conv(lib, st=states(50, 50, 52)) == ALIAS          # two states at once
     assert decode_conv(lib, st=states(50, 51, 40)) == ALIAS          # a state over taps
     assert decode_conv(lib, B=0) == OK
+
+
+# ------------------------------------------------------- sequence split ----
+
+def split(lib, dtype=BF16, B=1, T=4096, H=2, dk=128, dv=128, chunk=16, P=4, ptrs=None,
+          ws_bytes=None):
+    names = ["q", "k", "v", "z", "beta", "A", "S0", "o", "S_T", "ws"]
+    p = {n: P_(i) for i, n in enumerate(names)}
+    if ptrs:
+        p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.kda_prefill_split_workspace_size(dtype, B, T, H, dk, dv, chunk, P)
+    return lib.kda_prefill_split(dtype, B, T, H, dk, dv, chunk, P, p["q"], p["k"], p["v"],
+                                 p["z"], p["beta"], p["A"], p["S0"], p["o"], p["S_T"], p["ws"],
+                                 ws_bytes, None)
+
+
+P_ = P
+
+
+def test_split_argument_errors(lib):
+    assert split(lib, T=-1) == SHAPE
+    assert split(lib, P=0) == UNSUP
+    assert split(lib, P=1025) == UNSUP
+    assert split(lib, dtype=F32) == UNSUP            # the role-split kernel only
+    assert split(lib, chunk=64) == UNSUP
+    assert split(lib, dk=16, dv=16) == UNSUP
+    assert split(lib, ptrs={"z": None}) == NULL
+    assert split(lib, ptrs={"ws": None}) == WORKSPACE
+    assert split(lib, ws_bytes=4096) == WORKSPACE
+    assert split(lib, ptrs={"ws": P_(9, 8)}) == MISALIGNED
+    assert split(lib, ptrs={"ws": P_(7, 0)}) == ALIAS   # workspace over o
+    assert split(lib, ptrs={"o": P_(0, 64)}) == ALIAS   # the plain call's rules hold
+    assert split(lib, B=0) == OK
+    # workspace: three [B*P, H, d, d] fp32 state sets plus offsets
+    n = lib.kda_prefill_split_workspace_size(BF16, 1, 4096, 2, 128, 128, 16, 4)
+    assert n >= 3 * 4 * 2 * 128 * 128 * 4
+    assert lib.kda_prefill_split_workspace_size(BF16, 1, 4096, 2, 128, 128, 16, 1) == 0
+    assert lib.kda_prefill_split_workspace_size(F32, 1, 4096, 2, 128, 128, 16, 4) == 0
