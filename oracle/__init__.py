@@ -15,6 +15,9 @@ Parity status of each function (what pins it, see ``tests/test_oracle_pins.py``)
                T=1, dk=1), overwrite, capacity, an independent fp64 chunked
                model, split / linearity / independence invariants.
   decode_step -- pinned: T single steps equal one prefill over T, T=1 closed form.
+  prefill_bwd -- pinned: central finite differences of the (pinned) forward
+               on every input element of small cases, T = 0 and beta = 0
+               special cases, a planted-mistake battery.
   prefill_conv, decode_step_conv -- the prologue of ``oracle/prologue.py``
                (short convolutions, q/k normalization) followed by the pinned
                recurrence; see that module for the readings and pins.
@@ -32,8 +35,8 @@ _SRC = os.path.join(_HERE, "kda_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
 _lib = None
 
-__all__ = ["build", "gate", "prefill", "decode_step", "prefill_conv", "decode_step_conv",
-           "max_threads"]
+__all__ = ["build", "gate", "prefill", "prefill_bwd", "decode_step", "prefill_conv",
+           "decode_step_conv", "max_threads"]
 
 
 def build(force: bool = True) -> str:
@@ -59,6 +62,8 @@ def _bind(path: str):
     lib.kda_oracle_gate_f64.argtypes = [i64, dp, ctypes.c_double, dp]
     lib.kda_oracle_max_threads.restype = ctypes.c_int
     lib.kda_oracle_max_threads.argtypes = []
+    lib.kda_oracle_bwd_f64.restype = ctypes.c_int
+    lib.kda_oracle_bwd_f64.argtypes = [i64, i64, i64, i64, i64] + [dp] * 16 + [ctypes.c_int]
     return lib
 
 
@@ -132,6 +137,29 @@ def prefill(q, k, v, z, beta, A, S0=None, threads: int | None = None, lib=None):
     if rc != 0:
         raise RuntimeError(f"kda_oracle_f64 failed with code {rc}")
     return o, S_T
+
+
+def prefill_bwd(q, k, v, z, beta, A, S0, dO, dST=None, threads: int | None = None, lib=None):
+    """Gradients of L through the recurrence, given dO = dL/do [B,T,H,dv] and
+    dST = dL/dS_T [B,H,dk,dv] (None = 0).  Returns a dict with dq, dk, dz
+    [B,T,H,dk], dv [B,T,H,dv], dbeta [B,T,H], dA [H], dS0 [B,H,dk,dv] (fp64)."""
+    q, k, v, z, beta, A, dO = (_f64(x) for x in (q, k, v, z, beta, A, dO))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    s0 = None if S0 is None else _f64(S0)
+    dst = None if dST is None else _f64(dST)
+    out = {"dq": np.zeros((B, T, H, dk)), "dk": np.zeros((B, T, H, dk)),
+           "dv": np.zeros((B, T, H, dv)), "dz": np.zeros((B, T, H, dk)),
+           "dbeta": np.zeros((B, T, H)), "dA": np.zeros((H,)), "dS0": np.zeros((B, H, dk, dv))}
+    n = threads if threads is not None else (os.cpu_count() or 1)
+    n = max(1, min(int(n), max(1, B * H)))
+    rc = (lib or _load()).kda_oracle_bwd_f64(
+        B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A), _ptr(s0),
+        _ptr(dO), _ptr(dst), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dz"]),
+        _ptr(out["dbeta"]), _ptr(out["dA"]), _ptr(out["dS0"]), n)
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_bwd_f64 failed with code {rc}")
+    return out
 
 
 def decode_step(q, k, v, z, beta, A, S, threads: int | None = None):
