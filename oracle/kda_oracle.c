@@ -179,7 +179,7 @@ int kda_oracle_bwd_f64(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
 #pragma omp parallel for schedule(static) num_threads(nthreads) reduction(| : failed)
     for (int64_t u = 0; u < units; ++u) {
         const int64_t b = u / H, h = u % H;
-        const double c = exp(A[h]);
+        const double ce = exp(A[h]);   /* e^A */
         /* states S_0 .. S_T (S_0 = initial) */
         double *Sall = (double *)malloc(sizeof(double) * (size_t)((T + 1) * sd));
         double *F = (double *)malloc(sizeof(double) * (size_t)sd);
@@ -203,7 +203,7 @@ int kda_oracle_bwd_f64(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
             const double bt = beta[row];
             const double *Sp = Sall + t * sd;
             double *Sn = Sall + (t + 1) * sd;
-            for (int64_t i = 0; i < dk; ++i) alpha[i] = exp(oracle_gate(c, zt[i]));
+            for (int64_t i = 0; i < dk; ++i) alpha[i] = exp(oracle_gate(ce, zt[i]));
             for (int64_t i = 0; i < dk; ++i)
                 for (int64_t j = 0; j < dv; ++j) Sn[i * dv + j] = alpha[i] * Sp[i * dv + j];
             for (int64_t j = 0; j < dv; ++j) w[j] = 0.0;
@@ -230,7 +230,7 @@ int kda_oracle_bwd_f64(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
             double *dvt = dv_out + row * dv;
             double dbt = 0.0;
             /* recompute F and w of this token */
-            for (int64_t i = 0; i < dk; ++i) alpha[i] = exp(oracle_gate(c, zt[i]));
+            for (int64_t i = 0; i < dk; ++i) alpha[i] = exp(oracle_gate(ce, zt[i]));
             for (int64_t i = 0; i < dk; ++i)
                 for (int64_t j = 0; j < dv; ++j) F[i * dv + j] = alpha[i] * Sp[i * dv + j];
             for (int64_t j = 0; j < dv; ++j) w[j] = 0.0;
@@ -282,16 +282,16 @@ int kda_oracle_bwd_f64(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                 double da = 0.0;
                 for (int64_t j = 0; j < dv; ++j) da += dS[i * dv + j] * Sp[i * dv + j];
                 dalpha[i] = da;
-                for (int64_t j = 0; j < dv; ++j) dS[i * dv + j] *= alpha[i];
+                for (int64_t j = 0; j < dv; ++j) dS[i * dv + j] = alpha[i] * dS[i * dv + j];
             }
             /* gate: alpha = exp(g), g = g_min sigma(c z) */
             for (int64_t i = 0; i < dk; ++i) {
-                const double x = c * zt[i];
+                const double x = ce * zt[i];
                 const double s = 1.0 / (1.0 + exp(-x));
                 const double dg = dalpha[i] * alpha[i];
                 const double dx = dg * KDA_ORACLE_GMIN * s * (1.0 - s);
-                dzt[i] = c * dx;
-                dA_acc += c * zt[i] * dx;
+                dzt[i] = ce * dx;
+                dA_acc += ce * zt[i] * dx;
             }
             dbeta[row] = dbt;
         }

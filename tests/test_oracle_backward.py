@@ -112,10 +112,11 @@ def test_backward_thread_count_invariant():
 
 MUTANTS = {
     "erase_beta_sign": ("dbt -= kt[i] * sw;", "dbt += kt[i] * sw;"),
-    "fade_on_columns": ("dS[i * dv + j] *= alpha[i];", "dS[i * dv + j] *= alpha[j % dk];"),
+    "fade_on_columns": ("dS[i * dv + j] = alpha[i] * dS[i * dv + j];",
+                        "dS[i * dv + j] = alpha[j % dk] * dS[i * dv + j];"),
     "drop_key_through_w": ("dkt[i] += fd;", "(void)fd;"),
-    "gate_without_scale": ("dzt[i] = c * dx;", "dzt[i] = dx;"),
-    "dA_without_z": ("dA_acc += c * zt[i] * dx;", "dA_acc += c * dx;"),
+    "gate_without_scale": ("dzt[i] = ce * dx;", "dzt[i] = dx;"),
+    "dA_without_z": ("dA_acc += ce * zt[i] * dx;", "dA_acc += ce * dx;"),
     "read_old_state": ("acc += St[i * dv + j] * dot[j];", "acc += Sp[i * dv + j] * dot[j];"),
     "dv_without_beta": ("dvt[j] = bt * sk;", "dvt[j] = sk;"),
     "sigmoid_slope": ("dg * KDA_ORACLE_GMIN * s * (1.0 - s)", "dg * KDA_ORACLE_GMIN * s"),
