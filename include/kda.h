@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -287,6 +287,24 @@ kda_status kda_conv_norm(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
                          const void *q, const void *k, const void *v,
                          const void *const *state_in, void *const *state_out,
                          void *q_out, void *k_out, void *v_out, void *stream);
+
+/*
+ * The prologue over N packed variable-length sequences (the layout of
+ * kda_prefill_varlen: cu_seqlens device int64 [N+1], 8-byte aligned; tokens
+ * [cu_seqlens[i], cu_seqlens[i+1]) belong to sequence i; offsets are clamped
+ * into [0, T_total]).  q, k, v, q_out, k_out, v_out: [T_total, H, d]; the
+ * convolution states are per sequence, [N, W-1, H, d] each: a token's taps
+ * never reach into another sequence, they read its sequence's state_in rows
+ * (or zeros) instead, and state_out receives each sequence's last W-1 raw
+ * inputs.  Each sequence's result equals kda_conv_norm on that sequence
+ * alone.  Other conventions as kda_conv_norm.
+ */
+kda_status kda_conv_norm_varlen(int dtype, int64_t N, int64_t T_total, int64_t H, int64_t dk,
+                                int64_t dv, const int64_t *cu_seqlens,
+                                const kda_short_conv *conv,
+                                const void *q, const void *k, const void *v,
+                                const void *const *state_in, void *const *state_out,
+                                void *q_out, void *k_out, void *v_out, void *stream);
 
 /* Bytes of device workspace kda_prefill_conv needs (the prologue's outputs:
  * three [B,T,H,d] tensors in dtype, each rounded up to 256 bytes). */

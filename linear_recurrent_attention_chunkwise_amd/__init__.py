@@ -6,12 +6,14 @@ binding over it: torch supplies device memory and streams, every arithmetic
 step runs in the library.  There is no CPU fallback; calling into the binding
 without a built library or without a GPU raises.
 """
-from .kda import (KDAError, ShortConv, abi_version, checkpoint_rows, conv_norm, decode_step,
+from .kda import (KDAError, ShortConv, abi_version, checkpoint_rows, conv_norm, conv_norm_varlen,
+                  decode_step,
                   decode_step_conv, library_path, prefill, prefill_conv,
                   prefill_conv_workspace_size, prefill_split_workspace_size, prefill_varlen,
                   prefill_workspace_size)
 
 __all__ = ["KDAError", "ShortConv", "abi_version", "checkpoint_rows", "conv_norm",
+           "conv_norm_varlen",
            "decode_step", "decode_step_conv", "library_path", "prefill", "prefill_conv",
            "prefill_conv_workspace_size", "prefill_split_workspace_size", "prefill_varlen",
            "prefill_workspace_size"]

@@ -391,6 +391,48 @@ kda_status kda_conv_norm(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
     return kda::launch_conv_norm(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_conv_norm_varlen(int dtype, int64_t N, int64_t T_total, int64_t H, int64_t dk,
+                                int64_t dv, const int64_t *cu_seqlens, const kda_short_conv *conv,
+                                const void *q, const void *k, const void *v,
+                                const void *const *state_in, void *const *state_out,
+                                void *q_out, void *k_out, void *v_out, void *stream) {
+    if (N < 0 || T_total < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (dk != dv) return KDA_ERR_UNSUPPORTED;
+    const int64_t D = dk, esz = dtype == KDA_BF16 ? 2 : 4;
+    ConvSpec cs;
+    const kda_status st = conv_check(dtype, N, H, D, conv, state_in, state_out, false, &cs);
+    if (st != KDA_OK) return st;
+    int64_t th, nin;
+    if (!mul_ok(T_total, H, kMaxElems, &th) || !mul_ok(th, D, kMaxElems / 4, &nin))
+        return KDA_ERR_SHAPE;
+    if (!conv_sizes_ok(dtype, 1, T_total, H, D)) return KDA_ERR_SHAPE;
+    if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
+    if (cu_seqlens && ((uintptr_t)cu_seqlens & 7u) != 0) return KDA_ERR_MISALIGNED;
+    if (nin > 0 && (!q || !k || !v || !q_out || !k_out || !v_out)) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, q_out, k_out, v_out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const Range rin[] = {range_of(q, nin * esz), range_of(k, nin * esz), range_of(v, nin * esz),
+                         cs.rw[0], cs.rw[1], cs.rw[2], cs.rsin[0], cs.rsin[1], cs.rsin[2],
+                         range_of(cu_seqlens, N > 0 ? (N + 1) * 8 : 0)};
+    const Range rout[] = {range_of(q_out, nin * esz), range_of(k_out, nin * esz),
+                          range_of(v_out, nin * esz), cs.rsout[0], cs.rsout[1], cs.rsout[2]};
+    for (int i = 0; i < 6; ++i) {
+        for (const Range &r : rin)
+            if (overlaps(rout[i], r)) return KDA_ERR_ALIAS;
+        for (int j = 0; j < 6; ++j)
+            if (i != j && overlaps(rout[i], rout[j])) return KDA_ERR_ALIAS;
+    }
+    if (N == 0 || H == 0) return KDA_OK;
+    const void *x[3] = {q, k, v};
+    void *y[3] = {q_out, k_out, v_out};
+    kda::ConvNormArgs a = conv_args(dtype, 1, T_total, H, D, cs, x, y, stream);
+    a.cu = cu_seqlens;
+    a.N = N;
+    return kda::launch_conv_norm(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 size_t kda_prefill_conv_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
                                        int64_t dv, int32_t chunk) {
     (void)chunk;

@@ -133,8 +133,24 @@ __device__ __forceinline__ float silu(float y) {
 }  // namespace
 
 
+// Sequence of packed token t: the largest b < N with cu[b] <= t (offsets
+// clamped into [0, T] as in seq_range).
+__device__ __forceinline__ int64_t seq_of(const int64_t *cu, int64_t N, int64_t T, int64_t t) {
+    int64_t lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        int64_t c = cu[mid];
+        c = c < 0 ? 0 : (c > T ? T : c);
+        if (c <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
 // The tile of one wave: TT tokens x 512 channels (lane = channel octet).
-template <typename TI, int D, int TT, int W, bool ACT, bool NORM>
+// VL: the token axis packs N sequences (cu offsets); a row's taps that reach
+// before its sequence's first token read that sequence's convolution state.
+template <typename TI, int D, int TT, int W, bool ACT, bool NORM, bool VL>
 __device__ __forceinline__ void conv_body(const ConvTensor &ct, const ConvNormArgs &p, int64_t b,
                                           int64_t slab, int64_t tile, int lane,
                                           const float *sw) {
@@ -165,6 +181,9 @@ __device__ __forceinline__ void conv_body(const ConvTensor &ct, const ConvNormAr
         const auto rs = make_rsrc(xb - 3 * (int64_t)rowbytes, 3 * (int64_t)rowbytes);
 #pragma unroll
         for (int r = 0; r < 3; ++r) xr[r].load(rs, voff, r * rowbytes);
+    } else if (VL) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) xr[r].zero();   // replaced per row below
     } else if (ct.sin && W > 1) {
         const char *sb = static_cast<const char *>(ct.sin) + (b * (W - 1) * rowel) * ESZ;
         const auto rs = make_rsrc(sb, (int64_t)(W - 1) * rowbytes);
@@ -181,15 +200,50 @@ __device__ __forceinline__ void conv_body(const ConvTensor &ct, const ConvNormAr
     char *yb = static_cast<char *>(ct.y) + ((b * T + t0) * rowel) * ESZ;
     const auto ys = make_rsrc(yb, nrows * rowbytes);
     const float eps = p.eps;
+    // packed sequences: the sequence of the current row and its first token
+    int64_t sq = 0, sq_start = 0, sq_next = 0;
+    if constexpr (VL) {
+        sq = seq_of(p.cu, p.N, T, t0);
+        auto clampT = [&](int64_t c) { return c < 0 ? 0 : (c > T ? T : c); };
+        sq_start = clampT(p.cu[sq]);
+        sq_next = sq + 1 < p.N ? clampT(p.cu[sq + 1]) : T;
+    }
 #pragma unroll
     for (int s = 0; s < TT; ++s) {
+        Oct<TI> src[4] = {xr[s], xr[s + 1], xr[s + 2], xr[s + 3]};
+        if constexpr (VL) {
+            const int64_t t = t0 + s;
+            // next sequence(s) starting at or before this row (empty ones skipped)
+            while (sq + 1 < p.N && sq_next <= t) {
+                ++sq;
+                sq_start = sq_next;
+                int64_t c = sq + 1 < p.N ? p.cu[sq + 1] : T;
+                sq_next = c < sq_start ? sq_start : (c > T ? T : c);
+            }
+            if (t - 3 < sq_start) {
+                // taps before the sequence start: its state rows, or zeros
+                const char *sb = ct.sin ? static_cast<const char *>(ct.sin) +
+                                              (sq * (W - 1) * rowel) * ESZ
+                                        : nullptr;
+                const auto rs = make_rsrc(sb, sb ? (int64_t)(W - 1) * rowbytes : 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t tok = t - 3 + j;
+                    if (tok < sq_start) {
+                        const int64_t sr = (W - 1) + (tok - sq_start);
+                        if (sb && sr >= 0) src[j].load(rs, voff, (int)sr * rowbytes);
+                        else src[j].zero();
+                    }
+                }
+            }
+        }
         float y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            y[e] = wt[e][0] * xr[s].at(e);
-            y[e] = fmaf(wt[e][1], xr[s + 1].at(e), y[e]);
-            y[e] = fmaf(wt[e][2], xr[s + 2].at(e), y[e]);
-            y[e] = fmaf(wt[e][3], xr[s + 3].at(e), y[e]);
+            y[e] = wt[e][0] * src[0].at(e);
+            y[e] = fmaf(wt[e][1], src[1].at(e), y[e]);
+            y[e] = fmaf(wt[e][2], src[2].at(e), y[e]);
+            y[e] = fmaf(wt[e][3], src[3].at(e), y[e]);
         }
         if constexpr (ACT) {
 #pragma unroll
@@ -206,7 +260,7 @@ __device__ __forceinline__ void conv_body(const ConvTensor &ct, const ConvNormAr
         }
         if (active) Oct<TI>::store_f32(y, ys, voff, s * rowbytes);
     }
-    if (tile == p.ntile - 1 && ct.sout && W > 1 && active) {
+    if (!VL && tile == p.ntile - 1 && ct.sout && W > 1 && active) {
         char *sb = static_cast<char *>(ct.sout) + (b * (W - 1) * rowel) * ESZ;
         const auto rs = make_rsrc(sb, (int64_t)(W - 1) * rowbytes);
         const int64_t first = T - (W - 1);
@@ -220,7 +274,7 @@ __device__ __forceinline__ void conv_body(const ConvTensor &ct, const ConvNormAr
 
 // One workgroup = 4 waves = 4 consecutive token tiles of one 512-channel slab
 // of one tensor (blockIdx.y: q, k, v) of one sequence.
-template <typename TI, int D, int TT, int W, bool ACT>
+template <typename TI, int D, int TT, int W, bool ACT, bool VL>
 __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormArgs p) {
     __shared__ float sw[8 * 4 * 64];   // taps of the slab's 512 channels, [e*W + j][lane]
     const ConvTensor ct = blockIdx.y == 0 ? p.t[0] : (blockIdx.y == 1 ? p.t[1] : p.t[2]);
@@ -246,8 +300,8 @@ __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormArgs p) {
     __syncthreads();
     const int64_t tile = grp * 4 + wave;
     if (tile >= p.ntile) return;
-    if (ct.norm) conv_body<TI, D, TT, W, ACT, true>(ct, p, b, slab, tile, lane, sw);
-    else conv_body<TI, D, TT, W, ACT, false>(ct, p, b, slab, tile, lane, sw);
+    if (ct.norm) conv_body<TI, D, TT, W, ACT, true, VL>(ct, p, b, slab, tile, lane, sw);
+    else conv_body<TI, D, TT, W, ACT, false, VL>(ct, p, b, slab, tile, lane, sw);
 }
 
 bool conv_supported(int dtype, int64_t D) {
@@ -255,6 +309,43 @@ bool conv_supported(int dtype, int64_t D) {
 }
 
 int conv_tile_tokens(int dtype) { return dtype == 1 ? 16 : 8; }
+
+// New convolution states of packed sequences: row i of sequence b's state is
+// raw token end_b - (W-1) + i, or, for a sequence shorter than W-1, a row of
+// its old state (zeros without one).  One thread per (sequence, channel
+// octet, tensor).
+template <typename TI>
+__global__ __launch_bounds__(256) void kda_conv_state_varlen_kernel(ConvNormArgs p) {
+    constexpr int ESZ = sizeof(TI);
+    const ConvTensor ct = blockIdx.y == 0 ? p.t[0] : (blockIdx.y == 1 ? p.t[1] : p.t[2]);
+    const int64_t rowoct = p.H * (p.D / 8);
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (!ct.sout || i >= p.N * rowoct) return;
+    const int64_t b = i / rowoct, c8 = i % rowoct;
+    const SeqRange sr = seq_range(p.cu, b, p.T);
+    const int64_t rowel = p.H * p.D;
+    const int W = p.W;
+    for (int r = 0; r < W - 1; ++r) {
+        const int64_t tok = sr.start + sr.len - (W - 1) + r;
+        Oct<TI> val;
+        if (tok >= sr.start) {
+            const auto rs = make_rsrc(static_cast<const char *>(ct.x) + tok * rowel * ESZ,
+                                      rowel * ESZ);
+            val.load(rs, (int)(c8 * 8 * ESZ), 0);
+        } else if (ct.sin) {
+            const int64_t srow = (W - 1) + (tok - sr.start);   // >= 0: tok >= start - (W-1)
+            const auto rs = make_rsrc(static_cast<const char *>(ct.sin) +
+                                          ((b * (W - 1) + srow) * rowel) * ESZ,
+                                      rowel * ESZ);
+            val.load(rs, (int)(c8 * 8 * ESZ), 0);
+        } else {
+            val.zero();
+        }
+        const auto ws = make_rsrc(static_cast<char *>(ct.sout) + ((b * (W - 1) + r) * rowel) * ESZ,
+                                  rowel * ESZ);
+        val.store(ws, (int)(c8 * 8 * ESZ), 0);
+    }
+}
 
 template <typename TI, int D, int TT, int W, bool ACT>
 static hipError_t launch_conv_t(const ConvNormArgs &a0) {
@@ -264,9 +355,20 @@ static hipError_t launch_conv_t(const ConvNormArgs &a0) {
     const int64_t nslab = (rowoct + 63) / 64;
     a.ntile = ntile;
     a.ngroup = (ntile + 3) / 4;
+    if (a.cu) {
+        // packed sequences: tiles over the whole token axis, then the states
+        if (a.T > 0)
+            hipLaunchKernelGGL((kda_conv_norm_kernel<TI, D, TT, W, ACT, true>),
+                               dim3((unsigned)(nslab * a.ngroup), 3), dim3(256), 0, a.stream, a);
+        const int64_t nst = a.N * rowoct;
+        if (W > 1 && nst > 0)
+            hipLaunchKernelGGL((kda_conv_state_varlen_kernel<TI>),
+                               dim3((unsigned)((nst + 255) / 256), 3), dim3(256), 0, a.stream, a);
+        return hipGetLastError();
+    }
     const int64_t nblk = a.B * nslab * a.ngroup;
-    hipLaunchKernelGGL((kda_conv_norm_kernel<TI, D, TT, W, ACT>), dim3((unsigned)nblk, 3), dim3(256), 0,
-                       a.stream, a);
+    hipLaunchKernelGGL((kda_conv_norm_kernel<TI, D, TT, W, ACT, false>), dim3((unsigned)nblk, 3),
+                       dim3(256), 0, a.stream, a);
     return hipGetLastError();
 }
 

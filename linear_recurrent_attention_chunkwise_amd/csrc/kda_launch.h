@@ -56,7 +56,11 @@ struct ConvNormArgs {
     int W;                // taps, 1..4
     int act;              // 0: none, 1: SiLU
     float eps;
-    int64_t ntile, ngroup;   // set by the launcher
+    // Packed sequences (cu != NULL): N sequences over the T-token axis (B = 1);
+    // states are [N, W-1, H, D].
+    const int64_t *cu = nullptr;
+    int64_t N = 0;
+    int64_t ntile = 0, ngroup = 0;   // set by the launcher
     hipStream_t stream;
 };
 

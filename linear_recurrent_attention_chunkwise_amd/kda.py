@@ -85,6 +85,9 @@ def _load():
     lib.kda_conv_norm.restype = ctypes.c_int
     lib.kda_conv_norm.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, cp, vp, vp, vp,
                                   vp, vp, vp, vp, vp, vp]
+    lib.kda_conv_norm_varlen.restype = ctypes.c_int
+    lib.kda_conv_norm_varlen.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, vp, cp, vp, vp,
+                                         vp, vp, vp, vp, vp, vp, vp]
     lib.kda_prefill_conv_workspace_size.restype = sz
     lib.kda_prefill_conv_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i32]
     lib.kda_prefill_conv.restype = ctypes.c_int
@@ -388,6 +391,49 @@ def conv_norm(q, k, v, wq, wk, wv, state=None, act: str = "none", eps: float = 1
                            _ptr(v), sin, sout, _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
                            _stream_handle(dev))
     _check(st, "kda_conv_norm")
+    return out[0], out[1], out[2], state_out
+
+
+def conv_norm_varlen(q, k, v, wq, wk, wv, cu_seqlens, state=None, act: str = "none",
+                     eps: float = 1e-6, out=None, state_out=True):
+    """The prologue over N packed sequences: q, k [T,H,dk], v [T,H,dv];
+    cu_seqlens int64 [N+1] (a cuda tensor, or host values copied over);
+    ``state`` None or (sq, sk, sv) each [N,W-1,H,d].  Returns (q_hat, k_hat,
+    v_conv, new_state) as ``conv_norm`` does."""
+    lib = _load()
+    if q.dim() != 3:
+        raise ValueError("q must be [T,H,dk] (packed sequences)")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("the KDA prologue runs on the GPU; inputs must be cuda tensors")
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    if not isinstance(cu_seqlens, torch.Tensor):
+        cu_seqlens = torch.tensor(list(cu_seqlens), dtype=torch.int64)
+    if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int64 tensor [N+1]")
+    cu_dev = cu_seqlens.to(dev).contiguous()
+    N = cu_dev.numel() - 1
+    _require(q, "q", (T, H, dk), dt, dev)
+    _require(k, "k", (T, H, dk), dt, dev)
+    _require(v, "v", (T, H, dv), dt, dev)
+    cs, W = _short_conv(wq, wk, wv, act, eps, H, dk, dv, dev)
+    sin = _states(state, "state", N, W, H, dk, dv, dt, dev)
+    if state_out is True:
+        state_out = _new_states(N, W, H, dk, dv, dt, dev)
+    elif state_out is False:
+        state_out = None
+    sout = _states(state_out, "state_out", N, W, H, dk, dv, dt, dev)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    for t, ref, name in zip(out, (q, k, v), ("q_out", "k_out", "v_out")):
+        _require(t, name, tuple(ref.shape), dt, dev)
+    st = lib.kda_conv_norm_varlen(_DTYPES[dt], N, T, H, dk, dv, _ptr(cu_dev), ctypes.byref(cs),
+                                  _ptr(q), _ptr(k), _ptr(v), sin, sout, _ptr(out[0]),
+                                  _ptr(out[1]), _ptr(out[2]), _stream_handle(dev))
+    _check(st, "kda_conv_norm_varlen")
     return out[0], out[1], out[2], state_out
 
 

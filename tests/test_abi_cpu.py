@@ -36,7 +36,7 @@ def test_header_declares_expected_api():
         "kda_prefill", "kda_prefill_ex", "kda_prefill_varlen",
         "kda_prefill_varlen_workspace_size", "kda_decode_step", "kda_conv_norm",
         "kda_prefill_conv_workspace_size", "kda_prefill_conv", "kda_decode_step_conv",
-        "kda_prefill_split", "kda_prefill_split_workspace_size"])
+        "kda_prefill_split", "kda_prefill_split_workspace_size", "kda_conv_norm_varlen"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 5
+    assert lib.kda_abi_version() == 6
     for s in range(8):
         assert lib.kda_status_str(s).decode().startswith("KDA_")
     assert lib.kda_status_str(99) == b"unknown kda_status"
@@ -335,3 +335,25 @@ def test_split_argument_errors(lib):
     assert n >= 3 * 4 * 2 * 128 * 128 * 4
     assert lib.kda_prefill_split_workspace_size(BF16, 1, 4096, 2, 128, 128, 16, 1) == 0
     assert lib.kda_prefill_split_workspace_size(F32, 1, 4096, 2, 128, 128, 16, 4) == 0
+
+
+def conv_varlen(lib, dtype=BF16, N=3, T=64, H=2, dk=128, dv=128, conv=None, sin=None,
+                sout=None, ptrs=None):
+    p = {n: P(i) for i, n in enumerate(["q", "k", "v", "qo", "ko", "vo", "cu"])}
+    if ptrs:
+        p.update(ptrs)
+    cs = conv if conv is not None else short_conv()
+    return lib.kda_conv_norm_varlen(dtype, N, T, H, dk, dv, p["cu"], ctypes.byref(cs), p["q"],
+                                    p["k"], p["v"], sin, sout, p["qo"], p["ko"], p["vo"], None)
+
+
+def test_conv_norm_varlen_argument_errors(lib):
+    assert conv_varlen(lib, N=-1) == SHAPE
+    assert conv_varlen(lib, dk=64, dv=64) == UNSUP
+    assert conv_varlen(lib, conv=short_conv(W=6)) == UNSUP
+    assert conv_varlen(lib, ptrs={"cu": None}) == NULL            # N > 0 needs offsets
+    assert conv_varlen(lib, ptrs={"cu": P(6, 4)}) == MISALIGNED   # int64 offsets
+    assert conv_varlen(lib, ptrs={"qo": P(6, 0)}) == ALIAS        # output over the offsets
+    assert conv_varlen(lib, ptrs={"vo": P(2, 32)}) == ALIAS       # output over v
+    assert conv_varlen(lib, sin=states(50, 51, 52), sout=states(53, 52, 55)) == ALIAS
+    assert conv_varlen(lib, N=0, ptrs={"cu": None}) == OK

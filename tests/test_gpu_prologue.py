@@ -27,7 +27,7 @@ EPS = 1e-6
 @pytest.fixture(scope="module")
 def kda():
     import linear_recurrent_attention_chunkwise_amd as m
-    assert m.abi_version() == 5
+    assert m.abi_version() == 6
     return m
 
 
@@ -120,6 +120,66 @@ def test_conv_norm_segments_carry_exactly(kda, gpu_device):
         assert torch.equal(torch.cat([p[i] for p in parts], dim=1), whole[i])
     for a, b in zip(st, whole[3]):
         assert torch.equal(a, b)
+
+
+# ----------------------------------------------------- kda_conv_norm_varlen ----
+
+VARLEN_CONV_LENGTHS = [0, 1, 2, 5, 17, 40, 3, 100, 0, 33]
+
+
+@pytest.mark.parametrize("wname", ["k3_prefill_bf16", "tiny_prefill_f32"])
+@pytest.mark.parametrize("W,act", [(4, "silu"), (2, "none"), (1, "silu")])
+@pytest.mark.parametrize("use_state", [False, True])
+def test_conv_norm_varlen_equals_per_sequence(kda, gpu_device, wname, W, act, use_state):
+    """Packed sequences give, sequence by sequence, the bits of kda_conv_norm on
+    that sequence alone: taps never cross a sequence boundary, each sequence
+    reads its own state rows, and every new state (empty and short sequences
+    included) is that sequence's."""
+    lengths = VARLEN_CONV_LENGTHS
+    Tt = sum(lengths)
+    N = len(lengths)
+    w = WORKLOADS[wname].with_(B=1, H=3)
+    inp = make_layer_inputs(w.with_(B=N), W, T=max(lengths))
+    # packed tokens: sequence i takes its first lengths[i] tokens of batch row i
+    pk = {n: torch.cat([inp[n][i, :L] for i, L in enumerate(lengths)], dim=0).contiguous()
+          for n in ("q", "k", "v")}
+    g = {n: pk[n].to(gpu_device) for n in pk}
+    taps = tuple(inp[n].to(gpu_device) for n in ("wq", "wk", "wv"))
+    st = tuple(inp[n].to(gpu_device) for n in ("sq", "sk", "sv")) if use_state else None
+    cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int64)
+    _say(f"[conv_norm_varlen] {wname} W={W} act={act} state={use_state} lengths={lengths}")
+    qh, kh, vc, ns = kda.conv_norm_varlen(g["q"], g["k"], g["v"], *taps, cu, state=st, act=act,
+                                          eps=EPS)
+    torch.cuda.synchronize()
+    off = 0
+    for i, L in enumerate(lengths):
+        seg = [x[off:off + L].unsqueeze(0).contiguous() for x in (g["q"], g["k"], g["v"])]
+        sti = tuple(t[i:i + 1].contiguous() for t in st) if use_state else None
+        r = kda.conv_norm(*seg, *taps, state=sti, act=act, eps=EPS)
+        torch.cuda.synchronize()
+        for a, b_ in zip((qh, kh, vc), r[:3]):
+            assert torch.equal(a[off:off + L], b_[0]), (i, L)
+        for a, b_ in zip(ns, r[3]):
+            assert torch.equal(a[i:i + 1], b_), (i, L)
+        off += L
+    # and the oracle on the whole packing, sequence by sequence
+    tol = TOL[inp["q"].dtype]
+    off = 0
+    for i, L in enumerate(lengths):
+        sti = tuple(host(inp[n][i:i + 1]) for n in ("sq", "sk", "sv")) if use_state else (
+            None, None, None)
+        rq, rk, rv, rs = prologue.conv_norm(*(host(pk[n][off:off + L]).reshape(
+                                                  1, L, 3, pk[n].shape[-1])
+                                              for n in ("q", "k", "v")),
+                                            host(inp["wq"]), host(inp["wk"]), host(inp["wv"]),
+                                            *sti, act, EPS)
+        if L > 0:
+            errs = [slice_relerr(host(x[off:off + L])[None], r_, 2)
+                    for x, r_ in ((qh, rq), (kh, rk), (vc, rv))]
+            assert max(errs) <= tol, (i, errs)
+        for a, b_ in zip(ns, rs):
+            assert np.array_equal(host(a[i:i + 1]), b_), i
+        off += L
 
 
 # --------------------------------------------------------- kda_prefill_conv ----
