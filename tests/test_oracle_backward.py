@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+from tests.kda_pins import chunked_bwd, relerr
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "kda_oracle.c")
 
@@ -138,3 +139,18 @@ def test_backward_mutant_is_caught(tmp_path, name):
     x, G, Hs = _case(0)
     errs = finite_difference_errors(_grads(x, G, Hs, lib=lib), x, G, Hs)
     assert max(errs.values()) > 1e-4, f"mutant {name} passed the finite-difference pin"
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 3, 5, 16])
+def test_chunked_backward_model_matches_adjoint(chunk):
+    """The chunk-parallel reverse mode (a model of a chunked GPU backward)
+    equals the step-by-step adjoint, for chunk lengths that divide T, do not,
+    and exceed it; decays near 1 included."""
+    for T, zshift in ((7, 0.0), (11, -6.0), (4, 0.0)):
+        x, G, Hs = _case(7 + T, B=2, T=T, H=2, dk=4, dv=3)
+        x["z"] = x["z"] + zshift
+        ref = _grads(x, G, Hs)
+        got = chunked_bwd(*(x[n] for n in ("q", "k", "v", "z", "beta", "A", "S0")), G, Hs,
+                          chunk=chunk)
+        for key in ref:
+            assert relerr(got[key], ref[key]) < 1e-10, (chunk, T, key)
