@@ -288,7 +288,7 @@ def test_prefill_conv_k3_sampled_heads(kda, gpu_device):
 # ----------------------------------------------------- kda_decode_step_conv ----
 
 DECODE_CASES = [(wname, W, act) for wname in ("k3_decode_bf16", "tiny_decode_f32")
-                for W in (1, 2, 4) for act in ACTS]
+                for W in (1, 2, 3, 4) for act in ACTS]
 
 
 def _decode_workload(wname):
