@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -208,6 +208,44 @@ kda_status kda_prefill_split(int dtype, int64_t B, int64_t T, int64_t H, int64_t
 size_t kda_prefill_split_workspace_size(int dtype, int64_t B, int64_t T, int64_t H,
                                         int64_t dk, int64_t dv, int32_t chunk,
                                         int32_t segments);
+
+/*
+ * Backward of the prefill: gradients of a loss L through the recurrence of
+ * section 1, in the chunked-parallel form that the K3 coverage page
+ * (nishifamily.com/k3, innovation table, row "Kimi Delta Attention (linear)")
+ * names as the next KDA primitive after the serving form.
+ *
+ *   in : q, k, z [B,T,H,dk], v [B,T,H,dv], beta [B,T,H] (dtype), A [H] fp32,
+ *        S0 [B,H,dk,dv] fp32 or NULL (zeros) -- the forward call's inputs;
+ *        dO [B,T,H,dv] (dtype) = dL/do; dS_T [B,H,dk,dv] fp32 = dL/dS_T, or
+ *        NULL (zero).
+ *   out (all fp32): dq, dk, dz [B,T,H,dk]; dv [B,T,H,dv]; dbeta [B,T,H];
+ *        dA [H] (summed over b, t and key channels); dS0 [B,H,dk,dv].
+ *        Every output is written in full (dS0 also when S0 is NULL).
+ *   workspace: kda_prefill_bwd_workspace_size bytes, 16-byte aligned; scratch
+ *        (calls sharing it must not overlap).
+ *
+ * The call reruns the forward with a state checkpoint every 16 tokens, then
+ * works chunk by chunk in reverse: per 16-token chunk the S-independent
+ * factors in parallel, the state gradient carried backwards over the chunks
+ * (one workgroup per (b, h, 64 value columns)), and the per-token gradients
+ * in parallel again.  Arithmetic is fp32; no atomics, so results are bitwise
+ * reproducible.  Supported: dtype in {KDA_F32, KDA_BF16}, dk == dv in {16,
+ * 128}.  Outputs must not overlap one another, any input or the workspace.
+ * Errors as kda_prefill_ex.
+ */
+kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                           int64_t dv,
+                           const void *q, const void *k, const void *v, const void *z,
+                           const void *beta, const float *A, const float *S0,
+                           const void *dO, const float *dS_T,
+                           float *dq, float *dk_out, float *dv_out, float *dz,
+                           float *dbeta, float *dA, float *dS0,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace kda_prefill_bwd needs (0 for unsupported arguments). */
+size_t kda_prefill_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t H,
+                                      int64_t dk, int64_t dv);
 
 /*
  * One fused recurrent decode step for B sequences (the "KDA decode" half of

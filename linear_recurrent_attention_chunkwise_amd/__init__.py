@@ -7,13 +7,14 @@ step runs in the library.  There is no CPU fallback; calling into the binding
 without a built library or without a GPU raises.
 """
 from .kda import (KDAError, ShortConv, abi_version, checkpoint_rows, conv_norm, conv_norm_varlen,
-                  decode_step,
-                  decode_step_conv, library_path, prefill, prefill_conv,
+                  decode_step, decode_step_conv, library_path, prefill, prefill_bwd,
+                  prefill_bwd_workspace_size, prefill_conv,
                   prefill_conv_workspace_size, prefill_split_workspace_size, prefill_varlen,
                   prefill_workspace_size)
 
 __all__ = ["KDAError", "ShortConv", "abi_version", "checkpoint_rows", "conv_norm",
            "conv_norm_varlen",
-           "decode_step", "decode_step_conv", "library_path", "prefill", "prefill_conv",
+           "decode_step", "decode_step_conv", "library_path", "prefill", "prefill_bwd",
+           "prefill_bwd_workspace_size", "prefill_conv",
            "prefill_conv_workspace_size", "prefill_split_workspace_size", "prefill_varlen",
            "prefill_workspace_size"]

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_conv.hip", "kda_decode.hip", "kda_prefill.hip", "kda_prefill16.hip", "kda_split.hip"]
+SOURCES = ["kda_api.hip", "kda_backward.hip", "kda_conv.hip", "kda_decode.hip", "kda_prefill.hip", "kda_prefill16.hip", "kda_split.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 # Per-source code-generation options.  The role-split prefill is bound by the
 # latency of its per-chunk chain; the instruction-level-parallelism scheduler

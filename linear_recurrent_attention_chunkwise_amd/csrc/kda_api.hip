@@ -667,3 +667,114 @@ kda_status kda_prefill_split(int dtype, int64_t B, int64_t T, int64_t H, int64_t
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- backward --
+
+namespace {
+
+constexpr int kBwdChunk = 16;
+
+struct BwdLayout {
+    size_t o, S_T, ckpt, prep, part, dA, total;   // byte offsets, and the size
+};
+
+bool bwd_layout(int dtype, int64_t B, int64_t T, int64_t H, int64_t D, BwdLayout *lay) {
+    const int64_t esz = dtype == KDA_BF16 ? 2 : 4;
+    const int64_t nchunk = (T + kBwdChunk - 1) / kBwdChunk, nfull = T / kBwdChunk;
+    int64_t bt, bth, nin, bh, units, nst, nck, nprep, npart;
+    if (!mul_ok(B, T, kMaxElems, &bt) || !mul_ok(bt, H, kMaxElems, &bth) ||
+        !mul_ok(bth, D, kMaxElems / 16, &nin) || !mul_ok(B, H, kMaxElems, &bh) ||
+        !mul_ok(bh, D * D, kMaxElems / 16, &nst) || !mul_ok(bh, nchunk, kMaxElems, &units) ||
+        !mul_ok(bh * nfull, D * D, kMaxElems / 16, &nck) ||
+        !mul_ok(units, (int64_t)kda::bwd_prep_floats(D), kMaxElems / 16, &nprep) ||
+        !mul_ok(units, (int64_t)kda::bwd_part_floats(D), kMaxElems / 16, &npart))
+        return false;
+    lay->o = 0;
+    lay->S_T = round256(nin * esz);
+    lay->ckpt = lay->S_T + round256(nst * 4);
+    lay->prep = lay->ckpt + round256(nck * 4);
+    lay->part = lay->prep + round256(nprep * 4);
+    lay->dA = lay->part + round256(npart * 4);
+    lay->total = lay->dA + round256(units * 4);
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_prefill_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                                      int64_t dv) {
+    if ((dtype != KDA_F32 && dtype != KDA_BF16) || dk != dv || (dk != 16 && dk != 128) ||
+        B < 0 || T < 0 || H < 0)
+        return 0;
+    BwdLayout lay;
+    return bwd_layout(dtype, B, T, H, dk, &lay) ? lay.total : 0;
+}
+
+kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                           const void *q, const void *k, const void *v, const void *z,
+                           const void *beta, const float *A, const float *S0, const void *dO,
+                           const float *dS_T, float *dq, float *dk_out, float *dv_out,
+                           float *dz, float *dbeta, float *dA, float *dS0, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (dk != dv || (dk != 16 && dk != 128)) return KDA_ERR_UNSUPPORTED;
+    const int64_t D = dk, esz = dtype == KDA_BF16 ? 2 : 4;
+    BwdLayout lay;
+    if (!bwd_layout(dtype, B, T, H, D, &lay)) return KDA_ERR_SHAPE;
+    const int64_t bh = B * H, nchunk = (T + kBwdChunk - 1) / kBwdChunk;
+    if (bh > 0x7fffffff / 8 || bh * nchunk > 0x7fffffff) return KDA_ERR_SHAPE;   // grid size
+    const int64_t bth = B * T * H, nin = bth * D, nst = bh * D * D;
+    if (!A || !dA) return KDA_ERR_NULL;
+    if (bh > 0 && (!dS0)) return KDA_ERR_NULL;
+    if (bth > 0 && (!q || !k || !v || !z || !beta || !dO || !dq || !dk_out || !dv_out || !dz ||
+                    !dbeta))
+        return KDA_ERR_NULL;
+    if (bh > 0 && (!workspace || workspace_bytes < lay.total)) return KDA_ERR_WORKSPACE;
+    const void *ptrs[] = {q, k, v, z, beta, A, S0, dO, dS_T, dq, dk_out, dv_out, dz, dbeta,
+                          dA, dS0, bh > 0 ? workspace : nullptr};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const Range ins[] = {range_of(q, nin * esz), range_of(k, nin * esz), range_of(v, nin * esz),
+                         range_of(z, nin * esz), range_of(beta, bth * esz), range_of(A, H * 4),
+                         range_of(S0, nst * 4), range_of(dO, nin * esz),
+                         range_of(dS_T, nst * 4)};
+    const Range outs[] = {range_of(dq, nin * 4), range_of(dk_out, nin * 4),
+                          range_of(dv_out, nin * 4), range_of(dz, nin * 4),
+                          range_of(dbeta, bth * 4), range_of(dA, H * 4), range_of(dS0, nst * 4),
+                          range_of(bh > 0 ? workspace : nullptr, (int64_t)lay.total)};
+    const int nout = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < nout; ++i) {
+        for (const Range &r : ins)
+            if (overlaps(outs[i], r)) return KDA_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlaps(outs[i], outs[j])) return KDA_ERR_ALIAS;
+    }
+    if (H == 0) return KDA_OK;   // every output is empty
+    char *ws = static_cast<char *>(workspace);
+    const hipStream_t s = (hipStream_t)stream;
+    const int64_t nfull = T / kBwdChunk;
+    float *ckpt = bh > 0 ? reinterpret_cast<float *>(ws + lay.ckpt) : nullptr;
+    // forward with a checkpoint at every chunk boundary
+    if (bth > 0) {
+        kda_status st = prefill_impl(dtype, B, T, H, dk, dv, kBwdChunk, nullptr, q, k, v, z, beta,
+                                     A, S0, ws + lay.o, reinterpret_cast<float *>(ws + lay.S_T),
+                                     nfull > 0 ? kBwdChunk : 0, ckpt, B * nfull, nullptr, 0,
+                                     stream, 0);
+        if (st != KDA_OK) return st;
+    }
+    kda::BwdArgs a;
+    a.dtype = dtype; a.B = B; a.T = T; a.H = H; a.D = D; a.nchunk = nchunk;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.dO = dO;
+    a.A = A; a.S0 = S0; a.dST = dS_T; a.ckpt = ckpt;
+    a.prep = bh > 0 ? reinterpret_cast<float *>(ws + lay.prep) : nullptr;
+    a.part = bh > 0 ? reinterpret_cast<float *>(ws + lay.part) : nullptr;
+    a.dA_part = bh > 0 ? reinterpret_cast<float *>(ws + lay.dA) : nullptr;
+    a.dq = dq; a.dk = dk_out; a.dv = dv_out; a.dz = dz; a.dbeta = dbeta; a.dA = dA; a.dS0 = dS0;
+    a.stream = s;
+    return kda::launch_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

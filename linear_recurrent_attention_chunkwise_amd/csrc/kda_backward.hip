@@ -1,0 +1,513 @@
+// kda_backward.hip -- chunk-parallel reverse mode of the KDA prefill (gfx950).
+//
+// The training form the K3 coverage page lists as the next KDA primitive
+// (nishifamily.com K3 page, innovation table, row "Kimi Delta Attention
+// (linear)"): gradients of a loss through the recurrence of "Kimi K3 Open
+// Weights: What Is Actually New", section 1, computed chunk by chunk.  Per
+// 16-token chunk with entering state S, in-chunk cumulative log-decay G
+// (chunk-start reference), Q^ = Q e^G, K^ = K e^G, Ki = K e^-G,
+// Kb = K e^{G_n - G}, A = strict_tril(K^ Ki^T), P = tril(Q^ Ki^T),
+// T = (I + diag(beta) A)^-1, W = T diag(beta) K^, U = T diag(beta) V - W S:
+//
+//   dU = P^T dO + Kb dS'                  dS = Q^^T dO + e^{G_n} dS' - W^T dU
+//   dP = tril(dO U^T)                     dW = -dU S^T
+//   dT = dW (beta K^)^T + dU (beta V)^T   dL = -T^T dT T^T  (strictly lower)
+//
+// and the decayed products pass the rest to q, k, beta and G; the reverse
+// cumulative sum of dG is dg, and the gate gives dz and dA.  Every decayed
+// product factors as (X e^G)(Y e^-G)^T: over 16 tokens e^-G <= e^80 stays in
+// fp32 range, so all of them are plain 16 x 16 x d products.  Arithmetic is
+// fp32 throughout.
+//
+// Kernels (all fp32, LDS-staged, plain FMA loops):
+//   prep  -- one workgroup per (sequence, head, chunk): the chunk's W, Q^,
+//            Kb, P, T and e^{G_n} (S-independent), into the workspace.
+//   chain -- one workgroup per (sequence, head, value-column slice): walks the
+//            chunks backwards carrying dS, with each chunk's entering state
+//            from the forward pass's state checkpoints; writes dV and the
+//            slice's partial sums of the quantities that contract over value
+//            columns (dQ^, dKb, dW, dP, the V part of dT and dbeta, and
+//            sum_j dS' S); the final dS is dS0.
+//   grad  -- one workgroup per (sequence, head, chunk): adds the slices'
+//            partials in slice order and forms dq, dk, dbeta, dz and the
+//            chunk's share of dA.
+//   dA    -- sums the shares of each head in (sequence, chunk) order.
+// No atomics: results are bitwise reproducible.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int C = 16;   // chunk length of the backward
+
+__device__ __forceinline__ float sigmoidf_(float x) {
+    return 1.0f / (1.0f + __expf(-x));
+}
+
+// Per-chunk prep record in the workspace (floats):
+//   W [C][D], Qh [C][D], Kb [C][D], P [C][C], T [C][C], Gn [D] (= e^{G_n})
+template <int D> struct PrepLayout {
+    static constexpr int W = 0, QH = C * D, KB = 2 * C * D, P = 3 * C * D, T = 3 * C * D + C * C,
+                         GN = 3 * C * D + 2 * C * C, SIZE = 3 * C * D + 2 * C * C + D;
+};
+
+// Per-(chunk, slice) partial record (floats):
+//   dQh [C][D], dKb [C][D], dW [C][D], dP [C][C], dTV [C][C], dbV [C], dGn [D]
+template <int D> struct PartLayout {
+    static constexpr int DQH = 0, DKB = C * D, DW = 2 * C * D, DP = 3 * C * D,
+                         DTV = 3 * C * D + C * C, DBV = 3 * C * D + 2 * C * C,
+                         DGN = 3 * C * D + 2 * C * C + C, SIZE = 3 * C * D + 2 * C * C + C + D;
+};
+
+// The S-independent quantities of one chunk, in LDS.  Rows r >= n are absent
+// tokens: zero inputs, beta 0 and g 0 (alpha 1), so they contribute nothing.
+template <typename TI, int D> struct ChunkOps {
+    float q[C][D], k[C][D], G[C][D];
+    float A[C][C], P[C][C], T[C][C];
+    float beta[C];
+};
+
+template <typename TI, int D>
+__device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64_t h, int64_t c,
+                          int n) {
+    const TI *q = static_cast<const TI *>(p.q), *k = static_cast<const TI *>(p.k),
+             *z = static_cast<const TI *>(p.z), *beta = static_cast<const TI *>(p.beta);
+    const int64_t H = p.H;
+    const int64_t row0 = (b * p.T + c * C) * H + h;   // token row of the chunk's first token
+    const float cA = __expf(p.A[h]);
+    for (int i = threadIdx.x; i < C * D; i += blockDim.x) {
+        const int r = i / D, d = i % D;
+        float qv = 0.f, kv = 0.f, g = 0.f;
+        if (r < n) {
+            const int64_t off = (row0 + (int64_t)r * H) * D + d;
+            qv = to_f32(q[off]);
+            kv = to_f32(k[off]);
+            g = kGMin * sigmoidf_(cA * to_f32(z[off]));
+        }
+        s.q[r][d] = qv;
+        s.k[r][d] = kv;
+        s.G[r][d] = g;
+    }
+    for (int r = threadIdx.x; r < C; r += blockDim.x)
+        s.beta[r] = r < n ? to_f32(beta[row0 + (int64_t)r * H]) : 0.f;
+    __syncthreads();
+    // cumulative log-decay over the chunk
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r) {
+            acc += s.G[r][d];
+            s.G[r][d] = acc;
+        }
+    }
+    __syncthreads();
+    // A[r][s] = sum_d k_r k_s e^{G_r - G_s} (s < r),  P[r][s] = sum_d q_r k_s e^{G_r - G_s} (s <= r)
+    for (int i = threadIdx.x; i < C * C; i += blockDim.x) {
+        const int r = i / C, sc = i % C;
+        float a = 0.f, pp = 0.f;
+        if (sc <= r) {
+            for (int d = 0; d < D; ++d) {
+                const float e = __expf(s.G[r][d] - s.G[sc][d]);
+                a += s.k[r][d] * s.k[sc][d] * e;
+                pp += s.q[r][d] * s.k[sc][d] * e;
+            }
+        }
+        s.A[r][sc] = sc < r ? a : 0.f;
+        s.P[r][sc] = pp;
+    }
+    __syncthreads();
+    // T = (I + diag(beta) A)^-1 by forward substitution, one column per thread
+    for (int col = threadIdx.x; col < C; col += blockDim.x) {
+        for (int r = 0; r < C; ++r) {
+            float acc = r == col ? 1.f : 0.f;
+            for (int u = 0; u < r; ++u) acc -= s.beta[r] * s.A[r][u] * s.T[u][col];
+            s.T[r][col] = acc;
+        }
+    }
+    __syncthreads();
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ prep ----
+
+template <typename TI, int D>
+__global__ __launch_bounds__(256) void kda_bwd_prep_kernel(BwdArgs p) {
+    __shared__ ChunkOps<TI, D> s;
+    using Lay = PrepLayout<D>;
+    const int64_t x = blockIdx.x;
+    const int64_t c = x % p.nchunk, bh = x / p.nchunk;
+    const int64_t b = bh / p.H, h = bh % p.H;
+    const int n = (int)(p.T - c * C < C ? p.T - c * C : C);
+    chunk_ops<TI, D>(s, p, b, h, c, n);
+    float *rec = p.prep + x * (int64_t)Lay::SIZE;
+    for (int i = threadIdx.x; i < C * D; i += blockDim.x) {
+        const int r = i / D, d = i % D;
+        const float G = s.G[r][d], Gn = s.G[C - 1][d];
+        float w = 0.f;
+        for (int sc = 0; sc < C; ++sc) w += s.T[r][sc] * s.beta[sc] * s.k[sc][d] * __expf(s.G[sc][d]);
+        rec[Lay::W + i] = w;
+        rec[Lay::QH + i] = s.q[r][d] * __expf(G);
+        rec[Lay::KB + i] = s.k[r][d] * __expf(Gn - G);
+    }
+    for (int i = threadIdx.x; i < C * C; i += blockDim.x) {
+        rec[Lay::P + i] = (&s.P[0][0])[i];
+        rec[Lay::T + i] = (&s.T[0][0])[i];
+    }
+    for (int d = threadIdx.x; d < D; d += blockDim.x) rec[Lay::GN + d] = __expf(s.G[C - 1][d]);
+}
+
+// ----------------------------------------------------------------- chain ----
+
+template <int D, int NC> struct ChainLds {
+    float S[D][NC], dS[D][NC];
+    float W[C][D], Qh[C][D], Kb[C][D];
+    float P[C][C], T[C][C];
+    float Gn[D];
+    float dO[C][NC], V[C][NC], U[C][NC], dU[C][NC], BV[C][NC];
+    float beta[C];
+};
+
+template <typename TI, int D, int NC, int NT>
+__global__ __launch_bounds__(NT) void kda_bwd_chain_kernel(BwdArgs p) {
+    __shared__ ChainLds<D, NC> s;
+    using Lay = PrepLayout<D>;
+    using PL = PartLayout<D>;
+    const TI *v = static_cast<const TI *>(p.v), *beta = static_cast<const TI *>(p.beta),
+             *dO = static_cast<const TI *>(p.dO);
+    constexpr int NS = D / NC;   // column slices per head
+    const int64_t x = blockIdx.x;
+    const int sl = (int)(x % NS);
+    const int64_t bh = x / NS;
+    const int64_t b = bh / p.H, h = bh % p.H, H = p.H;
+    const int j0 = sl * NC;
+    const int tid = threadIdx.x;
+    const int64_t nfull = p.T / C;   // checkpoints per sequence
+
+    // dS' of the last chunk: dL/dS_T (or 0)
+    for (int i = tid; i < D * NC; i += NT) {
+        const int d = i / NC, j = i % NC;
+        s.dS[d][j] = p.dST ? p.dST[(bh * D + d) * D + j0 + j] : 0.f;
+    }
+    for (int64_t c = p.nchunk - 1; c >= 0; --c) {
+        const int n = (int)(p.T - c * C < C ? p.T - c * C : C);
+        const int64_t row0 = (b * p.T + c * C) * H + h;
+        const float *Sin = c == 0 ? (p.S0 ? p.S0 + bh * (int64_t)(D * D) : nullptr)
+                                  : p.ckpt + ((b * nfull + c - 1) * H + h) * (int64_t)(D * D);
+        const float *rec = p.prep + (bh * p.nchunk + c) * (int64_t)Lay::SIZE;
+        for (int i = tid; i < D * NC; i += NT) {
+            const int d = i / NC, j = i % NC;
+            s.S[d][j] = Sin ? Sin[(int64_t)d * D + j0 + j] : 0.f;
+        }
+        for (int i = tid; i < C * D; i += NT) {
+            const int r = i / D, d = i % D;
+            s.W[r][d] = rec[Lay::W + i];
+            s.Qh[r][d] = rec[Lay::QH + i];
+            s.Kb[r][d] = rec[Lay::KB + i];
+        }
+        for (int i = tid; i < C * C; i += NT) {
+            (&s.P[0][0])[i] = rec[Lay::P + i];
+            (&s.T[0][0])[i] = rec[Lay::T + i];
+        }
+        for (int d = tid; d < D; d += NT) s.Gn[d] = rec[Lay::GN + d];
+        for (int i = tid; i < C * NC; i += NT) {
+            const int r = i / NC, j = i % NC;
+            float ov = 0.f, vv = 0.f;
+            if (r < n) {
+                const int64_t off = (row0 + (int64_t)r * H) * D + j0 + j;
+                ov = to_f32(dO[off]);
+                vv = to_f32(v[off]);
+            }
+            s.dO[r][j] = ov;
+            s.V[r][j] = vv;
+        }
+        for (int r = tid; r < C; r += NT) s.beta[r] = r < n ? to_f32(beta[row0 + (int64_t)r * H]) : 0.f;
+        __syncthreads();
+
+        // U = T diag(beta) V - W S;  dU = P^T dO + Kb dS'
+        for (int i = tid; i < C * NC; i += NT) {
+            const int r = i / NC, j = i % NC;
+            float u = 0.f, du = 0.f;
+            for (int sc = 0; sc < C; ++sc) {
+                u += s.T[r][sc] * s.beta[sc] * s.V[sc][j];
+                du += s.P[sc][r] * s.dO[sc][j];
+            }
+            for (int d = 0; d < D; ++d) {
+                u -= s.W[r][d] * s.S[d][j];
+                du += s.Kb[r][d] * s.dS[d][j];
+            }
+            s.U[r][j] = u;
+            s.dU[r][j] = du;
+        }
+        __syncthreads();
+
+        // partial sums over this slice's value columns, and dV
+        float *part = p.part + ((bh * p.nchunk + c) * NS + sl) * (int64_t)PL::SIZE;
+        for (int i = tid; i < C * D; i += NT) {
+            const int r = i / D, d = i % D;
+            float a = 0.f, bb = 0.f, w = 0.f;
+            for (int j = 0; j < NC; ++j) {
+                a += s.dO[r][j] * s.S[d][j];
+                bb += s.U[r][j] * s.dS[d][j];
+                w -= s.dU[r][j] * s.S[d][j];
+            }
+            part[PL::DQH + i] = a;
+            part[PL::DKB + i] = bb;
+            part[PL::DW + i] = w;
+        }
+        for (int i = tid; i < C * C; i += NT) {
+            const int r = i / C, sc = i % C;
+            float dp = 0.f, dtv = 0.f;
+            for (int j = 0; j < NC; ++j) {
+                dp += s.dO[r][j] * s.U[sc][j];
+                dtv += s.dU[r][j] * s.beta[sc] * s.V[sc][j];
+            }
+            part[PL::DP + i] = dp;
+            part[PL::DTV + i] = dtv;
+        }
+        for (int d = tid; d < D; d += NT) {
+            float a = 0.f;
+            for (int j = 0; j < NC; ++j) a += s.dS[d][j] * s.S[d][j];
+            part[PL::DGN + d] = a;
+        }
+        // dBV = T^T dU;  dV = beta dBV
+        for (int i = tid; i < C * NC; i += NT) {
+            const int r = i / NC, j = i % NC;
+            float a = 0.f;
+            for (int sc = 0; sc < C; ++sc) a += s.T[sc][r] * s.dU[sc][j];
+            s.BV[r][j] = a;
+            if (r < n) p.dv[(row0 + (int64_t)r * H) * D + j0 + j] = s.beta[r] * a;
+        }
+        __syncthreads();
+        for (int r = tid; r < C; r += NT) {
+            float a = 0.f;
+            for (int j = 0; j < NC; ++j) a += s.BV[r][j] * s.V[r][j];
+            part[PL::DBV + r] = a;
+        }
+        // dS <- Q^^T dO + e^{G_n} dS' - W^T dU   (each thread its own entries)
+        for (int i = tid; i < D * NC; i += NT) {
+            const int d = i / NC, j = i % NC;
+            float a = s.Gn[d] * s.dS[d][j];
+            for (int r = 0; r < C; ++r) a += s.Qh[r][d] * s.dO[r][j] - s.W[r][d] * s.dU[r][j];
+            s.dS[d][j] = a;
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < D * NC; i += NT) {
+        const int d = i / NC, j = i % NC;
+        p.dS0[(bh * D + d) * D + j0 + j] = s.dS[d][j];
+    }
+}
+
+// ------------------------------------------------------------------ grad ----
+
+template <typename TI, int D> struct GradLds {
+    ChunkOps<TI, D> o;
+    float dQh[C][D], dKb[C][D], dW[C][D], dG[C][D];
+    float dP[C][C], dTV[C][C], dT[C][C], M1[C][C], dL[C][C];
+    float dbV[C], dGn[D];
+};
+
+template <typename TI, int D>
+__global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
+    __shared__ GradLds<TI, D> s;
+    using PL = PartLayout<D>;
+    constexpr int NS = D == 128 ? 2 : 1;
+    const int64_t x = blockIdx.x;
+    const int64_t c = x % p.nchunk, bh = x / p.nchunk;
+    const int64_t b = bh / p.H, h = bh % p.H, H = p.H;
+    const int n = (int)(p.T - c * C < C ? p.T - c * C : C);
+    const int tid = threadIdx.x;
+    chunk_ops<TI, D>(s.o, p, b, h, c, n);
+    // the slices' partial sums, added in slice order
+    const float *part = p.part + x * NS * (int64_t)PL::SIZE;
+    for (int i = tid; i < C * D; i += blockDim.x) {
+        float a = 0.f, bb = 0.f, w = 0.f;
+        for (int q = 0; q < NS; ++q) {
+            a += part[q * PL::SIZE + PL::DQH + i];
+            bb += part[q * PL::SIZE + PL::DKB + i];
+            w += part[q * PL::SIZE + PL::DW + i];
+        }
+        (&s.dQh[0][0])[i] = a;
+        (&s.dKb[0][0])[i] = bb;
+        (&s.dW[0][0])[i] = w;
+    }
+    for (int i = tid; i < C * C; i += blockDim.x) {
+        float a = 0.f, bb = 0.f;
+        for (int q = 0; q < NS; ++q) {
+            a += part[q * PL::SIZE + PL::DP + i];
+            bb += part[q * PL::SIZE + PL::DTV + i];
+        }
+        const int r = i / C, sc = i % C;
+        (&s.dP[0][0])[i] = sc <= r ? a : 0.f;   // P is lower triangular
+        (&s.dTV[0][0])[i] = bb;
+    }
+    for (int r = tid; r < C; r += blockDim.x) {
+        float a = 0.f;
+        for (int q = 0; q < NS; ++q) a += part[q * PL::SIZE + PL::DBV + r];
+        s.dbV[r] = a;
+    }
+    for (int d = tid; d < D; d += blockDim.x) {
+        float a = 0.f;
+        for (int q = 0; q < NS; ++q) a += part[q * PL::SIZE + PL::DGN + d];
+        s.dGn[d] = a * __expf(s.o.G[C - 1][d]);   // d/dG_n of e^{G_n} * (sum_j dS' S)
+    }
+    __syncthreads();
+    auto &o = s.o;
+    // dT = dW (beta K^)^T + dU (beta V)^T
+    for (int i = tid; i < C * C; i += blockDim.x) {
+        const int r = i / C, sc = i % C;
+        float a = s.dTV[r][sc];
+        for (int d = 0; d < D; ++d) a += s.dW[r][d] * o.beta[sc] * o.k[sc][d] * __expf(o.G[sc][d]);
+        s.dT[r][sc] = a;
+    }
+    __syncthreads();
+    // M1 = T^T dT;  dL = -M1 T^T (strictly lower)
+    for (int i = tid; i < C * C; i += blockDim.x) {
+        const int r = i / C, sc = i % C;
+        float a = 0.f;
+        for (int u = 0; u < C; ++u) a += o.T[u][r] * s.dT[u][sc];
+        s.M1[r][sc] = a;
+    }
+    __syncthreads();
+    for (int i = tid; i < C * C; i += blockDim.x) {
+        const int r = i / C, sc = i % C;
+        float a = 0.f;
+        for (int u = 0; u < C; ++u) a += s.M1[r][u] * o.T[sc][u];
+        s.dL[r][sc] = sc < r ? -a : 0.f;
+    }
+    __syncthreads();
+    // dbeta: V part, K^ part (through W), L part;  dA = beta dL (kept in dL)
+    for (int r = tid; r < C; r += blockDim.x) {
+        float a = s.dbV[r];
+        for (int d = 0; d < D; ++d) {
+            float dbk = 0.f;   // (T^T dW)[r][d]
+            for (int u = 0; u < C; ++u) dbk += o.T[u][r] * s.dW[u][d];
+            a += dbk * o.k[r][d] * __expf(o.G[r][d]);
+        }
+        for (int sc = 0; sc < C; ++sc) a += s.dL[r][sc] * o.A[r][sc];
+        if (r < n) p.dbeta[(b * p.T + c * C + r) * H + h] = a;
+    }
+    __syncthreads();
+    for (int i = tid; i < C * C; i += blockDim.x) {
+        const int r = i / C;
+        (&s.dL[0][0])[i] *= o.beta[r];   // now dA
+    }
+    __syncthreads();
+    // dq, dk and dG per (r, d)
+    float dA_acc = 0.f;
+    for (int i = tid; i < C * D; i += blockDim.x) {
+        const int r = i / D, d = i % D;
+        const float G = o.G[r][d], Gm = __expf(G), Gi = __expf(-G);
+        const float Gn = o.G[C - 1][d];
+        const float qv = o.q[r][d], kv = o.k[r][d];
+        float dqh = s.dQh[r][d];     // total dQ^
+        float dkh = 0.f;             // total dK^ (from A and W)
+        float dki = 0.f;             // total dKi (from A and P)
+        for (int sc = 0; sc < C; ++sc) {
+            const float ki_s = o.k[sc][d] * __expf(-o.G[sc][d]);
+            const float kh_s = o.k[sc][d] * __expf(o.G[sc][d]);
+            const float qh_s = o.q[sc][d] * __expf(o.G[sc][d]);
+            dqh += s.dP[r][sc] * ki_s;
+            dkh += s.dL[r][sc] * ki_s;
+            dki += s.dL[sc][r] * kh_s + s.dP[sc][r] * qh_s;
+        }
+        float dbk = 0.f;
+        for (int u = 0; u < C; ++u) dbk += o.T[u][r] * s.dW[u][d];
+        dkh += o.beta[r] * dbk;                      // through W = T diag(beta) K^
+        const float kb = kv * __expf(Gn - G);
+        const float dq = dqh * Gm;
+        const float dk = dkh * Gm + dki * Gi + s.dKb[r][d] * __expf(Gn - G);
+        const float dG = dqh * qv * Gm + dkh * kv * Gm - dki * kv * Gi - s.dKb[r][d] * kb;
+        if (r < n) {
+            const int64_t off = ((b * p.T + c * C + r) * H + h) * D + d;
+            p.dq[off] = dq;
+            p.dk[off] = dk;
+        }
+        s.dG[r][d] = dG;
+    }
+    __syncthreads();
+    // dG_n from Kb = K e^{G_n - G} and from e^{G_n} (sum_j dS' S); G_n = G of the last row
+    for (int d = tid; d < D; d += blockDim.x) {
+        float a = s.dGn[d];
+        const float Gn = o.G[C - 1][d];
+        for (int r = 0; r < C; ++r) a += s.dKb[r][d] * o.k[r][d] * __expf(Gn - o.G[r][d]);
+        s.dG[C - 1][d] += a;
+    }
+    __syncthreads();
+    // dg = reverse cumulative sum of dG; gate: g = g_min sigma(c z)
+    const float cA = __expf(p.A[h]);
+    const TI *z = static_cast<const TI *>(p.z);
+    for (int d = tid; d < D; d += blockDim.x) {
+        float acc = 0.f;
+        for (int r = C - 1; r >= 0; --r) {
+            acc += s.dG[r][d];
+            if (r < n) {
+                const int64_t off = ((b * p.T + c * C + r) * H + h) * D + d;
+                const float xz = cA * to_f32(z[off]);
+                const float sg = sigmoidf_(xz);
+                const float dx = acc * kGMin * sg * (1.0f - sg);
+                p.dz[off] = cA * dx;
+                dA_acc += dx * xz;
+            }
+        }
+    }
+    // the chunk's share of dA: block sum in a fixed order
+    __shared__ float red[256];
+    red[tid] = dA_acc;
+    __syncthreads();
+    if (tid == 0) {
+        float a = 0.f;
+        for (int i = 0; i < (int)blockDim.x; ++i) a += red[i];
+        p.dA_part[x] = a;
+    }
+}
+
+// dA[h] = sum over (sequence, chunk) of the shares, in that order.
+__global__ void kda_bwd_dA_kernel(const float *dA_part, float *dA, int64_t B, int64_t H,
+                                  int64_t nchunk) {
+    const int64_t h = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (h >= H) return;
+    float a = 0.f;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < nchunk; ++c) a += dA_part[(b * H + h) * nchunk + c];
+    dA[h] = a;
+}
+
+size_t bwd_prep_floats(int64_t D) {
+    return D == 128 ? PrepLayout<128>::SIZE : PrepLayout<16>::SIZE;
+}
+size_t bwd_part_floats(int64_t D) {
+    return D == 128 ? 2 * PartLayout<128>::SIZE : PartLayout<16>::SIZE;
+}
+
+template <typename TI, int D, int NC, int NT>
+static hipError_t launch_bwd_t(const BwdArgs &a) {
+    const int64_t bh = a.B * a.H, units = bh * a.nchunk;
+    if (units > 0)
+        hipLaunchKernelGGL((kda_bwd_prep_kernel<TI, D>), dim3((unsigned)units), dim3(256), 0,
+                           a.stream, a);
+    // with no tokens the chain only writes dS0 = dS_T
+    if (bh > 0)
+        hipLaunchKernelGGL((kda_bwd_chain_kernel<TI, D, NC, NT>), dim3((unsigned)(bh * (D / NC))),
+                           dim3(NT), 0, a.stream, a);
+    if (units > 0)
+        hipLaunchKernelGGL((kda_bwd_grad_kernel<TI, D>), dim3((unsigned)units), dim3(256), 0,
+                           a.stream, a);
+    if (a.H > 0)
+        hipLaunchKernelGGL(kda_bwd_dA_kernel, dim3((unsigned)((a.H + 255) / 256)), dim3(256), 0,
+                           a.stream, a.dA_part, a.dA, a.B, a.H, a.nchunk);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs &a) {
+    if (a.dtype == 1) {
+        if (a.D == 128) return launch_bwd_t<bf16, 128, 64, 512>(a);
+        return launch_bwd_t<bf16, 16, 16, 256>(a);
+    }
+    if (a.D == 128) return launch_bwd_t<float, 128, 64, 512>(a);
+    return launch_bwd_t<float, 16, 16, 256>(a);
+}
+
+}  // namespace kda

@@ -115,4 +115,22 @@ hipError_t launch_split_gather(const float *Sseg, float *S_T, int64_t B, int64_t
 bool decode_supported(int dtype, int64_t D);
 hipError_t launch_decode(const DecodeArgs &a);
 
+// Chunk-parallel backward of the prefill (16-token chunks).  Inputs as in the
+// prefill; dO in the input dtype, dST (dL/dS_T) fp32 or NULL (zero).  ckpt
+// holds the forward's state checkpoints every 16 tokens ([B*(T/16), H, D, D]);
+// prep, part and dA_part are workspace.  Gradients are fp32.
+struct BwdArgs {
+    int dtype;
+    int64_t B, T, H, D;
+    int64_t nchunk;     // ceil(T / 16)
+    const void *q, *k, *v, *z, *beta, *dO;
+    const float *A, *S0, *dST, *ckpt;
+    float *prep, *part, *dA_part;
+    float *dq, *dk, *dv, *dz, *dbeta, *dA, *dS0;
+    hipStream_t stream;
+};
+size_t bwd_prep_floats(int64_t D);   // per (b, h, chunk)
+size_t bwd_part_floats(int64_t D);   // per (b, h, chunk), all column slices
+hipError_t launch_bwd(const BwdArgs &a);
+
 }  // namespace kda

@@ -16,6 +16,11 @@ q, k, v, z, beta are then rounded to the run dtype (round-to-nearest-even for
 bf16); A and S0 stay fp32.  Decode workloads draw every step up front with a
 leading [steps] axis and start from a zero state.
 
+Cotangents for the backward come from a second generator seeded with the
+workload's seed + 1000: dO ~ N(0, 1) [B, T, H, dv] rounded to the run dtype,
+then dL/dS_T ~ N(0, 1) [B, H, dk, dv] (fp32), i.e. the gradient of a loss
+<dO, o> + <dS_T, S_T> with unit-scale random weights.
+
 Layer inputs for the prologue (short convolutions + q/k normalization) follow
 the same recipe without the L2 normalization of q and k (the prologue
 normalizes), then draw, from the same generator: taps wq, wk, wv ~ N(0, 1/W)
@@ -35,7 +40,7 @@ from dataclasses import dataclass, replace
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_prefill_inputs", "make_decode_inputs", "make_varlen_inputs",
-           "make_layer_inputs", "make_layer_decode_inputs", "torch_dtype"]
+           "make_layer_inputs", "make_layer_decode_inputs", "make_cotangents", "torch_dtype"]
 
 
 @dataclass(frozen=True)
@@ -217,3 +222,14 @@ def make_layer_decode_inputs(w: Workload, width: int, device="cpu", steps: int |
     return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), z=z.to(dt),
                 beta=torch.sigmoid(beta_logit).to(dt), A=A, S=S,
                 wq=wq, wk=wk, wv=wv, sq=sq, sk=sk, sv=sv)
+
+
+def make_cotangents(w: Workload, device="cpu", T: int | None = None, with_dST: bool = True):
+    """dO [B, T, H, dv] (run dtype) and dL/dS_T [B, H, dk, dv] (fp32, or None)
+    for a prefill workload, from the seed + 1000 stream."""
+    T = w.T if T is None else int(T)
+    g = _gen(w.seed + 1000, device)
+    f32 = dict(dtype=torch.float32, device=device, generator=g)
+    dO = torch.randn(w.B, T, w.H, w.dv, **f32).to(torch_dtype(w.dtype))
+    dST = torch.randn(w.B, w.H, w.dk, w.dv, **f32) if with_dST else None
+    return dO, dST

@@ -96,6 +96,11 @@ def _load():
     lib.kda_decode_step_conv.restype = ctypes.c_int
     lib.kda_decode_step_conv.argtypes = [ctypes.c_int, i64, i64, i64, i64, cp, vp, vp, vp, vp,
                                          vp, vp, vp, vp, vp, vp]
+    lib.kda_prefill_bwd.restype = ctypes.c_int
+    lib.kda_prefill_bwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64] + [vp] * 17 + [
+        sz, vp]
+    lib.kda_prefill_bwd_workspace_size.restype = sz
+    lib.kda_prefill_bwd_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64]
     _lib = lib
     return lib
 
@@ -518,3 +523,57 @@ def decode_step_conv(q, k, v, z, beta, A, wq, wk, wv, state, S, act: str = "none
                                   _ptr(S), _ptr(out), _stream_handle(dev))
     _check(st, "kda_decode_step_conv")
     return out
+
+
+def prefill_bwd_workspace_size(dtype: torch.dtype, B: int, T: int, H: int, dk: int,
+                               dv: int) -> int:
+    return int(_load().kda_prefill_bwd_workspace_size(_DTYPES[dtype], B, T, H, dk, dv))
+
+
+def prefill_bwd(q, k, v, z, beta, A, S0, dO, dS_T=None, workspace=None):
+    """Gradients of a loss through the prefill (kda_prefill_bwd).
+
+    Inputs as ``prefill`` (S0 may be None), dO [B,T,H,dv] in the input dtype
+    (dL/do) and dS_T [B,H,dk,dv] fp32 or None (dL/dS_T).  Returns a dict of
+    fp32 tensors: dq, dk, dz [B,T,H,dk]; dv [B,T,H,dv]; dbeta [B,T,H];
+    dA [H]; dS0 [B,H,dk,dv].  ``workspace`` may be a preallocated uint8 cuda
+    tensor of ``prefill_bwd_workspace_size`` bytes."""
+    lib = _load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("KDA backward runs on the GPU; inputs must be cuda tensors")
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    _require(q, "q", (B, T, H, dk), dt, dev)
+    _require(k, "k", (B, T, H, dk), dt, dev)
+    _require(z, "z", (B, T, H, dk), dt, dev)
+    _require(v, "v", (B, T, H, dv), dt, dev)
+    _require(beta, "beta", (B, T, H), dt, dev)
+    _require(A, "A", (H,), torch.float32, dev)
+    _require(dO, "dO", (B, T, H, dv), dt, dev)
+    if S0 is not None:
+        _require(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if dS_T is not None:
+        _require(dS_T, "dS_T", (B, H, dk, dv), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
+         "dv": torch.empty((B, T, H, dv), **f32), "dz": torch.empty((B, T, H, dk), **f32),
+         "dbeta": torch.empty((B, T, H), **f32), "dA": torch.empty((H,), **f32),
+         "dS0": torch.empty((B, H, dk, dv), **f32)}
+    ws_bytes = prefill_bwd_workspace_size(dt, B, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    elif workspace.numel() < ws_bytes or workspace.device != dev:
+        raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
+    st = lib.kda_prefill_bwd(_DTYPES[dt], B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(z),
+                             _ptr(beta), _ptr(A), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(g["dq"]),
+                             _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dz"]), _ptr(g["dbeta"]),
+                             _ptr(g["dA"]), _ptr(g["dS0"]), _ptr(workspace),
+                             workspace.numel() if workspace is not None else 0,
+                             _stream_handle(dev))
+    _check(st, "kda_prefill_bwd")
+    return g

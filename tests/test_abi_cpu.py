@@ -36,7 +36,8 @@ def test_header_declares_expected_api():
         "kda_prefill", "kda_prefill_ex", "kda_prefill_varlen",
         "kda_prefill_varlen_workspace_size", "kda_decode_step", "kda_conv_norm",
         "kda_prefill_conv_workspace_size", "kda_prefill_conv", "kda_decode_step_conv",
-        "kda_prefill_split", "kda_prefill_split_workspace_size", "kda_conv_norm_varlen"])
+        "kda_prefill_split", "kda_prefill_split_workspace_size", "kda_conv_norm_varlen",
+        "kda_prefill_bwd", "kda_prefill_bwd_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 6
+    assert lib.kda_abi_version() == 7
     for s in range(8):
         assert lib.kda_status_str(s).decode().startswith("KDA_")
     assert lib.kda_status_str(99) == b"unknown kda_status"
@@ -357,3 +358,47 @@ def test_conv_norm_varlen_argument_errors(lib):
     assert conv_varlen(lib, ptrs={"vo": P(2, 32)}) == ALIAS       # output over v
     assert conv_varlen(lib, sin=states(50, 51, 52), sout=states(53, 52, 55)) == ALIAS
     assert conv_varlen(lib, N=0, ptrs={"cu": None}) == OK
+
+
+# ------------------------------------------------------------- backward ----
+
+BWD_NAMES = ["q", "k", "v", "z", "beta", "A", "S0", "dO", "dST", "dq", "dk", "dv", "dz",
+             "dbeta", "dA", "dS0", "ws"]
+
+
+def bwd(lib, dtype=BF16, B=1, T=40, H=2, dk=128, dv=128, ptrs=None, ws_bytes=None):
+    p = {n: P(i) for i, n in enumerate(BWD_NAMES)}
+    if ptrs:
+        p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.kda_prefill_bwd_workspace_size(dtype, B, T, H, dk, dv)
+    return lib.kda_prefill_bwd(dtype, B, T, H, dk, dv, *(p[n] for n in BWD_NAMES[:-1]),
+                               p["ws"], ws_bytes, None)
+
+
+def test_backward_argument_errors(lib):
+    assert bwd(lib, T=-1) == SHAPE
+    assert bwd(lib, dtype=7) == UNSUP
+    assert bwd(lib, dk=64, dv=64) == UNSUP
+    assert bwd(lib, dk=128, dv=16) == UNSUP
+    for name in ("q", "beta", "dO", "dq", "dbeta", "dA", "dS0", "A"):
+        assert bwd(lib, ptrs={name: None}) == NULL, name
+    assert bwd(lib, ptrs={"ws": None}) == WORKSPACE
+    assert bwd(lib, ws_bytes=256) == WORKSPACE
+    assert bwd(lib, ptrs={"dz": P(12, 4)}) == MISALIGNED
+    assert bwd(lib, ptrs={"dq": P(1, 64)}) == ALIAS        # a gradient over k
+    assert bwd(lib, ptrs={"dk": P(9, 16)}) == ALIAS        # two gradients overlap
+    assert bwd(lib, ptrs={"ws": P(0, 0)}) == ALIAS         # workspace over q
+    assert bwd(lib, ptrs={"dS0": P(6, 0)}) == ALIAS        # dS0 over S0
+    assert bwd(lib, H=0) == OK                              # nothing to do
+    # S0 and dS_T are optional
+    assert lib.kda_prefill_bwd_workspace_size(F32, 1, 40, 2, 16, 16) > 0
+    assert lib.kda_prefill_bwd_workspace_size(BF16, 1, 40, 2, 64, 64) == 0
+
+
+def test_backward_workspace_holds_forward_and_checkpoints(lib):
+    B, T, H, d = 2, 100, 3, 128
+    n = lib.kda_prefill_bwd_workspace_size(BF16, B, T, H, d, d)
+    o = B * T * H * d * 2
+    ckpt = B * (T // 16) * H * d * d * 4
+    assert n >= o + ckpt + B * H * d * d * 4

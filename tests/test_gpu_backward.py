@@ -1,0 +1,155 @@
+"""GPU parity of the chunk-parallel backward (kda_prefill_bwd) against the
+fp64 adjoint oracle (oracle.prefill_bwd, pinned by finite differences in
+test_oracle_backward.py), on the same seeded inputs and cotangents.
+
+Every gradient is compared normwise per (b, h) slice: max|x - ref| / max|ref|
+at most 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (the forward's
+tolerances; the backward reruns that forward for its chunk-entry states and
+does the rest in fp32).  Cases span one chunk, chunk multiples, ragged tails,
+both head sizes and dtypes, long memory (decays near 1), S0 / dS_T absent,
+T = 0 and B = 0, run-to-run bit equality, and sampled heads of the K3 prefill
+workload at full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrent_attention_chunkwise_amd.inputs import (WORKLOADS, make_cotangents,
+                                                             make_prefill_inputs)
+from tests.gpu_helpers import TOL, host, slice_relerr, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GRAD_HEAD_AXIS = {"dq": 2, "dk": 2, "dv": 2, "dz": 2, "dbeta": 2, "dS0": 1}
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import linear_recurrent_attention_chunkwise_amd as m
+    assert m.abi_version() == 7
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _oracle_bwd(inp, dO, dST, heads=None):
+    def sel(t, axis):
+        if t is None:
+            return None
+        if heads is not None:
+            t = torch.index_select(t, axis, torch.as_tensor(heads, device=t.device))
+        return host(t)
+    A = host(inp["A"]) if heads is None else host(inp["A"])[heads]
+    return oracle.prefill_bwd(sel(inp["q"], 2), sel(inp["k"], 2), sel(inp["v"], 2),
+                              sel(inp["z"], 2), sel(inp["beta"], 2), A, sel(inp["S0"], 1),
+                              sel(dO, 2), sel(dST, 1))
+
+
+def _gpu_bwd(kda, g, dO, dST):
+    out = kda.prefill_bwd(g["q"], g["k"], g["v"], g["z"], g["beta"], g["A"], g["S0"], dO, dST)
+    torch.cuda.synchronize()
+    return out
+
+
+def _errors(got, ref):
+    errs = {}
+    for key, ax in GRAD_HEAD_AXIS.items():
+        errs[key] = slice_relerr(host(got[key]), ref[key], ax)
+    a, r = host(got["dA"]).astype(np.float64), ref["dA"]
+    errs["dA"] = float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-30)) if r.size else 0.0
+    return errs
+
+
+def _check(kda, w, T, gpu_device, with_dST=True):
+    inp = make_prefill_inputs(w, T=T)
+    dO, dST = make_cotangents(w, T=T, with_dST=with_dST)
+    g = to_dev(inp, gpu_device)
+    got = _gpu_bwd(kda, g, dO.to(gpu_device), None if dST is None else dST.to(gpu_device))
+    ref = _oracle_bwd(inp, dO, dST)
+    errs = _errors(got, ref)
+    _say("   " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    tol = TOL[torch.float32 if w.dtype == "f32" else torch.bfloat16]
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, (w.name, w.dtype, w.dk, T, bad)
+
+
+CASES = [
+    ("f32", 16, 2, 2, (1, 15, 16, 17, 50)),
+    ("f32", 128, 1, 2, (16, 40, 100)),
+    ("bf16", 128, 1, 2, (33, 200)),
+    ("bf16", 16, 2, 3, (70,)),
+]
+
+
+@pytest.mark.parametrize("dtype,d,B,H,Ts", CASES)
+def test_backward_matches_oracle(kda, gpu_device, dtype, d, B, H, Ts):
+    w = WORKLOADS["k3_prefill_bf16"].with_(B=B, H=H, dk=d, dv=d, dtype=dtype, s0_std=0.5)
+    for T in Ts:
+        _say(f"[bwd] {dtype} d={d} B={B} H={H} T={T}")
+        _check(kda, w, T, gpu_device)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_long_memory(kda, gpu_device, dtype):
+    """z ~ N(-6, 1): alpha near 1, so dS carries across every chunk."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(B=1, H=2, dtype=dtype, z_mean=-6.0, s0_std=0.5)
+    _say(f"[bwd] long memory {dtype} T=160")
+    _check(kda, w, 160, gpu_device)
+
+
+def test_backward_without_state_inputs(kda, gpu_device):
+    """S0 = None (zero start) and dS_T = None (no loss on the final state)."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(B=2, H=2, dk=16, dv=16, dtype="f32", s0_std=None)
+    _say("[bwd] S0 None, dS_T None")
+    _check(kda, w, 37, gpu_device, with_dST=False)
+
+
+def test_backward_empty(kda, gpu_device):
+    """T = 0: dS0 = dS_T (zero when absent) and dA = 0; B = 0: dA = 0."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(B=2, H=3, s0_std=0.5)
+    g = to_dev(make_prefill_inputs(w, T=0), gpu_device)
+    dO, dST = make_cotangents(w, T=0)
+    got = _gpu_bwd(kda, g, dO.to(gpu_device), dST.to(gpu_device))
+    assert torch.equal(got["dS0"], dST.to(gpu_device))
+    assert torch.equal(got["dA"], torch.zeros_like(got["dA"]))
+    got = _gpu_bwd(kda, g, dO.to(gpu_device), None)
+    assert torch.equal(got["dS0"], torch.zeros_like(got["dS0"]))
+    w0 = w.with_(B=0)
+    g0 = to_dev(make_prefill_inputs(w0, T=5), gpu_device)
+    dO0, _ = make_cotangents(w0, T=5)
+    got = _gpu_bwd(kda, g0, dO0.to(gpu_device), None)
+    assert torch.equal(got["dA"], torch.zeros_like(got["dA"]))
+
+
+def test_backward_is_deterministic(kda, gpu_device):
+    w = WORKLOADS["k3_prefill_bf16"].with_(B=1, H=4, s0_std=0.5)
+    g = to_dev(make_prefill_inputs(w, T=300), gpu_device)
+    dO, dST = (t.to(gpu_device) for t in make_cotangents(w, T=300))
+    a = _gpu_bwd(kda, g, dO, dST)
+    b = _gpu_bwd(kda, g, dO, dST)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_backward_k3_full_size_sampled_heads(kda, gpu_device):
+    """B1 H96 T4096 bf16 (the K3 prefill workload) in one call; heads 0, 47
+    and 95 against the oracle (the oracle runs per head, so a subset of heads
+    is an exact sample of the same computation)."""
+    w = WORKLOADS["k3_prefill_bf16"]
+    _say(f"[bwd] {w.name} full size")
+    inp = make_prefill_inputs(w)
+    dO, dST = make_cotangents(w)
+    g = to_dev(inp, gpu_device)
+    got = _gpu_bwd(kda, g, dO.to(gpu_device), dST.to(gpu_device))
+    heads = [0, 47, 95]
+    ref = _oracle_bwd(inp, dO, dST, heads=heads)
+    idx = torch.as_tensor(heads, device=gpu_device)
+    sub = {key: torch.index_select(got[key], GRAD_HEAD_AXIS.get(key, 0), idx) for key in got}
+    errs = _errors(sub, ref)
+    _say("   " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL[torch.bfloat16] for v in errs.values()), errs
+    for key in got:
+        assert torch.isfinite(got[key]).all(), key
