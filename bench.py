@@ -323,6 +323,31 @@ LONG_CASES = [("long_prefill_bf16", 64, 1), ("long_prefill_bf16", 16, 1),
               ("million_prefill_bf16", 16, 4), ("million_prefill_bf16", 16, 8)]
 
 
+def time_backward(torch, kda, inp, dO, dST, steps, warmup):
+    """ms per call of the chunk-parallel backward (kda_prefill_bwd: forward
+    rerun with per-chunk state checkpoints, then the reverse chunk kernels),
+    outputs and workspace allocated once outside the timed region."""
+    B, T, H, d = inp["q"].shape
+    dev = inp["q"].device
+    ws = torch.empty(kda.prefill_bwd_workspace_size(inp["q"].dtype, B, T, H, d, d),
+                     dtype=torch.uint8, device=dev)
+
+    def run():
+        kda.prefill_bwd(inp["q"], inp["k"], inp["v"], inp["z"], inp["beta"], inp["A"],
+                        inp["S0"], dO, dST, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, ws.numel()
+
+
 def time_long(torch, kda, steps):
     """The long-context (B1 H96 T65536) and million-token (B1 H16 T2^20) prefill
     workloads, inputs drawn on the device (same recipe and seed, device
@@ -362,6 +387,8 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the chunk-parallel backward timing")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the long-context and million-token prefill timings")
     ap.add_argument("--calib-mib", type=int, default=0,
@@ -490,6 +517,19 @@ def main(argv=None):
                                  "kda_decode_kernel", f"kda_decode_kernel_conv_{wd.name}.md"),
                              "kernel": "kda_decode_kernel (prologue fused)",
                              "bytes_per_launch": dcb}}}
+    if not args.no_backward:
+        from linear_recurrent_attention_chunkwise_amd.inputs import make_cotangents
+        dO, dST = make_cotangents(w, device=dev)
+        bms, wsb = time_backward(torch, kda, inp, dO, dST,
+                                 max(1, args.steps // 20), max(1, args.warmup // 400))
+        del dO, dST
+        torch.cuda.empty_cache()
+        result["backward"] = {
+            "value": w.B * w.T / (bms * 1e-3), "unit": "tokens/s", "ms_per_call": bms,
+            "workload": f"{w.name}: gradients of q, k, v, z, beta, A, S0 from dL/do and "
+                        f"dL/dS_T (B={w.B} H={w.H} T={w.T} d={w.dk}, bf16 in, fp32 gradients)",
+            "workspace_bytes": wsb,
+            "kernels": "forward rerun with 16-token checkpoints + kda_bwd_prep/chain/grad/dA"}
     if not args.no_long:
         result["long"] = time_long(torch, kda, 3)
     if args.calib_mib > 0:

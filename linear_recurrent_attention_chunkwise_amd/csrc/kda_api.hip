@@ -675,19 +675,20 @@ namespace {
 constexpr int kBwdChunk = 16;
 
 struct BwdLayout {
-    size_t o, S_T, ckpt, prep, part, dA, total;   // byte offsets, and the size
+    size_t o, S_T, ckpt, prep, part, dA, dsp, total;   // byte offsets, and the size
 };
 
 bool bwd_layout(int dtype, int64_t B, int64_t T, int64_t H, int64_t D, BwdLayout *lay) {
     const int64_t esz = dtype == KDA_BF16 ? 2 : 4;
     const int64_t nchunk = (T + kBwdChunk - 1) / kBwdChunk, nfull = T / kBwdChunk;
-    int64_t bt, bth, nin, bh, units, nst, nck, nprep, npart;
+    int64_t bt, bth, nin, bh, units, nst, nck, nprep, npart, ndsp;
     if (!mul_ok(B, T, kMaxElems, &bt) || !mul_ok(bt, H, kMaxElems, &bth) ||
         !mul_ok(bth, D, kMaxElems / 16, &nin) || !mul_ok(B, H, kMaxElems, &bh) ||
         !mul_ok(bh, D * D, kMaxElems / 16, &nst) || !mul_ok(bh, nchunk, kMaxElems, &units) ||
         !mul_ok(bh * nfull, D * D, kMaxElems / 16, &nck) ||
         !mul_ok(units, (int64_t)kda::bwd_prep_floats(D), kMaxElems / 16, &nprep) ||
-        !mul_ok(units, (int64_t)kda::bwd_part_floats(D), kMaxElems / 16, &npart))
+        !mul_ok(units, (int64_t)kda::bwd_part_floats(D), kMaxElems / 16, &npart) ||
+        !mul_ok(units, (int64_t)kda::bwd_dsp_floats(dtype, D), kMaxElems / 16, &ndsp))
         return false;
     lay->o = 0;
     lay->S_T = round256(nin * esz);
@@ -695,7 +696,8 @@ bool bwd_layout(int dtype, int64_t B, int64_t T, int64_t H, int64_t D, BwdLayout
     lay->prep = lay->ckpt + round256(nck * 4);
     lay->part = lay->prep + round256(nprep * 4);
     lay->dA = lay->part + round256(npart * 4);
-    lay->total = lay->dA + round256(units * 4);
+    lay->dsp = lay->dA + round256(units * 4);
+    lay->total = lay->dsp + round256(ndsp * 4);
     return true;
 }
 
@@ -772,6 +774,7 @@ kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
     a.prep = bh > 0 ? reinterpret_cast<float *>(ws + lay.prep) : nullptr;
     a.part = bh > 0 ? reinterpret_cast<float *>(ws + lay.part) : nullptr;
     a.dA_part = bh > 0 ? reinterpret_cast<float *>(ws + lay.dA) : nullptr;
+    a.dsp = bh > 0 && lay.total > lay.dsp ? reinterpret_cast<float *>(ws + lay.dsp) : nullptr;
     a.dq = dq; a.dk = dk_out; a.dv = dv_out; a.dz = dz; a.dbeta = dbeta; a.dA = dA; a.dS0 = dS0;
     a.stream = s;
     return kda::launch_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;

@@ -300,6 +300,351 @@ __global__ __launch_bounds__(NT) void kda_bwd_chain_kernel(BwdArgs p) {
     }
 }
 
+// ------------------------------------------- bf16, d = 128: MFMA kernels ----
+//
+// For bf16 inputs at d = 128 the chain is split in two, both on bf16 MFMA
+// tiles with fp32 accumulation (the forward's operand precision):
+//   dstate -- sequential over chunks, one workgroup per (b, h, 64 value
+//             columns), a wave per 16 columns with its 128 x 16 slice of dS in
+//             accumulator tiles.  Per chunk (reverse order) it stores the
+//             incoming dS' and applies
+//                dU = P^T dO + Kb dS',   dS = e^{G_n} dS' + Q^^T dO - W^T dU.
+//             The chunk's prep record is staged through LDS (double buffer,
+//             one barrier per chunk).
+//   part   -- one workgroup per (b, h, chunk), all chunks in parallel: from the
+//             chunk-entry state S (forward checkpoints) and the stored dS' it
+//             recomputes U and dU and forms, over all 128 value columns at once,
+//             the sums the grad kernel consumes (dQ^, dKb, dW, dP, the V part of
+//             dT and of dbeta, sum_j dS' S), plus dV.  The record has a single
+//             column slice.
+
+namespace {
+
+constexpr int BD = 128;          // head size of the MFMA backward
+constexpr int BLD = BD + 8;      // bf16 row stride of [.][d] / [.][j] LDS tiles
+constexpr int BLT = C + 8;       // bf16 row stride of [.][token] LDS tiles
+
+__device__ __forceinline__ Frag<bf16> frag_rows(const bf16 *tile, int ld, int r0, int col, int lane) {
+    // K16 fragment over k = r0 + 4*(lane/16) + e of column `col`: tile[k][col]
+    Frag<bf16> f;
+    const int g = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.v[e] = tile[(r0 + 4 * g + e) * ld + col];
+    return f;
+}
+
+__device__ __forceinline__ void store_bf16x4(bf16 *p, float a, float b, float c, float d) {
+    *reinterpret_cast<bf16x4 *>(p) = bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+}
+
+// Sum over the 16 lanes n of each row group (lanes 16g .. 16g+15), fixed order.
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 8, 16);
+    x += __shfl_xor(x, 4, 16);
+    x += __shfl_xor(x, 2, 16);
+    x += __shfl_xor(x, 1, 16);
+    return x;
+}
+
+struct DstateBuf {
+    bf16 Kb[C][BLD];      // Kb [r][d]
+    bf16 QhT[BD][BLT];    // Q^ transposed [d][r]
+    bf16 WTn[BD][BLT];    // -W transposed [d][r]
+    bf16 PT[C][BLT];      // P transposed [r][s] = P[s][r]
+    float Gn[BD];         // e^{G_n}
+};
+
+}  // namespace
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, float *dsp) {
+    using Lay = PrepLayout<BD>;
+    constexpr int NDT = BD / 16, NT = 64 * NW, NSL = BD / (16 * NW);
+    __shared__ __attribute__((aligned(16))) DstateBuf buf[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const int64_t x = blockIdx.x;
+    const int64_t bh = x / NSL;
+    const int jw = (int)(x % NSL) * 16 * NW + 16 * wave;   // this wave's first value column
+    const int64_t b = bh / p.H, h = bh % p.H, H = p.H;
+    const int64_t nchunk = p.nchunk;
+    const bf16 *dO = static_cast<const bf16 *>(p.dO);
+
+    f32x4 dS[NDT];
+#pragma unroll
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dS[i][e] = p.dST ? p.dST[(bh * BD + 16 * i + 4 * g + e) * BD + jw + n] : 0.f;
+
+    // staging registers: this thread's float4s of the record of one chunk
+    f32x4 rw[2048 / 4 / NT], rq[2048 / 4 / NT], rk[2048 / 4 / NT], rp, rg;
+    auto load_rec = [&](int64_t c) {
+        const f32x4 *rec =
+            reinterpret_cast<const f32x4 *>(p.prep + (bh * nchunk + c) * (int64_t)Lay::SIZE);
+#pragma unroll
+        for (int u = 0; u < 2048 / 4 / NT; ++u) {
+            rw[u] = rec[Lay::W / 4 + tid + NT * u];
+            rq[u] = rec[Lay::QH / 4 + tid + NT * u];
+            rk[u] = rec[Lay::KB / 4 + tid + NT * u];
+        }
+        if (tid < C * C / 4) rp = rec[Lay::P / 4 + tid];
+        if (tid < BD / 4) rg = rec[Lay::GN / 4 + tid];
+    };
+    auto store_rec = [&](DstateBuf &B) {
+#pragma unroll
+        for (int u = 0; u < 2048 / 4 / NT; ++u) {
+            const int f = tid + NT * u, r = f / (BD / 4), d = 4 * (f % (BD / 4));
+            store_bf16x4(&B.Kb[r][d], rk[u][0], rk[u][1], rk[u][2], rk[u][3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                B.QhT[d + e][r] = (bf16)rq[u][e];
+                B.WTn[d + e][r] = (bf16)(-rw[u][e]);
+            }
+        }
+        if (tid < C * C / 4) {
+            const int sidx = tid / 4, r0 = 4 * (tid % 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) B.PT[r0 + e][sidx] = (bf16)rp[e];
+        }
+        if (tid < BD / 4) *reinterpret_cast<f32x4 *>(&B.Gn[4 * tid]) = rg;
+    };
+    // dO fragment of a chunk: dO[t0 + 4g + e][jw + n] (zero past T)
+    const int64_t tok_stride = H * BD, row_bytes = tok_stride * 2;
+    const int64_t base = (b * p.T * H + h) * BD;
+    short dr[4];
+    auto load_do = [&](int64_t c) {
+        const int64_t t0 = c * C, rows = p.T - t0 < C ? p.T - t0 : (int64_t)C;
+        const auto rs = make_rsrc(dO + base + t0 * tok_stride + jw, rows * row_bytes);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dr[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, (4 * g + e) * (int)row_bytes + 2 * n, 0, 0);
+    };
+
+    if (nchunk > 0) {
+        load_rec(nchunk - 1);
+        load_do(nchunk - 1);
+        store_rec(buf[(nchunk - 1) & 1]);
+    }
+    __syncthreads();
+    for (int64_t c = nchunk - 1; c >= 0; --c) {
+        Frag<bf16> dOf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dOf.v[e] = __builtin_bit_cast(bf16, dr[e]);
+        if (c > 0) {
+            load_rec(c - 1);
+            load_do(c - 1);
+        }
+        const DstateBuf &B = buf[c & 1];
+        // the incoming dS' of chunk c
+        float *out = dsp + (bh * nchunk + c) * (int64_t)(BD * BD);
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[(16 * i + 4 * g + e) * BD + jw + n] = dS[i][e];
+        // dU = P^T dO + Kb dS'
+        Frag<bf16> dSf[NDT];
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) dSf[i] = acc_frag<bf16>(dS[i]);
+        f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = {0.f, 0.f, 0.f, 0.f};
+        mma16(ua, lds_frag(&B.PT[0][0], BLT, 0, lane), dOf);
+#pragma unroll
+        for (int i = 0; i < NDT; i += 2) {
+            f32x4 &acc = (i / 2) % 2 ? ua : ub;
+            mma32(acc, lds_frag(&B.Kb[0][0], BLD, 16 * i, lane),
+                  lds_frag(&B.Kb[0][0], BLD, 16 * i + 16, lane), dSf[i], dSf[i + 1]);
+        }
+        const Frag<bf16> dUf = acc_frag<bf16>(ua + ub);
+        // dS = e^{G_n} dS' + Q^^T dO - W^T dU
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) {
+            const f32x4 gn = *reinterpret_cast<const f32x4 *>(&B.Gn[16 * i + 4 * g]);
+            dS[i] *= gn;
+            mma32(dS[i], lds_frag(&B.QhT[16 * i][0], BLT, 0, lane),
+                  lds_frag(&B.WTn[16 * i][0], BLT, 0, lane), dOf, dUf);
+        }
+        if (c > 0) store_rec(buf[(c - 1) & 1]);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p.dS0[(bh * BD + 16 * i + 4 * g + e) * BD + jw + n] = dS[i][e];
+}
+
+namespace {
+struct PartLds {
+    bf16 S[BD][BLD], dS[BD][BLD];          // chunk-entry state, incoming dS' [d][j]
+    bf16 W[C][BLD], Kb[C][BLD];            // [r][d]
+    bf16 V[C][BLD], dO[C][BLD], U[C][BLD], dU[C][BLD];   // [r][j]
+    bf16 Tb[C][BLT], PT[C][BLT], TT[C][BLT];            // T diag(beta), P^T, T^T
+    float beta[C];
+    float dbV[8][C];
+};
+}  // namespace
+
+__global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const float *dsp) {
+    using Lay = PrepLayout<BD>;
+    using PL = PartLayout<BD>;
+    constexpr int NT = 512;
+    __shared__ __attribute__((aligned(16))) PartLds s;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const int64_t x = blockIdx.x;
+    const int64_t c = x % p.nchunk, bh = x / p.nchunk;
+    const int64_t b = bh / p.H, h = bh % p.H, H = p.H;
+    const int nv = (int)(p.T - c * C < C ? p.T - c * C : C);   // tokens in the chunk
+    const int64_t nfull = p.T / C;
+    const int64_t row0 = (b * p.T + c * C) * H + h;            // token row of the chunk's first token
+    const bf16 *v = static_cast<const bf16 *>(p.v), *dOg = static_cast<const bf16 *>(p.dO),
+               *betag = static_cast<const bf16 *>(p.beta);
+    float *part = p.part + x * (int64_t)PL::SIZE;
+
+    // ---- stage: S, dS' (fp32 -> bf16) and sum_j dS' S per key row ----
+    {
+        const float *Sin = c == 0 ? (p.S0 ? p.S0 + bh * (int64_t)(BD * BD) : nullptr)
+                                  : p.ckpt + ((b * nfull + c - 1) * H + h) * (int64_t)(BD * BD);
+        const f32x4 *S4 = reinterpret_cast<const f32x4 *>(Sin);
+        const f32x4 *D4 = reinterpret_cast<const f32x4 *>(dsp + x * (int64_t)(BD * BD));
+        f32x4 sv[8], dv4[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            sv[u] = S4 ? S4[tid + NT * u] : f32x4{0.f, 0.f, 0.f, 0.f};
+            dv4[u] = D4[tid + NT * u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int f = tid + NT * u, d = f / 32, j = 4 * (f % 32);
+            store_bf16x4(&s.S[d][j], sv[u][0], sv[u][1], sv[u][2], sv[u][3]);
+            store_bf16x4(&s.dS[d][j], dv4[u][0], dv4[u][1], dv4[u][2], dv4[u][3]);
+            float a = sv[u][0] * dv4[u][0] + sv[u][1] * dv4[u][1] + sv[u][2] * dv4[u][2] +
+                      sv[u][3] * dv4[u][3];
+            a += __shfl_xor(a, 16, 32);
+            a += __shfl_xor(a, 8, 32);
+            a += __shfl_xor(a, 4, 32);
+            a += __shfl_xor(a, 2, 32);
+            a += __shfl_xor(a, 1, 32);
+            if ((tid & 31) == 0) part[PL::DGN + d] = a;
+        }
+    }
+    // ---- stage: the chunk's W, Kb, T, P, beta, V, dO ----
+    {
+        const float *rec = p.prep + x * (int64_t)Lay::SIZE;
+        const int f = tid, r = f / 32, d = 4 * (f % 32);   // 512 float4s of a [C][D] matrix
+        const f32x4 w4 = reinterpret_cast<const f32x4 *>(rec + Lay::W)[f];
+        const f32x4 k4 = reinterpret_cast<const f32x4 *>(rec + Lay::KB)[f];
+        store_bf16x4(&s.W[r][d], w4[0], w4[1], w4[2], w4[3]);
+        store_bf16x4(&s.Kb[r][d], k4[0], k4[1], k4[2], k4[3]);
+        if (tid < C * C / 4) {
+            // T row r = tid / 4, columns s0 .. s0+3
+            const int rr = tid / 4, s0 = 4 * (tid % 4);
+            const f32x4 t4 = reinterpret_cast<const f32x4 *>(rec + Lay::T)[tid];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int sc = s0 + e;
+                const float bs = sc < nv ? (float)betag[row0 + (int64_t)sc * H] : 0.f;
+                s.Tb[rr][sc] = (bf16)(t4[e] * bs);
+                s.TT[sc][rr] = (bf16)t4[e];
+            }
+        } else if (tid < 2 * C * C / 4) {
+            // P row sidx, columns r0 .. r0+3  ->  P^T[r][sidx]
+            const int f2 = tid - C * C / 4, sidx = f2 / 4, r0 = 4 * (f2 % 4);
+            const f32x4 p4 = reinterpret_cast<const f32x4 *>(rec + Lay::P)[f2];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s.PT[r0 + e][sidx] = (bf16)p4[e];
+        } else if (tid < 2 * C * C / 4 + C) {
+            const int rr = tid - 2 * C * C / 4;
+            s.beta[rr] = rr < nv ? (float)betag[row0 + (int64_t)rr * H] : 0.f;
+        }
+        // V and dO rows: 16 rows x 16 pieces of 8 bf16 each
+        const int t2 = tid & 255, rr = t2 / 16, pc = t2 % 16;
+        const bf16 *src = tid < 256 ? v : dOg;
+        uint4 val = {0u, 0u, 0u, 0u};
+        if (rr < nv) val = *reinterpret_cast<const uint4 *>(src + (row0 + (int64_t)rr * H) * BD + 8 * pc);
+        bf16 *dst = tid < 256 ? &s.V[rr][8 * pc] : &s.dO[rr][8 * pc];
+        *reinterpret_cast<uint4 *>(dst) = val;
+    }
+    __syncthreads();
+
+    // ---- wave w: value columns jw .. jw+15: U, dU, T^T dU, dV, dbeta's V part ----
+    {
+        const int jw = 16 * wave;
+        const Frag<bf16> Vf = frag_rows(&s.V[0][0], BLD, 0, jw + n, lane);
+        const Frag<bf16> dOf = frag_rows(&s.dO[0][0], BLD, 0, jw + n, lane);
+        f32x4 ta = {0.f, 0.f, 0.f, 0.f}, tb = {0.f, 0.f, 0.f, 0.f};   // U = T b V - W S
+        f32x4 da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};   // dU = P^T dO + Kb dS'
+        mma16(ta, lds_frag(&s.Tb[0][0], BLT, 0, lane), Vf);
+        mma16(da, lds_frag(&s.PT[0][0], BLT, 0, lane), dOf);
+#pragma unroll
+        for (int i = 0; i < BD / 16; i += 2) {
+            mma32(tb, lds_frag(&s.W[0][0], BLD, 16 * i, lane), lds_frag(&s.W[0][0], BLD, 16 * i + 16, lane),
+                  frag_rows(&s.S[0][0], BLD, 16 * i, jw + n, lane),
+                  frag_rows(&s.S[0][0], BLD, 16 * i + 16, jw + n, lane));
+            mma32(db, lds_frag(&s.Kb[0][0], BLD, 16 * i, lane), lds_frag(&s.Kb[0][0], BLD, 16 * i + 16, lane),
+                  frag_rows(&s.dS[0][0], BLD, 16 * i, jw + n, lane),
+                  frag_rows(&s.dS[0][0], BLD, 16 * i + 16, jw + n, lane));
+        }
+        const f32x4 U = ta - tb, dU = da + db;
+        f32x4 BV = {0.f, 0.f, 0.f, 0.f};
+        mma16(BV, lds_frag(&s.TT[0][0], BLT, 0, lane), acc_frag<bf16>(dU));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            s.U[r][jw + n] = (bf16)U[e];
+            s.dU[r][jw + n] = (bf16)dU[e];
+            if (r < nv) p.dv[(row0 + (int64_t)r * H) * BD + jw + n] = s.beta[r] * BV[e];
+            const float part_bv = sum16(BV[e] * (float)Vf.v[e]);
+            if (n == 0) s.dbV[wave][r] = part_bv;
+        }
+    }
+    __syncthreads();
+
+    // ---- wave w: key rows dw .. dw+15 of dQ^, dW, dKb (sums over all columns) ----
+    {
+        const int dw = 16 * wave;
+        f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < BD / 16; i += 2) {
+            const Frag<bf16> s0 = lds_frag(&s.S[dw][0], BLD, 16 * i, lane),
+                             s1 = lds_frag(&s.S[dw][0], BLD, 16 * i + 16, lane);
+            mma32(aq, lds_frag(&s.dO[0][0], BLD, 16 * i, lane), lds_frag(&s.dO[0][0], BLD, 16 * i + 16, lane),
+                  s0, s1);
+            mma32(aw, lds_frag(&s.dU[0][0], BLD, 16 * i, lane), lds_frag(&s.dU[0][0], BLD, 16 * i + 16, lane),
+                  s0, s1);
+            mma32(ak, lds_frag(&s.U[0][0], BLD, 16 * i, lane), lds_frag(&s.U[0][0], BLD, 16 * i + 16, lane),
+                  lds_frag(&s.dS[dw][0], BLD, 16 * i, lane), lds_frag(&s.dS[dw][0], BLD, 16 * i + 16, lane));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            part[PL::DQH + r * BD + dw + n] = aq[e];
+            part[PL::DW + r * BD + dw + n] = -aw[e];
+            part[PL::DKB + r * BD + dw + n] = ak[e];
+        }
+        if (wave == 0 || wave == 1) {
+            // dP = dO U^T (wave 0);  dT's V part = dU (beta V)^T (wave 1)
+            const bf16 *A = wave == 0 ? &s.dO[0][0] : &s.dU[0][0];
+            const bf16 *Bm = wave == 0 ? &s.U[0][0] : &s.V[0][0];
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < BD / 16; i += 2)
+                mma32(acc, lds_frag(A, BLD, 16 * i, lane), lds_frag(A, BLD, 16 * i + 16, lane),
+                      lds_frag(Bm, BLD, 16 * i, lane), lds_frag(Bm, BLD, 16 * i + 16, lane));
+            const float sc = wave == 0 ? 1.f : s.beta[n];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                part[(wave == 0 ? PL::DP : PL::DTV) + (4 * g + e) * C + n] = acc[e] * sc;
+        } else if (wave == 2 && lane < C) {
+            float a = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) a += s.dbV[w][lane];
+            part[PL::DBV + lane] = a;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ grad ----
 
 template <typename TI, int D> struct GradLds {
@@ -309,11 +654,10 @@ template <typename TI, int D> struct GradLds {
     float dbV[C], dGn[D];
 };
 
-template <typename TI, int D>
+template <typename TI, int D, int NS>
 __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     __shared__ GradLds<TI, D> s;
     using PL = PartLayout<D>;
-    constexpr int NS = D == 128 ? 2 : 1;
     const int64_t x = blockIdx.x;
     const int64_t c = x % p.nchunk, bh = x / p.nchunk;
     const int64_t b = bh / p.H, h = bh % p.H, H = p.H;
@@ -493,17 +837,41 @@ static hipError_t launch_bwd_t(const BwdArgs &a) {
         hipLaunchKernelGGL((kda_bwd_chain_kernel<TI, D, NC, NT>), dim3((unsigned)(bh * (D / NC))),
                            dim3(NT), 0, a.stream, a);
     if (units > 0)
-        hipLaunchKernelGGL((kda_bwd_grad_kernel<TI, D>), dim3((unsigned)units), dim3(256), 0,
-                           a.stream, a);
+        hipLaunchKernelGGL((kda_bwd_grad_kernel<TI, D, D / NC>), dim3((unsigned)units), dim3(256),
+                           0, a.stream, a);
     if (a.H > 0)
         hipLaunchKernelGGL(kda_bwd_dA_kernel, dim3((unsigned)((a.H + 255) / 256)), dim3(256), 0,
                            a.stream, a.dA_part, a.dA, a.B, a.H, a.nchunk);
     return hipGetLastError();
 }
 
+// bf16, d = 128: prep, the dS recurrence (dstate) and the chunk-parallel sums
+// (part) on MFMA tiles, then grad with a single column slice.
+static hipError_t launch_bwd_mfma(const BwdArgs &a) {
+    const int64_t bh = a.B * a.H, units = bh * a.nchunk;
+    if (units > 0)
+        hipLaunchKernelGGL((kda_bwd_prep_kernel<bf16, BD>), dim3((unsigned)units), dim3(256), 0,
+                           a.stream, a);
+    if (bh > 0)
+        hipLaunchKernelGGL(kda_bwd_dstate_kernel<4>, dim3((unsigned)(bh * 2)), dim3(256), 0,
+                           a.stream, a, a.dsp);
+    if (units > 0) {
+        hipLaunchKernelGGL(kda_bwd_part_kernel, dim3((unsigned)units), dim3(512), 0, a.stream, a,
+                           (const float *)a.dsp);
+        hipLaunchKernelGGL((kda_bwd_grad_kernel<bf16, BD, 1>), dim3((unsigned)units), dim3(256), 0,
+                           a.stream, a);
+    }
+    if (a.H > 0)
+        hipLaunchKernelGGL(kda_bwd_dA_kernel, dim3((unsigned)((a.H + 255) / 256)), dim3(256), 0,
+                           a.stream, a.dA_part, a.dA, a.B, a.H, a.nchunk);
+    return hipGetLastError();
+}
+
+size_t bwd_dsp_floats(int dtype, int64_t D) { return dtype == 1 && D == 128 ? D * D : 0; }
+
 hipError_t launch_bwd(const BwdArgs &a) {
     if (a.dtype == 1) {
-        if (a.D == 128) return launch_bwd_t<bf16, 128, 64, 512>(a);
+        if (a.D == 128) return launch_bwd_mfma(a);
         return launch_bwd_t<bf16, 16, 16, 256>(a);
     }
     if (a.D == 128) return launch_bwd_t<float, 128, 64, 512>(a);
