@@ -63,9 +63,14 @@ template <int D> struct PartLayout {
 
 // The S-independent quantities of one chunk, in LDS.  Rows r >= n are absent
 // tokens: zero inputs, beta 0 and g 0 (alpha 1), so they contribute nothing.
+// E = e^{G} and Ei = e^{-G} (G the in-chunk cumulative log-decay; over 16
+// tokens e^{-G} <= e^80 stays in fp32 range), so e^{G_r - G_s} = E_r Ei_s.
+// [C][D] rows are padded by one float: threads that read one column d of
+// several rows then hit distinct LDS banks.
+template <int D> constexpr int rowpad() { return D + 1; }
 template <typename TI, int D> struct ChunkOps {
-    float q[C][D], k[C][D], G[C][D];
-    float A[C][C], P[C][C], T[C][C];
+    float q[C][rowpad<D>()], k[C][rowpad<D>()], E[C][rowpad<D>()], Ei[C][rowpad<D>()];
+    float A[C][C + 1], P[C][C + 1], T[C][C + 1];
     float beta[C];
 };
 
@@ -88,17 +93,18 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
         }
         s.q[r][d] = qv;
         s.k[r][d] = kv;
-        s.G[r][d] = g;
+        s.E[r][d] = g;
     }
     for (int r = threadIdx.x; r < C; r += blockDim.x)
         s.beta[r] = r < n ? to_f32(beta[row0 + (int64_t)r * H]) : 0.f;
     __syncthreads();
-    // cumulative log-decay over the chunk
+    // cumulative log-decay over the chunk, kept as e^{G} and e^{-G}
     for (int d = threadIdx.x; d < D; d += blockDim.x) {
         float acc = 0.f;
         for (int r = 0; r < C; ++r) {
-            acc += s.G[r][d];
-            s.G[r][d] = acc;
+            acc += s.E[r][d];
+            s.E[r][d] = __expf(acc);
+            s.Ei[r][d] = __expf(-acc);
         }
     }
     __syncthreads();
@@ -108,9 +114,9 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
         float a = 0.f, pp = 0.f;
         if (sc <= r) {
             for (int d = 0; d < D; ++d) {
-                const float e = __expf(s.G[r][d] - s.G[sc][d]);
-                a += s.k[r][d] * s.k[sc][d] * e;
-                pp += s.q[r][d] * s.k[sc][d] * e;
+                const float ks = s.k[sc][d] * s.Ei[sc][d], er = s.E[r][d];
+                a += s.k[r][d] * er * ks;
+                pp += s.q[r][d] * er * ks;
             }
         }
         s.A[r][sc] = sc < r ? a : 0.f;
@@ -144,18 +150,17 @@ __global__ __launch_bounds__(256) void kda_bwd_prep_kernel(BwdArgs p) {
     float *rec = p.prep + x * (int64_t)Lay::SIZE;
     for (int i = threadIdx.x; i < C * D; i += blockDim.x) {
         const int r = i / D, d = i % D;
-        const float G = s.G[r][d], Gn = s.G[C - 1][d];
         float w = 0.f;
-        for (int sc = 0; sc < C; ++sc) w += s.T[r][sc] * s.beta[sc] * s.k[sc][d] * __expf(s.G[sc][d]);
+        for (int sc = 0; sc < C; ++sc) w += s.T[r][sc] * s.beta[sc] * s.k[sc][d] * s.E[sc][d];
         rec[Lay::W + i] = w;
-        rec[Lay::QH + i] = s.q[r][d] * __expf(G);
-        rec[Lay::KB + i] = s.k[r][d] * __expf(Gn - G);
+        rec[Lay::QH + i] = s.q[r][d] * s.E[r][d];
+        rec[Lay::KB + i] = s.k[r][d] * (s.E[C - 1][d] * s.Ei[r][d]);
     }
     for (int i = threadIdx.x; i < C * C; i += blockDim.x) {
-        rec[Lay::P + i] = (&s.P[0][0])[i];
-        rec[Lay::T + i] = (&s.T[0][0])[i];
+        rec[Lay::P + i] = s.P[i / C][i % C];
+        rec[Lay::T + i] = s.T[i / C][i % C];
     }
-    for (int d = threadIdx.x; d < D; d += blockDim.x) rec[Lay::GN + d] = __expf(s.G[C - 1][d]);
+    for (int d = threadIdx.x; d < D; d += blockDim.x) rec[Lay::GN + d] = s.E[C - 1][d];
 }
 
 // ----------------------------------------------------------------- chain ----
@@ -649,7 +654,7 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const floa
 
 template <typename TI, int D> struct GradLds {
     ChunkOps<TI, D> o;
-    float dQh[C][D], dKb[C][D], dW[C][D], dG[C][D];
+    float dQh[C][rowpad<D>()], dKb[C][rowpad<D>()], dW[C][rowpad<D>()], dG[C][rowpad<D>()];
     float dP[C][C], dTV[C][C], dT[C][C], M1[C][C], dL[C][C];
     float dbV[C], dGn[D];
 };
@@ -673,9 +678,9 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
             bb += part[q * PL::SIZE + PL::DKB + i];
             w += part[q * PL::SIZE + PL::DW + i];
         }
-        (&s.dQh[0][0])[i] = a;
-        (&s.dKb[0][0])[i] = bb;
-        (&s.dW[0][0])[i] = w;
+        s.dQh[i / D][i % D] = a;
+        s.dKb[i / D][i % D] = bb;
+        s.dW[i / D][i % D] = w;
     }
     for (int i = tid; i < C * C; i += blockDim.x) {
         float a = 0.f, bb = 0.f;
@@ -695,16 +700,23 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     for (int d = tid; d < D; d += blockDim.x) {
         float a = 0.f;
         for (int q = 0; q < NS; ++q) a += part[q * PL::SIZE + PL::DGN + d];
-        s.dGn[d] = a * __expf(s.o.G[C - 1][d]);   // d/dG_n of e^{G_n} * (sum_j dS' S)
+        s.dGn[d] = a * s.o.E[C - 1][d];   // d/dG_n of e^{G_n} * (sum_j dS' S)
     }
     __syncthreads();
     auto &o = s.o;
     // dT = dW (beta K^)^T + dU (beta V)^T
     for (int i = tid; i < C * C; i += blockDim.x) {
         const int r = i / C, sc = i % C;
-        float a = s.dTV[r][sc];
-        for (int d = 0; d < D; ++d) a += s.dW[r][d] * o.beta[sc] * o.k[sc][d] * __expf(o.G[sc][d]);
-        s.dT[r][sc] = a;
+        float a = 0.f;
+        for (int d = 0; d < D; ++d) a += s.dW[r][d] * (o.k[sc][d] * o.E[sc][d]);
+        s.dT[r][sc] = s.dTV[r][sc] + o.beta[sc] * a;
+    }
+    // (T^T dW)[r][d], held in dG until dG itself is formed below
+    for (int i = tid; i < C * D; i += blockDim.x) {
+        const int r = i / D, d = i % D;
+        float a = 0.f;
+        for (int u = 0; u < C; ++u) a += o.T[u][r] * s.dW[u][d];
+        s.dG[r][d] = a;
     }
     __syncthreads();
     // M1 = T^T dT;  dL = -M1 T^T (strictly lower)
@@ -722,16 +734,17 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
         s.dL[r][sc] = sc < r ? -a : 0.f;
     }
     __syncthreads();
-    // dbeta: V part, K^ part (through W), L part;  dA = beta dL (kept in dL)
-    for (int r = tid; r < C; r += blockDim.x) {
-        float a = s.dbV[r];
-        for (int d = 0; d < D; ++d) {
-            float dbk = 0.f;   // (T^T dW)[r][d]
-            for (int u = 0; u < C; ++u) dbk += o.T[u][r] * s.dW[u][d];
-            a += dbk * o.k[r][d] * __expf(o.G[r][d]);
+    // dbeta: V part, K^ part (through W), L part; 16 lanes per token row
+    {
+        const int r = tid / 16, l = tid % 16;   // blockDim.x == 16 * C
+        float a = 0.f;
+        for (int d = l; d < D; d += 16) a += s.dG[r][d] * o.k[r][d] * o.E[r][d];
+        a = sum16(a);
+        if (l == 0) {
+            a += s.dbV[r];
+            for (int sc = 0; sc < C; ++sc) a += s.dL[r][sc] * o.A[r][sc];
+            if (r < n) p.dbeta[(b * p.T + c * C + r) * H + h] = a;
         }
-        for (int sc = 0; sc < C; ++sc) a += s.dL[r][sc] * o.A[r][sc];
-        if (r < n) p.dbeta[(b * p.T + c * C + r) * H + h] = a;
     }
     __syncthreads();
     for (int i = tid; i < C * C; i += blockDim.x) {
@@ -743,40 +756,37 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     float dA_acc = 0.f;
     for (int i = tid; i < C * D; i += blockDim.x) {
         const int r = i / D, d = i % D;
-        const float G = o.G[r][d], Gm = __expf(G), Gi = __expf(-G);
-        const float Gn = o.G[C - 1][d];
+        const float Em = o.E[r][d], Ei = o.Ei[r][d], En = o.E[C - 1][d];
         const float qv = o.q[r][d], kv = o.k[r][d];
         float dqh = s.dQh[r][d];     // total dQ^
         float dkh = 0.f;             // total dK^ (from A and W)
         float dki = 0.f;             // total dKi (from A and P)
         for (int sc = 0; sc < C; ++sc) {
-            const float ki_s = o.k[sc][d] * __expf(-o.G[sc][d]);
-            const float kh_s = o.k[sc][d] * __expf(o.G[sc][d]);
-            const float qh_s = o.q[sc][d] * __expf(o.G[sc][d]);
+            const float ks = o.k[sc][d], es = o.E[sc][d];
+            const float ki_s = ks * o.Ei[sc][d], kh_s = ks * es, qh_s = o.q[sc][d] * es;
             dqh += s.dP[r][sc] * ki_s;
             dkh += s.dL[r][sc] * ki_s;
             dki += s.dL[sc][r] * kh_s + s.dP[sc][r] * qh_s;
         }
-        float dbk = 0.f;
-        for (int u = 0; u < C; ++u) dbk += o.T[u][r] * s.dW[u][d];
-        dkh += o.beta[r] * dbk;                      // through W = T diag(beta) K^
-        const float kb = kv * __expf(Gn - G);
-        const float dq = dqh * Gm;
-        const float dk = dkh * Gm + dki * Gi + s.dKb[r][d] * __expf(Gn - G);
-        const float dG = dqh * qv * Gm + dkh * kv * Gm - dki * kv * Gi - s.dKb[r][d] * kb;
+        dkh += o.beta[r] * s.dG[r][d];               // through W = T diag(beta) K^
+        const float enr = En * Ei;                   // e^{G_n - G}
+        const float kb = kv * enr;
+        const float dq = dqh * Em;
+        const float dk = dkh * Em + dki * Ei + s.dKb[r][d] * enr;
+        const float dG = dqh * qv * Em + dkh * kv * Em - dki * kv * Ei - s.dKb[r][d] * kb;
         if (r < n) {
             const int64_t off = ((b * p.T + c * C + r) * H + h) * D + d;
             p.dq[off] = dq;
             p.dk[off] = dk;
         }
-        s.dG[r][d] = dG;
+        s.dG[r][d] = dG;   // this thread read (T^T dW)[r][d] above
     }
     __syncthreads();
     // dG_n from Kb = K e^{G_n - G} and from e^{G_n} (sum_j dS' S); G_n = G of the last row
     for (int d = tid; d < D; d += blockDim.x) {
         float a = s.dGn[d];
-        const float Gn = o.G[C - 1][d];
-        for (int r = 0; r < C; ++r) a += s.dKb[r][d] * o.k[r][d] * __expf(Gn - o.G[r][d]);
+        const float En = o.E[C - 1][d];
+        for (int r = 0; r < C; ++r) a += s.dKb[r][d] * o.k[r][d] * (En * o.Ei[r][d]);
         s.dG[C - 1][d] += a;
     }
     __syncthreads();
