@@ -688,7 +688,7 @@ bool bwd_layout(int dtype, int64_t B, int64_t T, int64_t H, int64_t D, BwdLayout
         !mul_ok(bh * nfull, D * D, kMaxElems / 16, &nck) ||
         !mul_ok(units, (int64_t)kda::bwd_prep_floats(D), kMaxElems / 16, &nprep) ||
         !mul_ok(units, (int64_t)kda::bwd_part_floats(D), kMaxElems / 16, &npart) ||
-        !mul_ok(units, (int64_t)kda::bwd_dsp_floats(dtype, D), kMaxElems / 16, &ndsp))
+        !mul_ok(units, (int64_t)kda::bwd_dsp_bytes(dtype, D), kMaxElems / 16, &ndsp))
         return false;
     lay->o = 0;
     lay->S_T = round256(nin * esz);
@@ -697,7 +697,7 @@ bool bwd_layout(int dtype, int64_t B, int64_t T, int64_t H, int64_t D, BwdLayout
     lay->part = lay->prep + round256(nprep * 4);
     lay->dA = lay->part + round256(npart * 4);
     lay->dsp = lay->dA + round256(units * 4);
-    lay->total = lay->dsp + round256(ndsp * 4);
+    lay->total = lay->dsp + round256(ndsp);
     return true;
 }
 
@@ -774,7 +774,7 @@ kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
     a.prep = bh > 0 ? reinterpret_cast<float *>(ws + lay.prep) : nullptr;
     a.part = bh > 0 ? reinterpret_cast<float *>(ws + lay.part) : nullptr;
     a.dA_part = bh > 0 ? reinterpret_cast<float *>(ws + lay.dA) : nullptr;
-    a.dsp = bh > 0 && lay.total > lay.dsp ? reinterpret_cast<float *>(ws + lay.dsp) : nullptr;
+    a.dsp = bh > 0 && lay.total > lay.dsp ? static_cast<void *>(ws + lay.dsp) : nullptr;
     a.dq = dq; a.dk = dk_out; a.dv = dv_out; a.dz = dz; a.dbeta = dbeta; a.dA = dA; a.dS0 = dS0;
     a.stream = s;
     return kda::launch_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;

@@ -362,7 +362,7 @@ struct DstateBuf {
 }  // namespace
 
 template <int NW>
-__global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, float *dsp) {
+__global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, bf16 *dsp) {
     using Lay = PrepLayout<BD>;
     constexpr int NDT = BD / 16, NT = 64 * NW, NSL = BD / (16 * NW);
     __shared__ __attribute__((aligned(16))) DstateBuf buf[2];
@@ -442,16 +442,16 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, floa
             load_do(c - 1);
         }
         const DstateBuf &B = buf[c & 1];
-        // the incoming dS' of chunk c
-        float *out = dsp + (bh * nchunk + c) * (int64_t)(BD * BD);
-#pragma unroll
-        for (int i = 0; i < NDT; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[(16 * i + 4 * g + e) * BD + jw + n] = dS[i][e];
-        // dU = P^T dO + Kb dS'
+        // dU = P^T dO + Kb dS'; the incoming dS' of chunk c is stored as the
+        // same bf16 values the products use
         Frag<bf16> dSf[NDT];
 #pragma unroll
         for (int i = 0; i < NDT; ++i) dSf[i] = acc_frag<bf16>(dS[i]);
+        bf16 *out = dsp + (bh * nchunk + c) * (int64_t)(BD * BD);
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[(16 * i + 4 * g + e) * BD + jw + n] = dSf[i].v[e];
         f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = {0.f, 0.f, 0.f, 0.f};
         mma16(ua, lds_frag(&B.PT[0][0], BLT, 0, lane), dOf);
 #pragma unroll
@@ -489,7 +489,7 @@ struct PartLds {
 };
 }  // namespace
 
-__global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const float *dsp) {
+__global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16 *dsp) {
     using Lay = PrepLayout<BD>;
     using PL = PartLayout<BD>;
     constexpr int NT = 512;
@@ -512,18 +512,19 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const floa
         const float *Sin = c == 0 ? (p.S0 ? p.S0 + bh * (int64_t)(BD * BD) : nullptr)
                                   : p.ckpt + ((b * nfull + c - 1) * H + h) * (int64_t)(BD * BD);
         const f32x4 *S4 = reinterpret_cast<const f32x4 *>(Sin);
-        const f32x4 *D4 = reinterpret_cast<const f32x4 *>(dsp + x * (int64_t)(BD * BD));
+        const bf16x4 *D4 = reinterpret_cast<const bf16x4 *>(dsp + x * (int64_t)(BD * BD));
         f32x4 sv[8], dv4[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             sv[u] = S4 ? S4[tid + NT * u] : f32x4{0.f, 0.f, 0.f, 0.f};
-            dv4[u] = D4[tid + NT * u];
+            const bf16x4 t = D4[tid + NT * u];
+            dv4[u] = f32x4{(float)t[0], (float)t[1], (float)t[2], (float)t[3]};
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int f = tid + NT * u, d = f / 32, j = 4 * (f % 32);
             store_bf16x4(&s.S[d][j], sv[u][0], sv[u][1], sv[u][2], sv[u][3]);
-            store_bf16x4(&s.dS[d][j], dv4[u][0], dv4[u][1], dv4[u][2], dv4[u][3]);
+            *reinterpret_cast<bf16x4 *>(&s.dS[d][j]) = D4[tid + NT * u];
             float a = sv[u][0] * dv4[u][0] + sv[u][1] * dv4[u][1] + sv[u][2] * dv4[u][2] +
                       sv[u][3] * dv4[u][3];
             a += __shfl_xor(a, 16, 32);
@@ -864,10 +865,10 @@ static hipError_t launch_bwd_mfma(const BwdArgs &a) {
                            a.stream, a);
     if (bh > 0)
         hipLaunchKernelGGL(kda_bwd_dstate_kernel<4>, dim3((unsigned)(bh * 2)), dim3(256), 0,
-                           a.stream, a, a.dsp);
+                           a.stream, a, static_cast<bf16 *>(a.dsp));
     if (units > 0) {
         hipLaunchKernelGGL(kda_bwd_part_kernel, dim3((unsigned)units), dim3(512), 0, a.stream, a,
-                           (const float *)a.dsp);
+                           static_cast<const bf16 *>(a.dsp));
         hipLaunchKernelGGL((kda_bwd_grad_kernel<bf16, BD, 1>), dim3((unsigned)units), dim3(256), 0,
                            a.stream, a);
     }
@@ -877,7 +878,7 @@ static hipError_t launch_bwd_mfma(const BwdArgs &a) {
     return hipGetLastError();
 }
 
-size_t bwd_dsp_floats(int dtype, int64_t D) { return dtype == 1 && D == 128 ? D * D : 0; }
+size_t bwd_dsp_bytes(int dtype, int64_t D) { return dtype == 1 && D == 128 ? D * D * 2 : 0; }
 
 hipError_t launch_bwd(const BwdArgs &a) {
     if (a.dtype == 1) {

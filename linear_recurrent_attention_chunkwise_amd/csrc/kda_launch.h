@@ -126,13 +126,13 @@ struct BwdArgs {
     const void *q, *k, *v, *z, *beta, *dO;
     const float *A, *S0, *dST, *ckpt;
     float *prep, *part, *dA_part;
-    float *dsp;         // incoming dS' of every chunk [B, H, nchunk, D, D] (MFMA path), or NULL
+    void *dsp;          // incoming dS' of every chunk, bf16 [B, H, nchunk, D, D] (MFMA path), or NULL
     float *dq, *dk, *dv, *dz, *dbeta, *dA, *dS0;
     hipStream_t stream;
 };
 size_t bwd_prep_floats(int64_t D);   // per (b, h, chunk)
 size_t bwd_part_floats(int64_t D);   // per (b, h, chunk), all column slices
-size_t bwd_dsp_floats(int dtype, int64_t D);   // per (b, h, chunk): D*D on the MFMA path, else 0
+size_t bwd_dsp_bytes(int dtype, int64_t D);   // per (b, h, chunk): 2*D*D on the MFMA path, else 0
 hipError_t launch_bwd(const BwdArgs &a);
 
 }  // namespace kda
