@@ -63,13 +63,14 @@ template <int D> struct PartLayout {
 
 // The S-independent quantities of one chunk, in LDS.  Rows r >= n are absent
 // tokens: zero inputs, beta 0 and g 0 (alpha 1), so they contribute nothing.
-// E = e^{G} and Ei = e^{-G} (G the in-chunk cumulative log-decay; over 16
-// tokens e^{-G} <= e^80 stays in fp32 range), so e^{G_r - G_s} = E_r Ei_s.
+// With G the in-chunk cumulative log-decay, the decayed operands are kept:
+// Qh = q e^{G}, Kh = k e^{G}, Ki = k e^{-G} (over 16 tokens e^{-G} <= e^80
+// stays in fp32 range), and E = e^{G}; so k_r k_s e^{G_r - G_s} = Kh_r Ki_s.
 // [C][D] rows are padded by one float: threads that read one column d of
 // several rows then hit distinct LDS banks.
 template <int D> constexpr int rowpad() { return D + 1; }
 template <typename TI, int D> struct ChunkOps {
-    float q[C][rowpad<D>()], k[C][rowpad<D>()], E[C][rowpad<D>()], Ei[C][rowpad<D>()];
+    float Qh[C][rowpad<D>()], Kh[C][rowpad<D>()], Ki[C][rowpad<D>()], E[C][rowpad<D>()];
     float A[C][C + 1], P[C][C + 1], T[C][C + 1];
     float beta[C];
 };
@@ -91,20 +92,24 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
             kv = to_f32(k[off]);
             g = kGMin * sigmoidf_(cA * to_f32(z[off]));
         }
-        s.q[r][d] = qv;
-        s.k[r][d] = kv;
+        s.Qh[r][d] = qv;
+        s.Kh[r][d] = kv;
         s.E[r][d] = g;
     }
     for (int r = threadIdx.x; r < C; r += blockDim.x)
         s.beta[r] = r < n ? to_f32(beta[row0 + (int64_t)r * H]) : 0.f;
     __syncthreads();
-    // cumulative log-decay over the chunk, kept as e^{G} and e^{-G}
+    // cumulative log-decay over the chunk, applied to q and k
     for (int d = threadIdx.x; d < D; d += blockDim.x) {
         float acc = 0.f;
+#pragma unroll
         for (int r = 0; r < C; ++r) {
             acc += s.E[r][d];
-            s.E[r][d] = __expf(acc);
-            s.Ei[r][d] = __expf(-acc);
+            const float e = __expf(acc), ei = __expf(-acc), kv = s.Kh[r][d];
+            s.E[r][d] = e;
+            s.Qh[r][d] *= e;
+            s.Kh[r][d] = kv * e;
+            s.Ki[r][d] = kv * ei;
         }
     }
     __syncthreads();
@@ -114,22 +119,29 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
         float a = 0.f, pp = 0.f;
         if (sc <= r) {
             for (int d = 0; d < D; ++d) {
-                const float ks = s.k[sc][d] * s.Ei[sc][d], er = s.E[r][d];
-                a += s.k[r][d] * er * ks;
-                pp += s.q[r][d] * er * ks;
+                const float ks = s.Ki[sc][d];
+                a += s.Kh[r][d] * ks;
+                pp += s.Qh[r][d] * ks;
             }
         }
         s.A[r][sc] = sc < r ? a : 0.f;
         s.P[r][sc] = pp;
     }
     __syncthreads();
-    // T = (I + diag(beta) A)^-1 by forward substitution, one column per thread
-    for (int col = threadIdx.x; col < C; col += blockDim.x) {
+    // T = (I + diag(beta) A)^-1 by forward substitution, one column per thread,
+    // the column kept in registers
+    if (threadIdx.x < C) {
+        const int col = threadIdx.x;
+        float t[C];
+#pragma unroll
         for (int r = 0; r < C; ++r) {
             float acc = r == col ? 1.f : 0.f;
-            for (int u = 0; u < r; ++u) acc -= s.beta[r] * s.A[r][u] * s.T[u][col];
-            s.T[r][col] = acc;
+#pragma unroll
+            for (int u = 0; u < r; ++u) acc -= s.beta[r] * s.A[r][u] * t[u];
+            t[r] = acc;
         }
+#pragma unroll
+        for (int r = 0; r < C; ++r) s.T[r][col] = t[r];
     }
     __syncthreads();
 }
@@ -151,10 +163,10 @@ __global__ __launch_bounds__(256) void kda_bwd_prep_kernel(BwdArgs p) {
     for (int i = threadIdx.x; i < C * D; i += blockDim.x) {
         const int r = i / D, d = i % D;
         float w = 0.f;
-        for (int sc = 0; sc < C; ++sc) w += s.T[r][sc] * s.beta[sc] * s.k[sc][d] * s.E[sc][d];
+        for (int sc = 0; sc < C; ++sc) w += s.T[r][sc] * s.beta[sc] * s.Kh[sc][d];
         rec[Lay::W + i] = w;
-        rec[Lay::QH + i] = s.q[r][d] * s.E[r][d];
-        rec[Lay::KB + i] = s.k[r][d] * (s.E[C - 1][d] * s.Ei[r][d]);
+        rec[Lay::QH + i] = s.Qh[r][d];
+        rec[Lay::KB + i] = s.Ki[r][d] * s.E[C - 1][d];
     }
     for (int i = threadIdx.x; i < C * C; i += blockDim.x) {
         rec[Lay::P + i] = s.P[i / C][i % C];
@@ -709,7 +721,7 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     for (int i = tid; i < C * C; i += blockDim.x) {
         const int r = i / C, sc = i % C;
         float a = 0.f;
-        for (int d = 0; d < D; ++d) a += s.dW[r][d] * (o.k[sc][d] * o.E[sc][d]);
+        for (int d = 0; d < D; ++d) a += s.dW[r][d] * o.Kh[sc][d];
         s.dT[r][sc] = s.dTV[r][sc] + o.beta[sc] * a;
     }
     // (T^T dW)[r][d], held in dG until dG itself is formed below
@@ -739,7 +751,7 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     {
         const int r = tid / 16, l = tid % 16;   // blockDim.x == 16 * C
         float a = 0.f;
-        for (int d = l; d < D; d += 16) a += s.dG[r][d] * o.k[r][d] * o.E[r][d];
+        for (int d = l; d < D; d += 16) a += s.dG[r][d] * o.Kh[r][d];
         a = sum16(a);
         if (l == 0) {
             a += s.dbV[r];
@@ -753,54 +765,71 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
         (&s.dL[0][0])[i] *= o.beta[r];   // now dA
     }
     __syncthreads();
-    // dq, dk and dG per (r, d)
-    float dA_acc = 0.f;
-    for (int i = tid; i < C * D; i += blockDim.x) {
-        const int r = i / D, d = i % D;
-        const float Em = o.E[r][d], Ei = o.Ei[r][d], En = o.E[C - 1][d];
-        const float qv = o.q[r][d], kv = o.k[r][d];
-        float dqh = s.dQh[r][d];     // total dQ^
-        float dkh = 0.f;             // total dK^ (from A and W)
-        float dki = 0.f;             // total dKi (from A and P)
+    // dq, dk and dG per (r, d).  blockDim.x == 256, a multiple of D: each thread
+    // keeps one key channel d and takes the rows r0, r0 + 256/D, ...; the
+    // channel's decayed operands of all 16 tokens stay in registers.
+    {
+        const int d = tid % D, r0 = tid / D;
+        constexpr int RSTEP = 256 / D, RPT = C * D / 256;
+        float kis[C], khs[C], qhs[C];
+#pragma unroll
         for (int sc = 0; sc < C; ++sc) {
-            const float ks = o.k[sc][d], es = o.E[sc][d];
-            const float ki_s = ks * o.Ei[sc][d], kh_s = ks * es, qh_s = o.q[sc][d] * es;
-            dqh += s.dP[r][sc] * ki_s;
-            dkh += s.dL[r][sc] * ki_s;
-            dki += s.dL[sc][r] * kh_s + s.dP[sc][r] * qh_s;
+            kis[sc] = o.Ki[sc][d];
+            khs[sc] = o.Kh[sc][d];
+            qhs[sc] = o.Qh[sc][d];
         }
-        dkh += o.beta[r] * s.dG[r][d];               // through W = T diag(beta) K^
-        const float enr = En * Ei;                   // e^{G_n - G}
-        const float kb = kv * enr;
-        const float dq = dqh * Em;
-        const float dk = dkh * Em + dki * Ei + s.dKb[r][d] * enr;
-        const float dG = dqh * qv * Em + dkh * kv * Em - dki * kv * Ei - s.dKb[r][d] * kb;
-        if (r < n) {
-            const int64_t off = ((b * p.T + c * C + r) * H + h) * D + d;
-            p.dq[off] = dq;
-            p.dk[off] = dk;
+        const float En = o.E[C - 1][d];
+#pragma unroll 2
+        for (int jr = 0; jr < RPT; ++jr) {
+            const int r = r0 + RSTEP * jr;
+            float dqh = s.dQh[r][d];     // total dQ^
+            float dkh = 0.f;             // total dK^ (from A and W)
+            float dki = 0.f;             // total dKi (from A and P)
+#pragma unroll
+            for (int sc = 0; sc < C; ++sc) {
+                dqh += s.dP[r][sc] * kis[sc];
+                dkh += s.dL[r][sc] * kis[sc];
+                dki += s.dL[sc][r] * khs[sc] + s.dP[sc][r] * qhs[sc];
+            }
+            dkh += o.beta[r] * s.dG[r][d];               // through W = T diag(beta) K^
+            const float Em = o.E[r][d], Ei = 1.0f / Em;  // e^{G}, e^{-G}
+            const float dKb = s.dKb[r][d], kb = o.Ki[r][d] * En;   // Kb = k e^{G_n - G}
+            const float dq = dqh * Em;
+            const float dk = dkh * Em + dki * Ei + dKb * En * Ei;
+            const float dG = dqh * o.Qh[r][d] + dkh * o.Kh[r][d] - dki * o.Ki[r][d] - dKb * kb;
+            if (r < n) {
+                const int64_t off = ((b * p.T + c * C + r) * H + h) * D + d;
+                p.dq[off] = dq;
+                p.dk[off] = dk;
+            }
+            s.dG[r][d] = dG;   // this thread read (T^T dW)[r][d] above
         }
-        s.dG[r][d] = dG;   // this thread read (T^T dW)[r][d] above
     }
     __syncthreads();
     // dG_n from Kb = K e^{G_n - G} and from e^{G_n} (sum_j dS' S); G_n = G of the last row
     for (int d = tid; d < D; d += blockDim.x) {
         float a = s.dGn[d];
         const float En = o.E[C - 1][d];
-        for (int r = 0; r < C; ++r) a += s.dKb[r][d] * o.k[r][d] * (En * o.Ei[r][d]);
+        for (int r = 0; r < C; ++r) a += s.dKb[r][d] * o.Ki[r][d] * En;
         s.dG[C - 1][d] += a;
     }
     __syncthreads();
     // dg = reverse cumulative sum of dG; gate: g = g_min sigma(c z)
     const float cA = __expf(p.A[h]);
     const TI *z = static_cast<const TI *>(p.z);
+    float dA_acc = 0.f;
     for (int d = tid; d < D; d += blockDim.x) {
+        float zr[C];   // all of the channel's z loads are issued before the scan
+#pragma unroll
+        for (int r = 0; r < C; ++r)
+            zr[r] = r < n ? to_f32(z[((b * p.T + c * C + r) * H + h) * D + d]) : 0.f;
         float acc = 0.f;
+#pragma unroll
         for (int r = C - 1; r >= 0; --r) {
             acc += s.dG[r][d];
             if (r < n) {
                 const int64_t off = ((b * p.T + c * C + r) * H + h) * D + d;
-                const float xz = cA * to_f32(z[off]);
+                const float xz = cA * zr[r];
                 const float sg = sigmoidf_(xz);
                 const float dx = acc * kGMin * sg * (1.0f - sg);
                 p.dz[off] = cA * dx;
@@ -808,13 +837,22 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
             }
         }
     }
-    // the chunk's share of dA: block sum in a fixed order
-    __shared__ float red[256];
+    // the chunk's share of dA: block sum in a fixed order (16 partial sums of
+    // 16 consecutive threads each, then their sum)
+    __shared__ float red[256 + 16];
     red[tid] = dA_acc;
+    __syncthreads();
+    if (tid < 16) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a += red[16 * tid + i];
+        red[256 + tid] = a;
+    }
     __syncthreads();
     if (tid == 0) {
         float a = 0.f;
-        for (int i = 0; i < (int)blockDim.x; ++i) a += red[i];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a += red[256 + i];
         p.dA_part[x] = a;
     }
 }
