@@ -1,8 +1,8 @@
 """KDA benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk 16|64] [--no-cpu]
-                    [--no-decode] [--no-varlen] [--no-prologue] [--decode-reps R]
-                    [--calib-mib M]
+                    [--no-decode] [--no-varlen] [--no-prologue] [--no-backward]
+                    [--no-long] [--decode-reps R] [--calib-mib M]
 
 A step is one chunkwise prefill over the K3 head-shape workload (B=1, H=96,
 T=4096, dk=dv=128, bf16 inputs, fp32 state, S0 ~ N(0, 0.02^2)) with inputs
@@ -25,6 +25,10 @@ The fp64 oracle is timed on the host cores over the full prefill workload
 each, inputs drawn on the device; the million-token head share also split
 into 4 and 8 segments (kda_prefill_split).  ``timing`` gives the median and minimum
 per-launch time of 10 equal segments of the timed steps.
+
+``backward`` times kda_prefill_bwd on the same workload: gradients of q, k,
+v, z, beta, A and S0 from seeded dL/do and dL/dS_T (the forward is rerun with
+16-token state checkpoints inside the call).
 
 ``prologue`` times the layer's prologue on raw inputs of the same shapes
 (short convolutions of width 4, SiLU, q/k L2 norm, continued sequences): the
@@ -529,7 +533,8 @@ def main(argv=None):
             "workload": f"{w.name}: gradients of q, k, v, z, beta, A, S0 from dL/do and "
                         f"dL/dS_T (B={w.B} H={w.H} T={w.T} d={w.dk}, bf16 in, fp32 gradients)",
             "workspace_bytes": wsb,
-            "kernels": "forward rerun with 16-token checkpoints + kda_bwd_prep/chain/grad/dA"}
+            "kernels": "forward rerun with 16-token checkpoints, then kda_bwd_prep, "
+                       "kda_bwd_dstate, kda_bwd_part, kda_bwd_grad, kda_bwd_dA"}
     if not args.no_long:
         result["long"] = time_long(torch, kda, 3)
     if args.calib_mib > 0:
