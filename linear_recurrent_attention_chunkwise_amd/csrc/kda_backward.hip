@@ -459,11 +459,13 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, bf16
         Frag<bf16> dSf[NDT];
 #pragma unroll
         for (int i = 0; i < NDT; ++i) dSf[i] = acc_frag<bf16>(dS[i]);
-        bf16 *out = dsp + (bh * nchunk + c) * (int64_t)(BD * BD);
+        // stored in 4-row blocks, element (d, j) at ((d/4)*D + j)*4 + d%4: a
+        // lane's four rows of a tile are one 8-byte group, and the 16 lanes of
+        // a row group write 128 contiguous bytes
+        bf16 *out = dsp + (bh * nchunk + c) * (int64_t)(BD * BD) + (g * BD + jw + n) * 4;
 #pragma unroll
         for (int i = 0; i < NDT; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[(16 * i + 4 * g + e) * BD + jw + n] = dSf[i].v[e];
+            *reinterpret_cast<bf16x4 *>(out + i * 4 * 4 * BD) = dSf[i].v;
         f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = {0.f, 0.f, 0.f, 0.f};
         mma16(ua, lds_frag(&B.PT[0][0], BLT, 0, lane), dOf);
 #pragma unroll
@@ -519,32 +521,43 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
                *betag = static_cast<const bf16 *>(p.beta);
     float *part = p.part + x * (int64_t)PL::SIZE;
 
-    // ---- stage: S, dS' (fp32 -> bf16) and sum_j dS' S per key row ----
+    // ---- stage: S (fp32 -> bf16), dS' (bf16) and sum_j dS' S per key
+    // row.  A thread takes 4 x 4 blocks, rows d0..d0+3 by columns j0..j0+3, so
+    // that it holds both operands of its 16 products; 32 consecutive threads
+    // cover one block row and reduce it in a fixed order.
     {
         const float *Sin = c == 0 ? (p.S0 ? p.S0 + bh * (int64_t)(BD * BD) : nullptr)
                                   : p.ckpt + ((b * nfull + c - 1) * H + h) * (int64_t)(BD * BD);
-        const f32x4 *S4 = reinterpret_cast<const f32x4 *>(Sin);
-        const bf16x4 *D4 = reinterpret_cast<const bf16x4 *>(dsp + x * (int64_t)(BD * BD));
-        f32x4 sv[8], dv4[8];
+        const bf16 *Dt = dsp + x * (int64_t)(BD * BD);   // 4-row blocks, as dstate stores them
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            sv[u] = S4 ? S4[tid + NT * u] : f32x4{0.f, 0.f, 0.f, 0.f};
-            const bf16x4 t = D4[tid + NT * u];
-            dv4[u] = f32x4{(float)t[0], (float)t[1], (float)t[2], (float)t[3]};
-        }
+        for (int u = 0; u < 2; ++u) {
+            const int d0 = 4 * (tid / 32 + 16 * u), j0 = 4 * (tid % 32);
+            f32x4 sv[4];
+            bf16x4 tv[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int f = tid + NT * u, d = f / 32, j = 4 * (f % 32);
-            store_bf16x4(&s.S[d][j], sv[u][0], sv[u][1], sv[u][2], sv[u][3]);
-            *reinterpret_cast<bf16x4 *>(&s.dS[d][j]) = D4[tid + NT * u];
-            float a = sv[u][0] * dv4[u][0] + sv[u][1] * dv4[u][1] + sv[u][2] * dv4[u][2] +
-                      sv[u][3] * dv4[u][3];
-            a += __shfl_xor(a, 16, 32);
-            a += __shfl_xor(a, 8, 32);
-            a += __shfl_xor(a, 4, 32);
-            a += __shfl_xor(a, 2, 32);
-            a += __shfl_xor(a, 1, 32);
-            if ((tid & 31) == 0) part[PL::DGN + d] = a;
+            for (int e = 0; e < 4; ++e) {
+                sv[e] = Sin ? *reinterpret_cast<const f32x4 *>(Sin + (d0 + e) * BD + j0)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+                tv[e] = *reinterpret_cast<const bf16x4 *>(Dt + ((d0 / 4) * BD + j0 + e) * 4);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                store_bf16x4(&s.S[d0 + e][j0], sv[e][0], sv[e][1], sv[e][2], sv[e][3]);
+                *reinterpret_cast<bf16x4 *>(&s.dS[d0 + e][j0]) =
+                    bf16x4{tv[0][e], tv[1][e], tv[2][e], tv[3][e]};
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // row d0 + r: S[d0+r][j0+e] * dS'[d0+r][j0+e]
+                float a = sv[r][0] * (float)tv[0][r] + sv[r][1] * (float)tv[1][r] +
+                          sv[r][2] * (float)tv[2][r] + sv[r][3] * (float)tv[3][r];
+                a += __shfl_xor(a, 16, 32);
+                a += __shfl_xor(a, 8, 32);
+                a += __shfl_xor(a, 4, 32);
+                a += __shfl_xor(a, 2, 32);
+                a += __shfl_xor(a, 1, 32);
+                if ((tid & 31) == 0) part[PL::DGN + d0 + r] = a;
+            }
         }
     }
     // ---- stage: the chunk's W, Kb, T, P, beta, V, dO ----
