@@ -75,6 +75,24 @@ template <typename TI, int D> struct ChunkOps {
     float beta[C];
 };
 
+// fp32 K16 fragments of an LDS matrix M with row stride ld (see kda_device.h):
+// rowfrag -- lane (m, g) holds M[r0 + m][k0 + 4g + e]  (A operand M, or B = M^T)
+// colfrag -- lane (n, g) holds M[k0 + 4g + e][c0 + n]  (B operand M, or A = M^T)
+__device__ __forceinline__ Frag<float> rowfrag(const float *M, int ld, int r0, int k0, int lane) {
+    Frag<float> f;
+    const float *p = M + (r0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.v[e] = p[e];
+    return f;
+}
+__device__ __forceinline__ Frag<float> colfrag(const float *M, int ld, int k0, int c0, int lane) {
+    Frag<float> f;
+    const float *p = M + (k0 + 4 * (lane >> 4)) * ld + c0 + (lane & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.v[e] = p[e * ld];
+    return f;
+}
+
 template <typename TI, int D>
 __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64_t h, int64_t c,
                           int n) {
@@ -113,19 +131,27 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
         }
     }
     __syncthreads();
-    // A[r][s] = sum_d k_r k_s e^{G_r - G_s} (s < r),  P[r][s] = sum_d q_r k_s e^{G_r - G_s} (s <= r)
-    for (int i = threadIdx.x; i < C * C; i += blockDim.x) {
-        const int r = i / C, sc = i % C;
-        float a = 0.f, pp = 0.f;
-        if (sc <= r) {
-            for (int d = 0; d < D; ++d) {
-                const float ks = s.Ki[sc][d];
-                a += s.Kh[r][d] * ks;
-                pp += s.Qh[r][d] * ks;
+    // A[r][s] = sum_d k_r k_s e^{G_r - G_s} (s < r),  P[r][s] = sum_d q_r k_s e^{G_r - G_s} (s <= r):
+    // Kh Ki^T and Qh Ki^T on fp32 matrix-core tiles, wave 0 and wave 1
+    {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        const int g = lane >> 4, nn = lane & 15;
+        constexpr int LDD = rowpad<D>();
+        if (wave < 2) {
+            const float *X = wave == 0 ? &s.Kh[0][0] : &s.Qh[0][0];
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < D; k0 += 16)
+                mma16(acc, rowfrag(X, LDD, 0, k0, lane), rowfrag(&s.Ki[0][0], LDD, 0, k0, lane));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                if (wave == 0)
+                    s.A[r][nn] = nn < r ? acc[e] : 0.f;
+                else
+                    s.P[r][nn] = nn <= r ? acc[e] : 0.f;
             }
         }
-        s.A[r][sc] = sc < r ? a : 0.f;
-        s.P[r][sc] = pp;
     }
     __syncthreads();
     // T = (I + diag(beta) A)^-1 by forward substitution, one column per thread,
@@ -681,8 +707,9 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
 template <typename TI, int D> struct GradLds {
     ChunkOps<TI, D> o;
     float dQh[C][rowpad<D>()], dKb[C][rowpad<D>()], dW[C][rowpad<D>()], dG[C][rowpad<D>()];
-    float dP[C][C], dTV[C][C], dT[C][C], M1[C][C], dL[C][C];
+    float dP[C][C + 1], dTV[C][C + 1], dT[C][C + 1], M1[C][C + 1], dL[C][C + 1];
     float dbV[C], dGn[D];
+    float dbk[4][C];   // per-wave sums over d of (T^T dW)[r][d] Kh[r][d]
 };
 
 template <typename TI, int D, int NS>
@@ -715,8 +742,8 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
             bb += part[q * PL::SIZE + PL::DTV + i];
         }
         const int r = i / C, sc = i % C;
-        (&s.dP[0][0])[i] = sc <= r ? a : 0.f;   // P is lower triangular
-        (&s.dTV[0][0])[i] = bb;
+        s.dP[r][sc] = sc <= r ? a : 0.f;   // P is lower triangular
+        s.dTV[r][sc] = bb;
     }
     for (int r = tid; r < C; r += blockDim.x) {
         float a = 0.f;
@@ -730,19 +757,41 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     }
     __syncthreads();
     auto &o = s.o;
-    // dT = dW (beta K^)^T + dU (beta V)^T
-    for (int i = tid; i < C * C; i += blockDim.x) {
-        const int r = i / C, sc = i % C;
-        float a = 0.f;
-        for (int d = 0; d < D; ++d) a += s.dW[r][d] * o.Kh[sc][d];
-        s.dT[r][sc] = s.dTV[r][sc] + o.beta[sc] * a;
+    const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, nn = lane & 15;
+    constexpr int LDD = rowpad<D>(), LDC = C + 1, NDT = D / 16, TPW = (NDT + 3) / 4;
+    // dT = dW (beta K^)^T + dU (beta V)^T: a 16 x 16 tile over d (wave 0)
+    if (wave == 0) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 16)
+            mma16(acc, rowfrag(&s.dW[0][0], LDD, 0, k0, lane), rowfrag(&o.Kh[0][0], LDD, 0, k0, lane));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            s.dT[r][nn] = s.dTV[r][nn] + o.beta[nn] * acc[e];
+        }
     }
-    // (T^T dW)[r][d], held in dG until dG itself is formed below
-    for (int i = tid; i < C * D; i += blockDim.x) {
-        const int r = i / D, d = i % D;
-        float a = 0.f;
-        for (int u = 0; u < C; ++u) a += o.T[u][r] * s.dW[u][d];
-        s.dG[r][d] = a;
+    // T^T dW: wave w takes the 16-column tiles w, w+4, ..., keeps them in
+    // registers for dk below, and sums its share of (T^T dW) . K^ per row
+    f32x4 tdw[TPW];
+    {
+        float part_b[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int t = wave + 4 * j;
+            tdw[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (t < NDT) {
+                mma16(tdw[j], colfrag(&o.T[0][0], LDC, 0, 0, lane),
+                      colfrag(&s.dW[0][0], LDD, 0, 16 * t, lane));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) part_b[e] += tdw[j][e] * o.Kh[4 * g + e][16 * t + nn];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v = sum16(part_b[e]);
+            if (nn == 0) s.dbk[wave][4 * g + e] = v;
+        }
     }
     __syncthreads();
     // M1 = T^T dT;  dL = -M1 T^T (strictly lower)
@@ -760,62 +809,53 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
         s.dL[r][sc] = sc < r ? -a : 0.f;
     }
     __syncthreads();
-    // dbeta: V part, K^ part (through W), L part; 16 lanes per token row
-    {
-        const int r = tid / 16, l = tid % 16;   // blockDim.x == 16 * C
-        float a = 0.f;
-        for (int d = l; d < D; d += 16) a += s.dG[r][d] * o.Kh[r][d];
-        a = sum16(a);
-        if (l == 0) {
-            a += s.dbV[r];
-            for (int sc = 0; sc < C; ++sc) a += s.dL[r][sc] * o.A[r][sc];
-            if (r < n) p.dbeta[(b * p.T + c * C + r) * H + h] = a;
-        }
+    // dbeta: V part, K^ part (through W), L part
+    if (tid < C) {
+        const int r = tid;
+        float a = s.dbV[r] + ((s.dbk[0][r] + s.dbk[1][r]) + (s.dbk[2][r] + s.dbk[3][r]));
+        for (int sc = 0; sc < C; ++sc) a += s.dL[r][sc] * o.A[r][sc];
+        if (r < n) p.dbeta[(b * p.T + c * C + r) * H + h] = a;
     }
     __syncthreads();
     for (int i = tid; i < C * C; i += blockDim.x) {
-        const int r = i / C;
-        (&s.dL[0][0])[i] *= o.beta[r];   // now dA
+        const int r = i / C, sc = i % C;
+        s.dL[r][sc] *= o.beta[r];   // now dA
     }
     __syncthreads();
-    // dq, dk and dG per (r, d).  blockDim.x == 256, a multiple of D: each thread
-    // keeps one key channel d and takes the rows r0, r0 + 256/D, ...; the
-    // channel's decayed operands of all 16 tokens stay in registers.
-    {
-        const int d = tid % D, r0 = tid / D;
-        constexpr int RSTEP = 256 / D, RPT = C * D / 256;
-        float kis[C], khs[C], qhs[C];
+    // dq, dk and dG on the same column tiles:
+    //   dQ^ += dP Ki,  dK^ = dA Ki + beta (T^T dW),  dKi = dA^T K^ + dP^T Q^
+    // (products over the 16 tokens s on fp32 matrix-core tiles)
 #pragma unroll
-        for (int sc = 0; sc < C; ++sc) {
-            kis[sc] = o.Ki[sc][d];
-            khs[sc] = o.Kh[sc][d];
-            qhs[sc] = o.Qh[sc][d];
-        }
-        const float En = o.E[C - 1][d];
-#pragma unroll 2
-        for (int jr = 0; jr < RPT; ++jr) {
-            const int r = r0 + RSTEP * jr;
-            float dqh = s.dQh[r][d];     // total dQ^
-            float dkh = 0.f;             // total dK^ (from A and W)
-            float dki = 0.f;             // total dKi (from A and P)
+    for (int j = 0; j < TPW; ++j) {
+        const int t = wave + 4 * j;
+        if (t < NDT) {
+            const int d = 16 * t + nn;
+            f32x4 dqh, dkh = {0.f, 0.f, 0.f, 0.f}, dki = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int sc = 0; sc < C; ++sc) {
-                dqh += s.dP[r][sc] * kis[sc];
-                dkh += s.dL[r][sc] * kis[sc];
-                dki += s.dL[sc][r] * khs[sc] + s.dP[sc][r] * qhs[sc];
+            for (int e = 0; e < 4; ++e) dqh[e] = s.dQh[4 * g + e][d];
+            const Frag<float> kiB = colfrag(&o.Ki[0][0], LDD, 0, 16 * t, lane);
+            mma16(dqh, rowfrag(&s.dP[0][0], LDC, 0, 0, lane), kiB);
+            mma16(dkh, rowfrag(&s.dL[0][0], LDC, 0, 0, lane), kiB);
+            mma16(dki, colfrag(&s.dL[0][0], LDC, 0, 0, lane), colfrag(&o.Kh[0][0], LDD, 0, 16 * t, lane));
+            mma16(dki, colfrag(&s.dP[0][0], LDC, 0, 0, lane), colfrag(&o.Qh[0][0], LDD, 0, 16 * t, lane));
+            const float En = o.E[C - 1][d];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                const float dk_h = dkh[e] + o.beta[r] * tdw[j][e];   // through W = T diag(beta) K^
+                const float Em = o.E[r][d], Ei = 1.0f / Em;          // e^{G}, e^{-G}
+                const float dKb = s.dKb[r][d], kb = o.Ki[r][d] * En;  // Kb = k e^{G_n - G}
+                const float dq = dqh[e] * Em;
+                const float dk = dk_h * Em + dki[e] * Ei + dKb * En * Ei;
+                const float dG =
+                    dqh[e] * o.Qh[r][d] + dk_h * o.Kh[r][d] - dki[e] * o.Ki[r][d] - dKb * kb;
+                if (r < n) {
+                    const int64_t off = ((b * p.T + c * C + r) * H + h) * D + d;
+                    p.dq[off] = dq;
+                    p.dk[off] = dk;
+                }
+                s.dG[r][d] = dG;
             }
-            dkh += o.beta[r] * s.dG[r][d];               // through W = T diag(beta) K^
-            const float Em = o.E[r][d], Ei = 1.0f / Em;  // e^{G}, e^{-G}
-            const float dKb = s.dKb[r][d], kb = o.Ki[r][d] * En;   // Kb = k e^{G_n - G}
-            const float dq = dqh * Em;
-            const float dk = dkh * Em + dki * Ei + dKb * En * Ei;
-            const float dG = dqh * o.Qh[r][d] + dkh * o.Kh[r][d] - dki * o.Ki[r][d] - dKb * kb;
-            if (r < n) {
-                const int64_t off = ((b * p.T + c * C + r) * H + h) * D + d;
-                p.dq[off] = dq;
-                p.dk[off] = dk;
-            }
-            s.dG[r][d] = dG;   // this thread read (T^T dW)[r][d] above
         }
     }
     __syncthreads();
