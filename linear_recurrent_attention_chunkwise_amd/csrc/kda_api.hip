@@ -80,7 +80,7 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
                         const float *S0, void *o, float *S_T, int32_t ckpt_every,
                         float *ckpt, int64_t n_ckpt, void *workspace, size_t workspace_bytes,
                         void *stream, int32_t dv_per_block, int mode = 0,
-                        bool check_only = false) {
+                        bool check_only = false, bool ckpt_blocked = false) {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || n_ckpt < 0 || ckpt_every < 0)
         return KDA_ERR_SHAPE;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -114,6 +114,7 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
     if (want_ckpt && !role_split && !kda::prefill_ckpt_supported(dtype, D, chunk, dvb))
         return KDA_ERR_UNSUPPORTED;
     if (mode != 0 && (!role_split || dvb != 64 || want_ckpt)) return KDA_ERR_UNSUPPORTED;
+    if (ckpt_blocked && want_ckpt && !role_split) return KDA_ERR_UNSUPPORTED;
     if (!A || !S_T) return KDA_ERR_NULL;
     if (bth > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL;
     if (ckpt_every > 0 && n_ckpt > 0 && !ckpt) return KDA_ERR_NULL;
@@ -161,6 +162,7 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
     }
     a.ckpt_every = ckpt_every > 0 && n_ckpt > 0 ? ckpt_every : 0;
     a.ckpt = a.ckpt_every > 0 ? ckpt : nullptr;
+    a.ckpt_blocked = ckpt_blocked;
     a.n_ckpt = n_ckpt;
     a.mode = mode;
     a.stream = (hipStream_t)stream;
@@ -761,10 +763,12 @@ kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
     float *ckpt = bh > 0 ? reinterpret_cast<float *>(ws + lay.ckpt) : nullptr;
     // forward with a checkpoint at every chunk boundary
     if (bth > 0) {
+        // bf16 d = 128: checkpoints in the 4-row block layout the MFMA backward reads
+        const bool blocked = kda::bwd_dsp_bytes(dtype, D) > 0;
         kda_status st = prefill_impl(dtype, B, T, H, dk, dv, kBwdChunk, nullptr, q, k, v, z, beta,
                                      A, S0, ws + lay.o, reinterpret_cast<float *>(ws + lay.S_T),
                                      nfull > 0 ? kBwdChunk : 0, ckpt, B * nfull, nullptr, 0,
-                                     stream, 0);
+                                     stream, 0, 0, false, blocked);
         if (st != KDA_OK) return st;
     }
     kda::BwdArgs a;

@@ -558,14 +558,26 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int d0 = 4 * (tid / 32 + 16 * u), j0 = 4 * (tid % 32);
-            f32x4 sv[4];
-            bf16x4 tv[4];
+            f32x4 sv[4];   // sv[r] = S[d0 + r][j0 .. j0+3]
+            bf16x4 tv[4];  // tv[e] = dS'[d0 .. d0+3][j0 + e]
+            if (c == 0) {
+                // S0 is the caller's, row-major
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sv[e] = Sin ? *reinterpret_cast<const f32x4 *>(Sin + (d0 + e) * BD + j0)
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
-                tv[e] = *reinterpret_cast<const bf16x4 *>(Dt + ((d0 / 4) * BD + j0 + e) * 4);
+                for (int e = 0; e < 4; ++e)
+                    sv[e] = Sin ? *reinterpret_cast<const f32x4 *>(Sin + (d0 + e) * BD + j0)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {
+                // the forward rerun's checkpoints are in 4-row blocks
+                f32x4 cv[4];   // cv[e] = S[d0 .. d0+3][j0 + e]
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    cv[e] = *reinterpret_cast<const f32x4 *>(Sin + ((d0 / 4) * BD + j0 + e) * 4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sv[r] = f32x4{cv[0][r], cv[1][r], cv[2][r], cv[3][r]};
             }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                tv[e] = *reinterpret_cast<const bf16x4 *>(Dt + ((d0 / 4) * BD + j0 + e) * 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 store_bf16x4(&s.S[d0 + e][j0], sv[e][0], sv[e][1], sv[e][2], sv[e][3]);

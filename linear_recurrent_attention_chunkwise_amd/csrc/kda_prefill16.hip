@@ -62,6 +62,7 @@ struct Prefill16Params {
     float *ckpt;         // state checkpoints [n_ckpt, H, D, D], or NULL
     int64_t n_ckpt;
     int ckpt_every;      // tokens between checkpoints (0: none)
+    int ckpt_blocked;    // 1: checkpoints in 4-row blocks ((d/4)*D + j)*4 + d%4
 };
 
 template <int NCW, int NPW, int NSLOT>
@@ -277,13 +278,23 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
                     // one lane offset, row offsets as scalars: no per-store addresses
                     const auto crs = make_rsrc(prm.ckpt + (ck_row * H + h) * (int64_t)(D * D),
                                                (int64_t)(D * D) * 4);
-                    const int voff = (4 * g * D + jw + n) * 4;
+                    if (prm.ckpt_blocked) {
+                        // rows 16i+4g .. 16i+4g+3 of column jw+n: one 16-byte group
+                        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                        const int voff = ((g * D + jw + n) * 4) * 4;
 #pragma unroll
-                    for (int i = 0; i < NDT; ++i)
+                        for (int i = 0; i < NDT; ++i)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                __builtin_bit_cast(u32x4, S[i]), crs, voff, i * 4 * D * 4 * 4, 0);
+                    } else {
+                        const int voff = (4 * g * D + jw + n) * 4;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[i][e]), crs, voff,
-                                                                  (16 * i + e) * D * 4, 0);
+                        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[i][e]), crs,
+                                                                      voff, (16 * i + e) * D * 4, 0);
+                    }
                 }
                 ++ck_row;
                 ck_next += every;
@@ -539,6 +550,7 @@ static hipError_t launch_p16(const PrefillArgs &a) {
     prm.ckpt = a.ckpt;
     prm.n_ckpt = a.n_ckpt;
     prm.ckpt_every = a.ckpt_every;
+    prm.ckpt_blocked = a.ckpt_blocked ? 1 : 0;
     const int64_t nblk = a.B * a.H * prm.nsplit;
     hipLaunchKernelGGL((kda_prefill16_kernel<NCW, NPW, NSLOT, CKPT, MODE>), dim3((unsigned)nblk),
                        dim3(64 * (NCW + NPW)), 0, a.stream, prm);
