@@ -428,9 +428,11 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, bf16
             reinterpret_cast<const f32x4 *>(p.prep + (bh * nchunk + c) * (int64_t)Lay::SIZE);
 #pragma unroll
         for (int u = 0; u < 2048 / 4 / NT; ++u) {
-            rw[u] = rec[Lay::W / 4 + tid + NT * u];
-            rq[u] = rec[Lay::QH / 4 + tid + NT * u];
-            rk[u] = rec[Lay::KB / 4 + tid + NT * u];
+            // W and Q^ in (token, 4-column group) order, Kb row-major
+            const int f = tid + NT * u, r = f % C, q4 = f / C;
+            rw[u] = rec[Lay::W / 4 + r * (BD / 4) + q4];
+            rq[u] = rec[Lay::QH / 4 + r * (BD / 4) + q4];
+            rk[u] = rec[Lay::KB / 4 + f];
         }
         if (tid < C * C / 4) rp = rec[Lay::P / 4 + tid];
         if (tid < BD / 4) rg = rec[Lay::GN / 4 + tid];
@@ -440,6 +442,12 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, bf16
         for (int u = 0; u < 2048 / 4 / NT; ++u) {
             const int f = tid + NT * u, r = f / (BD / 4), d = 4 * (f % (BD / 4));
             store_bf16x4(&B.Kb[r][d], rk[u][0], rk[u][1], rk[u][2], rk[u][3]);
+        }
+        // Q^ and W go in transposed: lanes take consecutive tokens r of one
+        // 4-column group, so their 2-byte writes fall in distinct LDS banks
+#pragma unroll
+        for (int u = 0; u < 2048 / 4 / NT; ++u) {
+            const int f = tid + NT * u, r = f % C, d = 4 * (f / C);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 B.QhT[d + e][r] = (bf16)rq[u][e];
@@ -855,7 +863,7 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g + e;
                 const float dk_h = dkh[e] + o.beta[r] * tdw[j][e];   // through W = T diag(beta) K^
-                const float Em = o.E[r][d], Ei = 1.0f / Em;          // e^{G}, e^{-G}
+                const float Em = o.E[r][d], Ei = 1.0f / Em;   // e^{G}, e^{-G}
                 const float dKb = s.dKb[r][d], kb = o.Ki[r][d] * En;  // Kb = k e^{G_n - G}
                 const float dq = dqh[e] * Em;
                 const float dk = dk_h * Em + dki[e] * Ei + dKb * En * Ei;
