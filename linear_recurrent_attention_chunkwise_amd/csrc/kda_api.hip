@@ -695,7 +695,8 @@ bool bwd_layout(int dtype, int64_t B, int64_t T, int64_t H, int64_t D, BwdLayout
     lay->o = 0;
     lay->S_T = round256(nin * esz);
     lay->ckpt = lay->S_T + round256(nst * 4);
-    lay->prep = lay->ckpt + round256(nck * 4);
+    // the MFMA backward (bf16, d = 128) keeps its checkpoints in bf16
+    lay->prep = lay->ckpt + round256(nck * (kda::bwd_dsp_bytes(dtype, D) > 0 ? 2 : 4));
     lay->part = lay->prep + round256(nprep * 4);
     lay->dA = lay->part + round256(npart * 4);
     lay->dsp = lay->dA + round256(units * 4);

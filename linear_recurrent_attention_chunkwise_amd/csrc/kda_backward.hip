@@ -560,8 +560,10 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
     // that it holds both operands of its 16 products; 32 consecutive threads
     // cover one block row and reduce it in a fixed order.
     {
-        const float *Sin = c == 0 ? (p.S0 ? p.S0 + bh * (int64_t)(BD * BD) : nullptr)
-                                  : p.ckpt + ((b * nfull + c - 1) * H + h) * (int64_t)(BD * BD);
+        const float *Sin = c == 0 && p.S0 ? p.S0 + bh * (int64_t)(BD * BD) : nullptr;
+        const bf16 *Ck = c >= 1 ? reinterpret_cast<const bf16 *>(p.ckpt) +
+                                      ((b * nfull + c - 1) * H + h) * (int64_t)(BD * BD)
+                                : nullptr;
         const bf16 *Dt = dsp + x * (int64_t)(BD * BD);   // 4-row blocks, as dstate stores them
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -575,13 +577,14 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
                     sv[e] = Sin ? *reinterpret_cast<const f32x4 *>(Sin + (d0 + e) * BD + j0)
                                 : f32x4{0.f, 0.f, 0.f, 0.f};
             } else {
-                // the forward rerun's checkpoints are in 4-row blocks
-                f32x4 cv[4];   // cv[e] = S[d0 .. d0+3][j0 + e]
+                // the forward rerun's checkpoints: bf16 in 4-row blocks
+                bf16x4 cv[4];   // cv[e] = S[d0 .. d0+3][j0 + e]
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    cv[e] = *reinterpret_cast<const f32x4 *>(Sin + ((d0 / 4) * BD + j0 + e) * 4);
+                    cv[e] = *reinterpret_cast<const bf16x4 *>(Ck + ((d0 / 4) * BD + j0 + e) * 4);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sv[r] = f32x4{cv[0][r], cv[1][r], cv[2][r], cv[3][r]};
+                for (int r = 0; r < 4; ++r)
+                    sv[r] = f32x4{(float)cv[0][r], (float)cv[1][r], (float)cv[2][r], (float)cv[3][r]};
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e)

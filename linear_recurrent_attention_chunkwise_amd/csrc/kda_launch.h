@@ -32,9 +32,9 @@ struct PrefillArgs {
     int ckpt_every;
     float *ckpt;
     int64_t n_ckpt;
-    // Checkpoint layout: false -- row-major [D][D]; true -- 4-row blocks, state
-    // element (d, j) at ((d/4)*D + j)*4 + d%4 (the backward's own rerun; role-
-    // split kernel only).
+    // Checkpoint layout: false -- fp32 row-major [D][D]; true -- bf16 in 4-row
+    // blocks, state element (d, j) at ((d/4)*D + j)*4 + d%4 (the backward's own
+    // rerun; role-split kernel only).
     bool ckpt_blocked = false;
     // 0: the prefill.  1: final states only (o not written).  2: the state
     // transition of each sequence (v read as zero, o not written).  Modes 1

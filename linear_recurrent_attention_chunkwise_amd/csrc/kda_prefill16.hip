@@ -62,7 +62,7 @@ struct Prefill16Params {
     float *ckpt;         // state checkpoints [n_ckpt, H, D, D], or NULL
     int64_t n_ckpt;
     int ckpt_every;      // tokens between checkpoints (0: none)
-    int ckpt_blocked;    // 1: checkpoints in 4-row blocks ((d/4)*D + j)*4 + d%4
+    int ckpt_blocked;    // 1: bf16 checkpoints in 4-row blocks ((d/4)*D + j)*4 + d%4
 };
 
 template <int NCW, int NPW, int NSLOT>
@@ -279,13 +279,17 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
                     const auto crs = make_rsrc(prm.ckpt + (ck_row * H + h) * (int64_t)(D * D),
                                                (int64_t)(D * D) * 4);
                     if (prm.ckpt_blocked) {
-                        // rows 16i+4g .. 16i+4g+3 of column jw+n: one 16-byte group
-                        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-                        const int voff = ((g * D + jw + n) * 4) * 4;
+                        // bf16, rows 16i+4g .. 16i+4g+3 of column jw+n: one 8-byte group
+                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                        const auto brs = make_rsrc(reinterpret_cast<bf16 *>(prm.ckpt) +
+                                                       (ck_row * H + h) * (int64_t)(D * D),
+                                                   (int64_t)(D * D) * 2);
+                        const int voff = ((g * D + jw + n) * 4) * 2;
 #pragma unroll
                         for (int i = 0; i < NDT; ++i)
-                            __builtin_amdgcn_raw_buffer_store_b128(
-                                __builtin_bit_cast(u32x4, S[i]), crs, voff, i * 4 * D * 4 * 4, 0);
+                            __builtin_amdgcn_raw_buffer_store_b64(
+                                u32x2{pack_bf16(S[i][0], S[i][1]), pack_bf16(S[i][2], S[i][3])},
+                                brs, voff, i * 4 * D * 4 * 2, 0);
                     } else {
                         const int voff = (4 * g * D + jw + n) * 4;
 #pragma unroll
