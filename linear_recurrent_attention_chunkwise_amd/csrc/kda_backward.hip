@@ -531,6 +531,7 @@ struct PartLds {
     bf16 S[BD][BLD], dS[BD][BLD];          // chunk-entry state, incoming dS' [d][j]
     bf16 W[C][BLD], Kb[C][BLD];            // [r][d]
     bf16 V[C][BLD], dO[C][BLD], U[C][BLD], dU[C][BLD];   // [r][j]
+    bf16 Ulo[C][BLD], dUlo[C][BLD];        // U - bf16(U), dU - bf16(dU): U, dU to ~16 bits
     bf16 Tb[C][BLT], PT[C][BLT], TT[C][BLT];            // T diag(beta), P^T, T^T
     float beta[C];
     float dbV[8][C];
@@ -667,13 +668,23 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
                   frag_rows(&s.dS[0][0], BLD, 16 * i + 16, jw + n, lane));
         }
         const f32x4 U = ta - tb, dU = da + db;
+        // U and dU enter the products below as bf16 pairs hi + lo
+        const Frag<bf16> dUh = acc_frag<bf16>(dU);
+        f32x4 dUl4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dUl4[e] = dU[e] - (float)dUh.v[e];
         f32x4 BV = {0.f, 0.f, 0.f, 0.f};
-        mma16(BV, lds_frag(&s.TT[0][0], BLT, 0, lane), acc_frag<bf16>(dU));
+        const Frag<bf16> TTf = lds_frag(&s.TT[0][0], BLT, 0, lane);
+        mma16(BV, TTf, dUh);
+        mma16(BV, TTf, acc_frag<bf16>(dUl4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            s.U[r][jw + n] = (bf16)U[e];
-            s.dU[r][jw + n] = (bf16)dU[e];
+            const bf16 uh = (bf16)U[e];
+            s.U[r][jw + n] = uh;
+            s.Ulo[r][jw + n] = (bf16)(U[e] - (float)uh);
+            s.dU[r][jw + n] = dUh.v[e];
+            s.dUlo[r][jw + n] = (bf16)dUl4[e];
             if (r < nv) p.dv[(row0 + (int64_t)r * H) * BD + jw + n] = s.beta[r] * BV[e];
             const float part_bv = sum16(BV[e] * (float)Vf.v[e]);
             if (n == 0) s.dbV[wave][r] = part_bv;
@@ -693,8 +704,14 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
                   s0, s1);
             mma32(aw, lds_frag(&s.dU[0][0], BLD, 16 * i, lane), lds_frag(&s.dU[0][0], BLD, 16 * i + 16, lane),
                   s0, s1);
+            mma32(aw, lds_frag(&s.dUlo[0][0], BLD, 16 * i, lane),
+                  lds_frag(&s.dUlo[0][0], BLD, 16 * i + 16, lane), s0, s1);
+            const Frag<bf16> t0 = lds_frag(&s.dS[dw][0], BLD, 16 * i, lane),
+                             t1 = lds_frag(&s.dS[dw][0], BLD, 16 * i + 16, lane);
             mma32(ak, lds_frag(&s.U[0][0], BLD, 16 * i, lane), lds_frag(&s.U[0][0], BLD, 16 * i + 16, lane),
-                  lds_frag(&s.dS[dw][0], BLD, 16 * i, lane), lds_frag(&s.dS[dw][0], BLD, 16 * i + 16, lane));
+                  t0, t1);
+            mma32(ak, lds_frag(&s.Ulo[0][0], BLD, 16 * i, lane),
+                  lds_frag(&s.Ulo[0][0], BLD, 16 * i + 16, lane), t0, t1);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -705,13 +722,19 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
         }
         if (wave == 0 || wave == 1) {
             // dP = dO U^T (wave 0);  dT's V part = dU (beta V)^T (wave 1)
+            // (U, dU as hi + lo pairs)
             const bf16 *A = wave == 0 ? &s.dO[0][0] : &s.dU[0][0];
             const bf16 *Bm = wave == 0 ? &s.U[0][0] : &s.V[0][0];
+            const bf16 *A2 = wave == 0 ? &s.dO[0][0] : &s.dUlo[0][0];
+            const bf16 *B2 = wave == 0 ? &s.Ulo[0][0] : &s.V[0][0];
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < BD / 16; i += 2)
+            for (int i = 0; i < BD / 16; i += 2) {
                 mma32(acc, lds_frag(A, BLD, 16 * i, lane), lds_frag(A, BLD, 16 * i + 16, lane),
                       lds_frag(Bm, BLD, 16 * i, lane), lds_frag(Bm, BLD, 16 * i + 16, lane));
+                mma32(acc, lds_frag(A2, BLD, 16 * i, lane), lds_frag(A2, BLD, 16 * i + 16, lane),
+                      lds_frag(B2, BLD, 16 * i, lane), lds_frag(B2, BLD, 16 * i + 16, lane));
+            }
             const float sc = wave == 0 ? 1.f : s.beta[n];
 #pragma unroll
             for (int e = 0; e < 4; ++e)

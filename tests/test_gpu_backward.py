@@ -80,6 +80,9 @@ CASES = [
     ("f32", 16, 2, 2, (1, 15, 16, 17, 50)),
     ("f32", 128, 1, 2, (16, 40, 100)),
     ("bf16", 128, 1, 2, (33, 200)),
+    # the matrix-core path (bf16, d = 128) with several sequences (per-sequence
+    # checkpoint and state indexing), one partial chunk, exactly one chunk
+    ("bf16", 128, 2, 3, (5, 16, 47)),
     ("bf16", 16, 2, 3, (70,)),
 ]
 
@@ -104,6 +107,13 @@ def test_backward_without_state_inputs(kda, gpu_device):
     """S0 = None (zero start) and dS_T = None (no loss on the final state)."""
     w = WORKLOADS["k3_prefill_bf16"].with_(B=2, H=2, dk=16, dv=16, dtype="f32", s0_std=None)
     _say("[bwd] S0 None, dS_T None")
+    _check(kda, w, 37, gpu_device, with_dST=False)
+
+
+def test_backward_without_state_inputs_bf16_d128(kda, gpu_device):
+    """The matrix-core path from a zero start state, with no loss on S_T."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(B=2, H=2, s0_std=None)
+    _say("[bwd] bf16 d=128 S0 None, dS_T None")
     _check(kda, w, 37, gpu_device, with_dST=False)
 
 
