@@ -93,6 +93,25 @@ __device__ __forceinline__ Frag<float> colfrag(const float *M, int ld, int k0, i
     return f;
 }
 
+// Eight consecutive inputs (16-byte aligned) as fp32.
+__device__ __forceinline__ void load8(const bf16 *p, float *out) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(w[i] << 16);
+        out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(const float *p, float *out) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[i] = a[i];
+        out[4 + i] = b[i];
+    }
+}
+
 template <typename TI, int D>
 __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64_t h, int64_t c,
                           int n) {
@@ -101,18 +120,27 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
     const int64_t H = p.H;
     const int64_t row0 = (b * p.T + c * C) * H + h;   // token row of the chunk's first token
     const float cA = __expf(p.A[h]);
-    for (int i = threadIdx.x; i < C * D; i += blockDim.x) {
-        const int r = i / D, d = i % D;
-        float qv = 0.f, kv = 0.f, g = 0.f;
+    // q, k, z: a thread takes 8 consecutive channels of one token row (16- or
+    // 32-byte loads, all three issued before any use)
+    constexpr int VEC = 8, NVEC = C * D / VEC;   // 256 for D = 128 (blockDim.x == 256)
+    for (int t = threadIdx.x; t < NVEC; t += blockDim.x) {
+        const int r = t / (D / VEC), d0 = VEC * (t % (D / VEC));
+        float qv[VEC], kv[VEC], zv[VEC];
         if (r < n) {
-            const int64_t off = (row0 + (int64_t)r * H) * D + d;
-            qv = to_f32(q[off]);
-            kv = to_f32(k[off]);
-            g = kGMin * sigmoidf_(cA * to_f32(z[off]));
+            const int64_t off = (row0 + (int64_t)r * H) * D + d0;
+            load8(q + off, qv);
+            load8(k + off, kv);
+            load8(z + off, zv);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) qv[e] = kv[e] = zv[e] = 0.f;
         }
-        s.Qh[r][d] = qv;
-        s.Kh[r][d] = kv;
-        s.E[r][d] = g;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            s.Qh[r][d0 + e] = qv[e];
+            s.Kh[r][d0 + e] = kv[e];
+            s.E[r][d0 + e] = r < n ? kGMin * sigmoidf_(cA * zv[e]) : 0.f;
+        }
     }
     for (int r = threadIdx.x; r < C; r += blockDim.x)
         s.beta[r] = r < n ? to_f32(beta[row0 + (int64_t)r * H]) : 0.f;
@@ -768,38 +796,72 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     const int n = (int)(p.T - c * C < C ? p.T - c * C : C);
     const int tid = threadIdx.x;
     chunk_ops<TI, D>(s.o, p, b, h, c, n);
-    // the slices' partial sums, added in slice order
+    // the slices' partial sums, added in slice order (4-float loads, all issued
+    // before any use; blockDim.x == 256)
     const float *part = p.part + x * NS * (int64_t)PL::SIZE;
-    for (int i = tid; i < C * D; i += blockDim.x) {
-        float a = 0.f, bb = 0.f, w = 0.f;
-        for (int q = 0; q < NS; ++q) {
-            a += part[q * PL::SIZE + PL::DQH + i];
-            bb += part[q * PL::SIZE + PL::DKB + i];
-            w += part[q * PL::SIZE + PL::DW + i];
+    {
+        constexpr int NV4 = C * D / 4, PER = (NV4 + 255) / 256;
+        f32x4 a[PER], bb[PER], w[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int v = tid + 256 * j;
+            a[j] = bb[j] = w[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (v < NV4) {
+#pragma unroll
+                for (int q = 0; q < NS; ++q) {
+                    const f32x4 *pq = reinterpret_cast<const f32x4 *>(part + q * PL::SIZE);
+                    a[j] += pq[PL::DQH / 4 + v];
+                    bb[j] += pq[PL::DKB / 4 + v];
+                    w[j] += pq[PL::DW / 4 + v];
+                }
+            }
         }
-        s.dQh[i / D][i % D] = a;
-        s.dKb[i / D][i % D] = bb;
-        s.dW[i / D][i % D] = w;
-    }
-    for (int i = tid; i < C * C; i += blockDim.x) {
-        float a = 0.f, bb = 0.f;
-        for (int q = 0; q < NS; ++q) {
-            a += part[q * PL::SIZE + PL::DP + i];
-            bb += part[q * PL::SIZE + PL::DTV + i];
+        // dP, dT's V part (64 float4 each), dbeta's V part (4), sum_j dS' S (D/4)
+        f32x4 e4 = {0.f, 0.f, 0.f, 0.f}, f4 = {0.f, 0.f, 0.f, 0.f};
+        const int u = tid - C * C / 4;       // dbV / dGn lanes
+        if (tid < C * C / 4) {
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                const f32x4 *pq = reinterpret_cast<const f32x4 *>(part + q * PL::SIZE);
+                e4 += pq[PL::DP / 4 + tid];
+                f4 += pq[PL::DTV / 4 + tid];
+            }
+        } else if (u < C / 4 + D / 4) {
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                const f32x4 *pq = reinterpret_cast<const f32x4 *>(part + q * PL::SIZE);
+                e4 += u < C / 4 ? pq[PL::DBV / 4 + u] : pq[PL::DGN / 4 + (u - C / 4)];
+            }
         }
-        const int r = i / C, sc = i % C;
-        s.dP[r][sc] = sc <= r ? a : 0.f;   // P is lower triangular
-        s.dTV[r][sc] = bb;
-    }
-    for (int r = tid; r < C; r += blockDim.x) {
-        float a = 0.f;
-        for (int q = 0; q < NS; ++q) a += part[q * PL::SIZE + PL::DBV + r];
-        s.dbV[r] = a;
-    }
-    for (int d = tid; d < D; d += blockDim.x) {
-        float a = 0.f;
-        for (int q = 0; q < NS; ++q) a += part[q * PL::SIZE + PL::DGN + d];
-        s.dGn[d] = a * s.o.E[C - 1][d];   // d/dG_n of e^{G_n} * (sum_j dS' S)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int v = tid + 256 * j;
+            if (v < NV4) {
+                const int r = (4 * v) / D, d = (4 * v) % D;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s.dQh[r][d + e] = a[j][e];
+                    s.dKb[r][d + e] = bb[j][e];
+                    s.dW[r][d + e] = w[j][e];
+                }
+            }
+        }
+        if (tid < C * C / 4) {
+            const int r = (4 * tid) / C, s0 = (4 * tid) % C;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s.dP[r][s0 + e] = s0 + e <= r ? e4[e] : 0.f;   // P is lower triangular
+                s.dTV[r][s0 + e] = f4[e];
+            }
+        } else if (u < C / 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s.dbV[4 * u + e] = e4[e];
+        } else if (u < C / 4 + D / 4) {
+            const int d = 4 * (u - C / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                s.dGn[d + e] = e4[e] * s.o.E[C - 1][d + e];   // d/dG_n of e^{G_n} (sum_j dS' S)
+        }
     }
     __syncthreads();
     auto &o = s.o;
