@@ -560,7 +560,7 @@ struct PartLds {
     bf16 W[C][BLD], Kb[C][BLD];            // [r][d]
     bf16 V[C][BLD], dO[C][BLD], U[C][BLD], dU[C][BLD];   // [r][j]
     bf16 Ulo[C][BLD], dUlo[C][BLD];        // U - bf16(U), dU - bf16(dU): U, dU to ~16 bits
-    bf16 Tb[C][BLT], PT[C][BLT], TT[C][BLT];            // T diag(beta), P^T, T^T
+    bf16 Tb[C][BLT], PT[C][BLT], TT[C][BLT];            // T, P^T, T^T
     float beta[C];
     float dbV[8][C];
 };
@@ -584,9 +584,10 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
                *betag = static_cast<const bf16 *>(p.beta);
     float *part = p.part + x * (int64_t)PL::SIZE;
 
-    // ---- stage: S (fp32 -> bf16), dS' (bf16) and sum_j dS' S per key
-    // row.  A thread takes 4 x 4 blocks, rows d0..d0+3 by columns j0..j0+3, so
-    // that it holds both operands of its 16 products; 32 consecutive threads
+    // ---- stage: every global load first, then the LDS tiles ----
+    // S (fp32 S0 for the first chunk, else the bf16 checkpoint) and dS' come as
+    // 4 x 4 blocks, rows d0..d0+3 by columns j0..j0+3, so that a thread holds
+    // both operands of its 16 products of sum_j dS' S; 32 consecutive threads
     // cover one block row and reduce it in a fixed order.
     {
         const float *Sin = c == 0 && p.S0 ? p.S0 + bh * (int64_t)(BD * BD) : nullptr;
@@ -594,41 +595,63 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
                                       ((b * nfull + c - 1) * H + h) * (int64_t)(BD * BD)
                                 : nullptr;
         const bf16 *Dt = dsp + x * (int64_t)(BD * BD);   // 4-row blocks, as dstate stores them
+        const float *rec = p.prep + x * (int64_t)Lay::SIZE;
+        f32x4 sv[2][4];    // sv[u][r] = S[d0 + r][j0 .. j0+3]
+        bf16x4 tv[2][4];   // tv[u][e] = dS'[d0 .. d0+3][j0 + e]
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int d0 = 4 * (tid / 32 + 16 * u), j0 = 4 * (tid % 32);
-            f32x4 sv[4];   // sv[r] = S[d0 + r][j0 .. j0+3]
-            bf16x4 tv[4];  // tv[e] = dS'[d0 .. d0+3][j0 + e]
             if (c == 0) {
-                // S0 is the caller's, row-major
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    sv[e] = Sin ? *reinterpret_cast<const f32x4 *>(Sin + (d0 + e) * BD + j0)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
+                    sv[u][e] = Sin ? *reinterpret_cast<const f32x4 *>(Sin + (d0 + e) * BD + j0)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
             } else {
-                // the forward rerun's checkpoints: bf16 in 4-row blocks
                 bf16x4 cv[4];   // cv[e] = S[d0 .. d0+3][j0 + e]
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     cv[e] = *reinterpret_cast<const bf16x4 *>(Ck + ((d0 / 4) * BD + j0 + e) * 4);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    sv[r] = f32x4{(float)cv[0][r], (float)cv[1][r], (float)cv[2][r], (float)cv[3][r]};
+                    sv[u][r] = f32x4{(float)cv[0][r], (float)cv[1][r], (float)cv[2][r], (float)cv[3][r]};
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                tv[e] = *reinterpret_cast<const bf16x4 *>(Dt + ((d0 / 4) * BD + j0 + e) * 4);
+                tv[u][e] = *reinterpret_cast<const bf16x4 *>(Dt + ((d0 / 4) * BD + j0 + e) * 4);
+        }
+        // the chunk's W, Kb (one float4 of each per thread), T or P rows, beta,
+        // and one 16-byte piece of a V or dO row
+        const int rW = tid / 32, dW = 4 * (tid % 32);
+        const f32x4 w4 = reinterpret_cast<const f32x4 *>(rec + Lay::W)[tid];
+        const f32x4 k4 = reinterpret_cast<const f32x4 *>(rec + Lay::KB)[tid];
+        f32x4 tp4 = {0.f, 0.f, 0.f, 0.f};
+        if (tid < C * C / 4)
+            tp4 = reinterpret_cast<const f32x4 *>(rec + Lay::T)[tid];
+        else if (tid < 2 * C * C / 4)
+            tp4 = reinterpret_cast<const f32x4 *>(rec + Lay::P)[tid - C * C / 4];
+        const int rb = tid - 2 * C * C / 4;
+        float bv = 0.f;
+        if (rb >= 0 && rb < nv) bv = (float)betag[row0 + (int64_t)rb * H];
+        const int t2 = tid & 255, rv = t2 / 16, pc = t2 % 16;
+        uint4 val = {0u, 0u, 0u, 0u};
+        if (rv < nv)
+            val = *reinterpret_cast<const uint4 *>((tid < 256 ? v : dOg) +
+                                                   (row0 + (int64_t)rv * H) * BD + 8 * pc);
+
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int d0 = 4 * (tid / 32 + 16 * u), j0 = 4 * (tid % 32);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                store_bf16x4(&s.S[d0 + e][j0], sv[e][0], sv[e][1], sv[e][2], sv[e][3]);
+                store_bf16x4(&s.S[d0 + e][j0], sv[u][e][0], sv[u][e][1], sv[u][e][2], sv[u][e][3]);
                 *reinterpret_cast<bf16x4 *>(&s.dS[d0 + e][j0]) =
-                    bf16x4{tv[0][e], tv[1][e], tv[2][e], tv[3][e]};
+                    bf16x4{tv[u][0][e], tv[u][1][e], tv[u][2][e], tv[u][3][e]};
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 // row d0 + r: S[d0+r][j0+e] * dS'[d0+r][j0+e]
-                float a = sv[r][0] * (float)tv[0][r] + sv[r][1] * (float)tv[1][r] +
-                          sv[r][2] * (float)tv[2][r] + sv[r][3] * (float)tv[3][r];
+                float a = sv[u][r][0] * (float)tv[u][0][r] + sv[u][r][1] * (float)tv[u][1][r] +
+                          sv[u][r][2] * (float)tv[u][2][r] + sv[u][r][3] * (float)tv[u][3][r];
                 a += __shfl_xor(a, 16, 32);
                 a += __shfl_xor(a, 8, 32);
                 a += __shfl_xor(a, 4, 32);
@@ -637,43 +660,24 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
                 if ((tid & 31) == 0) part[PL::DGN + d0 + r] = a;
             }
         }
-    }
-    // ---- stage: the chunk's W, Kb, T, P, beta, V, dO ----
-    {
-        const float *rec = p.prep + x * (int64_t)Lay::SIZE;
-        const int f = tid, r = f / 32, d = 4 * (f % 32);   // 512 float4s of a [C][D] matrix
-        const f32x4 w4 = reinterpret_cast<const f32x4 *>(rec + Lay::W)[f];
-        const f32x4 k4 = reinterpret_cast<const f32x4 *>(rec + Lay::KB)[f];
-        store_bf16x4(&s.W[r][d], w4[0], w4[1], w4[2], w4[3]);
-        store_bf16x4(&s.Kb[r][d], k4[0], k4[1], k4[2], k4[3]);
+        store_bf16x4(&s.W[rW][dW], w4[0], w4[1], w4[2], w4[3]);
+        store_bf16x4(&s.Kb[rW][dW], k4[0], k4[1], k4[2], k4[3]);
         if (tid < C * C / 4) {
-            // T row r = tid / 4, columns s0 .. s0+3
+            // T row rr, columns s0 .. s0+3 (beta is applied to V below)
             const int rr = tid / 4, s0 = 4 * (tid % 4);
-            const f32x4 t4 = reinterpret_cast<const f32x4 *>(rec + Lay::T)[tid];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int sc = s0 + e;
-                const float bs = sc < nv ? (float)betag[row0 + (int64_t)sc * H] : 0.f;
-                s.Tb[rr][sc] = (bf16)(t4[e] * bs);
-                s.TT[sc][rr] = (bf16)t4[e];
+                s.Tb[rr][s0 + e] = (bf16)tp4[e];
+                s.TT[s0 + e][rr] = (bf16)tp4[e];
             }
         } else if (tid < 2 * C * C / 4) {
             // P row sidx, columns r0 .. r0+3  ->  P^T[r][sidx]
             const int f2 = tid - C * C / 4, sidx = f2 / 4, r0 = 4 * (f2 % 4);
-            const f32x4 p4 = reinterpret_cast<const f32x4 *>(rec + Lay::P)[f2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s.PT[r0 + e][sidx] = (bf16)p4[e];
-        } else if (tid < 2 * C * C / 4 + C) {
-            const int rr = tid - 2 * C * C / 4;
-            s.beta[rr] = rr < nv ? (float)betag[row0 + (int64_t)rr * H] : 0.f;
+            for (int e = 0; e < 4; ++e) s.PT[r0 + e][sidx] = (bf16)tp4[e];
         }
-        // V and dO rows: 16 rows x 16 pieces of 8 bf16 each
-        const int t2 = tid & 255, rr = t2 / 16, pc = t2 % 16;
-        const bf16 *src = tid < 256 ? v : dOg;
-        uint4 val = {0u, 0u, 0u, 0u};
-        if (rr < nv) val = *reinterpret_cast<const uint4 *>(src + (row0 + (int64_t)rr * H) * BD + 8 * pc);
-        bf16 *dst = tid < 256 ? &s.V[rr][8 * pc] : &s.dO[rr][8 * pc];
-        *reinterpret_cast<uint4 *>(dst) = val;
+        if (rb >= 0 && rb < C) s.beta[rb] = bv;
+        *reinterpret_cast<uint4 *>(tid < 256 ? &s.V[rv][8 * pc] : &s.dO[rv][8 * pc]) = val;
     }
     __syncthreads();
 
@@ -682,9 +686,12 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
         const int jw = 16 * wave;
         const Frag<bf16> Vf = frag_rows(&s.V[0][0], BLD, 0, jw + n, lane);
         const Frag<bf16> dOf = frag_rows(&s.dO[0][0], BLD, 0, jw + n, lane);
-        f32x4 ta = {0.f, 0.f, 0.f, 0.f}, tb = {0.f, 0.f, 0.f, 0.f};   // U = T b V - W S
+        Frag<bf16> bVf;   // diag(beta) V, rows 4g + e
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bVf.v[e] = (bf16)(s.beta[4 * g + e] * (float)Vf.v[e]);
+        f32x4 ta = {0.f, 0.f, 0.f, 0.f}, tb = {0.f, 0.f, 0.f, 0.f};   // U = T diag(b) V - W S
         f32x4 da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};   // dU = P^T dO + Kb dS'
-        mma16(ta, lds_frag(&s.Tb[0][0], BLT, 0, lane), Vf);
+        mma16(ta, lds_frag(&s.Tb[0][0], BLT, 0, lane), bVf);
         mma16(da, lds_frag(&s.PT[0][0], BLT, 0, lane), dOf);
 #pragma unroll
         for (int i = 0; i < BD / 16; i += 2) {
