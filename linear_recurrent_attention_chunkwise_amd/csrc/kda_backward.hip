@@ -449,27 +449,40 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, bf16
         for (int e = 0; e < 4; ++e)
             dS[i][e] = p.dST ? p.dST[(bh * BD + 16 * i + 4 * g + e) * BD + jw + n] : 0.f;
 
-    // staging registers: this thread's float4s of the record of one chunk
-    f32x4 rw[2048 / 4 / NT], rq[2048 / 4 / NT], rk[2048 / 4 / NT], rp, rg;
-    auto load_rec = [&](int64_t c) {
+    // Staging registers: this thread's float4s of the record of one chunk and
+    // the wave's dO fragment.  Two sets alternate, so every chunk's loads are
+    // issued two chunk steps before the step that writes them to LDS.
+    struct Regs {
+        f32x4 rw[2048 / 4 / NT], rq[2048 / 4 / NT], rk[2048 / 4 / NT], rp, rg;
+        short dr[4];
+    };
+    const int64_t tok_stride = H * BD, row_bytes = tok_stride * 2;
+    const int64_t base = (b * p.T * H + h) * BD;
+    auto load = [&](int64_t c, Regs &R) {
         const f32x4 *rec =
             reinterpret_cast<const f32x4 *>(p.prep + (bh * nchunk + c) * (int64_t)Lay::SIZE);
 #pragma unroll
         for (int u = 0; u < 2048 / 4 / NT; ++u) {
             // W and Q^ in (token, 4-column group) order, Kb row-major
             const int f = tid + NT * u, r = f % C, q4 = f / C;
-            rw[u] = rec[Lay::W / 4 + r * (BD / 4) + q4];
-            rq[u] = rec[Lay::QH / 4 + r * (BD / 4) + q4];
-            rk[u] = rec[Lay::KB / 4 + f];
+            R.rw[u] = rec[Lay::W / 4 + r * (BD / 4) + q4];
+            R.rq[u] = rec[Lay::QH / 4 + r * (BD / 4) + q4];
+            R.rk[u] = rec[Lay::KB / 4 + f];
         }
-        if (tid < C * C / 4) rp = rec[Lay::P / 4 + tid];
-        if (tid < BD / 4) rg = rec[Lay::GN / 4 + tid];
+        if (tid < C * C / 4) R.rp = rec[Lay::P / 4 + tid];
+        if (tid < BD / 4) R.rg = rec[Lay::GN / 4 + tid];
+        // dO fragment: dO[t0 + 4g + e][jw + n] (zero past T)
+        const int64_t t0 = c * C, rows = p.T - t0 < C ? p.T - t0 : (int64_t)C;
+        const auto rs = make_rsrc(dO + base + t0 * tok_stride + jw, rows * row_bytes);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            R.dr[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, (4 * g + e) * (int)row_bytes + 2 * n, 0, 0);
     };
-    auto store_rec = [&](DstateBuf &B) {
+    auto store = [&](const Regs &R, DstateBuf &B) {
 #pragma unroll
         for (int u = 0; u < 2048 / 4 / NT; ++u) {
             const int f = tid + NT * u, r = f / (BD / 4), d = 4 * (f % (BD / 4));
-            store_bf16x4(&B.Kb[r][d], rk[u][0], rk[u][1], rk[u][2], rk[u][3]);
+            store_bf16x4(&B.Kb[r][d], R.rk[u][0], R.rk[u][1], R.rk[u][2], R.rk[u][3]);
         }
         // Q^ and W go in transposed: lanes take consecutive tokens r of one
         // 4-column group, so their 2-byte writes fall in distinct LDS banks
@@ -478,43 +491,25 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, bf16
             const int f = tid + NT * u, r = f % C, d = 4 * (f / C);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                B.QhT[d + e][r] = (bf16)rq[u][e];
-                B.WTn[d + e][r] = (bf16)(-rw[u][e]);
+                B.QhT[d + e][r] = (bf16)R.rq[u][e];
+                B.WTn[d + e][r] = (bf16)(-R.rw[u][e]);
             }
         }
         if (tid < C * C / 4) {
             const int sidx = tid / 4, r0 = 4 * (tid % 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) B.PT[r0 + e][sidx] = (bf16)rp[e];
+            for (int e = 0; e < 4; ++e) B.PT[r0 + e][sidx] = (bf16)R.rp[e];
         }
-        if (tid < BD / 4) *reinterpret_cast<f32x4 *>(&B.Gn[4 * tid]) = rg;
+        if (tid < BD / 4) *reinterpret_cast<f32x4 *>(&B.Gn[4 * tid]) = R.rg;
     };
-    // dO fragment of a chunk: dO[t0 + 4g + e][jw + n] (zero past T)
-    const int64_t tok_stride = H * BD, row_bytes = tok_stride * 2;
-    const int64_t base = (b * p.T * H + h) * BD;
-    short dr[4];
-    auto load_do = [&](int64_t c) {
-        const int64_t t0 = c * C, rows = p.T - t0 < C ? p.T - t0 : (int64_t)C;
-        const auto rs = make_rsrc(dO + base + t0 * tok_stride + jw, rows * row_bytes);
+    auto dO_frag = [](const Regs &R) {
+        Frag<bf16> f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            dr[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, (4 * g + e) * (int)row_bytes + 2 * n, 0, 0);
+        for (int e = 0; e < 4; ++e) f.v[e] = __builtin_bit_cast(bf16, R.dr[e]);
+        return f;
     };
-
-    if (nchunk > 0) {
-        load_rec(nchunk - 1);
-        load_do(nchunk - 1);
-        store_rec(buf[(nchunk - 1) & 1]);
-    }
-    __syncthreads();
-    for (int64_t c = nchunk - 1; c >= 0; --c) {
-        Frag<bf16> dOf;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dOf.v[e] = __builtin_bit_cast(bf16, dr[e]);
-        if (c > 0) {
-            load_rec(c - 1);
-            load_do(c - 1);
-        }
+    // one chunk step (reverse order), from the chunk's record in buf[c & 1]
+    auto step = [&](int64_t c, const Frag<bf16> &dOf) {
         const DstateBuf &B = buf[c & 1];
         // dU = P^T dO + Kb dS'; the incoming dS' of chunk c is stored as the
         // same bf16 values the products use
@@ -545,7 +540,28 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, bf16
             mma32(dS[i], lds_frag(&B.QhT[16 * i][0], BLT, 0, lane),
                   lds_frag(&B.WTn[16 * i][0], BLT, 0, lane), dOf, dUf);
         }
-        if (c > 0) store_rec(buf[(c - 1) & 1]);
+    };
+
+    Regs RA, RB;
+    if (nchunk > 0) {
+        load(nchunk - 1, RA);
+        store(RA, buf[(nchunk - 1) & 1]);
+    }
+    if (nchunk > 1) load(nchunk - 2, RB);
+    __syncthreads();
+    for (int64_t c = nchunk - 1; c >= 0; c -= 2) {
+        // chunk c: RA holds its dO; RB (chunk c-1) is in flight
+        const Frag<bf16> dOa = dO_frag(RA);
+        if (c >= 2) load(c - 2, RA);
+        step(c, dOa);
+        if (c >= 1) store(RB, buf[(c - 1) & 1]);
+        __syncthreads();
+        if (c < 1) break;
+        // chunk c-1: RB holds its dO; RA (chunk c-2) is in flight
+        const Frag<bf16> dOb = dO_frag(RB);
+        if (c >= 3) load(c - 3, RB);
+        step(c - 1, dOb);
+        if (c >= 2) store(RA, buf[c & 1]);
         __syncthreads();
     }
 #pragma unroll
