@@ -16,22 +16,27 @@
 // and the decayed products pass the rest to q, k, beta and G; the reverse
 // cumulative sum of dG is dg, and the gate gives dz and dA.  Every decayed
 // product factors as (X e^G)(Y e^-G)^T: over 16 tokens e^-G <= e^80 stays in
-// fp32 range, so all of them are plain 16 x 16 x d products.  Arithmetic is
-// fp32 throughout.
+// fp32 range, so all of them are plain 16 x 16 x d products.
 //
-// Kernels (all fp32, LDS-staged, plain FMA loops):
-//   prep  -- one workgroup per (sequence, head, chunk): the chunk's W, Q^,
-//            Kb, P, T and e^{G_n} (S-independent), into the workspace.
-//   chain -- one workgroup per (sequence, head, value-column slice): walks the
-//            chunks backwards carrying dS, with each chunk's entering state
-//            from the forward pass's state checkpoints; writes dV and the
-//            slice's partial sums of the quantities that contract over value
-//            columns (dQ^, dKb, dW, dP, the V part of dT and dbeta, and
-//            sum_j dS' S); the final dS is dS0.
-//   grad  -- one workgroup per (sequence, head, chunk): adds the slices'
-//            partials in slice order and forms dq, dk, dbeta, dz and the
-//            chunk's share of dA.
-//   dA    -- sums the shares of each head in (sequence, chunk) order.
+// Kernels:
+//   prep   -- one workgroup per (sequence, head, chunk): the chunk's W, Q^,
+//             Kb, P, T and e^{G_n} (S-independent, fp32; A and P on fp32
+//             matrix-core tiles), into the workspace.
+//   dstate -- (bf16, d = 128) one workgroup per (sequence, head, 64 value
+//             columns): walks the chunks backwards carrying dS in fp32
+//             accumulator tiles (bf16 matrix-core products) and stores every
+//             chunk's incoming dS'; the final dS is dS0.
+//   part   -- (bf16, d = 128) one workgroup per (sequence, head, chunk), all
+//             chunks at once: from the forward rerun's checkpoint S and the
+//             stored dS' it forms dV and the sums over all value columns
+//             (dQ^, dKb, dW, dP, the V parts of dT and dbeta, sum_j dS' S).
+//   chain  -- (fp32 inputs, d = 16) dstate and part in one fp32 kernel per
+//             (sequence, head, value-column slice), carrying dS through LDS.
+//   grad   -- one workgroup per (sequence, head, chunk): adds the slices'
+//             partials in slice order and forms dq, dk, dbeta, dz and the
+//             chunk's share of dA (fp32; its chunk products on fp32
+//             matrix-core tiles).
+//   dA     -- sums the shares of each head in (sequence, chunk) order.
 // No atomics: results are bitwise reproducible.
 #include "kda_device.h"
 #include "kda_launch.h"
