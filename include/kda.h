@@ -231,9 +231,10 @@ size_t kda_prefill_split_workspace_size(int dtype, int64_t B, int64_t T, int64_t
  * (one workgroup per (b, h, 64 value columns)), and the per-token gradients
  * in parallel again.  For bf16 inputs with dk = dv = 128 the state-gradient
  * chain and the value-column contractions run on bf16 matrix-core tiles with
- * fp32 accumulation (the forward's operand precision; the per-chunk dL/dS'
- * hand-off between them is stored in bf16); every other case, and all
- * per-token work, is fp32.  No atomics, so results are bitwise reproducible.
+ * fp32 accumulation (the forward's operand precision; the forward rerun's
+ * state checkpoints and the per-chunk dL/dS' hand-off between them are kept
+ * in bf16 in the workspace); every other case, and all per-token work, is
+ * fp32.  No atomics, so results are bitwise reproducible.
  * Supported: dtype in {KDA_F32, KDA_BF16}, dk == dv in {16, 128}.  Outputs
  * must not overlap one another, any input or the workspace.  Errors as
  * kda_prefill_ex.
