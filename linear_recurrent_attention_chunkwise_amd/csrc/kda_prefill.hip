@@ -139,6 +139,11 @@ __device__ __forceinline__ void store_pair(bf16 *p, float a, float b) {
 __device__ __forceinline__ void store_pair(float *p, float a, float b) {
     *reinterpret_cast<float2 *>(p) = make_float2(a, b);
 }
+// two values as one bf16 pair (a at the lower address)
+__device__ __forceinline__ uint32_t pack_pair_bf16(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, bf16x2{(bf16)a, (bf16)b});
+}
 
 template <typename T>
 __device__ __forceinline__ Frag<T> frag_from_f32(const f32x4 &x) {
@@ -351,6 +356,13 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
             const float itot0 = __builtin_amdgcn_rcpf(tot[sp][0]);
             const float itot1 = __builtin_amdgcn_rcpf(tot[sp][1]);
             float rl0 = aft0, rl1 = aft1;   // decay over (r, end of sub-tile]
+            // bf16 with whole 8-token groups: the transposed rows d0, d0+1 of
+            // K~ and Kh are packed in registers and written 8 tokens at a time
+            // (one 16-byte store per row instead of eight 2-byte ones, whose
+            // rows 2*cp fell into the same few LDS banks)
+            constexpr bool kPackT = sizeof(T) == 2 && SEGLEN % 8 == 0;
+            uint32_t pg0[4], pg1[4], ph0[4], ph1[4];
+            float ng0 = 0.f, ng1 = 0.f, nh0 = 0.f, nh1 = 0.f;   // token s+1's values
 #pragma unroll
             for (int s = SEGLEN - 1; s >= 0; --s) {
                 const int r = 16 * sp + sg * SEGLEN + s;
@@ -368,10 +380,31 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
                 store_pair(sKd + r * DP + d0, k0 * F0 * itot0, k1 * F1 * itot1);
                 store_pair(sKt + r * DP + d0, k0 * rl0, k1 * rl1);
                 store_pair(sQG + r * DP + d0, q0 * F0 * pre0, q1 * F1 * pre1);
-                sKGbT[d0 * CP + r] = from_f32<T>(bt * k0 * F0 * pre0);
-                sKGbT[(d0 + 1) * CP + r] = from_f32<T>(bt * k1 * F1 * pre1);
-                sKhT[d0 * CP + r] = from_f32<T>(k0 * rl0 * post0);
-                sKhT[(d0 + 1) * CP + r] = from_f32<T>(k1 * rl1 * post1);
+                const float g0 = bt * k0 * F0 * pre0, g1 = bt * k1 * F1 * pre1;
+                const float h0 = k0 * rl0 * post0, h1 = k1 * rl1 * post1;
+                if constexpr (kPackT) {
+                    if (s % 2 == 0) {
+                        pg0[(s / 2) % 4] = pack_pair_bf16(g0, ng0);
+                        pg1[(s / 2) % 4] = pack_pair_bf16(g1, ng1);
+                        ph0[(s / 2) % 4] = pack_pair_bf16(h0, nh0);
+                        ph1[(s / 2) % 4] = pack_pair_bf16(h1, nh1);
+                    }
+                    if (s % 8 == 0) {   // tokens r .. r+7 complete
+                        *reinterpret_cast<uint4 *>(sKGbT + d0 * CP + r) = uint4{pg0[0], pg0[1], pg0[2], pg0[3]};
+                        *reinterpret_cast<uint4 *>(sKGbT + (d0 + 1) * CP + r) = uint4{pg1[0], pg1[1], pg1[2], pg1[3]};
+                        *reinterpret_cast<uint4 *>(sKhT + d0 * CP + r) = uint4{ph0[0], ph0[1], ph0[2], ph0[3]};
+                        *reinterpret_cast<uint4 *>(sKhT + (d0 + 1) * CP + r) = uint4{ph1[0], ph1[1], ph1[2], ph1[3]};
+                    }
+                    ng0 = g0;
+                    ng1 = g1;
+                    nh0 = h0;
+                    nh1 = h1;
+                } else {
+                    sKGbT[d0 * CP + r] = from_f32<T>(g0);
+                    sKGbT[(d0 + 1) * CP + r] = from_f32<T>(g1);
+                    sKhT[d0 * CP + r] = from_f32<T>(h0);
+                    sKhT[(d0 + 1) * CP + r] = from_f32<T>(h1);
+                }
                 rl0 *= al0[ii][s];
                 rl1 *= al1[ii][s];
             }
