@@ -590,8 +590,7 @@ struct PartLds {
 __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16 *dsp) {
     using Lay = PrepLayout<BD>;
     using PL = PartLayout<BD>;
-    constexpr int NT = 512;
-    __shared__ __attribute__((aligned(16))) PartLds s;
+    __shared__ __attribute__((aligned(16))) PartLds s;   // blockDim.x == 512
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
