@@ -437,6 +437,7 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, bf16
     using Lay = PrepLayout<BD>;
     constexpr int NDT = BD / 16, NT = 64 * NW, NSL = BD / (16 * NW);
     __shared__ __attribute__((aligned(16))) DstateBuf buf[2];
+    static_assert(2 * sizeof(DstateBuf) <= 150 * 1024, "LDS budget");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
@@ -590,7 +591,8 @@ struct PartLds {
 __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16 *dsp) {
     using Lay = PrepLayout<BD>;
     using PL = PartLayout<BD>;
-    __shared__ __attribute__((aligned(16))) PartLds s;   // blockDim.x == 512
+    __shared__ __attribute__((aligned(16))) PartLds s;
+    static_assert(sizeof(PartLds) <= 150 * 1024, "LDS budget");   // blockDim.x == 512
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
@@ -816,6 +818,7 @@ template <typename TI, int D> struct GradLds {
 template <typename TI, int D, int NS>
 __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     __shared__ GradLds<TI, D> s;
+    static_assert(sizeof(GradLds<TI, D>) <= 150 * 1024, "LDS budget");
     using PL = PartLayout<D>;
     const int64_t x = blockIdx.x;
     const int64_t c = x % p.nchunk, bh = x / p.nchunk;
