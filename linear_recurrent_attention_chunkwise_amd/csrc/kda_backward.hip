@@ -212,6 +212,7 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
 template <typename TI, int D>
 __global__ __launch_bounds__(256) void kda_bwd_prep_kernel(BwdArgs p) {
     __shared__ ChunkOps<TI, D> s;
+    static_assert(sizeof(ChunkOps<TI, D>) <= 150 * 1024, "LDS budget");
     using Lay = PrepLayout<D>;
     const int64_t x = blockIdx.x;
     const int64_t c = x % p.nchunk, bh = x / p.nchunk;
@@ -248,6 +249,7 @@ template <int D, int NC> struct ChainLds {
 template <typename TI, int D, int NC, int NT>
 __global__ __launch_bounds__(NT) void kda_bwd_chain_kernel(BwdArgs p) {
     __shared__ ChainLds<D, NC> s;
+    static_assert(sizeof(ChainLds<D, NC>) <= 150 * 1024, "LDS budget");
     using Lay = PrepLayout<D>;
     using PL = PartLayout<D>;
     const TI *v = static_cast<const TI *>(p.v), *beta = static_cast<const TI *>(p.beta),
