@@ -20,6 +20,12 @@ algorithmic bytes one launch must move divided by its average duration:
 The fp64 oracle is timed on the host cores over the full prefill workload
 (``cpu_baseline``), reported in the same unit.  Prints ONE JSON line.
 
+``mfma`` reports the same prefill against the bf16 matrix-core peak: the
+algorithmic flops of a launch (6d^2 + 5Cd + C^2/3 per token-head) over its
+time, and the MFMA flops a counter run measured for this kernel source
+(``SQ_INSTS_VALU_MFMA_MOPS_BF16`` x 512; masked and duplicated tiles
+included), read from the kernel's summary under profiles/.
+
 ``long`` times the long-context (B1 H96 T65536, z ~ N(2,1)) and million-token
 (B1 H16 T2^20) prefill workloads at 64- and 16-token chunks over 3 launches
 each, inputs drawn on the device; the million-token head share also split
@@ -70,6 +76,15 @@ def prefill_bytes(B, T, H, d, esz=2):
     return B * T * H * (4 * d * esz + d * esz + esz) + 2 * B * H * d * d * 4 + H * 4
 
 
+MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
+
+
+def prefill_flops(B, T, H, d, chunk):
+    """Algorithmic flops of one prefill: 6d^2 + 5Cd + C^2/3 per token-head (the
+    state products, the chunk-local products and the triangular inverse)."""
+    return B * T * H * (6 * d * d + 5 * chunk * d + chunk * chunk / 3.0)
+
+
 def decode_bytes(B, H, d, esz=2):
     return B * H * (2 * d * d * 4 + 4 * d * esz + esz + d * esz) + H * 4
 
@@ -96,18 +111,24 @@ KERNEL_SOURCES = {
 }
 
 
-def recorded_traffic(kernel, summary):
-    """HBM bytes per launch from a committed counter summary, or None when the
-    summary is missing or was taken on a different kernel source."""
+def recorded_counter(kernel, summary, key="traffic_bytes_per_launch"):
+    """A per-launch counter figure (`key: value` line) from a committed counter
+    summary, or None when the summary is missing or was taken on a different
+    kernel source."""
     path = os.path.join(PROFILES, summary)
     if kernel not in KERNEL_SOURCES or not os.path.exists(path):
         return None
     text = open(path).read()
-    mb = re.search(r"^traffic_bytes_per_launch:\s*([0-9]+)", text, re.M)
+    mb = re.search(r"^" + re.escape(key) + r":\s*([0-9]+)", text, re.M)
     mh = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
     if not mb or not mh or mh.group(1) != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return int(mb.group(1))
+
+
+def recorded_traffic(kernel, summary):
+    """HBM bytes per launch from a committed counter summary (see recorded_counter)."""
+    return recorded_counter(kernel, summary)
 
 
 def calibration_copy(torch, mib):
@@ -440,6 +461,18 @@ def main(argv=None):
                      "frac": achieved / HBM_PEAK_GBS, "traffic": ptraffic,
                      "kernel": pkernel, "bytes_per_launch": pbytes},
     }
+    # the prefill against the matrix cores as well: algorithmic flops, and the
+    # MFMA flops a counter run measured (masked and duplicated tiles included)
+    pflops = prefill_flops(w.B, w.T, w.H, w.dk, args.chunk)
+    counted = recorded_counter(pkernel, f"{pkernel}_{w.name}_c{args.chunk}.md",
+                               "mfma_flops_per_launch")
+    result["mfma"] = {
+        "algorithmic_flops_per_launch": pflops,
+        "achieved": pflops / (ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": pflops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
+        "counted_flops_per_launch": counted,
+        "counted_frac": (counted / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS
+                         if counted is not None else None)}
     if not args.no_decode:
         wd = WORKLOADS["k3_decode_bf16"]
         dinp = make_decode_inputs(wd, device=dev)

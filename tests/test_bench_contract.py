@@ -39,3 +39,12 @@ def test_decode_bytes_k3_shape():
 
 def test_prologue_bytes_k3_shape():
     assert bench.conv_norm_bytes(1, 4096, 96, 128, 4) == 605_011_968
+
+
+def test_prefill_flops_k3_shape():
+    # 6 d^2 + 5 C d + C^2 / 3 per token-head: the three d x d state products of a
+    # token (U, O and the update), the chunk-local products and the inverse
+    B, T, H, d, C = 1, 4096, 96, 128, 16
+    per = 6 * d * d + 5 * C * d + C * C / 3
+    assert abs(bench.prefill_flops(B, T, H, d, C) - B * T * H * per) < 1.0
+    assert round(bench.prefill_flops(B, T, H, d, C)) == 42_714_791_936
