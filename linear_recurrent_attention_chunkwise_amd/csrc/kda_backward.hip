@@ -811,7 +811,7 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
 
 template <typename TI, int D> struct GradLds {
     ChunkOps<TI, D> o;
-    float dQh[C][rowpad<D>()], dKb[C][rowpad<D>()], dW[C][rowpad<D>()], dG[C][rowpad<D>()];
+    float dW[C][rowpad<D>()];
     float dP[C][C + 1], dTV[C][C + 1], dT[C][C + 1], M1[C][C + 1], dL[C][C + 1];
     float dbV[C], dGn[D];
     float dbk[4][C];   // per-wave sums over d of (T^T dW)[r][d] Kh[r][d]
@@ -831,21 +831,42 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     // the slices' partial sums, added in slice order (4-float loads, all issued
     // before any use; blockDim.x == 256)
     const float *part = p.part + x * NS * (int64_t)PL::SIZE;
+    const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, nn = lane & 15;
+    constexpr int LDD = rowpad<D>(), LDC = C + 1, NDT = D / 16, TPW = (NDT + 3) / 4;
+    const TI *zg = static_cast<const TI *>(p.z);
+    float tq[TPW][4], tkb[TPW][4], tz[TPW][4];
     {
         constexpr int NV4 = C * D / 4, PER = (NV4 + 255) / 256;
-        f32x4 a[PER], bb[PER], w[PER];
+        f32x4 w[PER];
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int v = tid + 256 * j;
-            a[j] = bb[j] = w[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            w[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (v < NV4) {
 #pragma unroll
-                for (int q = 0; q < NS; ++q) {
-                    const f32x4 *pq = reinterpret_cast<const f32x4 *>(part + q * PL::SIZE);
-                    a[j] += pq[PL::DQH / 4 + v];
-                    bb[j] += pq[PL::DKB / 4 + v];
-                    w[j] += pq[PL::DW / 4 + v];
+                for (int q = 0; q < NS; ++q)
+                    w[j] += reinterpret_cast<const f32x4 *>(part + q * PL::SIZE)[PL::DW / 4 + v];
+            }
+        }
+        // dQ^, dKb and z at this thread's elements of its column tiles (rows
+        // 4g..4g+3 of column 16t + nn), used directly by the dq/dk pass
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int t = wave + 4 * j;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e, d = 16 * t + nn;
+                float a = 0.f, bq = 0.f;
+                if (t < NDT) {
+#pragma unroll
+                    for (int q = 0; q < NS; ++q) {
+                        a += part[q * PL::SIZE + PL::DQH + r * D + d];
+                        bq += part[q * PL::SIZE + PL::DKB + r * D + d];
+                    }
                 }
+                tq[j][e] = a;
+                tkb[j][e] = bq;
+                tz[j][e] = t < NDT && r < n ? to_f32(zg[((b * p.T + c * C + r) * H + h) * D + d]) : 0.f;
             }
         }
         // dP, dT's V part (64 float4 each), dbeta's V part (4), sum_j dS' S (D/4)
@@ -871,11 +892,7 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
             if (v < NV4) {
                 const int r = (4 * v) / D, d = (4 * v) % D;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    s.dQh[r][d + e] = a[j][e];
-                    s.dKb[r][d + e] = bb[j][e];
-                    s.dW[r][d + e] = w[j][e];
-                }
+                for (int e = 0; e < 4; ++e) s.dW[r][d + e] = w[j][e];
             }
         }
         if (tid < C * C / 4) {
@@ -897,8 +914,6 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     }
     __syncthreads();
     auto &o = s.o;
-    const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, nn = lane & 15;
-    constexpr int LDD = rowpad<D>(), LDC = C + 1, NDT = D / 16, TPW = (NDT + 3) / 4;
     // dT = dW (beta K^)^T + dU (beta V)^T: a 16 x 16 tile over d (wave 0)
     if (wave == 0) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -962,9 +977,14 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
         s.dL[r][sc] *= o.beta[r];   // now dA
     }
     __syncthreads();
-    // dq, dk and dG on the same column tiles:
+    // dq, dk, dG and dz on the same column tiles:
     //   dQ^ += dP Ki,  dK^ = dA Ki + beta (T^T dW),  dKi = dA^T K^ + dP^T Q^
-    // (products over the 16 tokens s on fp32 matrix-core tiles)
+    // (products over the 16 tokens s on fp32 matrix-core tiles).  A tile's
+    // rows 4g..4g+3 of column d sit in lane group g, so the column's dG_n terms
+    // and the reverse cumulative sum of dG over the 16 rows are formed across
+    // the four lane groups, and the gate's derivative gives dz in place.
+    const float cA = __expf(p.A[h]);
+    float dA_acc = 0.f;
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
         const int t = wave + 4 * j;
@@ -972,61 +992,58 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
             const int d = 16 * t + nn;
             f32x4 dqh, dkh = {0.f, 0.f, 0.f, 0.f}, dki = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dqh[e] = s.dQh[4 * g + e][d];
+            for (int e = 0; e < 4; ++e) dqh[e] = tq[j][e];
             const Frag<float> kiB = colfrag(&o.Ki[0][0], LDD, 0, 16 * t, lane);
             mma16(dqh, rowfrag(&s.dP[0][0], LDC, 0, 0, lane), kiB);
             mma16(dkh, rowfrag(&s.dL[0][0], LDC, 0, 0, lane), kiB);
             mma16(dki, colfrag(&s.dL[0][0], LDC, 0, 0, lane), colfrag(&o.Kh[0][0], LDD, 0, 16 * t, lane));
             mma16(dki, colfrag(&s.dP[0][0], LDC, 0, 0, lane), colfrag(&o.Qh[0][0], LDD, 0, 16 * t, lane));
             const float En = o.E[C - 1][d];
+            float dGv[4], colp = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g + e;
                 const float dk_h = dkh[e] + o.beta[r] * tdw[j][e];   // through W = T diag(beta) K^
                 const float Em = o.E[r][d], Ei = 1.0f / Em;   // e^{G}, e^{-G}
-                const float dKb = s.dKb[r][d], kb = o.Ki[r][d] * En;  // Kb = k e^{G_n - G}
+                const float dKb = tkb[j][e], kb = o.Ki[r][d] * En;   // Kb = k e^{G_n - G}
                 const float dq = dqh[e] * Em;
                 const float dk = dk_h * Em + dki[e] * Ei + dKb * En * Ei;
-                const float dG =
-                    dqh[e] * o.Qh[r][d] + dk_h * o.Kh[r][d] - dki[e] * o.Ki[r][d] - dKb * kb;
+                dGv[e] = dqh[e] * o.Qh[r][d] + dk_h * o.Kh[r][d] - dki[e] * o.Ki[r][d] - dKb * kb;
+                colp += dKb * kb;   // d/dG_n of Kb = k e^{G_n - G}
                 if (r < n) {
                     const int64_t off = ((b * p.T + c * C + r) * H + h) * D + d;
                     p.dq[off] = dq;
                     p.dk[off] = dk;
                 }
-                s.dG[r][d] = dG;
             }
-        }
-    }
-    __syncthreads();
-    // dG_n from Kb = K e^{G_n - G} and from e^{G_n} (sum_j dS' S); G_n = G of the last row
-    for (int d = tid; d < D; d += blockDim.x) {
-        float a = s.dGn[d];
-        const float En = o.E[C - 1][d];
-        for (int r = 0; r < C; ++r) a += s.dKb[r][d] * o.Ki[r][d] * En;
-        s.dG[C - 1][d] += a;
-    }
-    __syncthreads();
-    // dg = reverse cumulative sum of dG; gate: g = g_min sigma(c z)
-    const float cA = __expf(p.A[h]);
-    const TI *z = static_cast<const TI *>(p.z);
-    float dA_acc = 0.f;
-    for (int d = tid; d < D; d += blockDim.x) {
-        float zr[C];   // all of the channel's z loads are issued before the scan
+            // G_n is G of the last row: it collects the column's Kb terms and
+            // e^{G_n} (sum_j dS' S)
+            colp += __shfl_xor(colp, 16);
+            colp += __shfl_xor(colp, 32);
+            if (g == 3) dGv[3] += s.dGn[d] + colp;
+            // dg = reverse cumulative sum of dG over the rows: within the lane,
+            // then the totals of the higher lane groups
+            float suf[4];
+            suf[3] = dGv[3];
+            suf[2] = dGv[2] + suf[3];
+            suf[1] = dGv[1] + suf[2];
+            suf[0] = dGv[0] + suf[1];
+            const float t1 = __shfl_xor(suf[0], 16), t2 = __shfl_xor(suf[0], 32),
+                        t3 = __shfl_xor(suf[0], 48);
+            const float higher = ((g ^ 1) > g ? t1 : 0.f) + ((g ^ 2) > g ? t2 : 0.f) +
+                                 ((g ^ 3) > g ? t3 : 0.f);
+            // gate: g = g_min sigma(c z)
 #pragma unroll
-        for (int r = 0; r < C; ++r)
-            zr[r] = r < n ? to_f32(z[((b * p.T + c * C + r) * H + h) * D + d]) : 0.f;
-        float acc = 0.f;
-#pragma unroll
-        for (int r = C - 1; r >= 0; --r) {
-            acc += s.dG[r][d];
-            if (r < n) {
-                const int64_t off = ((b * p.T + c * C + r) * H + h) * D + d;
-                const float xz = cA * zr[r];
-                const float sg = sigmoidf_(xz);
-                const float dx = acc * kGMin * sg * (1.0f - sg);
-                p.dz[off] = cA * dx;
-                dA_acc += dx * xz;
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                if (r < n) {
+                    const int64_t off = ((b * p.T + c * C + r) * H + h) * D + d;
+                    const float xz = cA * tz[j][e];
+                    const float sg = sigmoidf_(xz);
+                    const float dx = (suf[e] + higher) * kGMin * sg * (1.0f - sg);
+                    p.dz[off] = cA * dx;
+                    dA_acc += dx * xz;
+                }
             }
         }
     }
