@@ -113,10 +113,12 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
         return KDA_ERR_UNSUPPORTED;
     if (want_ckpt && !role_split && !kda::prefill_ckpt_supported(dtype, D, chunk, dvb))
         return KDA_ERR_UNSUPPORTED;
-    if (mode != 0 && (!role_split || dvb != 64 || want_ckpt)) return KDA_ERR_UNSUPPORTED;
+    // modes 1 and 2 write states only (o is neither read nor written)
+    if (mode != 0 && (!role_split || dvb != 64 || (want_ckpt && mode != 1)))
+        return KDA_ERR_UNSUPPORTED;
     if (ckpt_blocked && want_ckpt && !role_split) return KDA_ERR_UNSUPPORTED;
     if (!A || !S_T) return KDA_ERR_NULL;
-    if (bth > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL;
+    if (bth > 0 && (!q || !k || !v || !z || !beta || (mode == 0 && !o))) return KDA_ERR_NULL;
     if (ckpt_every > 0 && n_ckpt > 0 && !ckpt) return KDA_ERR_NULL;
     const void *ptrs[] = {q, k, v, z, beta, A, S0, o, S_T, ckpt};
     for (const void *p : ptrs)
@@ -128,7 +130,7 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
     const Range rq = range_of(q, nin * esz), rk = range_of(k, nin * esz),
                 rv = range_of(v, nin * esz), rz = range_of(z, nin * esz),
                 rb = range_of(beta, bth * esz), rA = range_of(A, H * 4),
-                rS0 = range_of(S0, nstate * 4), ro = range_of(o, nin * esz),
+                rS0 = range_of(S0, nstate * 4), ro = range_of(mode == 0 ? o : nullptr, nin * esz),
                 rST = range_of(S_T, nstate * 4),
                 rcu = range_of(cu, cu ? (B + 1) * 8 : 0),
                 rws = range_of(need_ws > 0 ? workspace : nullptr, (int64_t)need_ws),
@@ -151,7 +153,7 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
     a.dtype = dtype; a.B = B; a.T = T; a.H = H; a.D = D; a.chunk = chunk;
     a.dv_per_block = dvb;
     a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.A = A; a.S0 = S0;
-    a.o = o; a.S_T = S_T;
+    a.o = mode == 0 ? o : nullptr; a.S_T = S_T;
     a.cu_seqlens = cu;
     a.order = nullptr;
     if (need_ws > 0) {
@@ -692,11 +694,13 @@ bool bwd_layout(int dtype, int64_t B, int64_t T, int64_t H, int64_t D, BwdLayout
         !mul_ok(units, (int64_t)kda::bwd_part_floats(D), kMaxElems / 16, &npart) ||
         !mul_ok(units, (int64_t)kda::bwd_dsp_bytes(dtype, D), kMaxElems / 16, &ndsp))
         return false;
+    // the MFMA backward (bf16, d = 128) reruns the forward for its states only
+    const bool mfma = kda::bwd_dsp_bytes(dtype, D) > 0;
     lay->o = 0;
-    lay->S_T = round256(nin * esz);
+    lay->S_T = mfma ? 0 : round256(nin * esz);
     lay->ckpt = lay->S_T + round256(nst * 4);
     // the MFMA backward (bf16, d = 128) keeps its checkpoints in bf16
-    lay->prep = lay->ckpt + round256(nck * (kda::bwd_dsp_bytes(dtype, D) > 0 ? 2 : 4));
+    lay->prep = lay->ckpt + round256(nck * (mfma ? 2 : 4));
     lay->part = lay->prep + round256(nprep * 4);
     lay->dA = lay->part + round256(npart * 4);
     lay->dsp = lay->dA + round256(units * 4);
@@ -764,12 +768,14 @@ kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
     float *ckpt = bh > 0 ? reinterpret_cast<float *>(ws + lay.ckpt) : nullptr;
     // forward with a checkpoint at every chunk boundary
     if (bth > 0) {
-        // bf16 d = 128: checkpoints in the 4-row block layout the MFMA backward reads
+        // bf16 d = 128: states only (no o), checkpoints in the 4-row block
+        // layout the MFMA backward reads
         const bool blocked = kda::bwd_dsp_bytes(dtype, D) > 0;
         kda_status st = prefill_impl(dtype, B, T, H, dk, dv, kBwdChunk, nullptr, q, k, v, z, beta,
-                                     A, S0, ws + lay.o, reinterpret_cast<float *>(ws + lay.S_T),
+                                     A, S0, blocked ? nullptr : ws + lay.o,
+                                     reinterpret_cast<float *>(ws + lay.S_T),
                                      nfull > 0 ? kBwdChunk : 0, ckpt, B * nfull, nullptr, 0,
-                                     stream, 0, 0, false, blocked);
+                                     stream, blocked ? 64 : 0, blocked ? 1 : 0, false, blocked);
         if (st != KDA_OK) return st;
     }
     kda::BwdArgs a;

@@ -444,8 +444,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
                 F0 *= a0[s];
                 F1 *= a1[s];
                 const float f0 = F0 * ic0, f1 = F1 * ic1;
-                *reinterpret_cast<uint32_t *>(sQG + s * DP + d0) =
-                    pack_bf16(bf_lo(rq[s]) * f0, bf_hi(rq[s]) * f1);
+                if constexpr (MODE == 0)   // Q~ feeds the output only
+                    *reinterpret_cast<uint32_t *>(sQG + s * DP + d0) =
+                        pack_bf16(bf_lo(rq[s]) * f0, bf_hi(rq[s]) * f1);
                 *reinterpret_cast<uint32_t *>(sWn + s * DP + d0) =
                     pack_bf16(bf_lo(rk[s]) * f0, bf_hi(rk[s]) * f1);
             }
@@ -464,9 +465,12 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
 #pragma unroll
         for (int k32 = 0; k32 < D; k32 += 32) {
             const Frag<bf16> c0 = lds_frag(sKh, DP, k32, lane), c1 = lds_frag(sKh, DP, k32 + 16, lane);
-            const Frag<bf16> q0f = lds_frag(sQG, DP, k32, lane), q1f = lds_frag(sQG, DP, k32 + 16, lane);
             const Frag<bf16> h0f = lds_frag(sWn, DP, k32, lane), h1f = lds_frag(sWn, DP, k32 + 16, lane);
-            mma32(accP, c0, c1, q0f, q1f);
+            if constexpr (MODE == 0) {
+                const Frag<bf16> q0f = lds_frag(sQG, DP, k32, lane),
+                                 q1f = lds_frag(sQG, DP, k32 + 16, lane);
+                mma32(accP, c0, c1, q0f, q1f);
+            }
             mma32(accL, h0f, h1f, c0, c1);
             mma32(accLT, c0, c1, h0f, h1f);
         }
@@ -484,7 +488,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
                 LTb[e] = r < n ? bcol * accLT[e] : 0.0f;            // L[n][4g+e]
                 ImLT[e] = (r == n ? 1.0f : 0.0f) - LTb[e];
             }
-            *reinterpret_cast<bf16x4v *>(sP + n * CP + 4 * g) = pw4;
+            if constexpr (MODE == 0) *reinterpret_cast<bf16x4v *>(sP + n * CP + 4 * g) = pw4;
         }
         // ---- T^T = Y^T X^T with X = (I-L)(I+L^2), Y = (I+L^4)(I+L^8) ----------
         // B-layout inputs: M (B) and M^T (= A-layout of M).
@@ -567,9 +571,10 @@ bool prefill16_supported(int dtype, int64_t D, int chunk, int dv_per_block) {
 
 hipError_t launch_prefill16(const PrefillArgs &a) {
     const bool ck = a.ckpt != nullptr && a.ckpt_every > 0;
-    if (a.mode != 0) {   // segment passes: 64 columns, no checkpoints
-        if (a.dv_per_block != 64 || ck) return hipErrorInvalidValue;
-        return a.mode == 1 ? launch_p16<4, 8, 6, false, 1>(a) : launch_p16<4, 8, 6, false, 2>(a);
+    if (a.mode != 0) {   // states only: 64 columns; checkpoints in MODE 1 only
+        if (a.dv_per_block != 64 || (ck && a.mode != 1)) return hipErrorInvalidValue;
+        if (a.mode == 1) return ck ? launch_p16<4, 8, 6, true, 1>(a) : launch_p16<4, 8, 6, false, 1>(a);
+        return launch_p16<4, 8, 6, false, 2>(a);
     }
     if (a.dv_per_block == 64)
         return ck ? launch_p16<4, 8, 6, true>(a) : launch_p16<4, 8, 6, false>(a);

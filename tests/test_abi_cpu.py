@@ -398,7 +398,13 @@ def test_backward_argument_errors(lib):
 
 def test_backward_workspace_holds_forward_and_checkpoints(lib):
     B, T, H, d = 2, 100, 3, 128
-    n = lib.kda_prefill_bwd_workspace_size(BF16, B, T, H, d, d)
-    o = B * T * H * d * 2
+    # fp32: the rerun forward's o, fp32 checkpoints and final states
+    n = lib.kda_prefill_bwd_workspace_size(F32, B, T, H, d, d)
+    o = B * T * H * d * 4
     ckpt = B * (T // 16) * H * d * d * 4
     assert n >= o + ckpt + B * H * d * d * 4
+    # bf16 (matrix-core backward): states only, checkpoints in bf16, plus the
+    # per-chunk dS' hand-off (d*d bf16 per chunk)
+    n = lib.kda_prefill_bwd_workspace_size(BF16, B, T, H, d, d)
+    units = B * H * ((T + 15) // 16)
+    assert n >= ckpt // 2 + B * H * d * d * 4 + units * d * d * 2
