@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kda_launch.h"
 
 namespace {
@@ -678,6 +680,40 @@ namespace {
 
 constexpr int kBwdChunk = 16;
 
+// A second stream per device (default priority) and two events, so that the
+// backward's forward rerun runs beside prep, which does not read its
+// checkpoints.  Created on first use and kept until the process ends;
+// the mutex keeps the record/wait pairs of concurrent calls apart.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// with g_side_mu held
+SideStream *side_stream() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    SideStream &ss = g_side[dev];
+    if (!ss.s) {
+        hipStream_t st = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+            if (f) (void)hipEventDestroy(f);
+            (void)hipStreamDestroy(st);
+            return nullptr;
+        }
+        ss.s = st;
+        ss.fork = f;
+        ss.join = j;
+    }
+    return &ss;
+}
+
 struct BwdLayout {
     size_t o, S_T, ckpt, prep, part, dA, dsp, total;   // byte offsets, and the size
 };
@@ -766,18 +802,16 @@ kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
     const hipStream_t s = (hipStream_t)stream;
     const int64_t nfull = T / kBwdChunk;
     float *ckpt = bh > 0 ? reinterpret_cast<float *>(ws + lay.ckpt) : nullptr;
+    // bf16 d = 128 (MFMA path): the rerun writes states only (no o), its
+    // checkpoints in the 4-row block layout the backward reads
+    const bool mfma = kda::bwd_dsp_bytes(dtype, D) > 0;
     // forward with a checkpoint at every chunk boundary
-    if (bth > 0) {
-        // bf16 d = 128: states only (no o), checkpoints in the 4-row block
-        // layout the MFMA backward reads
-        const bool blocked = kda::bwd_dsp_bytes(dtype, D) > 0;
-        kda_status st = prefill_impl(dtype, B, T, H, dk, dv, kBwdChunk, nullptr, q, k, v, z, beta,
-                                     A, S0, blocked ? nullptr : ws + lay.o,
-                                     reinterpret_cast<float *>(ws + lay.S_T),
-                                     nfull > 0 ? kBwdChunk : 0, ckpt, B * nfull, nullptr, 0,
-                                     stream, blocked ? 64 : 0, blocked ? 1 : 0, false, blocked);
-        if (st != KDA_OK) return st;
-    }
+    auto rerun = [&](void *on, bool check_only) {
+        return prefill_impl(dtype, B, T, H, dk, dv, kBwdChunk, nullptr, q, k, v, z, beta, A, S0,
+                            mfma ? nullptr : ws + lay.o, reinterpret_cast<float *>(ws + lay.S_T),
+                            nfull > 0 ? kBwdChunk : 0, ckpt, B * nfull, nullptr, 0, on,
+                            mfma ? 64 : 0, mfma ? 1 : 0, check_only, mfma);
+    };
     kda::BwdArgs a;
     a.dtype = dtype; a.B = B; a.T = T; a.H = H; a.D = D; a.nchunk = nchunk;
     a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.dO = dO;
@@ -788,7 +822,31 @@ kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
     a.dsp = bh > 0 && lay.total > lay.dsp ? static_cast<void *>(ws + lay.dsp) : nullptr;
     a.dq = dq; a.dk = dk_out; a.dv = dv_out; a.dz = dz; a.dbeta = dbeta; a.dA = dA; a.dS0 = dS0;
     a.stream = s;
-    return kda::launch_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (!mfma || bth == 0) {
+        if (bth > 0) {
+            const kda_status st = rerun(stream, false);
+            if (st != KDA_OK) return st;
+        }
+        return kda::launch_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    // fork: the rerun on the side stream, prep here; join before the dS
+    // recurrence (run beside the rerun, two latency-bound chains slow each other)
+    {
+        const kda_status chk = rerun(nullptr, true);   // validation only, before any launch
+        if (chk != KDA_OK) return chk;
+    }
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream *ss = side_stream();
+    if (!ss) return KDA_ERR_HIP;
+    if (hipEventRecord(ss->fork, s) != hipSuccess ||
+        hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+        return KDA_ERR_HIP;
+    const kda_status st = rerun(ss->s, false);
+    if (hipEventRecord(ss->join, ss->s) != hipSuccess) return KDA_ERR_HIP;
+    if (st != KDA_OK) return st;
+    if (kda::launch_bwd_front(a) != hipSuccess) return KDA_ERR_HIP;
+    if (hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return KDA_ERR_HIP;
+    return kda::launch_bwd_back(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // extern "C"

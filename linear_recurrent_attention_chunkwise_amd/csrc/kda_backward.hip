@@ -1105,12 +1105,20 @@ static hipError_t launch_bwd_t(const BwdArgs &a) {
 }
 
 // bf16, d = 128: prep, the dS recurrence (dstate) and the chunk-parallel sums
-// (part) on MFMA tiles, then grad with a single column slice.
-static hipError_t launch_bwd_mfma(const BwdArgs &a) {
-    const int64_t bh = a.B * a.H, units = bh * a.nchunk;
+// (part) on MFMA tiles, then grad with a single column slice.  prep reads no
+// checkpoint (the front); the rest follows the forward rerun (the back).
+hipError_t launch_bwd_front(const BwdArgs &a) {
+    if (!(a.dtype == 1 && a.D == BD)) return hipErrorInvalidValue;
+    const int64_t units = a.B * a.H * a.nchunk;
     if (units > 0)
         hipLaunchKernelGGL((kda_bwd_prep_kernel<bf16, BD>), dim3((unsigned)units), dim3(256), 0,
                            a.stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_back(const BwdArgs &a) {
+    if (!(a.dtype == 1 && a.D == BD)) return hipErrorInvalidValue;
+    const int64_t bh = a.B * a.H, units = bh * a.nchunk;
     if (bh > 0)
         hipLaunchKernelGGL(kda_bwd_dstate_kernel<4>, dim3((unsigned)(bh * 2)), dim3(256), 0,
                            a.stream, a, static_cast<bf16 *>(a.dsp));
@@ -1124,6 +1132,11 @@ static hipError_t launch_bwd_mfma(const BwdArgs &a) {
         hipLaunchKernelGGL(kda_bwd_dA_kernel, dim3((unsigned)((a.H + 255) / 256)), dim3(256), 0,
                            a.stream, a.dA_part, a.dA, a.B, a.H, a.nchunk);
     return hipGetLastError();
+}
+
+static hipError_t launch_bwd_mfma(const BwdArgs &a) {
+    const hipError_t e = launch_bwd_front(a);
+    return e != hipSuccess ? e : launch_bwd_back(a);
 }
 
 size_t bwd_dsp_bytes(int dtype, int64_t D) { return dtype == 1 && D == 128 ? D * D * 2 : 0; }

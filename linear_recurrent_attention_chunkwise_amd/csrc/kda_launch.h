@@ -138,5 +138,9 @@ size_t bwd_prep_floats(int64_t D);   // per (b, h, chunk)
 size_t bwd_part_floats(int64_t D);   // per (b, h, chunk), all column slices
 size_t bwd_dsp_bytes(int dtype, int64_t D);   // per (b, h, chunk): 2*D*D on the MFMA path, else 0
 hipError_t launch_bwd(const BwdArgs &a);
+// the MFMA path (bf16, d = 128) in two halves: prep, which reads no state
+// checkpoint and may run beside the forward rerun, then the rest
+hipError_t launch_bwd_front(const BwdArgs &a);
+hipError_t launch_bwd_back(const BwdArgs &a);
 
 }  // namespace kda
