@@ -52,10 +52,11 @@ __device__ __forceinline__ float sigmoidf_(float x) {
 }
 
 // Per-chunk prep record in the workspace (floats):
-//   W [C][D], Qh [C][D], Kb [C][D], P [C][C], T [C][C], Gn [D] (= e^{G_n})
+//   W [C][D], Qh [C][D], Kb [C][D], P [C][C], T [C][C], Gn [D] (= e^{G_n}), A [C][C]
 template <int D> struct PrepLayout {
     static constexpr int W = 0, QH = C * D, KB = 2 * C * D, P = 3 * C * D, T = 3 * C * D + C * C,
-                         GN = 3 * C * D + 2 * C * C, SIZE = 3 * C * D + 2 * C * C + D;
+                         GN = 3 * C * D + 2 * C * C, A = 3 * C * D + 2 * C * C + D,
+                         SIZE = 3 * C * D + 3 * C * C + D;
 };
 
 // Per-(chunk, slice) partial record (floats):
@@ -117,9 +118,11 @@ __device__ __forceinline__ void load8(const float *p, float *out) {
     }
 }
 
-template <typename TI, int D>
+// SOLVE: form A, P and T here (prep); otherwise (grad) A and T are read from
+// the chunk's prep record `rec` and P is left unset.
+template <typename TI, int D, bool SOLVE>
 __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64_t h, int64_t c,
-                          int n) {
+                          int n, const float *rec = nullptr) {
     const TI *q = static_cast<const TI *>(p.q), *k = static_cast<const TI *>(p.k),
              *z = static_cast<const TI *>(p.z), *beta = static_cast<const TI *>(p.beta);
     const int64_t H = p.H;
@@ -128,6 +131,15 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
     // q, k, z: a thread takes 8 consecutive channels of one token row (16- or
     // 32-byte loads, all three issued before any use)
     constexpr int VEC = 8, NVEC = C * D / VEC;   // 256 for D = 128 (blockDim.x == 256)
+    f32x4 at4 = {0.f, 0.f, 0.f, 0.f};           // !SOLVE: A (threads < 64), T (64 .. 127)
+    if constexpr (!SOLVE) {
+        using Lay = PrepLayout<D>;
+        const int t = threadIdx.x;
+        if (t < C * C / 4)
+            at4 = reinterpret_cast<const f32x4 *>(rec + Lay::A)[t];
+        else if (t < C * C / 2)
+            at4 = reinterpret_cast<const f32x4 *>(rec + Lay::T)[t - C * C / 4];
+    }
     for (int t = threadIdx.x; t < NVEC; t += blockDim.x) {
         const int r = t / (D / VEC), d0 = VEC * (t % (D / VEC));
         float qv[VEC], kv[VEC], zv[VEC];
@@ -149,6 +161,15 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
     }
     for (int r = threadIdx.x; r < C; r += blockDim.x)
         s.beta[r] = r < n ? to_f32(beta[row0 + (int64_t)r * H]) : 0.f;
+    if constexpr (!SOLVE) {
+        const int t = threadIdx.x;
+        if (t < C * C / 2) {
+            const int f = 4 * (t % (C * C / 4)), r = f / C, s0 = f % C;
+            float(*M)[C + 1] = t < C * C / 4 ? s.A : s.T;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) M[r][s0 + e] = at4[e];
+        }
+    }
     __syncthreads();
     // cumulative log-decay over the chunk, applied to q and k
     for (int d = threadIdx.x; d < D; d += blockDim.x) {
@@ -164,18 +185,25 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
         }
     }
     __syncthreads();
+    if constexpr (!SOLVE) return;
     // A[r][s] = sum_d k_r k_s e^{G_r - G_s} (s < r),  P[r][s] = sum_d q_r k_s e^{G_r - G_s} (s <= r):
-    // Kh Ki^T and Qh Ki^T on fp32 matrix-core tiles, wave 0 and wave 1
+    // Kh Ki^T and Qh Ki^T on fp32 matrix-core tiles, wave 0 and wave 1 (two
+    // accumulators each, to halve the dependent chain)
     {
         const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
         const int g = lane >> 4, nn = lane & 15;
         constexpr int LDD = rowpad<D>();
         if (wave < 2) {
             const float *X = wave == 0 ? &s.Kh[0][0] : &s.Qh[0][0];
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k0 = 0; k0 < D; k0 += 16)
-                mma16(acc, rowfrag(X, LDD, 0, k0, lane), rowfrag(&s.Ki[0][0], LDD, 0, k0, lane));
+            for (int k0 = 0; k0 < D; k0 += 16) {
+                if ((k0 / 16) % 2 == 0)
+                    mma16(acc, rowfrag(X, LDD, 0, k0, lane), rowfrag(&s.Ki[0][0], LDD, 0, k0, lane));
+                else
+                    mma16(acc2, rowfrag(X, LDD, 0, k0, lane), rowfrag(&s.Ki[0][0], LDD, 0, k0, lane));
+            }
+            acc += acc2;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g + e;
@@ -218,7 +246,7 @@ __global__ __launch_bounds__(256) void kda_bwd_prep_kernel(BwdArgs p) {
     const int64_t c = x % p.nchunk, bh = x / p.nchunk;
     const int64_t b = bh / p.H, h = bh % p.H;
     const int n = (int)(p.T - c * C < C ? p.T - c * C : C);
-    chunk_ops<TI, D>(s, p, b, h, c, n);
+    chunk_ops<TI, D, true>(s, p, b, h, c, n);
     float *rec = p.prep + x * (int64_t)Lay::SIZE;
     for (int i = threadIdx.x; i < C * D; i += blockDim.x) {
         const int r = i / D, d = i % D;
@@ -231,6 +259,7 @@ __global__ __launch_bounds__(256) void kda_bwd_prep_kernel(BwdArgs p) {
     for (int i = threadIdx.x; i < C * C; i += blockDim.x) {
         rec[Lay::P + i] = s.P[i / C][i % C];
         rec[Lay::T + i] = s.T[i / C][i % C];
+        rec[Lay::A + i] = s.A[i / C][i % C];
     }
     for (int d = threadIdx.x; d < D; d += blockDim.x) rec[Lay::GN + d] = s.E[C - 1][d];
 }
@@ -812,9 +841,10 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
 template <typename TI, int D> struct GradLds {
     ChunkOps<TI, D> o;
     float dW[C][rowpad<D>()];
-    float dP[C][C + 1], dTV[C][C + 1], dT[C][C + 1], M1[C][C + 1], dL[C][C + 1];
+    float dP[C][C + 1], dTV[C][C + 1], dL[C][C + 1];
     float dbV[C], dGn[D];
     float dbk[4][C];   // per-wave sums over d of (T^T dW)[r][d] Kh[r][d]
+    float dbL[C];      // sum_s dL[r][s] A[r][s]
 };
 
 template <typename TI, int D, int NS>
@@ -827,7 +857,7 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     const int64_t b = bh / p.H, h = bh % p.H, H = p.H;
     const int n = (int)(p.T - c * C < C ? p.T - c * C : C);
     const int tid = threadIdx.x;
-    chunk_ops<TI, D>(s.o, p, b, h, c, n);
+    chunk_ops<TI, D, false>(s.o, p, b, h, c, n, p.prep + x * (int64_t)PrepLayout<D>::SIZE);
     // the slices' partial sums, added in slice order (4-float loads, all issued
     // before any use; blockDim.x == 256)
     const float *part = p.part + x * NS * (int64_t)PL::SIZE;
@@ -914,17 +944,39 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     }
     __syncthreads();
     auto &o = s.o;
-    // dT = dW (beta K^)^T + dU (beta V)^T: a 16 x 16 tile over d (wave 0)
+    // wave 0: dT = dW (beta K^)^T + dU (beta V)^T (a 16 x 16 tile over d), then
+    // dL = -(T^T dT) T^T (strictly lower), its share of dbeta and dA = diag(beta) dL,
+    // all on fp32 matrix-core tiles in registers.  A tile in accumulator layout
+    // (lane (g, n) holds X[4g+e][n]) is the B operand of X and the A operand of X^T.
     if (wave == 0) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k0 = 0; k0 < D; k0 += 16)
-            mma16(acc, rowfrag(&s.dW[0][0], LDD, 0, k0, lane), rowfrag(&o.Kh[0][0], LDD, 0, k0, lane));
+        for (int k0 = 0; k0 < D; k0 += 16) {
+            if ((k0 / 16) % 2 == 0)
+                mma16(acc, rowfrag(&s.dW[0][0], LDD, 0, k0, lane), rowfrag(&o.Kh[0][0], LDD, 0, k0, lane));
+            else
+                mma16(acc2, rowfrag(&s.dW[0][0], LDD, 0, k0, lane), rowfrag(&o.Kh[0][0], LDD, 0, k0, lane));
+        }
+        Frag<float> dTf;   // dT[4g+e][nn]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dTf.v[e] = s.dTV[4 * g + e][nn] + o.beta[nn] * (acc[e] + acc2[e]);
+        f32x4 m1t = {0.f, 0.f, 0.f, 0.f};   // M1^T = dT^T T:  M1^T[4g+e][nn]
+        mma16(m1t, dTf, colfrag(&o.T[0][0], LDC, 0, 0, lane));
+        Frag<float> m1f;
+        m1f.v = m1t;
+        f32x4 tm = {0.f, 0.f, 0.f, 0.f};    // T M1^T = -dL^T:  -dL[nn][4g+e]
+        mma16(tm, rowfrag(&o.T[0][0], LDC, 0, 0, lane), m1f);
+        float lb = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            s.dT[r][nn] = s.dTV[r][nn] + o.beta[nn] * acc[e];
+            const int sc = 4 * g + e;
+            const float dl = sc < nn ? -tm[e] : 0.f;   // dL[nn][sc]
+            lb += dl * o.A[nn][sc];
+            s.dL[nn][sc] = dl * o.beta[nn];            // now dA
         }
+        lb += __shfl_xor(lb, 16);
+        lb += __shfl_xor(lb, 32);
+        if (g == 0) s.dbL[nn] = lb;
     }
     // T^T dW: wave w takes the 16-column tiles w, w+4, ..., keeps them in
     // registers for dk below, and sums its share of (T^T dW) . K^ per row
@@ -949,34 +1001,13 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
         }
     }
     __syncthreads();
-    // M1 = T^T dT;  dL = -M1 T^T (strictly lower)
-    for (int i = tid; i < C * C; i += blockDim.x) {
-        const int r = i / C, sc = i % C;
-        float a = 0.f;
-        for (int u = 0; u < C; ++u) a += o.T[u][r] * s.dT[u][sc];
-        s.M1[r][sc] = a;
-    }
-    __syncthreads();
-    for (int i = tid; i < C * C; i += blockDim.x) {
-        const int r = i / C, sc = i % C;
-        float a = 0.f;
-        for (int u = 0; u < C; ++u) a += s.M1[r][u] * o.T[sc][u];
-        s.dL[r][sc] = sc < r ? -a : 0.f;
-    }
-    __syncthreads();
     // dbeta: V part, K^ part (through W), L part
     if (tid < C) {
         const int r = tid;
-        float a = s.dbV[r] + ((s.dbk[0][r] + s.dbk[1][r]) + (s.dbk[2][r] + s.dbk[3][r]));
-        for (int sc = 0; sc < C; ++sc) a += s.dL[r][sc] * o.A[r][sc];
+        const float a = s.dbV[r] + ((s.dbk[0][r] + s.dbk[1][r]) + (s.dbk[2][r] + s.dbk[3][r])) +
+                        s.dbL[r];
         if (r < n) p.dbeta[(b * p.T + c * C + r) * H + h] = a;
     }
-    __syncthreads();
-    for (int i = tid; i < C * C; i += blockDim.x) {
-        const int r = i / C, sc = i % C;
-        s.dL[r][sc] *= o.beta[r];   // now dA
-    }
-    __syncthreads();
     // dq, dk, dG and dz on the same column tiles:
     //   dQ^ += dP Ki,  dK^ = dA Ki + beta (T^T dW),  dKi = dA^T K^ + dP^T Q^
     // (products over the 16 tokens s on fp32 matrix-core tiles).  A tile's
