@@ -236,10 +236,11 @@ size_t kda_prefill_split_workspace_size(int dtype, int64_t B, int64_t T, int64_t
  * in bf16 in the workspace); every other case, and all per-token work, is
  * fp32.  No atomics, so results are bitwise reproducible.
  * Streams: all work is ordered after earlier work on `stream`, and later work
- * on `stream` sees every output.  On that bf16 dk = dv = 128 path the forward
- * rerun runs on a library-owned stream of the current device (created on the
- * first call, default priority) beside the first backward kernel, joined
- * back to `stream` with events; the calls serialise that fork under a lock.
+ * on `stream` sees every output.  On that bf16 dk = dv = 128 path the first
+ * backward kernel runs on a library-owned stream of the current device
+ * (created on the first call, default priority) beside the forward rerun,
+ * forked from and joined back to `stream` with events; the calls serialise
+ * that fork under a lock.
  * Supported: dtype in {KDA_F32, KDA_BF16}, dk == dv in {16, 128}.  Outputs
  * must not overlap one another, any input or the workspace.  Errors as
  * kda_prefill_ex.

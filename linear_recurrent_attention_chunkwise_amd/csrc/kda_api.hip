@@ -681,8 +681,7 @@ namespace {
 constexpr int kBwdChunk = 16;
 
 // A second stream per device (default priority) and two events, so that the
-// backward's forward rerun runs beside prep, which does not read its
-// checkpoints.  Created on first use and kept until the process ends;
+// backward's prep runs beside its forward rerun (prep reads no checkpoint).  Created on first use and kept until the process ends;
 // the mutex keeps the record/wait pairs of concurrent calls apart.
 struct SideStream {
     hipStream_t s = nullptr;
@@ -829,8 +828,10 @@ kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
         }
         return kda::launch_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
-    // fork: the rerun on the side stream, prep here; join before the dS
-    // recurrence (run beside the rerun, two latency-bound chains slow each other)
+    // fork: the rerun here (launched first and behind no event wait, so that
+    // its 192 large workgroups get their CUs before prep's many small ones),
+    // prep on the side stream; join before the dS recurrence (run beside the
+    // rerun, two latency-bound chains slow each other)
     {
         const kda_status chk = rerun(nullptr, true);   // validation only, before any launch
         if (chk != KDA_OK) return chk;
@@ -838,14 +839,15 @@ kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream *ss = side_stream();
     if (!ss) return KDA_ERR_HIP;
-    if (hipEventRecord(ss->fork, s) != hipSuccess ||
-        hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
-        return KDA_ERR_HIP;
-    const kda_status st = rerun(ss->s, false);
-    if (hipEventRecord(ss->join, ss->s) != hipSuccess) return KDA_ERR_HIP;
+    if (hipEventRecord(ss->fork, s) != hipSuccess) return KDA_ERR_HIP;
+    const kda_status st = rerun(stream, false);
     if (st != KDA_OK) return st;
-    if (kda::launch_bwd_front(a) != hipSuccess) return KDA_ERR_HIP;
-    if (hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return KDA_ERR_HIP;
+    kda::BwdArgs af = a;
+    af.stream = ss->s;
+    if (hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess ||
+        kda::launch_bwd_front(af) != hipSuccess || hipEventRecord(ss->join, ss->s) != hipSuccess ||
+        hipStreamWaitEvent(s, ss->join, 0) != hipSuccess)
+        return KDA_ERR_HIP;
     return kda::launch_bwd_back(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -144,6 +144,36 @@ def test_backward_is_deterministic(kda, gpu_device):
         assert torch.equal(a[key], b[key]), key
 
 
+def test_backward_on_a_caller_stream_is_ordered(kda, gpu_device):
+    """bf16 d = 128 forks its forward rerun onto a library stream.  On a caller
+    stream, behind long work that writes the inputs just before the call, the
+    rerun must read the written inputs, the later kernels its checkpoints (the
+    workspace starts as NaN bytes), and the caller stream's next work must see
+    every output: the results equal a default-stream call bit for bit."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(B=1, H=4, s0_std=0.5)
+    T = 300
+    g = to_dev(make_prefill_inputs(w, T=T), gpu_device)
+    dO, dST = (t.to(gpu_device) for t in make_cotangents(w, T=T))
+    ref = _gpu_bwd(kda, g, dO, dST)
+    nbytes = kda.prefill_bwd_workspace_size(torch.bfloat16, w.B, T, w.H, w.dk, w.dv)
+    s = torch.cuda.Stream(device=gpu_device)
+    x = torch.randn(2048, 2048, device=gpu_device)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        late = {k: torch.empty_like(v) for k, v in g.items() if isinstance(v, torch.Tensor)}
+        ws = torch.full((nbytes,), 255, dtype=torch.uint8, device=gpu_device)
+        for _ in range(20):                      # ~ms of work ahead of the input writes
+            x = torch.tanh(x @ x) * 0.05
+        for k in late:
+            late[k].copy_(g[k])
+        got = kda.prefill_bwd(late["q"], late["k"], late["v"], late["z"], late["beta"],
+                              late["A"], late["S0"], dO, dST, workspace=ws)
+        copies = {k: t.clone() for k, t in got.items()}
+    s.synchronize()
+    for key in ref:
+        assert torch.equal(ref[key], copies[key]), key
+
+
 def test_backward_k3_full_size_sampled_heads(kda, gpu_device):
     """B1 H96 T4096 bf16 (the K3 prefill workload) in one call; heads 0, 47
     and 95 against the oracle (the oracle runs per head, so a subset of heads
