@@ -248,11 +248,23 @@ __global__ __launch_bounds__(256) void kda_bwd_prep_kernel(BwdArgs p) {
     const int n = (int)(p.T - c * C < C ? p.T - c * C : C);
     chunk_ops<TI, D, true>(s, p, b, h, c, n);
     float *rec = p.prep + x * (int64_t)Lay::SIZE;
+    // W = T diag(beta) Kh on fp32 matrix-core tiles: wave w takes the 16-column
+    // tiles w, w+4, ...; lane (g, nn) gets W[4g+e][16t+nn]  (blockDim.x == 256)
+    {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, nn = lane & 15;
+        constexpr int LDD = rowpad<D>();
+        Frag<float> tb;   // A operand: T[nn][4g+e] beta[4g+e]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tb.v[e] = s.T[nn][4 * g + e] * s.beta[4 * g + e];
+        for (int t = wave; t < D / 16; t += 4) {
+            f32x4 w = {0.f, 0.f, 0.f, 0.f};
+            mma16(w, tb, colfrag(&s.Kh[0][0], LDD, 0, 16 * t, lane));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rec[Lay::W + (4 * g + e) * D + 16 * t + nn] = w[e];
+        }
+    }
     for (int i = threadIdx.x; i < C * D; i += blockDim.x) {
         const int r = i / D, d = i % D;
-        float w = 0.f;
-        for (int sc = 0; sc < C; ++sc) w += s.T[r][sc] * s.beta[sc] * s.Kh[sc][d];
-        rec[Lay::W + i] = w;
         rec[Lay::QH + i] = s.Qh[r][d];
         rec[Lay::KB + i] = s.Ki[r][d] * s.E[C - 1][d];
     }
