@@ -631,11 +631,15 @@ struct PartLds {
 };
 }  // namespace
 
-__global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16 *dsp) {
+// 16 waves per chunk (the LDS of one chunk allows one workgroup per CU, so
+// its waves are what hides latency): value-column phase split into U (waves
+// 0-7) and dU (waves 8-15), key-row phase into dQ^, dW (0-7) and dKb, dP,
+// dT's V part (8-15).
+__global__ __launch_bounds__(1024) void kda_bwd_part_kernel(BwdArgs p, const bf16 *dsp) {
     using Lay = PrepLayout<BD>;
     using PL = PartLayout<BD>;
     __shared__ __attribute__((aligned(16))) PartLds s;
-    static_assert(sizeof(PartLds) <= 150 * 1024, "LDS budget");   // blockDim.x == 512
+    static_assert(sizeof(PartLds) <= 150 * 1024, "LDS budget");   // blockDim.x == 1024
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
@@ -661,34 +665,30 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
                                 : nullptr;
         const bf16 *Dt = dsp + x * (int64_t)(BD * BD);   // 4-row blocks, as dstate stores them
         const float *rec = p.prep + x * (int64_t)Lay::SIZE;
-        f32x4 sv[2][4];    // sv[u][r] = S[d0 + r][j0 .. j0+3]
-        bf16x4 tv[2][4];   // tv[u][e] = dS'[d0 .. d0+3][j0 + e]
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int d0 = 4 * (tid / 32 + 16 * u), j0 = 4 * (tid % 32);
-            if (c == 0) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sv[u][e] = Sin ? *reinterpret_cast<const f32x4 *>(Sin + (d0 + e) * BD + j0)
-                                   : f32x4{0.f, 0.f, 0.f, 0.f};
-            } else {
-                bf16x4 cv[4];   // cv[e] = S[d0 .. d0+3][j0 + e]
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    cv[e] = *reinterpret_cast<const bf16x4 *>(Ck + ((d0 / 4) * BD + j0 + e) * 4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sv[u][r] = f32x4{(float)cv[0][r], (float)cv[1][r], (float)cv[2][r], (float)cv[3][r]};
-            }
+        const int d0 = 4 * (tid / 32), j0 = 4 * (tid % 32);
+        f32x4 sv[4];    // sv[r] = S[d0 + r][j0 .. j0+3]
+        bf16x4 tv[4];   // tv[e] = dS'[d0 .. d0+3][j0 + e]
+        if (c == 0) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                tv[u][e] = *reinterpret_cast<const bf16x4 *>(Dt + ((d0 / 4) * BD + j0 + e) * 4);
+                sv[e] = Sin ? *reinterpret_cast<const f32x4 *>(Sin + (d0 + e) * BD + j0)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+            bf16x4 cv[4];   // cv[e] = S[d0 .. d0+3][j0 + e]
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                cv[e] = *reinterpret_cast<const bf16x4 *>(Ck + ((d0 / 4) * BD + j0 + e) * 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sv[r] = f32x4{(float)cv[0][r], (float)cv[1][r], (float)cv[2][r], (float)cv[3][r]};
         }
-        // the chunk's W, Kb (one float4 of each per thread), T or P rows, beta,
-        // and one 16-byte piece of a V or dO row
-        const int rW = tid / 32, dW = 4 * (tid % 32);
-        const f32x4 w4 = reinterpret_cast<const f32x4 *>(rec + Lay::W)[tid];
-        const f32x4 k4 = reinterpret_cast<const f32x4 *>(rec + Lay::KB)[tid];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            tv[e] = *reinterpret_cast<const bf16x4 *>(Dt + ((d0 / 4) * BD + j0 + e) * 4);
+        // one float4 of W (threads 0-511) or Kb (512-1023), T or P rows, beta,
+        // and one 16-byte piece of a V (0-255) or dO (256-511) row
+        const int t5 = tid & 511, rW = t5 / 32, dW = 4 * (t5 % 32);
+        const f32x4 wk4 = reinterpret_cast<const f32x4 *>(rec + (tid < 512 ? Lay::W : Lay::KB))[t5];
         f32x4 tp4 = {0.f, 0.f, 0.f, 0.f};
         if (tid < C * C / 4)
             tp4 = reinterpret_cast<const f32x4 *>(rec + Lay::T)[tid];
@@ -699,34 +699,29 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
         if (rb >= 0 && rb < nv) bv = (float)betag[row0 + (int64_t)rb * H];
         const int t2 = tid & 255, rv = t2 / 16, pc = t2 % 16;
         uint4 val = {0u, 0u, 0u, 0u};
-        if (rv < nv)
+        if (tid < 512 && rv < nv)
             val = *reinterpret_cast<const uint4 *>((tid < 256 ? v : dOg) +
                                                    (row0 + (int64_t)rv * H) * BD + 8 * pc);
 
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int d0 = 4 * (tid / 32 + 16 * u), j0 = 4 * (tid % 32);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                store_bf16x4(&s.S[d0 + e][j0], sv[u][e][0], sv[u][e][1], sv[u][e][2], sv[u][e][3]);
-                *reinterpret_cast<bf16x4 *>(&s.dS[d0 + e][j0]) =
-                    bf16x4{tv[u][0][e], tv[u][1][e], tv[u][2][e], tv[u][3][e]};
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // row d0 + r: S[d0+r][j0+e] * dS'[d0+r][j0+e]
-                float a = sv[u][r][0] * (float)tv[u][0][r] + sv[u][r][1] * (float)tv[u][1][r] +
-                          sv[u][r][2] * (float)tv[u][2][r] + sv[u][r][3] * (float)tv[u][3][r];
-                a += __shfl_xor(a, 16, 32);
-                a += __shfl_xor(a, 8, 32);
-                a += __shfl_xor(a, 4, 32);
-                a += __shfl_xor(a, 2, 32);
-                a += __shfl_xor(a, 1, 32);
-                if ((tid & 31) == 0) part[PL::DGN + d0 + r] = a;
-            }
+        for (int e = 0; e < 4; ++e) {
+            store_bf16x4(&s.S[d0 + e][j0], sv[e][0], sv[e][1], sv[e][2], sv[e][3]);
+            *reinterpret_cast<bf16x4 *>(&s.dS[d0 + e][j0]) =
+                bf16x4{tv[0][e], tv[1][e], tv[2][e], tv[3][e]};
         }
-        store_bf16x4(&s.W[rW][dW], w4[0], w4[1], w4[2], w4[3]);
-        store_bf16x4(&s.Kb[rW][dW], k4[0], k4[1], k4[2], k4[3]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            // row d0 + r: S[d0+r][j0+e] * dS'[d0+r][j0+e]
+            float a = sv[r][0] * (float)tv[0][r] + sv[r][1] * (float)tv[1][r] +
+                      sv[r][2] * (float)tv[2][r] + sv[r][3] * (float)tv[3][r];
+            a += __shfl_xor(a, 16, 32);
+            a += __shfl_xor(a, 8, 32);
+            a += __shfl_xor(a, 4, 32);
+            a += __shfl_xor(a, 2, 32);
+            a += __shfl_xor(a, 1, 32);
+            if ((tid & 31) == 0) part[PL::DGN + d0 + r] = a;
+        }
+        store_bf16x4(tid < 512 ? &s.W[rW][dW] : &s.Kb[rW][dW], wk4[0], wk4[1], wk4[2], wk4[3]);
         if (tid < C * C / 4) {
             // T row rr, columns s0 .. s0+3 (beta is applied to V below)
             const int rr = tid / 4, s0 = 4 * (tid % 4);
@@ -742,108 +737,135 @@ __global__ __launch_bounds__(512) void kda_bwd_part_kernel(BwdArgs p, const bf16
             for (int e = 0; e < 4; ++e) s.PT[r0 + e][sidx] = (bf16)tp4[e];
         }
         if (rb >= 0 && rb < C) s.beta[rb] = bv;
-        *reinterpret_cast<uint4 *>(tid < 256 ? &s.V[rv][8 * pc] : &s.dO[rv][8 * pc]) = val;
+        if (tid < 512)
+            *reinterpret_cast<uint4 *>(tid < 256 ? &s.V[rv][8 * pc] : &s.dO[rv][8 * pc]) = val;
     }
     __syncthreads();
 
-    // ---- wave w: value columns jw .. jw+15: U, dU, T^T dU, dV, dbeta's V part ----
+    // ---- value columns jw .. jw+15: U = T diag(b) V - W S (waves 0-7);
+    //      dU = P^T dO + Kb dS', T^T dU, dV, dbeta's V part (waves 8-15) ----
     {
-        const int jw = 16 * wave;
+        const int jw = 16 * (wave & 7);
         const Frag<bf16> Vf = frag_rows(&s.V[0][0], BLD, 0, jw + n, lane);
-        const Frag<bf16> dOf = frag_rows(&s.dO[0][0], BLD, 0, jw + n, lane);
-        Frag<bf16> bVf;   // diag(beta) V, rows 4g + e
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+        if (wave < 8) {
+            Frag<bf16> bVf;   // diag(beta) V, rows 4g + e
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bVf.v[e] = (bf16)(s.beta[4 * g + e] * (float)Vf.v[e]);
-        f32x4 ta = {0.f, 0.f, 0.f, 0.f}, tb = {0.f, 0.f, 0.f, 0.f};   // U = T diag(b) V - W S
-        f32x4 da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};   // dU = P^T dO + Kb dS'
-        mma16(ta, lds_frag(&s.Tb[0][0], BLT, 0, lane), bVf);
-        mma16(da, lds_frag(&s.PT[0][0], BLT, 0, lane), dOf);
-#pragma unroll
-        for (int i = 0; i < BD / 16; i += 2) {
-            mma32(tb, lds_frag(&s.W[0][0], BLD, 16 * i, lane), lds_frag(&s.W[0][0], BLD, 16 * i + 16, lane),
-                  frag_rows(&s.S[0][0], BLD, 16 * i, jw + n, lane),
-                  frag_rows(&s.S[0][0], BLD, 16 * i + 16, jw + n, lane));
-            mma32(db, lds_frag(&s.Kb[0][0], BLD, 16 * i, lane), lds_frag(&s.Kb[0][0], BLD, 16 * i + 16, lane),
-                  frag_rows(&s.dS[0][0], BLD, 16 * i, jw + n, lane),
-                  frag_rows(&s.dS[0][0], BLD, 16 * i + 16, jw + n, lane));
-        }
-        const f32x4 U = ta - tb, dU = da + db;
-        // U and dU enter the products below as bf16 pairs hi + lo
-        const Frag<bf16> dUh = acc_frag<bf16>(dU);
-        f32x4 dUl4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dUl4[e] = dU[e] - (float)dUh.v[e];
-        f32x4 BV = {0.f, 0.f, 0.f, 0.f};
-        const Frag<bf16> TTf = lds_frag(&s.TT[0][0], BLT, 0, lane);
-        mma16(BV, TTf, dUh);
-        mma16(BV, TTf, acc_frag<bf16>(dUl4));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            const bf16 uh = (bf16)U[e];
-            s.U[r][jw + n] = uh;
-            s.Ulo[r][jw + n] = (bf16)(U[e] - (float)uh);
-            s.dU[r][jw + n] = dUh.v[e];
-            s.dUlo[r][jw + n] = (bf16)dUl4[e];
-            if (r < nv) p.dv[(row0 + (int64_t)r * H) * BD + jw + n] = s.beta[r] * BV[e];
-            const float part_bv = sum16(BV[e] * (float)Vf.v[e]);
-            if (n == 0) s.dbV[wave][r] = part_bv;
-        }
-    }
-    __syncthreads();
-
-    // ---- wave w: key rows dw .. dw+15 of dQ^, dW, dKb (sums over all columns) ----
-    {
-        const int dw = 16 * wave;
-        f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < BD / 16; i += 2) {
-            const Frag<bf16> s0 = lds_frag(&s.S[dw][0], BLD, 16 * i, lane),
-                             s1 = lds_frag(&s.S[dw][0], BLD, 16 * i + 16, lane);
-            mma32(aq, lds_frag(&s.dO[0][0], BLD, 16 * i, lane), lds_frag(&s.dO[0][0], BLD, 16 * i + 16, lane),
-                  s0, s1);
-            mma32(aw, lds_frag(&s.dU[0][0], BLD, 16 * i, lane), lds_frag(&s.dU[0][0], BLD, 16 * i + 16, lane),
-                  s0, s1);
-            mma32(aw, lds_frag(&s.dUlo[0][0], BLD, 16 * i, lane),
-                  lds_frag(&s.dUlo[0][0], BLD, 16 * i + 16, lane), s0, s1);
-            const Frag<bf16> t0 = lds_frag(&s.dS[dw][0], BLD, 16 * i, lane),
-                             t1 = lds_frag(&s.dS[dw][0], BLD, 16 * i + 16, lane);
-            mma32(ak, lds_frag(&s.U[0][0], BLD, 16 * i, lane), lds_frag(&s.U[0][0], BLD, 16 * i + 16, lane),
-                  t0, t1);
-            mma32(ak, lds_frag(&s.Ulo[0][0], BLD, 16 * i, lane),
-                  lds_frag(&s.Ulo[0][0], BLD, 16 * i + 16, lane), t0, t1);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            part[PL::DQH + r * BD + dw + n] = aq[e];
-            part[PL::DW + r * BD + dw + n] = -aw[e];
-            part[PL::DKB + r * BD + dw + n] = ak[e];
-        }
-        if (wave == 0 || wave == 1) {
-            // dP = dO U^T (wave 0);  dT's V part = dU (beta V)^T (wave 1)
-            // (U, dU as hi + lo pairs)
-            const bf16 *A = wave == 0 ? &s.dO[0][0] : &s.dU[0][0];
-            const bf16 *Bm = wave == 0 ? &s.U[0][0] : &s.V[0][0];
-            const bf16 *A2 = wave == 0 ? &s.dO[0][0] : &s.dUlo[0][0];
-            const bf16 *B2 = wave == 0 ? &s.Ulo[0][0] : &s.V[0][0];
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < 4; ++e) bVf.v[e] = (bf16)(s.beta[4 * g + e] * (float)Vf.v[e]);
+            mma16(a0, lds_frag(&s.Tb[0][0], BLT, 0, lane), bVf);
 #pragma unroll
             for (int i = 0; i < BD / 16; i += 2) {
-                mma32(acc, lds_frag(A, BLD, 16 * i, lane), lds_frag(A, BLD, 16 * i + 16, lane),
-                      lds_frag(Bm, BLD, 16 * i, lane), lds_frag(Bm, BLD, 16 * i + 16, lane));
-                mma32(acc, lds_frag(A2, BLD, 16 * i, lane), lds_frag(A2, BLD, 16 * i + 16, lane),
-                      lds_frag(B2, BLD, 16 * i, lane), lds_frag(B2, BLD, 16 * i + 16, lane));
+                f32x4 &acc = (i / 2) % 2 == 0 ? a1 : a2;
+                mma32(acc, lds_frag(&s.W[0][0], BLD, 16 * i, lane),
+                      lds_frag(&s.W[0][0], BLD, 16 * i + 16, lane),
+                      frag_rows(&s.S[0][0], BLD, 16 * i, jw + n, lane),
+                      frag_rows(&s.S[0][0], BLD, 16 * i + 16, jw + n, lane));
             }
-            const float sc = wave == 0 ? 1.f : s.beta[n];
+            const f32x4 U = a0 - (a1 + a2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                const bf16 uh = (bf16)U[e];
+                s.U[r][jw + n] = uh;
+                s.Ulo[r][jw + n] = (bf16)(U[e] - (float)uh);
+            }
+        } else {
+            const Frag<bf16> dOf = frag_rows(&s.dO[0][0], BLD, 0, jw + n, lane);
+            mma16(a0, lds_frag(&s.PT[0][0], BLT, 0, lane), dOf);
+#pragma unroll
+            for (int i = 0; i < BD / 16; i += 2) {
+                f32x4 &acc = (i / 2) % 2 == 0 ? a1 : a2;
+                mma32(acc, lds_frag(&s.Kb[0][0], BLD, 16 * i, lane),
+                      lds_frag(&s.Kb[0][0], BLD, 16 * i + 16, lane),
+                      frag_rows(&s.dS[0][0], BLD, 16 * i, jw + n, lane),
+                      frag_rows(&s.dS[0][0], BLD, 16 * i + 16, jw + n, lane));
+            }
+            const f32x4 dU = a0 + (a1 + a2);
+            // dU enters the products below as a bf16 pair hi + lo
+            const Frag<bf16> dUh = acc_frag<bf16>(dU);
+            f32x4 dUl4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dUl4[e] = dU[e] - (float)dUh.v[e];
+            f32x4 BV = {0.f, 0.f, 0.f, 0.f};
+            const Frag<bf16> TTf = lds_frag(&s.TT[0][0], BLT, 0, lane);
+            mma16(BV, TTf, dUh);
+            mma16(BV, TTf, acc_frag<bf16>(dUl4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                s.dU[r][jw + n] = dUh.v[e];
+                s.dUlo[r][jw + n] = (bf16)dUl4[e];
+                if (r < nv) p.dv[(row0 + (int64_t)r * H) * BD + jw + n] = s.beta[r] * BV[e];
+                const float part_bv = sum16(BV[e] * (float)Vf.v[e]);
+                if (n == 0) s.dbV[wave - 8][r] = part_bv;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- key rows dw .. dw+15 (sums over all columns): dQ^ and dW (waves
+    //      0-7), dKb (8-15); dP (wave 8) and dT's V part (wave 9) ----
+    {
+        const int dw = 16 * (wave & 7);
+        if (wave < 8) {
+            f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < BD / 16; i += 2) {
+                const Frag<bf16> s0 = lds_frag(&s.S[dw][0], BLD, 16 * i, lane),
+                                 s1 = lds_frag(&s.S[dw][0], BLD, 16 * i + 16, lane);
+                mma32(aq, lds_frag(&s.dO[0][0], BLD, 16 * i, lane),
+                      lds_frag(&s.dO[0][0], BLD, 16 * i + 16, lane), s0, s1);
+                mma32(aw, lds_frag(&s.dU[0][0], BLD, 16 * i, lane),
+                      lds_frag(&s.dU[0][0], BLD, 16 * i + 16, lane), s0, s1);
+                mma32(aw, lds_frag(&s.dUlo[0][0], BLD, 16 * i, lane),
+                      lds_frag(&s.dUlo[0][0], BLD, 16 * i + 16, lane), s0, s1);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                part[PL::DQH + r * BD + dw + n] = aq[e];
+                part[PL::DW + r * BD + dw + n] = -aw[e];
+            }
+        } else {
+            f32x4 ak = {0.f, 0.f, 0.f, 0.f}, ak2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < BD / 16; i += 2) {
+                const Frag<bf16> t0 = lds_frag(&s.dS[dw][0], BLD, 16 * i, lane),
+                                 t1 = lds_frag(&s.dS[dw][0], BLD, 16 * i + 16, lane);
+                mma32(ak, lds_frag(&s.U[0][0], BLD, 16 * i, lane),
+                      lds_frag(&s.U[0][0], BLD, 16 * i + 16, lane), t0, t1);
+                mma32(ak2, lds_frag(&s.Ulo[0][0], BLD, 16 * i, lane),
+                      lds_frag(&s.Ulo[0][0], BLD, 16 * i + 16, lane), t0, t1);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                part[(wave == 0 ? PL::DP : PL::DTV) + (4 * g + e) * C + n] = acc[e] * sc;
-        } else if (wave == 2 && lane < C) {
-            float a = 0.f;
+                part[PL::DKB + (4 * g + e) * BD + dw + n] = ak[e] + ak2[e];
+            if (wave == 8 || wave == 9) {
+                // dP = dO U^T (wave 8);  dT's V part = dU (beta V)^T (wave 9)
+                // (U, dU as hi + lo pairs)
+                const bool w8 = wave == 8;
+                const bf16 *A = w8 ? &s.dO[0][0] : &s.dU[0][0];
+                const bf16 *Bm = w8 ? &s.U[0][0] : &s.V[0][0];
+                const bf16 *A2 = w8 ? &s.dO[0][0] : &s.dUlo[0][0];
+                const bf16 *B2 = w8 ? &s.Ulo[0][0] : &s.V[0][0];
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int w = 0; w < 8; ++w) a += s.dbV[w][lane];
-            part[PL::DBV + lane] = a;
+                for (int i = 0; i < BD / 16; i += 2) {
+                    mma32(acc, lds_frag(A, BLD, 16 * i, lane), lds_frag(A, BLD, 16 * i + 16, lane),
+                          lds_frag(Bm, BLD, 16 * i, lane), lds_frag(Bm, BLD, 16 * i + 16, lane));
+                    mma32(acc2, lds_frag(A2, BLD, 16 * i, lane), lds_frag(A2, BLD, 16 * i + 16, lane),
+                          lds_frag(B2, BLD, 16 * i, lane), lds_frag(B2, BLD, 16 * i + 16, lane));
+                }
+                const float sc = w8 ? 1.f : s.beta[n];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    part[(w8 ? PL::DP : PL::DTV) + (4 * g + e) * C + n] = (acc[e] + acc2[e]) * sc;
+            } else if (wave == 10 && lane < C) {
+                float a = 0.f;
+#pragma unroll
+                for (int w = 0; w < 8; ++w) a += s.dbV[w][lane];
+                part[PL::DBV + lane] = a;
+            }
         }
     }
 }
@@ -1166,7 +1188,7 @@ hipError_t launch_bwd_back(const BwdArgs &a) {
         hipLaunchKernelGGL(kda_bwd_dstate_kernel<4>, dim3((unsigned)(bh * 2)), dim3(256), 0,
                            a.stream, a, static_cast<bf16 *>(a.dsp));
     if (units > 0) {
-        hipLaunchKernelGGL(kda_bwd_part_kernel, dim3((unsigned)units), dim3(512), 0, a.stream, a,
+        hipLaunchKernelGGL(kda_bwd_part_kernel, dim3((unsigned)units), dim3(1024), 0, a.stream, a,
                            static_cast<const bf16 *>(a.dsp));
         hipLaunchKernelGGL((kda_bwd_grad_kernel<bf16, BD, 1>), dim3((unsigned)units), dim3(256), 0,
                            a.stream, a);
