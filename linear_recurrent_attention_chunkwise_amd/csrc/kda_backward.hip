@@ -118,11 +118,9 @@ __device__ __forceinline__ void load8(const float *p, float *out) {
     }
 }
 
-// SOLVE: form A, P and T here (prep); otherwise (grad) A and T are read from
-// the chunk's prep record `rec` and P is left unset.
-template <typename TI, int D, bool SOLVE>
+template <typename TI, int D>
 __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64_t h, int64_t c,
-                          int n, const float *rec = nullptr) {
+                          int n) {
     const TI *q = static_cast<const TI *>(p.q), *k = static_cast<const TI *>(p.k),
              *z = static_cast<const TI *>(p.z), *beta = static_cast<const TI *>(p.beta);
     const int64_t H = p.H;
@@ -131,15 +129,6 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
     // q, k, z: a thread takes 8 consecutive channels of one token row (16- or
     // 32-byte loads, all three issued before any use)
     constexpr int VEC = 8, NVEC = C * D / VEC;   // 256 for D = 128 (blockDim.x == 256)
-    f32x4 at4 = {0.f, 0.f, 0.f, 0.f};           // !SOLVE: A (threads < 64), T (64 .. 127)
-    if constexpr (!SOLVE) {
-        using Lay = PrepLayout<D>;
-        const int t = threadIdx.x;
-        if (t < C * C / 4)
-            at4 = reinterpret_cast<const f32x4 *>(rec + Lay::A)[t];
-        else if (t < C * C / 2)
-            at4 = reinterpret_cast<const f32x4 *>(rec + Lay::T)[t - C * C / 4];
-    }
     for (int t = threadIdx.x; t < NVEC; t += blockDim.x) {
         const int r = t / (D / VEC), d0 = VEC * (t % (D / VEC));
         float qv[VEC], kv[VEC], zv[VEC];
@@ -161,15 +150,6 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
     }
     for (int r = threadIdx.x; r < C; r += blockDim.x)
         s.beta[r] = r < n ? to_f32(beta[row0 + (int64_t)r * H]) : 0.f;
-    if constexpr (!SOLVE) {
-        const int t = threadIdx.x;
-        if (t < C * C / 2) {
-            const int f = 4 * (t % (C * C / 4)), r = f / C, s0 = f % C;
-            float(*M)[C + 1] = t < C * C / 4 ? s.A : s.T;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) M[r][s0 + e] = at4[e];
-        }
-    }
     __syncthreads();
     // cumulative log-decay over the chunk, applied to q and k
     for (int d = threadIdx.x; d < D; d += blockDim.x) {
@@ -185,7 +165,6 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
         }
     }
     __syncthreads();
-    if constexpr (!SOLVE) return;
     // A[r][s] = sum_d k_r k_s e^{G_r - G_s} (s < r),  P[r][s] = sum_d q_r k_s e^{G_r - G_s} (s <= r):
     // Kh Ki^T and Qh Ki^T on fp32 matrix-core tiles, wave 0 and wave 1 (two
     // accumulators each, to halve the dependent chain)
@@ -246,7 +225,7 @@ __global__ __launch_bounds__(256) void kda_bwd_prep_kernel(BwdArgs p) {
     const int64_t c = x % p.nchunk, bh = x / p.nchunk;
     const int64_t b = bh / p.H, h = bh % p.H;
     const int n = (int)(p.T - c * C < C ? p.T - c * C : C);
-    chunk_ops<TI, D, true>(s, p, b, h, c, n);
+    chunk_ops<TI, D>(s, p, b, h, c, n);
     float *rec = p.prep + x * (int64_t)Lay::SIZE;
     // W = T diag(beta) Kh on fp32 matrix-core tiles: wave w takes the 16-column
     // tiles w, w+4, ...; lane (g, nn) gets W[4g+e][16t+nn]  (blockDim.x == 256)
@@ -872,34 +851,54 @@ __global__ __launch_bounds__(1024) void kda_bwd_part_kernel(BwdArgs p, const bf1
 
 // ------------------------------------------------------------------ grad ----
 
-template <typename TI, int D> struct GradLds {
-    ChunkOps<TI, D> o;
+// Only what several waves read goes through LDS: Kh (dT's row fragments), A,
+// T, beta and the partial sums.  q e^{G}, k e^{-G} and e^{G} are read only
+// at each thread's own tile elements and stay in its registers (so that four
+// workgroups fit per CU).
+template <int D> struct GradLds {
+    float Kh[C][rowpad<D>()];          // k e^{G}
+    float A[C][C + 1], T[C][C + 1];    // from the chunk's prep record
+    float beta[C];
     float dW[C][rowpad<D>()];
     float dP[C][C + 1], dTV[C][C + 1], dL[C][C + 1];
-    float dbV[C], dGn[D];
+    float dbV[C], dGn[D];   // dGn: sum_j dS' S (times e^{G_n} where used)
     float dbk[4][C];   // per-wave sums over d of (T^T dW)[r][d] Kh[r][d]
     float dbL[C];      // sum_s dL[r][s] A[r][s]
 };
 
 template <typename TI, int D, int NS>
-__global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
-    __shared__ GradLds<TI, D> s;
-    static_assert(sizeof(GradLds<TI, D>) <= 150 * 1024, "LDS budget");
+__global__ __launch_bounds__(256, 4) void kda_bwd_grad_kernel(BwdArgs p) {
+    __shared__ GradLds<D> s;
+    static_assert(sizeof(GradLds<D>) <= 150 * 1024, "LDS budget");
     using PL = PartLayout<D>;
+    using Lay = PrepLayout<D>;
     const int64_t x = blockIdx.x;
     const int64_t c = x % p.nchunk, bh = x / p.nchunk;
     const int64_t b = bh / p.H, h = bh % p.H, H = p.H;
     const int n = (int)(p.T - c * C < C ? p.T - c * C : C);
     const int tid = threadIdx.x;
-    chunk_ops<TI, D, false>(s.o, p, b, h, c, n, p.prep + x * (int64_t)PrepLayout<D>::SIZE);
     // the slices' partial sums, added in slice order (4-float loads, all issued
     // before any use; blockDim.x == 256)
     const float *part = p.part + x * NS * (int64_t)PL::SIZE;
+    const float *rec = p.prep + x * (int64_t)Lay::SIZE;
     const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, nn = lane & 15;
     constexpr int LDD = rowpad<D>(), LDC = C + 1, NDT = D / 16, TPW = (NDT + 3) / 4;
-    const TI *zg = static_cast<const TI *>(p.z);
+    const TI *qg = static_cast<const TI *>(p.q), *kg = static_cast<const TI *>(p.k),
+             *zg = static_cast<const TI *>(p.z), *bg = static_cast<const TI *>(p.beta);
+    const int64_t row0 = (b * p.T + c * C) * H + h;   // token row of the chunk's first token
+    const float cA = __expf(p.A[h]);
+    // per thread, rows 4g..4g+3 of column 16t + nn of each of its tiles t:
+    // dQ^ and dKb partial sums, q, k, z; then e^{G}, q e^{G}, k e^{G}, k e^{-G}
     float tq[TPW][4], tkb[TPW][4], tz[TPW][4];
+    float ev[TPW][4], qh[TPW][4], kh[TPW][4], ki[TPW][4];
     {
+        float qv[TPW][4], kv[TPW][4];
+        f32x4 at4 = {0.f, 0.f, 0.f, 0.f};   // A (threads < 64), T (64 .. 127)
+        if (tid < C * C / 4)
+            at4 = reinterpret_cast<const f32x4 *>(rec + Lay::A)[tid];
+        else if (tid < C * C / 2)
+            at4 = reinterpret_cast<const f32x4 *>(rec + Lay::T)[tid - C * C / 4];
+        const float bt = tid < n ? to_f32(bg[row0 + (int64_t)tid * H]) : 0.f;   // tid < C
         constexpr int NV4 = C * D / 4, PER = (NV4 + 255) / 256;
         f32x4 w[PER];
 #pragma unroll
@@ -930,7 +929,11 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
                 }
                 tq[j][e] = a;
                 tkb[j][e] = bq;
-                tz[j][e] = t < NDT && r < n ? to_f32(zg[((b * p.T + c * C + r) * H + h) * D + d]) : 0.f;
+                const bool in = t < NDT && r < n;
+                const int64_t off = (row0 + (int64_t)r * H) * D + d;
+                qv[j][e] = in ? to_f32(qg[off]) : 0.f;
+                kv[j][e] = in ? to_f32(kg[off]) : 0.f;
+                tz[j][e] = in ? to_f32(zg[off]) : 0.f;
             }
         }
         // dP, dT's V part (64 float4 each), dbeta's V part (4), sum_j dS' S (D/4)
@@ -972,12 +975,42 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
         } else if (u < C / 4 + D / 4) {
             const int d = 4 * (u - C / 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                s.dGn[d + e] = e4[e] * s.o.E[C - 1][d + e];   // d/dG_n of e^{G_n} (sum_j dS' S)
+            for (int e = 0; e < 4; ++e) s.dGn[d + e] = e4[e];
+        }
+        if (tid < C * C / 2) {
+            const int f = 4 * (tid % (C * C / 4)), r = f / C, s0 = f % C;
+            float(*M)[C + 1] = tid < C * C / 4 ? s.A : s.T;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) M[r][s0 + e] = at4[e];
+        }
+        if (tid < C) s.beta[tid] = bt;
+        // G = cumulative sum over the rows of g_min sigma(c z) (0 past the
+        // chunk's tokens): within the lane's four rows, then the totals of the
+        // lower lane groups, added in group order
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int t = wave + 4 * j;
+            float cs[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float gz = 4 * g + e < n ? kGMin * sigmoidf_(cA * tz[j][e]) : 0.f;
+                cs[e] = e == 0 ? gz : cs[e - 1] + gz;
+            }
+            const float t0 = __shfl(cs[3], nn), t1 = __shfl(cs[3], 16 + nn),
+                        t2 = __shfl(cs[3], 32 + nn);
+            const float pre = g == 0 ? 0.f : g == 1 ? t0 : g == 2 ? t0 + t1 : (t0 + t1) + t2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float G = pre + cs[e], E = __expf(G), Ei = __expf(-G);
+                ev[j][e] = E;
+                qh[j][e] = qv[j][e] * E;
+                kh[j][e] = kv[j][e] * E;
+                ki[j][e] = kv[j][e] * Ei;
+                if (t < NDT) s.Kh[4 * g + e][16 * t + nn] = kh[j][e];
+            }
         }
     }
     __syncthreads();
-    auto &o = s.o;
     // wave 0: dT = dW (beta K^)^T + dU (beta V)^T (a 16 x 16 tile over d), then
     // dL = -(T^T dT) T^T (strictly lower), its share of dbeta and dA = diag(beta) dL,
     // all on fp32 matrix-core tiles in registers.  A tile in accumulator layout
@@ -987,26 +1020,26 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
 #pragma unroll
         for (int k0 = 0; k0 < D; k0 += 16) {
             if ((k0 / 16) % 2 == 0)
-                mma16(acc, rowfrag(&s.dW[0][0], LDD, 0, k0, lane), rowfrag(&o.Kh[0][0], LDD, 0, k0, lane));
+                mma16(acc, rowfrag(&s.dW[0][0], LDD, 0, k0, lane), rowfrag(&s.Kh[0][0], LDD, 0, k0, lane));
             else
-                mma16(acc2, rowfrag(&s.dW[0][0], LDD, 0, k0, lane), rowfrag(&o.Kh[0][0], LDD, 0, k0, lane));
+                mma16(acc2, rowfrag(&s.dW[0][0], LDD, 0, k0, lane), rowfrag(&s.Kh[0][0], LDD, 0, k0, lane));
         }
         Frag<float> dTf;   // dT[4g+e][nn]
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dTf.v[e] = s.dTV[4 * g + e][nn] + o.beta[nn] * (acc[e] + acc2[e]);
+        for (int e = 0; e < 4; ++e) dTf.v[e] = s.dTV[4 * g + e][nn] + s.beta[nn] * (acc[e] + acc2[e]);
         f32x4 m1t = {0.f, 0.f, 0.f, 0.f};   // M1^T = dT^T T:  M1^T[4g+e][nn]
-        mma16(m1t, dTf, colfrag(&o.T[0][0], LDC, 0, 0, lane));
+        mma16(m1t, dTf, colfrag(&s.T[0][0], LDC, 0, 0, lane));
         Frag<float> m1f;
         m1f.v = m1t;
         f32x4 tm = {0.f, 0.f, 0.f, 0.f};    // T M1^T = -dL^T:  -dL[nn][4g+e]
-        mma16(tm, rowfrag(&o.T[0][0], LDC, 0, 0, lane), m1f);
+        mma16(tm, rowfrag(&s.T[0][0], LDC, 0, 0, lane), m1f);
         float lb = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int sc = 4 * g + e;
             const float dl = sc < nn ? -tm[e] : 0.f;   // dL[nn][sc]
-            lb += dl * o.A[nn][sc];
-            s.dL[nn][sc] = dl * o.beta[nn];            // now dA
+            lb += dl * s.A[nn][sc];
+            s.dL[nn][sc] = dl * s.beta[nn];            // now dA
         }
         lb += __shfl_xor(lb, 16);
         lb += __shfl_xor(lb, 32);
@@ -1022,10 +1055,10 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
             const int t = wave + 4 * j;
             tdw[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (t < NDT) {
-                mma16(tdw[j], colfrag(&o.T[0][0], LDC, 0, 0, lane),
+                mma16(tdw[j], colfrag(&s.T[0][0], LDC, 0, 0, lane),
                       colfrag(&s.dW[0][0], LDD, 0, 16 * t, lane));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) part_b[e] += tdw[j][e] * o.Kh[4 * g + e][16 * t + nn];
+                for (int e = 0; e < 4; ++e) part_b[e] += tdw[j][e] * kh[j][e];
             }
         }
 #pragma unroll
@@ -1048,7 +1081,6 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
     // rows 4g..4g+3 of column d sit in lane group g, so the column's dG_n terms
     // and the reverse cumulative sum of dG over the 16 rows are formed across
     // the four lane groups, and the gate's derivative gives dz in place.
-    const float cA = __expf(p.A[h]);
     float dA_acc = 0.f;
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
@@ -1058,22 +1090,30 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
             f32x4 dqh, dkh = {0.f, 0.f, 0.f, 0.f}, dki = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) dqh[e] = tq[j][e];
-            const Frag<float> kiB = colfrag(&o.Ki[0][0], LDD, 0, 16 * t, lane);
+            // B operands straight from the registers (lane (g, nn) holds rows
+            // 4g..4g+3 of column d)
+            Frag<float> kiB, khB, qhB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kiB.v[e] = ki[j][e];
+                khB.v[e] = kh[j][e];
+                qhB.v[e] = qh[j][e];
+            }
             mma16(dqh, rowfrag(&s.dP[0][0], LDC, 0, 0, lane), kiB);
             mma16(dkh, rowfrag(&s.dL[0][0], LDC, 0, 0, lane), kiB);
-            mma16(dki, colfrag(&s.dL[0][0], LDC, 0, 0, lane), colfrag(&o.Kh[0][0], LDD, 0, 16 * t, lane));
-            mma16(dki, colfrag(&s.dP[0][0], LDC, 0, 0, lane), colfrag(&o.Qh[0][0], LDD, 0, 16 * t, lane));
-            const float En = o.E[C - 1][d];
+            mma16(dki, colfrag(&s.dL[0][0], LDC, 0, 0, lane), khB);
+            mma16(dki, colfrag(&s.dP[0][0], LDC, 0, 0, lane), qhB);
+            const float En = __shfl(ev[j][3], 48 + nn);   // e^{G} of the last row
             float dGv[4], colp = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g + e;
-                const float dk_h = dkh[e] + o.beta[r] * tdw[j][e];   // through W = T diag(beta) K^
-                const float Em = o.E[r][d], Ei = 1.0f / Em;   // e^{G}, e^{-G}
-                const float dKb = tkb[j][e], kb = o.Ki[r][d] * En;   // Kb = k e^{G_n - G}
+                const float dk_h = dkh[e] + s.beta[r] * tdw[j][e];   // through W = T diag(beta) K^
+                const float Em = ev[j][e], Ei = 1.0f / Em;   // e^{G}, e^{-G}
+                const float dKb = tkb[j][e], kb = ki[j][e] * En;   // Kb = k e^{G_n - G}
                 const float dq = dqh[e] * Em;
                 const float dk = dk_h * Em + dki[e] * Ei + dKb * En * Ei;
-                dGv[e] = dqh[e] * o.Qh[r][d] + dk_h * o.Kh[r][d] - dki[e] * o.Ki[r][d] - dKb * kb;
+                dGv[e] = dqh[e] * qh[j][e] + dk_h * kh[j][e] - dki[e] * ki[j][e] - dKb * kb;
                 colp += dKb * kb;   // d/dG_n of Kb = k e^{G_n - G}
                 if (r < n) {
                     const int64_t off = ((b * p.T + c * C + r) * H + h) * D + d;
@@ -1085,7 +1125,7 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdArgs p) {
             // e^{G_n} (sum_j dS' S)
             colp += __shfl_xor(colp, 16);
             colp += __shfl_xor(colp, 32);
-            if (g == 3) dGv[3] += s.dGn[d] + colp;
+            if (g == 3) dGv[3] += s.dGn[d] * En + colp;   // d/dG_n of e^{G_n} (sum_j dS' S)
             // dg = reverse cumulative sum of dG over the rows: within the lane,
             // then the totals of the higher lane groups
             float suf[4];
