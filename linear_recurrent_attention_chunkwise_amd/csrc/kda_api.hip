@@ -769,7 +769,10 @@ kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
     BwdLayout lay;
     if (!bwd_layout(dtype, B, T, H, D, &lay)) return KDA_ERR_SHAPE;
     const int64_t bh = B * H, nchunk = (T + kBwdChunk - 1) / kBwdChunk;
-    if (bh > 0x7fffffff / 8 || bh * nchunk > 0x7fffffff) return KDA_ERR_SHAPE;   // grid size
+    // grid sizes: the per-chunk kernels launch up to 1024 work-items per chunk
+    // and a dispatch counts work-items in 32 bits (the bound is ~4.2 M
+    // chunk-heads, past any workspace that fits in HBM)
+    if (bh > 0x7fffffff / 8 || bh * nchunk > (int64_t)(0xffffffffu / 1024)) return KDA_ERR_SHAPE;
     const int64_t bth = B * T * H, nin = bth * D, nst = bh * D * D;
     if (!A || !dA) return KDA_ERR_NULL;
     if (bh > 0 && (!dS0)) return KDA_ERR_NULL;

@@ -1172,15 +1172,26 @@ __global__ __launch_bounds__(256, 4) void kda_bwd_grad_kernel(BwdArgs p) {
     }
 }
 
-// dA[h] = sum over (sequence, chunk) of the shares, in that order.
-__global__ void kda_bwd_dA_kernel(const float *dA_part, float *dA, int64_t B, int64_t H,
-                                  int64_t nchunk) {
-    const int64_t h = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (h >= H) return;
+// dA[h] = sum over (sequence, chunk) of the shares: one workgroup per head,
+// thread t sums shares t, t + 256, ... (in order), then a fixed-order tree.
+__global__ __launch_bounds__(256) void kda_bwd_dA_kernel(const float *dA_part, float *dA,
+                                                          int64_t B, int64_t H, int64_t nchunk) {
+    __shared__ float red[256];
+    const int64_t h = blockIdx.x;
+    const int t = threadIdx.x;
     float a = 0.f;
-    for (int64_t b = 0; b < B; ++b)
-        for (int64_t c = 0; c < nchunk; ++c) a += dA_part[(b * H + h) * nchunk + c];
-    dA[h] = a;
+    for (int64_t i = t; i < B * nchunk; i += 256) {
+        const int64_t b = i / nchunk, c = i % nchunk;
+        a += dA_part[(b * H + h) * nchunk + c];
+    }
+    red[t] = a;
+    __syncthreads();
+#pragma unroll
+    for (int w = 128; w > 0; w /= 2) {
+        if (t < w) red[t] += red[t + w];
+        __syncthreads();
+    }
+    if (t == 0) dA[h] = red[0];
 }
 
 size_t bwd_prep_floats(int64_t D) {
@@ -1204,8 +1215,8 @@ static hipError_t launch_bwd_t(const BwdArgs &a) {
         hipLaunchKernelGGL((kda_bwd_grad_kernel<TI, D, D / NC>), dim3((unsigned)units), dim3(256),
                            0, a.stream, a);
     if (a.H > 0)
-        hipLaunchKernelGGL(kda_bwd_dA_kernel, dim3((unsigned)((a.H + 255) / 256)), dim3(256), 0,
-                           a.stream, a.dA_part, a.dA, a.B, a.H, a.nchunk);
+        hipLaunchKernelGGL(kda_bwd_dA_kernel, dim3((unsigned)a.H), dim3(256), 0, a.stream,
+                           a.dA_part, a.dA, a.B, a.H, a.nchunk);
     return hipGetLastError();
 }
 
@@ -1234,8 +1245,8 @@ hipError_t launch_bwd_back(const BwdArgs &a) {
                            a.stream, a);
     }
     if (a.H > 0)
-        hipLaunchKernelGGL(kda_bwd_dA_kernel, dim3((unsigned)((a.H + 255) / 256)), dim3(256), 0,
-                           a.stream, a.dA_part, a.dA, a.B, a.H, a.nchunk);
+        hipLaunchKernelGGL(kda_bwd_dA_kernel, dim3((unsigned)a.H), dim3(256), 0, a.stream,
+                           a.dA_part, a.dA, a.B, a.H, a.nchunk);
     return hipGetLastError();
 }
 

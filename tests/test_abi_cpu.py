@@ -391,6 +391,8 @@ def test_backward_argument_errors(lib):
     assert bwd(lib, ptrs={"ws": P(0, 0)}) == ALIAS         # workspace over q
     assert bwd(lib, ptrs={"dS0": P(6, 0)}) == ALIAS        # dS0 over S0
     assert bwd(lib, H=0) == OK                              # nothing to do
+    # a dispatch counts work-items in 32 bits: at most 2^32 / 1024 chunk-heads
+    assert bwd(lib, B=1, T=16 * 4096, H=1024, ws_bytes=1 << 62) == SHAPE
     # S0 and dS_T are optional
     assert lib.kda_prefill_bwd_workspace_size(F32, 1, 40, 2, 16, 16) > 0
     assert lib.kda_prefill_bwd_workspace_size(BF16, 1, 40, 2, 64, 64) == 0
