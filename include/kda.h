@@ -60,7 +60,11 @@ extern "C" {
 typedef enum kda_status {
     KDA_OK = 0,
     KDA_ERR_NULL = 1,        /* a required pointer is NULL                    */
-    KDA_ERR_SHAPE = 2,       /* a size is negative, or B*H overflows           */
+    KDA_ERR_SHAPE = 2,       /* a size is negative, or a product of sizes (B*H,
+                              * element counts, or a launch's work-items, which a
+                              * dispatch counts in 32 bits: B*H heads above ~1 M
+                              * for prefill, ~8.4 M for decode, B*H*ceil(T/16)
+                              * above ~4.2 M for the backward) is too large     */
     KDA_ERR_UNSUPPORTED = 3, /* dtype / head size / chunk outside the set      */
     KDA_ERR_MISALIGNED = 4,  /* a pointer is not 16-byte aligned               */
     KDA_ERR_ALIAS = 5,       /* outputs overlap inputs (other than S_T == S0)  */

@@ -101,7 +101,9 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
     if (ckpt_every > 0 && (!mul_ok(n_ckpt, H, kMaxElems, &nckh) ||
                            !mul_ok(nckh, D * D, kMaxElems / 4, &nck)))
         return KDA_ERR_SHAPE;
-    if (bh > 0x7fffffff / 8) return KDA_ERR_SHAPE;  // grid size
+    // grid size: at most 4096 work-items per head, and a dispatch counts
+    // work-items in 32 bits
+    if (bh > (int64_t)(0xffffffffu / 4096)) return KDA_ERR_SHAPE;
     const bool want_ckpt = ckpt_every > 0 && n_ckpt > 0;
     int dvb = dv_per_block;
     if (dvb == 0) {
@@ -226,7 +228,7 @@ kda_status kda_decode_step(int dtype, int64_t B, int64_t H, int64_t dk, int64_t 
     if (!mul_ok(B, H, kMaxElems, &bh) || !mul_ok(bh, D, kMaxElems / 4, &nin) ||
         !mul_ok(bh, D * D, kMaxElems / 4, &nstate))
         return KDA_ERR_SHAPE;
-    if (bh > 0x7fffffff) return KDA_ERR_SHAPE;
+    if (bh > (int64_t)(0xffffffffu / 512)) return KDA_ERR_SHAPE;   // 512 work-items per head
     if (!A) return KDA_ERR_NULL;
     if (bh > 0 && (!q || !k || !v || !z || !beta || !S || !o)) return KDA_ERR_NULL;
     const void *ptrs[] = {q, k, v, z, beta, A, S, o};
@@ -529,7 +531,7 @@ kda_status kda_decode_step_conv(int dtype, int64_t B, int64_t H, int64_t dk, int
     if (!mul_ok(B, H, kMaxElems, &bh) || !mul_ok(bh, D, kMaxElems / 4, &nin) ||
         !mul_ok(bh, D * D, kMaxElems / 4, &nstate))
         return KDA_ERR_SHAPE;
-    if (bh > 0x7fffffff) return KDA_ERR_SHAPE;
+    if (bh > (int64_t)(0xffffffffu / 512)) return KDA_ERR_SHAPE;   // 512 work-items per head
     if (!A) return KDA_ERR_NULL;
     if (bh > 0 && (!q || !k || !v || !z || !beta || !S || !o)) return KDA_ERR_NULL;
     const void *ptrs[] = {q, k, v, z, beta, A, S, o};

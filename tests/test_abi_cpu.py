@@ -90,6 +90,7 @@ def test_prefill_shape_and_support_errors(lib):
     assert prefill(lib, dtype=F32, chunk=64) == UNSUP      # fp32 with dk=128 runs chunk 16
     assert prefill(lib, chunk=64, dvb=16) == UNSUP         # one-wave 64-token variant not built
     assert prefill(lib, B=1 << 40, T=1 << 40) == SHAPE     # element count overflows
+    assert prefill(lib, B=1 << 14, T=1, H=1 << 7) == SHAPE  # 2^21 heads: grid work-items overflow
 
 
 def test_prefill_null_and_alignment_errors(lib):
@@ -120,6 +121,7 @@ def test_prefill_empty_work_launches_nothing(lib):
 
 def test_decode_errors(lib):
     assert decode(lib, B=-1) == SHAPE
+    assert decode(lib, B=1 << 16, H=1 << 7) == SHAPE       # 2^23 heads x 512 work-items
     assert decode(lib, dk=64, dv=64) == UNSUP
     assert decode(lib, dtype=3) == UNSUP
     for name in ["q", "k", "v", "z", "beta", "A", "S", "o"]:
