@@ -183,31 +183,46 @@ __device__ void chunk_ops(ChunkOps<TI, D> &s, const BwdArgs &p, int64_t b, int64
                     mma16(acc2, rowfrag(X, LDD, 0, k0, lane), rowfrag(&s.Ki[0][0], LDD, 0, k0, lane));
             }
             acc += acc2;
+            if (wave == 1) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * g + e;
-                if (wave == 0)
-                    s.A[r][nn] = nn < r ? acc[e] : 0.f;
-                else
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
                     s.P[r][nn] = nn <= r ? acc[e] : 0.f;
+                }
+            } else {
+                // T = (I + N)^-1 with N = diag(beta) A strictly lower, so N^16 = 0:
+                // T = (I - N)(I + N^2)(I + N^4)(I + N^8), on fp32 tiles in
+                // registers.  A tile in accumulator layout (lane (g, nn) holds
+                // X[4g+e][nn]) is the B operand of X and the A operand of X^T, so
+                // mm(a, b) below, with a holding X^T and b holding Y, gives X Y.
+                f32x4 N, I;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    const float a = nn < r ? acc[e] : 0.f;
+                    s.A[r][nn] = a;
+                    N[e] = s.beta[r] * a;
+                    I[e] = r == nn ? 1.f : 0.f;
+                }
+                auto mm = [](const f32x4 &a, const f32x4 &b) {
+                    Frag<float> fa, fb;
+                    fa.v = a;
+                    fb.v = b;
+                    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+                    mma16(d, fa, fb);
+                    return d;
+                };
+                const f32x4 NT = mm(N, I);            // N^T I
+                const f32x4 N2 = mm(NT, N), N2T = mm(N, NT);
+                const f32x4 N4 = mm(N2T, N2), N4T = mm(N2, N2T);
+                const f32x4 N8 = mm(N4T, N4);
+                const f32x4 Y = mm(I + N4T, I + N8);  // (I + N^4)(I + N^8)
+                const f32x4 XT = mm(I + N2, I - NT);  // ((I - N)(I + N^2))^T
+                const f32x4 Tm = mm(XT, Y);           // T
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s.T[4 * g + e][nn] = Tm[e];
             }
         }
-    }
-    __syncthreads();
-    // T = (I + diag(beta) A)^-1 by forward substitution, one column per thread,
-    // the column kept in registers
-    if (threadIdx.x < C) {
-        const int col = threadIdx.x;
-        float t[C];
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            float acc = r == col ? 1.f : 0.f;
-#pragma unroll
-            for (int u = 0; u < r; ++u) acc -= s.beta[r] * s.A[r][u] * t[u];
-            t[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < C; ++r) s.T[r][col] = t[r];
     }
     __syncthreads();
 }
