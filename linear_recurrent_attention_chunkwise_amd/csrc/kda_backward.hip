@@ -20,8 +20,8 @@
 //
 // Kernels:
 //   prep   -- one workgroup per (sequence, head, chunk): the chunk's W, Q^,
-//             Kb, P, T and e^{G_n} (S-independent, fp32; A and P on fp32
-//             matrix-core tiles), into the workspace.
+//             Kb, P, T, e^{G_n} and A (S-independent, fp32; A, P, T and W on
+//             fp32 matrix-core tiles), into the workspace.
 //   dstate -- (bf16, d = 128) one workgroup per (sequence, head, 64 value
 //             columns): walks the chunks backwards carrying dS in fp32
 //             accumulator tiles (bf16 matrix-core products) and stores every
@@ -33,10 +33,11 @@
 //   chain  -- (fp32 inputs, d = 16) dstate and part in one fp32 kernel per
 //             (sequence, head, value-column slice), carrying dS through LDS.
 //   grad   -- one workgroup per (sequence, head, chunk): adds the slices'
-//             partials in slice order and forms dq, dk, dbeta, dz and the
-//             chunk's share of dA (fp32; its chunk products on fp32
-//             matrix-core tiles).
-//   dA     -- sums the shares of each head in (sequence, chunk) order.
+//             partials in slice order and, with A and T from prep's record,
+//             forms dq, dk, dbeta, dz and the chunk's share of dA (fp32; its
+//             chunk products on fp32 matrix-core tiles).
+//   dA     -- one workgroup per head: sums its (sequence, chunk) shares in a
+//             fixed order (strided per thread, then a fixed tree).
 // No atomics: results are bitwise reproducible.
 #include "kda_device.h"
 #include "kda_launch.h"
