@@ -438,12 +438,23 @@ constexpr int BD = 128;          // head size of the MFMA backward
 constexpr int BLD = BD + 8;      // bf16 row stride of [.][d] / [.][j] LDS tiles
 constexpr int BLT = C + 8;       // bf16 row stride of [.][token] LDS tiles
 
-__device__ __forceinline__ Frag<bf16> frag_rows(const bf16 *tile, int ld, int r0, int col, int lane) {
-    // K16 fragment over k = r0 + 4*(lane/16) + e of column `col`: tile[k][col]
+// K16 fragment over k = r0 + 4*(lane/16) + e of column col0 + lane%16 of a
+// row-major LDS tile, tile[k][col0 + lane%16], from one transposing 8-byte
+// LDS read per lane (gfx950's ds_read_b64_tr_b16, in place of four 2-byte
+// reads): within each 16-lane group the hardware hands lane i,
+// element e, element i % 4 of the 8 bytes that lane 4e + i/4 addressed.  So
+// lane (g, j) addresses row r0 + 4g + j/4, columns col0 + 4(j%4) .. +3, and
+// lane (g, n) receives tile[r0 + 4g + e][col0 + n].  `tile` must be in LDS,
+// col0 a multiple of 4 and the row stride a multiple of 4 elements.
+__device__ __forceinline__ Frag<bf16> frag_rows_tr(const bf16 *tile, int ld, int r0, int col0,
+                                                   int lane) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int g = lane >> 4, j = lane & 15;
+    const bf16 *a = tile + (r0 + 4 * g + (j >> 2)) * ld + col0 + 4 * (j & 3);
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(a));
     Frag<bf16> f;
-    const int g = lane >> 4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f.v[e] = tile[(r0 + 4 * g + e) * ld + col];
+    f.v = __builtin_bit_cast(bf16x4, r);
     return f;
 }
 
@@ -741,7 +752,8 @@ __global__ __launch_bounds__(1024) void kda_bwd_part_kernel(BwdArgs p, const bf1
     //      dU = P^T dO + Kb dS', T^T dU, dV, dbeta's V part (waves 8-15) ----
     {
         const int jw = 16 * (wave & 7);
-        const Frag<bf16> Vf = frag_rows(&s.V[0][0], BLD, 0, jw + n, lane);
+        static_assert(BLD % 4 == 0, "transposing reads need 8-byte rows");
+        const Frag<bf16> Vf = frag_rows_tr(&s.V[0][0], BLD, 0, jw, lane);
         f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
         if (wave < 8) {
             Frag<bf16> bVf;   // diag(beta) V, rows 4g + e
@@ -753,8 +765,8 @@ __global__ __launch_bounds__(1024) void kda_bwd_part_kernel(BwdArgs p, const bf1
                 f32x4 &acc = (i / 2) % 2 == 0 ? a1 : a2;
                 mma32(acc, lds_frag(&s.W[0][0], BLD, 16 * i, lane),
                       lds_frag(&s.W[0][0], BLD, 16 * i + 16, lane),
-                      frag_rows(&s.S[0][0], BLD, 16 * i, jw + n, lane),
-                      frag_rows(&s.S[0][0], BLD, 16 * i + 16, jw + n, lane));
+                      frag_rows_tr(&s.S[0][0], BLD, 16 * i, jw, lane),
+                      frag_rows_tr(&s.S[0][0], BLD, 16 * i + 16, jw, lane));
             }
             const f32x4 U = a0 - (a1 + a2);
 #pragma unroll
@@ -765,15 +777,15 @@ __global__ __launch_bounds__(1024) void kda_bwd_part_kernel(BwdArgs p, const bf1
                 s.Ulo[r][jw + n] = (bf16)(U[e] - (float)uh);
             }
         } else {
-            const Frag<bf16> dOf = frag_rows(&s.dO[0][0], BLD, 0, jw + n, lane);
+            const Frag<bf16> dOf = frag_rows_tr(&s.dO[0][0], BLD, 0, jw, lane);
             mma16(a0, lds_frag(&s.PT[0][0], BLT, 0, lane), dOf);
 #pragma unroll
             for (int i = 0; i < BD / 16; i += 2) {
                 f32x4 &acc = (i / 2) % 2 == 0 ? a1 : a2;
                 mma32(acc, lds_frag(&s.Kb[0][0], BLD, 16 * i, lane),
                       lds_frag(&s.Kb[0][0], BLD, 16 * i + 16, lane),
-                      frag_rows(&s.dS[0][0], BLD, 16 * i, jw + n, lane),
-                      frag_rows(&s.dS[0][0], BLD, 16 * i + 16, jw + n, lane));
+                      frag_rows_tr(&s.dS[0][0], BLD, 16 * i, jw, lane),
+                      frag_rows_tr(&s.dS[0][0], BLD, 16 * i + 16, jw, lane));
             }
             const f32x4 dU = a0 + (a1 + a2);
             // dU enters the products below as a bf16 pair hi + lo
