@@ -437,6 +437,8 @@ namespace {
 constexpr int BD = 128;          // head size of the MFMA backward
 constexpr int BLD = BD + 8;      // bf16 row stride of [.][d] / [.][j] LDS tiles
 constexpr int BLT = C + 8;       // bf16 row stride of [.][token] LDS tiles
+constexpr int BLQ = BD + 16;     // bf16 row stride of tiles read only by transposing reads
+                                 // (8 banks between rows: the 16 rows of a read do not collide)
 
 // K16 fragment over k = r0 + 4*(lane/16) + e of column col0 + lane%16 of a
 // row-major LDS tile, tile[k][col0 + lane%16], from one transposing 8-byte
@@ -473,8 +475,8 @@ __device__ __forceinline__ float sum16(float x) {
 
 struct DstateBuf {
     bf16 Kb[C][BLD];      // Kb [r][d]
-    bf16 QhT[BD][BLT];    // Q^ transposed [d][r]
-    bf16 WTn[BD][BLT];    // -W transposed [d][r]
+    bf16 Qh[C][BLQ];      // Q^ [r][d]  (read transposed by ds_read_b64_tr_b16)
+    bf16 Wn[C][BLQ];      // -W [r][d]
     bf16 PT[C][BLT];      // P transposed [r][s] = P[s][r]
     float Gn[BD];         // e^{G_n}
 };
@@ -539,16 +541,12 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, bf16
             const int f = tid + NT * u, r = f / (BD / 4), d = 4 * (f % (BD / 4));
             store_bf16x4(&B.Kb[r][d], R.rk[u][0], R.rk[u][1], R.rk[u][2], R.rk[u][3]);
         }
-        // Q^ and W go in transposed: lanes take consecutive tokens r of one
-        // 4-column group, so their 2-byte writes fall in distinct LDS banks
+        // Q^ and -W row-major (the products read them transposed)
 #pragma unroll
         for (int u = 0; u < 2048 / 4 / NT; ++u) {
             const int f = tid + NT * u, r = f % C, d = 4 * (f / C);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                B.QhT[d + e][r] = (bf16)R.rq[u][e];
-                B.WTn[d + e][r] = (bf16)(-R.rw[u][e]);
-            }
+            store_bf16x4(&B.Qh[r][d], R.rq[u][0], R.rq[u][1], R.rq[u][2], R.rq[u][3]);
+            store_bf16x4(&B.Wn[r][d], -R.rw[u][0], -R.rw[u][1], -R.rw[u][2], -R.rw[u][3]);
         }
         if (tid < C * C / 4) {
             const int sidx = tid / 4, r0 = 4 * (tid % 4);
@@ -592,8 +590,8 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_dstate_kernel(BwdArgs p, bf16
         for (int i = 0; i < NDT; ++i) {
             const f32x4 gn = *reinterpret_cast<const f32x4 *>(&B.Gn[16 * i + 4 * g]);
             dS[i] *= gn;
-            mma32(dS[i], lds_frag(&B.QhT[16 * i][0], BLT, 0, lane),
-                  lds_frag(&B.WTn[16 * i][0], BLT, 0, lane), dOf, dUf);
+            mma32(dS[i], frag_rows_tr(&B.Qh[0][0], BLQ, 0, 16 * i, lane),
+                  frag_rows_tr(&B.Wn[0][0], BLQ, 0, 16 * i, lane), dOf, dUf);
         }
     };
 
