@@ -122,6 +122,23 @@ __device__ __forceinline__ void store_row16(bf16 *row, const float *x) {
                  pack_bf16(x[14], x[15])};
 }
 
+// K16 fragment over rows 4*(lane/16) + e of column col0 + lane%16 of a
+// row-major LDS tile, tile[4g + e][col0 + n], from one transposing 8-byte LDS
+// read per lane (gfx950's ds_read_b64_tr_b16): within each 16-lane group the
+// hardware hands lane i, element e, element i % 4 of the 8 bytes that lane
+// 4e + i/4 addressed, so lane (g, j) addresses row 4g + j/4, columns
+// col0 + 4(j%4) .. +3.  col0 and the row stride are multiples of 4.
+__device__ __forceinline__ Frag<bf16> frag_rows_tr(const bf16 *tile, int ld, int col0, int lane) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int g = lane >> 4, j = lane & 15;
+    const bf16 *a = tile + (4 * g + (j >> 2)) * ld + col0 + 4 * (j & 3);
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(a));
+    Frag<bf16> f;
+    f.v = __builtin_bit_cast(bf16x4, r);
+    return f;
+}
+
 // MODE 0: the prefill.  MODE 1: the final states only (no o).  MODE 2: the
 // segment's state transition -- V taken as zero and no o, so that run from
 // S0 = I (dv = dk columns) the final "state" is the matrix M with
@@ -524,9 +541,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         // before its W rows overwrite the same columns.
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            Frag<bf16> ka;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ka.v[e] = sWn[(4 * g + e) * DP + 16 * dt + n];
+            const Frag<bf16> ka = frag_rows_tr(sWn, DP, 16 * dt, lane);
             f32x4 w = {0.f, 0.f, 0.f, 0.f};
             mma16(w, ka, Tf);
             // w[e] = W[n][16 dt + 4 g + e]
