@@ -70,18 +70,19 @@ struct P16Cfg {
     static constexpr int D = 128, C = 16;
     static constexpr int DVB = 16 * NCW;           // value columns per workgroup
     static constexpr int DP = D + 8;               // [token][d] row stride
-    static constexpr int CP = C + 8;               // [d][token] / [token][token] row stride
+    static constexpr int CP = C + 8;               // [token][token] row stride
+    static constexpr int KP = D + 16;              // Kh row stride (read by transposing reads:
+                                                   // 8 banks between rows, no collisions)
     // slot: the chain operands of one chunk
     static constexpr int S_QG = 0;                         // Q~         [C][DP]
     static constexpr int S_WN = S_QG + C * DP * 2;         // K~, then -W~ [C][DP]
-    static constexpr int S_KHT = S_WN + C * DP * 2;        // Kh^T       [D][CP]
-    static constexpr int S_P = S_KHT + D * CP * 2;         // P          [C][CP]
+    static constexpr int S_KH = S_WN + C * DP * 2;         // Kh         [C][KP]
+    static constexpr int S_P = S_KH + C * KP * 2;          // P          [C][CP]
     static constexpr int S_TB = S_P + C * CP * 2;          // T diag(b)  [C][CP]
     static constexpr int S_GC = S_TB + C * CP * 2;         // e^{G_C}    [D] fp32
     static constexpr int SLOT = S_GC + D * 4;
     // prep-wave scratch
-    static constexpr int W_KH = 0;                          // Kh    [C][DP]
-    static constexpr int W_BETA = W_KH + C * DP * 2;        // beta  [C] fp32
+    static constexpr int W_BETA = 0;                        // beta  [C] fp32
     static constexpr int SCR = (W_BETA + C * 4 + 15) / 16 * 16;
     static constexpr int OFF_FLAGS = 0;                     // ready[8], done[NSLOT][NCW]
     static constexpr int OFF_DONE = 32;
@@ -211,7 +212,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             f.v = *reinterpret_cast<const bf16x4 *>(p);
             return f;
         };
-        // W, T diag(beta) and Kh^T fragments of a chunk (read one chunk ahead)
+        // W, T diag(beta) and Kh^T fragments of a chunk (read one chunk ahead;
+        // Kh^T by transposing reads of the token-major Kh)
         Frag<bf16> Wf[NDT], Kf[NDT], Tf;
         auto read_wtk = [&](int sl, int use) {
             wait_at_least(&ready[sl], use + 1);
@@ -221,8 +223,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
 #pragma unroll
             for (int i = 0; i < NDT; ++i) Wf[i] = frag_at(pd + Cfg::S_WN + 32 * i);
             Tf = frag_at(pc + Cfg::S_TB);
+            const bf16 *kh = reinterpret_cast<const bf16 *>(smem + off + Cfg::S_KH);
 #pragma unroll
-            for (int i = 0; i < NDT; ++i) Kf[i] = frag_at(pc + Cfg::S_KHT + 32 * CP * i);
+            for (int i = 0; i < NDT; ++i) Kf[i] = frag_rows_tr(kh, Cfg::KP, 16 * i, lane);
         };
         if (nchunks > 0) read_wtk(0, 0);
         int sl = 0, use = 0;   // slot and use of chunk m
@@ -354,7 +357,6 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
     // ============================== prep wave ===============================
     const int pw = wave - NCW;
     char *scr = smem + Cfg::OFF_SCR + pw * Cfg::SCR;
-    bf16 *sKh = reinterpret_cast<bf16 *>(scr + Cfg::W_KH);
     float *sBeta = reinterpret_cast<float *>(scr + Cfg::W_BETA);
 
     const float c2 = -__builtin_amdgcn_exp2f(prm.A[h] * kLog2e) * kLog2e;
@@ -390,7 +392,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         char *slot = smem + Cfg::OFF_SLOTS + s_ * Cfg::SLOT;
         bf16 *sQG = reinterpret_cast<bf16 *>(slot + Cfg::S_QG);
         bf16 *sWn = reinterpret_cast<bf16 *>(slot + Cfg::S_WN);   // K~ until -W~ overwrites it
-        bf16 *sKhT = reinterpret_cast<bf16 *>(slot + Cfg::S_KHT);
+        bf16 *sKh = reinterpret_cast<bf16 *>(slot + Cfg::S_KH);   // Kh token-major
         bf16 *sP = reinterpret_cast<bf16 *>(slot + Cfg::S_P);
         bf16 *sTb = reinterpret_cast<bf16 *>(slot + Cfg::S_TB);
         float *sGC = reinterpret_cast<float *>(slot + Cfg::S_GC);
@@ -421,33 +423,16 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
 
         // ---- decay factors and operands (lane = channel pair d0, d0+1) ------
         // Backward over the chunk: R = decay over (s, end of chunk], so that
-        // Kh = K e^{G_C - G} (<= 1), written token-major (scratch, for P and
-        // L) and as Kh^T rows (slot, for the state update).  At the end R is
-        // the decay over the whole chunk, e^{G_C}.
+        // Kh = K e^{G_C - G} (<= 1), written token-major into the slot (for P
+        // and L here, and read transposed by the state update).  At the end R
+        // is the decay over the whole chunk, e^{G_C}.
         float R0 = 1.f, R1 = 1.f;
-        {
-            static_assert(C == 16, "two 16-byte stores per Kh^T row");
-            uint4 *r0 = reinterpret_cast<uint4 *>(sKhT + d0 * CP);
-            uint4 *r1 = reinterpret_cast<uint4 *>(sKhT + (d0 + 1) * CP);
-            uint32_t p0[4], p1[4];       // 8 tokens of Kh^T rows d0, d0+1 as bf16 pairs
-            float hn0 = 0.f, hn1 = 0.f;  // Kh of token s+1
 #pragma unroll
-            for (int s = C - 1; s >= 0; --s) {
-                const float h0 = bf_lo(rk[s]) * R0, h1 = bf_hi(rk[s]) * R1;
-                *reinterpret_cast<uint32_t *>(sKh + s * DP + d0) = pack_bf16(h0, h1);
-                if (s % 2 == 0) {
-                    p0[(s / 2) % 4] = pack_bf16(h0, hn0);
-                    p1[(s / 2) % 4] = pack_bf16(h1, hn1);
-                }
-                if (s % 8 == 0) {   // tokens s .. s+7 complete: one 16-byte store per row
-                    r0[s / 8] = uint4{p0[0], p0[1], p0[2], p0[3]};
-                    r1[s / 8] = uint4{p1[0], p1[1], p1[2], p1[3]};
-                }
-                hn0 = h0;
-                hn1 = h1;
-                R0 *= a0[s];
-                R1 *= a1[s];
-            }
+        for (int s = C - 1; s >= 0; --s) {
+            const float h0 = bf_lo(rk[s]) * R0, h1 = bf_hi(rk[s]) * R1;
+            *reinterpret_cast<uint32_t *>(sKh + s * Cfg::KP + d0) = pack_bf16(h0, h1);
+            R0 *= a0[s];
+            R1 *= a1[s];
         }
         sGC[d0] = R0;
         sGC[d0 + 1] = R1;
@@ -481,7 +466,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
               accLT = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k32 = 0; k32 < D; k32 += 32) {
-            const Frag<bf16> c0 = lds_frag(sKh, DP, k32, lane), c1 = lds_frag(sKh, DP, k32 + 16, lane);
+            const Frag<bf16> c0 = lds_frag(sKh, Cfg::KP, k32, lane), c1 = lds_frag(sKh, Cfg::KP, k32 + 16, lane);
             const Frag<bf16> h0f = lds_frag(sWn, DP, k32, lane), h1f = lds_frag(sWn, DP, k32 + 16, lane);
             if constexpr (MODE == 0) {
                 const Frag<bf16> q0f = lds_frag(sQG, DP, k32, lane),
