@@ -80,7 +80,10 @@ struct P16Cfg {
     static constexpr int S_P = S_KH + C * KP * 2;          // P          [C][CP]
     static constexpr int S_TB = S_P + C * CP * 2;          // T diag(b)  [C][CP]
     static constexpr int S_GC = S_TB + C * CP * 2;         // e^{G_C}    [D] fp32
-    static constexpr int SLOT = S_GC + D * 4;
+    static constexpr int VP = DVB + 16;                    // V row stride (transposing reads:
+                                                           // the rows they touch in distinct banks)
+    static constexpr int S_V = S_GC + D * 4;               // V, this workgroup's columns [C][VP]
+    static constexpr int SLOT = S_V + C * VP * 2;
     // prep-wave scratch
     static constexpr int W_BETA = 0;                        // beta  [C] fp32
     static constexpr int SCR = (W_BETA + C * 4 + 15) / 16 * 16;
@@ -191,17 +194,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
 #pragma unroll
             for (int i = 0; i < NDT; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        // V fragment of a chunk: V[t0 + 4g + e][jw + n], e = 0..3 (zero past T)
         const int64_t row_bytes = tok_stride * 2;
         auto chunk_rows = [&](int64_t t0) { return (Tn - t0 < C ? Tn - t0 : (int64_t)C); };
-        short vr[4];
-        auto load_v = [&](int64_t t0) {
-            const auto rs = make_rsrc(prm.v + base + t0 * tok_stride + jw, chunk_rows(t0) * row_bytes);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                vr[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, (4 * g + e) * (int)row_bytes + 2 * n, 0, 0);
-        };
-        if (MODE != 2 && nchunks > 0) load_v(0);
         // per-lane byte offsets of the fragment reads, fixed over chunks; a
         // chunk adds its slot's (uniform) byte offset once per tile layout
         const int offDP = ((lane & 15) * DP + 4 * (lane >> 4)) * 2;   // [.][DP] tiles
@@ -212,9 +206,10 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             f.v = *reinterpret_cast<const bf16x4 *>(p);
             return f;
         };
-        // W, T diag(beta) and Kh^T fragments of a chunk (read one chunk ahead;
-        // Kh^T by transposing reads of the token-major Kh)
-        Frag<bf16> Wf[NDT], Kf[NDT], Tf;
+        // W, T diag(beta), Kh^T and V fragments of a chunk (read one chunk
+        // ahead; Kh^T and V by transposing reads of token-major tiles: V as
+        // V[t0 + 4g + e][jw + n], staged by the prep wave, zero past T)
+        Frag<bf16> Wf[NDT], Kf[NDT], Tf, Vn;
         auto read_wtk = [&](int sl, int use) {
             wait_at_least(&ready[sl], use + 1);
             const int off = Cfg::OFF_SLOTS + sl * Cfg::SLOT;
@@ -226,6 +221,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             const bf16 *kh = reinterpret_cast<const bf16 *>(smem + off + Cfg::S_KH);
 #pragma unroll
             for (int i = 0; i < NDT; ++i) Kf[i] = frag_rows_tr(kh, Cfg::KP, 16 * i, lane);
+            if constexpr (MODE != 2)
+                Vn = frag_rows_tr(reinterpret_cast<const bf16 *>(smem + off + Cfg::S_V), Cfg::VP,
+                                  16 * wave, lane);
         };
         if (nchunks > 0) read_wtk(0, 0);
         int sl = 0, use = 0;   // slot and use of chunk m
@@ -246,12 +244,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             f32x4 gc[NDT];
 #pragma unroll
             for (int i = 0; i < NDT; ++i) gc[i] = *reinterpret_cast<const f32x4 *>(pg + 64 * i);
-            Frag<bf16> Vf;
-            if constexpr (MODE != 2) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Vf.v[e] = __builtin_bit_cast(bf16, vr[e]);
-                if (m + 1 < nchunks) load_v(t0 + C);
-            }
+            const Frag<bf16> Vf = Vn;
             __builtin_amdgcn_sched_barrier(0);
             // (2) S <- e^{G_C} S; U = T diag(beta) V - W~ S, where W~ = W e^{-G_C}
             // (two accumulators halve the dependent chain)
@@ -364,6 +357,11 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
 
     uint32_t rq[C], rk[C], rz[C];
     short rb;   // lane s < 16: beta of token s
+    // V of this workgroup's DVB columns: lane -> row lane / 4, columns
+    // (lane % 4) * DVB/4 + 8u, u < DVB/32 (16-byte loads, zero past T)
+    constexpr int VU = DVB / 32;
+    const int vrow = lane >> 2, vcol = (lane & 3) * (DVB / 4);
+    uint4 rvv[VU];
     const int64_t row_bytes = tok_stride * 2;
     auto load_chunk = [&](int64_t t0) {
         // one uniform buffer resource per tensor and chunk; rows past T read 0
@@ -373,6 +371,15 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         const auto rz_ = make_rsrc(prm.z + base + t0 * tok_stride, rows * row_bytes);
         const auto rb_ = make_rsrc(prm.beta + bbase + t0 * H, rows * H * 2);
         rb = __builtin_amdgcn_raw_buffer_load_b16(rb_, (lane & 15) * (int)H * 2, 0, 0);
+        if constexpr (MODE != 2) {
+            const auto rv_ = make_rsrc(prm.v + base + t0 * tok_stride, rows * row_bytes);
+#pragma unroll
+            for (int u = 0; u < VU; ++u) {
+                const auto w = __builtin_amdgcn_raw_buffer_load_b128(
+                    rv_, vrow * (int)row_bytes + (j0 + vcol + 8 * u) * 2, 0, 0);
+                rvv[u] = uint4{w[0], w[1], w[2], w[3]};
+            }
+        }
 #pragma unroll
         for (int s = 0; s < C; ++s) {
             const int so = s * (int)row_bytes;
@@ -421,6 +428,12 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
 #pragma unroll
         for (int w = 0; w < NCW; ++w) wait_at_least(&done[s_ * NCW + w], use);
 
+        if constexpr (MODE != 2) {
+            bf16 *sV = reinterpret_cast<bf16 *>(slot + Cfg::S_V);
+#pragma unroll
+            for (int u = 0; u < VU; ++u)
+                *reinterpret_cast<uint4 *>(sV + vrow * Cfg::VP + vcol + 8 * u) = rvv[u];
+        }
         // ---- decay factors and operands (lane = channel pair d0, d0+1) ------
         // Backward over the chunk: R = decay over (s, end of chunk], so that
         // Kh = K e^{G_C - G} (<= 1), written token-major into the slot (for P
