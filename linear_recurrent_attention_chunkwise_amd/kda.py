@@ -195,11 +195,13 @@ def prefill(q, k, v, z, beta, A, S0=None, chunk: int = 16, out=None, S_T=None,
         return out, S_T
     ws_bytes = int(lib.kda_prefill_workspace_size(_DTYPES[dt], B, T, H, dk, dv, int(chunk)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    st = lib.kda_prefill_ex(_DTYPES[dt], B, T, H, dk, dv, int(chunk), _ptr(q), _ptr(k),
-                            _ptr(v), _ptr(z), _ptr(beta), _ptr(A), _ptr(S0), _ptr(out),
-                            _ptr(S_T), _ptr(ws), ws_bytes, _stream_handle(dev),
-                            int(dv_per_block))
-    _check(st, "kda_prefill")
+    args = [_DTYPES[dt], B, T, H, dk, dv, int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(z),
+            _ptr(beta), _ptr(A), _ptr(S0), _ptr(out), _ptr(S_T), _ptr(ws), ws_bytes,
+            _stream_handle(dev)]
+    if dv_per_block:   # an explicit column split: the _ex entry point
+        _check(lib.kda_prefill_ex(*args, int(dv_per_block)), "kda_prefill_ex")
+    else:
+        _check(lib.kda_prefill(*args), "kda_prefill")
     return out, S_T
 
 

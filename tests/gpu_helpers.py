@@ -23,6 +23,57 @@ def slice_relerr(x, ref, head_axis: int) -> float:
     return float(worst)
 
 
+def elem_relerr(x, ref, head_axis: int, floor: float = 1e-6):
+    """Elementwise diagnostic (reported, not gated): per (b, h) slice, the
+    relative error of every element, |x - ref| / max(|ref|, floor * max|ref|).
+    Returns (max, 99.9th percentile, fraction of elements above 2e-2), each
+    the worst over slices."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    worst = [0.0, 0.0, 0.0]
+    for b in range(ref.shape[0]):
+        for h in range(ref.shape[head_axis]):
+            xs = np.take(x[b], h, axis=head_axis - 1).ravel()
+            rs = np.take(ref[b], h, axis=head_axis - 1).ravel()
+            if rs.size == 0:
+                continue
+            m = np.max(np.abs(rs))
+            if m == 0:
+                continue
+            r = np.abs(xs - rs) / np.maximum(np.abs(rs), floor * m)
+            worst[0] = max(worst[0], float(np.max(r)))
+            worst[1] = max(worst[1], float(np.percentile(r, 99.9)))
+            worst[2] = max(worst[2], float(np.mean(r > 2e-2)))
+    return tuple(worst)
+
+
+def row_relerr(x, ref, floor: float = 1e-3):
+    """Token-row diagnostic (reported, not gated) for [B, T, H, d] outputs:
+    per (b, t, h) row, max|x - ref| / max(max|ref row|, floor * max|ref|
+    over the (b, h) slice).  Returns (max, 99.9th percentile) over rows."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return (0.0, 0.0)
+    num = np.max(np.abs(x - ref), axis=-1)                       # [B, T, H]
+    den = np.max(np.abs(ref), axis=-1)
+    scale = np.max(den, axis=1, keepdims=True)                   # per (b, h)
+    r = num / np.maximum(np.maximum(den, floor * scale), 1e-300)
+    return (float(np.max(r)), float(np.percentile(r, 99.9)))
+
+
+def fmt_elem(e, rows=None) -> str:
+    s = f"elementwise max {e[0]:.2e} p99.9 {e[1]:.2e} frac>2e-2 {e[2]:.2e}"
+    if rows is not None:
+        s += f"; token rows max {rows[0]:.2e} p99.9 {rows[1]:.2e}"
+    return s
+
+
+def diag(x, ref) -> str:
+    """Both diagnostics of an output [B, T, H, d] against its reference."""
+    return fmt_elem(elem_relerr(x, ref, 2), row_relerr(x, ref))
+
+
 def host(t):
     return None if t is None else t.detach().float().cpu().numpy()
 
@@ -48,6 +99,31 @@ def oracle_prefill(inp, heads=None, T=None):
     A = host(inp["A"]) if heads is None else host(inp["A"])[heads]
     S0 = sel(inp["S0"], 1)
     return oracle.prefill(q, k, v, z, beta, A, S0)
+
+
+def oracle_prefill_chained(inp, heads, seg: int = 1 << 17):
+    """Oracle over the full length for a few heads, run segment by segment
+    with the state carried from one segment into the next (the split property
+    of the recurrence, pinned on the oracle itself), so host memory holds one
+    segment's fp64 inputs at a time.  Returns (o as float32 [B, T, len(heads),
+    dv], S_T fp64)."""
+    idx = None
+    T = inp["q"].shape[1]
+    A = host(inp["A"])[heads]
+    S = None
+    if inp["S0"] is not None:
+        S = host(torch.index_select(inp["S0"], 1, torch.as_tensor(heads, device=inp["S0"].device)))
+    outs = []
+    for t0 in range(0, T, seg):
+        part = []
+        for n in ("q", "k", "v", "z", "beta"):
+            t = inp[n]
+            if idx is None:
+                idx = torch.as_tensor(heads, device=t.device)
+            part.append(host(torch.index_select(t[:, t0:t0 + seg], 2, idx)))
+        o, S = oracle.prefill(*part, A, S)
+        outs.append(o.astype(np.float32))
+    return np.concatenate(outs, axis=1), S
 
 
 def gpu_prefill(kda, g, chunk, **kw):

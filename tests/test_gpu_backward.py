@@ -103,6 +103,16 @@ def test_backward_long_memory(kda, gpu_device, dtype):
     _check(kda, w, 160, gpu_device)
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 16), ("bf16", 128)])
+def test_backward_near_gmin(kda, gpu_device, dtype, d):
+    """z ~ N(2, 1): decays near g_min, so e^{-G} over a 16-token chunk reaches
+    about e^{80}, the edge of the range the chunked form relies on."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(B=1, H=2, dk=d, dv=d, dtype=dtype, z_mean=2.0,
+                                           s0_std=0.5)
+    _say(f"[bwd] near g_min {dtype} d={d} T=100")
+    _check(kda, w, 100, gpu_device)
+
+
 def test_backward_without_state_inputs(kda, gpu_device):
     """S0 = None (zero start) and dS_T = None (no loss on the final state)."""
     w = WORKLOADS["k3_prefill_bf16"].with_(B=2, H=2, dk=16, dv=16, dtype="f32", s0_std=None)

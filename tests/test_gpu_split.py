@@ -5,8 +5,8 @@ the segments' affine state maps (S_end = M S_start + N).
 Against the fp64 oracle at the tolerances of the plain prefill (2e-2 for bf16
 inputs, normwise per (b, h) slice), over ragged lengths, segment counts that
 leave trailing segments empty, a long-memory variant (decays near 1, so the
-maps M carry the state across many segments), in-place state carry, and the
-million-token head share at full size against the unsplit GPU run.
+maps M carry the state across many segments) and in-place state carry.
+The million-token head share is tested in test_gpu_million.py.
 """
 import numpy as np
 import pytest
@@ -95,32 +95,3 @@ def test_split_first_segment_is_exact(kda, gpu_device):
     es = slice_relerr(host(S_T), host(S0_), 1)
     _say(f"[split] 4 segments vs unsplit: o {eo:.3e}  S_T {es:.3e}")
     assert eo <= 2e-2 and es <= 2e-2
-
-
-def _head_relerr(x, ref):
-    """max over heads of max|x - ref| / max|ref| over (b, t, d), on the GPU."""
-    worst = 0.0
-    for h in range(ref.shape[2]):
-        a = x[:, :, h].float()
-        b = ref[:, :, h].float()
-        worst = max(worst, ((a - b).abs().max() / b.abs().max()).item())
-    return worst
-
-
-def test_million_token_split(kda, gpu_device):
-    """B1 H16 T2^20 (one GPU's head share of a million-token context), split
-    into 8 segments (256 workgroups instead of 32), against the unsplit GPU
-    run at the same chunk: the unsplit run is itself checked against the oracle
-    over a prefix in the plain parity tests."""
-    w = WORKLOADS["million_prefill_bf16"]
-    _say(f"[split] {w.name} full size, 8 segments vs unsplit")
-    inp = make_prefill_inputs(w, device=gpu_device)
-    o0, S0_ = gpu_prefill(kda, inp, 16, dv_per_block=64)
-    o, S_T = _split(kda, inp, 8)
-    L = w.T // 8
-    assert torch.equal(o[:, :L], o0[:, :L])
-    eo = _head_relerr(o, o0)
-    es = slice_relerr(host(S_T), host(S0_), 1)
-    _say(f"   o err {eo:.3e}  S_T err {es:.3e}")
-    assert eo <= 2e-2 and es <= 2e-2
-    assert torch.isfinite(S_T).all()

@@ -234,6 +234,27 @@ def test_split_sequence_carries_state():
         assert np.array_equal(S2, S_T)
 
 
+def test_chained_oracle_helper_equals_one_run():
+    """The GPU tests' full-length reference (tests/gpu_helpers.py) runs the
+    oracle segment by segment over a head subset; on a small case it must give
+    exactly the one-shot oracle's numbers for those heads."""
+    import torch
+    from tests.gpu_helpers import oracle_prefill_chained
+    rng = np.random.default_rng(17)
+    B, T, H, dk, dv = 1, 45, 4, 6, 6
+    q, k, v, z, beta, A = _rand_inputs(rng, B, T, H, dk, dv)
+    S0 = rng.standard_normal((B, H, dk, dv))
+    # fp32 inputs, as the GPU tests hand over (the helper reads tensors as fp32)
+    q, k, v, z, beta, A, S0 = (x.astype(np.float32) for x in (q, k, v, z, beta, A, S0))
+    inp = {n: torch.from_numpy(x) for n, x in
+           dict(q=q, k=k, v=v, z=z, beta=beta, A=A, S0=S0).items()}
+    heads = [1, 3]
+    o, S_T = oracle.prefill(q, k, v, z, beta, A, S0)
+    oc, Sc = oracle_prefill_chained(inp, heads, seg=8)
+    assert np.array_equal(oc, o[:, :, heads].astype(np.float32))
+    assert np.array_equal(Sc, S_T[:, heads])
+
+
 def test_linearity_and_independence():
     rng = np.random.default_rng(8)
     B, T, H, dk, dv = 2, 20, 4, 5, 3
