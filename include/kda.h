@@ -39,6 +39,13 @@
  *  - Numerics: fp32 accumulation and an fp32 state.  bf16 outputs are rounded
  *    to nearest even.  NaN/Inf inputs are not checked and propagate.  Results
  *    are bitwise reproducible run to run (no atomics in the arithmetic).
+ *  - Internal waits are bounded.  The prefill kernels hand chunks between
+ *    waves of a workgroup through LDS counters; a wave that waits longer than
+ *    its bound (2^22 sleeps, about a tenth of a second; never seen) gives up,
+ *    and every state column it may have corrupted is then written to S_T as
+ *    NaN, so a give-up never passes for a valid result (o of those columns is
+ *    then unreliable as well).  The environment variable KDA_WAIT_SPIN_LIMIT,
+ *    read at each launch, lowers the bound for testing.
  *  - Preconditions (not checked): q and k are L2-normalised over dk (the
  *    caller's Q/K normalisation; the chunkwise rescaling relies on |k_d| <= 1
  *    for its bf16 range), beta is used as given.  The *_conv entry points

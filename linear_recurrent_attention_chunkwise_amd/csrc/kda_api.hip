@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <stdlib.h>
 
 #include "kda_launch.h"
 
@@ -40,6 +41,16 @@ bool overlaps(Range a, Range b) {
 }
 
 }  // namespace
+
+int kda::wait_spin_limit() {
+    const char *e = getenv("KDA_WAIT_SPIN_LIMIT");
+    if (e && *e) {
+        char *end = nullptr;
+        const long v = strtol(e, &end, 10);
+        if (end && *end == 0 && v >= 0 && v <= (1L << 30)) return (int)v;
+    }
+    return 1 << 22;
+}
 
 extern "C" {
 

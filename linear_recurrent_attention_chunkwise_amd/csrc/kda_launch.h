@@ -116,6 +116,12 @@ hipError_t launch_split_scan(const float *S0, const float *M, const float *N, fl
 hipError_t launch_split_gather(const float *Sseg, float *S_T, int64_t B, int64_t H, int P, int D,
                                hipStream_t stream);
 
+// Sleeps a role-split kernel's slot wait takes before it gives up (and
+// poisons the affected state columns with NaN): 2^22 by default, or the value
+// of the environment variable KDA_WAIT_SPIN_LIMIT (a testing knob: a host-side
+// test forces give-ups with a tiny limit, every kernel still exits normally).
+int wait_spin_limit();
+
 bool decode_supported(int dtype, int64_t D);
 hipError_t launch_decode(const DecodeArgs &a);
 

@@ -63,6 +63,7 @@ struct Prefill16Params {
     int64_t n_ckpt;
     int ckpt_every;      // tokens between checkpoints (0: none)
     int ckpt_blocked;    // 1: bf16 checkpoints in 4-row blocks ((d/4)*D + j)*4 + d%4
+    int spin_limit;      // sleeps before a slot wait gives up
 };
 
 template <int NCW, int NPW, int NSLOT>
@@ -87,24 +88,32 @@ struct P16Cfg {
     // prep-wave scratch
     static constexpr int W_BETA = 0;                        // beta  [C] fp32
     static constexpr int SCR = (W_BETA + C * 4 + 15) / 16 * 16;
-    static constexpr int OFF_FLAGS = 0;                     // ready[8], done[NSLOT][NCW]
+    static constexpr int OFF_FLAGS = 0;                     // ready[8], done[NSLOT][NCW], poison
     static constexpr int OFF_DONE = 32;
-    static constexpr int OFF_SLOTS = 128;
+    static constexpr int OFF_POISON = 128;
+    static constexpr int OFF_SLOTS = 144;
     static constexpr int OFF_SCR = OFF_SLOTS + NSLOT * SLOT;
     static constexpr int LDS_BYTES = OFF_SCR + NPW * SCR;
-    static_assert(NSLOT <= 8 && OFF_DONE + NSLOT * NCW * 4 <= OFF_SLOTS, "flag area");
+    static_assert(NSLOT <= 8 && OFF_DONE + NSLOT * NCW * 4 <= OFF_POISON, "flag area");
     static_assert(NCW + NPW <= 16, "workgroup size");
     static_assert(SLOT % 16 == 0 && SCR % 16 == 0, "alignment");
     static_assert(LDS_BYTES <= 150 * 1024, "LDS budget");
 };
 
-// Bounded LDS wait: returns once *flag >= target (workgroup-scope acquire).
-__device__ __forceinline__ void wait_at_least(int *flag, int target) {
-    for (int it = 0; it < (1 << 22); ++it) {
+// Bounded LDS wait: true once *flag >= target (workgroup-scope acquire);
+// false after `limit` sleeps without it.  A wave that gives up raises the
+// workgroup's poison flag, and every state column it may have corrupted is
+// then written as NaN (see the chain's final store), so a give-up can never
+// pass for a valid result.
+__device__ __forceinline__ bool wait_at_least(int *flag, int target, int limit, int *poison) {
+    for (int it = 0;; ++it) {
         if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
-            return;
+            return true;
+        if (it >= limit) break;
         __builtin_amdgcn_s_sleep(1);
     }
+    __hip_atomic_store(poison, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return false;
 }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -156,6 +165,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
     int *ready = reinterpret_cast<int *>(smem + Cfg::OFF_FLAGS);
     int *done = reinterpret_cast<int *>(smem + Cfg::OFF_DONE);   // [slot][chain wave]
+    int *poison = reinterpret_cast<int *>(smem + Cfg::OFF_POISON);
+    const int spin = prm.spin_limit;
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wave-uniform by construction; readfirstlane lets the compiler keep it
@@ -210,8 +221,9 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         // ahead; Kh^T and V by transposing reads of token-major tiles: V as
         // V[t0 + 4g + e][jw + n], staged by the prep wave, zero past T)
         Frag<bf16> Wf[NDT], Kf[NDT], Tf, Vn;
+        bool waited_ok = true;   // every slot wait of this wave succeeded
         auto read_wtk = [&](int sl, int use) {
-            wait_at_least(&ready[sl], use + 1);
+            waited_ok &= wait_at_least(&ready[sl], use + 1, spin, poison);
             const int off = Cfg::OFF_SLOTS + sl * Cfg::SLOT;
             const char *pd = smem + off + offDP;
             const char *pc = smem + off + offCP;
@@ -339,6 +351,15 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             sl = sl1;
             use = use1;
         }
+        // A prep wave that gave up a wait may have overwritten a slot this
+        // wave was still reading: its poison store precedes a release of
+        // `ready` that this wave has acquired since.  Another chain wave's
+        // give-up corrupts only that wave's own columns.
+        if (!waited_ok ||
+            __hip_atomic_load(poison, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) {
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) S[i] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        }
         float *st = prm.S_T + bh * (int64_t)(D * D);
 #pragma unroll
         for (int i = 0; i < NDT; ++i)
@@ -426,7 +447,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
 
         // every chain wave has read the previous use of the slot
 #pragma unroll
-        for (int w = 0; w < NCW; ++w) wait_at_least(&done[s_ * NCW + w], use);
+        for (int w = 0; w < NCW; ++w) wait_at_least(&done[s_ * NCW + w], use, spin, poison);
 
         if constexpr (MODE != 2) {
             bf16 *sV = reinterpret_cast<bf16 *>(slot + Cfg::S_V);
@@ -572,6 +593,7 @@ static hipError_t launch_p16(const PrefillArgs &a) {
     prm.n_ckpt = a.n_ckpt;
     prm.ckpt_every = a.ckpt_every;
     prm.ckpt_blocked = a.ckpt_blocked ? 1 : 0;
+    prm.spin_limit = wait_spin_limit();
     const int64_t nblk = a.B * a.H * prm.nsplit;
     hipLaunchKernelGGL((kda_prefill16_kernel<NCW, NPW, NSLOT, CKPT, MODE>), dim3((unsigned)nblk),
                        dim3(64 * (NCW + NPW)), 0, a.stream, prm);
