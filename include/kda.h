@@ -186,6 +186,29 @@ kda_status kda_prefill_varlen(int dtype, int64_t N, int64_t T_total, int64_t H,
 size_t kda_prefill_varlen_workspace_size(int64_t N);
 
 /*
+ * kda_prefill_varlen for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call without a workspace argument.  The longest-first
+ * ranking of the sequences goes to a static scratch array inside the library
+ * (32 KiB per GPU, for at most 8192 sequences, set up on the first call on
+ * each device and held until the process ends); nothing is allocated.
+ *   N > 8192 returns KDA_ERR_WORKSPACE (beyond the scratch); every other
+ *   argument, check and result is that of kda_prefill_varlen (bit for bit).
+ * All calls on one GPU share that GPU's scratch: calls that overlap in time on
+ * one GPU (different streams, threads) race and must be serialised by the
+ * caller.  The scratch needs no clearing: each call writes every rank it
+ * reads, before reading it, in stream order.
+ */
+kda_status kda_prefill_varlen_noalloc(int dtype, int64_t N, int64_t T_total, int64_t H,
+                                      int64_t dk, int64_t dv, int32_t chunk,
+                                      const int64_t *cu_seqlens,
+                                      const void *q, const void *k, const void *v,
+                                      const void *z, const void *beta, const float *A,
+                                      const float *S0, void *o, float *S_T,
+                                      int32_t ckpt_every, float *ckpt, int64_t n_ckpt,
+                                      void *stream, int32_t dv_per_block);
+
+/*
  * Prefill of long sequences split into `segments` parallel pieces.
  *
  * The recurrence is affine in the state, so over a segment S_end = M S_start

@@ -93,7 +93,8 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
                         const float *S0, void *o, float *S_T, int32_t ckpt_every,
                         float *ckpt, int64_t n_ckpt, void *workspace, size_t workspace_bytes,
                         void *stream, int32_t dv_per_block, int mode = 0,
-                        bool check_only = false, bool ckpt_blocked = false) {
+                        bool check_only = false, bool ckpt_blocked = false,
+                        bool scratch_ranking = false, int32_t *order_scratch = nullptr) {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || n_ckpt < 0 || ckpt_every < 0)
         return KDA_ERR_SHAPE;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -139,7 +140,10 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
     if (cu && ((uintptr_t)cu & 7u) != 0) return KDA_ERR_MISALIGNED;
-    const size_t need_ws = cu && H > 0 ? order_bytes(B) : 0;   // longest-first order
+    // longest-first order of packed sequences: in the caller's workspace, or
+    // in the library's static scratch (order_scratch, kMaxOrderSeqs entries)
+    const size_t need_ws = cu && H > 0 && !scratch_ranking ? order_bytes(B) : 0;
+    const bool rank = cu && H > 0 && order_bytes(B) > 0;
     if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_WORKSPACE;
     if (need_ws > 0 && !aligned16(workspace)) return KDA_ERR_MISALIGNED;
     const Range rq = range_of(q, nin * esz), rk = range_of(k, nin * esz),
@@ -171,8 +175,9 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
     a.o = mode == 0 ? o : nullptr; a.S_T = S_T;
     a.cu_seqlens = cu;
     a.order = nullptr;
-    if (need_ws > 0) {
-        int32_t *order = static_cast<int32_t *>(workspace);
+    if (rank) {
+        int32_t *order = scratch_ranking ? order_scratch : static_cast<int32_t *>(workspace);
+        if (!order) return KDA_ERR_NULL;
         if (kda::launch_seq_order(cu, B, T, order, (hipStream_t)stream) != hipSuccess)
             return KDA_ERR_HIP;
         a.order = order;
@@ -215,6 +220,62 @@ kda_status kda_prefill_varlen(int dtype, int64_t N, int64_t T_total, int64_t H, 
     return prefill_impl(dtype, N, T_total, H, dk, dv, chunk, cu_seqlens, q, k, v, z, beta, A,
                         S0, o, S_T, ckpt_every, ckpt, n_ckpt, workspace, workspace_bytes, stream,
                         dv_per_block);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of kda_prefill_varlen_noalloc: the longest-first ranking of up to
+// kMaxOrderSeqs packed sequences (32 KiB on every device the library runs
+// on, held until the process ends).  Host code never uses this name as an
+// address: each device's copy is looked up once with hipGetSymbolAddress
+// (that device current) and only that pointer is passed to kernels.
+static __device__ __align__(256) int32_t scratch[kda::kMaxOrderSeqs];
+
+constexpr int kScratchDevices = 256;
+std::mutex g_scratch_mu;
+int32_t *g_scratch_ptr[kScratchDevices] = {};
+
+// This device's copy of `scratch`, set up on the first call on the device.
+kda_status scratch_of_current_device(int32_t **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return KDA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_HIP;
+        g_scratch_ptr[dev] = static_cast<int32_t *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_varlen_noalloc(int dtype, int64_t N, int64_t T_total, int64_t H,
+                                      int64_t dk, int64_t dv, int32_t chunk,
+                                      const int64_t *cu_seqlens, const void *q, const void *k,
+                                      const void *v, const void *z, const void *beta,
+                                      const float *A, const float *S0, void *o, float *S_T,
+                                      int32_t ckpt_every, float *ckpt, int64_t n_ckpt,
+                                      void *stream, int32_t dv_per_block) {
+    if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
+    if (N > kda::kMaxOrderSeqs) return KDA_ERR_WORKSPACE;   // beyond the static scratch
+    // every other check first, so that an invalid call touches nothing
+    const kda_status st = prefill_impl(dtype, N, T_total, H, dk, dv, chunk, cu_seqlens, q, k, v,
+                                       z, beta, A, S0, o, S_T, ckpt_every, ckpt, n_ckpt, nullptr,
+                                       0, stream, dv_per_block, 0, /*check_only=*/true,
+                                       false, /*scratch_ranking=*/true);
+    if (st != KDA_OK) return st;
+    int32_t *order = nullptr;
+    const kda_status ss = scratch_of_current_device(&order);
+    if (ss != KDA_OK) return ss;
+    return prefill_impl(dtype, N, T_total, H, dk, dv, chunk, cu_seqlens, q, k, v, z, beta, A, S0,
+                        o, S_T, ckpt_every, ckpt, n_ckpt, nullptr, 0, stream, dv_per_block, 0,
+                        false, false, true, order);
 }
 
 kda_status kda_prefill(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,

@@ -70,6 +70,10 @@ def _load():
     lib.kda_prefill_varlen.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i32, vp,
                                        vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        i32, vp, i64, vp, sz, vp, i32]
+    lib.kda_prefill_varlen_noalloc.restype = ctypes.c_int
+    lib.kda_prefill_varlen_noalloc.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i32, vp,
+                                               vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               i32, vp, i64, vp, i32]
     lib.kda_prefill_varlen_workspace_size.restype = sz
     lib.kda_prefill_varlen_workspace_size.argtypes = [i64]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -224,7 +228,7 @@ def checkpoint_rows(seq_lens, ckpt_every: int):
 
 def prefill_varlen(q, k, v, z, beta, A, cu_seqlens, S0=None, chunk: int = 16,
                    ckpt_every: int = 0, out=None, S_T=None, ckpt=None,
-                   dv_per_block: int = 0, seq_lens=None):
+                   dv_per_block: int = 0, seq_lens=None, no_alloc: bool = False):
     """KDA prefill over N sequences packed along one token axis.
 
     q, k, z [T,H,dk]; v [T,H,dv]; beta [T,H] (one dtype, fp32 or bf16);
@@ -237,7 +241,12 @@ def prefill_varlen(q, k, v, z, beta, A, cu_seqlens, S0=None, chunk: int = 16,
     ``cu_seqlens`` may be a CPU or GPU tensor; the library reads a GPU copy,
     and host values size the checkpoint buffer.  Passing ``seq_lens`` (the
     host list of lengths) together with a GPU ``cu_seqlens`` avoids every
-    host-device copy in this call."""
+    host-device copy in this call.
+
+    ``no_alloc=True`` calls kda_prefill_varlen_noalloc, which ranks the
+    sequences in the library's static scratch instead of a workspace (at most
+    8192 sequences); with ``out``, ``S_T`` (and ``ckpt``) given and a GPU
+    ``cu_seqlens`` with ``seq_lens``, the call then allocates nothing."""
     lib = _load()
     if q.dim() != 3:
         raise ValueError("q must be [T,H,dk] (packed sequences)")
@@ -286,6 +295,14 @@ def prefill_varlen(q, k, v, z, beta, A, cu_seqlens, S0=None, chunk: int = 16,
         _require(ckpt, "ckpt", (n_ckpt, H, dk, dv), torch.float32, dev)
     else:
         ckpt = None
+    if no_alloc:
+        st = lib.kda_prefill_varlen_noalloc(_DTYPES[dt], N, T, H, dk, dv, int(chunk), _ptr(cu_dev),
+                                            _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta),
+                                            _ptr(A), _ptr(S0), _ptr(out), _ptr(S_T),
+                                            int(ckpt_every), _ptr(ckpt), n_ckpt,
+                                            _stream_handle(dev), int(dv_per_block))
+        _check(st, "kda_prefill_varlen_noalloc")
+        return out, S_T, ckpt
     ws_bytes = int(lib.kda_prefill_varlen_workspace_size(N))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     st = lib.kda_prefill_varlen(_DTYPES[dt], N, T, H, dk, dv, int(chunk), _ptr(cu_dev),

@@ -34,7 +34,8 @@ def test_header_declares_expected_api():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_str", "kda_prefill_workspace_size",
         "kda_prefill", "kda_prefill_ex", "kda_prefill_varlen",
-        "kda_prefill_varlen_workspace_size", "kda_decode_step", "kda_conv_norm",
+        "kda_prefill_varlen_workspace_size", "kda_prefill_varlen_noalloc", "kda_decode_step",
+        "kda_conv_norm",
         "kda_prefill_conv_workspace_size", "kda_prefill_conv", "kda_decode_step_conv",
         "kda_prefill_split", "kda_prefill_split_workspace_size", "kda_conv_norm_varlen",
         "kda_prefill_bwd", "kda_prefill_bwd_workspace_size"])
@@ -412,3 +413,24 @@ def test_backward_workspace_holds_forward_and_checkpoints(lib):
     n = lib.kda_prefill_bwd_workspace_size(BF16, B, T, H, d, d)
     units = B * H * ((T + 15) // 16)
     assert n >= ckpt // 2 + B * H * d * d * 4 + units * d * d * 2
+
+
+def test_noalloc_varlen_validates_before_any_device_call(lib):
+    """kda_prefill_varlen_noalloc checks its arguments before it touches the
+    device (its scratch is looked up only for a valid call), so these statuses
+    come back without a GPU."""
+    i64 = ctypes.c_int64
+    f = lib.kda_prefill_varlen_noalloc
+    cu = P(20)
+
+    def call(dtype=BF16, N=3, T=64, H=2, d=128, chunk=16, cu_=cu, beta=P(5)):
+        return f(dtype, N, T, H, d, d, chunk, cu_, P(1), P(2), P(3), P(4), beta, P(6), None,
+                 P(8), P(9), 0, None, 0, None, 0)
+    assert call(N=8193) == 6                    # beyond the static scratch
+    assert call(dtype=7) == 3
+    assert call(d=64) == 3
+    assert call(chunk=32) == 3
+    assert call(N=-1) == 2
+    assert call(cu_=None) == 1
+    assert call(beta=None) == 1
+    assert call(beta=ctypes.c_void_p(BASE + 8)) == 4
