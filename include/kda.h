@@ -19,8 +19,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every tensor pointer is a DEVICE pointer on the current HIP device; the
- *    caller owns all memory.  The library allocates no device memory and keeps
- *    no mutable global state; calls are thread-safe and re-entrant.
+ *    caller owns all memory and every stream.  The library allocates no device
+ *    memory.  Its only state across calls is the per-device address of the
+ *    static scratch of kda_prefill_varlen_noalloc, set once per device; calls
+ *    are thread-safe and re-entrant (except that noalloc calls overlapping on
+ *    one GPU share that scratch).
  *  - Layouts are dense row-major:
  *        q, k, z : [B, T, H, dk]        v, o : [B, T, H, dv]
  *        beta    : [B, T, H]            A    : [H]  (fp32)
@@ -62,7 +65,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 7
+#define KDA_ABI_VERSION 8
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -269,12 +272,8 @@ size_t kda_prefill_split_workspace_size(int dtype, int64_t B, int64_t T, int64_t
  * state checkpoints and the per-chunk dL/dS' hand-off between them are kept
  * in bf16 in the workspace); every other case, and all per-token work, is
  * fp32.  No atomics, so results are bitwise reproducible.
- * Streams: all work is ordered after earlier work on `stream`, and later work
- * on `stream` sees every output.  On that bf16 dk = dv = 128 path the first
- * backward kernel runs on a library-owned stream of the current device
- * (created on the first call, default priority) beside the forward rerun,
- * forked from and joined back to `stream` with events; the calls serialise
- * that fork under a lock.
+ * Every kernel runs on `stream`, in order (see kda_prefill_bwd_ex for an
+ * overlapped variant).
  * Supported: dtype in {KDA_F32, KDA_BF16}, dk == dv in {16, 128}.  Outputs
  * must not overlap one another, any input or the workspace.  Errors as
  * kda_prefill_ex.
@@ -287,6 +286,30 @@ kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
                            float *dq, float *dk_out, float *dv_out, float *dz,
                            float *dbeta, float *dA, float *dS0,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_prefill_bwd with a second stream of the caller's (`side_stream`, on the
+ * same device; NULL or equal to `stream` gives kda_prefill_bwd itself).  On
+ * the bf16 dk = dv = 128 path the per-chunk prep kernel, which reads no state
+ * checkpoint, then runs on `side_stream` beside the forward rerun on
+ * `stream`: forked after the work already on `stream`, joined back before the
+ * state-gradient chain, with two events created for the call and destroyed
+ * once enqueued.  Results are identical bit for bit.  All work stays ordered
+ * after earlier work on `stream`, later work on `stream` sees every output,
+ * and nothing else is enqueued on `side_stream` (work queued there after the
+ * call may run before the call's prep finishes; it never runs alongside
+ * earlier work on `stream` that the call depends on).  Use one side stream
+ * per concurrent call.
+ */
+kda_status kda_prefill_bwd_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                              int64_t dv,
+                              const void *q, const void *k, const void *v, const void *z,
+                              const void *beta, const float *A, const float *S0,
+                              const void *dO, const float *dS_T,
+                              float *dq, float *dk_out, float *dv_out, float *dz,
+                              float *dbeta, float *dA, float *dS0,
+                              void *workspace, size_t workspace_bytes, void *stream,
+                              void *side_stream);
 
 /* Bytes of workspace kda_prefill_bwd needs (0 for unsupported arguments). */
 size_t kda_prefill_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t H,

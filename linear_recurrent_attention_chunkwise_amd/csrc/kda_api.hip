@@ -1,8 +1,10 @@
 // kda_api.hip -- the extern "C" entry points of libkda.so (see include/kda.h).
 //
 // Every check runs before anything is enqueued; on an error status no kernel
-// is launched and no output is touched.  No device memory is allocated here
-// and no global state is kept.
+// is launched and no output is touched.  No device memory is allocated here.
+// The one piece of state kept across calls is the per-device address of the
+// static scratch of kda_prefill_varlen_noalloc (looked up once per device);
+// the backward's optional second stream belongs to the caller.
 #include "kda.h"
 
 #include <hip/hip_runtime.h>
@@ -754,39 +756,6 @@ namespace {
 
 constexpr int kBwdChunk = 16;
 
-// A second stream per device (default priority) and two events, so that the
-// backward's prep runs beside its forward rerun (prep reads no checkpoint).  Created on first use and kept until the process ends;
-// the mutex keeps the record/wait pairs of concurrent calls apart.
-struct SideStream {
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
-
-// with g_side_mu held
-SideStream *side_stream() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-    SideStream &ss = g_side[dev];
-    if (!ss.s) {
-        hipStream_t st = nullptr;
-        hipEvent_t f = nullptr, j = nullptr;
-        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-        if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
-            if (f) (void)hipEventDestroy(f);
-            (void)hipStreamDestroy(st);
-            return nullptr;
-        }
-        ss.s = st;
-        ss.fork = f;
-        ss.join = j;
-    }
-    return &ss;
-}
-
 struct BwdLayout {
     size_t o, S_T, ckpt, prep, part, dA, dsp, total;   // byte offsets, and the size
 };
@@ -830,12 +799,20 @@ size_t kda_prefill_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t H
     return bwd_layout(dtype, B, T, H, dk, &lay) ? lay.total : 0;
 }
 
-kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                           const void *q, const void *k, const void *v, const void *z,
-                           const void *beta, const float *A, const float *S0, const void *dO,
-                           const float *dS_T, float *dq, float *dk_out, float *dv_out,
-                           float *dz, float *dbeta, float *dA, float *dS0, void *workspace,
-                           size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward on `stream`; with a second caller stream `side` (not NULL and
+// not `stream`), the bf16 d = 128 path runs its prep kernel there, beside the
+// forward rerun, forked from and joined back to `stream` with two events made
+// for this call (destroyed once enqueued; HIP frees them when they complete).
+kda_status bwd_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                    const void *q, const void *k, const void *v, const void *z,
+                    const void *beta, const float *A, const float *S0, const void *dO,
+                    const float *dS_T, float *dq, float *dk_out, float *dv_out,
+                    float *dz, float *dbeta, float *dA, float *dS0, void *workspace,
+                    size_t workspace_bytes, void *stream, void *side) {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (dk != dv || (dk != 16 && dk != 128)) return KDA_ERR_UNSUPPORTED;
@@ -898,7 +875,7 @@ kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
     a.dsp = bh > 0 && lay.total > lay.dsp ? static_cast<void *>(ws + lay.dsp) : nullptr;
     a.dq = dq; a.dk = dk_out; a.dv = dv_out; a.dz = dz; a.dbeta = dbeta; a.dA = dA; a.dS0 = dS0;
     a.stream = s;
-    if (!mfma || bth == 0) {
+    if (!mfma || bth == 0 || !side || side == stream) {
         if (bth > 0) {
             const kda_status st = rerun(stream, false);
             if (st != KDA_OK) return st;
@@ -913,19 +890,50 @@ kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
         const kda_status chk = rerun(nullptr, true);   // validation only, before any launch
         if (chk != KDA_OK) return chk;
     }
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream *ss = side_stream();
-    if (!ss) return KDA_ERR_HIP;
-    if (hipEventRecord(ss->fork, s) != hipSuccess) return KDA_ERR_HIP;
-    const kda_status st = rerun(stream, false);
-    if (st != KDA_OK) return st;
-    kda::BwdArgs af = a;
-    af.stream = ss->s;
-    if (hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess ||
-        kda::launch_bwd_front(af) != hipSuccess || hipEventRecord(ss->join, ss->s) != hipSuccess ||
-        hipStreamWaitEvent(s, ss->join, 0) != hipSuccess)
+    const hipStream_t ss = (hipStream_t)side;
+    hipEvent_t fork = nullptr, join = nullptr;
+    if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) return KDA_ERR_HIP;
+    if (hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
+        (void)hipEventDestroy(fork);
         return KDA_ERR_HIP;
+    }
+    kda_status st = KDA_OK;
+    if (hipEventRecord(fork, s) != hipSuccess) st = KDA_ERR_HIP;
+    if (st == KDA_OK) st = rerun(stream, false);
+    kda::BwdArgs af = a;
+    af.stream = ss;
+    if (st == KDA_OK &&
+        (hipStreamWaitEvent(ss, fork, 0) != hipSuccess || kda::launch_bwd_front(af) != hipSuccess ||
+         hipEventRecord(join, ss) != hipSuccess || hipStreamWaitEvent(s, join, 0) != hipSuccess))
+        st = KDA_ERR_HIP;
+    (void)hipEventDestroy(fork);
+    (void)hipEventDestroy(join);
+    if (st != KDA_OK) return st;
     return kda::launch_bwd_back(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_bwd(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                           const void *q, const void *k, const void *v, const void *z,
+                           const void *beta, const float *A, const float *S0, const void *dO,
+                           const float *dS_T, float *dq, float *dk_out, float *dv_out,
+                           float *dz, float *dbeta, float *dA, float *dS0, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    return bwd_impl(dtype, B, T, H, dk, dv, q, k, v, z, beta, A, S0, dO, dS_T, dq, dk_out, dv_out,
+                    dz, dbeta, dA, dS0, workspace, workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_prefill_bwd_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                              const void *q, const void *k, const void *v, const void *z,
+                              const void *beta, const float *A, const float *S0, const void *dO,
+                              const float *dS_T, float *dq, float *dk_out, float *dv_out,
+                              float *dz, float *dbeta, float *dA, float *dS0, void *workspace,
+                              size_t workspace_bytes, void *stream, void *side_stream) {
+    return bwd_impl(dtype, B, T, H, dk, dv, q, k, v, z, beta, A, S0, dO, dS_T, dq, dk_out, dv_out,
+                    dz, dbeta, dA, dS0, workspace, workspace_bytes, stream, side_stream);
 }
 
 }  // extern "C"

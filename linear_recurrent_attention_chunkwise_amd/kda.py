@@ -103,6 +103,9 @@ def _load():
     lib.kda_prefill_bwd.restype = ctypes.c_int
     lib.kda_prefill_bwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64] + [vp] * 17 + [
         sz, vp]
+    lib.kda_prefill_bwd_ex.restype = ctypes.c_int
+    lib.kda_prefill_bwd_ex.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64] + [vp] * 17 + [
+        sz, vp, vp]
     lib.kda_prefill_bwd_workspace_size.restype = sz
     lib.kda_prefill_bwd_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64]
     _lib = lib
@@ -549,14 +552,29 @@ def prefill_bwd_workspace_size(dtype: torch.dtype, B: int, T: int, H: int, dk: i
     return int(_load().kda_prefill_bwd_workspace_size(_DTYPES[dtype], B, T, H, dk, dv))
 
 
-def prefill_bwd(q, k, v, z, beta, A, S0, dO, dS_T=None, workspace=None):
-    """Gradients of a loss through the prefill (kda_prefill_bwd).
+_side_streams = {}
+
+
+def _side_stream(dev):
+    """One torch stream per device (default priority) for the backward's
+    overlapped prep; owned here, on the caller's side of the C ABI."""
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    if idx not in _side_streams:
+        _side_streams[idx] = torch.cuda.Stream(device=idx)
+    return _side_streams[idx]
+
+
+def prefill_bwd(q, k, v, z, beta, A, S0, dO, dS_T=None, workspace=None, side_stream="auto"):
+    """Gradients of a loss through the prefill (kda_prefill_bwd_ex).
 
     Inputs as ``prefill`` (S0 may be None), dO [B,T,H,dv] in the input dtype
     (dL/do) and dS_T [B,H,dk,dv] fp32 or None (dL/dS_T).  Returns a dict of
     fp32 tensors: dq, dk, dz [B,T,H,dk]; dv [B,T,H,dv]; dbeta [B,T,H];
     dA [H]; dS0 [B,H,dk,dv].  ``workspace`` may be a preallocated uint8 cuda
-    tensor of ``prefill_bwd_workspace_size`` bytes."""
+    tensor of ``prefill_bwd_workspace_size`` bytes.  ``side_stream``: a
+    torch.cuda.Stream on which the library may run its prep kernel beside the
+    forward rerun, ``"auto"`` (a stream kept by this module, one per device)
+    or None (everything on the current stream; the same results)."""
     lib = _load()
     if q.dim() != 4:
         raise ValueError("q must be [B,T,H,dk]")
@@ -588,11 +606,16 @@ def prefill_bwd(q, k, v, z, beta, A, S0, dO, dS_T=None, workspace=None):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     elif workspace.numel() < ws_bytes or workspace.device != dev:
         raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
-    st = lib.kda_prefill_bwd(_DTYPES[dt], B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(z),
-                             _ptr(beta), _ptr(A), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(g["dq"]),
-                             _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dz"]), _ptr(g["dbeta"]),
-                             _ptr(g["dA"]), _ptr(g["dS0"]), _ptr(workspace),
-                             workspace.numel() if workspace is not None else 0,
-                             _stream_handle(dev))
-    _check(st, "kda_prefill_bwd")
+    if isinstance(side_stream, str):
+        if side_stream != "auto":
+            raise ValueError("side_stream must be a torch.cuda.Stream, 'auto' or None")
+        side_stream = _side_stream(dev)
+    side = ctypes.c_void_p(side_stream.cuda_stream) if side_stream is not None else None
+    st = lib.kda_prefill_bwd_ex(_DTYPES[dt], B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(z), _ptr(beta), _ptr(A), _ptr(S0), _ptr(dO), _ptr(dS_T),
+                                _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dz"]),
+                                _ptr(g["dbeta"]), _ptr(g["dA"]), _ptr(g["dS0"]), _ptr(workspace),
+                                workspace.numel() if workspace is not None else 0,
+                                _stream_handle(dev), side)
+    _check(st, "kda_prefill_bwd_ex")
     return g

@@ -38,7 +38,7 @@ def test_header_declares_expected_api():
         "kda_conv_norm",
         "kda_prefill_conv_workspace_size", "kda_prefill_conv", "kda_decode_step_conv",
         "kda_prefill_split", "kda_prefill_split_workspace_size", "kda_conv_norm_varlen",
-        "kda_prefill_bwd", "kda_prefill_bwd_workspace_size"])
+        "kda_prefill_bwd", "kda_prefill_bwd_ex", "kda_prefill_bwd_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 7
+    assert lib.kda_abi_version() == 8
     for s in range(8):
         assert lib.kda_status_str(s).decode().startswith("KDA_")
     assert lib.kda_status_str(99) == b"unknown kda_status"

@@ -27,7 +27,7 @@ GRAD_HEAD_AXIS = {"dq": 2, "dk": 2, "dv": 2, "dz": 2, "dbeta": 2, "dS0": 1}
 @pytest.fixture(scope="module")
 def kda():
     import linear_recurrent_attention_chunkwise_amd as m
-    assert m.abi_version() == 7
+    assert m.abi_version() == 8
     return m
 
 
@@ -154,12 +154,30 @@ def test_backward_is_deterministic(kda, gpu_device):
         assert torch.equal(a[key], b[key]), key
 
 
+def test_backward_side_stream_is_optional(kda, gpu_device):
+    """kda_prefill_bwd (everything on the caller's stream), kda_prefill_bwd_ex
+    with the binding's side stream and with an explicit caller stream give the
+    same bits."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(B=2, H=3, s0_std=0.5)
+    g = to_dev(make_prefill_inputs(w, T=260), gpu_device)
+    dO, dST = (t.to(gpu_device) for t in make_cotangents(w, T=260))
+    serial = kda.prefill_bwd(g["q"], g["k"], g["v"], g["z"], g["beta"], g["A"], g["S0"], dO,
+                             dST, side_stream=None)
+    auto = kda.prefill_bwd(g["q"], g["k"], g["v"], g["z"], g["beta"], g["A"], g["S0"], dO, dST)
+    mine = kda.prefill_bwd(g["q"], g["k"], g["v"], g["z"], g["beta"], g["A"], g["S0"], dO, dST,
+                           side_stream=torch.cuda.Stream(device=gpu_device))
+    torch.cuda.synchronize()
+    for key in serial:
+        assert torch.equal(serial[key], auto[key]) and torch.equal(serial[key], mine[key]), key
+
+
 def test_backward_on_a_caller_stream_is_ordered(kda, gpu_device):
-    """bf16 d = 128 forks its forward rerun onto a library stream.  On a caller
-    stream, behind long work that writes the inputs just before the call, the
-    rerun must read the written inputs, the later kernels its checkpoints (the
-    workspace starts as NaN bytes), and the caller stream's next work must see
-    every output: the results equal a default-stream call bit for bit."""
+    """bf16 d = 128 forks its prep onto a second stream (the binding's).  On a
+    caller stream, behind long work that writes the inputs just before the
+    call, the rerun must read the written inputs, the later kernels its
+    checkpoints (the workspace starts as NaN bytes), and the caller stream's
+    next work must see every output: the results equal a default-stream call
+    bit for bit."""
     w = WORKLOADS["k3_prefill_bf16"].with_(B=1, H=4, s0_std=0.5)
     T = 300
     g = to_dev(make_prefill_inputs(w, T=T), gpu_device)

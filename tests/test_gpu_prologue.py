@@ -27,7 +27,7 @@ EPS = 1e-6
 @pytest.fixture(scope="module")
 def kda():
     import linear_recurrent_attention_chunkwise_amd as m
-    assert m.abi_version() == 7
+    assert m.abi_version() == 8
     return m
 
 

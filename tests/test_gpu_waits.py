@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(scope="module")
 def kda():
     import linear_recurrent_attention_chunkwise_amd as m
-    assert m.abi_version() == 7
+    assert m.abi_version() == 8
     return m
 
 
