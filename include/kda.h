@@ -13,8 +13,8 @@
  * per batch entry b and head h.  S_t has dk key rows and dv value columns;
  * alpha_t is a per-key-channel vector scaling S's rows; sigma is the logistic
  * function.  The same section splits the work into a chunked-parallel prefill
- * ("tokens are processed in parallel within chunks") and a fused recurrent
- * one-token decode step that keeps the state persistent.
+ * (the tokens of a chunk handled together) and a fused recurrent one-token
+ * decode step whose state persists between calls.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -99,8 +99,8 @@ size_t kda_prefill_workspace_size(int dtype, int64_t B, int64_t T, int64_t H,
                                   int64_t dk, int64_t dv, int32_t chunk);
 
 /*
- * Chunkwise prefill over T tokens (the "KDA prefill" half of the runtime
- * split in the section quoted above).  Tokens are grouped into chunks of
+ * Chunkwise prefill over T tokens (the prefill half of the prefill/decode
+ * split in the section cited above).  Tokens are grouped into chunks of
  * `chunk`; within a chunk all interactions run as dense tiles, between chunks
  * the state is carried.  A last partial chunk is allowed (any T >= 0).
  *
@@ -140,9 +140,9 @@ kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk
 
 /*
  * Prefill over N variable-length sequences packed along one token axis, with
- * optional state checkpoints.  The state is "kept persistent per request and
- * layer", and a reused prefix is only valid together with the KDA state
- * checkpoint taken at the same token boundary ("Kimi K3 Open Weights: What Is
+ * optional state checkpoints.  The KDA state persists per request and layer,
+ * and a reused prefix is only valid together with the KDA state checkpoint
+ * taken at the same token boundary ("Kimi K3 Open Weights: What Is
  * Actually New ...", section "Why '104B active' still understates the systems
  * problem"); this entry point produces those checkpoints as it goes.
  *
@@ -316,9 +316,9 @@ size_t kda_prefill_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t H
                                       int64_t dk, int64_t dv);
 
 /*
- * One fused recurrent decode step for B sequences (the "KDA decode" half of
- * the runtime split: one recurrent-state update per layer and token, with the
- * state kept persistent).
+ * One fused recurrent decode step for B sequences (the decode half of the
+ * same section's prefill/decode split: the state is updated once per token
+ * and layer and persists between calls).
  *
  *   in : q, k, z [B,H,dk], v [B,H,dv], beta [B,H] (dtype); A [H] fp32.
  *   in/out: S [B,H,dk,dv] fp32 -- read once and overwritten with S_t.

@@ -1,9 +1,9 @@
 // kda_decode.hip -- fused one-token KDA decode step (gfx950).
 //
 // The step is the KDA recurrence of "Kimi K3 Open Weights: What Is Actually
-// New", section 1, for a single token, with the state kept in HBM between
-// calls ("one recurrent-state update per layer and token ... recurrent state
-// kept persistent").  Writing a = alpha*k, b = alpha*q:
+// New", section 1 (its prefill/decode split), for a single token: decode
+// updates the recurrent state once per token and layer, and the state stays
+// in HBM from one call to the next.  Writing a = alpha*k, b = alpha*q:
 //
 //     w = S^T a,  y = S^T b           (one pass over S, reductions over dk)
 //     u = beta (v - w)
@@ -18,8 +18,8 @@
 // and streaming it past the caches keeps the read stream of the other heads'
 // states at full rate (measured on MI355X: 6.9 TB/s instead of 5.3 TB/s).
 //
-// The CONV instantiation fuses the layer's prologue into the step (same page
-// section: decode keeps "convolution state and recurrent state" persistent):
+// The CONV instantiation fuses the layer's prologue into the step (the same
+// section has decode keep a convolution state alongside the recurrent one):
 // each of q, k, v is convolved with its W-1 previous raw inputs, held in a
 // per-sequence convolution state that the step shifts in place, and q, k are
 // L2-normalized.  The normalization is a scalar per vector, so it is applied

@@ -1,8 +1,9 @@
 // kda_prefill.hip -- chunkwise KDA prefill (gfx950).
 //
 // Method: the KDA recurrence and bounded decay gate of "Kimi K3 Open Weights:
-// What Is Actually New", section 1, processed "recurrent between, parallel
-// within" chunks (kimi-k3-course capstone, one-page map, SEQUENCE block).
+// What Is Actually New", section 1, with the state carried sequentially from
+// chunk to chunk and each chunk's tokens handled in parallel (kimi-k3-course
+// capstone, one-page map, SEQUENCE block).
 // The in-chunk algebra is the WY / UT form of the delta rule, derived from the
 // recurrence.  For a chunk of C tokens with entering state S, per key channel
 // cumulative log-decay G_r = sum_{s<=r} g_s (r = 0..C-1, chunk-relative):

@@ -3,8 +3,10 @@
 //
 // Same method and chunk algebra as kda_prefill.hip (the KDA recurrence and
 // bounded gate of "Kimi K3 Open Weights: What Is Actually New", section 1,
-// run "recurrent between, parallel within" 16-token chunks), organised for
-// overlap instead of lock-step phases:
+// with the state carried sequentially from chunk to chunk and the tokens
+// inside a 16-token chunk handled in parallel, as the kimi-k3-course
+// capstone's one-page map describes), organised for overlap instead of
+// lock-step phases:
 //
 //  * PREP waves (NPW per workgroup).  Prep wave w owns chunks w, w+NPW, ...
 //    and does the S-independent work of a chunk by itself, with no workgroup

@@ -15,8 +15,10 @@
  *       g_t = g_min * sigma(e^A * z_t),  alpha_t = e^{g_t},  g_min = -5
  *
  * S has dk key rows and dv value columns; alpha_t is a vector over the dk key
- * channels and scales S's rows ("fade (channel-wise alpha) -> erase (delta
- * rule) -> write", kimi-k3-course capstone, one-page map, SEQUENCE block).
+ * channels and scales S's rows.  Per token the state is first decayed channel
+ * by channel, then the old value stored along k is erased (the delta rule),
+ * then the new value is written (kimi-k3-course capstone, one-page map,
+ * SEQUENCE block).
  *
  * Readings where the page leaves a step open:
  *   - "sigma(e^A z_t)" is read as the logistic function of the product
