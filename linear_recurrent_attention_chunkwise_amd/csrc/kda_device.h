@@ -40,13 +40,29 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
 // Per-key-channel decay alpha = exp(g), g = g_min * sigma(e^A z), evaluated as
-// alpha = 2^(g_min log2(e) * s), s = 1 / (1 + 2^(c2 z)), c2 = -e^A log2(e).
-// For c2*z -> +inf: 2^inf = inf, 1/inf = 0, alpha = 1 exactly; for c2*z ->
-// -inf: s = 1, alpha = e^(g_min).  No NaN for any finite z.
+// alpha = 2^(K s), s = 1 / (1 + 2^(c2 z)), c2 = -e^A log2(e), K = g_min log2(e),
+// with the scale folded into the reciprocal: K s = 1 / (c + c 2^(c2 z)),
+// c = 1 / K (one fused multiply-add instead of an add and a multiply).
+// For c2*z -> +inf: 2^inf = inf, c + c inf = -inf, 1/-inf = -0, alpha = 1
+// exactly; for c2*z -> -inf: 1/c = K, alpha = e^(g_min).  No NaN for any
+// finite z.
 __device__ __forceinline__ float kda_alpha(float c2, float z) {
+    constexpr float c = 1.0f / (kGMin * kLog2e);
     const float e = __builtin_amdgcn_exp2f(c2 * z);
-    const float s = __builtin_amdgcn_rcpf(1.0f + e);
-    return __builtin_amdgcn_exp2f((kGMin * kLog2e) * s);
+    return __builtin_amdgcn_exp2f(__builtin_amdgcn_rcpf(__builtin_fmaf(e, c, c)));
+}
+
+// Two floats -> a packed pair of bf16 (round to nearest even), low half first:
+// one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
+}
+
+// Four floats -> four bf16 as two packed conversions.
+__device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
+    return __builtin_bit_cast(bf16x4, (uint64_t)pack_bf16x2(a, b) |
+                                          ((uint64_t)pack_bf16x2(c, d) << 32));
 }
 
 // ---------------------------------------------------------------- MFMA ----
@@ -97,7 +113,7 @@ template <typename TO>
 __device__ __forceinline__ Frag<TO> acc_frag(const f32x4 &d) {
     Frag<TO> f;
     if constexpr (sizeof(TO) == 2) {
-        f.v = bf16x4{(bf16)d[0], (bf16)d[1], (bf16)d[2], (bf16)d[3]};
+        f.v = to_bf16x4(d[0], d[1], d[2], d[3]);
     } else {
         f.v = d;
     }
@@ -116,8 +132,8 @@ template <typename TO>
 __device__ __forceinline__ Frag<TO> frag_scaled(const Frag<TO> &f, const f32x4 &s) {
     Frag<TO> r;
     if constexpr (sizeof(TO) == 2) {
-        r.v = bf16x4{(bf16)((float)f.v[0] * s[0]), (bf16)((float)f.v[1] * s[1]),
-                     (bf16)((float)f.v[2] * s[2]), (bf16)((float)f.v[3] * s[3])};
+        r.v = to_bf16x4((float)f.v[0] * s[0], (float)f.v[1] * s[1], (float)f.v[2] * s[2],
+                        (float)f.v[3] * s[3]);
     } else {
         r.v = f.v * s;
     }

@@ -37,9 +37,9 @@
 // so P = tril(Q~ Kh^T), L = diag(beta) strict_tril(K~ Kh^T).  Over at most 15
 // later tokens of a chunk, 1 <= e^{G - G_C} <= e^75 and e^{-75} <= e^{G_C - G}
 // <= 1, inside bf16 range: the range argument of the pages.  Referring to
-// the end (not the start) makes the factors of a chunk's last token exactly
-// 1, so the diagonal entry q.k of P, which can cancel, is formed from the
-// unrounded inputs for that token (a one-token sequence is exact there).
+// the end (not the start) makes the factors of a chunk's last token 1 up to
+// fp32 rounding, so after rounding to bf16 the diagonal entry q.k of P, which
+// can cancel, is formed from the unscaled inputs for that token.
 //
 // The 16 x 16 inverse T = (I + L)^-1 uses L's nilpotency (L^16 = 0):
 //    T = (I - L)(I + L^2)(I + L^4)(I + L^8),
@@ -72,17 +72,25 @@ template <int NCW, int NPW, int NSLOT>
 struct P16Cfg {
     static constexpr int D = 128, C = 16;
     static constexpr int DVB = 16 * NCW;           // value columns per workgroup
-    static constexpr int DP = D + 8;               // [token][d] row stride
-    static constexpr int CP = C + 8;               // [token][token] row stride
-    static constexpr int KP = D + 16;              // Kh row stride (read by transposing reads:
-                                                   // 8 banks between rows, no collisions)
+    // Row strides, for LDS served as 32 four-byte banks to each group of 16
+    // lanes.  A fragment read (16 rows, one 8-byte piece each) is
+    // conflict-free when the stride is 2 mod 32 words (rows 2 banks apart).
+    // Tiles that are also read by transposing reads (4 rows x 4 pieces) use a
+    // stride of 8 mod 32 words and store 8-byte piece p of row r at piece
+    // p ^ ((r >> 2) & 3) (swz_piece): the transposing read's 4 rows then fall
+    // 8 banks apart with its 4 pieces in distinct banks, and the 16 rows of a
+    // fragment read spread over 4 row strides x 4 piece positions.
+    static constexpr int DP = D + 4;               // Q~ [token][d] row stride (66 words)
+    static constexpr int CP = C + 4;               // [token][token] row stride (10 words)
+    static constexpr int KP = D + 16;              // K~/-W~ and Kh row stride (72 words, swizzled)
     // slot: the chain operands of one chunk
     static constexpr int S_QG = 0;                         // Q~         [C][DP]
-    static constexpr int S_WN = S_QG + C * DP * 2;         // K~, then -W~ [C][DP]
-    static constexpr int S_KH = S_WN + C * DP * 2;         // Kh         [C][KP]
+    static constexpr int S_WN = S_QG + C * DP * 2;         // K~, then -W~ [C][KP], swizzled
+    static constexpr int S_KH = S_WN + C * KP * 2;         // Kh         [C][KP], swizzled
     static constexpr int S_P = S_KH + C * KP * 2;          // P          [C][CP]
     static constexpr int S_TB = S_P + C * CP * 2;          // T diag(b)  [C][CP]
-    static constexpr int S_GC = S_TB + C * CP * 2;         // e^{G_C}    [D] fp32
+    static constexpr int S_GC = S_TB + C * CP * 2;         // e^{G_C}    [D] fp32, permuted
+                                                           // (gc_word)
     static constexpr int VP = DVB + 16;                    // V row stride (transposing reads:
                                                            // the rows they touch in distinct banks)
     static constexpr int S_V = S_GC + D * 4;               // V, this workgroup's columns [C][VP]
@@ -92,15 +100,58 @@ struct P16Cfg {
     static constexpr int SCR = (W_BETA + C * 4 + 15) / 16 * 16;
     static constexpr int OFF_FLAGS = 0;                     // ready[8], done[NSLOT][NCW], poison
     static constexpr int OFF_DONE = 32;
-    static constexpr int OFF_POISON = 128;
-    static constexpr int OFF_SLOTS = 144;
+    static constexpr int OFF_POISON = OFF_DONE + NSLOT * NCW * 4;
+    static constexpr int OFF_SLOTS = (OFF_POISON + 4 + 15) / 16 * 16;
     static constexpr int OFF_SCR = OFF_SLOTS + NSLOT * SLOT;
     static constexpr int LDS_BYTES = OFF_SCR + NPW * SCR;
-    static_assert(NSLOT <= 8 && OFF_DONE + NSLOT * NCW * 4 <= OFF_POISON, "flag area");
+    static_assert(NSLOT <= 8, "ready[] holds 8 slots");
     static_assert(NCW + NPW <= 16, "workgroup size");
     static_assert(SLOT % 16 == 0 && SCR % 16 == 0, "alignment");
     static_assert(LDS_BYTES <= 150 * 1024, "LDS budget");
 };
+
+// Swizzled 8-byte piece of row r of a [token][d] tile with a row stride of 8
+// mod 32 words (see the row strides): piece p is stored at p ^ ((r >> 2) & 3).
+__device__ __forceinline__ int swz_piece(int r, int p) { return p ^ ((r >> 2) & 3); }
+
+// K16 fragment of a swizzled tile (row stride `ld` elements): rows lane % 16,
+// contraction indices k0 + 4 (lane / 16) + 0..3, k0 a multiple of 32.
+__device__ __forceinline__ Frag<bf16> frag_swz(const bf16 *tile, int ld, int k0, int lane) {
+    const int r = lane & 15;
+    Frag<bf16> f;
+    f.v = *reinterpret_cast<const bf16x4 *>(tile + r * ld + k0 + 4 * swz_piece(r, lane >> 4));
+    return f;
+}
+
+// Transposing read of a swizzled tile: the K16 fragment tile[4g + e][col0 + n]
+// of frag_rows_tr, col0 a multiple of 16.  The 4 rows 4g .. 4g + 3 a lane
+// group touches share (r >> 2) & 3 = g, so piece j % 4 of the group sits at
+// (j % 4) ^ g.
+__device__ __forceinline__ Frag<bf16> frag_rows_tr_swz(const bf16 *tile, int ld, int col0,
+                                                       int lane) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int g = lane >> 4, j = lane & 15;
+    const bf16 *a = tile + (4 * g + (j >> 2)) * ld + col0 + 4 * ((j & 3) ^ g);
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(a));
+    Frag<bf16> f;
+    f.v = __builtin_bit_cast(bf16x4, r);
+    return f;
+}
+
+// Word of the slot's e^{G_C} vector that holds key channel d.  A chain wave's
+// lane (g, n) needs e^{G_C} of rows 16 i + 4 g + e of its state tiles; lane
+// (g, n) reads the two words 32 g + 2 n, +1 (the 16 lanes of a group read 128
+// contiguous bytes), and row i, element e of the group is then in lane
+// 2 i + e / 2 of the group, word e % 2: broadcast within the 16-lane row.
+__device__ __forceinline__ int gc_word(int d) { return 32 * ((d >> 2) & 3) + 4 * (d >> 4) + (d & 3); }
+
+// Value of lane I of this lane's 16-lane row (DPP row broadcast).
+template <int I>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                              0x150 + I, 0xF, 0xF, true));
+}
 
 // Bounded LDS wait: true once *flag >= target (workgroup-scope acquire);
 // false after `limit` sleeps without it.  A wave that gives up raises the
@@ -122,11 +173,7 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 v = bf16x2{(bf16)a, (bf16)b};
-    return __builtin_bit_cast(uint32_t, v);
-}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) { return pack_bf16x2(a, b); }
 
 // 16 values -> one [.][token] row of 16 bf16 (two 16-byte stores).
 __device__ __forceinline__ void store_row16(bf16 *row, const float *x) {
@@ -211,71 +258,113 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         auto chunk_rows = [&](int64_t t0) { return (Tn - t0 < C ? Tn - t0 : (int64_t)C); };
         // per-lane byte offsets of the fragment reads, fixed over chunks; a
         // chunk adds its slot's (uniform) byte offset once per tile layout
-        const int offDP = ((lane & 15) * DP + 4 * (lane >> 4)) * 2;   // [.][DP] tiles
+        const int offDP = ((lane & 15) * DP + 4 * (lane >> 4)) * 2;   // Q~ tile
+        const int offKP = ((lane & 15) * Cfg::KP + 4 * swz_piece(lane & 15, lane >> 4)) * 2;
         const int offCP = ((lane & 15) * CP + 4 * (lane >> 4)) * 2;   // [.][CP] tiles
-        const int offG = 16 * g;                                       // e^{G_C}[4g..4g+3]
+        const int offG = 4 * (32 * g + 2 * n);                         // e^{G_C} pair (gc_word)
         auto frag_at = [](const char *p) {
             Frag<bf16> f;
             f.v = *reinterpret_cast<const bf16x4 *>(p);
             return f;
         };
-        // W, T diag(beta), Kh^T and V fragments of a chunk (read one chunk
-        // ahead; Kh^T and V by transposing reads of token-major tiles: V as
-        // V[t0 + 4g + e][jw + n], staged by the prep wave, zero past T)
+        // W, T diag(beta), Kh^T and V fragments and the decay e^{G_C} of a chunk
+        // (read one chunk ahead; Kh^T and V by transposing reads of token-major
+        // tiles: V as V[t0 + 4g + e][jw + n], staged by the prep wave, zero past T)
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
         Frag<bf16> Wf[NDT], Kf[NDT], Tf, Vn;
+        f32x2 gvn;
         bool waited_ok = true;   // every slot wait of this wave succeeded
         auto read_wtk = [&](int sl, int use) {
             waited_ok &= wait_at_least(&ready[sl], use + 1, spin, poison);
             const int off = Cfg::OFF_SLOTS + sl * Cfg::SLOT;
-            const char *pd = smem + off + offDP;
+            const char *pk = smem + off + offKP;
             const char *pc = smem + off + offCP;
+            gvn = *reinterpret_cast<const f32x2 *>(smem + off + Cfg::S_GC + offG);
 #pragma unroll
-            for (int i = 0; i < NDT; ++i) Wf[i] = frag_at(pd + Cfg::S_WN + 32 * i);
+            for (int i = 0; i < NDT; ++i) Wf[i] = frag_at(pk + Cfg::S_WN + 32 * i);
             Tf = frag_at(pc + Cfg::S_TB);
             const bf16 *kh = reinterpret_cast<const bf16 *>(smem + off + Cfg::S_KH);
 #pragma unroll
-            for (int i = 0; i < NDT; ++i) Kf[i] = frag_rows_tr(kh, Cfg::KP, 16 * i, lane);
+            for (int i = 0; i < NDT; ++i) Kf[i] = frag_rows_tr_swz(kh, Cfg::KP, 16 * i, lane);
             if constexpr (MODE != 2)
                 Vn = frag_rows_tr(reinterpret_cast<const bf16 *>(smem + off + Cfg::S_V), Cfg::VP,
                                   16 * wave, lane);
         };
-        if (nchunks > 0) read_wtk(0, 0);
-        int sl = 0, use = 0;   // slot and use of chunk m
+        // The output of chunk m, O = Q~ (e^{G_C} S) + P U, does not feed the
+        // state, so it is software-pipelined: its products are issued at the
+        // top of step m + 1, where they run on the matrix cores while that
+        // step's decay is applied to S, and it is stored after the state update
+        // of step m + 1.  Carried over: chunk m's S', U (bf16), Q~, P fragments.
+        const int64_t row_stride_el = tok_stride;           // elements between token rows
+        const bf16 *obase = prm.o + base + jw;              // token 0, this wave's columns
+        const int ovoff = 4 * g * (int)row_bytes + 2 * n;   // lane offset of element e = 0
+        Frag<bf16> Sp[NDT], Qp[NDT], Pp, Up;
+        f32x4 Oa, Ob;
+        auto out_issue = [&]() {
+            Oa = f32x4{0.f, 0.f, 0.f, 0.f};
+            Ob = f32x4{0.f, 0.f, 0.f, 0.f};
+            mma32(Oa, Qp[0], Qp[1], Sp[0], Sp[1]);
+            mma32(Ob, Qp[2], Qp[3], Sp[2], Sp[3]);
+            mma32(Oa, Qp[4], Qp[5], Sp[4], Sp[5]);
+            mma32(Ob, Qp[6], Qp[7], Sp[6], Sp[7]);
+            mma16(Oa, Pp, Up);
+        };
+        auto out_store = [&](int64_t t0) {
+            const f32x4 O = Oa + Ob;
+            const auto ors = make_rsrc(obase + t0 * row_stride_el, chunk_rows(t0) * row_bytes);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (bf16)O[e]), ors,
+                                                      ovoff, e * (int)row_bytes, 0);
+        };
+        // Loop bounds and the output pointer are wave-uniform: keep them in
+        // scalar registers (readfirstlane) so the per-chunk bookkeeping is SALU
+        // on constants, and run the chunks NSLOT at a time so that every slot
+        // offset is a compile-time constant.
+        const int nch = __builtin_amdgcn_readfirstlane((int)nchunks);
+        if (nch > 0) read_wtk(0, 0);
         // state checkpoints: the state after every ckpt_every tokens
         const int every = CKPT ? prm.ckpt_every : 0;   // CKPT: prm.ckpt set, every > 0
         int64_t ck_row = every > 0 ? ckpt_row0(prm.cu, b, prm.T, every) : 0;
         int64_t ck_next = every;   // token count of the next checkpoint
-        for (int64_t m = 0; m < nchunks; ++m) {
-            const int64_t t0 = m * C;
+        for (int m0 = 0, use = 0; m0 < nch; m0 += NSLOT, ++use) {
+#pragma unroll
+        for (int sl = 0; sl < NSLOT; ++sl) {
+            const int m = m0 + sl;
+            if (m >= nch) break;
+            const int64_t t0 = (int64_t)m * C;
             const int off = Cfg::OFF_SLOTS + sl * Cfg::SLOT;
-            int sl1 = sl + 1, use1 = use;
-            if (sl1 == NSLOT) { sl1 = 0; ++use1; }
-            // (1) chunk m's remaining operands: the decay e^{G_C} (applied to S
-            // first) and Q~, P (needed by the output only)
+            const int sl1 = sl + 1 == NSLOT ? 0 : sl + 1;
+            const int use1 = sl + 1 == NSLOT ? use + 1 : use;
             const char *pd = smem + off + offDP;
             const char *pc = smem + off + offCP;
-            const char *pg = smem + off + Cfg::S_GC + offG;
-            f32x4 gc[NDT];
-#pragma unroll
-            for (int i = 0; i < NDT; ++i) gc[i] = *reinterpret_cast<const f32x4 *>(pg + 64 * i);
+            const f32x2 gv = gvn;
             const Frag<bf16> Vf = Vn;
-            __builtin_amdgcn_sched_barrier(0);
-            // (2) S <- e^{G_C} S; U = T diag(beta) V - W~ S, where W~ = W e^{-G_C}
+            // (1) the previous chunk's output products (matrix cores), then
+            // S <- e^{G_C} S and U = T diag(beta) V - W~ S, W~ = W e^{-G_C}
             // (two accumulators halve the dependent chain)
+            if constexpr (MODE == 0)
+                if (m > 0) out_issue();
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 Ua = {0.f, 0.f, 0.f, 0.f}, Ub = {0.f, 0.f, 0.f, 0.f};
             if constexpr (MODE != 2) mma16(Ua, Tf, Vf);
             Frag<bf16> Sf[NDT];
-#pragma unroll
-            for (int i = 0; i < NDT; ++i) {
-                S[i] *= gc[i];
-                Sf[i] = acc_frag<bf16>(S[i]);
-            }
+            // S <- e^{G_C} S: row 16 i + 4 g + e scaled by lane 2 i + e/2's word e%2
+#define KDA_DECAY_TILE(i)                                                   \
+            S[i][0] *= row_bcast<2 * (i)>(gv[0]);                           \
+            S[i][1] *= row_bcast<2 * (i)>(gv[1]);                           \
+            S[i][2] *= row_bcast<2 * (i) + 1>(gv[0]);                       \
+            S[i][3] *= row_bcast<2 * (i) + 1>(gv[1]);                       \
+            Sf[i] = acc_frag<bf16>(S[i]);
+            KDA_DECAY_TILE(0) KDA_DECAY_TILE(1) KDA_DECAY_TILE(2) KDA_DECAY_TILE(3)
+            KDA_DECAY_TILE(4) KDA_DECAY_TILE(5) KDA_DECAY_TILE(6) KDA_DECAY_TILE(7)
+#undef KDA_DECAY_TILE
+            static_assert(NDT == 8, "decay broadcast covers 8 row tiles");
             mma32(Ub, Wf[0], Wf[1], Sf[0], Sf[1]);
             mma32(Ua, Wf[2], Wf[3], Sf[2], Sf[3]);
             mma32(Ub, Wf[4], Wf[5], Sf[4], Sf[5]);
             mma32(Ua, Wf[6], Wf[7], Sf[6], Sf[7]);
-            // Q~ and P are only needed for the output; reading them now keeps
-            // their registers free while W~ and e^{G_C} are live
+            // (2) this chunk's Q~ and P for its output (next step)
             compiler_fence();
             Frag<bf16> Qf[NDT], Pf;
             if constexpr (MODE == 0) {
@@ -331,28 +420,27 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
                 ck_next += every;
             }
             __builtin_amdgcn_sched_barrier(0);
-            // (4) chunk m+1's W, T diag(beta), Kh^T, read while O is formed
-            if (m + 1 < nchunks) read_wtk(sl1, use1);
-            // (5) O = Q~ (e^{G_C} S_old) + P U
+            // (4) the previous chunk's output, then chunk m+1's operands
+            if constexpr (MODE == 0)
+                if (m > 0) out_store(t0 - C);
+            if (m + 1 < nch) read_wtk(sl1, use1);
             if constexpr (MODE == 0) {
-                f32x4 Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
-                mma32(Oa, Qf[0], Qf[1], Sf[0], Sf[1]);
-                mma32(Ob, Qf[2], Qf[3], Sf[2], Sf[3]);
-                mma32(Oa, Qf[4], Qf[5], Sf[4], Sf[5]);
-                mma32(Ob, Qf[6], Qf[7], Sf[6], Sf[7]);
-                mma16(Oa, Pf, Uf);
-                const f32x4 O = Oa + Ob;
-                const auto ors =
-                    make_rsrc(prm.o + base + t0 * tok_stride + jw, chunk_rows(t0) * row_bytes);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, (bf16)O[e]),
-                                                          ors, (4 * g + e) * (int)row_bytes + 2 * n,
-                                                          0, 0);
+                for (int i = 0; i < NDT; ++i) {
+                    Sp[i] = Sf[i];
+                    Qp[i] = Qf[i];
+                }
+                Pp = Pf;
+                Up = Uf;
             }
-            sl = sl1;
-            use = use1;
         }
+        }
+        // the last chunk's output
+        if constexpr (MODE == 0)
+            if (nch > 0) {
+                out_issue();
+                out_store((int64_t)(nch - 1) * C);
+            }
         // A prep wave that gave up a wait may have overwritten a slot this
         // wave was still reading: its poison store precedes a release of
         // `ready` that this wave has acquired since.  Another chain wave's
@@ -466,26 +554,27 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
 #pragma unroll
         for (int s = C - 1; s >= 0; --s) {
             const float h0 = bf_lo(rk[s]) * R0, h1 = bf_hi(rk[s]) * R1;
-            *reinterpret_cast<uint32_t *>(sKh + s * Cfg::KP + d0) = pack_bf16(h0, h1);
+            *reinterpret_cast<uint32_t *>(sKh + s * Cfg::KP + 4 * swz_piece(s, lane >> 1) +
+                                          2 * (lane & 1)) = pack_bf16(h0, h1);
             R0 *= a0[s];
             R1 *= a1[s];
         }
-        sGC[d0] = R0;
-        sGC[d0 + 1] = R1;
+        *reinterpret_cast<float2 *>(sGC + gc_word(d0)) = float2{R0, R1};   // d0 even: adjacent words
         // Forward: e^{G - G_C} = e^{G} / e^{G_C} (in [1, e^75]): Q~ = Q e^{G-G_C},
-        // K~ = K e^{G-G_C}.  For the chunk's last token both factors are exactly 1.
+        // K~ = K e^{G-G_C}, as a running product started at 1 / e^{G_C}.  For
+        // the chunk's last token both factors are 1 up to a few fp32 ulps, so
+        // that token's bf16 operands are its unscaled inputs.
         {
-            const float ic0 = __builtin_amdgcn_rcpf(R0), ic1 = __builtin_amdgcn_rcpf(R1);
-            float F0 = 1.f, F1 = 1.f;
+            float f0 = __builtin_amdgcn_rcpf(R0), f1 = __builtin_amdgcn_rcpf(R1);
 #pragma unroll
             for (int s = 0; s < C; ++s) {
-                F0 *= a0[s];
-                F1 *= a1[s];
-                const float f0 = F0 * ic0, f1 = F1 * ic1;
+                f0 *= a0[s];
+                f1 *= a1[s];
                 if constexpr (MODE == 0)   // Q~ feeds the output only
                     *reinterpret_cast<uint32_t *>(sQG + s * DP + d0) =
                         pack_bf16(bf_lo(rq[s]) * f0, bf_hi(rq[s]) * f1);
-                *reinterpret_cast<uint32_t *>(sWn + s * DP + d0) =
+                *reinterpret_cast<uint32_t *>(sWn + s * Cfg::KP + 4 * swz_piece(s, lane >> 1) +
+                                              2 * (lane & 1)) =
                     pack_bf16(bf_lo(rk[s]) * f0, bf_hi(rk[s]) * f1);
             }
         }
@@ -502,8 +591,10 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
               accLT = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k32 = 0; k32 < D; k32 += 32) {
-            const Frag<bf16> c0 = lds_frag(sKh, Cfg::KP, k32, lane), c1 = lds_frag(sKh, Cfg::KP, k32 + 16, lane);
-            const Frag<bf16> h0f = lds_frag(sWn, DP, k32, lane), h1f = lds_frag(sWn, DP, k32 + 16, lane);
+            const Frag<bf16> c0 = frag_swz(sKh, Cfg::KP, k32, lane),
+                             c1 = frag_swz(sKh, Cfg::KP, k32 + 16, lane);
+            const Frag<bf16> h0f = frag_swz(sWn, Cfg::KP, k32, lane),
+                             h1f = frag_swz(sWn, Cfg::KP, k32 + 16, lane);
             if constexpr (MODE == 0) {
                 const Frag<bf16> q0f = lds_frag(sQG, DP, k32, lane),
                                  q1f = lds_frag(sQG, DP, k32 + 16, lane);
@@ -516,17 +607,17 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         const float bcol = sBeta[n];                                            // beta_n
         f32x4 Lb, LTb, ImLT;   // L, L^T (B layout); I - L^T
         {
-            typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
-            bf16x4v pw4;
+            f32x4 pm;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g + e;
-                pw4[e] = (bf16)(r <= n ? accP[e] : 0.0f);          // P[n][4g+e]
+                pm[e] = r <= n ? accP[e] : 0.0f;                    // P[n][4g+e]
                 Lb[e] = n < r ? brow[e] * accL[e] : 0.0f;           // L[4g+e][n]
                 LTb[e] = r < n ? bcol * accLT[e] : 0.0f;            // L[n][4g+e]
                 ImLT[e] = (r == n ? 1.0f : 0.0f) - LTb[e];
             }
-            if constexpr (MODE == 0) *reinterpret_cast<bf16x4v *>(sP + n * CP + 4 * g) = pw4;
+            if constexpr (MODE == 0)
+                *reinterpret_cast<bf16x4 *>(sP + n * CP + 4 * g) = to_bf16x4(pm[0], pm[1], pm[2], pm[3]);
         }
         // ---- T^T = Y^T X^T with X = (I-L)(I+L^2), Y = (I+L^4)(I+L^8) ----------
         // B-layout inputs: M (B) and M^T (= A-layout of M).
@@ -552,8 +643,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         const f32x4 TT = mm(bf(Y), bf(XT));                              // T^T = Y^T X^T
         // T^T in B layout = T in A layout: lane (g,n) holds T[n][4g+e]
         Frag<bf16> Tf;   // A-layout of Tb = T diag(beta): T[n][4g+e] beta_{4g+e}
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Tf.v[e] = (bf16)(TT[e] * brow[e]);
+        Tf.v = to_bf16x4(TT[0] * brow[0], TT[1] * brow[1], TT[2] * brow[2], TT[3] * brow[3]);
         *reinterpret_cast<bf16x4 *>(sTb + n * CP + 4 * g) = Tf.v;
 
         // ---- W~^T = K~^T Tb^T, written as -W~ rows over K~ -------------------
@@ -562,12 +652,12 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         // before its W rows overwrite the same columns.
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const Frag<bf16> ka = frag_rows_tr(sWn, DP, 16 * dt, lane);
+            const Frag<bf16> ka = frag_rows_tr_swz(sWn, Cfg::KP, 16 * dt, lane);
             f32x4 w = {0.f, 0.f, 0.f, 0.f};
             mma16(w, ka, Tf);
             // w[e] = W[n][16 dt + 4 g + e]
-            *reinterpret_cast<bf16x4 *>(sWn + n * DP + 16 * dt + 4 * g) =
-                bf16x4{(bf16)(-w[0]), (bf16)(-w[1]), (bf16)(-w[2]), (bf16)(-w[3])};
+            *reinterpret_cast<bf16x4 *>(sWn + n * Cfg::KP + 16 * dt + 4 * swz_piece(n, g)) =
+                to_bf16x4(-w[0], -w[1], -w[2], -w[3]);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __hip_atomic_store(&ready[s_], use + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -610,11 +700,11 @@ hipError_t launch_prefill16(const PrefillArgs &a) {
     const bool ck = a.ckpt != nullptr && a.ckpt_every > 0;
     if (a.mode != 0) {   // states only: 64 columns; checkpoints in MODE 1 only
         if (a.dv_per_block != 64 || (ck && a.mode != 1)) return hipErrorInvalidValue;
-        if (a.mode == 1) return ck ? launch_p16<4, 8, 6, true, 1>(a) : launch_p16<4, 8, 6, false, 1>(a);
-        return launch_p16<4, 8, 6, false, 2>(a);
+        if (a.mode == 1) return ck ? launch_p16<4, 8, 8, true, 1>(a) : launch_p16<4, 8, 8, false, 1>(a);
+        return launch_p16<4, 8, 8, false, 2>(a);
     }
     if (a.dv_per_block == 64)
-        return ck ? launch_p16<4, 8, 6, true>(a) : launch_p16<4, 8, 6, false>(a);
+        return ck ? launch_p16<4, 8, 8, true>(a) : launch_p16<4, 8, 8, false>(a);
     if (a.dv_per_block == 32)
         return ck ? launch_p16<2, 6, 6, true>(a) : launch_p16<2, 6, 6, false>(a);
     return hipErrorInvalidValue;
