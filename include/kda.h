@@ -170,9 +170,7 @@ kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk
  *        Its contents are scratch; calls sharing a workspace must not overlap.
  * All other conventions (dtype, sizes, alignment, aliasing, errors, the
  * dv_per_block split) are those of kda_prefill_ex; each sequence's result is
- * that of kda_prefill on the sequence alone.  Exception: with checkpoints,
- * bf16 with dk = 128 and chunk 64 runs 32 value columns per workgroup (0
- * picks it; 64 returns KDA_ERR_UNSUPPORTED).
+ * that of kda_prefill on the sequence alone.
  */
 kda_status kda_prefill_varlen(int dtype, int64_t N, int64_t T_total, int64_t H,
                               int64_t dk, int64_t dv, int32_t chunk,

@@ -570,11 +570,18 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
             Frag<T> Sf[NDT];
 #pragma unroll
             for (int i = 0; i < NDT; ++i) Sf[i] = acc_frag<T>(S[i]);
+            // A product of one MFMA shape never accumulates directly onto the
+            // result of the other shape: a 16x16x16 product issued shortly
+            // after a 16x16x32 product writing its accumulator returned wrong
+            // values on MI355X (the compiler inserts no wait states between
+            // the two shapes), so mixed-shape sums go through separate
+            // accumulators and a VALU add.
             f32x4 U[NP], O[NP];
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                U[p] = Ut[p];   // U = U~ - W S  (sWn holds -W)
+                U[p] = f32x4{0.f, 0.f, 0.f, 0.f};   // U = U~ - W S  (sWn holds -W)
                 contract_lds_frag<T, D>(U[p], sWn + 16 * p * DP, DP, Sf, lane);
+                U[p] += Ut[p];
             }
             Frag<T> Uf[NP];
 #pragma unroll
@@ -583,9 +590,11 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
             for (int p = 0; p < NP; ++p) {
                 O[p] = f32x4{0.f, 0.f, 0.f, 0.f};
                 contract_lds_frag<T, D>(O[p], sQG + 16 * p * DP, DP, Sf, lane);
+                f32x4 Opu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j <= p; ++j)
-                    mma16(O[p], lds_frag(sP + 16 * p * CP, CP, 16 * j, lane), Uf[j]);
+                    mma16(Opu, lds_frag(sP + 16 * p * CP, CP, 16 * j, lane), Uf[j]);
+                O[p] += Opu;
             }
             // S <- e^{G_C} * S + Kh^T U
 #pragma unroll
@@ -662,13 +671,9 @@ __global__ __launch_bounds__(256) void kda_seq_order_kernel(const int64_t *cu, i
 
 // ---------------------------------------------------------------- host ----
 
-template <typename T, int D, int C, int NW>
-constexpr bool ckpt_variant_supported() {
-    return !(sizeof(T) == 2 && D == 128 && C == 64 && NW == 4);
-}
-
 bool prefill_ckpt_supported(int dtype, int64_t D, int chunk, int dv_per_block) {
-    return !(dtype == 1 && D == 128 && chunk == 64 && dv_per_block == 64);
+    (void)dtype; (void)D; (void)chunk; (void)dv_per_block;
+    return true;
 }
 
 template <typename T, int D, int C, int NW>
@@ -681,17 +686,10 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
     prm.ckpt_every = a.ckpt_every;
     prm.nsplit = (int)(D / (16 * NW));
     const int64_t nblk = a.B * a.H * prm.nsplit;
-    if (a.ckpt != nullptr && a.ckpt_every > 0) {
-        // The checkpointing build of the 64-token, 64-column bf16 variant
-        // (4 waves, at the register-file limit) produced wrong outputs on
-        // MI355X while its checkpoints and final state were right; it is not
-        // built, and the entry points refuse that combination.
-        if constexpr (ckpt_variant_supported<T, D, C, NW>())
-            hipLaunchKernelGGL((kda_prefill_kernel<T, D, C, NW, true>), dim3((unsigned)nblk),
-                               dim3(64 * NW), 0, a.stream, prm);
-        else
-            return hipErrorInvalidValue;
-    } else
+    if (a.ckpt != nullptr && a.ckpt_every > 0)
+        hipLaunchKernelGGL((kda_prefill_kernel<T, D, C, NW, true>), dim3((unsigned)nblk),
+                           dim3(64 * NW), 0, a.stream, prm);
+    else
         hipLaunchKernelGGL((kda_prefill_kernel<T, D, C, NW, false>), dim3((unsigned)nblk),
                            dim3(64 * NW), 0, a.stream, prm);
     return hipGetLastError();

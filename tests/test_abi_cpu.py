@@ -167,8 +167,6 @@ def test_varlen_argument_errors(lib):
     assert varlen(lib, ptrs={"ws": None}) == WORKSPACE
     assert varlen(lib, ptrs={"ws": P(11, 8)}) == MISALIGNED
     assert varlen(lib, ptrs={"ws": P(7, 16)}) == ALIAS       # workspace over the outputs
-    # checkpoints at 64-token chunks: not with 64 value columns per workgroup
-    assert varlen(lib, chunk=64, every=64, n_ckpt=4, dvb=64) == UNSUP
 
 
 def test_varlen_empty_work_launches_nothing(lib):
