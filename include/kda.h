@@ -220,9 +220,11 @@ kda_status kda_prefill_varlen_noalloc(int dtype, int64_t N, int64_t T_total, int
  * alone cannot (a head share of a long context: e.g. H = 16, T = 2^20).  Each
  * sequence is cut into `segments` pieces of L = ceil(T / segments) tokens
  * rounded up to a whole chunk (trailing pieces may be empty); the call runs
- * (1) every piece's M and N, (2) the pieces' start states by the scan
- * S_{j+1} = M_j S_j + N_j in fp32, (3) every piece from its start state.  It
- * costs about three prefills of work spread over B*H*segments units.
+ * (1) M and N of every piece but the last of its sequence, in one pass that
+ * shares the per-chunk preparation between them, (2) the pieces' start states
+ * by the scan S_{j+1} = M_j S_j + N_j in fp32, (3) every piece from its start
+ * state.  It costs about two prefills of work spread over B*H*segments
+ * units.
  *
  * Arguments and results as kda_prefill (o, S_T identical in meaning; S_T may
  * be S0).  Supported: bf16, dk = dv = 128, chunk 16, 1 <= segments <= 1024

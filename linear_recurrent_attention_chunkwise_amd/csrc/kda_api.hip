@@ -131,8 +131,8 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
         return KDA_ERR_UNSUPPORTED;
     if (want_ckpt && !role_split && !kda::prefill_ckpt_supported(dtype, D, chunk, dvb))
         return KDA_ERR_UNSUPPORTED;
-    // modes 1 and 2 write states only (o is neither read nor written)
-    if (mode != 0 && (!role_split || dvb != 64 || (want_ckpt && mode != 1)))
+    // mode 1 writes final states only (o is neither read nor written)
+    if (mode != 0 && (mode != 1 || !role_split || dvb != 64))
         return KDA_ERR_UNSUPPORTED;
     if (ckpt_blocked && want_ckpt && !role_split) return KDA_ERR_UNSUPPORTED;
     if (!A || !S_T) return KDA_ERR_NULL;
@@ -652,7 +652,7 @@ int64_t split_len(int64_t T, int P, int chunk) {
 }
 
 struct SplitLayout {
-    size_t cu, order, M, N, S, total;   // byte offsets into the workspace, and its size
+    size_t cu, first, M, N, S, total;   // byte offsets into the workspace, and its size
 };
 
 bool split_layout(int64_t B, int64_t H, int64_t D, int P, SplitLayout *lay) {
@@ -661,12 +661,33 @@ bool split_layout(int64_t B, int64_t H, int64_t D, int P, SplitLayout *lay) {
         !mul_ok(nh, D * D, kMaxElems / 16, &ne))
         return false;
     lay->cu = 0;
-    lay->order = round256((n + 1) * 8);
-    lay->M = lay->order + round256((int64_t)order_bytes(n));
+    lay->first = round256((n + 1) * 8);
+    lay->M = lay->first + round256(n * 4);
     lay->N = lay->M + round256(ne * 4);
     lay->S = lay->N + round256(ne * 4);
     lay->total = lay->S + round256(ne * 4);
     return true;
+}
+
+// One pass of the role-split prefill over the segments of a split call (whose
+// arguments were validated on entry): `nseq` segments of the packing `cu`,
+// rank r running segment order[r] (or r).
+kda_status split_pass(int64_t nseq, int64_t Ttot, int64_t H, const int64_t *cu,
+                      const int32_t *order, const void *q, const void *k, const void *v,
+                      const void *z, const void *beta, const float *A, const float *S0, void *o,
+                      float *S_T, float *S_T2, int mode, hipStream_t stream) {
+    if (nseq * H == 0) return KDA_OK;
+    kda::PrefillArgs a;
+    a.dtype = KDA_BF16; a.B = nseq; a.T = Ttot; a.H = H; a.D = 128; a.chunk = 16;
+    a.dv_per_block = 64;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.A = A; a.S0 = S0;
+    a.o = o; a.S_T = S_T; a.S_T2 = S_T2;
+    a.cu_seqlens = cu;
+    a.order = order;
+    a.ckpt_every = 0; a.ckpt = nullptr; a.n_ckpt = 0;
+    a.mode = mode;
+    a.stream = stream;
+    return kda::launch_prefill16(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // namespace
@@ -702,8 +723,10 @@ kda_status kda_prefill_split(int dtype, int64_t B, int64_t T, int64_t H, int64_t
                             S_T, 0, nullptr, 0, nullptr, 0, stream, 64);
     SplitLayout lay;
     if (!split_layout(B, H, dk, P, &lay)) return KDA_ERR_SHAPE;
+    // segments; the passes' grids hold at most 4096 work-items per (segment,
+    // head) unit, and a dispatch counts work-items in 32 bits
     int64_t nseg;
-    if (!mul_ok(B, P, 0x7fffffff / 8 / (H > 0 ? H : 1), &nseg)) return KDA_ERR_SHAPE;
+    if (!mul_ok(B, P, (int64_t)(0xffffffffu / 4096) / (H > 0 ? H : 1), &nseg)) return KDA_ERR_SHAPE;
     if (!workspace || workspace_bytes < lay.total) return KDA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;
     {
@@ -720,29 +743,24 @@ kda_status kda_prefill_split(int dtype, int64_t B, int64_t T, int64_t H, int64_t
     if (B * H == 0) return KDA_OK;
     char *ws = static_cast<char *>(workspace);
     int64_t *cu = reinterpret_cast<int64_t *>(ws + lay.cu);
-    void *order = ws + lay.order;
-    const size_t order_sz = order_bytes(nseg);
+    int32_t *first = reinterpret_cast<int32_t *>(ws + lay.first);
     float *Mb = reinterpret_cast<float *>(ws + lay.M);
     float *Nb = reinterpret_cast<float *>(ws + lay.N);
     float *Sb = reinterpret_cast<float *>(ws + lay.S);
     const hipStream_t s = (hipStream_t)stream;
     const int64_t L = split_len(T, P, chunk);
     const int64_t Ttot = B * T;   // [B, T, H, d] read as the packing [B*T, H, d]
-    if (kda::launch_split_setup(cu, Mb, B, T, L, P, H, (int)dk, s) != hipSuccess)
-        return KDA_ERR_HIP;
-    // (1) transitions M (from S0 = I, v as zero) and offsets N (from S0 = 0)
-    st = prefill_impl(dtype, nseg, Ttot, H, dk, dv, chunk, cu, q, k, v, z, beta, A, Mb, o, Mb, 0,
-                      nullptr, 0, order, order_sz, stream, 64, 2);
-    if (st != KDA_OK) return st;
-    st = prefill_impl(dtype, nseg, Ttot, H, dk, dv, chunk, cu, q, k, v, z, beta, A, nullptr, o,
-                      Nb, 0, nullptr, 0, order, order_sz, stream, 64, 1);
+    if (kda::launch_split_setup(cu, first, B, T, L, P, s) != hipSuccess) return KDA_ERR_HIP;
+    // (1) maps M (from I, v as zero) and offsets N (from 0) of every segment
+    // but the last of each sequence, in one pass
+    st = split_pass(B * (P - 1), Ttot, H, cu, first, q, k, v, z, beta, A, nullptr, nullptr, Mb,
+                    Nb, 2, s);
     if (st != KDA_OK) return st;
     // (2) start state of every segment
     if (kda::launch_split_scan(S0, Mb, Nb, Sb, B, H, P, (int)dk, s) != hipSuccess)
         return KDA_ERR_HIP;
     // (3) every segment from its start state; its final states go to Mb
-    st = prefill_impl(dtype, nseg, Ttot, H, dk, dv, chunk, cu, q, k, v, z, beta, A, Sb, o, Mb, 0,
-                      nullptr, 0, order, order_sz, stream, 64, 0);
+    st = split_pass(nseg, Ttot, H, cu, nullptr, q, k, v, z, beta, A, Sb, o, Mb, nullptr, 0, s);
     if (st != KDA_OK) return st;
     return kda::launch_split_gather(Mb, S_T, B, H, P, (int)dk, s) == hipSuccess ? KDA_OK
                                                                                 : KDA_ERR_HIP;

@@ -20,6 +20,7 @@ struct PrefillArgs {
     const float *A, *S0;
     void *o;
     float *S_T;
+    float *S_T2 = nullptr;   // mode 2: the offsets N
     // Packed variable-length mode: sequence b holds tokens
     // [cu_seqlens[b], cu_seqlens[b+1]) of a [T, H, d] packing (T = total
     // tokens).  NULL: dense [B, T, H, d].
@@ -36,9 +37,11 @@ struct PrefillArgs {
     // blocks, state element (d, j) at ((d/4)*D + j)*4 + d%4 (the backward's own
     // rerun; role-split kernel only).
     bool ckpt_blocked = false;
-    // 0: the prefill.  1: final states only (o not written).  2: the state
-    // transition of each sequence (v read as zero, o not written).  Modes 1
-    // and 2 exist for the role-split kernel at 64 columns without checkpoints.
+    // 0: the prefill.  1: final states only (o not written).  2: the affine
+    // state map S_end = M S_start + N of each sequence in one pass (M to S_T,
+    // N -- the final state from S0, or zero -- to S_T2; o not written).  Modes
+    // 1 and 2 exist for the role-split kernel at 64 columns (checkpoints in
+    // mode 1 only).
     int mode = 0;
     hipStream_t stream;
 };
@@ -107,10 +110,11 @@ constexpr int64_t kMaxOrderSeqs = 8192;
 hipError_t launch_seq_order(const int64_t *cu, int64_t N, int64_t T, int32_t *order,
                             hipStream_t stream);
 
-// Sequence split (kda_split.hip): segment offsets + identity start states,
-// the scan of segment start states, the gather of the final states.
-hipError_t launch_split_setup(int64_t *cu, float *eye, int64_t B, int64_t T, int64_t L, int P,
-                              int64_t H, int D, hipStream_t stream);
+// Sequence split (kda_split.hip): segment offsets and the list of segments
+// that are not the last of their sequence (P >= 2), the scan of segment start
+// states, the gather of the final states.
+hipError_t launch_split_setup(int64_t *cu, int32_t *first, int64_t B, int64_t T, int64_t L,
+                              int P, hipStream_t stream);
 hipError_t launch_split_scan(const float *S0, const float *M, const float *N, float *Sstart,
                              int64_t B, int64_t H, int P, int D, hipStream_t stream);
 hipError_t launch_split_gather(const float *Sseg, float *S_T, int64_t B, int64_t H, int P, int D,

@@ -57,6 +57,7 @@ struct Prefill16Params {
     const float *A, *S0;
     bf16 *o;
     float *S_T;
+    float *S_T2;         // MODE 2: final states of the value-carrying columns (N)
     int64_t T, H;   // T: tokens per sequence (dense) or in the packing (cu != NULL)
     int nsplit;
     const int64_t *cu;   // packed sequence offsets, or NULL
@@ -201,11 +202,12 @@ __device__ __forceinline__ Frag<bf16> frag_rows_tr(const bf16 *tile, int ld, int
     return f;
 }
 
-// MODE 0: the prefill.  MODE 1: the final states only (no o).  MODE 2: the
-// segment's state transition -- V taken as zero and no o, so that run from
-// S0 = I (dv = dk columns) the final "state" is the matrix M with
-// S_end = M S_start + (the MODE 1 result from S_start = 0); used to split one
-// long sequence into segments that run in parallel.
+// MODE 0: the prefill.  MODE 1: the final states only (no o).  MODE 2: a
+// sequence's affine state map S_end = M S_start + N, for splitting one long
+// sequence into segments that run in parallel: no o, and each chain wave
+// carries two 16-column state slices on the same prep, columns jw.. of M
+// (started from the identity with V taken as zero; written to S_T) and of N
+// (the final state from S0, or from zero, with V; written to S_T2).
 template <int NCW, int NPW, int NSLOT, bool CKPT, int MODE>
 __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill16Params prm) {
     using Cfg = P16Cfg<NCW, NPW, NSLOT>;
@@ -243,16 +245,34 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
     if (wave < NCW) {
         // ============================ chain wave ============================
         const int jw = j0 + 16 * wave;
-        f32x4 S[NDT];
-        if (prm.S0) {
-            const float *s0 = prm.S0 + bh * (int64_t)(D * D);
+        // S: the state slice (MODE 2: of M, from the identity); S2: MODE 2's
+        // value-carrying slice (of N)
+        f32x4 S[NDT], S2[NDT];
+        // state element (16 i + 4 g + e, jw + n) of a [D][D] matrix: one lane
+        // offset, the row offsets as constants (no per-element addresses)
+        const int svoff = (4 * g * D + jw + n) * 4;
+        auto load_s0 = [&](f32x4 (&X)[NDT]) {
+            if (prm.S0) {
+                const auto srs = make_rsrc(prm.S0 + bh * (int64_t)(D * D), (int64_t)(D * D) * 4);
+#pragma unroll
+                for (int i = 0; i < NDT; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        X[i][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                            srs, svoff, (16 * i + e) * D * 4, 0));
+            } else {
+#pragma unroll
+                for (int i = 0; i < NDT; ++i) X[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        };
+        if constexpr (MODE == 2) {
 #pragma unroll
             for (int i = 0; i < NDT; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) S[i][e] = s0[(16 * i + 4 * g + e) * D + jw + n];
+                for (int e = 0; e < 4; ++e) S[i][e] = 16 * i + 4 * g + e == jw + n ? 1.f : 0.f;
+            load_s0(S2);
         } else {
-#pragma unroll
-            for (int i = 0; i < NDT; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            load_s0(S);
         }
         const int64_t row_bytes = tok_stride * 2;
         auto chunk_rows = [&](int64_t t0) { return (Tn - t0 < C ? Tn - t0 : (int64_t)C); };
@@ -286,9 +306,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             const bf16 *kh = reinterpret_cast<const bf16 *>(smem + off + Cfg::S_KH);
 #pragma unroll
             for (int i = 0; i < NDT; ++i) Kf[i] = frag_rows_tr_swz(kh, Cfg::KP, 16 * i, lane);
-            if constexpr (MODE != 2)
-                Vn = frag_rows_tr(reinterpret_cast<const bf16 *>(smem + off + Cfg::S_V), Cfg::VP,
-                                  16 * wave, lane);
+            Vn = frag_rows_tr(reinterpret_cast<const bf16 *>(smem + off + Cfg::S_V), Cfg::VP,
+                              16 * wave, lane);
         };
         // The output of chunk m, O = Q~ (e^{G_C} S) + P U, does not feed the
         // state, so it is software-pipelined: its products are issued at the
@@ -342,28 +361,46 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             const Frag<bf16> Vf = Vn;
             // (1) the previous chunk's output products (matrix cores), then
             // S <- e^{G_C} S and U = T diag(beta) V - W~ S, W~ = W e^{-G_C}
-            // (two accumulators halve the dependent chain)
+            // (two accumulators halve the dependent chain; T diag(beta) V, a
+            // product of the other MFMA shape, has its own accumulator: no
+            // MFMA takes the fresh result of an MFMA of another shape as its
+            // accumulator, which MI355X does not order)
             if constexpr (MODE == 0)
                 if (m > 0) out_issue();
             __builtin_amdgcn_sched_barrier(0);
-            f32x4 Ua = {0.f, 0.f, 0.f, 0.f}, Ub = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (MODE != 2) mma16(Ua, Tf, Vf);
-            Frag<bf16> Sf[NDT];
-            // S <- e^{G_C} S: row 16 i + 4 g + e scaled by lane 2 i + e/2's word e%2
-#define KDA_DECAY_TILE(i)                                                   \
-            S[i][0] *= row_bcast<2 * (i)>(gv[0]);                           \
-            S[i][1] *= row_bcast<2 * (i)>(gv[1]);                           \
-            S[i][2] *= row_bcast<2 * (i) + 1>(gv[0]);                       \
-            S[i][3] *= row_bcast<2 * (i) + 1>(gv[1]);                       \
-            Sf[i] = acc_frag<bf16>(S[i]);
-            KDA_DECAY_TILE(0) KDA_DECAY_TILE(1) KDA_DECAY_TILE(2) KDA_DECAY_TILE(3)
-            KDA_DECAY_TILE(4) KDA_DECAY_TILE(5) KDA_DECAY_TILE(6) KDA_DECAY_TILE(7)
-#undef KDA_DECAY_TILE
+            f32x4 Ua = {0.f, 0.f, 0.f, 0.f}, Ub = {0.f, 0.f, 0.f, 0.f},
+                  Uv = {0.f, 0.f, 0.f, 0.f};
+            mma16(Uv, Tf, Vf);
+            Frag<bf16> Sf[NDT], Sf2[NDT];
+            // X <- e^{G_C} X: row 16 i + 4 g + e scaled by lane 2 i + e/2's word e%2
+#define KDA_DECAY_TILE(X, Xf, i)                                            \
+            X[i][0] *= row_bcast<2 * (i)>(gv[0]);                           \
+            X[i][1] *= row_bcast<2 * (i)>(gv[1]);                           \
+            X[i][2] *= row_bcast<2 * (i) + 1>(gv[0]);                       \
+            X[i][3] *= row_bcast<2 * (i) + 1>(gv[1]);                       \
+            Xf[i] = acc_frag<bf16>(X[i]);
+#define KDA_DECAY(X, Xf)                                                    \
+            KDA_DECAY_TILE(X, Xf, 0) KDA_DECAY_TILE(X, Xf, 1)               \
+            KDA_DECAY_TILE(X, Xf, 2) KDA_DECAY_TILE(X, Xf, 3)               \
+            KDA_DECAY_TILE(X, Xf, 4) KDA_DECAY_TILE(X, Xf, 5)               \
+            KDA_DECAY_TILE(X, Xf, 6) KDA_DECAY_TILE(X, Xf, 7)
             static_assert(NDT == 8, "decay broadcast covers 8 row tiles");
+            KDA_DECAY(S, Sf)
             mma32(Ub, Wf[0], Wf[1], Sf[0], Sf[1]);
             mma32(Ua, Wf[2], Wf[3], Sf[2], Sf[3]);
             mma32(Ub, Wf[4], Wf[5], Sf[4], Sf[5]);
             mma32(Ua, Wf[6], Wf[7], Sf[6], Sf[7]);
+            // MODE 2: the value-carrying slice, U2 = T diag(beta) V - W~ S2'
+            f32x4 U2a = {0.f, 0.f, 0.f, 0.f}, U2b = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (MODE == 2) {
+                KDA_DECAY(S2, Sf2)
+                mma32(U2b, Wf[0], Wf[1], Sf2[0], Sf2[1]);
+                mma32(U2a, Wf[2], Wf[3], Sf2[2], Sf2[3]);
+                mma32(U2b, Wf[4], Wf[5], Sf2[4], Sf2[5]);
+                mma32(U2a, Wf[6], Wf[7], Sf2[6], Sf2[7]);
+            }
+#undef KDA_DECAY
+#undef KDA_DECAY_TILE
             // (2) this chunk's Q~ and P for its output (next step)
             compiler_fence();
             Frag<bf16> Qf[NDT], Pf;
@@ -380,15 +417,21 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             __hip_atomic_store(&done[sl * NCW + wave], use + 1, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
             compiler_fence();
-            Frag<bf16> Uf;
-            {
-                const uint32_t lo = pack_bf16(Ua[0] + Ub[0], Ua[1] + Ub[1]);
-                const uint32_t hi = pack_bf16(Ua[2] + Ub[2], Ua[3] + Ub[3]);
-                Uf.v = __builtin_bit_cast(bf16x4, (uint64_t)lo | ((uint64_t)hi << 32));
+            Frag<bf16> Uf, Uf2;
+            if constexpr (MODE == 2) {
+                const f32x4 U = Ua + Ub, U2 = (U2a + U2b) + Uv;
+                Uf.v = to_bf16x4(U[0], U[1], U[2], U[3]);
+                Uf2.v = to_bf16x4(U2[0], U2[1], U2[2], U2[3]);
+            } else {
+                const f32x4 U = (Ua + Ub) + Uv;
+                Uf.v = to_bf16x4(U[0], U[1], U[2], U[3]);
             }
             // (3) S <- S + Kh^T U
 #pragma unroll
             for (int i = 0; i < NDT; ++i) mma16(S[i], Kf[i], Uf);
+            if constexpr (MODE == 2)
+#pragma unroll
+                for (int i = 0; i < NDT; ++i) mma16(S2[i], Kf[i], Uf2);
             if (CKPT && t0 + C == ck_next) {
                 if (t0 + C <= Tn && ck_row < prm.n_ckpt) {
                     // one lane offset, row offsets as scalars: no per-store addresses
@@ -447,14 +490,21 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         // give-up corrupts only that wave's own columns.
         if (!waited_ok ||
             __hip_atomic_load(poison, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) {
+            const float nan = __builtin_nanf("");
 #pragma unroll
-            for (int i = 0; i < NDT; ++i) S[i] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+            for (int i = 0; i < NDT; ++i) S[i] = S2[i] = f32x4{nan, nan, nan, nan};
         }
-        float *st = prm.S_T + bh * (int64_t)(D * D);
+        auto store_state = [&](float *dst, const f32x4 (&X)[NDT]) {
+            const auto srs = make_rsrc(dst + bh * (int64_t)(D * D), (int64_t)(D * D) * 4);
 #pragma unroll
-        for (int i = 0; i < NDT; ++i)
+            for (int i = 0; i < NDT; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) st[(16 * i + 4 * g + e) * D + jw + n] = S[i][e];
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(X[i][e]), srs, svoff,
+                                                          (16 * i + e) * D * 4, 0);
+        };
+        store_state(prm.S_T, S);
+        if constexpr (MODE == 2) store_state(prm.S_T2, S2);
         return;
     }
 
@@ -482,7 +532,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         const auto rz_ = make_rsrc(prm.z + base + t0 * tok_stride, rows * row_bytes);
         const auto rb_ = make_rsrc(prm.beta + bbase + t0 * H, rows * H * 2);
         rb = __builtin_amdgcn_raw_buffer_load_b16(rb_, (lane & 15) * (int)H * 2, 0, 0);
-        if constexpr (MODE != 2) {
+        {
             const auto rv_ = make_rsrc(prm.v + base + t0 * tok_stride, rows * row_bytes);
 #pragma unroll
             for (int u = 0; u < VU; ++u) {
@@ -539,7 +589,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
 #pragma unroll
         for (int w = 0; w < NCW; ++w) wait_at_least(&done[s_ * NCW + w], use, spin, poison);
 
-        if constexpr (MODE != 2) {
+        {
             bf16 *sV = reinterpret_cast<bf16 *>(slot + Cfg::S_V);
 #pragma unroll
             for (int u = 0; u < VU; ++u)
@@ -676,6 +726,7 @@ static hipError_t launch_p16(const PrefillArgs &a) {
     prm.S0 = a.S0;
     prm.o = static_cast<bf16 *>(a.o);
     prm.S_T = a.S_T;
+    prm.S_T2 = a.S_T2;
     prm.T = a.T;
     prm.H = a.H;
     prm.nsplit = 128 / (16 * NCW);
@@ -699,7 +750,8 @@ bool prefill16_supported(int dtype, int64_t D, int chunk, int dv_per_block) {
 hipError_t launch_prefill16(const PrefillArgs &a) {
     const bool ck = a.ckpt != nullptr && a.ckpt_every > 0;
     if (a.mode != 0) {   // states only: 64 columns; checkpoints in MODE 1 only
-        if (a.dv_per_block != 64 || (ck && a.mode != 1)) return hipErrorInvalidValue;
+        if (a.dv_per_block != 64 || (ck && a.mode != 1) || (a.mode == 2 && !a.S_T2))
+            return hipErrorInvalidValue;
         if (a.mode == 1) return ck ? launch_p16<4, 8, 8, true, 1>(a) : launch_p16<4, 8, 8, false, 1>(a);
         return launch_p16<4, 8, 8, false, 2>(a);
     }

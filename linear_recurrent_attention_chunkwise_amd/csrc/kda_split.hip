@@ -3,18 +3,19 @@
 // The recurrence is affine in the state: over a segment, S_end = M S_start + N,
 // where N is the segment's final state from S_start = 0 and M (dk x dk) the
 // product of its per-token transitions (I - beta k k^T) Diag(alpha).  So a
-// sequence of T tokens can run as P segments at once: (1) every segment's M
-// (the prefill kernel's transition mode, from S0 = I with v read as zero) and
-// N (its state-only mode, from S0 = 0); (2) the segments' true start states
-// by the scan S_{j+1} = M_j S_j + N_j; (3) the prefill of every segment from
-// its start state (the packed-sequence path).  This is the sequence-parallel
+// sequence of T tokens can run as P segments at once: (1) M and N of every
+// segment but the last, in one pass of the prefill kernel's state-map mode
+// (M from the identity with v read as zero, N from zero, on shared prep);
+// (2) the segments' true start states by the scan S_{j+1} = M_j S_j + N_j;
+// (3) the prefill of every segment from its start state (the packed-sequence
+// path).  This is the sequence-parallel
 // combine of the sharding design, done inside one GPU: it turns B*H units of
 // sequential work into B*H*P when B*H is too small to fill the chip (a head
 // share of a million-token context has 16 heads for 256 compute units).
 //
-// This file holds the small kernels around the three prefill passes: the
-// segment offsets, the identity start states, the scan, and the gather of the
-// last segment's final state.
+// This file holds the small kernels around the two prefill passes: the
+// segment offsets and the list of segments of pass (1), the scan, and the
+// gather of the last segment's final state.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -22,29 +23,23 @@ namespace kda {
 
 // cu[i] for the B*P segments: sequence b, segment j covers tokens
 // [b*T + min(j*L, T), b*T + min((j+1)*L, T)) of the [B*T, H, d] packing.
-__global__ void kda_split_offsets_kernel(int64_t *cu, int64_t B, int64_t T, int64_t L, int P) {
+// first[r] for r < B*(P-1): the r-th segment that is not the last of its
+// sequence (the ranks of pass (1)).
+__global__ void kda_split_offsets_kernel(int64_t *cu, int32_t *first, int64_t B, int64_t T,
+                                         int64_t L, int P) {
     const int64_t n = B * P;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i <= n;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t b = i / P, j = i % P;
         const int64_t t = j * L < T ? j * L : T;
         cu[i] = i == n ? B * T : b * T + t;
-    }
-}
-
-// eye[u] = I (D x D, fp32) for every unit u < n.
-__global__ void kda_split_identity_kernel(float *eye, int64_t n, int D) {
-    const int64_t total = n * D * D;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = (i / D) % D, c = i % D;
-        eye[i] = r == c ? 1.0f : 0.0f;
+        if (i < B * (P - 1)) first[i] = (int32_t)((i / (P - 1)) * P + i % (P - 1));
     }
 }
 
 // Start states of the segments.  One workgroup per (b, h, 32-column slice):
 // S = S0[b, h][:, cols] (or 0); for j < P: Sstart[b*P + j, h][:, cols] = S,
-// S <- M_j S + N_j, in fp32.  S lives in LDS; thread t computes row t / 2,
+// then (j < P - 1) S <- M_j S + N_j, in fp32.  S lives in LDS; thread t computes row t / 2,
 // columns 16 (t % 2) .. +15 of the slice (D = 128, 256 threads).
 constexpr int kScanCols = 32;
 __global__ __launch_bounds__(256) void kda_split_scan_kernel(const float *__restrict__ S0,
@@ -74,6 +69,7 @@ __global__ __launch_bounds__(256) void kda_split_scan_kernel(const float *__rest
             const int r = i / NC, c = i % NC;
             Sstart[(u * D + r) * D + c0 + c] = sS[r][c];
         }
+        if (j == P - 1) break;   // the last segment's map is never formed
         // row r0 of M_j S + N_j, columns cq .. cq+15
         float acc[16];
         const float *Nr = N + (u * D + r0) * D + c0 + cq;
@@ -111,12 +107,11 @@ static unsigned grid_for(int64_t n, int threads) {
     return (unsigned)g;
 }
 
-hipError_t launch_split_setup(int64_t *cu, float *eye, int64_t B, int64_t T, int64_t L, int P,
-                              int64_t H, int D, hipStream_t stream) {
+hipError_t launch_split_setup(int64_t *cu, int32_t *first, int64_t B, int64_t T, int64_t L,
+                              int P, hipStream_t stream) {
+    if (P < 2) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kda_split_offsets_kernel, dim3(grid_for(B * P + 1, 256)), dim3(256), 0,
-                       stream, cu, B, T, L, P);
-    hipLaunchKernelGGL(kda_split_identity_kernel, dim3(grid_for(B * P * H * D * D, 256)),
-                       dim3(256), 0, stream, eye, B * P * H, D);
+                       stream, cu, first, B, T, L, P);
     return hipGetLastError();
 }
 
