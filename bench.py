@@ -32,9 +32,10 @@ each, inputs drawn on the device; the million-token head share also split
 into 4 and 8 segments (kda_prefill_split).  ``timing`` gives the median and minimum
 per-launch time of 10 equal segments of the timed steps.
 
-``backward`` times kda_prefill_bwd on the same workload: gradients of q, k,
-v, z, beta, A and S0 from seeded dL/do and dL/dS_T (the forward is rerun with
-16-token state checkpoints inside the call).
+``backward`` times kda_prefill_bwd_ex on the same workload: gradients of q,
+k, v, z, beta, A and S0 from seeded dL/do and dL/dS_T (the forward is rerun
+with 16-token state checkpoints inside the call, beside the backward's prep on
+a second stream of the caller's).
 
 ``prologue`` times the layer's prologue on raw inputs of the same shapes
 (short convolutions of width 4, SiLU, q/k L2 norm, continued sequences): the
@@ -49,8 +50,11 @@ WRITE_SIZE) is scaled by when the kernels' HBM traffic is measured.
 kernel's summary under profiles/, reported only while the kernel source still
 hashes to the one the counters were taken on (null otherwise).
 
-The default warm-up (several seconds of back-to-back launches) lets the GPU's
-clocks settle before the timed region.
+Order: the other sections run first and the headline prefill is timed last,
+so that its W warm-up and K timed steps run on a GPU that has been under load
+for several seconds (its working clocks), whatever W is; on a GPU fresh out of
+idle the same kernel reads ~25% slower for its first few hundred launches.
+The oracle baseline runs after every GPU timing.
 """
 from __future__ import annotations
 
@@ -434,6 +438,108 @@ def main(argv=None):
     w = WORKLOADS["k3_prefill_bf16"].with_(chunk=args.chunk)
     inp_cpu = make_prefill_inputs(w)
     inp = {k: (v.to(dev) if v is not None else None) for k, v in inp_cpu.items()}
+    sections = {}
+    if not args.no_decode:
+        wd = WORKLOADS["k3_decode_bf16"]
+        dinp = make_decode_inputs(wd, device=dev)
+        dms = time_decode(torch, kda, dinp, args.decode_reps)
+        dbytes = decode_bytes(wd.B, wd.H, wd.dk)
+        dach = dbytes / (dms * 1e-3) / 1e9
+        sections["decode"] = {
+            "value": wd.B * wd.H / (dms * 1e-3), "unit": "head-state-updates/s",
+            "us_per_step": dms * 1e3,
+            "workload": f"{wd.name}: B={wd.B} H={wd.H} d={wd.dk}, {wd.steps} steps, fp32 state",
+            "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dach / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic("kda_decode_kernel",
+                                                     f"kda_decode_kernel_{wd.name}.md"),
+                         "kernel": "kda_decode_kernel", "bytes_per_launch": dbytes}}
+    if not args.no_varlen:
+        from linear_recurrent_attention_chunkwise_amd.inputs import make_varlen_inputs
+        wv = WORKLOADS["k3_prefill_bf16"].with_(seed=5)
+        vin = {k: (v.to(dev) if v is not None else None)
+               for k, v in make_varlen_inputs(wv, VARLEN_LENGTHS).items()}
+        ntok = sum(VARLEN_LENGTHS)
+        nseq = len(VARLEN_LENGTHS)
+        vbytes = (ntok * wv.H * (5 * wv.dk * 2 + 2) + 2 * nseq * wv.H * wv.dk * wv.dk * 4
+                  + wv.H * 4)
+        vms = time_varlen(torch, kda, vin, 0, max(1, args.steps // 4), max(1, args.warmup // 40))
+        cms = time_varlen(torch, kda, vin, VARLEN_CKPT_EVERY, max(1, args.steps // 4),
+                          max(1, args.warmup // 40))
+        nck = sum(L // VARLEN_CKPT_EVERY for L in VARLEN_LENGTHS)
+        cbytes = vbytes + nck * wv.H * wv.dk * wv.dk * 4
+        sections["varlen"] = {
+            "value": ntok / (vms * 1e-3), "unit": "tokens/s", "ms_per_launch": vms,
+            "workload": f"packed prefill, {nseq} sequences of lengths {VARLEN_LENGTHS} "
+                        f"({ntok} tokens), H={wv.H}, d={wv.dk}, bf16, chunk 16",
+            "roofline": {"bound": "hbm", "achieved": vbytes / (vms * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": vbytes / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "bytes_per_launch": vbytes},
+            "with_checkpoints": {"ckpt_every": VARLEN_CKPT_EVERY, "checkpoints": nck,
+                                 "ms_per_launch": cms, "value": ntok / (cms * 1e-3),
+                                 "bytes_per_launch": cbytes}}
+    if not args.no_prologue:
+        from linear_recurrent_attention_chunkwise_amd.inputs import (make_layer_decode_inputs,
+                                                                     make_layer_inputs)
+        Wc = PROLOGUE_WIDTH
+        lin = {k: (v.to(dev) if v is not None else None)
+               for k, v in make_layer_inputs(w, Wc).items()}
+        cms_, lms = time_layer(torch, kda, lin, max(1, args.steps // 4), max(1, args.warmup // 40))
+        del lin
+        cb = conv_norm_bytes(w.B, w.T, w.H, w.dk, Wc)
+        wd = WORKLOADS["k3_decode_bf16"]
+        dl = make_layer_decode_inputs(wd, Wc, device=dev)
+        dcms = time_decode_conv(torch, kda, dl, args.decode_reps)
+        del dl
+        dcb = (decode_bytes(wd.B, wd.H, wd.dk) + 2 * 3 * wd.B * (Wc - 1) * wd.H * wd.dk * 2
+               + 3 * wd.H * wd.dk * Wc * 4)
+        sections["prologue"] = {
+            "width": Wc, "activation": PROLOGUE_ACT,
+            "workload": f"{w.name} raw layer inputs (B={w.B} H={w.H} T={w.T} d={w.dk} bf16), "
+                        f"short convolutions of width {Wc} + {PROLOGUE_ACT} + q/k L2 norm, "
+                        f"continued sequence",
+            "conv_norm": {"us_per_launch": cms_ * 1e3, "kernel": "kda_conv_norm_kernel",
+                          "roofline": {"bound": "hbm", "achieved": cb / (cms_ * 1e-3) / 1e9,
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": cb / (cms_ * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                       "traffic": recorded_traffic(
+                                           "kda_conv_norm_kernel",
+                                           f"kda_conv_norm_kernel_{w.name}.md"),
+                                       "bytes_per_launch": cb}},
+            "prefill_conv": {"value": w.B * w.T / (lms * 1e-3), "unit": "tokens/s",
+                             "ms_per_launch": lms},
+            "decode_step_conv": {
+                "value": wd.B * wd.H / (dcms * 1e-3), "unit": "head-state-updates/s",
+                "us_per_step": dcms * 1e3,
+                "workload": f"{wd.name} with the fused prologue (B={wd.B} H={wd.H})",
+                "roofline": {"bound": "hbm", "achieved": dcb / (dcms * 1e-3) / 1e9,
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": dcb / (dcms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "traffic": recorded_traffic(
+                                 "kda_decode_kernel", f"kda_decode_kernel_conv_{wd.name}.md"),
+                             "kernel": "kda_decode_kernel (prologue fused)",
+                             "bytes_per_launch": dcb}}}
+    if not args.no_backward:
+        from linear_recurrent_attention_chunkwise_amd.inputs import make_cotangents
+        dO, dST = make_cotangents(w, device=dev)
+        bms, wsb = time_backward(torch, kda, inp, dO, dST,
+                                 max(1, args.steps // 20), max(1, args.warmup // 400))
+        del dO, dST
+        torch.cuda.empty_cache()
+        sections["backward"] = {
+            "value": w.B * w.T / (bms * 1e-3), "unit": "tokens/s", "ms_per_call": bms,
+            "workload": f"{w.name}: gradients of q, k, v, z, beta, A, S0 from dL/do and "
+                        f"dL/dS_T (B={w.B} H={w.H} T={w.T} d={w.dk}, bf16 in, fp32 gradients)",
+            "workspace_bytes": wsb,
+            "kernels": "forward rerun with 16-token checkpoints, then kda_bwd_prep, "
+                       "kda_bwd_dstate, kda_bwd_part, kda_bwd_grad, kda_bwd_dA"}
+    if not args.no_long:
+        sections["long"] = time_long(torch, kda, 3)
+    # The headline is timed last: the sections above keep the GPU busy for
+    # several seconds, so its W warm-up and K timed steps run at the clocks a
+    # GPU under load holds, not the ramp out of idle (timed first on an idle
+    # GPU, the K3 prefill reads ~25% slower for its first few hundred launches).
     ms, ms_med, ms_min = time_prefill(torch, kda, inp, args.chunk, args.steps, args.warmup)
     pbytes = prefill_bytes(w.B, w.T, w.H, w.dk)
     achieved = pbytes / (ms * 1e-3) / 1e9
@@ -473,103 +579,7 @@ def main(argv=None):
         "counted_flops_per_launch": counted,
         "counted_frac": (counted / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS
                          if counted is not None else None)}
-    if not args.no_decode:
-        wd = WORKLOADS["k3_decode_bf16"]
-        dinp = make_decode_inputs(wd, device=dev)
-        dms = time_decode(torch, kda, dinp, args.decode_reps)
-        dbytes = decode_bytes(wd.B, wd.H, wd.dk)
-        dach = dbytes / (dms * 1e-3) / 1e9
-        result["decode"] = {
-            "value": wd.B * wd.H / (dms * 1e-3), "unit": "head-state-updates/s",
-            "us_per_step": dms * 1e3,
-            "workload": f"{wd.name}: B={wd.B} H={wd.H} d={wd.dk}, {wd.steps} steps, fp32 state",
-            "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dach / HBM_PEAK_GBS,
-                         "traffic": recorded_traffic("kda_decode_kernel",
-                                                     f"kda_decode_kernel_{wd.name}.md"),
-                         "kernel": "kda_decode_kernel", "bytes_per_launch": dbytes}}
-    if not args.no_varlen:
-        from linear_recurrent_attention_chunkwise_amd.inputs import make_varlen_inputs
-        wv = WORKLOADS["k3_prefill_bf16"].with_(seed=5)
-        vin = {k: (v.to(dev) if v is not None else None)
-               for k, v in make_varlen_inputs(wv, VARLEN_LENGTHS).items()}
-        ntok = sum(VARLEN_LENGTHS)
-        nseq = len(VARLEN_LENGTHS)
-        vbytes = (ntok * wv.H * (5 * wv.dk * 2 + 2) + 2 * nseq * wv.H * wv.dk * wv.dk * 4
-                  + wv.H * 4)
-        vms = time_varlen(torch, kda, vin, 0, max(1, args.steps // 4), max(1, args.warmup // 40))
-        cms = time_varlen(torch, kda, vin, VARLEN_CKPT_EVERY, max(1, args.steps // 4),
-                          max(1, args.warmup // 40))
-        nck = sum(L // VARLEN_CKPT_EVERY for L in VARLEN_LENGTHS)
-        cbytes = vbytes + nck * wv.H * wv.dk * wv.dk * 4
-        result["varlen"] = {
-            "value": ntok / (vms * 1e-3), "unit": "tokens/s", "ms_per_launch": vms,
-            "workload": f"packed prefill, {nseq} sequences of lengths {VARLEN_LENGTHS} "
-                        f"({ntok} tokens), H={wv.H}, d={wv.dk}, bf16, chunk 16",
-            "roofline": {"bound": "hbm", "achieved": vbytes / (vms * 1e-3) / 1e9,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": vbytes / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "bytes_per_launch": vbytes},
-            "with_checkpoints": {"ckpt_every": VARLEN_CKPT_EVERY, "checkpoints": nck,
-                                 "ms_per_launch": cms, "value": ntok / (cms * 1e-3),
-                                 "bytes_per_launch": cbytes}}
-    if not args.no_prologue:
-        from linear_recurrent_attention_chunkwise_amd.inputs import (make_layer_decode_inputs,
-                                                                     make_layer_inputs)
-        Wc = PROLOGUE_WIDTH
-        lin = {k: (v.to(dev) if v is not None else None)
-               for k, v in make_layer_inputs(w, Wc).items()}
-        cms_, lms = time_layer(torch, kda, lin, max(1, args.steps // 4), max(1, args.warmup // 40))
-        del lin
-        cb = conv_norm_bytes(w.B, w.T, w.H, w.dk, Wc)
-        wd = WORKLOADS["k3_decode_bf16"]
-        dl = make_layer_decode_inputs(wd, Wc, device=dev)
-        dcms = time_decode_conv(torch, kda, dl, args.decode_reps)
-        del dl
-        dcb = (decode_bytes(wd.B, wd.H, wd.dk) + 2 * 3 * wd.B * (Wc - 1) * wd.H * wd.dk * 2
-               + 3 * wd.H * wd.dk * Wc * 4)
-        result["prologue"] = {
-            "width": Wc, "activation": PROLOGUE_ACT,
-            "workload": f"{w.name} raw layer inputs (B={w.B} H={w.H} T={w.T} d={w.dk} bf16), "
-                        f"short convolutions of width {Wc} + {PROLOGUE_ACT} + q/k L2 norm, "
-                        f"continued sequence",
-            "conv_norm": {"us_per_launch": cms_ * 1e3, "kernel": "kda_conv_norm_kernel",
-                          "roofline": {"bound": "hbm", "achieved": cb / (cms_ * 1e-3) / 1e9,
-                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                       "frac": cb / (cms_ * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                       "traffic": recorded_traffic(
-                                           "kda_conv_norm_kernel",
-                                           f"kda_conv_norm_kernel_{w.name}.md"),
-                                       "bytes_per_launch": cb}},
-            "prefill_conv": {"value": w.B * w.T / (lms * 1e-3), "unit": "tokens/s",
-                             "ms_per_launch": lms},
-            "decode_step_conv": {
-                "value": wd.B * wd.H / (dcms * 1e-3), "unit": "head-state-updates/s",
-                "us_per_step": dcms * 1e3,
-                "workload": f"{wd.name} with the fused prologue (B={wd.B} H={wd.H})",
-                "roofline": {"bound": "hbm", "achieved": dcb / (dcms * 1e-3) / 1e9,
-                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": dcb / (dcms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                             "traffic": recorded_traffic(
-                                 "kda_decode_kernel", f"kda_decode_kernel_conv_{wd.name}.md"),
-                             "kernel": "kda_decode_kernel (prologue fused)",
-                             "bytes_per_launch": dcb}}}
-    if not args.no_backward:
-        from linear_recurrent_attention_chunkwise_amd.inputs import make_cotangents
-        dO, dST = make_cotangents(w, device=dev)
-        bms, wsb = time_backward(torch, kda, inp, dO, dST,
-                                 max(1, args.steps // 20), max(1, args.warmup // 400))
-        del dO, dST
-        torch.cuda.empty_cache()
-        result["backward"] = {
-            "value": w.B * w.T / (bms * 1e-3), "unit": "tokens/s", "ms_per_call": bms,
-            "workload": f"{w.name}: gradients of q, k, v, z, beta, A, S0 from dL/do and "
-                        f"dL/dS_T (B={w.B} H={w.H} T={w.T} d={w.dk}, bf16 in, fp32 gradients)",
-            "workspace_bytes": wsb,
-            "kernels": "forward rerun with 16-token checkpoints, then kda_bwd_prep, "
-                       "kda_bwd_dstate, kda_bwd_part, kda_bwd_grad, kda_bwd_dA"}
-    if not args.no_long:
-        result["long"] = time_long(torch, kda, 3)
+    result.update(sections)
     if args.calib_mib > 0:
         calibration_copy(torch, args.calib_mib)
     if not args.no_cpu:

@@ -71,6 +71,11 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
+    # KDA_ORACLE_LIB: another build of kda_oracle.c to run (the sanitizer test
+    # runs the pin tests against an instrumented build)
+    if os.environ.get("KDA_ORACLE_LIB"):
+        _lib = _bind(os.environ["KDA_ORACLE_LIB"])
+        return _lib
     if not os.path.exists(_LIB_PATH) or (
             os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
         build(force=True)

@@ -10,7 +10,10 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
-LIB = os.path.join(ROOT, "linear_recurrent_attention_chunkwise_amd", "libkda.so")
+# KDA_TEST_LIB: another build of the library to check (test_sanitizers.py runs
+# this file against a host-sanitized build)
+LIB = os.environ.get("KDA_TEST_LIB") or os.path.join(ROOT, "linear_recurrent_attention_chunkwise_amd",
+                                                      "libkda.so")
 
 OK, NULL, SHAPE, UNSUP, MISALIGNED, ALIAS, WORKSPACE = 0, 1, 2, 3, 4, 5, 6
 F32, BF16 = 0, 1
@@ -21,6 +24,8 @@ def lib():
     if not os.path.exists(LIB):
         pytest.fail("libkda.so is not built (run __graft_entry__.build())")
     from linear_recurrent_attention_chunkwise_amd import kda as binding
+    if os.environ.get("KDA_TEST_LIB"):
+        binding.library_path = lambda: LIB
     return binding._load()
 
 
