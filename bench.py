@@ -50,11 +50,14 @@ WRITE_SIZE) is scaled by when the kernels' HBM traffic is measured.
 kernel's summary under profiles/, reported only while the kernel source still
 hashes to the one the counters were taken on (null otherwise).
 
-Order: the other sections run first and the headline prefill is timed last,
-so that its W warm-up and K timed steps run on a GPU that has been under load
-for several seconds (its working clocks), whatever W is; on a GPU fresh out of
-idle the same kernel reads ~25% slower for its first few hundred launches.
-The oracle baseline runs after every GPU timing.
+Order: packed, prologue, backward, long, decode, then the headline prefill,
+timed last so that its W warm-up and K timed steps run on a GPU that has been
+under load for a while (the decode timing, 16 runs of 256 steps, ends right
+before it), whatever W is.  The clocks of an MI355X drop within about a second
+of idling, and the K3 prefill then reads ~25% slower until they ramp up again
+(measured: 225-230 us per launch just after 1 s idle, 187 us after 2 s of
+decode steps, 180 us after 0.5 s of back-to-back prefills).  The oracle
+baseline runs after every GPU timing.
 """
 from __future__ import annotations
 
@@ -411,7 +414,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=8000)
     ap.add_argument("--chunk", type=int, default=16, choices=(16, 64))
-    ap.add_argument("--decode-reps", type=int, default=2)
+    ap.add_argument("--decode-reps", type=int, default=16,
+                    help="runs of the 256-step decode workload in its timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
@@ -439,21 +443,6 @@ def main(argv=None):
     inp_cpu = make_prefill_inputs(w)
     inp = {k: (v.to(dev) if v is not None else None) for k, v in inp_cpu.items()}
     sections = {}
-    if not args.no_decode:
-        wd = WORKLOADS["k3_decode_bf16"]
-        dinp = make_decode_inputs(wd, device=dev)
-        dms = time_decode(torch, kda, dinp, args.decode_reps)
-        dbytes = decode_bytes(wd.B, wd.H, wd.dk)
-        dach = dbytes / (dms * 1e-3) / 1e9
-        sections["decode"] = {
-            "value": wd.B * wd.H / (dms * 1e-3), "unit": "head-state-updates/s",
-            "us_per_step": dms * 1e3,
-            "workload": f"{wd.name}: B={wd.B} H={wd.H} d={wd.dk}, {wd.steps} steps, fp32 state",
-            "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dach / HBM_PEAK_GBS,
-                         "traffic": recorded_traffic("kda_decode_kernel",
-                                                     f"kda_decode_kernel_{wd.name}.md"),
-                         "kernel": "kda_decode_kernel", "bytes_per_launch": dbytes}}
     if not args.no_varlen:
         from linear_recurrent_attention_chunkwise_amd.inputs import make_varlen_inputs
         wv = WORKLOADS["k3_prefill_bf16"].with_(seed=5)
@@ -536,6 +525,21 @@ def main(argv=None):
                        "kda_bwd_dstate, kda_bwd_part, kda_bwd_grad, kda_bwd_dA"}
     if not args.no_long:
         sections["long"] = time_long(torch, kda, 3)
+    if not args.no_decode:
+        wd = WORKLOADS["k3_decode_bf16"]
+        dinp = make_decode_inputs(wd, device=dev)
+        dms = time_decode(torch, kda, dinp, args.decode_reps)
+        dbytes = decode_bytes(wd.B, wd.H, wd.dk)
+        dach = dbytes / (dms * 1e-3) / 1e9
+        sections["decode"] = {
+            "value": wd.B * wd.H / (dms * 1e-3), "unit": "head-state-updates/s",
+            "us_per_step": dms * 1e3,
+            "workload": f"{wd.name}: B={wd.B} H={wd.H} d={wd.dk}, {wd.steps} steps, fp32 state",
+            "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dach / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic("kda_decode_kernel",
+                                                     f"kda_decode_kernel_{wd.name}.md"),
+                         "kernel": "kda_decode_kernel", "bytes_per_launch": dbytes}}
     # The headline is timed last: the sections above keep the GPU busy for
     # several seconds, so its W warm-up and K timed steps run at the clocks a
     # GPU under load holds, not the ramp out of idle (timed first on an idle

@@ -10,14 +10,14 @@
 //
 //  * PREP waves (NPW per workgroup).  Prep wave w owns chunks w, w+NPW, ...
 //    and does the S-independent work of a chunk by itself, with no workgroup
-//    barrier: gate, decay factors, the P and L tiles, the 16 x 16 inverse and
-//    W.  It writes the chain operands into an LDS slot (chunk m uses slot
-//    m mod NSLOT).
+//    barrier: gate, decay factors, the P and L tiles and the 16 x 16
+//    inverse T.  It writes the chain operands into an LDS slot (chunk m uses
+//    slot m mod NSLOT).
 //  * CHAIN waves (NCW per workgroup, 16 value columns each, fp32 state slice
 //    in registers).  They consume the slots in chunk order and run the
-//    S-dependent chain: S' = e^{G_C} S, U = T diag(beta) V - W~ S',
-//    O = Q~ S' + P U, S <- S' + Kh^T U.  Each chain wave loads its own 16
-//    columns of V straight into MFMA fragments.
+//    S-dependent chain: S' = e^{G_C} S, U = T diag(beta) (V - K~ S'),
+//    O = Q~ S' + P U, S <- S' + Kh^T U.  Each chain wave reads its own 16
+//    columns of V (staged by the prep) as an MFMA fragment.
 //  Slot hand-off uses LDS counters: `ready[slot]` (stored by the prep wave
 //  as u+1 once the slot holds its u-th chunk) and `done[slot][chain wave]`
 //  (stored by each chain wave as u+1 once it has issued every read of the
@@ -32,7 +32,7 @@
 // With one chunk per 16-token sub-tile, every decay factor can be referred to
 // the chunk end: with G_r = sum_{s<=r} g_s and G_C the chunk total,
 //    Q~ = Q * e^{G - G_C}   (row operand of P; the read O = Q~ (e^{G_C} S))
-//    K~ = K * e^{G - G_C}   (row operand of L; W~ = T diag(beta) K~ = W e^{-G_C})
+//    K~ = K * e^{G - G_C}   (row operand of L, and of the chain's K~ S')
 //    Kh = K * e^{G_C - G}   (column operand of P and L; the state update)
 // so P = tril(Q~ Kh^T), L = diag(beta) strict_tril(K~ Kh^T).  Over at most 15
 // later tokens of a chunk, 1 <= e^{G - G_C} <= e^75 and e^{-75} <= e^{G_C - G}
@@ -83,11 +83,11 @@ struct P16Cfg {
     // fragment read spread over 4 row strides x 4 piece positions.
     static constexpr int DP = D + 4;               // Q~ [token][d] row stride (66 words)
     static constexpr int CP = C + 4;               // [token][token] row stride (10 words)
-    static constexpr int KP = D + 16;              // K~/-W~ and Kh row stride (72 words, swizzled)
+    static constexpr int KP = D + 16;              // K~ and Kh row stride (72 words, swizzled)
     // slot: the chain operands of one chunk
     static constexpr int S_QG = 0;                         // Q~         [C][DP]
-    static constexpr int S_WN = S_QG + C * DP * 2;         // K~, then -W~ [C][KP], swizzled
-    static constexpr int S_KH = S_WN + C * KP * 2;         // Kh         [C][KP], swizzled
+    static constexpr int S_KT = S_QG + C * DP * 2;         // K~         [C][KP], swizzled
+    static constexpr int S_KH = S_KT + C * KP * 2;         // Kh         [C][KP], swizzled
     static constexpr int S_P = S_KH + C * KP * 2;          // P          [C][CP]
     static constexpr int S_TB = S_P + C * CP * 2;          // T diag(b)  [C][CP]
     static constexpr int S_GC = S_TB + C * CP * 2;         // e^{G_C}    [D] fp32, permuted
@@ -287,11 +287,11 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             f.v = *reinterpret_cast<const bf16x4 *>(p);
             return f;
         };
-        // W, T diag(beta), Kh^T and V fragments and the decay e^{G_C} of a chunk
+        // K~, T diag(beta), Kh^T and V fragments and the decay e^{G_C} of a chunk
         // (read one chunk ahead; Kh^T and V by transposing reads of token-major
         // tiles: V as V[t0 + 4g + e][jw + n], staged by the prep wave, zero past T)
         typedef float f32x2 __attribute__((ext_vector_type(2)));
-        Frag<bf16> Wf[NDT], Kf[NDT], Tf, Vn;
+        Frag<bf16> Ktf[NDT], Kf[NDT], Tf, Vn;
         f32x2 gvn;
         bool waited_ok = true;   // every slot wait of this wave succeeded
         auto read_wtk = [&](int sl, int use) {
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             const char *pc = smem + off + offCP;
             gvn = *reinterpret_cast<const f32x2 *>(smem + off + Cfg::S_GC + offG);
 #pragma unroll
-            for (int i = 0; i < NDT; ++i) Wf[i] = frag_at(pk + Cfg::S_WN + 32 * i);
+            for (int i = 0; i < NDT; ++i) Ktf[i] = frag_at(pk + Cfg::S_KT + 32 * i);
             Tf = frag_at(pc + Cfg::S_TB);
             const bf16 *kh = reinterpret_cast<const bf16 *>(smem + off + Cfg::S_KH);
 #pragma unroll
@@ -360,17 +360,15 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             const f32x2 gv = gvn;
             const Frag<bf16> Vf = Vn;
             // (1) the previous chunk's output products (matrix cores), then
-            // S <- e^{G_C} S and U = T diag(beta) V - W~ S, W~ = W e^{-G_C}
-            // (two accumulators halve the dependent chain; T diag(beta) V, a
-            // product of the other MFMA shape, has its own accumulator: no
-            // MFMA takes the fresh result of an MFMA of another shape as its
+            // S <- e^{G_C} S and the products K~ S' of U = T diag(beta) (V - K~ S')
+            // (two accumulators halve the dependent chain; the product with
+            // T diag(beta), of the other MFMA shape, starts from zero: no MFMA
+            // takes the fresh result of an MFMA of another shape as its
             // accumulator, which MI355X does not order)
             if constexpr (MODE == 0)
                 if (m > 0) out_issue();
             __builtin_amdgcn_sched_barrier(0);
-            f32x4 Ua = {0.f, 0.f, 0.f, 0.f}, Ub = {0.f, 0.f, 0.f, 0.f},
-                  Uv = {0.f, 0.f, 0.f, 0.f};
-            mma16(Uv, Tf, Vf);
+            f32x4 Ua = {0.f, 0.f, 0.f, 0.f}, Ub = {0.f, 0.f, 0.f, 0.f};
             Frag<bf16> Sf[NDT], Sf2[NDT];
             // X <- e^{G_C} X: row 16 i + 4 g + e scaled by lane 2 i + e/2's word e%2
 #define KDA_DECAY_TILE(X, Xf, i)                                            \
@@ -386,18 +384,18 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             KDA_DECAY_TILE(X, Xf, 6) KDA_DECAY_TILE(X, Xf, 7)
             static_assert(NDT == 8, "decay broadcast covers 8 row tiles");
             KDA_DECAY(S, Sf)
-            mma32(Ub, Wf[0], Wf[1], Sf[0], Sf[1]);
-            mma32(Ua, Wf[2], Wf[3], Sf[2], Sf[3]);
-            mma32(Ub, Wf[4], Wf[5], Sf[4], Sf[5]);
-            mma32(Ua, Wf[6], Wf[7], Sf[6], Sf[7]);
-            // MODE 2: the value-carrying slice, U2 = T diag(beta) V - W~ S2'
+            mma32(Ub, Ktf[0], Ktf[1], Sf[0], Sf[1]);
+            mma32(Ua, Ktf[2], Ktf[3], Sf[2], Sf[3]);
+            mma32(Ub, Ktf[4], Ktf[5], Sf[4], Sf[5]);
+            mma32(Ua, Ktf[6], Ktf[7], Sf[6], Sf[7]);
+            // MODE 2: the value-carrying slice, K~ S2' (its U2 takes V)
             f32x4 U2a = {0.f, 0.f, 0.f, 0.f}, U2b = {0.f, 0.f, 0.f, 0.f};
             if constexpr (MODE == 2) {
                 KDA_DECAY(S2, Sf2)
-                mma32(U2b, Wf[0], Wf[1], Sf2[0], Sf2[1]);
-                mma32(U2a, Wf[2], Wf[3], Sf2[2], Sf2[3]);
-                mma32(U2b, Wf[4], Wf[5], Sf2[4], Sf2[5]);
-                mma32(U2a, Wf[6], Wf[7], Sf2[6], Sf2[7]);
+                mma32(U2b, Ktf[0], Ktf[1], Sf2[0], Sf2[1]);
+                mma32(U2a, Ktf[2], Ktf[3], Sf2[2], Sf2[3]);
+                mma32(U2b, Ktf[4], Ktf[5], Sf2[4], Sf2[5]);
+                mma32(U2a, Ktf[6], Ktf[7], Sf2[6], Sf2[7]);
             }
 #undef KDA_DECAY
 #undef KDA_DECAY_TILE
@@ -417,14 +415,26 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
             __hip_atomic_store(&done[sl * NCW + wave], use + 1, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
             compiler_fence();
+            // U = T diag(beta) (V - K~ S'): Y = V - K~ S' rounded once, then one
+            // product with T diag(beta)
             Frag<bf16> Uf, Uf2;
+            auto apply_t = [&](const f32x4 &X, bool with_v) {
+                f32x4 Y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Y[e] = (with_v ? (float)Vf.v[e] : 0.0f) - X[e];
+                Frag<bf16> Yf;
+                Yf.v = to_bf16x4(Y[0], Y[1], Y[2], Y[3]);
+                f32x4 U = {0.f, 0.f, 0.f, 0.f};
+                mma16(U, Tf, Yf);
+                Frag<bf16> r;
+                r.v = to_bf16x4(U[0], U[1], U[2], U[3]);
+                return r;
+            };
             if constexpr (MODE == 2) {
-                const f32x4 U = Ua + Ub, U2 = (U2a + U2b) + Uv;
-                Uf.v = to_bf16x4(U[0], U[1], U[2], U[3]);
-                Uf2.v = to_bf16x4(U2[0], U2[1], U2[2], U2[3]);
+                Uf = apply_t(Ua + Ub, false);
+                Uf2 = apply_t(U2a + U2b, true);
             } else {
-                const f32x4 U = (Ua + Ub) + Uv;
-                Uf.v = to_bf16x4(U[0], U[1], U[2], U[3]);
+                Uf = apply_t(Ua + Ub, true);
             }
             // (3) S <- S + Kh^T U
 #pragma unroll
@@ -559,7 +569,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         const int use = (int)(m / NSLOT);
         char *slot = smem + Cfg::OFF_SLOTS + s_ * Cfg::SLOT;
         bf16 *sQG = reinterpret_cast<bf16 *>(slot + Cfg::S_QG);
-        bf16 *sWn = reinterpret_cast<bf16 *>(slot + Cfg::S_WN);   // K~ until -W~ overwrites it
+        bf16 *sKt = reinterpret_cast<bf16 *>(slot + Cfg::S_KT);   // K~ token-major
         bf16 *sKh = reinterpret_cast<bf16 *>(slot + Cfg::S_KH);   // Kh token-major
         bf16 *sP = reinterpret_cast<bf16 *>(slot + Cfg::S_P);
         bf16 *sTb = reinterpret_cast<bf16 *>(slot + Cfg::S_TB);
@@ -623,7 +633,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
                 if constexpr (MODE == 0)   // Q~ feeds the output only
                     *reinterpret_cast<uint32_t *>(sQG + s * DP + d0) =
                         pack_bf16(bf_lo(rq[s]) * f0, bf_hi(rq[s]) * f1);
-                *reinterpret_cast<uint32_t *>(sWn + s * Cfg::KP + 4 * swz_piece(s, lane >> 1) +
+                *reinterpret_cast<uint32_t *>(sKt + s * Cfg::KP + 4 * swz_piece(s, lane >> 1) +
                                               2 * (lane & 1)) =
                     pack_bf16(bf_lo(rk[s]) * f0, bf_hi(rk[s]) * f1);
             }
@@ -643,8 +653,8 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         for (int k32 = 0; k32 < D; k32 += 32) {
             const Frag<bf16> c0 = frag_swz(sKh, Cfg::KP, k32, lane),
                              c1 = frag_swz(sKh, Cfg::KP, k32 + 16, lane);
-            const Frag<bf16> h0f = frag_swz(sWn, Cfg::KP, k32, lane),
-                             h1f = frag_swz(sWn, Cfg::KP, k32 + 16, lane);
+            const Frag<bf16> h0f = frag_swz(sKt, Cfg::KP, k32, lane),
+                             h1f = frag_swz(sKt, Cfg::KP, k32 + 16, lane);
             if constexpr (MODE == 0) {
                 const Frag<bf16> q0f = lds_frag(sQG, DP, k32, lane),
                                  q1f = lds_frag(sQG, DP, k32 + 16, lane);
@@ -696,19 +706,6 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
         Tf.v = to_bf16x4(TT[0] * brow[0], TT[1] * brow[1], TT[2] * brow[2], TT[3] * brow[3]);
         *reinterpret_cast<bf16x4 *>(sTb + n * CP + 4 * g) = Tf.v;
 
-        // ---- W~^T = K~^T Tb^T, written as -W~ rows over K~ -------------------
-        // A-layout of K~^T for d-tile dt: lane (g,n) holds K~[4g+e][16 dt + n]
-        // (strided 2-byte reads, conflict-free); a tile is read completely
-        // before its W rows overwrite the same columns.
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const Frag<bf16> ka = frag_rows_tr_swz(sWn, Cfg::KP, 16 * dt, lane);
-            f32x4 w = {0.f, 0.f, 0.f, 0.f};
-            mma16(w, ka, Tf);
-            // w[e] = W[n][16 dt + 4 g + e]
-            *reinterpret_cast<bf16x4 *>(sWn + n * Cfg::KP + 16 * dt + 4 * swz_piece(n, g)) =
-                to_bf16x4(-w[0], -w[1], -w[2], -w[3]);
-        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __hip_atomic_store(&ready[s_], use + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
