@@ -29,7 +29,9 @@ included), read from the kernel's summary under profiles/.
 ``long`` times the long-context (B1 H96 T65536, z ~ N(2,1)) and million-token
 (B1 H16 T2^20) prefill workloads at 64- and 16-token chunks over 3 launches
 each, inputs drawn on the device; the million-token head share also split
-into 4 and 8 segments (kda_prefill_split).  ``timing`` gives the median and minimum
+into 4 and 8 segments (kda_prefill_split).  Each entry's ``roofline.traffic``
+is the HBM bytes per call from its counter summary under profiles/ (for a
+split call, both passes), null once the kernel source has changed.  ``timing`` gives the median and minimum
 per-launch time of 10 equal segments of the timed steps.
 
 ``backward`` times kda_prefill_bwd_ex on the same workload: gradients of q,
@@ -398,11 +400,21 @@ def time_long(torch, kda, steps):
         ms, med, mn = time_prefill(torch, kda, inp, chunk, steps, 1, segments)
         b = prefill_bytes(w.B, w.T, w.H, w.dk)
         key = f"{name}_c{chunk}" + (f"_split{segments}" if segments > 1 else "")
+        kernel = prefill_kernel_name(chunk)
+        if segments > 1:   # the split call's two passes of the role-split kernel
+            traffic = recorded_counter(kernel, f"kda_prefill_split_{name}.md",
+                                       f"traffic_bytes_per_launch_split{segments}")
+        else:
+            traffic = recorded_traffic(kernel, f"{kernel}_{name}_c{chunk}.md")
         res[key] = {
             "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s", "ms_per_launch": ms,
             "median_ms": med, "min_ms": mn, "chunk": chunk, "segments": segments,
             "workload": f"{name}: B={w.B} H={w.H} T={w.T} d={w.dk} bf16, z mean {w.z_mean}",
-            "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "roofline": {"bound": "hbm", "achieved": b / (ms * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+                         "kernel": kernel, "bytes_per_launch": b}}
     cache.clear()
     torch.cuda.empty_cache()
     return res
