@@ -62,8 +62,14 @@ struct PrefillCfg {
     static constexpr int DVB = 16 * NW;
     static constexpr int NP = C / 16;
     static constexpr int NDT = D / 16;
+    // Row strides.  LDS serves each group of 16 lanes from 32 four-byte banks;
+    // a fragment read (16 rows, one 8-byte piece each) is conflict-free when
+    // the stride is 2 mod 32 words.  [token][d] tiles take D + 4 elements
+    // (66 words for bf16, 132 for fp32, whose 16-byte pieces need 4 mod 32);
+    // [d][token] tiles are written 16 bytes per row and keep rows 16-byte
+    // aligned (C + 8 bf16 / C + 4 fp32 elements).
     static constexpr int PADE = sizeof(T) == 2 ? 8 : 4;
-    static constexpr int DP = D + PADE;      // row stride of [token][d] tiles
+    static constexpr int DP = D + 4;         // row stride of [token][d] tiles
     static constexpr int CP = C + PADE;      // row stride of [d][token] / [token][token] tiles
     static constexpr int LP = C + 4;         // row stride of the fp32 L tile
     static constexpr int OP = DVB + PADE;    // row stride of the output staging tile
