@@ -354,7 +354,8 @@ def cpu_baseline(w, inp_cpu):
 
 LONG_CASES = [("long_prefill_bf16", 64, 1), ("long_prefill_bf16", 16, 1),
               ("million_prefill_bf16", 64, 1), ("million_prefill_bf16", 16, 1),
-              ("million_prefill_bf16", 16, 4), ("million_prefill_bf16", 16, 8)]
+              ("million_prefill_bf16", 16, 4), ("million_prefill_bf16", 16, 8),
+              ("million_prefill_bf16", 16, 9)]
 
 
 def time_backward(torch, kda, inp, dO, dST, steps, warmup):

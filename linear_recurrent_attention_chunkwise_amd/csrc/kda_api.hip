@@ -662,21 +662,20 @@ bool split_layout(int64_t B, int64_t H, int64_t D, int P, SplitLayout *lay) {
         return false;
     lay->cu = 0;
     lay->first = round256((n + 1) * 8);
-    lay->M = lay->first + round256(n * 4);
+    lay->M = lay->first + round256(n * 8);   // three rank lists: B * (2P - 2) <= 2n entries
     lay->N = lay->M + round256(ne * 4);
     lay->S = lay->N + round256(ne * 4);
     lay->total = lay->S + round256(ne * 4);
     return true;
 }
 
-// One pass of the role-split prefill over the segments of a split call (whose
-// arguments were validated on entry): `nseq` segments of the packing `cu`,
-// rank r running segment order[r] (or r).
-kda_status split_pass(int64_t nseq, int64_t Ttot, int64_t H, const int64_t *cu,
-                      const int32_t *order, const void *q, const void *k, const void *v,
-                      const void *z, const void *beta, const float *A, const float *S0, void *o,
-                      float *S_T, float *S_T2, int mode, hipStream_t stream) {
-    if (nseq * H == 0) return KDA_OK;
+// Arguments of one role-split prefill run over segments of a split call
+// (whose arguments were validated on entry): `nseq` segments of the packing
+// `cu`, rank r running segment order[r]; S0, S_T, S_T2 indexed by segment.
+kda::PrefillArgs split_args(int64_t nseq, int64_t Ttot, int64_t H, const int64_t *cu,
+                            const int32_t *order, const void *q, const void *k, const void *v,
+                            const void *z, const void *beta, const float *A, const float *S0,
+                            void *o, float *S_T, float *S_T2, int mode, hipStream_t stream) {
     kda::PrefillArgs a;
     a.dtype = KDA_BF16; a.B = nseq; a.T = Ttot; a.H = H; a.D = 128; a.chunk = 16;
     a.dv_per_block = 64;
@@ -687,7 +686,7 @@ kda_status split_pass(int64_t nseq, int64_t Ttot, int64_t H, const int64_t *cu,
     a.ckpt_every = 0; a.ckpt = nullptr; a.n_ckpt = 0;
     a.mode = mode;
     a.stream = stream;
-    return kda::launch_prefill16(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return a;
 }
 
 }  // namespace
@@ -743,25 +742,31 @@ kda_status kda_prefill_split(int dtype, int64_t B, int64_t T, int64_t H, int64_t
     if (B * H == 0) return KDA_OK;
     char *ws = static_cast<char *>(workspace);
     int64_t *cu = reinterpret_cast<int64_t *>(ws + lay.cu);
-    int32_t *first = reinterpret_cast<int32_t *>(ws + lay.first);
+    int32_t *lists = reinterpret_cast<int32_t *>(ws + lay.first);
     float *Mb = reinterpret_cast<float *>(ws + lay.M);
     float *Nb = reinterpret_cast<float *>(ws + lay.N);
-    float *Sb = reinterpret_cast<float *>(ws + lay.S);
+    float *Sb = reinterpret_cast<float *>(ws + lay.S);   // start states, by segment
     const hipStream_t s = (hipStream_t)stream;
     const int64_t L = split_len(T, P, chunk);
     const int64_t Ttot = B * T;   // [B, T, H, d] read as the packing [B*T, H, d]
-    if (kda::launch_split_setup(cu, first, B, T, L, P, s) != hipSuccess) return KDA_ERR_HIP;
-    // (1) maps M (from I, v as zero) and offsets N (from 0) of every segment
-    // but the last of each sequence, in one pass
-    st = split_pass(B * (P - 1), Ttot, H, cu, first, q, k, v, z, beta, A, nullptr, nullptr, Mb,
-                    Nb, 2, s);
-    if (st != KDA_OK) return st;
-    // (2) start state of every segment
-    if (kda::launch_split_scan(S0, Mb, Nb, Sb, B, H, P, (int)dk, s) != hipSuccess)
+    const int64_t per = H * dk * dk;   // one segment's states
+    if (kda::launch_split_setup(cu, lists, S0, Sb, B, T, L, P, H, (int)dk, s) != hipSuccess)
         return KDA_ERR_HIP;
-    // (3) every segment from its start state; its final states go to Mb
-    st = split_pass(nseg, Ttot, H, cu, nullptr, q, k, v, z, beta, A, Sb, o, Mb, nullptr, 0, s);
-    if (st != KDA_OK) return st;
+    // (1) one launch: the first segment of each sequence from S0 (its final
+    // state is the second segment's start), beside the maps M (from I, v as
+    // zero) and offsets N (from 0) of the segments between first and last
+    const kda::PrefillArgs a0 = split_args(B, Ttot, H, cu, lists, q, k, v, z, beta, A,
+                                           S0 ? Sb : nullptr, o, Sb + per, nullptr, 0, s);
+    const kda::PrefillArgs a2 = split_args(B * (P - 2), Ttot, H, cu, lists + B, q, k, v, z, beta,
+                                           A, nullptr, nullptr, Mb, Nb, 2, s);
+    if (kda::launch_prefill16_split_head(a0, a2) != hipSuccess) return KDA_ERR_HIP;
+    // (2) start states of segments 2 .. P-1
+    if (kda::launch_split_scan(Mb, Nb, Sb, B, H, P, (int)dk, s) != hipSuccess)
+        return KDA_ERR_HIP;
+    // (3) segments 1 .. P-1 from their start states; final states go to Mb
+    const kda::PrefillArgs a3 = split_args(B * (P - 1), Ttot, H, cu, lists + B + B * (P - 2), q,
+                                           k, v, z, beta, A, Sb, o, Mb, nullptr, 0, s);
+    if (kda::launch_prefill16(a3) != hipSuccess) return KDA_ERR_HIP;
     return kda::launch_split_gather(Mb, S_T, B, H, P, (int)dk, s) == hipSuccess ? KDA_OK
                                                                                 : KDA_ERR_HIP;
 }

@@ -103,6 +103,9 @@ bool prefill_ckpt_supported(int dtype, int64_t D, int chunk, int dv_per_block);
 // Role-split variant for bf16, D = 128, chunk 16 (kda_prefill16.hip).
 bool prefill16_supported(int dtype, int64_t D, int chunk, int dv_per_block);
 hipError_t launch_prefill16(const PrefillArgs &a);
+// One launch of the role-split kernel running a0 (mode 0) and a2 (mode 2,
+// 64 columns, same H) side by side: the first pass of a sequence split.
+hipError_t launch_prefill16_split_head(const PrefillArgs &a0, const PrefillArgs &a2);
 
 // Longest-first ranking of packed sequences (device): order[rank] = sequence.
 // Only used for 1 < N <= kMaxOrderSeqs.
@@ -110,13 +113,18 @@ constexpr int64_t kMaxOrderSeqs = 8192;
 hipError_t launch_seq_order(const int64_t *cu, int64_t N, int64_t T, int32_t *order,
                             hipStream_t stream);
 
-// Sequence split (kda_split.hip): segment offsets and the list of segments
-// that are not the last of their sequence (P >= 2), the scan of segment start
-// states, the gather of the final states.
-hipError_t launch_split_setup(int64_t *cu, int32_t *first, int64_t B, int64_t T, int64_t L,
-                              int P, hipStream_t stream);
-hipError_t launch_split_scan(const float *S0, const float *M, const float *N, float *Sstart,
-                             int64_t B, int64_t H, int P, int D, hipStream_t stream);
+// Sequence split (kda_split.hip), P >= 2 segments per sequence.  Setup: the
+// segment offsets cu [B*P + 1] and three rank lists in `lists`: the first
+// segment of each sequence [B], the middle ones (1 .. P-2) [B*(P-2)], and
+// all but the first [B*(P-1)]; with S0 given, S0[b] is copied to
+// Sstart[b*P] (the first segment's start state).  Scan: from Sstart[b*P+1]
+// (the first segment's final state), Sstart[b*P+j+1] = M_j Sstart[b*P+j] +
+// N_j for j = 1 .. P-2.  Gather: S_T[b] = Sseg[b*P + P-1].
+hipError_t launch_split_setup(int64_t *cu, int32_t *lists, const float *S0, float *Sstart,
+                              int64_t B, int64_t T, int64_t L, int P, int64_t H, int D,
+                              hipStream_t stream);
+hipError_t launch_split_scan(const float *M, const float *N, float *Sstart, int64_t B,
+                             int64_t H, int P, int D, hipStream_t stream);
 hipError_t launch_split_gather(const float *Sseg, float *S_T, int64_t B, int64_t H, int P, int D,
                                hipStream_t stream);
 

@@ -208,12 +208,15 @@ __device__ __forceinline__ Frag<bf16> frag_rows_tr(const bf16 *tile, int ld, int
 // carries two 16-column state slices on the same prep, columns jw.. of M
 // (started from the identity with V taken as zero; written to S_T) and of N
 // (the final state from S0, or from zero, with V; written to S_T2).
+//
+// The work of one workgroup (block `blk` of `nblk`), on the LDS block `smem`
+// of P16Cfg::LDS_BYTES; the kernels below are its entry points.
 template <int NCW, int NPW, int NSLOT, bool CKPT, int MODE>
-__global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill16Params prm) {
+__device__ __forceinline__ void prefill16_block(const Prefill16Params &prm, char *smem,
+                                                int64_t blk, int64_t nblk) {
     using Cfg = P16Cfg<NCW, NPW, NSLOT>;
     constexpr int D = Cfg::D, C = Cfg::C, DVB = Cfg::DVB, DP = Cfg::DP, CP = Cfg::CP,
                   NDT = D / 16;
-    __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
     int *ready = reinterpret_cast<int *>(smem + Cfg::OFF_FLAGS);
     int *done = reinterpret_cast<int *>(smem + Cfg::OFF_DONE);   // [slot][chain wave]
     int *poison = reinterpret_cast<int *>(smem + Cfg::OFF_POISON);
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
     const int g = lane >> 4, n = lane & 15;
 
     const int64_t H = prm.H;
-    const BlockMap bm = block_map(blockIdx.x, gridDim.x, prm.nsplit, H, prm.order);
+    const BlockMap bm = block_map(blk, nblk, prm.nsplit, H, prm.order);
     const int64_t b = bm.b;
     const int h = bm.h;
     const int split = bm.split;
@@ -711,8 +714,29 @@ __global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill
     }
 }
 
-template <int NCW, int NPW, int NSLOT, bool CKPT, int MODE = 0>
-static hipError_t launch_p16(const PrefillArgs &a) {
+template <int NCW, int NPW, int NSLOT, bool CKPT, int MODE>
+__global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_kernel(Prefill16Params prm) {
+    __shared__ __attribute__((aligned(16))) char smem[P16Cfg<NCW, NPW, NSLOT>::LDS_BYTES];
+    prefill16_block<NCW, NPW, NSLOT, CKPT, MODE>(prm, smem, blockIdx.x, gridDim.x);
+}
+
+// First pass of a sequence split, one launch: blocks [0, nblk0) run the
+// prefill (MODE 0) of every sequence's first segment from its start state,
+// the others the state maps (MODE 2) of the segments between the first and
+// the last.  Both halves fill the chip together.
+template <int NCW, int NPW, int NSLOT>
+__global__ __launch_bounds__(64 * (NCW + NPW)) void kda_prefill16_split_head_kernel(
+    Prefill16Params p0, Prefill16Params p2, int nblk0) {
+    __shared__ __attribute__((aligned(16))) char smem[P16Cfg<NCW, NPW, NSLOT>::LDS_BYTES];
+    if ((int)blockIdx.x < nblk0)
+        prefill16_block<NCW, NPW, NSLOT, false, 0>(p0, smem, blockIdx.x, nblk0);
+    else
+        prefill16_block<NCW, NPW, NSLOT, false, 2>(p2, smem, blockIdx.x - nblk0,
+                                                   gridDim.x - nblk0);
+}
+
+template <int NCW, int NPW, int NSLOT>
+static Prefill16Params p16_params(const PrefillArgs &a) {
     Prefill16Params prm;
     prm.q = static_cast<const bf16 *>(a.q);
     prm.k = static_cast<const bf16 *>(a.k);
@@ -734,6 +758,12 @@ static hipError_t launch_p16(const PrefillArgs &a) {
     prm.ckpt_every = a.ckpt_every;
     prm.ckpt_blocked = a.ckpt_blocked ? 1 : 0;
     prm.spin_limit = wait_spin_limit();
+    return prm;
+}
+
+template <int NCW, int NPW, int NSLOT, bool CKPT, int MODE = 0>
+static hipError_t launch_p16(const PrefillArgs &a) {
+    const Prefill16Params prm = p16_params<NCW, NPW, NSLOT>(a);
     const int64_t nblk = a.B * a.H * prm.nsplit;
     hipLaunchKernelGGL((kda_prefill16_kernel<NCW, NPW, NSLOT, CKPT, MODE>), dim3((unsigned)nblk),
                        dim3(64 * (NCW + NPW)), 0, a.stream, prm);
@@ -744,13 +774,24 @@ bool prefill16_supported(int dtype, int64_t D, int chunk, int dv_per_block) {
     return dtype == 1 && D == 128 && chunk == 16 && (dv_per_block == 32 || dv_per_block == 64);
 }
 
+hipError_t launch_prefill16_split_head(const PrefillArgs &a0, const PrefillArgs &a2) {
+    if (a0.dv_per_block != 64 || a2.dv_per_block != 64 || a0.mode != 0 || a2.mode != 2 ||
+        !a2.S_T2 || a0.H != a2.H)
+        return hipErrorInvalidValue;
+    const Prefill16Params p0 = p16_params<4, 8, 8>(a0), p2 = p16_params<4, 8, 8>(a2);
+    const int64_t nblk0 = a0.B * a0.H * p0.nsplit, nblk2 = a2.B * a2.H * p2.nsplit;
+    if (nblk0 + nblk2 == 0) return hipSuccess;
+    hipLaunchKernelGGL((kda_prefill16_split_head_kernel<4, 8, 8>), dim3((unsigned)(nblk0 + nblk2)),
+                       dim3(64 * 12), 0, a0.stream, p0, p2, (int)nblk0);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill16(const PrefillArgs &a) {
     const bool ck = a.ckpt != nullptr && a.ckpt_every > 0;
-    if (a.mode != 0) {   // states only: 64 columns; checkpoints in MODE 1 only
-        if (a.dv_per_block != 64 || (ck && a.mode != 1) || (a.mode == 2 && !a.S_T2))
-            return hipErrorInvalidValue;
+    if (a.mode != 0) {   // final states only: 64 columns
+        if (a.dv_per_block != 64 || a.mode != 1) return hipErrorInvalidValue;
         if (a.mode == 1) return ck ? launch_p16<4, 8, 8, true, 1>(a) : launch_p16<4, 8, 8, false, 1>(a);
-        return launch_p16<4, 8, 8, false, 2>(a);
+        return hipErrorInvalidValue;   // mode 2 runs inside launch_prefill16_split_head
     }
     if (a.dv_per_block == 64)
         return ck ? launch_p16<4, 8, 8, true>(a) : launch_p16<4, 8, 8, false>(a);
