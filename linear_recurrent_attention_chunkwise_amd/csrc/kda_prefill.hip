@@ -10,8 +10,7 @@
 //
 //   L[r,s] = beta_r sum_d k_r[d] k_s[d] e^{G_r[d]-G_s[d]}      (s <  r)
 //   P[r,s] =        sum_d q_r[d] k_s[d] e^{G_r[d]-G_s[d]}      (s <= r)
-//   W  = (I+L)^-1 diag(beta) (K * e^G),   U~ = (I+L)^-1 diag(beta) V
-//   U  = U~ - W S
+//   U  = (I+L)^-1 diag(beta) (V - (K * e^G) S)
 //   O  = (Q * e^G) S + P U
 //   S <- e^{G_C} * S + (K * e^{G_C - G})^T U
 //
@@ -25,16 +24,17 @@
 //   row side    Qd_r = q_r e^{G_r - E_p}      (E_p = G at the end of r's sub-tile p)
 //   column side Kt_s = k_s e^{E_p' - G_s}     (s in sub-tile p')
 //   block (p,p') = Qd_p (Kt_p' * F_{p,p'})^T,  F_{p,p'} = e^{E_p - E_p'} <= 1.
-// (I+L)^-1 is never formed beyond its 16 x 16 diagonal blocks: W and U~ are
-// obtained by block forward substitution, W_p = T_pp (B_p - sum_{j<p} L_pj W_j).
+// T = (I+L)^-1 is formed as 16 x 16 blocks: the diagonal ones by forward
+// substitution, the others from them by block forward substitution, and the
+// chain applies T to its rounded V - K e^G S (one product per block).
 //
 // Work split (one workgroup per (b, h, slice of value columns)):
 //   * value columns of the state evolve independently, so a workgroup owns
 //     DVB = 16 * NW of them; each wave owns 16 columns and the full dk x 16
 //     fp32 state slice in registers, and runs the S-dependent chain (U, O,
 //     state update) with no cross-wave traffic;
-//   * the S-independent per-chunk work (gate, decay factors, P, L, the
-//     triangular solve, W) is done cooperatively by the waves into LDS;
+//   * the S-independent per-chunk work (gate, decay factors, P, L and the
+//     blocks of T) is done cooperatively by the waves into LDS;
 //   * the next chunk's q, k, z, beta, v are prefetched into registers while
 //     the current chunk is processed.
 #include "kda_device.h"
@@ -88,23 +88,20 @@ struct PrefillCfg {
     static_assert(VQ >= 1 && (C * DVB) % (4 * NT) == 0, "v quads must tile the workgroup");
 
     // LDS map (bytes).  Small fp32 tables first, then region X, which holds
-    // Qd, Kd, Kt while P and L are formed, then P, T, L plus one slot shared
-    // by W^T (block forward substitution only) and the output staging tile
-    // (after the chain only); then the chain operands.
+    // Qd, Kd, Kt while P and L are formed, then P, T, L and the output
+    // staging tile (after the chain only); then the chain operands.
     static constexpr int SZ_TOKD = C * DP * (int)sizeof(T);
     static constexpr int SZ_DTOK = D * CP * (int)sizeof(T);
     static constexpr int SZ_P = C * CP * (int)sizeof(T);
     static constexpr int SZ_L = C * LP * 4;
     static constexpr int SZ_O = C * OP * (int)sizeof(T);
-    static constexpr int SZ_WT = NP > 1 ? SZ_DTOK : 0;
-    static constexpr int SZ_SLOT = SZ_WT > SZ_O ? SZ_WT : SZ_O;
     static constexpr int OFF_GC = 0;
     static constexpr int OFF_F = OFF_GC + D * 4;
     static constexpr int OFF_E = OFF_F + (NOFF > 0 ? NOFF : 1) * D * 4;
     static constexpr int OFF_BETA = OFF_E + NP * NSEG * D * 4;
     static constexpr int OFF_X = (OFF_BETA + C * 4 + 15) / 16 * 16;
     static constexpr int SZ_X1 = 3 * SZ_TOKD;
-    static constexpr int SZ_X2 = 2 * SZ_P + SZ_L + SZ_SLOT;
+    static constexpr int SZ_X2 = 2 * SZ_P + SZ_L + SZ_O;
     static constexpr int SZ_X = SZ_X1 > SZ_X2 ? SZ_X1 : SZ_X2;
     static constexpr int OFF_QD = OFF_X;
     static constexpr int OFF_KD = OFF_QD + SZ_TOKD;
@@ -112,16 +109,14 @@ struct PrefillCfg {
     static constexpr int OFF_P = OFF_X;
     static constexpr int OFF_T = OFF_P + SZ_P;
     static constexpr int OFF_L = OFF_T + SZ_P;
-    static constexpr int OFF_WT = OFF_L + SZ_L;
-    static constexpr int OFF_O = OFF_WT;
-    static constexpr int OFF_QG = OFF_X + SZ_X;
-    static constexpr int OFF_KGBT = OFF_QG + SZ_TOKD;
-    static constexpr int OFF_KHT = OFF_KGBT + SZ_DTOK;
-    static constexpr int OFF_VBT = OFF_KHT + SZ_DTOK;
-    static constexpr int OFF_WN = OFF_VBT + DVB * CP * (int)sizeof(T);
-    static constexpr int LDS_BYTES = OFF_WN + SZ_TOKD;
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget exceeded");
-    static_assert(OFF_WT + SZ_SLOT <= OFF_X + SZ_X, "region X overflow");
+    static constexpr int OFF_O = OFF_L + SZ_L;
+    static constexpr int OFF_QG = OFF_X + SZ_X;             // Q e^G        [token][d]
+    static constexpr int OFF_KG = OFF_QG + SZ_TOKD;         // beta K e^G   [token][d]
+    static constexpr int OFF_KHT = OFF_KG + SZ_TOKD;        // (K e^{G_C-G})^T [d][token]
+    static constexpr int OFF_VBT = OFF_KHT + SZ_DTOK;       // (beta V)^T   [column][token]
+    static constexpr int LDS_BYTES = OFF_VBT + DVB * CP * (int)sizeof(T);
+    static_assert(LDS_BYTES <= 150 * 1024, "LDS budget exceeded");
+    static_assert(OFF_O + SZ_O <= OFF_X + SZ_X, "region X overflow");
 };
 
 // Index of the off-diagonal sub-tile block (p, p'), p' < p, in the F table.
@@ -193,11 +188,9 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
     float *sL = reinterpret_cast<float *>(smem + Cfg::OFF_L);
     T *sO = reinterpret_cast<T *>(smem + Cfg::OFF_O);
     T *sQG = reinterpret_cast<T *>(smem + Cfg::OFF_QG);
-    T *sKGbT = reinterpret_cast<T *>(smem + Cfg::OFF_KGBT);
+    T *sKG = reinterpret_cast<T *>(smem + Cfg::OFF_KG);
     T *sKhT = reinterpret_cast<T *>(smem + Cfg::OFF_KHT);
-    T *sWT = reinterpret_cast<T *>(smem + Cfg::OFF_WT);
     T *sVbT = reinterpret_cast<T *>(smem + Cfg::OFF_VBT);
-    T *sWn = reinterpret_cast<T *>(smem + Cfg::OFF_WN);
     float *sGC = reinterpret_cast<float *>(smem + Cfg::OFF_GC);
     float *sF = reinterpret_cast<float *>(smem + Cfg::OFF_F);
     float *sE = reinterpret_cast<float *>(smem + Cfg::OFF_E);
@@ -287,8 +280,6 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
     constexpr bool kPrefetch = NW >= 4;
     if (kPrefetch && nchunks > 0) load_chunk(0);
 
-    f32x4 Ut[NP];   // U~ rows of each sub-tile for this wave's columns
-
     // state checkpoints: the state after every ckpt_every tokens
     const int every = CKPT ? prm.ckpt_every : 0;   // CKPT: prm.ckpt set, every > 0
     int64_t ck_row = every > 0 ? ckpt_row0(prm.cu, b, prm.T, every) : 0;
@@ -364,12 +355,12 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
             const float itot1 = __builtin_amdgcn_rcpf(tot[sp][1]);
             float rl0 = aft0, rl1 = aft1;   // decay over (r, end of sub-tile]
             // bf16 with whole 8-token groups: the transposed rows d0, d0+1 of
-            // K~ and Kh are packed in registers and written 8 tokens at a time
-            // (one 16-byte store per row instead of eight 2-byte ones, whose
-            // rows 2*cp fell into the same few LDS banks)
+            // Kh are packed in registers and written 8 tokens at a time (one
+            // 16-byte store per row instead of eight 2-byte ones, whose rows
+            // 2*cp fell into the same few LDS banks)
             constexpr bool kPackT = sizeof(T) == 2 && SEGLEN % 8 == 0;
-            uint32_t pg0[4], pg1[4], ph0[4], ph1[4];
-            float ng0 = 0.f, ng1 = 0.f, nh0 = 0.f, nh1 = 0.f;   // token s+1's values
+            uint32_t ph0[4], ph1[4];
+            float nh0 = 0.f, nh1 = 0.f;   // token s+1's values
 #pragma unroll
             for (int s = SEGLEN - 1; s >= 0; --s) {
                 const int r = 16 * sp + sg * SEGLEN + s;
@@ -387,28 +378,20 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
                 store_pair(sKd + r * DP + d0, k0 * F0 * itot0, k1 * F1 * itot1);
                 store_pair(sKt + r * DP + d0, k0 * rl0, k1 * rl1);
                 store_pair(sQG + r * DP + d0, q0 * F0 * pre0, q1 * F1 * pre1);
-                const float g0 = bt * k0 * F0 * pre0, g1 = bt * k1 * F1 * pre1;
+                store_pair(sKG + r * DP + d0, bt * k0 * F0 * pre0, bt * k1 * F1 * pre1);
                 const float h0 = k0 * rl0 * post0, h1 = k1 * rl1 * post1;
                 if constexpr (kPackT) {
                     if (s % 2 == 0) {
-                        pg0[(s / 2) % 4] = pack_pair_bf16(g0, ng0);
-                        pg1[(s / 2) % 4] = pack_pair_bf16(g1, ng1);
                         ph0[(s / 2) % 4] = pack_pair_bf16(h0, nh0);
                         ph1[(s / 2) % 4] = pack_pair_bf16(h1, nh1);
                     }
                     if (s % 8 == 0) {   // tokens r .. r+7 complete
-                        *reinterpret_cast<uint4 *>(sKGbT + d0 * CP + r) = uint4{pg0[0], pg0[1], pg0[2], pg0[3]};
-                        *reinterpret_cast<uint4 *>(sKGbT + (d0 + 1) * CP + r) = uint4{pg1[0], pg1[1], pg1[2], pg1[3]};
                         *reinterpret_cast<uint4 *>(sKhT + d0 * CP + r) = uint4{ph0[0], ph0[1], ph0[2], ph0[3]};
                         *reinterpret_cast<uint4 *>(sKhT + (d0 + 1) * CP + r) = uint4{ph1[0], ph1[1], ph1[2], ph1[3]};
                     }
-                    ng0 = g0;
-                    ng1 = g1;
                     nh0 = h0;
                     nh1 = h1;
                 } else {
-                    sKGbT[d0 * CP + r] = from_f32<T>(g0);
-                    sKGbT[(d0 + 1) * CP + r] = from_f32<T>(g1);
                     sKhT[d0 * CP + r] = from_f32<T>(h0);
                     sKhT[(d0 + 1) * CP + r] = from_f32<T>(h1);
                 }
@@ -527,49 +510,48 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
         }
         lds_barrier();
 
-        // ================= phase D: W and U~ by block forward substitution =
+        // ================= phase D: off-diagonal blocks of T ================
+        // T = (I + L)^-1 is block lower triangular; with its diagonal blocks
+        // from phase C, block row p follows from the rows above:
+        //    T_pj = -T_pp sum_{j <= m < p} L_pm T_mj     (j < p).
+        // One wave forms the NP(NP-1)/2 blocks in order, keeping them in
+        // accumulator layout (the B operand of the next products), and writes
+        // them into sT for the chain.
+        if constexpr (NP > 1) {
+            if (wave == 0) {
+                f32x4 Tblk[NP][NP];   // T_mj, m > j, accumulator layout
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const Frag<T> Tpp = lds_frag(sT + 16 * p * CP, CP, 16 * p, lane);
-            // W_p for the d-tiles of this wave
-            for (int dt = wave; dt < NDT; dt += NW) {
-                f32x4 R;
-                {
-                    const Frag<T> kb = lds_frag(sKGbT + 16 * dt * CP, CP, 16 * p, lane);
+                for (int p = 1; p < NP; ++p) {
+                    const Frag<T> Tpp = lds_frag(sT + 16 * p * CP, CP, 16 * p, lane);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) R[e] = to_f32(kb.v[e]);
-                }
-                for (int j = 0; j < p; ++j) {
-                    const f32x4 lf = *reinterpret_cast<const f32x4 *>(
-                        sL + (16 * p + n) * LP + 16 * j + 4 * g);
-                    mma16(R, frag_from_f32<T>(-lf), lds_frag(sWT + 16 * dt * CP, CP, 16 * j, lane));
-                }
-                f32x4 Wt = {0.f, 0.f, 0.f, 0.f};
-                mma16(Wt, Tpp, acc_frag<T>(R));
+                    for (int j = 0; j < p; ++j) {
+                        f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * p + 4 * g + e, d = 16 * dt + n;
-                    sWn[r * DP + d] = from_f32<T>(-Wt[e]);
-                    if constexpr (NP > 1) sWT[d * CP + r] = from_f32<T>(Wt[e]);
+                        for (int m = j; m < p; ++m) {
+                            // L_pm in A layout: L[16p + n][16m + 4g + e]
+                            const f32x4 lf = *reinterpret_cast<const f32x4 *>(
+                                sL + (16 * p + n) * LP + 16 * m + 4 * g);
+                            Frag<T> tb;   // T_mj in B layout: T[16m + 4g + e][16j + n]
+                            if (m == j) {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    tb.v[e] = sT[(16 * m + 4 * g + e) * CP + 16 * j + n];
+                            } else {
+                                tb = acc_frag<T>(Tblk[m][j]);
+                            }
+                            mma16(X, frag_from_f32<T>(lf), tb);
+                        }
+                        f32x4 R = {0.f, 0.f, 0.f, 0.f};
+                        mma16(R, Tpp, acc_frag<T>(X));
+                        Tblk[p][j] = -R;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sT[(16 * p + 4 * g + e) * CP + 16 * j + n] = from_f32<T>(-R[e]);
+                    }
                 }
             }
-            // U~_p for this wave's 16 value columns
-            {
-                f32x4 R;
-                const Frag<T> vb = lds_frag(sVbT + 16 * wave * CP, CP, 16 * p, lane);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) R[e] = to_f32(vb.v[e]);
-                for (int j = 0; j < p; ++j) {
-                    const f32x4 lf = *reinterpret_cast<const f32x4 *>(
-                        sL + (16 * p + n) * LP + 16 * j + 4 * g);
-                    mma16(R, frag_from_f32<T>(-lf), acc_frag<T>(Ut[j]));
-                }
-                Ut[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-                mma16(Ut[p], Tpp, acc_frag<T>(R));
-            }
-            if constexpr (NP > 1) lds_barrier();
+            lds_barrier();
         }
-        if constexpr (NP == 1) lds_barrier();
 
         // ================= phase E: the state chain (per wave) =============
         {
@@ -582,12 +564,27 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
             // values on MI355X (the compiler inserts no wait states between
             // the two shapes), so mixed-shape sums go through separate
             // accumulators and a VALU add.
+            // U = T (beta V - beta K e^G S): Y rounded once, then the block
+            // lower-triangular product with T
             f32x4 U[NP], O[NP];
+            Frag<T> Yf[NP];
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                U[p] = f32x4{0.f, 0.f, 0.f, 0.f};   // U = U~ - W S  (sWn holds -W)
-                contract_lds_frag<T, D>(U[p], sWn + 16 * p * DP, DP, Sf, lane);
-                U[p] += Ut[p];
+                f32x4 X = {0.f, 0.f, 0.f, 0.f};
+                contract_lds_frag<T, D>(X, sKG + 16 * p * DP, DP, Sf, lane);
+                // beta V[16p + 4g + e][jw + n]
+                const Frag<T> vb = lds_frag(sVbT + 16 * wave * CP, CP, 16 * p, lane);
+                f32x4 Y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Y[e] = to_f32(vb.v[e]) - X[e];
+                Yf[p] = acc_frag<T>(Y);
+            }
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                U[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j <= p; ++j)
+                    mma16(U[p], lds_frag(sT + 16 * p * CP, CP, 16 * j, lane), Yf[j]);
             }
             Frag<T> Uf[NP];
 #pragma unroll
