@@ -489,24 +489,45 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
         lds_barrier();
 
         // ================= phase C: 16 x 16 diagonal inverses ==============
-        // T_pp = (I + L_pp)^-1 by column-wise forward substitution in fp32:
-        // sub-tile p goes to wave p % NW, lane group p / NW, and lane c of
-        // that group owns column c; right-looking updates keep the dependent
-        // chain one FMA per row.
-        static_assert(NP <= 4 * NW, "diagonal blocks must fit the lane groups");
-        if (wave + NW * g < NP) {
-            const int p = wave + NW * g, c = n;
-            const float *Lb = sL + 16 * p * LP + 16 * p;
-            float t[16];
+        // T_pp = (I + L_pp)^-1 by L's nilpotency (L_pp^16 = 0):
+        //    T = (I - L)(I + L^2)(I + L^4)(I + L^8),
+        // nine 16 x 16 MFMA products; wave p % NW takes block p.  An
+        // accumulator tile (lane (g, n) holding X[4g+e][n]) is the B operand
+        // of X and the A operand of X^T, so each product is formed together
+        // with the transpose the next one needs.
+        for (int p = wave; p < NP; p += NW) {
+            const float *Lp = sL + 16 * p * LP + 16 * p;
+            f32x4 Lb, LTb, ImLT;   // L (B layout), L^T (B layout), I - L^T
+            LTb = *reinterpret_cast<const f32x4 *>(Lp + n * LP + 4 * g);   // L[n][4g+e]
 #pragma unroll
-            for (int r = 0; r < 16; ++r) t[r] = r == c ? 1.0f : 0.0f;
-#pragma unroll
-            for (int s = 0; s < 15; ++s) {
-#pragma unroll
-                for (int r = s + 1; r < 16; ++r) t[r] -= Lb[r * LP + s] * t[s];
+            for (int e = 0; e < 4; ++e) {
+                Lb[e] = Lp[(4 * g + e) * LP + n];                             // L[4g+e][n]
+                ImLT[e] = (4 * g + e == n ? 1.0f : 0.0f) - LTb[e];
             }
+            auto mm = [](const Frag<T> &a, const Frag<T> &b) {
+                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+                mma16(d, a, b);
+                return d;
+            };
+            auto plus_i = [&](f32x4 x) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sT[(16 * p + r) * CP + 16 * p + c] = from_f32<T>(t[r]);
+                for (int e = 0; e < 4; ++e) x[e] += (4 * g + e == n) ? 1.0f : 0.0f;
+                return x;
+            };
+            auto fr = [](const f32x4 &x) { return acc_frag<T>(x); };
+            const Frag<T> fL = fr(Lb), fLT = fr(LTb);
+            const f32x4 L2 = mm(fLT, fL), L2T = mm(fL, fLT);           // L^2, (L^2)^T
+            const Frag<T> fL2 = fr(L2), fL2T = fr(L2T);
+            const f32x4 L4 = mm(fL2T, fL2), L4T = mm(fL2, fL2T);       // L^4, (L^4)^T
+            const Frag<T> fL4 = fr(L4), fL4T = fr(L4T);
+            const f32x4 L8 = mm(fL4T, fL4);                            // L^8
+            const f32x4 Y = mm(fr(plus_i(L4T)), fr(plus_i(L8)));       // (I+L^4)(I+L^8)
+            const f32x4 XT = mm(fr(plus_i(L2)), fr(ImLT));             // (I+L^2)^T (I-L)^T
+            const f32x4 TT = mm(fr(Y), fr(XT));                        // T^T = Y^T X^T
+            // lane (g, n) holds T[n][4g+e]: row n, four consecutive columns
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sT[(16 * p + n) * CP + 16 * p + 4 * g + e] = from_f32<T>(TT[e]);
         }
         lds_barrier();
 
