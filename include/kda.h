@@ -126,8 +126,8 @@ kda_status kda_prefill(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
  * fixed by the caller (`dv_per_block` in {16, 32, 64, 128}, dividing dv; 0
  * picks automatically).  Value columns of the state evolve independently, so
  * every choice gives the same result up to rounding order; it only changes
- * how the work is spread over the GPU.  With dk = 128, chunk 64 runs 32 or
- * 64 columns per workgroup (bf16 only); other values return
+ * how the work is spread over the GPU.  With dk = 128, chunk 64 runs 32, 64
+ * or 128 columns per workgroup (bf16 only; 0 picks 128); other values return
  * KDA_ERR_UNSUPPORTED.
  */
 kda_status kda_prefill_ex(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,

@@ -65,12 +65,13 @@ struct PrefillCfg {
     // Row strides.  LDS serves each group of 16 lanes from 32 four-byte banks;
     // a fragment read (16 rows, one 8-byte piece each) is conflict-free when
     // the stride is 2 mod 32 words.  [token][d] tiles take D + 4 elements
-    // (66 words for bf16, 132 for fp32, whose 16-byte pieces need 4 mod 32);
-    // [d][token] tiles are written 16 bytes per row and keep rows 16-byte
-    // aligned (C + 8 bf16 / C + 4 fp32 elements).
+    // (66 words for bf16, 132 for fp32, whose 16-byte pieces need 4 mod 32),
+    // and so do [d][token] / [token][token] tiles (C + 4: 34 words for bf16
+    // at C = 64, 10 at C = 16, 68 for fp32 at C = 64), whose rows are then
+    // only 8-byte aligned.  The output staging tile is read 16 bytes per row.
     static constexpr int PADE = sizeof(T) == 2 ? 8 : 4;
     static constexpr int DP = D + 4;         // row stride of [token][d] tiles
-    static constexpr int CP = C + PADE;      // row stride of [d][token] / [token][token] tiles
+    static constexpr int CP = C + 4;         // row stride of [d][token] / [token][token] tiles
     static constexpr int LP = C + 4;         // row stride of the fp32 L tile
     static constexpr int OP = DVB + PADE;    // row stride of the output staging tile
     static constexpr int NPAIR = D / 2;
@@ -355,8 +356,8 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
             const float itot1 = __builtin_amdgcn_rcpf(tot[sp][1]);
             float rl0 = aft0, rl1 = aft1;   // decay over (r, end of sub-tile]
             // bf16 with whole 8-token groups: the transposed rows d0, d0+1 of
-            // Kh are packed in registers and written 8 tokens at a time (one
-            // 16-byte store per row instead of eight 2-byte ones, whose rows
+            // Kh are packed in registers and written 8 tokens at a time (two
+            // 8-byte stores per row instead of eight 2-byte ones, whose rows
             // 2*cp fell into the same few LDS banks)
             constexpr bool kPackT = sizeof(T) == 2 && SEGLEN % 8 == 0;
             uint32_t ph0[4], ph1[4];
@@ -386,8 +387,10 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
                         ph1[(s / 2) % 4] = pack_pair_bf16(h1, nh1);
                     }
                     if (s % 8 == 0) {   // tokens r .. r+7 complete
-                        *reinterpret_cast<uint4 *>(sKhT + d0 * CP + r) = uint4{ph0[0], ph0[1], ph0[2], ph0[3]};
-                        *reinterpret_cast<uint4 *>(sKhT + (d0 + 1) * CP + r) = uint4{ph1[0], ph1[1], ph1[2], ph1[3]};
+                        *reinterpret_cast<uint2 *>(sKhT + d0 * CP + r) = uint2{ph0[0], ph0[1]};
+                        *reinterpret_cast<uint2 *>(sKhT + d0 * CP + r + 4) = uint2{ph0[2], ph0[3]};
+                        *reinterpret_cast<uint2 *>(sKhT + (d0 + 1) * CP + r) = uint2{ph1[0], ph1[1]};
+                        *reinterpret_cast<uint2 *>(sKhT + (d0 + 1) * CP + r + 4) = uint2{ph1[2], ph1[3]};
                     }
                     nh0 = h0;
                     nh1 = h1;
@@ -721,7 +724,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
 
 #define KDA_PREFILL_CASES(X)                                                             \
     X(bf16, 128, 16, 1) X(bf16, 128, 16, 2) X(bf16, 128, 16, 4) X(bf16, 128, 16, 8)        \
-    X(bf16, 128, 64, 2) X(bf16, 128, 64, 4)                                                \
+    X(bf16, 128, 64, 2) X(bf16, 128, 64, 4) X(bf16, 128, 64, 8)                            \
     X(bf16, 16, 16, 1) X(bf16, 16, 64, 1)                                                  \
     X(float, 128, 16, 1) X(float, 128, 16, 2) X(float, 128, 16, 4)                         \
     X(float, 16, 16, 1) X(float, 16, 64, 1)
@@ -740,8 +743,11 @@ bool prefill_supported(int dtype, int64_t D, int chunk, int dv_per_block) {
 }
 
 int prefill_default_dv_per_block(int dtype, int64_t B, int64_t H, int64_t D, int chunk) {
-    (void)B; (void)H; (void)chunk; (void)dtype;
+    (void)B; (void)H;
     if (D == 16) return 16;
+    // bf16 at 64-token chunks: one 8-wave workgroup per head (two waves per
+    // SIMD, and the key-side work of a chunk is done once per head)
+    if (dtype == dtype_code<bf16>() && D == 128 && chunk == 64) return 128;
     return 64;
 }
 
