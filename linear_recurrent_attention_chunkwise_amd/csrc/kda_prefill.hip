@@ -171,6 +171,18 @@ __device__ __forceinline__ void contract_lds_frag(f32x4 &acc, const T *A, int ld
     }
 }
 
+// Item vi of a thread's share of a chunk's v tile (C tokens x DVB/4 column
+// quads): each group of 64 items is 16 consecutive tokens x 4 quads, so the
+// transposed LDS stores of a wave (rows 4 quads apart, C + 4 elements each)
+// fall into disjoint bank ranges.
+template <int C, int DVB, int NT>
+__device__ __forceinline__ void v_item(int tid, int vi, int &r, int &cq) {
+    const int Q = tid + NT * vi;
+    const int l = Q & 63, grp = Q >> 6;
+    r = 16 * (grp % (C / 16)) + (l & 15);
+    cq = 4 * (grp / (C / 16)) + (l >> 4);
+}
+
 template <typename T, int D, int C, int NW, bool CKPT>
 __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm) {
     using Cfg = PrefillCfg<T, D, C, NW>;
@@ -197,7 +209,8 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
     float *sE = reinterpret_cast<float *>(smem + Cfg::OFF_E);
     float *sBeta = reinterpret_cast<float *>(smem + Cfg::OFF_BETA);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int g = lane >> 4, n = lane & 15;
 
     // Workgroup -> (b, h, value-column slice); the slices of one head share
@@ -266,8 +279,8 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
         }
 #pragma unroll
         for (int vi = 0; vi < VQ; ++vi) {
-            const int Q = tid + NT * vi;
-            const int r = Q / (DVB / 4), cq = Q % (DVB / 4);
+            int r, cq;
+            v_item<C, DVB, NT>(tid, vi, r, cq);
             const int64_t t = t0 + r < Tn ? t0 + r : Tn - 1;
             rv[vi] = *reinterpret_cast<const Quad *>(gv + base + t * tok_stride + j0 + 4 * cq);
         }
@@ -423,8 +436,8 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
         // beta * v, transposed to [column][token]
 #pragma unroll
         for (int vi = 0; vi < VQ; ++vi) {
-            const int Q = tid + NT * vi;
-            const int r = Q / (DVB / 4), cq = Q % (DVB / 4);
+            int r, cq;
+            v_item<C, DVB, NT>(tid, vi, r, cq);
             const float bt = sBeta[r];
             float vv[4];
             if constexpr (sizeof(T) == 2) {
@@ -447,6 +460,9 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
         if (kPrefetch && ch + 1 < nchunks) load_chunk(t0 + C);
 
         // ================= phase B: P and L sub-tile blocks ================
+        // Block (p, pq) of P and of L on one wave: they share the column-side
+        // fragments (scaled by F_{p,pq} off the diagonal); the contraction
+        // over the D channels runs on 16x16x32 MFMAs.
         f32x4 accP[Cfg::BPW], accL[Cfg::BPW];
 #pragma unroll
         for (int bi = 0; bi < Cfg::BPW; ++bi) {
@@ -462,12 +478,25 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
                 const T *Ak = sKd + 16 * p * DP;
                 const T *Bk = sKt + 16 * pq * DP;
                 const float *Fs = pq < p ? sF + off_index(p, pq) * D : nullptr;
-#pragma unroll
-                for (int kk = 0; kk < D; kk += 16) {
+                auto bfrag = [&](int kk) {
                     Frag<T> bf = lds_frag(Bk, DP, kk, lane);
                     if (Fs) bf = frag_scaled(bf, *reinterpret_cast<const f32x4 *>(Fs + kk + 4 * g));
-                    mma16(accP[bi], lds_frag(Aq, DP, kk, lane), bf);
-                    mma16(accL[bi], lds_frag(Ak, DP, kk, lane), bf);
+                    return bf;
+                };
+                if constexpr (D % 32 == 0) {
+#pragma unroll
+                    for (int kk = 0; kk < D; kk += 32) {
+                        const Frag<T> b0 = bfrag(kk), b1 = bfrag(kk + 16);
+                        mma32(accP[bi], lds_frag(Aq, DP, kk, lane), lds_frag(Aq, DP, kk + 16, lane), b0, b1);
+                        mma32(accL[bi], lds_frag(Ak, DP, kk, lane), lds_frag(Ak, DP, kk + 16, lane), b0, b1);
+                    }
+                } else {
+#pragma unroll
+                    for (int kk = 0; kk < D; kk += 16) {
+                        const Frag<T> bf = bfrag(kk);
+                        mma16(accP[bi], lds_frag(Aq, DP, kk, lane), bf);
+                        mma16(accL[bi], lds_frag(Ak, DP, kk, lane), bf);
+                    }
                 }
             }
         }
@@ -479,13 +508,16 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
                 int p = 0;
                 while ((p + 1) * (p + 2) / 2 <= blk) ++p;
                 const int pq = blk - p * (p + 1) / 2;
+                // beta of rows 4g..4g+3, read once and unconditionally: a read
+                // under the strict-lower mask made every store wait on it
+                const f32x4 bt4 = *reinterpret_cast<const f32x4 *>(sBeta + 16 * p + 4 * g);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * p + 4 * g + e, s = 16 * pq + n;
                     const bool lower = pq < p || s <= r;
                     const bool strict = pq < p || s < r;
                     sP[r * CP + s] = from_f32<T>(lower ? accP[bi][e] : 0.0f);
-                    sL[r * LP + s] = strict ? sBeta[r] * accL[bi][e] : 0.0f;
+                    sL[r * LP + s] = strict ? bt4[e] * accL[bi][e] : 0.0f;
                 }
             }
         }
