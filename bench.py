@@ -29,10 +29,11 @@ included), read from the kernel's summary under profiles/.
 ``long`` times the long-context (B1 H96 T65536, z ~ N(2,1)) and million-token
 (B1 H16 T2^20) prefill workloads at 64- and 16-token chunks over 3 launches
 each, inputs drawn on the device; the million-token head share also split
-into 4 and 8 segments (kda_prefill_split).  Each entry's ``roofline.traffic``
-is the HBM bytes per call from its counter summary under profiles/ (for a
-split call, both passes), null once the kernel source has changed.  ``timing`` gives the median and minimum
-per-launch time of 10 equal segments of the timed steps.
+into 4, 8 and 9 segments at 16-token chunks and 9 at 64 (kda_prefill_split).
+Each entry's ``roofline.traffic`` is the HBM bytes per call from its counter
+summary under profiles/ (for a split call, both passes), null once the kernel
+source has changed.  ``timing`` gives the median and minimum per-launch time
+of 10 equal segments of the timed steps.
 
 ``backward`` times kda_prefill_bwd_ex on the same workload: gradients of q,
 k, v, z, beta, A and S0 from seeded dL/do and dL/dS_T (the forward is rerun
@@ -355,7 +356,7 @@ def cpu_baseline(w, inp_cpu):
 LONG_CASES = [("long_prefill_bf16", 64, 1), ("long_prefill_bf16", 16, 1),
               ("million_prefill_bf16", 64, 1), ("million_prefill_bf16", 16, 1),
               ("million_prefill_bf16", 16, 4), ("million_prefill_bf16", 16, 8),
-              ("million_prefill_bf16", 16, 9)]
+              ("million_prefill_bf16", 16, 9), ("million_prefill_bf16", 64, 9)]
 
 
 def time_backward(torch, kda, inp, dO, dST, steps, warmup):
@@ -402,9 +403,9 @@ def time_long(torch, kda, steps):
         b = prefill_bytes(w.B, w.T, w.H, w.dk)
         key = f"{name}_c{chunk}" + (f"_split{segments}" if segments > 1 else "")
         kernel = prefill_kernel_name(chunk)
-        if segments > 1:   # the split call's two passes of the role-split kernel
-            traffic = recorded_counter(kernel, f"kda_prefill_split_{name}.md",
-                                       f"traffic_bytes_per_launch_split{segments}")
+        if segments > 1:   # the split call's two passes of the prefill kernel
+            summary = f"kda_prefill_split_{name}" + ("" if chunk == 16 else f"_c{chunk}") + ".md"
+            traffic = recorded_counter(kernel, summary, f"traffic_bytes_per_launch_split{segments}")
         else:
             traffic = recorded_traffic(kernel, f"{kernel}_{name}_c{chunk}.md")
         res[key] = {

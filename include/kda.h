@@ -220,15 +220,18 @@ kda_status kda_prefill_varlen_noalloc(int dtype, int64_t N, int64_t T_total, int
  * alone cannot (a head share of a long context: e.g. H = 16, T = 2^20).  Each
  * sequence is cut into `segments` pieces of L = ceil(T / segments) tokens
  * rounded up to a whole chunk (trailing pieces may be empty); the call runs
- * (1) M and N of every piece but the last of its sequence, in one pass that
- * shares the per-chunk preparation between them, (2) the pieces' start states
- * by the scan S_{j+1} = M_j S_j + N_j in fp32, (3) every piece from its start
+ * (1) in one launch, the prefill of each sequence's first piece from S0 and M
+ * and N of every piece between the first and the last (chunk 16: M and N of a
+ * piece share one pass over its per-chunk preparation; chunk 64: they are
+ * runs of their own), (2) the pieces' start states by the scan
+ * S_{j+1} = M_j S_j + N_j in fp32, (3) every other piece from its start
  * state.  It costs about two prefills of work spread over B*H*segments
- * units.
+ * units (chunk 64: up to three).
  *
  * Arguments and results as kda_prefill (o, S_T identical in meaning; S_T may
- * be S0).  Supported: bf16, dk = dv = 128, chunk 16, 1 <= segments <= 1024
- * (1: the plain prefill).  workspace: kda_prefill_split_workspace_size bytes,
+ * be S0).  Supported: bf16, dk = dv = 128, chunk 16 or 64,
+ * 1 <= segments <= 1024 (1: the plain prefill).  workspace:
+ * kda_prefill_split_workspace_size bytes,
  * 16-byte aligned, not overlapping any other argument; scratch (calls sharing
  * it must not overlap).  The result equals the unsplit call's up to rounding
  * (the start states pass through bf16-rounded products once more).

@@ -669,16 +669,18 @@ bool split_layout(int64_t B, int64_t H, int64_t D, int P, SplitLayout *lay) {
     return true;
 }
 
-// Arguments of one role-split prefill run over segments of a split call
-// (whose arguments were validated on entry): `nseq` segments of the packing
-// `cu`, rank r running segment order[r]; S0, S_T, S_T2 indexed by segment.
-kda::PrefillArgs split_args(int64_t nseq, int64_t Ttot, int64_t H, const int64_t *cu,
+// Arguments of one prefill run over segments of a split call (whose
+// arguments were validated on entry): `nseq` segments of the packing `cu`,
+// rank r running segment order[r]; S0, S_T, S_T2 indexed by segment.  Chunk
+// 16 runs the role-split kernel at 64 columns per workgroup, chunk 64 the
+// general kernel at 128.
+kda::PrefillArgs split_args(int chunk, int64_t nseq, int64_t Ttot, int64_t H, const int64_t *cu,
                             const int32_t *order, const void *q, const void *k, const void *v,
                             const void *z, const void *beta, const float *A, const float *S0,
                             void *o, float *S_T, float *S_T2, int mode, hipStream_t stream) {
     kda::PrefillArgs a;
-    a.dtype = KDA_BF16; a.B = nseq; a.T = Ttot; a.H = H; a.D = 128; a.chunk = 16;
-    a.dv_per_block = 64;
+    a.dtype = KDA_BF16; a.B = nseq; a.T = Ttot; a.H = H; a.D = 128; a.chunk = chunk;
+    a.dv_per_block = chunk == 16 ? 64 : 128;
     a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.A = A; a.S0 = S0;
     a.o = o; a.S_T = S_T; a.S_T2 = S_T2;
     a.cu_seqlens = cu;
@@ -696,8 +698,8 @@ extern "C" {
 size_t kda_prefill_split_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
                                         int64_t dv, int32_t chunk, int32_t segments) {
     (void)T;
-    if (dtype != KDA_BF16 || dk != 128 || dv != 128 || chunk != 16 || B < 0 || H < 0 ||
-        segments < 1 || segments > kMaxSegments)
+    if (dtype != KDA_BF16 || dk != 128 || dv != 128 || (chunk != 16 && chunk != 64) || B < 0 ||
+        H < 0 || segments < 1 || segments > kMaxSegments)
         return 0;
     if (segments == 1) return 0;
     SplitLayout lay;
@@ -711,15 +713,17 @@ kda_status kda_prefill_split(int dtype, int64_t B, int64_t T, int64_t H, int64_t
                              size_t workspace_bytes, void *stream) {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
     if (segments < 1 || segments > kMaxSegments) return KDA_ERR_UNSUPPORTED;
-    if (dtype != KDA_BF16 || dk != 128 || dv != 128 || chunk != 16) return KDA_ERR_UNSUPPORTED;
+    if (dtype != KDA_BF16 || dk != 128 || dv != 128 || (chunk != 16 && chunk != 64))
+        return KDA_ERR_UNSUPPORTED;
+    const int dvb = chunk == 16 ? 64 : 128;
     // every check of the plain call on the caller's arguments
     kda_status st = prefill_impl(dtype, B, T, H, dk, dv, chunk, nullptr, q, k, v, z, beta, A, S0,
-                                 o, S_T, 0, nullptr, 0, nullptr, 0, stream, 64, 0, true);
+                                 o, S_T, 0, nullptr, 0, nullptr, 0, stream, dvb, 0, true);
     if (st != KDA_OK) return st;
     const int P = segments;
     if (P == 1)
         return prefill_impl(dtype, B, T, H, dk, dv, chunk, nullptr, q, k, v, z, beta, A, S0, o,
-                            S_T, 0, nullptr, 0, nullptr, 0, stream, 64);
+                            S_T, 0, nullptr, 0, nullptr, 0, stream, dvb);
     SplitLayout lay;
     if (!split_layout(B, H, dk, P, &lay)) return KDA_ERR_SHAPE;
     // segments; the passes' grids hold at most 4096 work-items per (segment,
@@ -755,18 +759,29 @@ kda_status kda_prefill_split(int dtype, int64_t B, int64_t T, int64_t H, int64_t
     // (1) one launch: the first segment of each sequence from S0 (its final
     // state is the second segment's start), beside the maps M (from I, v as
     // zero) and offsets N (from 0) of the segments between first and last
-    const kda::PrefillArgs a0 = split_args(B, Ttot, H, cu, lists, q, k, v, z, beta, A,
+    const kda::PrefillArgs a0 = split_args(chunk, B, Ttot, H, cu, lists, q, k, v, z, beta, A,
                                            S0 ? Sb : nullptr, o, Sb + per, nullptr, 0, s);
-    const kda::PrefillArgs a2 = split_args(B * (P - 2), Ttot, H, cu, lists + B, q, k, v, z, beta,
-                                           A, nullptr, nullptr, Mb, Nb, 2, s);
-    if (kda::launch_prefill16_split_head(a0, a2) != hipSuccess) return KDA_ERR_HIP;
+    if (chunk == 16) {   // M and N on one prep (role-split kernel, mode 2)
+        const kda::PrefillArgs a2 = split_args(chunk, B * (P - 2), Ttot, H, cu, lists + B, q, k,
+                                               v, z, beta, A, nullptr, nullptr, Mb, Nb, 2, s);
+        if (kda::launch_prefill16_split_head(a0, a2) != hipSuccess) return KDA_ERR_HIP;
+    } else {             // N (mode 1 from zero) and M (mode 3) as runs of their own
+        const kda::PrefillArgs a[3] = {
+            a0,
+            split_args(chunk, B * (P - 2), Ttot, H, cu, lists + B, q, k, v, z, beta, A, nullptr,
+                       nullptr, Nb, nullptr, 1, s),
+            split_args(chunk, B * (P - 2), Ttot, H, cu, lists + B, q, k, v, z, beta, A, nullptr,
+                       nullptr, Mb, nullptr, 3, s)};
+        if (kda::launch_prefill_multi(a) != hipSuccess) return KDA_ERR_HIP;
+    }
     // (2) start states of segments 2 .. P-1
     if (kda::launch_split_scan(Mb, Nb, Sb, B, H, P, (int)dk, s) != hipSuccess)
         return KDA_ERR_HIP;
     // (3) segments 1 .. P-1 from their start states; final states go to Mb
-    const kda::PrefillArgs a3 = split_args(B * (P - 1), Ttot, H, cu, lists + B + B * (P - 2), q,
-                                           k, v, z, beta, A, Sb, o, Mb, nullptr, 0, s);
-    if (kda::launch_prefill16(a3) != hipSuccess) return KDA_ERR_HIP;
+    const kda::PrefillArgs a3 = split_args(chunk, B * (P - 1), Ttot, H, cu, lists + B + B * (P - 2),
+                                           q, k, v, z, beta, A, Sb, o, Mb, nullptr, 0, s);
+    if ((chunk == 16 ? kda::launch_prefill16(a3) : kda::launch_prefill(a3)) != hipSuccess)
+        return KDA_ERR_HIP;
     return kda::launch_split_gather(Mb, S_T, B, H, P, (int)dk, s) == hipSuccess ? KDA_OK
                                                                                 : KDA_ERR_HIP;
 }

@@ -39,9 +39,11 @@ struct PrefillArgs {
     bool ckpt_blocked = false;
     // 0: the prefill.  1: final states only (o not written).  2: the affine
     // state map S_end = M S_start + N of each sequence in one pass (M to S_T,
-    // N -- the final state from S0, or zero -- to S_T2; o not written).  Modes
-    // 1 and 2 exist for the role-split kernel at 64 columns (checkpoints in
-    // mode 1 only).
+    // N -- the final state from S0, or zero -- to S_T2; o not written).
+    // 3: M alone (the state starts at the identity, v is read as zero; M to
+    // S_T; o not written).  Modes 1 and 2 run on the role-split kernel at 64
+    // columns (checkpoints in mode 1 only); modes 1 and 3 on the general kernel
+    // through launch_prefill_multi.
     int mode = 0;
     hipStream_t stream;
 };
@@ -98,6 +100,9 @@ bool prefill_supported(int dtype, int64_t D, int chunk, int dv_per_block);
 // Default value columns per workgroup for these sizes.
 int prefill_default_dv_per_block(int dtype, int64_t B, int64_t H, int64_t D, int chunk);
 hipError_t launch_prefill(const PrefillArgs &a);
+// Three general-kernel runs (bf16, d = 128, 64-token chunks, 128 columns per
+// workgroup, modes 0, 1 or 3, no checkpoints) in one launch.
+hipError_t launch_prefill_multi(const PrefillArgs *a);
 // Whether the general kernel takes state checkpoints for this configuration.
 bool prefill_ckpt_supported(int dtype, int64_t D, int chunk, int dv_per_block);
 // Role-split variant for bf16, D = 128, chunk 16 (kda_prefill16.hip).

@@ -54,6 +54,7 @@ struct PrefillParams {
     float *ckpt;         // state checkpoints [n_ckpt, H, D, D], or NULL
     int64_t n_ckpt;
     int ckpt_every;      // tokens between checkpoints (0: none)
+    int mode;            // 0: prefill; 1: final states only; 3: the state map M
 };
 
 template <typename T, int D, int C, int NW>
@@ -183,8 +184,14 @@ __device__ __forceinline__ void v_item(int tid, int vi, int &r, int &cq) {
     cq = 4 * (grp / (C / 16)) + (l >> 4);
 }
 
+// One workgroup's share: sequence, head and value-column slice from block
+// `blk` of `nblk`.  prm.mode: 0 the prefill; 1 final states only (o is not
+// written); 3 the linear part M of the segment's affine state map
+// S_end = M S_start + N (the state starts at the identity and v is read as
+// zero; M goes to S_T; o is not written).
 template <typename T, int D, int C, int NW, bool CKPT>
-__global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm) {
+__device__ __forceinline__ void prefill_block(const PrefillParams &prm, char *smem, int64_t blk,
+                                              int64_t nblk) {
     using Cfg = PrefillCfg<T, D, C, NW>;
     using Pair = typename PairOf<T>::type;
     constexpr int NT = Cfg::NT, DVB = Cfg::DVB, NP = Cfg::NP, NDT = Cfg::NDT;
@@ -192,7 +199,6 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
     constexpr int NSEG = Cfg::NSEG, SEGLEN = Cfg::SEGLEN, IPT = Cfg::IPT, NPAIR = Cfg::NPAIR;
     constexpr int VQ = Cfg::VQ;
 
-    __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
     T *sQd = reinterpret_cast<T *>(smem + Cfg::OFF_QD);
     T *sKd = reinterpret_cast<T *>(smem + Cfg::OFF_KD);
     T *sKt = reinterpret_cast<T *>(smem + Cfg::OFF_KT);
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
     // Workgroup -> (b, h, value-column slice); the slices of one head share
     // an XCD (and its L2), which dedupes their reads of q, k, z.
     const int64_t H = prm.H;
-    const BlockMap bm = block_map(blockIdx.x, gridDim.x, prm.nsplit, H, prm.order);
+    const BlockMap bm = block_map(blk, nblk, prm.nsplit, H, prm.order);
     const int64_t b = bm.b;
     const int split = bm.split;
     const int64_t bh = b * H + bm.h;
@@ -238,8 +244,15 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
     const float c2 = -__builtin_amdgcn_exp2f(prm.A[h] * kLog2e) * kLog2e;
 
     // ---- state slice: S[16 i + 4 g + e][jw + n] -------------------------
+    const bool want_o = prm.mode == 0;   // modes 1 and 3 write final states only
+    const bool vzero = prm.mode == 3;    // the map M: v read as zero
     f32x4 S[NDT];
-    if (prm.S0) {
+    if (prm.mode == 3) {   // the identity
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[i][e] = 16 * i + 4 * g + e == jw + n ? 1.0f : 0.0f;
+    } else if (prm.S0) {
         const float *s0 = prm.S0 + bh * (int64_t)(D * D);
 #pragma unroll
         for (int i = 0; i < NDT; ++i)
@@ -277,12 +290,14 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
                 rb[ii][s] = gbeta[bbase + t * H];
             }
         }
+        if (!vzero) {
 #pragma unroll
-        for (int vi = 0; vi < VQ; ++vi) {
-            int r, cq;
-            v_item<C, DVB, NT>(tid, vi, r, cq);
-            const int64_t t = t0 + r < Tn ? t0 + r : Tn - 1;
-            rv[vi] = *reinterpret_cast<const Quad *>(gv + base + t * tok_stride + j0 + 4 * cq);
+            for (int vi = 0; vi < VQ; ++vi) {
+                int r, cq;
+                v_item<C, DVB, NT>(tid, vi, r, cq);
+                const int64_t t = t0 + r < Tn ? t0 + r : Tn - 1;
+                rv[vi] = *reinterpret_cast<const Quad *>(gv + base + t * tok_stride + j0 + 4 * cq);
+            }
         }
     };
 
@@ -391,7 +406,7 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
                 store_pair(sQd + r * DP + d0, q0 * F0 * itot0, q1 * F1 * itot1);
                 store_pair(sKd + r * DP + d0, k0 * F0 * itot0, k1 * F1 * itot1);
                 store_pair(sKt + r * DP + d0, k0 * rl0, k1 * rl1);
-                store_pair(sQG + r * DP + d0, q0 * F0 * pre0, q1 * F1 * pre1);
+                if (want_o) store_pair(sQG + r * DP + d0, q0 * F0 * pre0, q1 * F1 * pre1);
                 store_pair(sKG + r * DP + d0, bt * k0 * F0 * pre0, bt * k1 * F1 * pre1);
                 const float h0 = k0 * rl0 * post0, h1 = k1 * rl1 * post1;
                 if constexpr (kPackT) {
@@ -452,7 +467,7 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
             const bool valid = t0 + r < Tn;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                sVbT[(4 * cq + e) * CP + r] = from_f32<T>(valid ? bt * vv[e] : 0.0f);
+                sVbT[(4 * cq + e) * CP + r] = from_f32<T>(valid && !vzero ? bt * vv[e] : 0.0f);
         }
         lds_barrier();
 
@@ -645,15 +660,18 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
             Frag<T> Uf[NP];
 #pragma unroll
             for (int p = 0; p < NP; ++p) Uf[p] = acc_frag<T>(U[p]);
+            // O = (Q e^G) S + P U, from the entering state's bf16 image Sf
+            if (want_o) {
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                O[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-                contract_lds_frag<T, D>(O[p], sQG + 16 * p * DP, DP, Sf, lane);
-                f32x4 Opu = {0.f, 0.f, 0.f, 0.f};
+                for (int p = 0; p < NP; ++p) {
+                    O[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    contract_lds_frag<T, D>(O[p], sQG + 16 * p * DP, DP, Sf, lane);
+                    f32x4 Opu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j <= p; ++j)
-                    mma16(Opu, lds_frag(sP + 16 * p * CP, CP, 16 * j, lane), Uf[j]);
-                O[p] += Opu;
+                    for (int j = 0; j <= p; ++j)
+                        mma16(Opu, lds_frag(sP + 16 * p * CP, CP, 16 * j, lane), Uf[j]);
+                    O[p] += Opu;
+                }
             }
             // S <- e^{G_C} * S + Kh^T U
 #pragma unroll
@@ -665,14 +683,16 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
                     mma16(S[i], lds_frag(sKhT + 16 * i * CP, CP, 16 * j, lane), Uf[j]);
             }
             // stage O for coalesced stores
+            if (want_o) {
 #pragma unroll
-            for (int p = 0; p < NP; ++p)
+                for (int p = 0; p < NP; ++p)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sO[(16 * p + 4 * g + e) * OP + 16 * wave + n] = from_f32<T>(O[p][e]);
+                    for (int e = 0; e < 4; ++e)
+                        sO[(16 * p + 4 * g + e) * OP + 16 * wave + n] = from_f32<T>(O[p][e]);
+            }
         }
         lds_barrier();
-        {
+        if (want_o) {
             constexpr int E16 = 16 / (int)sizeof(T);
             constexpr int CPR = DVB / E16;          // 16-byte pieces per row
             const int64_t nvalid = Tn - t0 < C ? Tn - t0 : C;
@@ -712,6 +732,30 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm)
         for (int e = 0; e < 4; ++e) sT_out[(16 * i + 4 * g + e) * D + jw + n] = S[i][e];
 }
 
+template <typename T, int D, int C, int NW, bool CKPT>
+__global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(PrefillParams prm) {
+    __shared__ __attribute__((aligned(16))) char smem[PrefillCfg<T, D, C, NW>::LDS_BYTES];
+    prefill_block<T, D, C, NW, CKPT>(prm, smem, blockIdx.x, gridDim.x);
+}
+
+// Three independent runs in one launch (the first pass of a sequence split):
+// blocks [0, n0) run p0, [n0, n0 + n1) p1 and the rest p2, so that together
+// they fill the chip.
+template <typename T, int D, int C, int NW>
+__global__ __launch_bounds__(64 * NW) void kda_prefill_multi_kernel(PrefillParams p0,
+                                                                    PrefillParams p1,
+                                                                    PrefillParams p2, int n0,
+                                                                    int n1) {
+    __shared__ __attribute__((aligned(16))) char smem[PrefillCfg<T, D, C, NW>::LDS_BYTES];
+    const int x = blockIdx.x;
+    if (x < n0)
+        prefill_block<T, D, C, NW, false>(p0, smem, x, n0);
+    else if (x < n0 + n1)
+        prefill_block<T, D, C, NW, false>(p1, smem, x - n0, n1);
+    else
+        prefill_block<T, D, C, NW, false>(p2, smem, x - n0 - n1, (int)gridDim.x - n0 - n1);
+}
+
 // Longest-first ranking of packed sequences: sequence j gets the rank
 // #{i : L_i > L_j, or L_i == L_j and i < j}, and order[rank] = j.  One thread
 // per sequence, O(N) each; lengths are the clamped ranges the prefill uses.
@@ -735,8 +779,8 @@ bool prefill_ckpt_supported(int dtype, int64_t D, int chunk, int dv_per_block) {
     return true;
 }
 
-template <typename T, int D, int C, int NW>
-static hipError_t launch_prefill_t(const PrefillArgs &a) {
+template <int D, int NW>
+static PrefillParams prefill_params(const PrefillArgs &a) {
     PrefillParams prm;
     prm.q = a.q; prm.k = a.k; prm.v = a.v; prm.z = a.z; prm.beta = a.beta;
     prm.A = a.A; prm.S0 = a.S0; prm.o = a.o; prm.S_T = a.S_T;
@@ -744,6 +788,13 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
     prm.cu = a.cu_seqlens; prm.order = a.order; prm.ckpt = a.ckpt; prm.n_ckpt = a.n_ckpt;
     prm.ckpt_every = a.ckpt_every;
     prm.nsplit = (int)(D / (16 * NW));
+    prm.mode = a.mode;
+    return prm;
+}
+
+template <typename T, int D, int C, int NW>
+static hipError_t launch_prefill_t(const PrefillArgs &a) {
+    const PrefillParams prm = prefill_params<D, NW>(a);
     const int64_t nblk = a.B * a.H * prm.nsplit;
     if (a.ckpt != nullptr && a.ckpt_every > 0)
         hipLaunchKernelGGL((kda_prefill_kernel<T, D, C, NW, true>), dim3((unsigned)nblk),
@@ -787,6 +838,22 @@ hipError_t launch_seq_order(const int64_t *cu, int64_t N, int64_t T, int32_t *or
                             hipStream_t stream) {
     const unsigned nb = (unsigned)((N + 255) / 256);
     hipLaunchKernelGGL(kda_seq_order_kernel, dim3(nb), dim3(256), 0, stream, cu, N, T, order);
+    return hipGetLastError();
+}
+
+// bf16, d = 128, 64-token chunks, 128 columns per workgroup: runs a[0..3)
+// (modes 0, 1 or 3, no checkpoints) in one launch.
+hipError_t launch_prefill_multi(const PrefillArgs *a) {
+    for (int i = 0; i < 3; ++i)
+        if (a[i].dtype != dtype_code<bf16>() || a[i].D != 128 || a[i].chunk != 64 ||
+            a[i].dv_per_block != 128 || a[i].ckpt != nullptr || a[i].H != a[0].H ||
+            (a[i].mode != 0 && a[i].mode != 1 && a[i].mode != 3))
+            return hipErrorInvalidValue;
+    const int64_t n0 = a[0].B * a[0].H, n1 = a[1].B * a[1].H, n2 = a[2].B * a[2].H;
+    if (n0 + n1 + n2 == 0) return hipSuccess;
+    hipLaunchKernelGGL((kda_prefill_multi_kernel<bf16, 128, 64, 8>), dim3((unsigned)(n0 + n1 + n2)),
+                       dim3(512), 0, a[0].stream, prefill_params<128, 8>(a[0]),
+                       prefill_params<128, 8>(a[1]), prefill_params<128, 8>(a[2]), (int)n0, (int)n1);
     return hipGetLastError();
 }
 

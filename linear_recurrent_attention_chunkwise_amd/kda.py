@@ -161,7 +161,7 @@ def prefill(q, k, v, z, beta, A, S0=None, chunk: int = 16, out=None, S_T=None,
     ``S_T`` may be given preallocated (``S_T`` may be ``S0`` itself).
     ``segments`` > 1 splits every sequence into that many pieces run in
     parallel and combined through their state maps (kda_prefill_split; bf16,
-    d = 128, chunk 16); ``workspace`` may then be a preallocated uint8 cuda
+    d = 128, chunk 16 or 64); ``workspace`` may then be a preallocated uint8 cuda
     tensor of ``prefill_split_workspace_size`` bytes."""
     lib = _load()
     if q.dim() != 4:

@@ -328,7 +328,7 @@ def test_split_argument_errors(lib):
     assert split(lib, P=0) == UNSUP
     assert split(lib, P=1025) == UNSUP
     assert split(lib, dtype=F32) == UNSUP            # the role-split kernel only
-    assert split(lib, chunk=64) == UNSUP
+    assert split(lib, chunk=32) == UNSUP
     assert split(lib, dk=16, dv=16) == UNSUP
     assert split(lib, ptrs={"z": None}) == NULL
     assert split(lib, ptrs={"ws": None}) == WORKSPACE
@@ -342,6 +342,10 @@ def test_split_argument_errors(lib):
     assert n >= 3 * 4 * 2 * 128 * 128 * 4
     assert lib.kda_prefill_split_workspace_size(BF16, 1, 4096, 2, 128, 128, 16, 1) == 0
     assert lib.kda_prefill_split_workspace_size(F32, 1, 4096, 2, 128, 128, 16, 4) == 0
+    assert lib.kda_prefill_split_workspace_size(BF16, 1, 4096, 2, 128, 128, 64, 4) == n
+    assert lib.kda_prefill_split_workspace_size(BF16, 1, 4096, 2, 128, 128, 32, 4) == 0
+    assert split(lib, chunk=64, ptrs={"ws": None}) == WORKSPACE
+    assert split(lib, chunk=64, B=0) == OK
 
 
 def conv_varlen(lib, dtype=BF16, N=3, T=64, H=2, dk=128, dv=128, conv=None, sin=None,

@@ -3,7 +3,8 @@ GPU's share of a context of 1,048,576 tokens (the context length stated for
 K3 in "Kimi K3 Open Weights: What Is Actually New", section "Start with the
 released configuration").
 
-Both chunk lengths and the 8-segment sequence split are compared with the
+Both chunk lengths and the sequence split at each (8 segments at chunk 16,
+9 at chunk 64) are compared with the
 fp64 oracle over the FULL length on two heads (the oracle runs segment by
 segment with the state carried across, which the split invariant pins on the
 oracle itself), normwise per head at the bf16 tolerance 2e-2.  On top of
@@ -86,20 +87,23 @@ def _head_relerr(x, ref):
     return worst
 
 
-def test_million_token_split(kda, gpu_device, million):
-    """Split into 8 segments (256 workgroups instead of 32): against the
-    oracle on the two full-length heads, against the unsplit run on all 16
+@pytest.mark.parametrize("chunk,P", [(16, 8), (64, 9)])
+def test_million_token_split(kda, gpu_device, million, chunk, P):
+    """Split into P segments (chunk 16: 256 workgroups instead of 32; chunk
+    64: 240 in the first pass and 128 in the second instead of 16): against
+    the oracle on the two full-length heads, against the unsplit run on all 16
     heads, and the first segment bit for bit (it starts from S0 itself)."""
     w, inp, o_ref, S_ref = million
-    _say("[million] split into 8 segments, chunk 16")
+    _say(f"[million] split into {P} segments, chunk {chunk}")
     o, S_T = kda.prefill(inp["q"], inp["k"], inp["v"], inp["z"], inp["beta"], inp["A"],
-                         inp["S0"], chunk=16, segments=8)
+                         inp["S0"], chunk=chunk, segments=P)
     torch.cuda.synchronize()
-    _against_oracle(o, S_T, o_ref, S_ref, "8 segments vs oracle")
-    o0, S0_ = gpu_prefill(kda, inp, 16, dv_per_block=64)
-    L = w.T // 8
+    _against_oracle(o, S_T, o_ref, S_ref, f"{P} segments vs oracle")
+    o0, S0_ = gpu_prefill(kda, inp, chunk, dv_per_block=64 if chunk == 16 else 128)
+    L = -(-w.T // P)
+    L = -(-L // chunk) * chunk   # segment length: a whole number of chunks
     assert torch.equal(o[:, :L], o0[:, :L])
     eo = _head_relerr(o, o0)
     es = slice_relerr(host(S_T), host(S0_), 1)
-    _say(f"   8 segments vs unsplit, all heads: o {eo:.3e}  S_T {es:.3e}")
+    _say(f"   {P} segments vs unsplit, all heads: o {eo:.3e}  S_T {es:.3e}")
     assert eo <= 2e-2 and es <= 2e-2
