@@ -74,7 +74,10 @@ typedef enum kda_status {
                               * element counts, or a launch's work-items, which a
                               * dispatch counts in 32 bits: B*H heads above ~1 M
                               * for prefill, ~8.4 M for decode, B*H*ceil(T/16)
-                              * above ~4.2 M for the backward) is too large     */
+                              * above ~4.2 M for the backward) is too large, or
+                              * 64 tokens' rows (64*H*d elements) of the
+                              * prefill, prologue or backward inputs pass
+                              * 2^31 bytes (bf16, d = 128: H above 131,071)    */
     KDA_ERR_UNSUPPORTED = 3, /* dtype / head size / chunk outside the set      */
     KDA_ERR_MISALIGNED = 4,  /* a pointer is not 16-byte aligned               */
     KDA_ERR_ALIAS = 5,       /* outputs overlap inputs (other than S_T == S0)  */

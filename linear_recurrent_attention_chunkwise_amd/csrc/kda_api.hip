@@ -18,6 +18,13 @@ namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 62;
 
+// The kernels read a tile of up to 64 consecutive tokens (rows of H*D
+// elements) through one buffer resource with 32-bit offsets: such a tile
+// must stay below 2^31 bytes (bf16, d = 128: H <= 131071).
+bool tile_rows_fit(int64_t H, int64_t D, int64_t esz) {
+    return H <= ((int64_t)0x7fffffff / 64) / (D * esz);
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // a * b without int64 overflow; returns false when the product exceeds lim.
@@ -118,6 +125,7 @@ kda_status prefill_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, 
     // grid size: at most 4096 work-items per head, and a dispatch counts
     // work-items in 32 bits
     if (bh > (int64_t)(0xffffffffu / 4096)) return KDA_ERR_SHAPE;
+    if (!tile_rows_fit(H, D, esz)) return KDA_ERR_SHAPE;
     const bool want_ckpt = ckpt_every > 0 && n_ckpt > 0;
     int dvb = dv_per_block;
     if (dvb == 0) {
@@ -362,7 +370,7 @@ kda_status conv_check(int dtype, int64_t B, int64_t H, int64_t D, const kda_shor
     const int64_t esz = dtype == KDA_BF16 ? 2 : 4;
     int64_t bw, bwh, nst;
     if (!mul_ok(B, W - 1, kMaxElems, &bw) || !mul_ok(bw, H, kMaxElems, &bwh) ||
-        !mul_ok(bwh, D, kMaxElems / 4, &nst))
+        !mul_ok(bwh, D, kMaxElems / 4, &nst) || !tile_rows_fit(H, D, esz))
         return KDA_ERR_SHAPE;
     cs->W = W;
     cs->act = conv->activation;
@@ -862,6 +870,7 @@ kda_status bwd_impl(int dtype, int64_t B, int64_t T, int64_t H, int64_t dk, int6
     // and a dispatch counts work-items in 32 bits (the bound is ~4.2 M
     // chunk-heads, past any workspace that fits in HBM)
     if (bh > 0x7fffffff / 8 || bh * nchunk > (int64_t)(0xffffffffu / 1024)) return KDA_ERR_SHAPE;
+    if (!tile_rows_fit(H, D, esz)) return KDA_ERR_SHAPE;
     const int64_t bth = B * T * H, nin = bth * D, nst = bh * D * D;
     if (!A || !dA) return KDA_ERR_NULL;
     if (bh > 0 && (!dS0)) return KDA_ERR_NULL;

@@ -97,6 +97,9 @@ def test_prefill_shape_and_support_errors(lib):
     assert prefill(lib, chunk=64, dvb=16) == UNSUP         # one-wave 64-token variant not built
     assert prefill(lib, B=1 << 40, T=1 << 40) == SHAPE     # element count overflows
     assert prefill(lib, B=1 << 14, T=1, H=1 << 7) == SHAPE  # 2^21 heads: grid work-items overflow
+    # a 64-token tile of rows (H*d elements each) must stay below 2^31 bytes
+    assert prefill(lib, B=1, T=1, H=1 << 17) == SHAPE
+    assert prefill(lib, B=1, T=1, H=1 << 17, chunk=64) == SHAPE
 
 
 def test_prefill_null_and_alignment_errors(lib):
@@ -211,6 +214,7 @@ def conv_norm(lib, dtype=BF16, B=2, T=64, H=2, dk=128, dv=128, conv=None, sin=No
 
 def test_conv_norm_argument_errors(lib):
     assert conv_norm(lib, B=-1) == SHAPE
+    assert conv_norm(lib, B=1, T=1, H=1 << 17) == SHAPE   # 64-token tile past 2^31 bytes
     assert conv_norm(lib, dk=64, dv=64) == UNSUP
     assert conv_norm(lib, dk=128, dv=16) == UNSUP
     for bad in (short_conv(W=0), short_conv(W=5), short_conv(act=2), short_conv(eps=-1.0),
@@ -388,6 +392,7 @@ def bwd(lib, dtype=BF16, B=1, T=40, H=2, dk=128, dv=128, ptrs=None, ws_bytes=Non
 
 def test_backward_argument_errors(lib):
     assert bwd(lib, T=-1) == SHAPE
+    assert bwd(lib, B=1, T=1, H=1 << 17, ws_bytes=1 << 40) == SHAPE   # 64-token tile past 2^31 bytes
     assert bwd(lib, dtype=7) == UNSUP
     assert bwd(lib, dk=64, dv=64) == UNSUP
     assert bwd(lib, dk=128, dv=16) == UNSUP
