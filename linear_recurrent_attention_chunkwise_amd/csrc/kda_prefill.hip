@@ -244,7 +244,11 @@ __device__ __forceinline__ void prefill_block(const PrefillParams &prm, char *sm
     const float c2 = -__builtin_amdgcn_exp2f(prm.A[h] * kLog2e) * kLog2e;
 
     // ---- state slice: S[16 i + 4 g + e][jw + n] -------------------------
-    const bool want_o = prm.mode == 0;   // modes 1 and 3 write final states only
+    // Modes 1 and 3 write final states only.  They still form the output
+    // tiles and skip only the global stores: branching around the output
+    // products, or fixing the mode at compile time, costs the plain prefill
+    // 2-40% through a worse register allocation at 8 waves.
+    const bool want_o = prm.mode == 0;
     const bool vzero = prm.mode == 3;    // the map M: v read as zero
     f32x4 S[NDT];
     if (prm.mode == 3) {   // the identity
@@ -290,14 +294,12 @@ __device__ __forceinline__ void prefill_block(const PrefillParams &prm, char *sm
                 rb[ii][s] = gbeta[bbase + t * H];
             }
         }
-        if (!vzero) {
 #pragma unroll
-            for (int vi = 0; vi < VQ; ++vi) {
-                int r, cq;
-                v_item<C, DVB, NT>(tid, vi, r, cq);
-                const int64_t t = t0 + r < Tn ? t0 + r : Tn - 1;
-                rv[vi] = *reinterpret_cast<const Quad *>(gv + base + t * tok_stride + j0 + 4 * cq);
-            }
+        for (int vi = 0; vi < VQ; ++vi) {
+            int r, cq;
+            v_item<C, DVB, NT>(tid, vi, r, cq);
+            const int64_t t = t0 + r < Tn ? t0 + r : Tn - 1;
+            rv[vi] = *reinterpret_cast<const Quad *>(gv + base + t * tok_stride + j0 + 4 * cq);
         }
     };
 
@@ -406,7 +408,7 @@ __device__ __forceinline__ void prefill_block(const PrefillParams &prm, char *sm
                 store_pair(sQd + r * DP + d0, q0 * F0 * itot0, q1 * F1 * itot1);
                 store_pair(sKd + r * DP + d0, k0 * F0 * itot0, k1 * F1 * itot1);
                 store_pair(sKt + r * DP + d0, k0 * rl0, k1 * rl1);
-                if (want_o) store_pair(sQG + r * DP + d0, q0 * F0 * pre0, q1 * F1 * pre1);
+                store_pair(sQG + r * DP + d0, q0 * F0 * pre0, q1 * F1 * pre1);
                 store_pair(sKG + r * DP + d0, bt * k0 * F0 * pre0, bt * k1 * F1 * pre1);
                 const float h0 = k0 * rl0 * post0, h1 = k1 * rl1 * post1;
                 if constexpr (kPackT) {
@@ -661,17 +663,15 @@ __device__ __forceinline__ void prefill_block(const PrefillParams &prm, char *sm
 #pragma unroll
             for (int p = 0; p < NP; ++p) Uf[p] = acc_frag<T>(U[p]);
             // O = (Q e^G) S + P U, from the entering state's bf16 image Sf
-            if (want_o) {
 #pragma unroll
-                for (int p = 0; p < NP; ++p) {
-                    O[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    contract_lds_frag<T, D>(O[p], sQG + 16 * p * DP, DP, Sf, lane);
-                    f32x4 Opu = {0.f, 0.f, 0.f, 0.f};
+            for (int p = 0; p < NP; ++p) {
+                O[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                contract_lds_frag<T, D>(O[p], sQG + 16 * p * DP, DP, Sf, lane);
+                f32x4 Opu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int j = 0; j <= p; ++j)
-                        mma16(Opu, lds_frag(sP + 16 * p * CP, CP, 16 * j, lane), Uf[j]);
-                    O[p] += Opu;
-                }
+                for (int j = 0; j <= p; ++j)
+                    mma16(Opu, lds_frag(sP + 16 * p * CP, CP, 16 * j, lane), Uf[j]);
+                O[p] += Opu;
             }
             // S <- e^{G_C} * S + Kh^T U
 #pragma unroll
@@ -683,13 +683,11 @@ __device__ __forceinline__ void prefill_block(const PrefillParams &prm, char *sm
                     mma16(S[i], lds_frag(sKhT + 16 * i * CP, CP, 16 * j, lane), Uf[j]);
             }
             // stage O for coalesced stores
-            if (want_o) {
 #pragma unroll
-                for (int p = 0; p < NP; ++p)
+            for (int p = 0; p < NP; ++p)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sO[(16 * p + 4 * g + e) * OP + 16 * wave + n] = from_f32<T>(O[p][e]);
-            }
+                for (int e = 0; e < 4; ++e)
+                    sO[(16 * p + 4 * g + e) * OP + 16 * wave + n] = from_f32<T>(O[p][e]);
         }
         lds_barrier();
         if (want_o) {
