@@ -29,7 +29,8 @@ included), read from the kernel's summary under profiles/.
 ``long`` times the long-context (B1 H96 T65536, z ~ N(2,1)) and million-token
 (B1 H16 T2^20) prefill workloads at 64- and 16-token chunks over 3 launches
 each, inputs drawn on the device; the million-token head share also split
-into 4, 8 and 9 segments at 16-token chunks and 9 at 64 (kda_prefill_split).
+into 4, 8 and 9 segments at 16-token chunks and 9 and 17 at 64
+(kda_prefill_split).
 Each entry's ``roofline.traffic`` is the HBM bytes per call from its counter
 summary under profiles/ (for a split call, both passes), null once the kernel
 source has changed.  ``timing`` gives the median and minimum per-launch time
@@ -356,7 +357,8 @@ def cpu_baseline(w, inp_cpu):
 LONG_CASES = [("long_prefill_bf16", 64, 1), ("long_prefill_bf16", 16, 1),
               ("million_prefill_bf16", 64, 1), ("million_prefill_bf16", 16, 1),
               ("million_prefill_bf16", 16, 4), ("million_prefill_bf16", 16, 8),
-              ("million_prefill_bf16", 16, 9), ("million_prefill_bf16", 64, 9)]
+              ("million_prefill_bf16", 16, 9), ("million_prefill_bf16", 64, 9),
+              ("million_prefill_bf16", 64, 17)]
 
 
 def time_backward(torch, kda, inp, dO, dST, steps, warmup):

@@ -4,7 +4,7 @@ K3 in "Kimi K3 Open Weights: What Is Actually New", section "Start with the
 released configuration").
 
 Both chunk lengths and the sequence split at each (8 segments at chunk 16,
-9 at chunk 64) are compared with the
+9 and 17 at chunk 64) are compared with the
 fp64 oracle over the FULL length on two heads (the oracle runs segment by
 segment with the state carried across, which the split invariant pins on the
 oracle itself), normwise per head at the bf16 tolerance 2e-2.  On top of
@@ -87,10 +87,11 @@ def _head_relerr(x, ref):
     return worst
 
 
-@pytest.mark.parametrize("chunk,P", [(16, 8), (64, 9)])
+@pytest.mark.parametrize("chunk,P", [(16, 8), (64, 9), (64, 17)])
 def test_million_token_split(kda, gpu_device, million, chunk, P):
     """Split into P segments (chunk 16: 256 workgroups instead of 32; chunk
-    64: 240 in the first pass and 128 in the second instead of 16): against
+    64: 240 + 128 workgroups at 9 segments and 496 + 256 at 17, instead of
+    16): against
     the oracle on the two full-length heads, against the unsplit run on all 16
     heads, and the first segment bit for bit (it starts from S0 itself)."""
     w, inp, o_ref, S_ref = million
