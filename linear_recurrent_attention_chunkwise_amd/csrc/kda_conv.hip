@@ -388,7 +388,9 @@ static hipError_t launch_conv_w(const ConvNormArgs &a) {
 
 hipError_t launch_conv_norm(const ConvNormArgs &a) {
     if (a.dtype == 1) {
-        if (a.D == 128) return launch_conv_w<bf16, 128, 16>(a);
+        // 8-token tiles at d = 128: ~2% faster than 16 (more workgroups in
+        // flight; 32 costs 7.5%), outputs identical
+        if (a.D == 128) return launch_conv_w<bf16, 128, 8>(a);
         return launch_conv_w<bf16, 16, 16>(a);
     }
     if (a.D == 128) return launch_conv_w<float, 128, 8>(a);
