@@ -24,15 +24,17 @@
 //   row side    Qd_r = q_r e^{G_r - E_p}      (E_p = G at the end of r's sub-tile p)
 //   column side Kt_s = k_s e^{E_p' - G_s}     (s in sub-tile p')
 //   block (p,p') = Qd_p (Kt_p' * F_{p,p'})^T,  F_{p,p'} = e^{E_p - E_p'} <= 1.
-// T = (I+L)^-1 is formed as 16 x 16 blocks: the diagonal ones by forward
-// substitution, the others from them by block forward substitution, and the
-// chain applies T to its rounded V - K e^G S (one product per block).
+// T = (I+L)^-1 is formed as 16 x 16 blocks: the diagonal ones by nilpotent
+// doubling on MFMA, the others from them by block forward substitution, and
+// the chain applies T to its rounded V - K e^G S (one product per block).
 //
 // Work split (one workgroup per (b, h, slice of value columns)):
 //   * value columns of the state evolve independently, so a workgroup owns
-//     DVB = 16 * NW of them; each wave owns 16 columns and the full dk x 16
-//     fp32 state slice in registers, and runs the S-dependent chain (U, O,
-//     state update) with no cross-wave traffic;
+//     DVB = 16 * NW of them (bf16, dk = 128, 64-token chunks: all 128, eight
+//     waves, so a chunk's key-side work is done once per head); each wave
+//     owns 16 columns and the full dk x 16 fp32 state slice in registers, and
+//     runs the S-dependent chain (U, O, state update) with no cross-wave
+//     traffic;
 //   * the S-independent per-chunk work (gate, decay factors, P, L and the
 //     blocks of T) is done cooperatively by the waves into LDS;
 //   * the next chunk's q, k, z, beta, v are prefetched into registers while
