@@ -410,16 +410,17 @@ kda_status conv_check(int dtype, int64_t B, int64_t H, int64_t D, const kda_shor
 }
 
 // Sizes the prologue kernel can address: (tile + 3) token rows in 32-bit
-// buffer offsets, and the grid.
+// buffer offsets, and the grid (256 work-items per workgroup, counted in 32
+// bits by a dispatch).
 bool conv_sizes_ok(int dtype, int64_t B, int64_t T, int64_t H, int64_t D) {
     const int64_t esz = dtype == KDA_BF16 ? 2 : 4;
-    const int64_t tt = kda::conv_tile_tokens(dtype);
+    const int64_t tt = kda::conv_tile_tokens(dtype, D);
     if (H * D * esz * (tt + 3) >= ((int64_t)1 << 31)) return false;
     const int64_t ntile = T > 0 ? (T + tt - 1) / tt : 1;
     const int64_t nslab = (H * (D / 8) + 63) / 64;
     int64_t n1, n2;
     return mul_ok(B, nslab, kMaxElems, &n1) && mul_ok(n1, (ntile + 3) / 4, kMaxElems, &n2) &&
-           n2 < ((int64_t)1 << 32) - 1;
+           n2 < ((int64_t)1 << 32) / 256;
 }
 
 kda::ConvNormArgs conv_args(int dtype, int64_t B, int64_t T, int64_t H, int64_t D,

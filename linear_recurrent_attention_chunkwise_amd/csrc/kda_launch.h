@@ -75,7 +75,7 @@ struct ConvNormArgs {
 
 bool conv_supported(int dtype, int64_t D);
 // Tokens per wave tile of the prologue kernel.
-int conv_tile_tokens(int dtype);
+int conv_tile_tokens(int dtype, int64_t D);
 hipError_t launch_conv_norm(const ConvNormArgs &a);
 
 struct DecodeArgs {
