@@ -45,6 +45,17 @@ def _check_prefill(kda, dev, w, chunk=None, T=None, dvb=0, heads=None, oracle_T=
     return o, S_T
 
 
+def _check_prefill_inp(kda, dev, inp, chunk, what):
+    """Prefill of given inputs against the oracle at the dtype's tolerance."""
+    o, S_T = gpu_prefill(kda, to_dev(inp, dev), chunk)
+    o_ref, S_ref = oracle_prefill(inp)
+    tol = TOL[inp["q"].dtype]
+    eo, es = slice_relerr(host(o), o_ref, 2), slice_relerr(host(S_T), S_ref, 1)
+    _say(f"[{what}] chunk {chunk}: o err {eo:.3e}  S_T err {es:.3e}  (o {diag(host(o), o_ref)})")
+    assert eo <= tol and es <= tol
+    return o, S_T
+
+
 # ------------------------------------------------------------- prefill ----
 
 def test_tiny_fp32_workload(kda, gpu_device):
@@ -222,6 +233,32 @@ def test_beta_zero_closed_form(kda, gpu_device, dtype, d, chunk, z_mean):
     _say(f"[beta=0] {dtype} d={d} chunk={chunk} z_mean={z_mean}: o err {eo:.3e}  "
          f"S_T err {es:.3e}")
     assert eo <= tol and es <= tol
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_extreme_gate_scales(kda, gpu_device, chunk):
+    """Per-head A far outside U(-1, 1): e^A underflowing fp32 (A = -100: the
+    gate is sigma(0) for every z, a decay of e^{g_min/2}), small (A = -20), and
+    large (A = 4: the gate saturates, decays of exactly 1 or e^{g_min}).
+    Prefill over a ragged length, and decode steps, against the oracle."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(B=2, H=4, s0_std=0.5)
+    inp = make_prefill_inputs(w, T=150)
+    inp["A"] = torch.tensor([-100.0, -20.0, 4.0, 0.5])
+    _check_prefill_inp(kda, gpu_device, inp, chunk, "extreme A")
+    # decode: 6 steps from the prefill's inputs, one token at a time
+    S = inp["S0"].to(gpu_device)
+    S_ref = inp["S0"].double().numpy()
+    A = inp["A"].to(gpu_device)
+    worst_o = worst_s = 0.0
+    for t in range(6):
+        args = [inp[n][:, t].contiguous() for n in ("q", "k", "v", "z", "beta")]
+        o = kda.decode_step(*[a.to(gpu_device) for a in args], A, S)
+        o_ref, S_ref = oracle.decode_step(*[host(a) for a in args], host(inp["A"]), S_ref)
+        torch.cuda.synchronize()
+        worst_o = max(worst_o, slice_relerr(host(o)[:, None], o_ref[:, None], 2))
+        worst_s = max(worst_s, slice_relerr(host(S), S_ref, 1))
+    _say(f"[extreme A] decode 6 steps: o err {worst_o:.3e} S err {worst_s:.3e}")
+    assert worst_o <= 2e-2 and worst_s <= 2e-2
 
 
 def test_plain_entry_point_symbol(kda, gpu_device):

@@ -56,6 +56,20 @@ def test_gate_matches_library_logistic_and_range():
         assert np.all(np.diff(g[order]) <= 0.0)   # decreasing in z (e^A > 0)
 
 
+def test_gate_extreme_scales():
+    """Far outside the usual A: e^A underflowing to 0 gives sigma(0) = 1/2 for
+    every finite z (g = g_min / 2); a large e^A saturates the logistic to
+    g_min or 0 except right at z = 0 -- as the library logistic says."""
+    z = np.array([-30.0, -1.0, -1e-3, 0.0, 1e-3, 1.0, 30.0])
+    assert np.all(oracle.gate(z, -800.0) == -2.5)          # e^A = 0 exactly in fp64
+    g = oracle.gate(z, -100.0)                              # e^A = 3.7e-44
+    np.testing.assert_allclose(g, -5.0 * expit(np.exp(-100.0) * z), rtol=1e-15)
+    assert np.all(np.abs(g + 2.5) < 1e-40)
+    g = oracle.gate(z, 4.0)                                 # e^A = 54.6
+    np.testing.assert_allclose(g, -5.0 * expit(np.exp(4.0) * z), rtol=1e-14, atol=1e-300)
+    assert g[0] == 0.0 and g[-1] == -5.0 and g[3] == -2.5
+
+
 def test_page_range_claim():
     """g_min = -5 bounds a 16-token log-decay window by -80, and e^80 fits bf16."""
     c = json.load(open(GOLDEN))
