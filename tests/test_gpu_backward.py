@@ -63,8 +63,10 @@ def _errors(got, ref):
     return errs
 
 
-def _check(kda, w, T, gpu_device, with_dST=True):
+def _check(kda, w, T, gpu_device, with_dST=True, A=None):
     inp = make_prefill_inputs(w, T=T)
+    if A is not None:
+        inp["A"] = torch.tensor(A, dtype=inp["A"].dtype)
     dO, dST = make_cotangents(w, T=T, with_dST=with_dST)
     g = to_dev(inp, gpu_device)
     got = _gpu_bwd(kda, g, dO.to(gpu_device), None if dST is None else dST.to(gpu_device))
@@ -111,6 +113,15 @@ def test_backward_near_gmin(kda, gpu_device, dtype, d):
                                            s0_std=0.5)
     _say(f"[bwd] near g_min {dtype} d={d} T=100")
     _check(kda, w, 100, gpu_device)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 16), ("bf16", 128)])
+def test_backward_extreme_gate_scales(kda, gpu_device, dtype, d):
+    """Per-head A = -100 (e^A underflows fp32: the gate is sigma(0) and dA
+    vanishes), -20, 4 (saturated gate) and 0.5, against the adjoint oracle."""
+    w = WORKLOADS["k3_prefill_bf16"].with_(B=1, H=4, dk=d, dv=d, dtype=dtype, s0_std=0.5)
+    _say(f"[bwd] extreme A {dtype} d={d} T=70")
+    _check(kda, w, 70, gpu_device, A=[-100.0, -20.0, 4.0, 0.5])
 
 
 def test_backward_without_state_inputs(kda, gpu_device):
