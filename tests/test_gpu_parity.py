@@ -324,6 +324,32 @@ def test_decode_full_batch_one_step(kda, gpu_device):
     assert eo <= 2e-2 and es <= 2e-2
 
 
+def test_decode_bench_workload_sampled_heads(kda, gpu_device):
+    """The decode bench workload itself (B64 H96 d128 bf16, 256 steps from a
+    zero state), every head stepped on the GPU as the bench does; nine (b, h)
+    heads followed by the oracle through all 256 steps: each step's o and the
+    final state."""
+    w = WORKLOADS["k3_decode_bf16"]
+    inp = make_decode_inputs(w)
+    bi, hi = [0, 31, 63], [0, 47, 95]
+    sel = lambda t: t[bi][:, hi]
+    S = inp["S"].to(gpu_device)
+    A = inp["A"].to(gpu_device)
+    S_ref = sel(inp["S"]).double().numpy()
+    A_ref = host(inp["A"])[hi]
+    worst_o = 0.0
+    for t in range(w.steps):
+        args = [inp[n][t] for n in ("q", "k", "v", "z", "beta")]
+        o = kda.decode_step(*[a.to(gpu_device) for a in args], A, S)
+        o_ref, S_ref = oracle.decode_step(*[host(sel(a)) for a in args], A_ref, S_ref)
+        worst_o = max(worst_o, slice_relerr(host(sel(o.cpu()))[:, None], o_ref[:, None], 2))
+    torch.cuda.synchronize()
+    es = slice_relerr(host(sel(S.cpu())), S_ref, 1)
+    _say(f"[decode] bench workload, {w.steps} steps, 9 sampled heads: o err {worst_o:.3e} "
+         f"S err {es:.3e}")
+    assert worst_o <= 2e-2 and es <= 2e-2
+
+
 def test_decode_fp32_d16(kda, gpu_device):
     g = torch.Generator().manual_seed(11)
     B, H, D = 3, 5, 16
