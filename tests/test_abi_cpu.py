@@ -215,6 +215,9 @@ def conv_norm(lib, dtype=BF16, B=2, T=64, H=2, dk=128, dv=128, conv=None, sin=No
 def test_conv_norm_argument_errors(lib):
     assert conv_norm(lib, B=-1) == SHAPE
     assert conv_norm(lib, B=1, T=1, H=1 << 17) == SHAPE   # 64-token tile past 2^31 bytes
+    # 2^24 workgroups of 256 work-items (8-token tiles at bf16 d = 128): the
+    # dispatch's 32-bit work-item count would wrap
+    assert conv_norm(lib, B=1, T=1 << 21, H=1024) == SHAPE
     assert conv_norm(lib, dk=64, dv=64) == UNSUP
     assert conv_norm(lib, dk=128, dv=16) == UNSUP
     for bad in (short_conv(W=0), short_conv(W=5), short_conv(act=2), short_conv(eps=-1.0),
