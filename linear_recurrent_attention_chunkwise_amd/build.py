@@ -21,10 +21,11 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["kda_api.hip", "kda_backward.hip", "kda_conv.hip", "kda_decode.hip", "kda_prefill.hip", "kda_prefill16.hip", "kda_split.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
-# Per-source code-generation options.  The role-split prefill is bound by the
-# latency of its per-chunk chain; the instruction-level-parallelism scheduler
-# orders it ~1.4% faster on MI355X than the default (229.8 vs 233.1 us on the
-# K3 prefill shape, A/B over back-to-back launches).
+# Per-source code-generation options.  The role-split prefill's waves are
+# latency-bound and share their SIMDs; the instruction-level-parallelism
+# scheduler orders it ~4.6% faster on MI355X than the default scheduler (169
+# vs 177 us on the K3 prefill shape, interleaved A/B in one process; the
+# memory-clause strategy also reads 177 us).
 EXTRA_FLAGS = {"kda_prefill16.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
