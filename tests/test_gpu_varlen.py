@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from linear_recurrent_attention_chunkwise_amd.inputs import WORKLOADS, make_varlen_inputs
-from tests.gpu_helpers import TOL, host, slice_relerr, to_dev
+from tests.gpu_helpers import TOL, diag, host, slice_relerr, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -165,6 +165,35 @@ def test_varlen_checkpoints_chunk64_full_shape(kda, gpu_device):
         ec = slice_relerr(host(ck[rows[i]:rows[i] + 1]), S_1, 1)
         _say(f"   seq {i}: o err {eo:.2e}  S_T err {es:.2e}  first checkpoint err {ec:.2e}")
         assert eo <= 2e-2 and es <= 2e-2 and ec <= 2e-2
+
+
+def test_varlen_bench_workload(kda, gpu_device):
+    """The packed workload the bench times (eight sequences of lengths 4096,
+    1000, 37, 2500, 16, 513, 64, 3000; all 96 heads; 16-token chunks; a
+    checkpoint every 1024 tokens), every head of every sequence and every
+    checkpoint against the oracle."""
+    lengths, every = [4096, 1000, 37, 2500, 16, 513, 64, 3000], 1024
+    w = WORKLOADS["k3_prefill_bf16"].with_(seed=5)
+    inp = make_varlen_inputs(w, lengths)
+    cu = inp["cu_seqlens"].tolist()
+    _say(f"[varlen] bench workload H={w.H} lengths={lengths} every={every}")
+    o, S_T, ck = _run(kda, inp, gpu_device, 16, every=every)
+    rows, _ = kda.checkpoint_rows(lengths, every)
+    worst = 0.0
+    for i, L in enumerate(lengths):
+        o_ref, S_ref = _oracle_seq(inp, cu, i)
+        a, b = cu[i], cu[i + 1]
+        eo = slice_relerr(host(o[a:b])[None], o_ref, 2)
+        es = slice_relerr(host(S_T[i:i + 1]), S_ref, 1)
+        ec = 0.0
+        for j in range(1, L // every + 1):
+            _, S_j = _oracle_seq(inp, cu, i, T=j * every)
+            ec = max(ec, slice_relerr(host(ck[rows[i] + j - 1:rows[i] + j]), S_j, 1))
+        _say(f"   seq {i} len {L}: o err {eo:.2e}  S_T err {es:.2e}  checkpoints err {ec:.2e}"
+             f"  (o {diag(host(o[a:b])[None], o_ref)})")
+        worst = max(worst, eo, es, ec)
+    _say(f"   worst over outputs, final states and {ck.shape[0]} checkpoints: {worst:.2e}")
+    assert worst <= TOL[inp["q"].dtype]
 
 
 def test_varlen_equals_dense_bitwise(kda, gpu_device):
