@@ -87,7 +87,7 @@ def _head_relerr(x, ref):
     return worst
 
 
-@pytest.mark.parametrize("chunk,P", [(16, 8), (64, 9), (64, 17)])
+@pytest.mark.parametrize("chunk,P", [(16, 4), (16, 8), (16, 9), (64, 9), (64, 17)])
 def test_million_token_split(kda, gpu_device, million, chunk, P):
     """Split into P segments (chunk 16: 256 workgroups instead of 32; chunk
     64: 240 + 128 workgroups at 9 segments and 496 + 256 at 17, instead of
